@@ -1,0 +1,97 @@
+"""Algorithmic byte counts of one decode step (the denominator of the roofline).
+
+The decode step reads every quantized weight once and the key/value cache once; its
+arithmetic intensity is about 2 flop/byte, so its floor is bytes / HBM bandwidth ("Every Frame
+Is a Memory Read", §3 "Predict first: the roofline": time per step is about the bytes read per
+step over the sustained bandwidth).  Counted per step:
+
+* weights   - every quantized matrix in its stored format (scales and biases included);
+* vectors   - fp32 norm gains/biases and linear biases;
+* embedding - the embedding rows gathered (token row, plus the learned position row for GPT-2;
+              sixteen code rows per frame for the Talker, one row per predictor pass);
+* kv        - the fp16 keys and values of every position the step attends to, the new position
+              included (it is written once and read by attention).
+
+Activations (a few KB) are not counted.
+"""
+from __future__ import annotations
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+
+
+def matrix_bytes(fmt: str, N: int, K: int) -> int:
+    if fmt == "q4_0":
+        return N * (K // 32) * 18
+    if fmt == "q8_0":
+        return N * (K // 32) * 34
+    if fmt == "aff8":
+        return N * K + N * (K // 64) * 4
+    raise ValueError(fmt)
+
+
+def _llama_layer_mats(c):
+    d, H, Hk, hd, ff = c["d_model"], c["n_head"], c["n_kv_head"], c["head_dim"], c["d_ff"]
+    return [(H * hd, d), (Hk * hd, d), (Hk * hd, d), (d, H * hd), (ff, d), (ff, d), (d, ff)]
+
+
+def _gpt2_layer_mats(c):
+    d, ff = c["d_model"], c["d_ff"]
+    return [(3 * d, d), (d, d), (ff, d), (d, ff)]
+
+
+def params_per_layer(c) -> int:
+    mats = _gpt2_layer_mats(c) if c["arch"] == "gpt2" else _llama_layer_mats(c)
+    return sum(N * K for N, K in mats)
+
+
+def kv_bytes_per_position(c, n_layer=None) -> int:
+    """fp16 K and V of one position over all layers, one batch row."""
+    L = c["n_layer"] if n_layer is None else n_layer
+    return L * 2 * c["n_kv_head"] * c["head_dim"] * 2
+
+
+def layer_weight_bytes(c) -> int:
+    mats = _gpt2_layer_mats(c) if c["arch"] == "gpt2" else _llama_layer_mats(c)
+    return sum(matrix_bytes(c["wfmt"], N, K) for N, K in mats)
+
+
+def step_bytes(c, pos: int) -> dict:
+    """Bytes of one decode step at position pos (keys 0..pos), all batch rows.
+
+    For talker_cp one step is one frame: the Talker step plus the 15 predictor passes."""
+    d, f, L, B = c["d_model"], c["wfmt"], c["n_layer"], c["batch"]
+    out = {}
+    if c["arch"] == "gpt2":
+        ff = c["d_ff"]
+        out["weights"] = L * layer_weight_bytes(c) + matrix_bytes(f, c["vocab"], d)
+        out["vectors"] = 4 * (L * (4 * d + 3 * d + d + ff + d) + 2 * d)
+        out["embedding"] = B * 2 * d * 4
+        out["kv"] = B * (pos + 1) * kv_bytes_per_position(c)
+    elif c["arch"] == "llama":
+        out["weights"] = L * layer_weight_bytes(c) + matrix_bytes(f, c["vocab"], d)
+        out["vectors"] = 4 * (L * 2 * d + d)
+        out["embedding"] = B * d * 4
+        out["kv"] = B * (pos + 1) * kv_bytes_per_position(c)
+    elif c["arch"] == "talker_cp":
+        C, Lc, Vc = c["n_codebooks"], c["cp_n_layer"], c["cp_vocab"]
+        passes = C - 1
+        talker_w = L * layer_weight_bytes(c) + matrix_bytes(f, c["vocab"], d)
+        cp_w = Lc * layer_weight_bytes(c) + matrix_bytes(f, Vc, d)
+        out["weights"] = talker_w + passes * cp_w
+        out["vectors"] = 4 * (L * 2 * d + d) + passes * 4 * (Lc * 2 * d + d)
+        out["embedding"] = B * C * d * 4 + B * passes * d * 4
+        cp_positions = sum(j + 1 for j in range(1, C))          # pass j attends to 0..j
+        out["kv"] = B * ((pos + 1) * kv_bytes_per_position(c) + cp_positions * kv_bytes_per_position(c, Lc))
+    else:
+        raise KeyError(c["arch"])
+    out["total"] = sum(out.values())
+    return out
+
+
+def mean_step_bytes(c, first_pos: int, n_steps: int) -> float:
+    return sum(step_bytes(c, p)["total"] for p in range(first_pos, first_pos + n_steps)) / n_steps
+
+
+def gemv_bytes(fmt: str, N: int, K: int, B: int = 1, bias: bool = False) -> int:
+    """One GEMV launch: the matrix, plus x [B][K] read and y [B][N] written in fp32."""
+    return matrix_bytes(fmt, N, K) + 4 * B * (K + N) + (4 * N if bias else 0)

@@ -1,0 +1,230 @@
+"""Whole-model pins of the oracle (CPU only, tiny shapes).
+
+* step-by-step decode with the KV cache == a from-scratch causal forward over the sequence;
+* causal invariance: later tokens never change earlier outputs;
+* one layer == the same layer composed in Python from the separately pinned operators;
+* the Talker + code-predictor frame == plain Llama-shaped forwards over the sequences the
+  frame loop defines (pins the embedding sum, the pass wiring, the per-frame restart);
+* greedy / top-k picks == the sampler applied to the returned logits;
+* batch rows are independent; bad inputs raise and leave the state alone.
+"""
+import numpy as np
+import pytest
+
+from quantized_gemv_kv_amd import synth
+
+
+def rel(a, b):
+    return float(np.max(np.abs(np.asarray(a) - np.asarray(b))) / np.max(np.abs(b)))
+
+
+def make(orc, cfg, seed=42, **kw):
+    w = synth.model_weights(cfg, seed, **kw)
+    return orc.OracleModel(cfg, w), w
+
+
+@pytest.mark.parametrize("arch,fmt", [("gpt2", "q4_0"), ("gpt2", "q8_0"), ("llama", "q8_0"), ("llama", "aff8")])
+def test_decode_equals_causal_sequence_forward(orc, arch, fmt):
+    cfg = synth.small_config(arch, fmt)
+    m, _ = make(orc, cfg, norm_std=0.5)
+    toks = synth.prompt_tokens(cfg, 12, seed=3)[0, :, 0]
+    seq = m.forward_sequence(toks)
+    for p, t in enumerate(toks):
+        m.step([t])
+        np.testing.assert_allclose(m.logits()[0], seq[p], rtol=1e-11, atol=1e-11 * np.abs(seq[p]).max())
+    # prefill of the same prompt from a reset state gives the last position's logits
+    m.reset()
+    nxt = m.prefill(toks[None, :, None])
+    np.testing.assert_allclose(m.logits()[0], seq[-1], rtol=1e-11, atol=1e-11 * np.abs(seq[-1]).max())
+    assert nxt[0, 0] == int(np.argmax(seq[-1]))
+    assert m.n_past == len(toks)
+
+
+@pytest.mark.parametrize("arch", ["gpt2", "llama"])
+def test_causal_invariance(orc, arch):
+    cfg = synth.small_config(arch, "q8_0")
+    m, _ = make(orc, cfg, norm_std=0.5)
+    toks = synth.prompt_tokens(cfg, 10, seed=5)[0, :, 0]
+    a = m.forward_sequence(toks)
+    for i in (2, 6):
+        t2 = toks.copy()
+        t2[i + 1:] = (t2[i + 1:] + 17) % cfg["vocab"]
+        b = m.forward_sequence(t2)
+        assert np.array_equal(a[: i + 1], b[: i + 1])
+        assert not np.array_equal(a[i + 1:], b[i + 1:])
+
+
+def _layer_by_hand(orc, cfg, w, l, x, pos, kc, vc):
+    """One layer composed from the pinned operators. kc/vc [Hkv][pos][hd] fp16 prior keys."""
+    d, H, Hk, hd, ff, f = (cfg[k] for k in ("d_model", "n_head", "n_kv_head", "head_dim", "d_ff", "wfmt"))
+    x = x.astype(np.float64).copy()
+    if cfg["arch"] == "gpt2":
+        g1, b1, wqkv, bqkv, wo, bo, g2, b2, wfc, bfc, wd, bd = w[2 + 12 * l: 2 + 12 * l + 12]
+        n = orc.layernorm(x, g1, b1, cfg["norm_eps"])
+        qkv = orc.gemv(f, wqkv, 3 * d, d, n, bqkv)
+        q, k, v = qkv[:d], qkv[d:2 * d], qkv[2 * d:]
+    else:
+        g1, wq, wk, wv, wo, g2, wg, wu, wd = w[1 + 9 * l: 1 + 9 * l + 9]
+        n = orc.rmsnorm(x, g1, cfg["norm_eps"])
+        q = orc.gemv(f, wq, H * hd, d, n)
+        k = orc.gemv(f, wk, Hk * hd, d, n)
+        v = orc.gemv(f, wv, Hk * hd, d, n)
+        q = np.concatenate([orc.rope_neox(q[h * hd:(h + 1) * hd], pos, cfg["rope_theta"]) for h in range(H)])
+        k = np.concatenate([orc.rope_neox(k[h * hd:(h + 1) * hd], pos, cfg["rope_theta"]) for h in range(Hk)])
+    o = []
+    for h in range(H):
+        g = h // (H // Hk)
+        kk = np.concatenate([kc[g], orc_half_row(orc, k[g * hd:(g + 1) * hd])[None]], 0)
+        vv = np.concatenate([vc[g], orc_half_row(orc, v[g * hd:(g + 1) * hd])[None]], 0)
+        o.append(orc.attend(q[h * hd:(h + 1) * hd], kk, vv))
+    o = np.concatenate(o)
+    if cfg["arch"] == "gpt2":
+        x += orc.gemv(f, wo, d, d, o, bo)
+        n = orc.layernorm(x, g2, b2, cfg["norm_eps"])
+        hmid = np.array([orc.gelu_tanh(t) for t in orc.gemv(f, wfc, ff, d, n, bfc)])
+        x += orc.gemv(f, wd, d, ff, hmid, bd)
+    else:
+        x += orc.gemv(f, wo, d, H * hd, o)
+        n = orc.rmsnorm(x, g2, cfg["norm_eps"])
+        gg, uu = orc.gemv(f, wg, ff, d, n), orc.gemv(f, wu, ff, d, n)
+        x += orc.gemv(f, wd, d, ff, np.array([orc.silu(a) for a in gg]) * uu)
+    return x
+
+
+def orc_half_row(orc, v):
+    return np.array([orc.double_to_half(float(t)) for t in v], np.uint16)
+
+
+@pytest.mark.parametrize("arch,fmt,hk", [("gpt2", "q4_0", 4), ("llama", "q8_0", 2), ("llama", "aff8", 1)])
+def test_layer_forward_equals_composed_operators(orc, arch, fmt, hk):
+    cfg = synth.small_config(arch, fmt, n_kv_head=hk if arch != "gpt2" else 4)
+    m, w = make(orc, cfg)
+    P = 20
+    k, v = synth.kv_cache(cfg, P, seed=9)
+    m.load_kv(k, v, P)
+    x = synth.hidden(cfg, seed=4)
+    for l in range(cfg["n_layer"]):
+        got = m.layer_forward(l, x, P)[0]
+        ref = _layer_by_hand(orc, cfg, w, l, x[0], P, k[l, 0], v[l, 0])
+        assert rel(got, ref) < 1e-12
+
+
+def test_talker_cp_frame_equals_llama_sequences(orc):
+    cfg = synth.small_config("talker_cp", "aff8")
+    C, L, Lc, d = cfg["n_codebooks"], cfg["n_layer"], cfg["cp_n_layer"], cfg["d_model"]
+    m, w = make(orc, cfg, norm_std=0.5)
+    E = [w[c].astype(np.float64) for c in range(C)]
+    talker_w = w[C:C + 9 * L + 2]
+    cp_layers = w[C + 9 * L + 2: C + 9 * L + 2 + 9 * Lc]
+    cp_norm = w[C + 9 * L + 2 + 9 * Lc]
+    cp_heads = w[C + 9 * L + 3 + 9 * Lc:]
+    assert len(cp_heads) == C - 1
+    n = 5
+    toks = synth.prompt_tokens(cfg, n, seed=6)                       # [B][n][C]
+    out1 = m.prefill(toks)
+    lg1 = m.logits()
+    out2 = m.step()                                                  # next frame from the sampled codes
+    lg2 = m.logits()
+
+    tcfg = dict(cfg, arch="llama", n_codebooks=0, cp_n_layer=0, cp_vocab=0, batch=1)
+    ccfg = dict(tcfg, n_layer=Lc, vocab=cfg["cp_vocab"])
+    for b in range(cfg["batch"]):
+        frames = [toks[b, t] for t in range(n)] + [out1[b]]
+        # Talker: embedding table whose row t is the sum of frame t's 16 code embeddings
+        emb = np.zeros((cfg["vocab"], d), np.float64)
+        for t, fr in enumerate(frames):
+            emb[t] = sum(E[c][fr[c]] for c in range(C))
+        tm = orc.OracleModel(tcfg, [emb.astype(np.float32)] + talker_w)
+        tl, th = tm.forward_sequence(np.arange(n + 1), with_hidden=True)
+        for frame, (outs, lgs, t) in enumerate([(out1, lg1, n - 1), (out2, lg2, n)]):
+            assert rel(lgs[b, 0, :cfg["vocab"]], tl[t]) < 1e-6
+            codes = outs[b]
+            assert codes[0] == int(np.argmax(lgs[b, 0, :cfg["vocab"]]))
+            # predictor: row 0 = Talker final-normed hidden, row j = E_{j-1}(c_{j-1})
+            cemb = np.zeros((cfg["cp_vocab"], d), np.float64)
+            cemb[0] = th[t]
+            for j in range(1, C):
+                cemb[j] = E[j - 1][codes[j - 1]]
+            for j in range(1, C):
+                cm = orc.OracleModel(ccfg, [cemb.astype(np.float32)] + cp_layers + [cp_norm, cp_heads[j - 1]])
+                cl = cm.forward_sequence(np.arange(j + 1))
+                got = lgs[b, j, :cfg["cp_vocab"]]
+                assert rel(got, cl[j]) < 1e-6, (b, frame, j)
+                assert codes[j] == int(np.argmax(got))
+
+
+def test_topk_mode_uses_counter_draws(orc):
+    cfg = synth.small_config("gpt2", "q8_0", sample_mode=1, top_k=7, temperature=0.8, seed=1234)
+    m, _ = make(orc, cfg, norm_std=0.5)
+    toks = synth.prompt_tokens(cfg, 6, seed=2)
+    nxt = m.prefill(toks)
+    for _ in range(8):
+        pos = m.n_past - 1
+        lg = m.logits()[0]
+        assert nxt[0, 0] == orc.sample_topk(lg, 7, 0.8, orc.uniform24(1234, 0, pos, 0))
+        nxt = m.step()
+
+
+def test_batch_rows_are_independent(orc):
+    cfg2 = synth.small_config("llama", "q8_0", batch=2)
+    cfg1 = dict(cfg2, batch=1)
+    w = synth.model_weights(cfg2, 42)
+    m2, m1 = orc.OracleModel(cfg2, w), orc.OracleModel(cfg1, w)
+    toks = synth.prompt_tokens(cfg2, 7, seed=8)
+    m2.prefill(toks)
+    for b in range(2):
+        m1.reset()
+        m1.prefill(toks[b:b + 1])
+        assert np.array_equal(m1.logits()[0], m2.logits()[b])
+
+
+def test_errors_leave_state_unchanged(orc):
+    cfg = synth.small_config("gpt2", "q4_0")
+    m, w = make(orc, cfg)
+    m.prefill(synth.prompt_tokens(cfg, 4))
+    with pytest.raises(ValueError):
+        m.step([cfg["vocab"]])                                   # token out of range
+    assert m.n_past == 4
+    with pytest.raises(ValueError):
+        m.prefill(np.zeros((1, cfg["n_ctx"], 1), np.int32))      # context full
+    assert m.n_past == 4
+    with pytest.raises(ValueError):
+        m.truncate(5)
+    m.truncate(2)
+    assert m.n_past == 2
+    with pytest.raises(ValueError):
+        orc.OracleModel(cfg, w[:-1])                             # wrong number of weights
+    bad = list(w)
+    bad[4] = bad[4][:-1]
+    with pytest.raises(ValueError):
+        orc.OracleModel(cfg, bad)                                # wrong byte size
+    with pytest.raises(ValueError):
+        orc.OracleModel(dict(cfg, d_model=130), w)               # K not a multiple of 32
+
+
+@pytest.mark.parametrize("arch,fmt", [("gpt2", "q4_0"), ("llama", "q8_0")])
+def test_step_equals_embedding_layers_norm_head(orc, arch, fmt):
+    """A decode step == the embedding rows added by hand (token row, plus the learned position
+    row for GPT-2), then layer_forward per layer, then the final norm and head GEMV."""
+    cfg = synth.small_config(arch, fmt)
+    w = synth.model_weights(cfg, 42, norm_std=0.5)
+    P = 13
+    k, v = synth.kv_cache(cfg, P, seed=1)
+    a, b = orc.OracleModel(cfg, w), orc.OracleModel(cfg, w)
+    a.load_kv(k, v, P)
+    b.load_kv(k, v, P)
+    tok = 77
+    a.step([tok])
+    d = cfg["d_model"]
+    x = w[0][tok].astype(np.float64)
+    if arch == "gpt2":
+        x = x + w[1][P].astype(np.float64)
+    x = x[None]
+    for l in range(cfg["n_layer"]):
+        x = b.layer_forward(l, x, P)
+    if arch == "gpt2":
+        h = orc.layernorm(x[0], w[-3], w[-2], cfg["norm_eps"])
+    else:
+        h = orc.rmsnorm(x[0], w[-2], cfg["norm_eps"])
+    ref = orc.gemv(fmt, w[-1], cfg["vocab"], d, h)
+    assert rel(a.logits()[0], ref) < 1e-12

@@ -1,0 +1,178 @@
+/*
+ * tsd.h — C ABI of libtsd: the single-token, memory-bound decode step of a speech-token
+ * transformer with block-quantized weights, on AMD Instinct MI355X (gfx950).
+ *
+ * Sources for what each call computes:
+ *   [J] "Chatterbox -> ggml Port: Development Journal" (chatterbox.cpp PROGRESS.md)
+ *   [F] "Every Frame Is a Memory Read: A Systems View of Speech Model Inference on Apple Silicon"
+ *
+ * General conventions
+ *   - Every function returns tsd_status; 0 (TSD_OK) is success.  No C++ exception crosses the
+ *     ABI.  On any error the model state is unchanged and tsd_last_error() describes it.
+ *   - Pointers named d_* are device pointers (HIP global memory) owned by the caller.  The
+ *     library never allocates device memory for tensors: all model state lives in the
+ *     caller's workspace.  (Creating the step graph lets the HIP runtime allocate its own
+ *     small bookkeeping.)
+ *   - `stream` is a hipStream_t passed as void*.  Calls only enqueue work on it; results in
+ *     device memory are valid once the caller synchronises that stream.
+ *   - A model is not thread-safe; use one model per stream.
+ *
+ * Weight formats ([J] appendix A3 "Quantize T3" and §3.23; [F] §3 "Counting the bytes"):
+ *   TSD_W_Q4_0        rows of K/32 blocks, 18 bytes each: fp16 scale d (little endian), then 16
+ *                     bytes; element j<16 is the low nibble of byte j, element j+16 its high
+ *                     nibble; w = (q - 8) * d.
+ *   TSD_W_Q8_0        rows of K/32 blocks, 34 bytes each: fp16 d, then 32 int8 q; w = d * q.
+ *   TSD_W_AFFINE8_G64 planar: q[N][K] uint8, then s[N][K/64] fp16, then b[N][K/64] fp16;
+ *                     w = s * q + b for each group of 64 along K.
+ *   All matrices are W[N][K]: N output rows, each contiguous along the reduction axis K
+ *   ([J] §3.2 issue 5).  K must be a multiple of 32 (Q4_0, Q8_0) or 64 (affine).
+ */
+#ifndef TSD_H
+#define TSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TSD_OK = 0,
+    TSD_ERR_INVALID_ARGUMENT = 1, /* null/undersized buffer, bad shape, token >= vocab */
+    TSD_ERR_UNSUPPORTED = 2,      /* a valid configuration this build has no kernel for */
+    TSD_ERR_OUT_OF_MEMORY = 3,    /* host allocation failed */
+    TSD_ERR_CONTEXT_FULL = 4,     /* n_past + n > n_ctx */
+    TSD_ERR_HIP = 5,              /* a HIP runtime call failed; message has hipGetErrorString */
+    TSD_ERR_STATE = 6             /* call not valid in the current state */
+} tsd_status;
+
+typedef enum { TSD_ARCH_GPT2 = 0, TSD_ARCH_LLAMA = 1, TSD_ARCH_TALKER_CP = 2 } tsd_arch;
+typedef enum { TSD_W_Q4_0 = 0, TSD_W_Q8_0 = 1, TSD_W_AFFINE8_G64 = 2 } tsd_wfmt;
+
+/* Model shape.
+ *   GPT2 : GPT-2-Medium-shaped T3 ([J] §3.2): learned positions, pre-LayerNorm, fused QKV with
+ *          bias, GELU (tanh form) MLP with biases, untied head without bias.  Requires
+ *          n_head * head_dim == d_model and n_kv_head == n_head.
+ *   LLAMA: Llama-shaped T3 ([J] §3.19): RMSNorm, separate Q/K/V without bias, RoPE (NEOX
+ *          half-split, theta rope_theta, no frequency scaling), SwiGLU MLP, head without bias.
+ *   TALKER_CP: Talker + code predictor frame loop ([F] §1): LLAMA-shaped Talker of n_layer,
+ *          then a LLAMA-shaped predictor of cp_n_layer (same widths) running n_codebooks-1
+ *          sequential passes.  One step is one frame of n_codebooks codes.
+ * norm_eps is used by every LayerNorm/RMSNorm. */
+typedef struct {
+    int32_t arch, wfmt;
+    int32_t n_layer, d_model, n_head, n_kv_head, head_dim, d_ff, vocab, n_ctx, batch;
+    float norm_eps, rope_theta;
+    int32_t cp_n_layer, n_codebooks, cp_vocab; /* TALKER_CP only, else 0 */
+} tsd_config;
+
+/* Sampler ([J] §3.2: temperature then top-k, in that order).
+ * mode 0: greedy argmax, ties to the lowest index.
+ * mode 1: keep the top_k largest of logits/temperature (ties by lower index), softmax over
+ *         them, draw u in [0,1) as the top 24 bits of the first word of Philox4x64-10
+ *         (Salmon et al. 2011) with key (seed, 0) and counter (position, row, pass, 0), and
+ *         return the first index in descending order whose cumulative mass exceeds u * total.
+ *         top_k <= 0 or > vocab means the whole vocabulary. */
+typedef struct {
+    int32_t mode;
+    int32_t top_k;
+    float temperature;
+    uint64_t seed;
+} tsd_sampling;
+
+typedef struct {
+    const void* ptr; /* device pointer */
+    size_t bytes;
+} tsd_tensor;
+
+typedef struct tsd_model tsd_model;
+
+/* Bytes of device workspace a model of this shape needs (packed weights, KV cache,
+ * activations, step state).  The caller allocates it (256-byte aligned). */
+tsd_status tsd_workspace_bytes(const tsd_config* cfg, size_t* out_bytes);
+
+/* Create a model.  `weights` is the canonical list (all device pointers, fp32 for tables,
+ * norms and biases, the configured format for matrices):
+ *   GPT2 : wte[V][d], wpe[n_ctx][d], per layer {ln1_g[d], ln1_b[d], qkv_w[3d][d], qkv_b[3d],
+ *          o_w[d][d], o_b[d], ln2_g[d], ln2_b[d], fc_w[ff][d], fc_b[ff], down_w[d][ff],
+ *          down_b[d]}, lnf_g[d], lnf_b[d], head_w[V][d]            (2 + 12 L + 3 tensors)
+ *   LLAMA: emb[V][d], per layer {rms1_g[d], q_w[H hd][d], k_w[Hkv hd][d], v_w[Hkv hd][d],
+ *          o_w[d][H hd], rms2_g[d], gate_w[ff][d], up_w[ff][d], down_w[d][ff]}, rmsf_g[d],
+ *          head_w[V][d]                                                (1 + 9 L + 2 tensors)
+ *   TALKER_CP: E_0[V][d], E_c[cp_vocab][d] for c = 1..C-1, Talker layers as LLAMA, rmsf_g,
+ *          head_w[V][d], predictor layers as LLAMA, predictor rmsf_g, predictor heads
+ *          c = 1..C-1 [cp_vocab][d]
+ * The weights are repacked into the workspace on `stream`; the canonical buffers may be freed
+ * once that stream has been synchronised.  The workspace must outlive the model.  The step
+ * is captured once into a HIP graph here.  `sampling` may be NULL (greedy). */
+tsd_status tsd_model_create(const tsd_config* cfg, const tsd_tensor* weights, int n_weights,
+                            void* d_workspace, size_t workspace_bytes, void* stream,
+                            const tsd_sampling* sampling, tsd_model** out);
+
+/* Prefill: the decode step run at every prompt position, so that prefill and decode agree
+ * exactly ([J] §3.2 prompt/step split over one persistent KV cache).  d_tokens is
+ * [batch][n][tokens per position] (1, or n_codebooks for TALKER_CP); d_next (may be NULL)
+ * receives [batch][tokens per step], the ids sampled after the last prompt position.
+ * TSD_ERR_CONTEXT_FULL if n_past + n > n_ctx.  Tokens are not range-checked on the device:
+ * an id outside its vocabulary is clamped into range. */
+tsd_status tsd_prefill(tsd_model* m, const int32_t* d_tokens, int n, int32_t* d_next);
+
+/* One decode step (one frame for TALKER_CP) at position n_past: replays the captured graph.
+ * d_in is [batch][tokens per position] or NULL for "the ids sampled by the previous step";
+ * d_next may be NULL.  The sampled ids are also appended to the device token history
+ * (tsd_get_tokens).  n_past increases by one. */
+tsd_status tsd_step(tsd_model* m, const int32_t* d_in, int32_t* d_next);
+
+tsd_status tsd_reset(tsd_model* m);                     /* n_past = 0, history cleared */
+tsd_status tsd_truncate(tsd_model* m, int n_past);      /* keep the first n_past positions */
+tsd_status tsd_n_past(const tsd_model* m, int* out);
+tsd_status tsd_model_destroy(tsd_model* m);
+/* Message of the last error on m (NULL: of the last failed tsd_model_create or standalone
+ * call on this thread). */
+const char* tsd_last_error(const tsd_model* m);
+
+/* Logits of the last step: [batch][vocab] fp32; for TALKER_CP [batch][n_codebooks][vmax]
+ * with vmax = max(vocab, cp_vocab) (entries past a head's vocabulary are 0). */
+tsd_status tsd_get_logits(tsd_model* m, float* d_out);
+/* Ids sampled at positions [first, first + n): [n][batch][tokens per step] int32. */
+tsd_status tsd_get_tokens(tsd_model* m, int first, int n, int32_t* d_out);
+
+/* Replace the (Talker) KV cache by d_k/d_v given as [n_layer][batch][n_kv_head][n_pos]
+ * [head_dim] fp16 and set n_past = n_pos (used to start from a given context). */
+tsd_status tsd_load_kv(tsd_model* m, const uint16_t* d_k, const uint16_t* d_v, int n_pos);
+
+/* One main decoder layer on hidden states d_x [batch][d_model] at position pos: writes that
+ * layer's K/V at pos, attends to positions 0..pos, writes the residual stream after the
+ * layer to d_out [batch][d_model].  n_past is not changed.  Uses the same kernels as the
+ * step. */
+tsd_status tsd_layer_forward(tsd_model* m, int layer, const float* d_x, int pos, float* d_out);
+
+/* ---- standalone operators (same kernels as the step) ------------------------------------- */
+
+/* Bytes of the kernel layout of one W[N][K] matrix (tsd_gemv_pack's output). */
+tsd_status tsd_gemv_packed_bytes(int wfmt, int N, int K, size_t* out_bytes);
+/* Repack a canonical matrix d_w into the kernel layout d_packed (device to device). */
+tsd_status tsd_gemv_pack(int wfmt, const void* d_w, size_t w_bytes, int N, int K, void* d_packed,
+                         size_t packed_bytes, void* stream);
+/* Fused block-dequant GEMV on the packed layout: d_y[b][n] = sum_k W[n][k] d_x[b][k]
+ * (+ d_bias[n] if not NULL) for b < B (1 <= B <= 4), fp32 accumulation
+ * ([J] §3.15 mat-vec with the bias added in the same kernel). */
+tsd_status tsd_gemv(int wfmt, const void* d_packed, int N, int K, int B, const float* d_x,
+                    const float* d_bias, float* d_y, void* stream);
+
+/* Split-KV flash-decode attention of one query per head over an fp16 cache
+ * ([J] §3.13: cache laid out head-dim fastest, then position, then head; no mask for a single
+ * new token): d_q [B][H][hd] fp32, d_k/d_v [B][Hkv][n_ctx][hd] fp16, attends keys
+ * 0..n_keys-1, d_out [B][H][hd] = softmax(q K^T / sqrt(hd)) V.  Query head h reads KV head
+ * h / (H / Hkv).  hd must be 64 or 128.  d_scratch holds the split partials
+ * (tsd_attention_scratch_bytes). */
+tsd_status tsd_attention_scratch_bytes(int B, int H, int n_ctx, int hd, size_t* out_bytes);
+tsd_status tsd_attention(const float* d_q, const uint16_t* d_k, const uint16_t* d_v, int B, int H,
+                         int Hkv, int hd, int n_keys, int n_ctx, float* d_out, void* d_scratch,
+                         size_t scratch_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,542 @@
+// gemv.hip — fused block-dequant GEMV for batch-1 decode on gfx950.
+//
+// What it computes ("Chatterbox -> ggml Port: Development Journal", §3.15/§3.16: the quantized
+// mat-vec with its bias, and then its residual, added in the same kernel; §3.14/§3.23: one fused
+// Q/K/V matrix whose output rows are Q, K, V; §3.21: SwiGLU as one fused op):
+//     y = epilogue( W . prologue(x) )
+// with W in Q4_0 / Q8_0 / affine-8 blocks, fp32 accumulation.
+//
+// Mapping onto CDNA4:
+//   * a workgroup is 4 wave64s; every lane owns one 16-byte slot of a row (one dwordx4 load:
+//     32 Q4_0 weights or 16 Q8_0 / affine weights) and keeps the matching slice of x in VGPRs,
+//     so x is read from LDS once per lane, never per weight;
+//   * a wave covers 64/slots-per-row rows per load when a row is shorter than the wave, or one
+//     row per ceil(slots/64) loads when it is longer;
+//   * order of issue: the input-vector loads first, then every weight and scale load of the
+//     lane (unconditional, clamped addresses), and only then the wait for the input.  Vector
+//     memory counters retire in order, so this is the order that lets the weight stream stay
+//     in flight while the norm prologue (LayerNorm / RMSNorm, or the first layer's embedding
+//     gather) runs; the prologue is recomputed by every workgroup from the 4 KB input, which
+//     costs no extra launch;
+//   * per-row partials are reduced with DPP row moves and cross-row swaps, no LDS traffic;
+//   * the block scale multiplies the integer-weighted sum once per slot; the Q4_0 "-8" and the
+//     Q8_0 "+128" storage offset are applied through the slot's precomputed sum of x.
+#include <math.h>
+
+#include "kernels.h"
+
+namespace tsd {
+namespace {
+
+constexpr int WG = 256;
+constexpr int NWAVE = WG / 64;
+constexpr int MAX_K = 4096;
+constexpr int NJ = MAX_K / 4 / WG;   // float4 of the input per thread
+
+// byte i of v as float (v_cvt_f32_ubyteN), written out because the compiler otherwise folds the
+// nibble masks into bit-field extracts and loses the one-instruction form
+template <int I>
+__device__ __forceinline__ float ubyte(uint32_t v)
+{
+    float r;
+    if constexpr (I == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(v));
+    else if constexpr (I == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(v));
+    else if constexpr (I == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(v));
+    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+
+template <int F>
+__device__ __forceinline__ float slot_dot(const uint4 w, const float* __restrict__ x)
+{
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    if constexpr (F == FMT_Q4_0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t lo = ws[j] & 0x0F0F0F0Fu, hi = (ws[j] >> 4) & 0x0F0F0F0Fu;
+            float& al = (j & 1) ? a1 : a0;
+            float& ah = (j & 1) ? a3 : a2;
+            al = fmaf(ubyte<0>(lo), x[4 * j + 0], al);
+            ah = fmaf(ubyte<0>(hi), x[16 + 4 * j + 0], ah);
+            al = fmaf(ubyte<1>(lo), x[4 * j + 1], al);
+            ah = fmaf(ubyte<1>(hi), x[16 + 4 * j + 1], ah);
+            al = fmaf(ubyte<2>(lo), x[4 * j + 2], al);
+            ah = fmaf(ubyte<2>(hi), x[16 + 4 * j + 2], ah);
+            al = fmaf(ubyte<3>(lo), x[4 * j + 3], al);
+            ah = fmaf(ubyte<3>(hi), x[16 + 4 * j + 3], ah);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float& a = j == 0 ? a0 : j == 1 ? a1 : j == 2 ? a2 : a3;
+            a = fmaf(ubyte<0>(ws[j]), x[4 * j + 0], a);
+            a = fmaf(ubyte<1>(ws[j]), x[4 * j + 1], a);
+            a = fmaf(ubyte<2>(ws[j]), x[4 * j + 2], a);
+            a = fmaf(ubyte<3>(ws[j]), x[4 * j + 3], a);
+        }
+    }
+    return (a0 + a1) + (a2 + a3);
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red)
+{
+    v = wave_sum(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    lds_barrier();
+    float r = 0.f;
+#pragma unroll
+    for (int i = 0; i < NWAVE; ++i) r += red[i];
+    lds_barrier();
+    return r;
+}
+
+__device__ __forceinline__ float4 f4add(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
+
+// x -> LDS, swizzled so that the lane owning slot s reads float4 e4 of its slice at
+// index e4 * slots_per_row + s (consecutive lanes, consecutive addresses)
+template <int E>
+__device__ __forceinline__ int swz(int k, int lpr) { return ((k % E) >> 2) * lpr + k / E; }
+
+// phase 1 of the prologue: issue the input loads (the embedding rows for the first layer) and
+// the norm's gain/bias
+template <int PRO>
+__device__ __forceinline__ void load_x(const ProArgs& p, const int K, float4 (&v)[NJ], float4 (&g)[NJ],
+                                       float4 (&bt)[NJ])
+{
+    constexpr bool EMB = PRO == PRO_LN_EMB || PRO == PRO_RMS_EMB;
+    constexpr bool LN = PRO == PRO_LN || PRO == PRO_LN_EMB;
+    const int nch = K / 4, t = threadIdx.x;
+    if constexpr (PRO != PRO_LOAD) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int c = t + j * WG;
+            g[j] = c < nch ? ((const float4*)p.g)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+            if constexpr (LN) bt[j] = c < nch ? ((const float4*)p.beta)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+    if constexpr (EMB) {
+        const int prow = p.pos_tab ? ld_uniform(p.pos) : 0;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int c = t + j * WG;
+            float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (c < nch) {
+                for (int i = 0; i < p.n_emb; ++i) {
+                    int tk = ld_uniform(p.tok + i);
+                    tk = tk < 0 ? 0 : (tk >= p.tab_rows[i] ? p.tab_rows[i] - 1 : tk);
+                    a = f4add(a, ((const float4*)(p.tab[i] + (size_t)tk * K))[c]);
+                }
+                if (p.pos_tab) a = f4add(a, ((const float4*)(p.pos_tab + (size_t)prow * K))[c]);
+            }
+            v[j] = a;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int c = t + j * WG;
+            v[j] = c < nch ? ((const float4*)p.src)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+}
+
+// phase 2: norm (if any) and the swizzled store into LDS
+template <int F, int PRO>
+__device__ __forceinline__ void finish_x(const ProArgs& p, const int K, float4 (&v)[NJ], const float4 (&gg)[NJ],
+                                         const float4 (&bt)[NJ], float4* xl4, float* red)
+{
+    constexpr int E = FmtT<F>::E;
+    constexpr bool EMB = PRO == PRO_LN_EMB || PRO == PRO_RMS_EMB;
+    constexpr bool LN = PRO == PRO_LN || PRO == PRO_LN_EMB;
+    const int lpr = K / E, nch = K / 4, t = threadIdx.x;
+    if (EMB && blockIdx.x == 0) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            if (t + j * WG < nch) ((float4*)p.x_out)[t + j * WG] = v[j];
+    }
+    if constexpr (PRO == PRO_LOAD) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int c = t + j * WG;
+            if (c < nch) xl4[swz<E>(4 * c, lpr)] = v[j];
+        }
+    } else {
+        const float invK = 1.0f / (float)K;
+        float mean = 0.f;
+        if constexpr (LN) {
+            float s = 0.f;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+            mean = block_sum(s, red) * invK;
+        }
+        float q2 = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            if (t + j * WG < nch) {
+                const float dx = v[j].x - mean, dy = v[j].y - mean, dz = v[j].z - mean, dw = v[j].w - mean;
+                q2 += (dx * dx + dy * dy) + (dz * dz + dw * dw);
+            }
+        }
+        const float r = 1.0f / sqrtf(block_sum(q2, red) * invK + p.eps);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int c = t + j * WG;
+            if (c < nch) {
+                const float4 g = gg[j];
+                float4 y = make_float4((v[j].x - mean) * r * g.x, (v[j].y - mean) * r * g.y,
+                                       (v[j].z - mean) * r * g.z, (v[j].w - mean) * r * g.w);
+                if constexpr (LN) y = f4add(y, bt[j]);
+                xl4[swz<E>(4 * c, lpr)] = y;
+            }
+        }
+    }
+    lds_barrier();
+}
+
+__device__ __forceinline__ float gelu_tanh(float x)
+{
+    // tanh form of GELU (Hendrycks & Gimpel): 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
+    const float c = 0.7978845608028654f;
+    return 0.5f * x * (1.0f + tanhf(c * fmaf(0.044715f * x, x * x, x)));
+}
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+
+template <int EPI>
+__device__ __forceinline__ void epi_single(const EpiArgs& e, int row, float t, int pos)
+{
+    if (e.bias) t += e.bias[row];
+    if constexpr (EPI == EPI_STORE || EPI == EPI_HEAD_ARGMAX) {
+        e.y[row] = t;
+    } else if constexpr (EPI == EPI_RESID) {
+        e.y[row] += t;
+    } else if constexpr (EPI == EPI_GELU) {
+        e.y[row] = gelu_tanh(t);
+    } else if constexpr (EPI == EPI_QKV) {
+        if (row < e.qrows) {
+            e.q[row] = t;
+        } else {
+            const bool isk = row < e.qrows + e.krows;
+            const int r = isk ? row - e.qrows : row - e.qrows - e.krows;
+            const int h = r / e.hd, i = r - h * e.hd;
+            __half* c = isk ? e.kc : e.vc;
+            c[((size_t)h * e.n_ctx + pos) * e.hd + i] = __float2half_rn(t);
+        }
+    }
+}
+
+// rows (row, row+1), row even
+template <int EPI>
+__device__ __forceinline__ void epi_pair(const EpiArgs& e, int row, float t0, float t1, int pos)
+{
+    if constexpr (EPI == EPI_SWIGLU) {
+        e.y[row >> 1] = silu(t0) * t1;
+    } else if constexpr (EPI == EPI_QKV_ROPE) {
+        const int half = e.hd >> 1;
+        if (row < e.qrows + e.krows) {
+            const bool isk = row >= e.qrows;
+            const int m = (isk ? row - e.qrows : row) >> 1;   // pair index within Q or K
+            const int h = m / half, i = m - h * half;
+            const float2 cs = e.rope[(size_t)pos * half + i];
+            const float a = t0 * cs.x - t1 * cs.y, bb = t0 * cs.y + t1 * cs.x;
+            if (!isk) {
+                e.q[h * e.hd + i] = a;
+                e.q[h * e.hd + i + half] = bb;
+            } else {
+                __half* c = e.kc + ((size_t)h * e.n_ctx + pos) * e.hd;
+                c[i] = __float2half_rn(a);
+                c[i + half] = __float2half_rn(bb);
+            }
+        } else {
+            const int r = row - e.qrows - e.krows;
+            const int h = r / e.hd, i = r - h * e.hd;
+            __half* c = e.vc + ((size_t)h * e.n_ctx + pos) * e.hd;
+            c[i] = __float2half_rn(t0);
+            c[i + 1] = __float2half_rn(t1);
+        }
+    }
+}
+
+template <int EPI> struct EpiIsPair { static constexpr bool v = EPI == EPI_SWIGLU || EPI == EPI_QKV_ROPE; };
+
+template <int F, int SPL, int NLOAD, int PRO, int EPI>
+__global__ __launch_bounds__(WG) void k_gemv(const PackedMat W, const ProArgs pa, const EpiArgs ea)
+{
+    constexpr int E = FmtT<F>::E, SPS = FmtT<F>::SLOTS_PER_SCALE, G = FmtT<F>::SCALE_GROUP;
+    constexpr int RWS = SPL == 1 ? 1 : NLOAD / SPL;       // rows per wave when rows span loads
+    constexpr int NP = SPL == 1 ? NLOAD : RWS;             // partial sums per lane
+    constexpr bool PAIR = EpiIsPair<EPI>::v;
+    static_assert(SPL == 1 || NLOAD % SPL == 0, "whole rows per wave");
+    static_assert(!PAIR || NP % 2 == 0, "pair epilogues need an even number of rows per lane");
+
+    __shared__ float4 xl4[MAX_K / 4];
+    __shared__ float red[NWAVE];
+    __shared__ unsigned long long bkey[NWAVE];
+
+    const int K = W.K, N = W.N, lpr = K / E;
+    const size_t rb = F == FMT_Q4_0 ? (size_t)K / 2 : (size_t)K;
+    const int spr = K / G;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int slot0 = SPL == 1 ? (lane & (lpr - 1)) : lane;
+    const int sub = SPL == 1 ? lane / lpr : 0;
+    const int rpw = SPL == 1 ? NLOAD * (64 / lpr) : RWS;
+    const int row0 = (blockIdx.x * NWAVE + wave) * rpw;
+
+    // 1. the input vector's loads first ...
+    float4 xv[NJ], xg[NJ], xb[NJ];
+    load_x<PRO>(pa, K, xv, xg, xb);
+
+    // 2. ... then every weight and raw scale of this lane, unconditionally (clamped address;
+    //    out-of-range slots get a zero scale)
+    uint4 w[NLOAD];
+    unsigned short sc_raw[NLOAD], sb_raw[NLOAD];
+    bool ok[NLOAD];
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i) {
+        const int row = SPL == 1 ? row0 + sub * NLOAD + i : row0 + i / SPL;
+        const int slot = SPL == 1 ? slot0 : (i % SPL) * 64 + lane;
+        ok[i] = row < N && slot < lpr;
+        const int rr = row < N ? row : N - 1, ss = slot < lpr ? slot : lpr - 1;
+        w[i] = *(const uint4*)(W.q + (size_t)rr * rb + (size_t)ss * 16);
+        sc_raw[i] = __half_as_ushort(W.s[(size_t)rr * spr + ss / SPS]);
+        if constexpr (F == FMT_AFF8) sb_raw[i] = __half_as_ushort(W.b[(size_t)rr * spr + ss / SPS]);
+    }
+
+    // 3. norm / embedding into LDS (waits for the input only)
+    finish_x<F, PRO>(pa, K, xv, xg, xb, xl4, red);
+
+    // 4. this lane's x slices and their sums
+    float xs[SPL][E];
+    float sx[SPL];
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+        const int slot = SPL == 1 ? slot0 : j * 64 + lane;
+        float s = 0.f;
+#pragma unroll
+        for (int e4 = 0; e4 < E / 4; ++e4) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (slot < lpr) v = xl4[e4 * lpr + slot];
+            xs[j][4 * e4 + 0] = v.x;
+            xs[j][4 * e4 + 1] = v.y;
+            xs[j][4 * e4 + 2] = v.z;
+            xs[j][4 * e4 + 3] = v.w;
+            s += (v.x + v.y) + (v.z + v.w);
+        }
+        sx[j] = s;
+    }
+
+    // 5. dequantize-and-dot
+    float part[NP];
+#pragma unroll
+    for (int r = 0; r < NP; ++r) part[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i) {
+        const int j = SPL == 1 ? 0 : i % SPL;
+        const int r = SPL == 1 ? i : i / SPL;
+        const float d = slot_dot<F>(w[i], xs[j]);
+        const float sc = ok[i] ? __half2float(__ushort_as_half(sc_raw[i])) : 0.f;
+        float v;
+        if constexpr (F == FMT_Q4_0) v = sc * fmaf(-8.f, sx[j], d);
+        else if constexpr (F == FMT_Q8_0) v = sc * fmaf(-128.f, sx[j], d);
+        else {
+            const float sb = ok[i] ? __half2float(__ushort_as_half(sb_raw[i])) : 0.f;
+            v = fmaf(sc, d, sb * sx[j]);
+        }
+        part[r] += v;
+    }
+
+    // 6. reduce over the lanes sharing a row
+#pragma unroll
+    for (int r = 0; r < NP; ++r) part[r] = group_sum(part[r], SPL == 1 ? lpr : 64);
+
+    // 7. epilogue, one lane per row group
+    const bool leader = SPL == 1 ? slot0 == 0 : lane == 0;
+    const int pos = (EPI == EPI_QKV || EPI == EPI_QKV_ROPE) ? ld_uniform(ea.pos) : 0;
+    unsigned long long best = 0ull;
+    if (leader) {
+#pragma unroll
+        for (int r = 0; r < NP; ++r) {
+            const int row = SPL == 1 ? row0 + sub * NLOAD + r : row0 + r;
+            if constexpr (PAIR) {
+                if ((r & 1) == 0 && row < N) epi_pair<EPI>(ea, row, part[r], part[r + 1], pos);
+            } else {
+                if (row < N) {
+                    epi_single<EPI>(ea, row, part[r], pos);
+                    if constexpr (EPI == EPI_HEAD_ARGMAX) {
+                        const unsigned long long key =
+                            ((unsigned long long)float_order_key(part[r]) << 32) | (0xFFFFFFFFu - (uint32_t)row);
+                        best = key > best ? key : best;
+                    }
+                }
+            }
+        }
+    }
+    if constexpr (EPI == EPI_HEAD_ARGMAX) {
+        // greedy sampler fused into the head: workgroup max, one atomic per workgroup, and the
+        // last workgroup to finish publishes the id, appends it to the history and advances
+        // the position.  Key = (ordered logit, ~index): ties go to the lowest index.
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            const unsigned long long other = __shfl_xor(best, o, 64);
+            best = other > best ? other : best;
+        }
+        if (lane == 0) bkey[wave] = best;
+        lds_barrier();
+        if (threadIdx.x == 0) {
+            unsigned long long m = bkey[0];
+#pragma unroll
+            for (int i = 1; i < NWAVE; ++i) m = bkey[i] > m ? bkey[i] : m;
+            atomicMax(ea.best, m);
+            __threadfence();
+            const unsigned int t = atomicAdd(ea.ticket, 1u);
+            if (t == gridDim.x - 1) {
+                __threadfence();
+                const unsigned long long fin = atomicExch(ea.best, 0ull);
+                const int id = (int)(0xFFFFFFFFu - (uint32_t)(fin & 0xFFFFFFFFull));
+                const int p = *ea.pos_inc;
+                *ea.tok_out = id;
+                if (ea.hist) ea.hist[(size_t)p * ea.hist_stride] = id;
+                atomicExch(ea.ticket, 0u);
+                *ea.pos_inc = p + 1;
+            }
+        }
+    }
+}
+
+// ---- host dispatch ---------------------------------------------------------------------------
+
+int spl_for(int fmt, int K)
+{
+    const int lpr = K / fmt_elems_per_slot(fmt);
+    return lpr <= 64 ? 1 : (lpr + 63) / 64;
+}
+
+template <int SPL> constexpr int nload_for() { return SPL == 1 ? 2 : 2 * SPL; }
+
+int rows_per_block_impl(int fmt, int K)
+{
+    const int spl = spl_for(fmt, K);
+    const int lpr = K / fmt_elems_per_slot(fmt);
+    const int rpw = spl == 1 ? 2 * (64 / lpr) : 2;
+    return NWAVE * rpw;
+}
+
+template <int F, int PRO, int EPI, int SPL>
+hipError_t go(const PackedMat& W, const ProArgs& pa, const EpiArgs& ea, hipStream_t st)
+{
+    constexpr int NLOAD = nload_for<SPL>();
+    const int rpb = rows_per_block_impl(F, W.K);
+    const int grid = (W.N + rpb - 1) / rpb;
+    hipLaunchKernelGGL((k_gemv<F, SPL, NLOAD, PRO, EPI>), dim3(grid), dim3(WG), 0, st, W, pa, ea);
+    return hipGetLastError();
+}
+
+template <int F, int PRO, int EPI>
+hipError_t go_spl(const PackedMat& W, const ProArgs& pa, const EpiArgs& ea, hipStream_t st)
+{
+    switch (spl_for(F, W.K)) {
+    case 1: return go<F, PRO, EPI, 1>(W, pa, ea, st);
+    case 2: return go<F, PRO, EPI, 2>(W, pa, ea, st);
+    case 3: return go<F, PRO, EPI, 3>(W, pa, ea, st);
+    case 4: return go<F, PRO, EPI, 4>(W, pa, ea, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int F>
+hipError_t go_fmt(int pro, int epi, const PackedMat& W, const ProArgs& pa, const EpiArgs& ea, hipStream_t st)
+{
+#define TSD_CASE(PRO_, EPI_) \
+    if (pro == PRO_ && epi == EPI_) return go_spl<F, PRO_, EPI_>(W, pa, ea, st);
+    TSD_CASE(PRO_LOAD, EPI_STORE)
+    TSD_CASE(PRO_LOAD, EPI_RESID)
+    TSD_CASE(PRO_LN, EPI_GELU)
+    TSD_CASE(PRO_RMS, EPI_SWIGLU)
+    TSD_CASE(PRO_LN, EPI_QKV)
+    TSD_CASE(PRO_RMS, EPI_QKV_ROPE)
+    TSD_CASE(PRO_LN_EMB, EPI_QKV)
+    TSD_CASE(PRO_RMS_EMB, EPI_QKV_ROPE)
+    TSD_CASE(PRO_LN, EPI_HEAD_ARGMAX)
+    TSD_CASE(PRO_RMS, EPI_HEAD_ARGMAX)
+    TSD_CASE(PRO_LN, EPI_STORE)
+    TSD_CASE(PRO_RMS, EPI_STORE)
+#undef TSD_CASE
+    return hipErrorInvalidValue;
+}
+
+// ---- repack canonical blocks into the kernel layout ----------------------------------------
+// one thread per (source row, scale group); `mode` places source row r at destination row
+//   IDENTITY: row0 + r
+//   ROPE_PAIRS: within each head of hd rows, element i < hd/2 -> 2i, i >= hd/2 -> 2(i-hd/2)+1
+//   INTERLEAVE_EVEN / _ODD: row0 + 2r (+1)
+__device__ __forceinline__ int place_row(int r, int mode, int hd, int row0)
+{
+    if (mode == PACK_ROPE_PAIRS) {
+        const int h = r / hd, i = r - h * hd, half = hd / 2;
+        return row0 + h * hd + (i < half ? 2 * i : 2 * (i - half) + 1);
+    }
+    if (mode == PACK_INTERLEAVE_EVEN) return row0 + 2 * r;
+    if (mode == PACK_INTERLEAVE_ODD) return row0 + 2 * r + 1;
+    return row0 + r;
+}
+
+__global__ void k_pack(int fmt, const uint8_t* __restrict__ src, int N, int K, uint8_t* dq, __half* ds,
+                       __half* db, int mode, int hd, int row0)
+{
+    const int G = fmt_group(fmt), gpr = K / G;
+    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (long long)N * gpr) return;
+    const int r = (int)(idx / gpr), g = (int)(idx - (long long)r * gpr);
+    const int dr = place_row(r, mode, hd, row0);
+    if (fmt == FMT_Q4_0) {
+        const uint8_t* blk = src + ((size_t)r * gpr + g) * 18;
+        uint8_t* o = dq + (size_t)dr * (K / 2) + (size_t)g * 16;
+        for (int j = 0; j < 16; ++j) o[j] = blk[2 + j];
+        ds[(size_t)dr * gpr + g] = __ushort_as_half((unsigned short)(blk[0] | (blk[1] << 8)));
+    } else if (fmt == FMT_Q8_0) {
+        const uint8_t* blk = src + ((size_t)r * gpr + g) * 34;
+        uint8_t* o = dq + (size_t)dr * K + (size_t)g * 32;
+        for (int j = 0; j < 32; ++j) o[j] = (uint8_t)(blk[2 + j] ^ 0x80u);   // int8 q -> q + 128
+        ds[(size_t)dr * gpr + g] = __ushort_as_half((unsigned short)(blk[0] | (blk[1] << 8)));
+    } else {
+        const uint8_t* q = src + (size_t)r * K + (size_t)g * 64;
+        const uint8_t* s = src + (size_t)N * K + ((size_t)r * gpr + g) * 2;
+        const uint8_t* b = src + (size_t)N * K + (size_t)N * gpr * 2 + ((size_t)r * gpr + g) * 2;
+        uint8_t* o = dq + (size_t)dr * K + (size_t)g * 64;
+        for (int j = 0; j < 64; ++j) o[j] = q[j];
+        ds[(size_t)dr * gpr + g] = __ushort_as_half((unsigned short)(s[0] | (s[1] << 8)));
+        db[(size_t)dr * gpr + g] = __ushort_as_half((unsigned short)(b[0] | (b[1] << 8)));
+    }
+}
+
+}  // namespace
+
+int gemv_rows_per_block(int fmt, int K, int) { return rows_per_block_impl(fmt, K); }
+
+hipError_t launch_gemv(int fmt, int pro, int epi, const PackedMat& W, const ProArgs& pa, const EpiArgs& ea,
+                       hipStream_t st)
+{
+    if (W.K > MAX_K || !gemv_shape_ok(fmt, W.K) || W.N <= 0) return hipErrorInvalidValue;
+    switch (fmt) {
+    case FMT_Q4_0: return go_fmt<FMT_Q4_0>(pro, epi, W, pa, ea, st);
+    case FMT_Q8_0: return go_fmt<FMT_Q8_0>(pro, epi, W, pa, ea, st);
+    case FMT_AFF8: return go_fmt<FMT_AFF8>(pro, epi, W, pa, ea, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_pack(int fmt, const void* src, int N, int K, void* dst_base, int dst_N, int dst_row0, int mode,
+                       int hd, hipStream_t st)
+{
+    PackedLayout L = packed_layout(fmt, dst_N, K);
+    uint8_t* base = (uint8_t*)dst_base;
+    const long long n = (long long)N * (K / fmt_group(fmt));
+    const int threads = 256;
+    const long long blocks = (n + threads - 1) / threads;
+    hipLaunchKernelGGL(k_pack, dim3((unsigned)blocks), dim3(threads), 0, st, fmt, (const uint8_t*)src, N, K,
+                       base + L.q_off, (__half*)(base + L.s_off), fmt == FMT_AFF8 ? (__half*)(base + L.b_off) : nullptr,
+                       mode, hd, dst_row0);
+    return hipGetLastError();
+}
+
+}  // namespace tsd

@@ -1,0 +1,98 @@
+// kernels.h — host-side launchers of the libtsd kernels (internal).
+#pragma once
+
+#include "common.h"
+
+namespace tsd {
+
+// ---- GEMV ------------------------------------------------------------------------------------
+// Prologue: how each workgroup builds its copy of the input vector x (into LDS).
+// PRO_*_EMB: the input is the embedding gather of the first layer instead of src
+enum ProKind : int { PRO_LOAD = 0, PRO_LN = 1, PRO_RMS = 2, PRO_LN_EMB = 3, PRO_RMS_EMB = 4 };
+
+struct ProArgs {
+    const float* src;   // [NB][ld_src] input (ignored when n_emb > 0)
+    int ld_src;
+    const float* g;     // norm gain (LN / RMS)
+    const float* beta;  // LayerNorm bias
+    float eps;
+    // embedding instead of src (one row): x0 = sum_c tab[c][tok[c]] (+ pos_tab[*pos]);
+    // workgroup 0 stores x0 to x_out (the residual stream)
+    int n_emb;
+    const float* tab[16];
+    int tab_rows[16];
+    const int* tok;
+    const float* pos_tab;
+    const int* pos;
+    float* x_out;
+};
+
+enum EpiKind : int {
+    EPI_STORE = 0,     // y[b][n] = acc + bias
+    EPI_RESID = 1,     // y[n] += acc + bias            (residual add into the stream)
+    EPI_GELU = 2,      // y[n] = gelu_tanh(acc + bias)
+    EPI_SWIGLU = 3,    // rows (2i, 2i+1) = (gate_i, up_i): y[i] = silu(gate) * up
+    EPI_QKV = 4,       // rows [0,qr) -> q, [qr, qr+kr) -> K cache, rest -> V cache (+bias)
+    EPI_QKV_ROPE = 5,  // as EPI_QKV, q/k rows stored in RoPE pairs (i, i+hd/2) and rotated
+    EPI_HEAD_ARGMAX = 6  // logits + greedy argmax, last workgroup publishes the id
+};
+
+struct EpiArgs {
+    float* y;
+    int ldy;
+    const float* bias;
+    // QKV
+    int qrows, krows, hd, n_ctx;
+    float* q;
+    __half* kc;
+    __half* vc;
+    const float2* rope;  // [n_ctx][hd/2] (cos, sin)
+    const int* pos;      // device position (K/V slot, RoPE angle)
+    // head / argmax
+    unsigned long long* best;
+    unsigned int* ticket;
+    int* tok_out;        // current-token slot (next step's input)
+    int* hist;           // history [n_ctx][hist_stride]
+    int hist_stride;
+    int* pos_inc;        // incremented by the last workgroup (end of step)
+};
+
+// Launch the fused GEMV y = epilogue(W . prologue(x)).  Returns hipSuccess or the launch error.
+hipError_t launch_gemv(int fmt, int pro, int epi, const PackedMat& W, const ProArgs& pa, const EpiArgs& ea,
+                       hipStream_t st);
+// the tile (rows per workgroup) the launcher uses for a shape; for byte/launch accounting
+int gemv_rows_per_block(int fmt, int K, int epi);
+
+hipError_t launch_pack(int fmt, const void* src, int N, int K, void* dst_base, int dst_N,
+                       int dst_row0, int mode, int hd, hipStream_t st);
+// row placement modes for launch_pack
+enum PackMode : int { PACK_IDENTITY = 0, PACK_ROPE_PAIRS = 1, PACK_INTERLEAVE_EVEN = 2, PACK_INTERLEAVE_ODD = 3 };
+
+// ---- attention -------------------------------------------------------------------------------
+struct AttnArgs {
+    const float* q;      // [B][ldq] with the H query heads at q + b*ldq
+    int ldq;
+    const __half* k;     // [B][Hkv][n_ctx][hd]
+    const __half* v;
+    float* out;          // [B][ldo] with head h at out + b*ldo + h*hd
+    int ldo;
+    float* part;         // [B][H][max_split][hd + 2]
+    unsigned int* cnt;   // [B][H], zero between launches
+    int B, H, Hkv, hd, n_ctx;
+    const int* pos;      // n_keys = *pos + 1 + pos_add when pos != null
+    int pos_add;
+    int n_keys;          // used when pos == null
+};
+int attn_max_split(int n_ctx);
+size_t attn_part_bytes(int B, int H, int n_ctx, int hd);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+
+// ---- small state kernels ---------------------------------------------------------------------
+hipError_t launch_copy_i32(int* dst, const int* src, int n, hipStream_t st);
+hipError_t launch_fill_i32(int* dst, int value, int n, hipStream_t st);
+hipError_t launch_fill_u32(unsigned int* dst, unsigned int value, int n, hipStream_t st);
+hipError_t launch_fill_u64(unsigned long long* dst, unsigned long long value, int n, hipStream_t st);
+hipError_t launch_fill_f32(float* dst, float value, size_t n, hipStream_t st);
+hipError_t launch_copy_bytes(void* dst, const void* src, size_t n, hipStream_t st);
+
+}  // namespace tsd

@@ -1,0 +1,697 @@
+// model.hip — the decode-step executor behind the C ABI (include/tsd.h).
+//
+// At creation: validate the shape, plan the caller's workspace, repack every canonical weight
+// into the kernel layout (fusing Q/K/V rows, pairing RoPE rows, interleaving gate/up rows),
+// then record the whole step — every layer's kernels, the head and the sampler — into one HIP
+// graph.  A step is then a single graph launch: the position, the input token and the sampled
+// id live in device memory and are advanced by the graph itself, so one instantiated graph
+// replays every step with no host work beyond the launch ("Chatterbox -> ggml Port:
+// Development Journal", §3.8 graph reuse and §3.22 no per-step allocator work; "Every Frame Is
+// a Memory Read", §5.2: the random state and the sampled ids stay inside the compiled graph).
+#include <math.h>
+
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "tsd.h"
+
+using namespace tsd;
+
+namespace {
+
+thread_local std::string g_err;
+
+struct LayerW {
+    PackedMat qkv, o, fc, down;            // fc = fc (GPT-2) or interleaved gate/up (Llama)
+    float *n1g = nullptr, *n1b = nullptr, *n2g = nullptr, *n2b = nullptr;
+    float *bqkv = nullptr, *bo = nullptr, *bfc = nullptr, *bdown = nullptr;
+};
+
+// bump planner over the workspace: the same walk sizes it and lays it out
+struct Planner {
+    uint8_t* base;
+    size_t off = 0;
+    explicit Planner(uint8_t* b) : base(b) {}
+    void* take(size_t bytes)
+    {
+        off = align256(off);
+        void* p = base ? base + off : nullptr;
+        off += bytes;
+        return p;
+    }
+};
+
+}  // namespace
+
+struct tsd_model {
+    tsd_config c{};
+    tsd_sampling samp{};
+    hipStream_t st = nullptr;
+    uint8_t* ws = nullptr;
+    size_t ws_bytes = 0;
+    int tpp = 1;          // tokens per position
+    int vmax = 0;
+    int qkv_rows = 0;
+    std::vector<LayerW> L;
+    const float* emb[16] = {};
+    int emb_rows[16] = {};
+    const float* wpe = nullptr;
+    float *nfg = nullptr, *nfb = nullptr;
+    PackedMat head{};
+    __half *kc = nullptr, *vc = nullptr;
+    size_t kv_layer_elems = 0;
+    float *x = nullptr, *qkv = nullptr, *attn = nullptr, *h = nullptr, *logits = nullptr, *part = nullptr;
+    float2* rope = nullptr;
+    unsigned int *acnt = nullptr, *ticket = nullptr;
+    unsigned long long* best = nullptr;
+    int *pos = nullptr, *tok = nullptr, *hist = nullptr, *dbg_pos = nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    int n_past = 0;
+    std::string err;
+};
+
+namespace {
+
+tsd_status fail(tsd_model* m, tsd_status s, const std::string& msg)
+{
+    if (m) m->err = msg;
+    else g_err = msg;
+    return s;
+}
+
+tsd_status hip_fail(tsd_model* m, hipError_t e, const char* what)
+{
+    return fail(m, TSD_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define HIP_TRY(m, expr, what)                          \
+    do {                                                \
+        hipError_t e_ = (expr);                         \
+        if (e_ != hipSuccess) return hip_fail(m, e_, what); \
+    } while (0)
+
+int group_of(int f) { return f == TSD_W_AFFINE8_G64 ? 64 : 32; }
+
+size_t canonical_matrix_bytes(int f, int N, int K)
+{
+    if (f == TSD_W_Q4_0) return (size_t)N * (K / 32) * 18;
+    if (f == TSD_W_Q8_0) return (size_t)N * (K / 32) * 34;
+    return (size_t)N * K + (size_t)N * (K / 64) * 4;
+}
+
+tsd_status validate(const tsd_config* c, std::string& msg)
+{
+    if (!c) { msg = "null config"; return TSD_ERR_INVALID_ARGUMENT; }
+    if (c->arch < 0 || c->arch > 2 || c->wfmt < 0 || c->wfmt > 2) { msg = "unknown arch or weight format"; return TSD_ERR_INVALID_ARGUMENT; }
+    if (c->n_layer <= 0 || c->d_model <= 0 || c->n_head <= 0 || c->n_kv_head <= 0 || c->head_dim <= 0 || c->d_ff <= 0 ||
+        c->vocab <= 0 || c->n_ctx <= 0 || c->batch <= 0 || c->n_head % c->n_kv_head) {
+        msg = "dimensions must be positive and n_head a multiple of n_kv_head";
+        return TSD_ERR_INVALID_ARGUMENT;
+    }
+    if (c->arch == TSD_ARCH_GPT2 && (c->n_head * c->head_dim != c->d_model || c->n_kv_head != c->n_head)) {
+        msg = "GPT2 needs n_head*head_dim == d_model and n_kv_head == n_head";
+        return TSD_ERR_INVALID_ARGUMENT;
+    }
+    const int g = group_of(c->wfmt);
+    const int qd = c->n_head * c->head_dim;
+    if (c->d_model % g || c->d_ff % g || qd % g) {
+        msg = "every reduction dimension (d_model, d_ff, n_head*head_dim) must be a multiple of the quant block (" +
+              std::to_string(g) + ")";
+        return TSD_ERR_INVALID_ARGUMENT;
+    }
+    if (c->arch == TSD_ARCH_TALKER_CP) { msg = "TALKER_CP is not built yet"; return TSD_ERR_UNSUPPORTED; }
+    if (c->batch != 1) { msg = "GPT2/LLAMA decode supports batch 1"; return TSD_ERR_UNSUPPORTED; }
+    if (c->head_dim != 64 && c->head_dim != 128) { msg = "head_dim must be 64 or 128"; return TSD_ERR_UNSUPPORTED; }
+    for (int K : {c->d_model, c->d_ff, qd})
+        if (K > 4096 || !gemv_shape_ok(c->wfmt, K)) {
+            msg = "reduction dimension " + std::to_string(K) + " has no GEMV lane mapping";
+            return TSD_ERR_UNSUPPORTED;
+        }
+    return TSD_OK;
+}
+
+int n_weights_of(const tsd_config* c)
+{
+    if (c->arch == TSD_ARCH_GPT2) return 2 + 12 * c->n_layer + 3;
+    if (c->arch == TSD_ARCH_LLAMA) return 1 + 9 * c->n_layer + 2;
+    return c->n_codebooks + 9 * c->n_layer + 2 + 9 * c->cp_n_layer + 1 + (c->n_codebooks - 1);
+}
+
+// expected canonical sizes in order; kinds: 0 fp32 tensor, 1 matrix
+void canonical_sizes(const tsd_config* c, std::vector<size_t>& sz)
+{
+    const int d = c->d_model, ff = c->d_ff, f = c->wfmt, qd = c->n_head * c->head_dim, kd = c->n_kv_head * c->head_dim;
+    auto F32 = [&](size_t n) { sz.push_back(n * 4); };
+    auto MAT = [&](int N, int K) { sz.push_back(canonical_matrix_bytes(f, N, K)); };
+    if (c->arch == TSD_ARCH_GPT2) {
+        F32((size_t)c->vocab * d);
+        F32((size_t)c->n_ctx * d);
+        for (int l = 0; l < c->n_layer; ++l) {
+            F32(d); F32(d); MAT(3 * d, d); F32(3 * d); MAT(d, d); F32(d);
+            F32(d); F32(d); MAT(ff, d); F32(ff); MAT(d, ff); F32(d);
+        }
+        F32(d); F32(d); MAT(c->vocab, d);
+    } else {
+        F32((size_t)c->vocab * d);
+        for (int l = 0; l < c->n_layer; ++l) {
+            F32(d); MAT(qd, d); MAT(kd, d); MAT(kd, d); MAT(d, qd);
+            F32(d); MAT(ff, d); MAT(ff, d); MAT(d, ff);
+        }
+        F32(d); MAT(c->vocab, d);
+    }
+}
+
+struct Layout {
+    size_t total = 0;
+};
+
+PackedMat take_mat(Planner& P, int f, int N, int K)
+{
+    PackedLayout L = packed_layout(f, N, K);
+    void* p = P.take(L.total);
+    if (!p) { PackedMat m{}; m.N = N; m.K = K; return m; }
+    return packed_view(f, p, N, K);
+}
+
+// walk the workspace; with base == nullptr it only sizes it
+size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
+{
+    Planner P(base);
+    const int d = c->d_model, H = c->n_head, Hk = c->n_kv_head, hd = c->head_dim, ff = c->d_ff, B = c->batch, f = c->wfmt;
+    const int tpp = 1, vmax = c->vocab;
+    const int qkv_rows = (H + 2 * Hk) * hd;
+    // step state
+    int* pos = (int*)P.take(4 * sizeof(int));
+    unsigned int* ticket = (unsigned int*)P.take(sizeof(unsigned int) * 4);
+    int* tok = (int*)P.take(sizeof(int) * B * tpp);
+    unsigned long long* best = (unsigned long long*)P.take(sizeof(unsigned long long) * B * tpp);
+    unsigned int* acnt = (unsigned int*)P.take(sizeof(unsigned int) * B * H);
+    int* hist = (int*)P.take(sizeof(int) * (size_t)c->n_ctx * B * tpp);
+    // activations
+    float* x = (float*)P.take(sizeof(float) * B * d);
+    float* qkv = (float*)P.take(sizeof(float) * B * qkv_rows);
+    float* attn = (float*)P.take(sizeof(float) * B * H * hd);
+    float* h = (float*)P.take(sizeof(float) * B * (size_t)ff);
+    float* logits = (float*)P.take(sizeof(float) * (size_t)B * tpp * vmax);
+    float* part = (float*)P.take(attn_part_bytes(B, H, c->n_ctx, hd));
+    float2* rope = (float2*)P.take(sizeof(float2) * (size_t)c->n_ctx * (hd / 2));
+    // embeddings
+    float* emb0 = (float*)P.take(sizeof(float) * (size_t)c->vocab * d);
+    float* wpe = c->arch == TSD_ARCH_GPT2 ? (float*)P.take(sizeof(float) * (size_t)c->n_ctx * d) : nullptr;
+    // layers
+    std::vector<LayerW> Ls(c->n_layer);
+    for (int l = 0; l < c->n_layer; ++l) {
+        LayerW& w = Ls[l];
+        if (c->arch == TSD_ARCH_GPT2) {
+            w.qkv = take_mat(P, f, 3 * d, d);
+            w.o = take_mat(P, f, d, d);
+            w.fc = take_mat(P, f, ff, d);
+            w.down = take_mat(P, f, d, ff);
+            w.n1g = (float*)P.take(4 * d); w.n1b = (float*)P.take(4 * d);
+            w.n2g = (float*)P.take(4 * d); w.n2b = (float*)P.take(4 * d);
+            w.bqkv = (float*)P.take(4 * 3 * d); w.bo = (float*)P.take(4 * d);
+            w.bfc = (float*)P.take(4 * (size_t)ff); w.bdown = (float*)P.take(4 * d);
+        } else {
+            w.qkv = take_mat(P, f, qkv_rows, d);
+            w.o = take_mat(P, f, d, H * hd);
+            w.fc = take_mat(P, f, 2 * ff, d);
+            w.down = take_mat(P, f, d, ff);
+            w.n1g = (float*)P.take(4 * d);
+            w.n2g = (float*)P.take(4 * d);
+        }
+    }
+    float* nfg = (float*)P.take(4 * d);
+    float* nfb = c->arch == TSD_ARCH_GPT2 ? (float*)P.take(4 * d) : nullptr;
+    PackedMat head = take_mat(P, f, c->vocab, d);
+    const size_t kv_layer = (size_t)B * Hk * c->n_ctx * hd;
+    __half* kc = (__half*)P.take(2 * kv_layer * c->n_layer);
+    __half* vc = (__half*)P.take(2 * kv_layer * c->n_layer);
+    if (m && base) {
+        m->pos = pos; m->dbg_pos = pos + 1; m->ticket = ticket; m->tok = tok; m->best = best; m->acnt = acnt;
+        m->hist = hist; m->x = x; m->qkv = qkv; m->attn = attn; m->h = h; m->logits = logits; m->part = part;
+        m->rope = rope; m->emb[0] = emb0; m->emb_rows[0] = c->vocab; m->wpe = wpe; m->L = Ls; m->nfg = nfg; m->nfb = nfb;
+        m->head = head; m->kc = kc; m->vc = vc; m->kv_layer_elems = kv_layer; m->tpp = tpp; m->vmax = vmax;
+        m->qkv_rows = qkv_rows;
+    }
+    return align256(P.off);
+}
+
+// ---- the step's kernels --------------------------------------------------------------------
+
+hipError_t enqueue_layer(tsd_model* m, int l, hipStream_t st, const int* pos, bool embed)
+{
+    const tsd_config& c = m->c;
+    const int d = c.d_model, H = c.n_head, Hk = c.n_kv_head, hd = c.head_dim;
+    const LayerW& w = m->L[l];
+    const bool gpt2 = c.arch == TSD_ARCH_GPT2;
+    __half* kc = m->kc + m->kv_layer_elems * l;
+    __half* vc = m->vc + m->kv_layer_elems * l;
+    hipError_t e;
+
+    // norm + fused QKV (+bias | +RoPE) + K/V append
+    ProArgs pa{};
+    pa.src = m->x;
+    pa.g = w.n1g;
+    pa.beta = w.n1b;
+    pa.eps = c.norm_eps;
+    if (embed) {
+        pa.n_emb = 1;
+        pa.tab[0] = m->emb[0];
+        pa.tab_rows[0] = m->emb_rows[0];
+        pa.tok = m->tok;
+        pa.pos_tab = m->wpe;
+        pa.pos = pos;
+        pa.x_out = m->x;
+    }
+    EpiArgs ea{};
+    ea.bias = w.bqkv;
+    ea.qrows = H * hd;
+    ea.krows = Hk * hd;
+    ea.hd = hd;
+    ea.n_ctx = c.n_ctx;
+    ea.q = m->qkv;
+    ea.kc = kc;
+    ea.vc = vc;
+    ea.rope = m->rope;
+    ea.pos = pos;
+    const int pro = embed ? (gpt2 ? PRO_LN_EMB : PRO_RMS_EMB) : (gpt2 ? PRO_LN : PRO_RMS);
+    e = launch_gemv(c.wfmt, pro, gpt2 ? EPI_QKV : EPI_QKV_ROPE, w.qkv, pa, ea, st);
+    if (e != hipSuccess) return e;
+
+    // split-KV flash-decode over positions 0..pos
+    AttnArgs aa{};
+    aa.q = m->qkv;
+    aa.ldq = m->qkv_rows;
+    aa.k = kc;
+    aa.v = vc;
+    aa.out = m->attn;
+    aa.ldo = H * hd;
+    aa.part = m->part;
+    aa.cnt = m->acnt;
+    aa.B = 1;
+    aa.H = H;
+    aa.Hkv = Hk;
+    aa.hd = hd;
+    aa.n_ctx = c.n_ctx;
+    aa.pos = pos;
+    e = launch_attention(aa, st);
+    if (e != hipSuccess) return e;
+
+    // output projection + bias + residual
+    ProArgs po{};
+    po.src = m->attn;
+    EpiArgs eo{};
+    eo.y = m->x;
+    eo.bias = w.bo;
+    e = launch_gemv(c.wfmt, PRO_LOAD, EPI_RESID, w.o, po, eo, st);
+    if (e != hipSuccess) return e;
+
+    // norm + FC (+bias, GELU) or gate/up (SwiGLU)
+    ProArgs pf{};
+    pf.src = m->x;
+    pf.g = w.n2g;
+    pf.beta = w.n2b;
+    pf.eps = c.norm_eps;
+    EpiArgs ef{};
+    ef.y = m->h;
+    ef.bias = w.bfc;
+    e = launch_gemv(c.wfmt, gpt2 ? PRO_LN : PRO_RMS, gpt2 ? EPI_GELU : EPI_SWIGLU, w.fc, pf, ef, st);
+    if (e != hipSuccess) return e;
+
+    // down projection + bias + residual
+    ProArgs pd{};
+    pd.src = m->h;
+    EpiArgs ed{};
+    ed.y = m->x;
+    ed.bias = w.bdown;
+    (void)d;
+    return launch_gemv(c.wfmt, PRO_LOAD, EPI_RESID, w.down, pd, ed, st);
+}
+
+hipError_t enqueue_step(tsd_model* m, hipStream_t st)
+{
+    const tsd_config& c = m->c;
+    for (int l = 0; l < c.n_layer; ++l) {
+        hipError_t e = enqueue_layer(m, l, st, m->pos, l == 0);
+        if (e != hipSuccess) return e;
+    }
+    ProArgs ph{};
+    ph.src = m->x;
+    ph.g = m->nfg;
+    ph.beta = m->nfb;
+    ph.eps = c.norm_eps;
+    EpiArgs eh{};
+    eh.y = m->logits;
+    eh.ldy = c.vocab;
+    eh.best = m->best;
+    eh.ticket = m->ticket;
+    eh.tok_out = m->tok;
+    eh.hist = m->hist;
+    eh.hist_stride = c.batch * m->tpp;
+    eh.pos_inc = m->pos;
+    return launch_gemv(c.wfmt, c.arch == TSD_ARCH_GPT2 ? PRO_LN : PRO_RMS, EPI_HEAD_ARGMAX, m->head, ph, eh, st);
+}
+
+tsd_status pack_weights(tsd_model* m, const tsd_tensor* w)
+{
+    const tsd_config& c = m->c;
+    const int d = c.d_model, H = c.n_head, Hk = c.n_kv_head, hd = c.head_dim, ff = c.d_ff, f = c.wfmt;
+    hipStream_t st = m->st;
+    int i = 0;
+    auto cp = [&](void* dst, int idx) { return hipMemcpyAsync(dst, w[idx].ptr, w[idx].bytes, hipMemcpyDeviceToDevice, st); };
+    auto pk = [&](const PackedMat& dst, int idx, int N, int K, int row0, int mode) {
+        return launch_pack(f, w[idx].ptr, N, K, (void*)dst.q, dst.N, row0, mode, hd, st);
+    };
+    HIP_TRY(m, cp((void*)m->emb[0], i++), "copy embedding");
+    if (c.arch == TSD_ARCH_GPT2) HIP_TRY(m, cp((void*)m->wpe, i++), "copy positions");
+    for (int l = 0; l < c.n_layer; ++l) {
+        LayerW& L = m->L[l];
+        if (c.arch == TSD_ARCH_GPT2) {
+            HIP_TRY(m, cp(L.n1g, i++), "copy"); HIP_TRY(m, cp(L.n1b, i++), "copy");
+            HIP_TRY(m, pk(L.qkv, i++, 3 * d, d, 0, PACK_IDENTITY), "pack qkv");
+            HIP_TRY(m, cp(L.bqkv, i++), "copy");
+            HIP_TRY(m, pk(L.o, i++, d, d, 0, PACK_IDENTITY), "pack o");
+            HIP_TRY(m, cp(L.bo, i++), "copy");
+            HIP_TRY(m, cp(L.n2g, i++), "copy"); HIP_TRY(m, cp(L.n2b, i++), "copy");
+            HIP_TRY(m, pk(L.fc, i++, ff, d, 0, PACK_IDENTITY), "pack fc");
+            HIP_TRY(m, cp(L.bfc, i++), "copy");
+            HIP_TRY(m, pk(L.down, i++, d, ff, 0, PACK_IDENTITY), "pack down");
+            HIP_TRY(m, cp(L.bdown, i++), "copy");
+        } else {
+            HIP_TRY(m, cp(L.n1g, i++), "copy");
+            HIP_TRY(m, pk(L.qkv, i++, H * hd, d, 0, PACK_ROPE_PAIRS), "pack q");
+            HIP_TRY(m, pk(L.qkv, i++, Hk * hd, d, H * hd, PACK_ROPE_PAIRS), "pack k");
+            HIP_TRY(m, pk(L.qkv, i++, Hk * hd, d, (H + Hk) * hd, PACK_IDENTITY), "pack v");
+            HIP_TRY(m, pk(L.o, i++, d, H * hd, 0, PACK_IDENTITY), "pack o");
+            HIP_TRY(m, cp(L.n2g, i++), "copy");
+            HIP_TRY(m, pk(L.fc, i++, ff, d, 0, PACK_INTERLEAVE_EVEN), "pack gate");
+            HIP_TRY(m, pk(L.fc, i++, ff, d, 0, PACK_INTERLEAVE_ODD), "pack up");
+            HIP_TRY(m, pk(L.down, i++, d, ff, 0, PACK_IDENTITY), "pack down");
+        }
+    }
+    HIP_TRY(m, cp(m->nfg, i++), "copy");
+    if (c.arch == TSD_ARCH_GPT2) HIP_TRY(m, cp(m->nfb, i++), "copy");
+    HIP_TRY(m, pk(m->head, i++, c.vocab, d, 0, PACK_IDENTITY), "pack head");
+    return TSD_OK;
+}
+
+tsd_status init_state(tsd_model* m)
+{
+    const tsd_config& c = m->c;
+    hipStream_t st = m->st;
+    HIP_TRY(m, launch_fill_i32(m->pos, 0, 4, st), "init");
+    HIP_TRY(m, launch_fill_u32(m->ticket, 0u, 4, st), "init");
+    HIP_TRY(m, launch_fill_i32(m->tok, 0, c.batch * m->tpp, st), "init");
+    HIP_TRY(m, launch_fill_u64(m->best, 0ull, c.batch * m->tpp, st), "init");
+    HIP_TRY(m, launch_fill_u32(m->acnt, 0u, c.batch * c.n_head, st), "init");
+    HIP_TRY(m, launch_fill_i32(m->hist, 0, c.n_ctx * c.batch * m->tpp, st), "init");
+    HIP_TRY(m, launch_fill_f32(m->logits, 0.f, (size_t)c.batch * m->tpp * m->vmax, st), "init");
+    // RoPE table in fp64 on the host: angle = pos * theta^(-2i/hd)
+    const int half = c.head_dim / 2;
+    std::vector<float2> tab((size_t)c.n_ctx * half);
+    for (int p = 0; p < c.n_ctx; ++p)
+        for (int i = 0; i < half; ++i) {
+            const double a = (double)p * pow((double)c.rope_theta, -2.0 * i / c.head_dim);
+            tab[(size_t)p * half + i] = make_float2((float)cos(a), (float)sin(a));
+        }
+    HIP_TRY(m, hipMemcpyAsync(m->rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice, st), "rope table");
+    HIP_TRY(m, hipStreamSynchronize(st), "create sync");
+    return TSD_OK;
+}
+
+tsd_status capture(tsd_model* m)
+{
+    hipStream_t cs;
+    HIP_TRY(m, hipStreamCreateWithFlags(&cs, hipStreamNonBlocking), "capture stream");
+    hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) { (void)hipStreamDestroy(cs); return hip_fail(m, e, "begin capture"); }
+    hipError_t le = enqueue_step(m, cs);
+    hipGraph_t g = nullptr;
+    e = hipStreamEndCapture(cs, &g);
+    (void)hipStreamDestroy(cs);
+    if (le != hipSuccess) { if (g) (void)hipGraphDestroy(g); return hip_fail(m, le, "step launch during capture"); }
+    if (e != hipSuccess) return hip_fail(m, e, "end capture");
+    hipGraphExec_t x = nullptr;
+    e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+    if (e != hipSuccess) { (void)hipGraphDestroy(g); return hip_fail(m, e, "instantiate"); }
+    m->graph = g;
+    m->exec = x;
+    return TSD_OK;
+}
+
+}  // namespace
+
+// ---- C ABI --------------------------------------------------------------------------------
+
+extern "C" {
+
+tsd_status tsd_workspace_bytes(const tsd_config* cfg, size_t* out)
+{
+    std::string msg;
+    tsd_status s = validate(cfg, msg);
+    if (s != TSD_OK) return fail(nullptr, s, msg);
+    if (!out) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null output");
+    *out = plan(nullptr, cfg, nullptr);
+    return TSD_OK;
+}
+
+tsd_status tsd_model_create(const tsd_config* cfg, const tsd_tensor* weights, int n_weights, void* d_ws,
+                            size_t ws_bytes, void* stream, const tsd_sampling* sampling, tsd_model** out)
+{
+    std::string msg;
+    tsd_status s = validate(cfg, msg);
+    if (s != TSD_OK) return fail(nullptr, s, msg);
+    if (!out || !weights || !d_ws) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null argument");
+    *out = nullptr;
+    if ((uintptr_t)d_ws % 256) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    const size_t need = plan(nullptr, cfg, nullptr);
+    if (ws_bytes < need)
+        return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "workspace too small: need " + std::to_string(need) + " bytes");
+    if (n_weights != n_weights_of(cfg))
+        return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "expected " + std::to_string(n_weights_of(cfg)) + " weights");
+    std::vector<size_t> sz;
+    canonical_sizes(cfg, sz);
+    for (int i = 0; i < n_weights; ++i)
+        if (!weights[i].ptr || weights[i].bytes != sz[i])
+            return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "weight " + std::to_string(i) + ": " +
+                        std::to_string(weights[i].bytes) + " bytes, expected " + std::to_string(sz[i]));
+    if (sampling && sampling->mode != 0) return fail(nullptr, TSD_ERR_UNSUPPORTED, "top-k sampling is not built yet");
+    tsd_model* m = new (std::nothrow) tsd_model();
+    if (!m) return fail(nullptr, TSD_ERR_OUT_OF_MEMORY, "host allocation");
+    m->c = *cfg;
+    if (sampling) m->samp = *sampling;
+    m->st = (hipStream_t)stream;
+    m->ws = (uint8_t*)d_ws;
+    m->ws_bytes = ws_bytes;
+    plan(m, cfg, (uint8_t*)d_ws);
+    tsd_status r = pack_weights(m, weights);
+    if (r == TSD_OK) r = init_state(m);
+    if (r == TSD_OK) r = capture(m);
+    if (r != TSD_OK) {
+        g_err = m->err;
+        tsd_model_destroy(m);
+        return r;
+    }
+    *out = m;
+    return TSD_OK;
+}
+
+tsd_status tsd_model_destroy(tsd_model* m)
+{
+    if (!m) return TSD_OK;
+    if (m->exec) (void)hipGraphExecDestroy(m->exec);
+    if (m->graph) (void)hipGraphDestroy(m->graph);
+    delete m;
+    return TSD_OK;
+}
+
+const char* tsd_last_error(const tsd_model* m) { return m ? m->err.c_str() : g_err.c_str(); }
+
+tsd_status tsd_step(tsd_model* m, const int32_t* d_in, int32_t* d_next)
+{
+    if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
+    if (m->n_past >= m->c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "context full");
+    const int nt = m->c.batch * m->tpp;
+    if (d_in) HIP_TRY(m, launch_copy_i32(m->tok, d_in, nt, m->st), "set input");
+    HIP_TRY(m, hipGraphLaunch(m->exec, m->st), "graph launch");
+    if (d_next) HIP_TRY(m, launch_copy_i32(d_next, m->tok, nt, m->st), "copy ids");
+    m->n_past += 1;
+    return TSD_OK;
+}
+
+tsd_status tsd_prefill(tsd_model* m, const int32_t* d_tokens, int n, int32_t* d_next)
+{
+    if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
+    if (!d_tokens || n <= 0) return fail(m, TSD_ERR_INVALID_ARGUMENT, "empty prompt");
+    if (m->n_past + n > m->c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "prompt does not fit the context");
+    const int nt = m->c.batch * m->tpp;
+    for (int t = 0; t < n; ++t) {
+        HIP_TRY(m, launch_copy_i32(m->tok, d_tokens + (size_t)t * nt, nt, m->st), "set input");
+        HIP_TRY(m, hipGraphLaunch(m->exec, m->st), "graph launch");
+        m->n_past += 1;
+    }
+    if (d_next) HIP_TRY(m, launch_copy_i32(d_next, m->tok, nt, m->st), "copy ids");
+    return TSD_OK;
+}
+
+tsd_status tsd_reset(tsd_model* m)
+{
+    if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
+    HIP_TRY(m, launch_fill_i32(m->pos, 0, 1, m->st), "reset");
+    HIP_TRY(m, launch_fill_i32(m->hist, 0, m->c.n_ctx * m->c.batch * m->tpp, m->st), "reset");
+    m->n_past = 0;
+    return TSD_OK;
+}
+
+tsd_status tsd_truncate(tsd_model* m, int n_past)
+{
+    if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
+    if (n_past < 0 || n_past > m->n_past) return fail(m, TSD_ERR_INVALID_ARGUMENT, "truncate beyond n_past");
+    HIP_TRY(m, launch_fill_i32(m->pos, n_past, 1, m->st), "truncate");
+    m->n_past = n_past;
+    return TSD_OK;
+}
+
+tsd_status tsd_n_past(const tsd_model* m, int* out)
+{
+    if (!m || !out) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null argument");
+    *out = m->n_past;
+    return TSD_OK;
+}
+
+tsd_status tsd_get_logits(tsd_model* m, float* d_out)
+{
+    if (!m || !d_out) return fail(m, TSD_ERR_INVALID_ARGUMENT, "null argument");
+    const size_t n = (size_t)m->c.batch * m->tpp * m->vmax;
+    HIP_TRY(m, hipMemcpyAsync(d_out, m->logits, n * sizeof(float), hipMemcpyDeviceToDevice, m->st), "copy logits");
+    return TSD_OK;
+}
+
+tsd_status tsd_get_tokens(tsd_model* m, int first, int n, int32_t* d_out)
+{
+    if (!m || !d_out) return fail(m, TSD_ERR_INVALID_ARGUMENT, "null argument");
+    if (first < 0 || n < 0 || first + n > m->c.n_ctx) return fail(m, TSD_ERR_INVALID_ARGUMENT, "range outside the context");
+    const size_t nt = (size_t)m->c.batch * m->tpp;
+    HIP_TRY(m, hipMemcpyAsync(d_out, m->hist + first * nt, n * nt * sizeof(int), hipMemcpyDeviceToDevice, m->st), "copy tokens");
+    return TSD_OK;
+}
+
+tsd_status tsd_load_kv(tsd_model* m, const uint16_t* d_k, const uint16_t* d_v, int n_pos)
+{
+    if (!m || !d_k || !d_v) return fail(m, TSD_ERR_INVALID_ARGUMENT, "null argument");
+    const tsd_config& c = m->c;
+    if (n_pos < 0 || n_pos > c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "n_pos outside the context");
+    if (n_pos > 0) {
+        const size_t w = (size_t)n_pos * c.head_dim * 2, dp = (size_t)c.n_ctx * c.head_dim * 2;
+        const size_t rows = (size_t)c.n_layer * c.batch * c.n_kv_head;
+        HIP_TRY(m, hipMemcpy2DAsync(m->kc, dp, d_k, w, w, rows, hipMemcpyDeviceToDevice, m->st), "load k");
+        HIP_TRY(m, hipMemcpy2DAsync(m->vc, dp, d_v, w, w, rows, hipMemcpyDeviceToDevice, m->st), "load v");
+    }
+    HIP_TRY(m, launch_fill_i32(m->pos, n_pos, 1, m->st), "set position");
+    m->n_past = n_pos;
+    return TSD_OK;
+}
+
+tsd_status tsd_layer_forward(tsd_model* m, int layer, const float* d_x, int pos, float* d_out)
+{
+    if (!m || !d_x || !d_out) return fail(m, TSD_ERR_INVALID_ARGUMENT, "null argument");
+    const tsd_config& c = m->c;
+    if (layer < 0 || layer >= c.n_layer) return fail(m, TSD_ERR_INVALID_ARGUMENT, "layer out of range");
+    if (pos < 0 || pos >= c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "position outside the context");
+    const size_t xb = (size_t)c.batch * c.d_model * sizeof(float);
+    HIP_TRY(m, hipMemcpyAsync(m->x, d_x, xb, hipMemcpyDeviceToDevice, m->st), "copy x");
+    HIP_TRY(m, launch_fill_i32(m->dbg_pos, pos, 1, m->st), "set position");
+    HIP_TRY(m, enqueue_layer(m, layer, m->st, m->dbg_pos, false), "layer");
+    HIP_TRY(m, hipMemcpyAsync(d_out, m->x, xb, hipMemcpyDeviceToDevice, m->st), "copy out");
+    return TSD_OK;
+}
+
+// ---- standalone operators -------------------------------------------------------------------
+
+tsd_status tsd_gemv_packed_bytes(int wfmt, int N, int K, size_t* out)
+{
+    if (!out || wfmt < 0 || wfmt > 2 || N <= 0 || K <= 0 || K % group_of(wfmt))
+        return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "bad format or shape");
+    *out = packed_layout(wfmt, N, K).total;
+    return TSD_OK;
+}
+
+tsd_status tsd_gemv_pack(int wfmt, const void* d_w, size_t w_bytes, int N, int K, void* d_packed, size_t packed_bytes,
+                         void* stream)
+{
+    size_t need = 0;
+    tsd_status s = tsd_gemv_packed_bytes(wfmt, N, K, &need);
+    if (s != TSD_OK) return s;
+    if (!d_w || !d_packed) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null buffer");
+    if (w_bytes != canonical_matrix_bytes(wfmt, N, K)) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "canonical size mismatch");
+    if (packed_bytes < need) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "packed buffer too small");
+    hipError_t e = launch_pack(wfmt, d_w, N, K, d_packed, N, 0, PACK_IDENTITY, 64, (hipStream_t)stream);
+    return e == hipSuccess ? TSD_OK : hip_fail(nullptr, e, "pack");
+}
+
+tsd_status tsd_gemv(int wfmt, const void* d_packed, int N, int K, int B, const float* d_x, const float* d_bias,
+                    float* d_y, void* stream)
+{
+    if (wfmt < 0 || wfmt > 2 || N <= 0 || K <= 0 || K % group_of(wfmt) || B < 1 || B > 4)
+        return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "bad format or shape");
+    if (!d_packed || !d_x || !d_y) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null buffer");
+    if (K > 4096 || !gemv_shape_ok(wfmt, K)) return fail(nullptr, TSD_ERR_UNSUPPORTED, "K has no GEMV lane mapping");
+    PackedMat W = packed_view(wfmt, (void*)d_packed, N, K);
+    for (int b = 0; b < B; ++b) {   // batch rows share nothing but the weights: one launch each
+        ProArgs pa{};
+        pa.src = d_x + (size_t)b * K;
+        EpiArgs ea{};
+        ea.y = d_y + (size_t)b * N;
+        ea.bias = d_bias;
+        hipError_t e = launch_gemv(wfmt, PRO_LOAD, EPI_STORE, W, pa, ea, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(nullptr, e, "gemv");
+    }
+    return TSD_OK;
+}
+
+tsd_status tsd_attention_scratch_bytes(int B, int H, int n_ctx, int hd, size_t* out)
+{
+    if (!out || B <= 0 || H <= 0 || n_ctx <= 0 || (hd != 64 && hd != 128))
+        return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "bad shape");
+    *out = align256((size_t)B * H * sizeof(unsigned int)) + attn_part_bytes(B, H, n_ctx, hd);
+    return TSD_OK;
+}
+
+tsd_status tsd_attention(const float* d_q, const uint16_t* d_k, const uint16_t* d_v, int B, int H, int Hkv, int hd,
+                         int n_keys, int n_ctx, float* d_out, void* d_scratch, size_t scratch_bytes, void* stream)
+{
+    size_t need = 0;
+    tsd_status s = tsd_attention_scratch_bytes(B, H, n_ctx, hd, &need);
+    if (s != TSD_OK) return s;
+    if (Hkv <= 0 || H % Hkv || n_keys < 1 || n_keys > n_ctx) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "bad shape");
+    if (!d_q || !d_k || !d_v || !d_out || !d_scratch) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null buffer");
+    if (scratch_bytes < need) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "scratch too small");
+    hipStream_t st = (hipStream_t)stream;
+    unsigned int* cnt = (unsigned int*)d_scratch;
+    hipError_t e = launch_fill_u32(cnt, 0u, B * H, st);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "attention scratch");
+    AttnArgs a{};
+    a.q = d_q;
+    a.ldq = H * hd;
+    a.k = (const __half*)d_k;
+    a.v = (const __half*)d_v;
+    a.out = d_out;
+    a.ldo = H * hd;
+    a.part = (float*)((uint8_t*)d_scratch + align256((size_t)B * H * sizeof(unsigned int)));
+    a.cnt = cnt;
+    a.B = B;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.hd = hd;
+    a.n_ctx = n_ctx;
+    a.pos = nullptr;
+    a.n_keys = n_keys;
+    e = launch_attention(a, st);
+    return e == hipSuccess ? TSD_OK : hip_fail(nullptr, e, "attention");
+}
+
+}  // extern "C"

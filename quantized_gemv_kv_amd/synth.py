@@ -112,12 +112,12 @@ def config(name: str) -> dict:
 
 def small_config(arch: str, wfmt: str, **kw) -> dict:
     """Tiny shapes for CPU tests: several GEMV tiles and a ragged tail are still present."""
-    c = dict(arch=arch, wfmt=wfmt, n_layer=2, d_model=128, n_head=4, n_kv_head=4, head_dim=32,
-             d_ff=192, vocab=160, n_ctx=48, batch=1, norm_eps=1e-5,
+    c = dict(arch=arch, wfmt=wfmt, n_layer=2, d_model=128, n_head=2, n_kv_head=2, head_dim=64,
+             d_ff=256, vocab=160, n_ctx=48, batch=1, norm_eps=1e-5,
              rope_theta=10000.0, cp_n_layer=0, n_codebooks=0, cp_vocab=0, sample_mode=0, top_k=0,
              temperature=1.0, seed=42)
     if arch == "talker_cp":
-        c.update(n_kv_head=2, cp_n_layer=2, n_codebooks=4, cp_vocab=96, batch=2)
+        c.update(n_kv_head=1, cp_n_layer=2, n_codebooks=4, cp_vocab=96, batch=2)
     c.update(kw)
     return c
 

@@ -1,0 +1,127 @@
+"""GPU parity of the standalone kernels (fused dequant GEMV, split-KV attention) against the
+CPU oracle, through the C ABI.  Tolerance: rel = max|got-ref| / max|ref| <= 2e-3 per output
+tensor; the GEMV is also held to the fp32 accumulation bound."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from parity import REL_TOL, rel_err
+from quantized_gemv_kv_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _t():
+    import torch
+    return torch
+
+
+def dev(a):
+    torch = _t()
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+GEMV_CASES = [
+    ("q8_0", 1024, 1024, 1),     # the lone Q8_0 GEMV workload (1024 x 1024, batch 1)
+    ("q8_0", 1024, 1024, 3),
+    ("q8_0", 4096, 1024, 1),
+    ("q8_0", 1024, 4096, 1),     # one row spans four loads
+    ("q8_0", 8192, 1024, 1),
+    ("q4_0", 3072, 1024, 1),     # GPT-2-Medium fused QKV
+    ("q4_0", 4096, 1024, 2),
+    ("q4_0", 1024, 4096, 1),     # down projection
+    ("q4_0", 8192, 1024, 1),     # head
+    ("aff8", 4096, 1024, 1),     # Talker fused QKV (2048 + 1024 + 1024)
+    ("aff8", 1024, 2048, 1),
+    ("aff8", 1024, 3072, 4),     # three loads per row, last one partly idle
+    ("q4_0", 40, 128, 1),        # ragged: not a multiple of the rows per block
+    ("q8_0", 7, 64, 2),
+    ("aff8", 3, 64, 1),
+    ("q4_0", 1, 32, 1),          # one slot per row, 128 rows per wave, one real row
+    ("q4_0", 130, 256, 1),
+]
+
+
+@pytest.mark.parametrize("fmt,N,K,B", GEMV_CASES)
+def test_gemv_matches_oracle(fmt, N, K, B):
+    torch = _t()
+    say(f"[gemv] fmt={fmt} N={N} K={K} B={B}")
+    rng = synth.rng_for(11, N, K, B)
+    blob = synth.matrix(fmt, rng, N, K)
+    x = synth.normal_f32(rng, (B, K))
+    bias = synth.normal_f32(rng, (N,), 0.5)
+    ref = oracle.gemv_f32(fmt, blob, N, K, x, bias)
+    from quantized_gemv_kv_amd import binding as tb
+    packed = torch.empty(tb.tsd_gemv_packed_bytes(fmt, N, K), dtype=torch.uint8, device="cuda")
+    tb.tsd_gemv_pack(fmt, dev(blob), N, K, packed)
+    y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+    tb.tsd_gemv(fmt, packed, N, K, B, dev(x), dev(bias), y)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    assert rel_err(got, ref) <= REL_TOL
+    # fp32 accumulation bound, row by row: |err| <= 4 K u sum_k |w x| + |b| u
+    W = oracle.dequant(fmt, blob, N, K)
+    mag = np.abs(x.astype(np.float64)) @ np.abs(W).T + np.abs(bias)
+    assert np.all(np.abs(got - ref) <= 4 * K * 2.0 ** -24 * mag + 1e-30)
+
+
+def test_gemv_rejects_bad_shapes():
+    torch = _t()
+    from quantized_gemv_kv_amd import binding as tb
+    with pytest.raises(tb.TsdError):
+        tb.tsd_gemv_packed_bytes("q4_0", 16, 48)                     # K not a multiple of 32
+    p = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
+    x = torch.zeros(8192, dtype=torch.float32, device="cuda")
+    with pytest.raises(tb.TsdError):
+        tb.tsd_gemv("q8_0", p, 4, 96, 1, x, None, x)                  # 6 slots per row: no lane mapping
+    with pytest.raises(tb.TsdError):
+        tb.tsd_gemv("q8_0", p, 4, 64, 5, x, None, x)                  # batch > 4
+
+
+ATTN_CASES = [
+    # hd, H, Hkv, B, n_keys, n_ctx, q scale
+    (64, 16, 16, 1, 1, 1024, 1.0),
+    (64, 16, 16, 1, 63, 1024, 1.0),
+    (64, 16, 16, 1, 64, 1024, 1.0),
+    (64, 16, 16, 1, 65, 1024, 1.0),
+    (64, 16, 16, 1, 513, 1024, 1.0),   # one GPT-2-Medium layer after 512 cached positions
+    (64, 16, 16, 1, 757, 1024, 4.0),   # peaked softmax
+    (64, 16, 16, 1, 1024, 1024, 1.0),  # full context
+    (128, 16, 8, 2, 300, 512, 1.0),    # GQA 16/8, head 128
+    (128, 16, 8, 16, 17, 64, 2.0),     # predictor-sized cache, batch 16
+    (64, 4, 1, 1, 200, 256, 1.0),      # all heads share one KV head
+]
+
+
+@pytest.mark.parametrize("hd,H,Hkv,B,n_keys,n_ctx,qs", ATTN_CASES)
+def test_attention_matches_oracle(hd, H, Hkv, B, n_keys, n_ctx, qs):
+    torch = _t()
+    from quantized_gemv_kv_amd import binding as tb
+    say(f"[attn] hd={hd} H={H} Hkv={Hkv} B={B} n_keys={n_keys} n_ctx={n_ctx}")
+    rng = synth.rng_for(5, hd, H, n_keys)
+    q = synth.normal_f32(rng, (B, H, hd), qs)
+    k = synth.fp16_cache(rng, (B, Hkv, n_ctx, hd))
+    v = synth.fp16_cache(rng, (B, Hkv, n_ctx, hd))
+    ref = np.empty((B, H, hd))
+    for b in range(B):
+        for h in range(H):
+            g = h // (H // Hkv)
+            ref[b, h] = oracle.attend(q[b, h], k[b, g, :n_keys], v[b, g, :n_keys])
+    scratch = torch.empty(tb.tsd_attention_scratch_bytes(B, H, n_ctx, hd), dtype=torch.uint8, device="cuda")
+    out = torch.full((B, H, hd), float("nan"), dtype=torch.float32, device="cuda")
+    dq, dk, dv = dev(q), dev(k), dev(v)
+    for rep in range(2):           # the split counters must be left at zero for the next call
+        tb.tsd_attention(dq, dk, dv, B, H, Hkv, hd, n_keys, n_ctx, out, scratch)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.all(np.isfinite(got))
+        assert rel_err(got, ref) <= REL_TOL, rep
+        assert rel_err(got, ref) <= 1e-5, rep

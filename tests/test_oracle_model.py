@@ -95,9 +95,10 @@ def orc_half_row(orc, v):
     return np.array([orc.double_to_half(float(t)) for t in v], np.uint16)
 
 
-@pytest.mark.parametrize("arch,fmt,hk", [("gpt2", "q4_0", 4), ("llama", "q8_0", 2), ("llama", "aff8", 1)])
-def test_layer_forward_equals_composed_operators(orc, arch, fmt, hk):
-    cfg = synth.small_config(arch, fmt, n_kv_head=hk if arch != "gpt2" else 4)
+@pytest.mark.parametrize("arch,fmt,kw", [("gpt2", "q4_0", {}), ("llama", "q8_0", {}), ("llama", "aff8", {"n_kv_head": 1}),
+                                         ("llama", "q8_0", {"d_model": 256, "n_head": 4, "n_kv_head": 2})])
+def test_layer_forward_equals_composed_operators(orc, arch, fmt, kw):
+    cfg = synth.small_config(arch, fmt, **kw)
     m, w = make(orc, cfg)
     P = 20
     k, v = synth.kv_cache(cfg, P, seed=9)

@@ -1,0 +1,179 @@
+"""Decode-step benchmark on one MI355X.
+
+Workload (the pages' T3 decoder at its real shape): a 24-layer GPT-2-Medium-shaped speech-token
+decoder, d 1024, 16 heads x 64, FFN 4096, learned positions, vocab 8192 head, Q4_0 weights,
+fp32 norms/embeddings ~N(0, 0.02), fp16 KV cache; 256-token prefill, then greedy decode steps at
+positions 256 .. 255+K, batch 1.  All inputs are seeded synthetic data.
+
+One step = one replay of the captured decode graph (every layer, the head and the greedy
+sampler).  W warm-up steps run first and the context is then truncated back to 256 positions,
+so the K timed steps cover exactly the positions of the configured run.  The timed region is
+bracketed by stream synchronisation and hipEvents recorded on the model's stream.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD = "gpt2_medium_q4_0"
+PROMPT = 256
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--seed", type=int, default=42)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="enqueue each step kernel by kernel instead of replaying the graph (for counter "
+                         "collection, which cannot follow graph launches); prefill is skipped: the cache "
+                         "is filled with random values instead")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run one plain fp32 device copy of this size (a known-traffic kernel for "
+                         "scaling hardware byte counters)")
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg, weights, seconds, seed):
+    """The CPU oracle as it stands (single-threaded C, fp64), timed on this host: decode steps
+    from position 256 over a random 256-position fp16 cache, until the time budget is spent."""
+    import oracle
+    om = oracle.OracleModel(cfg, weights)
+    from quantized_gemv_kv_amd import synth
+    k, v = synth.kv_cache(cfg, PROMPT, seed=seed)
+    om.load_kv(k, v, PROMPT)
+    tok = np.array([[1]], np.int32)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        tok = om.step(tok)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 64:
+            break
+    om.close()
+    return {"value": n / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} decode steps of the same 24-layer model at positions {PROMPT}..{PROMPT + n - 1} "
+                      f"over a random {PROMPT}-position fp16 cache, single-threaded fp64 oracle, {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode step is not sharded "
+              f"across GPUs in this build.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from quantized_gemv_kv_amd import Model, roofline, synth
+
+    cfg = synth.config(WORKLOAD)
+    K, W = args.steps, args.warmup
+    if PROMPT + max(K, W) > cfg["n_ctx"]:
+        print(f"steps/warmup exceed the {cfg['n_ctx']}-position context", file=sys.stderr)
+        sys.exit(2)
+    weights = synth.model_weights(cfg, args.seed)
+    stream = torch.cuda.Stream()
+    model = Model(cfg, weights, stream=stream)
+    prompt = torch.from_numpy(synth.prompt_tokens(cfg, PROMPT, seed=args.seed)).to("cuda")
+    step = model.step_eager if args.eager else model.step
+    with torch.cuda.stream(stream):
+        if args.eager:
+            k, v = synth.kv_cache(cfg, PROMPT, seed=args.seed)
+            model.load_kv(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), PROMPT)
+        else:
+            model.prefill(prompt)
+        for _ in range(W):
+            step(None, out=False)
+        stream.synchronize()
+        model.truncate(PROMPT)
+        stream.synchronize()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(K):
+            step(None, out=False)
+        e1.record(stream)
+        stream.synchronize()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1)
+    ids = model.tokens(PROMPT, K).cpu().numpy().reshape(-1)
+    assert ids.min() >= 0 and ids.max() < cfg["vocab"], "sampled ids out of range"
+
+    # dominant kernel: every kind timed inside real steps (event records around each launch on
+    # the model's stream), then the largest one re-timed over the timed region's positions
+    from quantized_gemv_kv_amd import TsdError
+    kinds = {}
+    with torch.cuda.stream(stream):
+        for kind in ("qkv", "attn", "oproj", "fc", "down", "head"):
+            model.truncate(PROMPT)
+            try:
+                kinds[kind] = model.time_kernel(kind, min(K, 100))
+            except TsdError:          # not a separate kernel in this step (fused)
+                pass
+        dom = max(kinds, key=lambda k: kinds[k][0] * kinds[k][1])
+        model.truncate(PROMPT)
+        dom_us, dom_n = model.time_kernel(dom, K)
+    dom_bytes = roofline.mean_kernel_bytes(cfg, dom, PROMPT, K)
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+
+    step_bytes = roofline.mean_step_bytes(cfg, PROMPT, K)
+    ms_step = ms / K
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    result = {
+        "metric": "decode tokens/sec at batch 1 + achieved HBM GB/s (% of peak) per step",
+        "value": K / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q4_0 weights, fp32 accumulate, fp16 kv",
+        "data": "synthetic (seeded random weights, prompt ids and values; no checkpoint)",
+        "config": {"workload": "GPT-2-Medium-shaped 24-layer speech-token decoder, Q4_0, 256-token prefill then "
+                               f"{K} greedy decode steps, batch 1",
+                   "d_model": 1024, "n_layer": 24, "n_head": 16, "d_ff": 4096, "vocab": 8192,
+                   "prompt": PROMPT, "global_batch": 1},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": roofline.HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / roofline.HBM_PEAK_GBS, "traffic": None,
+                     "kernel": dom, "launch_us": dom_us, "launches_per_step": dom_n,
+                     "bytes_per_launch": dom_bytes},
+        "kernel_us": {k: round(v[0], 3) for k, v in kinds.items()},
+        "step_gbs": gbs,
+        "step_frac_of_hbm_peak": gbs / roofline.HBM_PEAK_GBS,
+        "step_bytes": step_bytes,
+        "wall_tokens_per_s": K / wall,
+    }
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = 2 * n * 4
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, weights, args.cpu_seconds, args.seed)
+    model.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

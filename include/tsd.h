@@ -124,6 +124,11 @@ tsd_status tsd_prefill(tsd_model* m, const int32_t* d_tokens, int n, int32_t* d_
  * (tsd_get_tokens).  n_past increases by one. */
 tsd_status tsd_step(tsd_model* m, const int32_t* d_in, int32_t* d_next);
 
+/* The same step with the same kernels and arguments, enqueued launch by launch instead of as
+ * the captured graph (for profilers and counter collectors that cannot follow graph launches).
+ * Results are identical to tsd_step. */
+tsd_status tsd_step_eager(tsd_model* m, const int32_t* d_in, int32_t* d_next);
+
 tsd_status tsd_reset(tsd_model* m);                     /* n_past = 0, history cleared */
 tsd_status tsd_truncate(tsd_model* m, int n_past);      /* keep the first n_past positions */
 tsd_status tsd_n_past(const tsd_model* m, int* out);
@@ -147,6 +152,16 @@ tsd_status tsd_load_kv(tsd_model* m, const uint16_t* d_k, const uint16_t* d_v, i
  * layer to d_out [batch][d_model].  n_past is not changed.  Uses the same kernels as the
  * step. */
 tsd_status tsd_layer_forward(tsd_model* m, int layer, const float* d_x, int pos, float* d_out);
+
+/* Measurement: runs n_steps real decode steps (advancing n_past like tsd_step, sampled ids fed
+ * forward) by enqueueing the step's kernels, with the step's launch configuration and
+ * arguments, directly on the model's stream with every launch of one kernel kind bracketed by
+ * HIP event records; synchronises after each step and returns the mean duration of that kernel
+ * in *avg_us and its launches per step.  Each bracket's own cost is calibrated by an empty
+ * bracket recorded just before it and subtracted.  Kinds: 0 norm + fused
+ * QKV GEMV, 1 attention, 2 attention merge + output projection, 3 norm + FC / gate-up,
+ * 4 down projection, 5 final norm + head + sampler. */
+tsd_status tsd_time_kernel(tsd_model* m, int kind, int n_steps, float* avg_us, int* launches_per_step);
 
 /* ---- standalone operators (same kernels as the step) ------------------------------------- */
 

@@ -20,10 +20,11 @@ STATUS = {0: "TSD_OK", 1: "TSD_ERR_INVALID_ARGUMENT", 2: "TSD_ERR_UNSUPPORTED", 
           4: "TSD_ERR_CONTEXT_FULL", 5: "TSD_ERR_HIP", 6: "TSD_ERR_STATE"}
 
 # symbols declared in include/tsd.h
-EXPORTS = ["tsd_workspace_bytes", "tsd_model_create", "tsd_prefill", "tsd_step", "tsd_reset", "tsd_truncate",
+EXPORTS = ["tsd_workspace_bytes", "tsd_model_create", "tsd_prefill", "tsd_step", "tsd_step_eager", "tsd_reset", "tsd_truncate",
            "tsd_n_past", "tsd_model_destroy", "tsd_last_error", "tsd_get_logits", "tsd_get_tokens", "tsd_load_kv",
            "tsd_layer_forward", "tsd_gemv_packed_bytes", "tsd_gemv_pack", "tsd_gemv",
-           "tsd_attention_scratch_bytes", "tsd_attention"]
+           "tsd_attention_scratch_bytes", "tsd_attention", "tsd_time_kernel"]
+KERNEL_KINDS = {"qkv": 0, "attn": 1, "oproj": 2, "fc": 3, "down": 4, "head": 5}
 
 
 class TsdError(RuntimeError):
@@ -66,6 +67,7 @@ def lib():
                                  ctypes.POINTER(tsd_sampling), ctypes.POINTER(_P)],
             "tsd_prefill": [_P, _P, _I, _P],
             "tsd_step": [_P, _P, _P],
+            "tsd_step_eager": [_P, _P, _P],
             "tsd_reset": [_P],
             "tsd_truncate": [_P, _I],
             "tsd_n_past": [_P, ctypes.POINTER(_I)],
@@ -79,6 +81,7 @@ def lib():
             "tsd_gemv": [_I, _P, _I, _I, _I, _P, _P, _P, _P],
             "tsd_attention_scratch_bytes": [_I, _I, _I, _I, ctypes.POINTER(_SZ)],
             "tsd_attention": [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P],
+            "tsd_time_kernel": [_P, _I, _I, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_I)],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -211,6 +214,11 @@ class Model:
         self._chk(lib().tsd_step(self.h, _ptr(t), _ptr(self._next) if out else None))
         return self._next if out else None
 
+    def step_eager(self, tokens=None, out=True):
+        t = None if tokens is None else tokens.reshape(self.cfg["batch"], self.tpp).contiguous()
+        self._chk(lib().tsd_step_eager(self.h, _ptr(t), _ptr(self._next) if out else None))
+        return self._next if out else None
+
     def reset(self):
         self._chk(lib().tsd_reset(self.h))
 
@@ -228,6 +236,12 @@ class Model:
         out = self.torch.empty((n, self.cfg["batch"], self.tpp), dtype=self.torch.int32, device="cuda")
         self._chk(lib().tsd_get_tokens(self.h, first, n, _ptr(out)))
         return out
+
+    def time_kernel(self, kind, n_steps):
+        """(mean duration in us, launches per step) of one kernel kind over n_steps real steps."""
+        us, n = ctypes.c_float(), _I()
+        self._chk(lib().tsd_time_kernel(self.h, KERNEL_KINDS.get(kind, kind), n_steps, ctypes.byref(us), ctypes.byref(n)))
+        return us.value, n.value
 
     def load_kv(self, k, v, n_pos):
         self._chk(lib().tsd_load_kv(self.h, _ptr(k), _ptr(v), n_pos))

@@ -6,15 +6,20 @@
 // over a cache stored the way it is read — head-dim fastest, then position, then head).
 //
 // Mapping onto CDNA4:
-//   * the keys of a head are cut into tiles of 64 positions; one wave64 workgroup per
-//     (tile, head, row): lane j scores key j of its tile (its 128/256-byte key row is read with
-//     dwordx4 loads), while the whole V tile is fetched in the same burst, coalesced, and
-//     staged in LDS for the weighted sum;
-//   * each tile leaves an unnormalised partial (o, running max m, sum l) in log2 domain;
-//   * the last workgroup of a head to finish (an atomic ticket) merges the partials with the
-//     log-sum-exp rule  M = max m_i,  L = sum l_i 2^(m_i - M),  o = sum o_i 2^(m_i - M) / L,
-//     so the merge costs no extra launch;
-//   * the grid is sized for the full context and tiles past the current length exit at once,
+//   * the keys of a head are cut into chunks of 256 positions, one 4-wave workgroup per
+//     (chunk, head, row), one 64-key tile per wave;
+//   * lane layout: hd/8 lanes share a key and each holds 8 of its dims (16 bytes), so every load
+//     instruction reads 1 KB of consecutive K (or V) rows; the score is a DPP reduction inside
+//     the key's lane group and the weighted sum stays in VGPRs, reduced across key groups with a
+//     row rotation and the gfx950 row swaps at the end (no LDS per key);
+//   * log2-domain online softmax: each wave keeps (running max m, sum l, unnormalised o); the
+//     four waves merge in LDS and the workgroup writes one partial per chunk;
+//   * the partials of a head are merged with the log-sum-exp rule
+//       M = max m_i,  L = sum l_i 2^(m_i - M),  o = sum o_i 2^(m_i - M) / L
+//     by whoever consumes the attention output: in the decode step that is the prologue of the
+//     output-projection GEMV (so the merge costs neither a launch nor a device-wide fence);
+//     the standalone operator runs a small merge kernel;
+//   * the grid is sized for the full context and chunks past the current length exit at once,
 //     so one launch configuration serves every position (the step is replayed from a graph).
 #include <math.h>
 
@@ -24,130 +29,166 @@ namespace tsd {
 namespace {
 
 constexpr int TILE = 64;
+constexpr int NWAVE = 4;
+
+// sum over the lanes that hold the same dims of different keys (key groups of LPK lanes)
+template <int LPK>
+__device__ __forceinline__ float keygroup_sum(float v)
+{
+    if constexpr (LPK == 8) v += dpp_mov<0x128>(v);   // row_ror:8 (lane i and i^8 share dims)
+    v = swap16_sum(v);
+    v = swap32_sum(v);
+    return v;
+}
 
 template <int HD>
-__global__ __launch_bounds__(64) void k_attn(const AttnArgs a)
+__global__ __launch_bounds__(256) void k_attn(const AttnArgs a)
 {
-    constexpr int NV = HD / 8;          // uint4 per key row
-    constexpr int DPL = HD / 64;        // output dims per lane
-    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
-    const int n_keys = a.pos ? *a.pos + 1 + a.pos_add : a.n_keys;
-    const int n_split = (n_keys + TILE - 1) / TILE;
-    if (s >= n_split) return;
+    constexpr int LPK = HD / 8;           // lanes per key, 8 dims (16 bytes) each
+    constexpr int KPI = 64 / LPK;         // keys per load instruction (1 KB contiguous)
+    constexpr int R = TILE / KPI;         // load rounds per 64-key tile
+    constexpr int PS = HD + 4;            // partial stride (16-byte aligned)
+    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n_keys = a.pos ? ld_uniform(a.pos) + 1 + a.pos_add : a.n_keys;
+    if (s * ATTN_CHUNK >= n_keys) return;
     const int g = h / (a.H / a.Hkv);
+    const int k0 = s * ATTN_CHUNK + wave * TILE;          // first key of this wave's tile
+    const int c = lane % LPK, kq = lane / LPK;            // dims 8c..8c+7 of key k0 + r*KPI + kq
     const size_t head_off = ((size_t)b * a.Hkv + g) * a.n_ctx * HD;
-    const __half* Kt = a.k + head_off + (size_t)s * TILE * HD;
-    const __half* Vt = a.v + head_off + (size_t)s * TILE * HD;
-    const int nt = min(TILE, n_keys - s * TILE);   // keys in this tile
 
-    __shared__ float qs[HD];
-    __shared__ uint4 vt[TILE * NV];
-    __shared__ float ps[TILE];
+    __shared__ float ow[NWAVE][HD];
+    __shared__ float mw[NWAVE], lw[NWAVE];
 
-    // K row of this lane's key and the V tile, all in flight together
-    uint4 kr[NV], vr[NV];
+    // the tile's K and V, coalesced: round r reads keys k0 + r*KPI .. +KPI-1 (1 KB each);
+    // unconditional loads from clamped addresses, invalid keys masked after
+    // (clamped to the last valid key, so that a partial tile fetches nothing beyond it)
+    uint4 kr[R], vr[R];
+    const int klast = n_keys - 1;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        kr[i] = make_uint4(0u, 0u, 0u, 0u);
-        if (lane < nt) kr[i] = ((const uint4*)(Kt + (size_t)lane * HD))[i];
-        const int idx = i * 64 + lane;           // coalesced over the tile
-        vr[i] = make_uint4(0u, 0u, 0u, 0u);
-        if (idx / NV < nt) vr[i] = ((const uint4*)Vt)[idx];
+    for (int r = 0; r < R; ++r) {
+        const int key = min(k0 + r * KPI + kq, klast);
+        kr[r] = *(const uint4*)(a.k + head_off + (size_t)key * HD + c * 8);
+        vr[r] = *(const uint4*)(a.v + head_off + (size_t)key * HD + c * 8);
     }
-    // q, pre-scaled by log2(e)/sqrt(hd) so that the softmax runs on exp2
+    asm volatile("" ::: "memory");   // keep every load above: all of the tile in flight at once
+    __builtin_amdgcn_sched_barrier(0);
+    // this lane's 8 query dims, pre-scaled by log2(e)/sqrt(hd) so that the softmax runs on exp2
     const float qscale = 1.4426950408889634f / sqrtf((float)HD);
-    const float* qh = a.q + (size_t)b * a.ldq + (size_t)h * HD;
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) qs[lane + 64 * i] = qh[lane + 64 * i] * qscale;
-    __syncthreads();
+    const float4* qp = (const float4*)(a.q + (size_t)b * a.ldq + (size_t)h * HD + c * 8);
+    const float4 qa = qp[0], qb = qp[1];
+    const float q[8] = {qa.x * qscale, qa.y * qscale, qa.z * qscale, qa.w * qscale,
+                        qb.x * qscale, qb.y * qscale, qb.z * qscale, qb.w * qscale};
 
-    float acc = 0.f;
+    // scores: 8-dim partial dots, reduced over the key's LPK lanes
+    float sc[R];
+    float mloc = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const __half2* kh = (const __half2*)&kr[i];
-        const float4 q0 = *(const float4*)&qs[8 * i], q1 = *(const float4*)&qs[8 * i + 4];
-        float2 f;
-        f = __half22float2(kh[0]); acc = fmaf(f.x, q0.x, acc); acc = fmaf(f.y, q0.y, acc);
-        f = __half22float2(kh[1]); acc = fmaf(f.x, q0.z, acc); acc = fmaf(f.y, q0.w, acc);
-        f = __half22float2(kh[2]); acc = fmaf(f.x, q1.x, acc); acc = fmaf(f.y, q1.y, acc);
-        f = __half22float2(kh[3]); acc = fmaf(f.x, q1.z, acc); acc = fmaf(f.y, q1.w, acc);
+    for (int r = 0; r < R; ++r) {
+        const __half2* kh = (const __half2*)&kr[r];
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float2 f = __half22float2(kh[e]);
+            acc = fmaf(f.x, q[2 * e], acc);
+            acc = fmaf(f.y, q[2 * e + 1], acc);
+        }
+        acc = group_sum(acc, LPK);
+        sc[r] = k0 + r * KPI + kq < n_keys ? acc : -INFINITY;
+        mloc = fmaxf(mloc, sc[r]);
     }
-    const float sc = lane < nt ? acc : -INFINITY;
-    const float m = wave_max(sc);
-    const float p = lane < nt ? exp2f(sc - m) : 0.f;
-    const float l = wave_sum(p);
-
+    const float m = wave_max(mloc);
+    float lsum = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < NV; ++i) vt[i * 64 + lane] = vr[i];
-    ps[lane] = p;
-    __syncthreads();
-
-    float o[DPL];
+    for (int r = 0; r < R; ++r) {
+        const bool valid = k0 + r * KPI + kq < n_keys;
+        const float p = valid ? exp2f(sc[r] - m) : 0.f;
+        lsum += p;
+        const uint4 vv = valid ? vr[r] : make_uint4(0u, 0u, 0u, 0u);   // stale rows could hold NaN
+        const __half2* vh = (const __half2*)&vv;
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) o[i] = 0.f;
-    const __half* vh = (const __half*)vt;
-    for (int j = 0; j < nt; ++j) {
-        const float pj = ps[j];
-#pragma unroll
-        for (int i = 0; i < DPL; ++i) o[i] = fmaf(pj, __half2float(vh[j * HD + lane + 64 * i]), o[i]);
+        for (int e = 0; e < 4; ++e) {
+            const float2 f = __half22float2(vh[e]);
+            o[2 * e] = fmaf(p, f.x, o[2 * e]);
+            o[2 * e + 1] = fmaf(p, f.y, o[2 * e + 1]);
+        }
     }
-
-    const int max_split = (a.n_ctx + TILE - 1) / TILE;
-    float* part = a.part + (((size_t)b * a.H + h) * max_split + s) * (HD + 2);
+    // every key's p is held by its LPK lanes: the wave sum counts it LPK times (exact scaling)
+    const float l = wave_sum(lsum) * (1.0f / LPK);
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) part[lane + 64 * i] = o[i];
+    for (int e = 0; e < 8; ++e) o[e] = keygroup_sum<LPK>(o[e]);
+    if (kq == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ow[wave][c * 8 + e] = o[e];
+    }
     if (lane == 0) {
-        part[HD] = m;
-        part[HD + 1] = l;
+        mw[wave] = k0 < n_keys ? m : -INFINITY;
+        lw[wave] = l;
     }
-    if (n_split == 1) {
-        float* out = a.out + (size_t)b * a.ldo + (size_t)h * HD;
-#pragma unroll
-        for (int i = 0; i < DPL; ++i) out[lane + 64 * i] = o[i] / l;
-        return;
-    }
+    __syncthreads();
 
-    // the last tile of this head to finish merges all partials
-    __threadfence();
-    unsigned int ticket = 0;
-    if (lane == 0) ticket = atomicAdd(&a.cnt[b * a.H + h], 1u);
-    ticket = __shfl(ticket, 0, 64);
-    if (ticket != (unsigned)(n_split - 1)) return;
-    __threadfence();
-    const float* pb = a.part + ((size_t)b * a.H + h) * max_split * (HD + 2);
+    // merge the four tiles of this chunk into one partial
     float M = -INFINITY;
-    for (int t = 0; t < n_split; ++t) M = fmaxf(M, pb[(size_t)t * (HD + 2) + HD]);
-    float L = 0.f, O[DPL];
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) O[i] = 0.f;
-    for (int t = 0; t < n_split; ++t) {
-        const float* pt = pb + (size_t)t * (HD + 2);
-        const float wgt = exp2f(pt[HD] - M);
-        L = fmaf(pt[HD + 1], wgt, L);
+    for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, mw[w]);
+    float* part = a.part + (((size_t)b * a.H + h) * attn_max_split(a.n_ctx) + s) * PS;
+    for (int i = threadIdx.x; i < HD; i += 256) {
+        float acc = 0.f;
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) O[i] = fmaf(pt[lane + 64 * i], wgt, O[i]);
+        for (int w = 0; w < NWAVE; ++w) acc = fmaf(ow[w][i], exp2f(mw[w] - M), acc);
+        part[i] = acc;
     }
-    float* out = a.out + (size_t)b * a.ldo + (size_t)h * HD;
+    if (threadIdx.x == 0) {
+        float L = 0.f;
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) out[lane + 64 * i] = O[i] / L;
-    if (lane == 0) atomicExch(&a.cnt[b * a.H + h], 0u);
+        for (int w = 0; w < NWAVE; ++w) L = fmaf(lw[w], exp2f(mw[w] - M), L);
+        part[HD] = M;
+        part[HD + 1] = L;
+    }
+}
+
+// merge of the chunk partials for the standalone operator: one thread per output element
+__global__ void k_attn_merge(const float* __restrict__ part, float* __restrict__ out, int B, int H, int hd,
+                             int ldo, int max_split, int n_split)
+{
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= B * H * hd) return;
+    const int i = idx % hd, bh = idx / hd, b = bh / H, h = bh % H;
+    const int PS = hd + 4;
+    const float* pb = part + (size_t)bh * max_split * PS;
+    float M = -INFINITY;
+    for (int t = 0; t < n_split; ++t) M = fmaxf(M, pb[(size_t)t * PS + hd]);
+    float L = 0.f, O = 0.f;
+    for (int t = 0; t < n_split; ++t) {
+        const float wgt = exp2f(pb[(size_t)t * PS + hd] - M);
+        L = fmaf(pb[(size_t)t * PS + hd + 1], wgt, L);
+        O = fmaf(pb[(size_t)t * PS + i], wgt, O);
+    }
+    out[(size_t)b * ldo + (size_t)h * hd + i] = O / L;
 }
 
 }  // namespace
 
-int attn_max_split(int n_ctx) { return (n_ctx + TILE - 1) / TILE; }
-
 size_t attn_part_bytes(int B, int H, int n_ctx, int hd)
 {
-    return (size_t)B * H * attn_max_split(n_ctx) * (hd + 2) * sizeof(float);
+    return (size_t)B * H * attn_max_split(n_ctx) * (hd + 4) * sizeof(float);
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st)
 {
     dim3 grid(attn_max_split(a.n_ctx), a.H, a.B);
-    if (a.hd == 64) hipLaunchKernelGGL(k_attn<64>, grid, dim3(64), 0, st, a);
-    else if (a.hd == 128) hipLaunchKernelGGL(k_attn<128>, grid, dim3(64), 0, st, a);
+    if (a.hd == 64) hipLaunchKernelGGL(k_attn<64>, grid, dim3(256), 0, st, a);
+    else if (a.hd == 128) hipLaunchKernelGGL(k_attn<128>, grid, dim3(256), 0, st, a);
     else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_attention_merge(const AttnArgs& a, int n_keys, hipStream_t st)
+{
+    const int n = a.B * a.H * a.hd;
+    const int n_split = (n_keys + ATTN_CHUNK - 1) / ATTN_CHUNK;
+    hipLaunchKernelGGL(k_attn_merge, dim3((n + 255) / 256), dim3(256), 0, st, a.part, a.out, a.B, a.H, a.hd, a.ldo,
+                       attn_max_split(a.n_ctx), n_split);
     return hipGetLastError();
 }
 

@@ -95,7 +95,7 @@ __device__ __forceinline__ float swap32_sum(float v)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 #ifndef TSD_PERMLANE_SWAP
-#define TSD_PERMLANE_SWAP 0
+#define TSD_PERMLANE_SWAP 1
 #endif
 // sum over aligned groups of g lanes (g a power of two <= 64); every lane gets its group's sum
 __device__ __forceinline__ float group_sum(float v, int g)

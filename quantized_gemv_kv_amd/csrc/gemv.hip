@@ -23,184 +23,15 @@
 //     Q8_0 "+128" storage offset are applied through the slot's precomputed sum of x.
 #include <math.h>
 
-#include "kernels.h"
+#include "gemv_core.h"
 
 namespace tsd {
 namespace {
 
+using namespace core;
 constexpr int WG = 256;
 constexpr int NWAVE = WG / 64;
-constexpr int MAX_K = 4096;
 constexpr int NJ = MAX_K / 4 / WG;   // float4 of the input per thread
-
-// byte i of v as float (v_cvt_f32_ubyteN), written out because the compiler otherwise folds the
-// nibble masks into bit-field extracts and loses the one-instruction form
-template <int I>
-__device__ __forceinline__ float ubyte(uint32_t v)
-{
-    float r;
-    if constexpr (I == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(v));
-    else if constexpr (I == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(v));
-    else if constexpr (I == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(v));
-    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(v));
-    return r;
-}
-
-template <int F>
-__device__ __forceinline__ float slot_dot(const uint4 w, const float* __restrict__ x)
-{
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    if constexpr (F == FMT_Q4_0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t lo = ws[j] & 0x0F0F0F0Fu, hi = (ws[j] >> 4) & 0x0F0F0F0Fu;
-            float& al = (j & 1) ? a1 : a0;
-            float& ah = (j & 1) ? a3 : a2;
-            al = fmaf(ubyte<0>(lo), x[4 * j + 0], al);
-            ah = fmaf(ubyte<0>(hi), x[16 + 4 * j + 0], ah);
-            al = fmaf(ubyte<1>(lo), x[4 * j + 1], al);
-            ah = fmaf(ubyte<1>(hi), x[16 + 4 * j + 1], ah);
-            al = fmaf(ubyte<2>(lo), x[4 * j + 2], al);
-            ah = fmaf(ubyte<2>(hi), x[16 + 4 * j + 2], ah);
-            al = fmaf(ubyte<3>(lo), x[4 * j + 3], al);
-            ah = fmaf(ubyte<3>(hi), x[16 + 4 * j + 3], ah);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float& a = j == 0 ? a0 : j == 1 ? a1 : j == 2 ? a2 : a3;
-            a = fmaf(ubyte<0>(ws[j]), x[4 * j + 0], a);
-            a = fmaf(ubyte<1>(ws[j]), x[4 * j + 1], a);
-            a = fmaf(ubyte<2>(ws[j]), x[4 * j + 2], a);
-            a = fmaf(ubyte<3>(ws[j]), x[4 * j + 3], a);
-        }
-    }
-    return (a0 + a1) + (a2 + a3);
-}
-
-__device__ __forceinline__ float block_sum(float v, float* red)
-{
-    v = wave_sum(v);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    lds_barrier();
-    float r = 0.f;
-#pragma unroll
-    for (int i = 0; i < NWAVE; ++i) r += red[i];
-    lds_barrier();
-    return r;
-}
-
-__device__ __forceinline__ float4 f4add(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
-
-// x -> LDS, swizzled so that the lane owning slot s reads float4 e4 of its slice at
-// index e4 * slots_per_row + s (consecutive lanes, consecutive addresses)
-template <int E>
-__device__ __forceinline__ int swz(int k, int lpr) { return ((k % E) >> 2) * lpr + k / E; }
-
-// phase 1 of the prologue: issue the input loads (the embedding rows for the first layer) and
-// the norm's gain/bias
-template <int PRO>
-__device__ __forceinline__ void load_x(const ProArgs& p, const int K, float4 (&v)[NJ], float4 (&g)[NJ],
-                                       float4 (&bt)[NJ])
-{
-    constexpr bool EMB = PRO == PRO_LN_EMB || PRO == PRO_RMS_EMB;
-    constexpr bool LN = PRO == PRO_LN || PRO == PRO_LN_EMB;
-    const int nch = K / 4, t = threadIdx.x;
-    if constexpr (PRO != PRO_LOAD) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int c = t + j * WG;
-            g[j] = c < nch ? ((const float4*)p.g)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-            if constexpr (LN) bt[j] = c < nch ? ((const float4*)p.beta)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    }
-    if constexpr (EMB) {
-        const int prow = p.pos_tab ? ld_uniform(p.pos) : 0;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int c = t + j * WG;
-            float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (c < nch) {
-                for (int i = 0; i < p.n_emb; ++i) {
-                    int tk = ld_uniform(p.tok + i);
-                    tk = tk < 0 ? 0 : (tk >= p.tab_rows[i] ? p.tab_rows[i] - 1 : tk);
-                    a = f4add(a, ((const float4*)(p.tab[i] + (size_t)tk * K))[c]);
-                }
-                if (p.pos_tab) a = f4add(a, ((const float4*)(p.pos_tab + (size_t)prow * K))[c]);
-            }
-            v[j] = a;
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int c = t + j * WG;
-            v[j] = c < nch ? ((const float4*)p.src)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    }
-}
-
-// phase 2: norm (if any) and the swizzled store into LDS
-template <int F, int PRO>
-__device__ __forceinline__ void finish_x(const ProArgs& p, const int K, float4 (&v)[NJ], const float4 (&gg)[NJ],
-                                         const float4 (&bt)[NJ], float4* xl4, float* red)
-{
-    constexpr int E = FmtT<F>::E;
-    constexpr bool EMB = PRO == PRO_LN_EMB || PRO == PRO_RMS_EMB;
-    constexpr bool LN = PRO == PRO_LN || PRO == PRO_LN_EMB;
-    const int lpr = K / E, nch = K / 4, t = threadIdx.x;
-    if (EMB && blockIdx.x == 0) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-            if (t + j * WG < nch) ((float4*)p.x_out)[t + j * WG] = v[j];
-    }
-    if constexpr (PRO == PRO_LOAD) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int c = t + j * WG;
-            if (c < nch) xl4[swz<E>(4 * c, lpr)] = v[j];
-        }
-    } else {
-        const float invK = 1.0f / (float)K;
-        float mean = 0.f;
-        if constexpr (LN) {
-            float s = 0.f;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
-            mean = block_sum(s, red) * invK;
-        }
-        float q2 = 0.f;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            if (t + j * WG < nch) {
-                const float dx = v[j].x - mean, dy = v[j].y - mean, dz = v[j].z - mean, dw = v[j].w - mean;
-                q2 += (dx * dx + dy * dy) + (dz * dz + dw * dw);
-            }
-        }
-        const float r = 1.0f / sqrtf(block_sum(q2, red) * invK + p.eps);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int c = t + j * WG;
-            if (c < nch) {
-                const float4 g = gg[j];
-                float4 y = make_float4((v[j].x - mean) * r * g.x, (v[j].y - mean) * r * g.y,
-                                       (v[j].z - mean) * r * g.z, (v[j].w - mean) * r * g.w);
-                if constexpr (LN) y = f4add(y, bt[j]);
-                xl4[swz<E>(4 * c, lpr)] = y;
-            }
-        }
-    }
-    lds_barrier();
-}
-
-__device__ __forceinline__ float gelu_tanh(float x)
-{
-    // tanh form of GELU (Hendrycks & Gimpel): 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
-    const float c = 0.7978845608028654f;
-    return 0.5f * x * (1.0f + tanhf(c * fmaf(0.044715f * x, x * x, x)));
-}
-
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
 template <int EPI>
 __device__ __forceinline__ void epi_single(const EpiArgs& e, int row, float t, int pos)
@@ -270,7 +101,7 @@ __global__ __launch_bounds__(WG) void k_gemv(const PackedMat W, const ProArgs pa
     static_assert(!PAIR || NP % 2 == 0, "pair epilogues need an even number of rows per lane");
 
     __shared__ float4 xl4[MAX_K / 4];
-    __shared__ float red[NWAVE];
+    __shared__ float red[2 * NWAVE];
     __shared__ unsigned long long bkey[NWAVE];
 
     const int K = W.K, N = W.N, lpr = K / E;
@@ -284,12 +115,14 @@ __global__ __launch_bounds__(WG) void k_gemv(const PackedMat W, const ProArgs pa
 
     // 1. the input vector's loads first ...
     float4 xv[NJ], xg[NJ], xb[NJ];
-    load_x<PRO>(pa, K, xv, xg, xb);
+    AttnIn att;
+    if constexpr (PRO == PRO_ATTN) load_attn<WG>(pa, K, att);
+    else load_x<PRO, WG>(pa, K, xv, xg, xb);
 
     // 2. ... then every weight and raw scale of this lane, unconditionally (clamped address;
     //    out-of-range slots get a zero scale)
     uint4 w[NLOAD];
-    unsigned short sc_raw[NLOAD], sb_raw[NLOAD];
+    uint32_t sc_raw[NLOAD], sb_raw[NLOAD];   // 32-bit: 16-bit elements would be packed, forcing a wait per load
     bool ok[NLOAD];
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i) {
@@ -302,8 +135,12 @@ __global__ __launch_bounds__(WG) void k_gemv(const PackedMat W, const ProArgs pa
         if constexpr (F == FMT_AFF8) sb_raw[i] = __half_as_ushort(W.b[(size_t)rr * spr + ss / SPS]);
     }
 
-    // 3. norm / embedding into LDS (waits for the input only)
-    finish_x<F, PRO>(pa, K, xv, xg, xb, xl4, red);
+    asm volatile("" ::: "memory");   // keep every load above: all in flight before any wait
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 3. norm / embedding / attention merge into LDS (waits for the input only)
+    if constexpr (PRO == PRO_ATTN) finish_attn<WG>(pa, K, att, xv);
+    finish_x<F, PRO, WG>(pa, K, xv, xg, xb, xl4, red);
 
     // 4. this lane's x slices and their sums
     float xs[SPL][E];
@@ -334,12 +171,12 @@ __global__ __launch_bounds__(WG) void k_gemv(const PackedMat W, const ProArgs pa
         const int j = SPL == 1 ? 0 : i % SPL;
         const int r = SPL == 1 ? i : i / SPL;
         const float d = slot_dot<F>(w[i], xs[j]);
-        const float sc = ok[i] ? __half2float(__ushort_as_half(sc_raw[i])) : 0.f;
+        const float sc = ok[i] ? __half2float(__ushort_as_half((unsigned short)sc_raw[i])) : 0.f;
         float v;
         if constexpr (F == FMT_Q4_0) v = sc * fmaf(-8.f, sx[j], d);
         else if constexpr (F == FMT_Q8_0) v = sc * fmaf(-128.f, sx[j], d);
         else {
-            const float sb = ok[i] ? __half2float(__ushort_as_half(sb_raw[i])) : 0.f;
+            const float sb = ok[i] ? __half2float(__ushort_as_half((unsigned short)sb_raw[i])) : 0.f;
             v = fmaf(sc, d, sb * sx[j]);
         }
         part[r] += v;
@@ -372,9 +209,8 @@ __global__ __launch_bounds__(WG) void k_gemv(const PackedMat W, const ProArgs pa
         }
     }
     if constexpr (EPI == EPI_HEAD_ARGMAX) {
-        // greedy sampler fused into the head: workgroup max, one atomic per workgroup, and the
-        // last workgroup to finish publishes the id, appends it to the history and advances
-        // the position.  Key = (ordered logit, ~index): ties go to the lowest index.
+        // greedy sampler, first stage: the workgroup's best key (ordered logit, ~index: ties go
+        // to the lowest index); one plain store per workgroup, reduced by the finalize kernel
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) {
             const unsigned long long other = __shfl_xor(best, o, 64);
@@ -386,19 +222,7 @@ __global__ __launch_bounds__(WG) void k_gemv(const PackedMat W, const ProArgs pa
             unsigned long long m = bkey[0];
 #pragma unroll
             for (int i = 1; i < NWAVE; ++i) m = bkey[i] > m ? bkey[i] : m;
-            atomicMax(ea.best, m);
-            __threadfence();
-            const unsigned int t = atomicAdd(ea.ticket, 1u);
-            if (t == gridDim.x - 1) {
-                __threadfence();
-                const unsigned long long fin = atomicExch(ea.best, 0ull);
-                const int id = (int)(0xFFFFFFFFu - (uint32_t)(fin & 0xFFFFFFFFull));
-                const int p = *ea.pos_inc;
-                *ea.tok_out = id;
-                if (ea.hist) ea.hist[(size_t)p * ea.hist_stride] = id;
-                atomicExch(ea.ticket, 0u);
-                *ea.pos_inc = p + 1;
-            }
+            ea.best[blockIdx.x] = m;
         }
     }
 }
@@ -450,6 +274,7 @@ hipError_t go_fmt(int pro, int epi, const PackedMat& W, const ProArgs& pa, const
     if (pro == PRO_ && epi == EPI_) return go_spl<F, PRO_, EPI_>(W, pa, ea, st);
     TSD_CASE(PRO_LOAD, EPI_STORE)
     TSD_CASE(PRO_LOAD, EPI_RESID)
+    TSD_CASE(PRO_ATTN, EPI_RESID)
     TSD_CASE(PRO_LN, EPI_GELU)
     TSD_CASE(PRO_RMS, EPI_SWIGLU)
     TSD_CASE(PRO_LN, EPI_QKV)
@@ -513,10 +338,44 @@ __global__ void k_pack(int fmt, const uint8_t* __restrict__ src, int N, int K, u
 
 int gemv_rows_per_block(int fmt, int K, int) { return rows_per_block_impl(fmt, K); }
 
+namespace {
+__global__ __launch_bounds__(256) void k_argmax_finalize(const unsigned long long* __restrict__ best, int n, int* tok,
+                                                         int* hist, int hist_stride, int* pos)
+{
+    __shared__ unsigned long long bk[NWAVE];
+    unsigned long long m = 0ull;
+    for (int i = threadIdx.x; i < n; i += WG) m = best[i] > m ? best[i] : m;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const unsigned long long other = __shfl_xor(m, o, 64);
+        m = other > m ? other : m;
+    }
+    if ((threadIdx.x & 63) == 0) bk[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned long long b = bk[0];
+        for (int i = 1; i < NWAVE; ++i) b = bk[i] > b ? bk[i] : b;
+        const int id = (int)(0xFFFFFFFFu - (uint32_t)(b & 0xFFFFFFFFull));
+        const int p = *pos;
+        *tok = id;
+        if (hist) hist[(size_t)p * hist_stride] = id;
+        *pos = p + 1;
+    }
+}
+}  // namespace
+
+hipError_t launch_argmax_finalize(const unsigned long long* best, int n, int* tok, int* hist, int hist_stride, int* pos,
+                                  hipStream_t st)
+{
+    hipLaunchKernelGGL(k_argmax_finalize, dim3(1), dim3(WG), 0, st, best, n, tok, hist, hist_stride, pos);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemv(int fmt, int pro, int epi, const PackedMat& W, const ProArgs& pa, const EpiArgs& ea,
                        hipStream_t st)
 {
     if (W.K > MAX_K || !gemv_shape_ok(fmt, W.K) || W.N <= 0) return hipErrorInvalidValue;
+    if (pro == PRO_ATTN && W.K > 4 * NJA * WG) return hipErrorInvalidValue;
     switch (fmt) {
     case FMT_Q4_0: return go_fmt<FMT_Q4_0>(pro, epi, W, pa, ea, st);
     case FMT_Q8_0: return go_fmt<FMT_Q8_0>(pro, epi, W, pa, ea, st);

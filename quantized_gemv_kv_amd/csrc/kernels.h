@@ -7,8 +7,13 @@ namespace tsd {
 
 // ---- GEMV ------------------------------------------------------------------------------------
 // Prologue: how each workgroup builds its copy of the input vector x (into LDS).
-// PRO_*_EMB: the input is the embedding gather of the first layer instead of src
-enum ProKind : int { PRO_LOAD = 0, PRO_LN = 1, PRO_RMS = 2, PRO_LN_EMB = 3, PRO_RMS_EMB = 4 };
+// PRO_*_EMB: the input is the embedding gather of the first layer instead of src.
+// PRO_ATTN: the input is the attention output, merged here from the per-chunk partials.
+enum ProKind : int { PRO_LOAD = 0, PRO_LN = 1, PRO_RMS = 2, PRO_LN_EMB = 3, PRO_RMS_EMB = 4, PRO_ATTN = 5 };
+
+// attention works on chunks of ATTN_CHUNK cached positions (one workgroup each)
+constexpr int ATTN_CHUNK = 256;
+__host__ __device__ inline int attn_max_split(int n_ctx) { return (n_ctx + ATTN_CHUNK - 1) / ATTN_CHUNK; }
 
 struct ProArgs {
     const float* src;   // [NB][ld_src] input (ignored when n_emb > 0)
@@ -23,8 +28,12 @@ struct ProArgs {
     int tab_rows[16];
     const int* tok;
     const float* pos_tab;
-    const int* pos;
+    const int* pos;      // position (embedding row, or the attention length: pos + 1 + pos_add keys)
     float* x_out;
+    // attention partials [H][max_split][hd + 4] (o, m, l) for PRO_ATTN, one per chunk of
+    // a_chunk positions
+    const float* part;
+    int a_hd, a_max_split, a_chunk, pos_add;
 };
 
 enum EpiKind : int {
@@ -34,7 +43,7 @@ enum EpiKind : int {
     EPI_SWIGLU = 3,    // rows (2i, 2i+1) = (gate_i, up_i): y[i] = silu(gate) * up
     EPI_QKV = 4,       // rows [0,qr) -> q, [qr, qr+kr) -> K cache, rest -> V cache (+bias)
     EPI_QKV_ROPE = 5,  // as EPI_QKV, q/k rows stored in RoPE pairs (i, i+hd/2) and rotated
-    EPI_HEAD_ARGMAX = 6  // logits + greedy argmax, last workgroup publishes the id
+    EPI_HEAD_ARGMAX = 6  // logits + each workgroup's best (logit, index) key; a finalize kernel reduces
 };
 
 struct EpiArgs {
@@ -48,13 +57,8 @@ struct EpiArgs {
     __half* vc;
     const float2* rope;  // [n_ctx][hd/2] (cos, sin)
     const int* pos;      // device position (K/V slot, RoPE angle)
-    // head / argmax
+    // head / argmax: best key of workgroup i -> best[i]
     unsigned long long* best;
-    unsigned int* ticket;
-    int* tok_out;        // current-token slot (next step's input)
-    int* hist;           // history [n_ctx][hist_stride]
-    int hist_stride;
-    int* pos_inc;        // incremented by the last workgroup (end of step)
 };
 
 // Launch the fused GEMV y = epilogue(W . prologue(x)).  Returns hipSuccess or the launch error.
@@ -76,16 +80,22 @@ struct AttnArgs {
     const __half* v;
     float* out;          // [B][ldo] with head h at out + b*ldo + h*hd
     int ldo;
-    float* part;         // [B][H][max_split][hd + 2]
-    unsigned int* cnt;   // [B][H], zero between launches
+    float* part;         // [B][H][max_split][hd + 4]: unnormalised o, then m, l (log2 domain)
     int B, H, Hkv, hd, n_ctx;
     const int* pos;      // n_keys = *pos + 1 + pos_add when pos != null
     int pos_add;
     int n_keys;          // used when pos == null
 };
-int attn_max_split(int n_ctx);
 size_t attn_part_bytes(int B, int H, int n_ctx, int hd);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+// merges the partials into a.out (standalone operator only; the step merges in the O-proj)
+hipError_t launch_attention_merge(const AttnArgs& a, int n_keys, hipStream_t st);
+
+// ---- sampler finalize --------------------------------------------------------------------------
+// greedy: reduce the head's per-workgroup keys [n], publish the id into tok, append it to the
+// history at the current position and advance the position (one workgroup)
+hipError_t launch_argmax_finalize(const unsigned long long* best, int n, int* tok, int* hist, int hist_stride, int* pos,
+                                  hipStream_t st);
 
 // ---- small state kernels ---------------------------------------------------------------------
 hipError_t launch_copy_i32(int* dst, const int* src, int n, hipStream_t st);

@@ -46,6 +46,15 @@ struct Planner {
 
 }  // namespace
 
+// kernel kinds a timing probe can bracket
+enum { KIND_QKV = 0, KIND_ATTN = 1, KIND_OPROJ = 2, KIND_FC = 3, KIND_DOWN = 4, KIND_HEAD = 5, TSD_KERNEL_KINDS = 6 };
+
+struct Probe {
+    int kind = -1;
+    hipEvent_t* ev = nullptr;   // quadruples, consumed in launch order: empty bracket, kernel bracket
+    int next = 0;
+};
+
 struct tsd_model {
     tsd_config c{};
     tsd_sampling samp{};
@@ -65,11 +74,12 @@ struct tsd_model {
     size_t kv_layer_elems = 0;
     float *x = nullptr, *qkv = nullptr, *attn = nullptr, *h = nullptr, *logits = nullptr, *part = nullptr;
     float2* rope = nullptr;
-    unsigned int *acnt = nullptr, *ticket = nullptr;
-    unsigned long long* best = nullptr;
+    unsigned long long* best = nullptr;   // per head-workgroup best keys
     int *pos = nullptr, *tok = nullptr, *hist = nullptr, *dbg_pos = nullptr;
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
+    // timing probes: events around every launch of one kernel kind
+    std::vector<hipEvent_t> probe_ev[TSD_KERNEL_KINDS];
     int n_past = 0;
     std::string err;
 };
@@ -186,10 +196,9 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     const int qkv_rows = (H + 2 * Hk) * hd;
     // step state
     int* pos = (int*)P.take(4 * sizeof(int));
-    unsigned int* ticket = (unsigned int*)P.take(sizeof(unsigned int) * 4);
     int* tok = (int*)P.take(sizeof(int) * B * tpp);
-    unsigned long long* best = (unsigned long long*)P.take(sizeof(unsigned long long) * B * tpp);
-    unsigned int* acnt = (unsigned int*)P.take(sizeof(unsigned int) * B * H);
+    const int head_blocks = (c->vocab + gemv_rows_per_block(f, d, EPI_HEAD_ARGMAX) - 1) / gemv_rows_per_block(f, d, EPI_HEAD_ARGMAX);
+    unsigned long long* best = (unsigned long long*)P.take(sizeof(unsigned long long) * B * tpp * head_blocks);
     int* hist = (int*)P.take(sizeof(int) * (size_t)c->n_ctx * B * tpp);
     // activations
     float* x = (float*)P.take(sizeof(float) * B * d);
@@ -231,7 +240,7 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     __half* kc = (__half*)P.take(2 * kv_layer * c->n_layer);
     __half* vc = (__half*)P.take(2 * kv_layer * c->n_layer);
     if (m && base) {
-        m->pos = pos; m->dbg_pos = pos + 1; m->ticket = ticket; m->tok = tok; m->best = best; m->acnt = acnt;
+        m->pos = pos; m->dbg_pos = pos + 1; m->tok = tok; m->best = best;
         m->hist = hist; m->x = x; m->qkv = qkv; m->attn = attn; m->h = h; m->logits = logits; m->part = part;
         m->rope = rope; m->emb[0] = emb0; m->emb_rows[0] = c->vocab; m->wpe = wpe; m->L = Ls; m->nfg = nfg; m->nfb = nfb;
         m->head = head; m->kc = kc; m->vc = vc; m->kv_layer_elems = kv_layer; m->tpp = tpp; m->vmax = vmax;
@@ -242,7 +251,25 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
 
 // ---- the step's kernels --------------------------------------------------------------------
 
-hipError_t enqueue_layer(tsd_model* m, int l, hipStream_t st, const int* pos, bool embed)
+// brackets one launch with probe events when its kind is the probed one
+struct Bracket {
+    Probe* p;
+    hipStream_t st;
+    bool on;
+    Bracket(Probe* pr, int kind, hipStream_t s) : p(pr), st(s), on(pr && pr->kind == kind)
+    {
+        if (!on) return;
+        (void)hipEventRecord(p->ev[p->next], st);       // empty bracket: the cost of bracketing
+        (void)hipEventRecord(p->ev[p->next + 1], st);
+        (void)hipEventRecord(p->ev[p->next + 2], st);   // the kernel
+    }
+    ~Bracket()
+    {
+        if (on) (void)hipEventRecord(p->ev[p->next + 3], st), p->next += 4;
+    }
+};
+
+hipError_t enqueue_layer(tsd_model* m, int l, hipStream_t st, const int* pos, bool embed, Probe* pr = nullptr)
 {
     const tsd_config& c = m->c;
     const int d = c.d_model, H = c.n_head, Hk = c.n_kv_head, hd = c.head_dim;
@@ -279,7 +306,10 @@ hipError_t enqueue_layer(tsd_model* m, int l, hipStream_t st, const int* pos, bo
     ea.rope = m->rope;
     ea.pos = pos;
     const int pro = embed ? (gpt2 ? PRO_LN_EMB : PRO_RMS_EMB) : (gpt2 ? PRO_LN : PRO_RMS);
-    e = launch_gemv(c.wfmt, pro, gpt2 ? EPI_QKV : EPI_QKV_ROPE, w.qkv, pa, ea, st);
+    {
+        Bracket br(pr, KIND_QKV, st);
+        e = launch_gemv(c.wfmt, pro, gpt2 ? EPI_QKV : EPI_QKV_ROPE, w.qkv, pa, ea, st);
+    }
     if (e != hipSuccess) return e;
 
     // split-KV flash-decode over positions 0..pos
@@ -291,23 +321,32 @@ hipError_t enqueue_layer(tsd_model* m, int l, hipStream_t st, const int* pos, bo
     aa.out = m->attn;
     aa.ldo = H * hd;
     aa.part = m->part;
-    aa.cnt = m->acnt;
     aa.B = 1;
     aa.H = H;
     aa.Hkv = Hk;
     aa.hd = hd;
     aa.n_ctx = c.n_ctx;
     aa.pos = pos;
-    e = launch_attention(aa, st);
+    {
+        Bracket br(pr, KIND_ATTN, st);
+        e = launch_attention(aa, st);
+    }
     if (e != hipSuccess) return e;
 
-    // output projection + bias + residual
+    // merge of the attention partials + output projection + bias + residual
     ProArgs po{};
-    po.src = m->attn;
+    po.part = m->part;
+    po.a_hd = hd;
+    po.a_chunk = ATTN_CHUNK;
+    po.a_max_split = (c.n_ctx + po.a_chunk - 1) / po.a_chunk;
+    po.pos = pos;
     EpiArgs eo{};
     eo.y = m->x;
     eo.bias = w.bo;
-    e = launch_gemv(c.wfmt, PRO_LOAD, EPI_RESID, w.o, po, eo, st);
+    {
+        Bracket br(pr, KIND_OPROJ, st);
+        e = launch_gemv(c.wfmt, PRO_ATTN, EPI_RESID, w.o, po, eo, st);
+    }
     if (e != hipSuccess) return e;
 
     // norm + FC (+bias, GELU) or gate/up (SwiGLU)
@@ -319,7 +358,10 @@ hipError_t enqueue_layer(tsd_model* m, int l, hipStream_t st, const int* pos, bo
     EpiArgs ef{};
     ef.y = m->h;
     ef.bias = w.bfc;
-    e = launch_gemv(c.wfmt, gpt2 ? PRO_LN : PRO_RMS, gpt2 ? EPI_GELU : EPI_SWIGLU, w.fc, pf, ef, st);
+    {
+        Bracket br(pr, KIND_FC, st);
+        e = launch_gemv(c.wfmt, gpt2 ? PRO_LN : PRO_RMS, gpt2 ? EPI_GELU : EPI_SWIGLU, w.fc, pf, ef, st);
+    }
     if (e != hipSuccess) return e;
 
     // down projection + bias + residual
@@ -329,14 +371,15 @@ hipError_t enqueue_layer(tsd_model* m, int l, hipStream_t st, const int* pos, bo
     ed.y = m->x;
     ed.bias = w.bdown;
     (void)d;
+    Bracket br(pr, KIND_DOWN, st);
     return launch_gemv(c.wfmt, PRO_LOAD, EPI_RESID, w.down, pd, ed, st);
 }
 
-hipError_t enqueue_step(tsd_model* m, hipStream_t st)
+hipError_t enqueue_step(tsd_model* m, hipStream_t st, Probe* pr = nullptr)
 {
     const tsd_config& c = m->c;
     for (int l = 0; l < c.n_layer; ++l) {
-        hipError_t e = enqueue_layer(m, l, st, m->pos, l == 0);
+        hipError_t e = enqueue_layer(m, l, st, m->pos, l == 0, pr);
         if (e != hipSuccess) return e;
     }
     ProArgs ph{};
@@ -348,12 +391,12 @@ hipError_t enqueue_step(tsd_model* m, hipStream_t st)
     eh.y = m->logits;
     eh.ldy = c.vocab;
     eh.best = m->best;
-    eh.ticket = m->ticket;
-    eh.tok_out = m->tok;
-    eh.hist = m->hist;
-    eh.hist_stride = c.batch * m->tpp;
-    eh.pos_inc = m->pos;
-    return launch_gemv(c.wfmt, c.arch == TSD_ARCH_GPT2 ? PRO_LN : PRO_RMS, EPI_HEAD_ARGMAX, m->head, ph, eh, st);
+    Bracket br(pr, KIND_HEAD, st);
+    hipError_t e = launch_gemv(c.wfmt, c.arch == TSD_ARCH_GPT2 ? PRO_LN : PRO_RMS, EPI_HEAD_ARGMAX, m->head, ph, eh, st);
+    if (e != hipSuccess) return e;
+    const int nblk = (c.vocab + gemv_rows_per_block(c.wfmt, c.d_model, EPI_HEAD_ARGMAX) - 1) /
+                     gemv_rows_per_block(c.wfmt, c.d_model, EPI_HEAD_ARGMAX);
+    return launch_argmax_finalize(m->best, nblk, m->tok, m->hist, c.batch * m->tpp, m->pos, st);
 }
 
 tsd_status pack_weights(tsd_model* m, const tsd_tensor* w)
@@ -404,10 +447,7 @@ tsd_status init_state(tsd_model* m)
     const tsd_config& c = m->c;
     hipStream_t st = m->st;
     HIP_TRY(m, launch_fill_i32(m->pos, 0, 4, st), "init");
-    HIP_TRY(m, launch_fill_u32(m->ticket, 0u, 4, st), "init");
     HIP_TRY(m, launch_fill_i32(m->tok, 0, c.batch * m->tpp, st), "init");
-    HIP_TRY(m, launch_fill_u64(m->best, 0ull, c.batch * m->tpp, st), "init");
-    HIP_TRY(m, launch_fill_u32(m->acnt, 0u, c.batch * c.n_head, st), "init");
     HIP_TRY(m, launch_fill_i32(m->hist, 0, c.n_ctx * c.batch * m->tpp, st), "init");
     HIP_TRY(m, launch_fill_f32(m->logits, 0.f, (size_t)c.batch * m->tpp * m->vmax, st), "init");
     // RoPE table in fp64 on the host: angle = pos * theta^(-2i/hd)
@@ -423,13 +463,13 @@ tsd_status init_state(tsd_model* m)
     return TSD_OK;
 }
 
-tsd_status capture(tsd_model* m)
+tsd_status capture(tsd_model* m, Probe* pr, hipGraph_t* out_g, hipGraphExec_t* out_x)
 {
     hipStream_t cs;
     HIP_TRY(m, hipStreamCreateWithFlags(&cs, hipStreamNonBlocking), "capture stream");
     hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) { (void)hipStreamDestroy(cs); return hip_fail(m, e, "begin capture"); }
-    hipError_t le = enqueue_step(m, cs);
+    hipError_t le = enqueue_step(m, cs, pr);
     hipGraph_t g = nullptr;
     e = hipStreamEndCapture(cs, &g);
     (void)hipStreamDestroy(cs);
@@ -438,8 +478,8 @@ tsd_status capture(tsd_model* m)
     hipGraphExec_t x = nullptr;
     e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
     if (e != hipSuccess) { (void)hipGraphDestroy(g); return hip_fail(m, e, "instantiate"); }
-    m->graph = g;
-    m->exec = x;
+    *out_g = g;
+    *out_x = x;
     return TSD_OK;
 }
 
@@ -490,7 +530,7 @@ tsd_status tsd_model_create(const tsd_config* cfg, const tsd_tensor* weights, in
     plan(m, cfg, (uint8_t*)d_ws);
     tsd_status r = pack_weights(m, weights);
     if (r == TSD_OK) r = init_state(m);
-    if (r == TSD_OK) r = capture(m);
+    if (r == TSD_OK) r = capture(m, nullptr, &m->graph, &m->exec);
     if (r != TSD_OK) {
         g_err = m->err;
         tsd_model_destroy(m);
@@ -505,6 +545,8 @@ tsd_status tsd_model_destroy(tsd_model* m)
     if (!m) return TSD_OK;
     if (m->exec) (void)hipGraphExecDestroy(m->exec);
     if (m->graph) (void)hipGraphDestroy(m->graph);
+    for (int k = 0; k < TSD_KERNEL_KINDS; ++k)
+        for (hipEvent_t ev : m->probe_ev[k]) (void)hipEventDestroy(ev);
     delete m;
     return TSD_OK;
 }
@@ -518,6 +560,18 @@ tsd_status tsd_step(tsd_model* m, const int32_t* d_in, int32_t* d_next)
     const int nt = m->c.batch * m->tpp;
     if (d_in) HIP_TRY(m, launch_copy_i32(m->tok, d_in, nt, m->st), "set input");
     HIP_TRY(m, hipGraphLaunch(m->exec, m->st), "graph launch");
+    if (d_next) HIP_TRY(m, launch_copy_i32(d_next, m->tok, nt, m->st), "copy ids");
+    m->n_past += 1;
+    return TSD_OK;
+}
+
+tsd_status tsd_step_eager(tsd_model* m, const int32_t* d_in, int32_t* d_next)
+{
+    if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
+    if (m->n_past >= m->c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "context full");
+    const int nt = m->c.batch * m->tpp;
+    if (d_in) HIP_TRY(m, launch_copy_i32(m->tok, d_in, nt, m->st), "set input");
+    HIP_TRY(m, enqueue_step(m, m->st), "eager step");
     if (d_next) HIP_TRY(m, launch_copy_i32(d_next, m->tok, nt, m->st), "copy ids");
     m->n_past += 1;
     return TSD_OK;
@@ -610,6 +664,42 @@ tsd_status tsd_layer_forward(tsd_model* m, int layer, const float* d_x, int pos,
     return TSD_OK;
 }
 
+tsd_status tsd_time_kernel(tsd_model* m, int kind, int n_steps, float* avg_us, int* launches_per_step)
+{
+    if (!m || !avg_us) return fail(m, TSD_ERR_INVALID_ARGUMENT, "null argument");
+    if (kind < 0 || kind >= TSD_KERNEL_KINDS || n_steps <= 0) return fail(m, TSD_ERR_INVALID_ARGUMENT, "bad kind or step count");
+    if (m->n_past + n_steps > m->c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "probe steps do not fit the context");
+    const int pairs_max = kind == KIND_HEAD ? 1 : m->c.n_layer;
+    if (m->probe_ev[kind].empty()) {
+        m->probe_ev[kind].resize(4 * pairs_max);
+        for (auto& ev : m->probe_ev[kind]) HIP_TRY(m, hipEventCreate(&ev), "probe event");
+    }
+    // the step's kernels with their step arguments, enqueued directly on the model's stream
+    // (graph-recorded events carry no timestamps), events around every launch of `kind`
+    double total_ms = 0.0;
+    int pairs = 0;
+    for (int s = 0; s < n_steps; ++s) {
+        Probe pr;
+        pr.kind = kind;
+        pr.ev = m->probe_ev[kind].data();
+        HIP_TRY(m, enqueue_step(m, m->st, &pr), "probe step");
+        HIP_TRY(m, hipStreamSynchronize(m->st), "probe sync");
+        m->n_past += 1;
+        pairs = pr.next / 4;
+        if (pairs == 0) return fail(m, TSD_ERR_UNSUPPORTED, "this step has no kernel of that kind");
+        for (int i = 0; i < pairs; ++i) {
+            float e = 0.f, k = 0.f;
+            const hipEvent_t* ev = &m->probe_ev[kind][4 * i];
+            HIP_TRY(m, hipEventElapsedTime(&e, ev[0], ev[1]), "probe elapsed");
+            HIP_TRY(m, hipEventElapsedTime(&k, ev[2], ev[3]), "probe elapsed");
+            total_ms += k - e;
+        }
+    }
+    *avg_us = (float)(total_ms * 1e3 / ((double)n_steps * pairs));
+    if (launches_per_step) *launches_per_step = pairs;
+    return TSD_OK;
+}
+
 // ---- standalone operators -------------------------------------------------------------------
 
 tsd_status tsd_gemv_packed_bytes(int wfmt, int N, int K, size_t* out)
@@ -657,7 +747,7 @@ tsd_status tsd_attention_scratch_bytes(int B, int H, int n_ctx, int hd, size_t* 
 {
     if (!out || B <= 0 || H <= 0 || n_ctx <= 0 || (hd != 64 && hd != 128))
         return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "bad shape");
-    *out = align256((size_t)B * H * sizeof(unsigned int)) + attn_part_bytes(B, H, n_ctx, hd);
+    *out = attn_part_bytes(B, H, n_ctx, hd);
     return TSD_OK;
 }
 
@@ -671,9 +761,6 @@ tsd_status tsd_attention(const float* d_q, const uint16_t* d_k, const uint16_t* 
     if (!d_q || !d_k || !d_v || !d_out || !d_scratch) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null buffer");
     if (scratch_bytes < need) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "scratch too small");
     hipStream_t st = (hipStream_t)stream;
-    unsigned int* cnt = (unsigned int*)d_scratch;
-    hipError_t e = launch_fill_u32(cnt, 0u, B * H, st);
-    if (e != hipSuccess) return hip_fail(nullptr, e, "attention scratch");
     AttnArgs a{};
     a.q = d_q;
     a.ldq = H * hd;
@@ -681,8 +768,7 @@ tsd_status tsd_attention(const float* d_q, const uint16_t* d_k, const uint16_t* 
     a.v = (const __half*)d_v;
     a.out = d_out;
     a.ldo = H * hd;
-    a.part = (float*)((uint8_t*)d_scratch + align256((size_t)B * H * sizeof(unsigned int)));
-    a.cnt = cnt;
+    a.part = (float*)d_scratch;
     a.B = B;
     a.H = H;
     a.Hkv = Hkv;
@@ -690,7 +776,8 @@ tsd_status tsd_attention(const float* d_q, const uint16_t* d_k, const uint16_t* 
     a.n_ctx = n_ctx;
     a.pos = nullptr;
     a.n_keys = n_keys;
-    e = launch_attention(a, st);
+    hipError_t e = launch_attention(a, st);
+    if (e == hipSuccess) e = launch_attention_merge(a, n_keys, st);
     return e == hipSuccess ? TSD_OK : hip_fail(nullptr, e, "attention");
 }
 

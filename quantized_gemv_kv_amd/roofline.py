@@ -95,3 +95,37 @@ def mean_step_bytes(c, first_pos: int, n_steps: int) -> float:
 def gemv_bytes(fmt: str, N: int, K: int, B: int = 1, bias: bool = False) -> int:
     """One GEMV launch: the matrix, plus x [B][K] read and y [B][N] written in fp32."""
     return matrix_bytes(fmt, N, K) + 4 * B * (K + N) + (4 * N if bias else 0)
+
+
+ATTN_CHUNK = 256     # positions per attention workgroup (one partial each)
+
+
+def kernel_bytes(c, kind: str, pos: int) -> int:
+    """Algorithmic bytes of one launch of a step kernel at position pos (batch 1 GPT-2/Llama):
+    the matrix in its stored format, the fp32 vectors it reads (bias, norm gain/bias), the
+    activations it reads and writes, and for attention the fp16 keys/values of positions
+    0..pos plus the query and the per-chunk partials."""
+    d, f, H, Hk, hd, ff = c["d_model"], c["wfmt"], c["n_head"], c["n_kv_head"], c["head_dim"], c["d_ff"]
+    gpt2 = c["arch"] == "gpt2"
+    n_split = (pos + 1 + ATTN_CHUNK - 1) // ATTN_CHUNK
+    part = H * n_split * (hd + 4) * 4
+    qkv_rows = (H + 2 * Hk) * hd
+    if kind == "qkv":
+        return (matrix_bytes(f, qkv_rows, d) + 4 * d * (2 if gpt2 else 1) + (4 * qkv_rows if gpt2 else 0)
+                + 4 * d + 4 * H * hd + 2 * 2 * Hk * hd)
+    if kind == "attn":
+        return (pos + 1) * 2 * Hk * hd * 2 + 4 * H * hd + part
+    if kind == "oproj":
+        return matrix_bytes(f, d, H * hd) + (4 * d if gpt2 else 0) + part + 2 * 4 * d
+    if kind == "fc":
+        rows = ff if gpt2 else 2 * ff
+        return matrix_bytes(f, rows, d) + 4 * d * (2 if gpt2 else 1) + (4 * ff if gpt2 else 0) + 4 * d + 4 * ff
+    if kind == "down":
+        return matrix_bytes(f, d, ff) + (4 * d if gpt2 else 0) + 4 * ff + 2 * 4 * d
+    if kind == "head":
+        return matrix_bytes(f, c["vocab"], d) + 4 * d * (2 if gpt2 else 1) + 4 * d + 4 * c["vocab"]
+    raise KeyError(kind)
+
+
+def mean_kernel_bytes(c, kind: str, first_pos: int, n_steps: int) -> float:
+    return sum(kernel_bytes(c, kind, p) for p in range(first_pos, first_pos + n_steps)) / n_steps

@@ -1,0 +1,41 @@
+"""The C-ABI library loads and exports every function include/tsd.h declares; host-side
+validation works without a GPU (CPU only: no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_gemv_kv_amd import binding, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared():
+    src = open(os.path.join(ROOT, "include", "tsd.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tsd_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared()
+    assert len(names) >= 18
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert sorted(binding.EXPORTS) == names
+
+
+def test_workspace_sizes_and_validation():
+    c3 = synth.config("gpt2_medium_q4_0")
+    n = binding.tsd_workspace_bytes(c3)
+    # packed weights + fp16 cache + embedding tables fit in a few hundred MB
+    assert 300e6 < n < 340e6
+    for bad, status in [(dict(c3, d_model=1000), 1), (dict(c3, n_head=15), 1), (dict(c3, head_dim=32, n_head=32, n_kv_head=32), 2),
+                        (dict(c3, batch=2), 2), (dict(c3, wfmt="aff8", d_ff=4000), 1)]:
+        with pytest.raises(binding.TsdError) as e:
+            binding.tsd_workspace_bytes(bad)
+        assert e.value.status == status, bad
+    with pytest.raises(binding.TsdError):
+        binding.tsd_gemv_packed_bytes("q8_0", 8, 100)
+    assert binding.tsd_gemv_packed_bytes("q4_0", 3072, 1024) >= 3072 * 512 + 3072 * 32 * 2

@@ -6,9 +6,10 @@ fp32 norms/embeddings ~N(0, 0.02), fp16 KV cache; 256-token prefill, then greedy
 positions 256 .. 255+K, batch 1.  All inputs are seeded synthetic data.
 
 One step = one replay of the captured decode graph (every layer, the head and the greedy
-sampler).  W warm-up steps run first and the context is then truncated back to 256 positions,
-so the K timed steps cover exactly the positions of the configured run.  The timed region is
-bracketed by stream synchronisation and hipEvents recorded on the model's stream.
+sampler); by default the graph holds one persistent launch that runs the whole step.  W warm-up
+steps run first and the context is then truncated back to 256 positions, so the K timed steps
+cover exactly the positions of the configured run.  The timed region is bracketed by stream
+synchronisation and hipEvents recorded on the model's stream.
 
 Prints one JSON line.
 """
@@ -41,6 +42,8 @@ def parse():
                     help="enqueue each step kernel by kernel instead of replaying the graph (for counter "
                          "collection, which cannot follow graph launches); prefill is skipped: the cache "
                          "is filled with random values instead")
+    ap.add_argument("--launch-mode", default="persistent", choices=["persistent", "per_operator"],
+                    help="one persistent launch per step, or one launch per operator")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain fp32 device copy of this size (a known-traffic kernel for "
                          "scaling hardware byte counters)")
@@ -79,7 +82,7 @@ def main():
     import torch
     from quantized_gemv_kv_amd import Model, roofline, synth
 
-    cfg = synth.config(WORKLOAD)
+    cfg = dict(synth.config(WORKLOAD), launch_mode=args.launch_mode)
     K, W = args.steps, args.warmup
     if PROMPT + max(K, W) > cfg["n_ctx"]:
         print(f"steps/warmup exceed the {cfg['n_ctx']}-position context", file=sys.stderr)
@@ -115,20 +118,21 @@ def main():
     assert ids.min() >= 0 and ids.max() < cfg["vocab"], "sampled ids out of range"
 
     # dominant kernel: every kind timed inside real steps (event records around each launch on
-    # the model's stream), then the largest one re-timed over the timed region's positions
-    from quantized_gemv_kv_amd import TsdError
+    # the model's stream), then the largest one re-timed over the timed region's positions.
+    # With the persistent step there is one kind: the step kernel itself.
+    mode, n_wg = model.info()
+    kind_list = ("step",) if mode == "persistent" else ("qkv", "attn", "oproj", "fc", "down", "head")
     kinds = {}
     with torch.cuda.stream(stream):
-        for kind in ("qkv", "attn", "oproj", "fc", "down", "head"):
+        for kind in kind_list:
             model.truncate(PROMPT)
-            try:
-                kinds[kind] = model.time_kernel(kind, min(K, 100))
-            except TsdError:          # not a separate kernel in this step (fused)
-                pass
+            kinds[kind] = model.time_kernel(kind, min(K, 100))
         dom = max(kinds, key=lambda k: kinds[k][0] * kinds[k][1])
         model.truncate(PROMPT)
         dom_us, dom_n = model.time_kernel(dom, K)
-    dom_bytes = roofline.mean_kernel_bytes(cfg, dom, PROMPT, K)
+    model.synchronize()
+    dom_bytes = (roofline.mean_step_bytes(cfg, PROMPT, K) if dom == "step"
+                 else roofline.mean_kernel_bytes(cfg, dom, PROMPT, K))
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
 
     step_bytes = roofline.mean_step_bytes(cfg, PROMPT, K)
@@ -150,7 +154,7 @@ def main():
         "config": {"workload": "GPT-2-Medium-shaped 24-layer speech-token decoder, Q4_0, 256-token prefill then "
                                f"{K} greedy decode steps, batch 1",
                    "d_model": 1024, "n_layer": 24, "n_head": 16, "d_ff": 4096, "vocab": 8192,
-                   "prompt": PROMPT, "global_batch": 1},
+                   "prompt": PROMPT, "global_batch": 1, "launch_mode": mode, "workgroups": n_wg},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": roofline.HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / roofline.HBM_PEAK_GBS, "traffic": None,
                      "kernel": dom, "launch_us": dom_us, "launches_per_step": dom_n,

@@ -44,11 +44,22 @@ typedef enum {
     TSD_ERR_OUT_OF_MEMORY = 3,    /* host allocation failed */
     TSD_ERR_CONTEXT_FULL = 4,     /* n_past + n > n_ctx */
     TSD_ERR_HIP = 5,              /* a HIP runtime call failed; message has hipGetErrorString */
-    TSD_ERR_STATE = 6             /* call not valid in the current state */
+    TSD_ERR_STATE = 6,            /* call not valid in the current state */
+    TSD_ERR_TIMEOUT = 7           /* a bounded wait inside the persistent step gave up (see tsd_synchronize) */
 } tsd_status;
 
 typedef enum { TSD_ARCH_GPT2 = 0, TSD_ARCH_LLAMA = 1, TSD_ARCH_TALKER_CP = 2 } tsd_arch;
 typedef enum { TSD_W_Q4_0 = 0, TSD_W_Q8_0 = 1, TSD_W_AFFINE8_G64 = 2 } tsd_wfmt;
+
+/* How a step is launched.
+ *   PERSISTENT (default): batch-1 GPT2/LLAMA steps run as ONE launch of one workgroup per
+ *     compute unit that walks every layer, handing each phase's output to the next through
+ *     epoch-tagged 64-bit words in the workspace (no kernel boundary between operators; [J]
+ *     §3.14 and [F] §4 measure the per-kernel fixed cost this removes).  Shapes without a
+ *     persistent kernel fall back to PER_OPERATOR.
+ *   PER_OPERATOR: one launch per fused operator (QKV, attention, O-proj, FC, down, head,
+ *     sampler), all captured in the step graph. */
+typedef enum { TSD_LAUNCH_PERSISTENT = 0, TSD_LAUNCH_PER_OPERATOR = 1 } tsd_launch_mode;
 
 /* Model shape.
  *   GPT2 : GPT-2-Medium-shaped T3 ([J] §3.2): learned positions, pre-LayerNorm, fused QKV with
@@ -65,6 +76,9 @@ typedef struct {
     int32_t n_layer, d_model, n_head, n_kv_head, head_dim, d_ff, vocab, n_ctx, batch;
     float norm_eps, rope_theta;
     int32_t cp_n_layer, n_codebooks, cp_vocab; /* TALKER_CP only, else 0 */
+    int32_t launch_mode;  /* tsd_launch_mode */
+    int32_t n_workgroups; /* PERSISTENT: grid size, 0 = one per compute unit; more than can be
+                             resident at once is TSD_ERR_UNSUPPORTED */
 } tsd_config;
 
 /* Sampler ([J] §3.2: temperature then top-k, in that order).
@@ -129,7 +143,17 @@ tsd_status tsd_step(tsd_model* m, const int32_t* d_in, int32_t* d_next);
  * Results are identical to tsd_step. */
 tsd_status tsd_step_eager(tsd_model* m, const int32_t* d_in, int32_t* d_next);
 
-tsd_status tsd_reset(tsd_model* m);                     /* n_past = 0, history cleared */
+/* Wait for the model's stream, then report whether any persistent step since the last
+ * tsd_reset gave up on a bounded wait (TSD_ERR_TIMEOUT).  Such a step, and every step after it,
+ * leaves the ids, logits and cache unspecified; nothing hangs and no memory outside the
+ * workspace is touched.  Each wait in the step is limited to 20 ms. */
+tsd_status tsd_synchronize(tsd_model* m);
+
+tsd_status tsd_reset(tsd_model* m);                     /* n_past = 0, history and timeout cleared */
+/* The launch configuration in effect: *launch_mode is PERSISTENT only when the shape has a
+ * persistent kernel (else PER_OPERATOR), *n_workgroups its grid (0 for PER_OPERATOR).
+ * Either pointer may be NULL. */
+tsd_status tsd_model_info(const tsd_model* m, int32_t* launch_mode, int32_t* n_workgroups);
 tsd_status tsd_truncate(tsd_model* m, int n_past);      /* keep the first n_past positions */
 tsd_status tsd_n_past(const tsd_model* m, int* out);
 tsd_status tsd_model_destroy(tsd_model* m);
@@ -160,7 +184,9 @@ tsd_status tsd_layer_forward(tsd_model* m, int layer, const float* d_x, int pos,
  * in *avg_us and its launches per step.  Each bracket's own cost is calibrated by an empty
  * bracket recorded just before it and subtracted.  Kinds: 0 norm + fused
  * QKV GEMV, 1 attention, 2 attention merge + output projection, 3 norm + FC / gate-up,
- * 4 down projection, 5 final norm + head + sampler. */
+ * 4 down projection, 5 final norm + head + sampler (kinds 0-5: PER_OPERATOR launches),
+ * 6 the whole persistent step (PERSISTENT).  A kind the model does not launch is
+ * TSD_ERR_UNSUPPORTED. */
 tsd_status tsd_time_kernel(tsd_model* m, int kind, int n_steps, float* avg_us, int* launches_per_step);
 
 /* ---- standalone operators (same kernels as the step) ------------------------------------- */

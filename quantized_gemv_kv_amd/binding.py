@@ -17,14 +17,16 @@ LIB_PATH = os.path.join(HERE, "libtsd.so")
 ARCHS = {"gpt2": 0, "llama": 1, "talker_cp": 2}
 FORMATS = {"q4_0": 0, "q8_0": 1, "aff8": 2}
 STATUS = {0: "TSD_OK", 1: "TSD_ERR_INVALID_ARGUMENT", 2: "TSD_ERR_UNSUPPORTED", 3: "TSD_ERR_OUT_OF_MEMORY",
-          4: "TSD_ERR_CONTEXT_FULL", 5: "TSD_ERR_HIP", 6: "TSD_ERR_STATE"}
+          4: "TSD_ERR_CONTEXT_FULL", 5: "TSD_ERR_HIP", 6: "TSD_ERR_STATE", 7: "TSD_ERR_TIMEOUT"}
+LAUNCH_MODES = {"persistent": 0, "per_operator": 1}
 
 # symbols declared in include/tsd.h
 EXPORTS = ["tsd_workspace_bytes", "tsd_model_create", "tsd_prefill", "tsd_step", "tsd_step_eager", "tsd_reset", "tsd_truncate",
            "tsd_n_past", "tsd_model_destroy", "tsd_last_error", "tsd_get_logits", "tsd_get_tokens", "tsd_load_kv",
            "tsd_layer_forward", "tsd_gemv_packed_bytes", "tsd_gemv_pack", "tsd_gemv",
-           "tsd_attention_scratch_bytes", "tsd_attention", "tsd_time_kernel"]
-KERNEL_KINDS = {"qkv": 0, "attn": 1, "oproj": 2, "fc": 3, "down": 4, "head": 5}
+           "tsd_attention_scratch_bytes", "tsd_attention", "tsd_time_kernel", "tsd_synchronize",
+           "tsd_model_info"]
+KERNEL_KINDS = {"qkv": 0, "attn": 1, "oproj": 2, "fc": 3, "down": 4, "head": 5, "step": 6}
 
 
 class TsdError(RuntimeError):
@@ -37,7 +39,8 @@ class tsd_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("arch", "wfmt", "n_layer", "d_model", "n_head", "n_kv_head",
                                                "head_dim", "d_ff", "vocab", "n_ctx", "batch")] + [
         ("norm_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
-        ("cp_n_layer", ctypes.c_int32), ("n_codebooks", ctypes.c_int32), ("cp_vocab", ctypes.c_int32)]
+        ("cp_n_layer", ctypes.c_int32), ("n_codebooks", ctypes.c_int32), ("cp_vocab", ctypes.c_int32),
+        ("launch_mode", ctypes.c_int32), ("n_workgroups", ctypes.c_int32)]
 
 
 class tsd_sampling(ctypes.Structure):
@@ -82,6 +85,8 @@ def lib():
             "tsd_attention_scratch_bytes": [_I, _I, _I, _I, ctypes.POINTER(_SZ)],
             "tsd_attention": [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P],
             "tsd_time_kernel": [_P, _I, _I, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_I)],
+            "tsd_synchronize": [_P],
+            "tsd_model_info": [_P, _P, _P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -105,6 +110,8 @@ def make_config(cfg: dict) -> tsd_config:
             v = ARCHS[v] if isinstance(v, str) else v
         elif name == "wfmt":
             v = FORMATS[v] if isinstance(v, str) else v
+        elif name == "launch_mode":
+            v = LAUNCH_MODES[v] if isinstance(v, str) else v
         setattr(c, name, v)
     return c
 
@@ -225,7 +232,12 @@ class Model:
     def truncate(self, n):
         self._chk(lib().tsd_truncate(self.h, n))
 
+    def synchronize(self):
+        """Wait for the model's stream; TsdError(TSD_ERR_TIMEOUT) if a persistent step gave up."""
+        self._chk(lib().tsd_synchronize(self.h))
+
     def logits(self):
+        self.synchronize()
         B = self.cfg["batch"]
         out = self.torch.empty((B, self.tpp, self.vmax) if self.tpp > 1 else (B, self.vmax), dtype=self.torch.float32,
                                device="cuda")
@@ -233,9 +245,19 @@ class Model:
         return out
 
     def tokens(self, first, n):
+        self.synchronize()
         out = self.torch.empty((n, self.cfg["batch"], self.tpp), dtype=self.torch.int32, device="cuda")
         self._chk(lib().tsd_get_tokens(self.h, first, n, _ptr(out)))
         return out
+
+    def info(self):
+        """(launch mode name, workgroups) in effect (tsd_model_info)."""
+        mode, nwg = ctypes.c_int32(), ctypes.c_int32()
+        self._chk(lib().tsd_model_info(self.h, ctypes.byref(mode), ctypes.byref(nwg)))
+        return {v: k for k, v in LAUNCH_MODES.items()}[mode.value], nwg.value
+
+    def uses_persistent_step(self):
+        return self.info()[0] == "persistent"
 
     def time_kernel(self, kind, n_steps):
         """(mean duration in us, launches per step) of one kernel kind over n_steps real steps."""

@@ -125,6 +125,15 @@ __device__ __forceinline__ float wave_max(float v)
     return v;
 }
 
+// global-address-space views of a pointer: loads and stores through them are global_* (vector
+// memory counter only) even when the compiler cannot see where the pointer came from — flat
+// accesses would also count against the LDS counter and hold up LDS-only barriers
+#define TSD_GLOBAL __attribute__((address_space(1)))
+template <class T>
+__device__ __forceinline__ const TSD_GLOBAL T* glb(const T* p) { return (const TSD_GLOBAL T*)p; }
+template <class T>
+__device__ __forceinline__ TSD_GLOBAL T* glb(T* p) { return (TSD_GLOBAL T*)p; }
+
 // uniform load through the scalar cache (read only; the value was written by an earlier kernel)
 __device__ __forceinline__ int ld_uniform(const int* p)
 {

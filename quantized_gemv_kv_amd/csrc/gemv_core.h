@@ -1,5 +1,5 @@
-// gemv_core.h — device building blocks of the fused dequant GEMV, shared by the GEMV kernels
-// and the fused QKV + attention kernel (internal).  NT is the workgroup size in threads.
+// gemv_core.h — device building blocks of the fused dequant GEMV, shared by the per-operator
+// GEMV kernels and the persistent step (internal).  NT is the workgroup size in threads.
 #pragma once
 
 #include <math.h>
@@ -98,10 +98,6 @@ __device__ __forceinline__ float4 f4add(float4 a, float4 b) { return make_float4
 template <int E>
 __device__ __forceinline__ int swz(int k, int lpr) { return ((k % E) >> 2) * lpr + k / E; }
 
-// phase 1 of the prologue: issue the input loads (the embedding rows for the first layer) and
-// the norm's gain/bias
-// phase 1 of the prologue: issue the input loads (the embedding rows for the first layer) and
-// the norm's gain/bias
 // attention-merge prologue: per thread up to NJA float4 of the output, up to NSR chunks in
 // registers (longer contexts take a slower loop)
 constexpr int NJA = 2, NSR = 4;
@@ -172,6 +168,8 @@ __device__ __forceinline__ void finish_attn(const ProArgs& p, const int K, const
     }
 }
 
+// phase 1 of the prologue: issue the input loads (the embedding rows for the first layer) and
+// the norm's gain/bias
 template <int PRO, int NT>
 __device__ __forceinline__ void load_x(const ProArgs& p, const int K, float4 (&v)[MAX_K / 4 / NT],
                                        float4 (&g)[MAX_K / 4 / NT], float4 (&bt)[MAX_K / 4 / NT])
@@ -278,12 +276,13 @@ __device__ __forceinline__ void finish_x(const ProArgs& p, const int K, float4 (
 
 __device__ __forceinline__ float gelu_tanh(float x)
 {
-    // tanh form of GELU (Hendrycks & Gimpel): 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
-    const float c = 0.7978845608028654f;
-    return 0.5f * x * (1.0f + tanhf(c * fmaf(0.044715f * x, x * x, x)));
+    // tanh form of GELU (Hendrycks & Gimpel): 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3),
+    // evaluated as x / (1 + e^(-2u)) (the same function: 0.5 (1 + tanh u) is the logistic of 2u)
+    const float u = 0.7978845608028654f * fmaf(0.044715f * x, x * x, x);
+    return __fdividef(x, 1.0f + __expf(-2.0f * u));
 }
 
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+__device__ __forceinline__ float silu(float x) { return __fdividef(x, 1.0f + __expf(-x)); }
 
 }  // namespace core
 }  // namespace tsd

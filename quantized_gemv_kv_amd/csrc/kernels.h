@@ -97,6 +97,41 @@ hipError_t launch_attention_merge(const AttnArgs& a, int n_keys, hipStream_t st)
 hipError_t launch_argmax_finalize(const unsigned long long* best, int n, int* tok, int* hist, int hist_stride, int* pos,
                                   hipStream_t st);
 
+// ---- persistent decode step (step.hip) ---------------------------------------------------------
+// One launch runs the whole batch-1 step; phases hand data over through exchange words
+// (exchange.h).  Every layer's tensors sit at one fixed stride from the previous layer's in the
+// workspace, so the kernel derives them with scalar adds instead of loading a table.
+struct StepLayer {
+    PackedMat qkv, o, fc, down;               // fc: FC (GPT-2) or interleaved gate/up (Llama)
+    const float *n1g, *n1b, *n2g, *n2b;       // norm gains / LayerNorm biases (null for RMSNorm)
+    const float *bqkv, *bo, *bfc, *bdown;     // linear biases (null without)
+    __half *kc, *vc;                          // this layer's cache [Hkv][n_ctx][hd]
+};
+struct StepArgs {
+    StepLayer L0;                             // layer 0; layer l is layer 0 moved by l strides
+    long long lstride;                        // bytes between consecutive layers' weights and vectors
+    long long kvstride;                       // elements between consecutive layers' caches
+    int n_layer, H, Hk, n_ctx, vocab, max_split;
+    float eps;
+    const float* emb;                         // [vocab][d]
+    const float* wpe;                         // [n_ctx][d] learned positions, or null
+    const float *nfg, *nfb;                   // final norm
+    PackedMat head;
+    const float2* rope;                       // [n_ctx][hd/2] (cos, sin), Llama
+    int *pos, *tok, *hist;                    // step state (read at launch start, advanced at its end)
+    uint32_t* ctr;                            // launches completed: the epoch base
+    uint32_t* abort_word;                     // sticky: a wait gave up
+    float* logits;                            // [vocab]
+    // exchange words: QKV out, attention partials [H][max_split][hd+2], attention-block output
+    // (residual stream), MLP hidden, layer output (residual stream), per-workgroup argmax keys
+    uint64_t *x_qkv, *x_part, *x_attn, *x_h, *x_out, *x_best;
+    long long spin_limit;                     // ticks of the 100 MHz clock a wait may take
+};
+// the step kernel for a shape, or null when the shape has no instantiation
+const void* step_kernel_for(int fmt, int arch_llama, int d, int h, int hk, int hd, int ff, int vocab);
+// d_args: the arguments in device memory (read by every phase)
+hipError_t launch_step(const void* kernel, const StepArgs* d_args, int n_wg, hipStream_t st);
+
 // ---- small state kernels ---------------------------------------------------------------------
 hipError_t launch_copy_i32(int* dst, const int* src, int n, hipStream_t st);
 hipError_t launch_fill_i32(int* dst, int value, int n, hipStream_t st);

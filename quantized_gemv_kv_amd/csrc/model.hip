@@ -23,6 +23,8 @@ using namespace tsd;
 namespace {
 
 thread_local std::string g_err;
+constexpr int MAX_STEP_WG = 1024;          // workgroups of the persistent step, at most
+constexpr long long STEP_SPIN_LIMIT = 2000000;   // 20 ms of the 100 MHz clock per wait
 
 struct LayerW {
     PackedMat qkv, o, fc, down;            // fc = fc (GPT-2) or interleaved gate/up (Llama)
@@ -47,7 +49,7 @@ struct Planner {
 }  // namespace
 
 // kernel kinds a timing probe can bracket
-enum { KIND_QKV = 0, KIND_ATTN = 1, KIND_OPROJ = 2, KIND_FC = 3, KIND_DOWN = 4, KIND_HEAD = 5, TSD_KERNEL_KINDS = 6 };
+enum { KIND_QKV = 0, KIND_ATTN = 1, KIND_OPROJ = 2, KIND_FC = 3, KIND_DOWN = 4, KIND_HEAD = 5, KIND_STEP = 6, TSD_KERNEL_KINDS = 7 };
 
 struct Probe {
     int kind = -1;
@@ -76,6 +78,15 @@ struct tsd_model {
     float2* rope = nullptr;
     unsigned long long* best = nullptr;   // per head-workgroup best keys
     int *pos = nullptr, *tok = nullptr, *hist = nullptr, *dbg_pos = nullptr;
+    // persistent step: kernel (null: one launch per operator), grid, exchange state
+    const void* step_fn = nullptr;
+    int n_wg = 0;
+    StepArgs sa{};
+    StepArgs* d_sa = nullptr;         // sa in the workspace (the kernel reads it there)
+    uint64_t* xbuf = nullptr;
+    size_t xbuf_words = 0;
+    uint32_t* ctl = nullptr;          // [0] epoch base (launches), [1] abort word
+    uint64_t launches = 0, max_launches = 0;
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
     // timing probes: events around every launch of one kernel kind
@@ -239,12 +250,32 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     const size_t kv_layer = (size_t)B * Hk * c->n_ctx * hd;
     __half* kc = (__half*)P.take(2 * kv_layer * c->n_layer);
     __half* vc = (__half*)P.take(2 * kv_layer * c->n_layer);
+    // persistent step: layer table, control words, exchange words
+    uint32_t* ctl = (uint32_t*)P.take(sizeof(uint32_t) * 64);
+    StepArgs* d_sa = (StepArgs*)P.take(sizeof(StepArgs));
+    const size_t n_part = (size_t)H * attn_max_split(c->n_ctx) * (hd + 2);
+    const size_t xw[6] = {(size_t)qkv_rows, n_part, (size_t)d, (size_t)ff, (size_t)d, 2 * (size_t)MAX_STEP_WG};
+    size_t xtot = 0;
+    for (size_t n : xw) xtot += (n + 31) & ~(size_t)31;
+    uint64_t* xbuf = (uint64_t*)P.take(sizeof(uint64_t) * xtot);
     if (m && base) {
         m->pos = pos; m->dbg_pos = pos + 1; m->tok = tok; m->best = best;
         m->hist = hist; m->x = x; m->qkv = qkv; m->attn = attn; m->h = h; m->logits = logits; m->part = part;
         m->rope = rope; m->emb[0] = emb0; m->emb_rows[0] = c->vocab; m->wpe = wpe; m->L = Ls; m->nfg = nfg; m->nfb = nfb;
         m->head = head; m->kc = kc; m->vc = vc; m->kv_layer_elems = kv_layer; m->tpp = tpp; m->vmax = vmax;
         m->qkv_rows = qkv_rows;
+        m->ctl = ctl;
+        m->d_sa = d_sa;
+        m->xbuf = xbuf;
+        m->xbuf_words = xtot;
+        uint64_t* xp[6];
+        uint64_t* q = xbuf;
+        for (int i = 0; i < 6; ++i) {
+            xp[i] = q;
+            q += (xw[i] + 31) & ~(size_t)31;
+        }
+        StepArgs& a = m->sa;
+        a.x_qkv = xp[0]; a.x_part = xp[1]; a.x_attn = xp[2]; a.x_h = xp[3]; a.x_out = xp[4]; a.x_best = xp[5];
     }
     return align256(P.off);
 }
@@ -378,6 +409,10 @@ hipError_t enqueue_layer(tsd_model* m, int l, hipStream_t st, const int* pos, bo
 hipError_t enqueue_step(tsd_model* m, hipStream_t st, Probe* pr = nullptr)
 {
     const tsd_config& c = m->c;
+    if (m->step_fn) {
+        Bracket br(pr, KIND_STEP, st);
+        return launch_step(m->step_fn, m->d_sa, m->n_wg, st);
+    }
     for (int l = 0; l < c.n_layer; ++l) {
         hipError_t e = enqueue_layer(m, l, st, m->pos, l == 0, pr);
         if (e != hipSuccess) return e;
@@ -442,6 +477,88 @@ tsd_status pack_weights(tsd_model* m, const tsd_tensor* w)
     return TSD_OK;
 }
 
+// zero every exchange word and the control words: epochs restart at 1, nothing stale can match
+hipError_t reset_exchange(tsd_model* m)
+{
+    hipError_t e = launch_fill_u64((unsigned long long*)m->xbuf, 0ull, (int)m->xbuf_words, m->st);
+    if (e == hipSuccess) e = launch_fill_u32(m->ctl, 0u, 64, m->st);
+    m->launches = 0;
+    return e;
+}
+
+// choose the persistent step kernel and its grid; leaves step_fn null for one launch per operator
+tsd_status setup_step(tsd_model* m)
+{
+    const tsd_config& c = m->c;
+    if (c.launch_mode == TSD_LAUNCH_PER_OPERATOR) return TSD_OK;
+    if (c.launch_mode != TSD_LAUNCH_PERSISTENT) return fail(m, TSD_ERR_INVALID_ARGUMENT, "unknown launch_mode");
+    m->step_fn = step_kernel_for(c.wfmt, c.arch == TSD_ARCH_LLAMA, c.d_model, c.n_head, c.n_kv_head, c.head_dim, c.d_ff,
+                                 c.vocab);
+    if (!m->step_fn) return TSD_OK;   // this shape runs one launch per operator
+    int dev = 0, n_cu = 0, per_cu = 0;
+    HIP_TRY(m, hipGetDevice(&dev), "device");
+    HIP_TRY(m, hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev), "CU count");
+    HIP_TRY(m, hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, m->step_fn, 256, 0), "occupancy");
+    // every workgroup must be resident at once (they wait on each other): at most what fits
+    const int fit = n_cu * per_cu;
+    int g = c.n_workgroups > 0 ? c.n_workgroups : n_cu;
+    if (g > fit || g > MAX_STEP_WG)
+        return fail(m, TSD_ERR_UNSUPPORTED, "n_workgroups " + std::to_string(g) + " exceeds the " +
+                    std::to_string(fit < MAX_STEP_WG ? fit : MAX_STEP_WG) + " that can be resident at once");
+    // every layer at one stride from the previous (the planner lays layers out identically)
+    auto lay = [&](int l) {
+        const LayerW& w = m->L[l];
+        StepLayer t;
+        t.qkv = w.qkv; t.o = w.o; t.fc = w.fc; t.down = w.down;
+        t.n1g = w.n1g; t.n1b = w.n1b; t.n2g = w.n2g; t.n2b = w.n2b;
+        t.bqkv = w.bqkv; t.bo = w.bo; t.bfc = w.bfc; t.bdown = w.bdown;
+        t.kc = m->kc + m->kv_layer_elems * l;
+        t.vc = m->vc + m->kv_layer_elems * l;
+        return t;
+    };
+    const StepLayer L0 = lay(0);
+    const long long stride = c.n_layer > 1 ? (const char*)m->L[1].qkv.q - (const char*)m->L[0].qkv.q : 0;
+    auto same = [&](const void* p0, const void* pl, int l) {
+        return p0 ? (const char*)pl == (const char*)p0 + stride * l : pl == nullptr;
+    };
+    for (int l = 1; l < c.n_layer; ++l) {
+        const StepLayer t = lay(l);
+        const void* a0[] = {L0.qkv.q, L0.qkv.s, L0.qkv.b, L0.o.q, L0.o.s, L0.o.b, L0.fc.q, L0.fc.s, L0.fc.b, L0.down.q,
+                            L0.down.s, L0.down.b, L0.n1g, L0.n1b, L0.n2g, L0.n2b, L0.bqkv, L0.bo, L0.bfc, L0.bdown};
+        const void* al[] = {t.qkv.q, t.qkv.s, t.qkv.b, t.o.q, t.o.s, t.o.b, t.fc.q, t.fc.s, t.fc.b, t.down.q,
+                            t.down.s, t.down.b, t.n1g, t.n1b, t.n2g, t.n2b, t.bqkv, t.bo, t.bfc, t.bdown};
+        for (size_t i = 0; i < sizeof(a0) / sizeof(a0[0]); ++i)
+            if (!same(a0[i], al[i], l)) return fail(m, TSD_ERR_STATE, "layer tensors are not at a uniform stride");
+    }
+    m->n_wg = g;
+    StepArgs& a = m->sa;
+    a.L0 = L0;
+    a.lstride = stride;
+    a.kvstride = (long long)m->kv_layer_elems;
+    a.n_layer = c.n_layer; a.H = c.n_head; a.Hk = c.n_kv_head; a.n_ctx = c.n_ctx; a.vocab = c.vocab;
+    a.max_split = attn_max_split(c.n_ctx);
+    a.eps = c.norm_eps;
+    a.emb = m->emb[0]; a.wpe = m->wpe; a.nfg = m->nfg; a.nfb = m->nfb; a.head = m->head; a.rope = m->rope;
+    a.pos = m->pos; a.tok = m->tok; a.hist = m->hist; a.ctr = m->ctl; a.abort_word = m->ctl + 1;
+    a.logits = m->logits;
+    a.spin_limit = STEP_SPIN_LIMIT;
+    const uint64_t nph = 5ull * c.n_layer + 1ull;
+    m->max_launches = (0xFFFFFFF0ull - nph) / nph;
+    return TSD_OK;
+}
+
+// before each persistent launch: restart the epochs before they would wrap
+hipError_t before_launch(tsd_model* m)
+{
+    if (!m->step_fn) return hipSuccess;
+    if (m->launches >= m->max_launches) {
+        hipError_t e = reset_exchange(m);
+        if (e != hipSuccess) return e;
+    }
+    m->launches += 1;
+    return hipSuccess;
+}
+
 tsd_status init_state(tsd_model* m)
 {
     const tsd_config& c = m->c;
@@ -459,6 +576,11 @@ tsd_status init_state(tsd_model* m)
             tab[(size_t)p * half + i] = make_float2((float)cos(a), (float)sin(a));
         }
     HIP_TRY(m, hipMemcpyAsync(m->rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice, st), "rope table");
+    if (m->step_fn) {
+        HIP_TRY(m, hipMemcpyAsync(m->d_sa, &m->sa, sizeof(StepArgs), hipMemcpyHostToDevice, st), "step arguments");
+        HIP_TRY(m, hipStreamSynchronize(st), "step arguments");
+    }
+    HIP_TRY(m, reset_exchange(m), "exchange init");
     HIP_TRY(m, hipStreamSynchronize(st), "create sync");
     return TSD_OK;
 }
@@ -528,7 +650,8 @@ tsd_status tsd_model_create(const tsd_config* cfg, const tsd_tensor* weights, in
     m->ws = (uint8_t*)d_ws;
     m->ws_bytes = ws_bytes;
     plan(m, cfg, (uint8_t*)d_ws);
-    tsd_status r = pack_weights(m, weights);
+    tsd_status r = setup_step(m);
+    if (r == TSD_OK) r = pack_weights(m, weights);
     if (r == TSD_OK) r = init_state(m);
     if (r == TSD_OK) r = capture(m, nullptr, &m->graph, &m->exec);
     if (r != TSD_OK) {
@@ -559,6 +682,7 @@ tsd_status tsd_step(tsd_model* m, const int32_t* d_in, int32_t* d_next)
     if (m->n_past >= m->c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "context full");
     const int nt = m->c.batch * m->tpp;
     if (d_in) HIP_TRY(m, launch_copy_i32(m->tok, d_in, nt, m->st), "set input");
+    HIP_TRY(m, before_launch(m), "exchange restart");
     HIP_TRY(m, hipGraphLaunch(m->exec, m->st), "graph launch");
     if (d_next) HIP_TRY(m, launch_copy_i32(d_next, m->tok, nt, m->st), "copy ids");
     m->n_past += 1;
@@ -571,6 +695,7 @@ tsd_status tsd_step_eager(tsd_model* m, const int32_t* d_in, int32_t* d_next)
     if (m->n_past >= m->c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "context full");
     const int nt = m->c.batch * m->tpp;
     if (d_in) HIP_TRY(m, launch_copy_i32(m->tok, d_in, nt, m->st), "set input");
+    HIP_TRY(m, before_launch(m), "exchange restart");
     HIP_TRY(m, enqueue_step(m, m->st), "eager step");
     if (d_next) HIP_TRY(m, launch_copy_i32(d_next, m->tok, nt, m->st), "copy ids");
     m->n_past += 1;
@@ -585,10 +710,32 @@ tsd_status tsd_prefill(tsd_model* m, const int32_t* d_tokens, int n, int32_t* d_
     const int nt = m->c.batch * m->tpp;
     for (int t = 0; t < n; ++t) {
         HIP_TRY(m, launch_copy_i32(m->tok, d_tokens + (size_t)t * nt, nt, m->st), "set input");
+        HIP_TRY(m, before_launch(m), "exchange restart");
         HIP_TRY(m, hipGraphLaunch(m->exec, m->st), "graph launch");
         m->n_past += 1;
     }
     if (d_next) HIP_TRY(m, launch_copy_i32(d_next, m->tok, nt, m->st), "copy ids");
+    return TSD_OK;
+}
+
+tsd_status tsd_synchronize(tsd_model* m)
+{
+    if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
+    HIP_TRY(m, hipStreamSynchronize(m->st), "stream sync");
+    if (m->step_fn) {
+        uint32_t ab = 0;
+        HIP_TRY(m, hipMemcpy(&ab, m->ctl + 1, sizeof(ab), hipMemcpyDeviceToHost), "read abort word");
+        if (ab) return fail(m, TSD_ERR_TIMEOUT, "a wait inside the persistent step timed out; the steps since are void "
+                                                "(tsd_reset clears the state)");
+    }
+    return TSD_OK;
+}
+
+tsd_status tsd_model_info(const tsd_model* m, int32_t* launch_mode, int32_t* n_workgroups)
+{
+    if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
+    if (launch_mode) *launch_mode = m->step_fn ? TSD_LAUNCH_PERSISTENT : TSD_LAUNCH_PER_OPERATOR;
+    if (n_workgroups) *n_workgroups = m->step_fn ? m->n_wg : 0;
     return TSD_OK;
 }
 
@@ -597,6 +744,7 @@ tsd_status tsd_reset(tsd_model* m)
     if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
     HIP_TRY(m, launch_fill_i32(m->pos, 0, 1, m->st), "reset");
     HIP_TRY(m, launch_fill_i32(m->hist, 0, m->c.n_ctx * m->c.batch * m->tpp, m->st), "reset");
+    if (m->step_fn) HIP_TRY(m, reset_exchange(m), "reset");
     m->n_past = 0;
     return TSD_OK;
 }
@@ -669,7 +817,9 @@ tsd_status tsd_time_kernel(tsd_model* m, int kind, int n_steps, float* avg_us, i
     if (!m || !avg_us) return fail(m, TSD_ERR_INVALID_ARGUMENT, "null argument");
     if (kind < 0 || kind >= TSD_KERNEL_KINDS || n_steps <= 0) return fail(m, TSD_ERR_INVALID_ARGUMENT, "bad kind or step count");
     if (m->n_past + n_steps > m->c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "probe steps do not fit the context");
-    const int pairs_max = kind == KIND_HEAD ? 1 : m->c.n_layer;
+    if ((kind == KIND_STEP) != (m->step_fn != nullptr))
+        return fail(m, TSD_ERR_UNSUPPORTED, "this model does not launch a kernel of that kind");
+    const int pairs_max = (kind == KIND_HEAD || kind == KIND_STEP) ? 1 : m->c.n_layer;
     if (m->probe_ev[kind].empty()) {
         m->probe_ev[kind].resize(4 * pairs_max);
         for (auto& ev : m->probe_ev[kind]) HIP_TRY(m, hipEventCreate(&ev), "probe event");
@@ -682,6 +832,7 @@ tsd_status tsd_time_kernel(tsd_model* m, int kind, int n_steps, float* avg_us, i
         Probe pr;
         pr.kind = kind;
         pr.ev = m->probe_ev[kind].data();
+        HIP_TRY(m, before_launch(m), "exchange restart");
         HIP_TRY(m, enqueue_step(m, m->st, &pr), "probe step");
         HIP_TRY(m, hipStreamSynchronize(m->st), "probe sync");
         m->n_past += 1;

@@ -1,0 +1,874 @@
+// step.hip — the whole batch-1 decode step as one persistent launch.
+//
+// What it computes is the step of the per-operator kernels (gemv.hip, attention.hip): for each
+// layer norm -> fused QKV (+bias | +RoPE) -> K/V append -> split-KV attention -> output
+// projection + residual -> norm -> FC + GELU | gate/up + SwiGLU -> down projection + residual,
+// then the final norm, the head and the greedy sampler ("Chatterbox -> ggml Port: Development
+// Journal", §3.2 the T3 step and §3.19 the Llama-shaped variant; "Every Frame Is a Memory Read",
+// §3 and §4: the step is a chain of small matvecs whose cost is the bytes they read).
+//
+// Why one launch.  At batch 1 every operator moves only 0.5-5 MB, which the GPU streams in
+// about a microsecond, while a kernel boundary inside a graph costs about as much again and the
+// ramp of each new grid adds more; the journal measures the same effect as a step that is
+// "dispatch-bound" (§3.14) and the frame post as a fixed cost per kernel (§4).  Here the grid
+// is launched once, one workgroup per compute unit, and walks the step's phases in order:
+//   * a phase's work is cut into tiles (rows of a matrix, or one head x 256-key chunk of the
+//     cache); workgroup w takes tile w (and w + G, ... when there are more tiles);
+//   * a phase's output is published as exchange words (exchange.h) carrying the phase's epoch,
+//     and the next phase's workgroups poll exactly the words they need — there is no grid-wide
+//     barrier, only data dependencies, each resolved by one round trip to the memory-side cache;
+//   * each tile issues its weight, scale, bias and residual loads before it polls its input, so
+//     they are in flight while the previous phase finishes elsewhere;
+//   * the new token's key and value travel through the exchange (the attention of the same
+//     launch reads them from there); the cache rows are written with plain stores and are read
+//     by later launches, after the kernel boundary has made them visible on every XCD;
+//   * the position, the input token and the epoch base are read at the start of the launch,
+//     and workgroup 0 publishes the sampled id, the next position and the next epoch base at
+//     the end, after every other workgroup has handed it its part of the argmax.
+// The model's shape is a template parameter: every index, trip count and tile size is a
+// compile-time constant, which keeps the per-phase instruction count (the step's critical path
+// at batch 1) small.
+// Epochs: launch n uses n * P + 1 .. n * P + P for its P = 5 * n_layer + 1 phases.
+#include <math.h>
+
+#include "exchange.h"
+#include "gemv_core.h"
+
+namespace tsd {
+namespace {
+
+using namespace core;
+constexpr int NT = 256;
+constexpr int NWAVE = NT / 64;
+constexpr int KTILE = 64;    // keys per wave in the attention phase (4 waves: one 256-key chunk)
+constexpr int SG = 4;        // attention chunks merged per exchange round in the O-proj input
+
+enum { A_GPT2 = 0, A_LLAMA = 1 };
+enum { IN_XCHG = 0, IN_NORM = 1, IN_EMB_NORM = 2, IN_ATTN = 3 };
+enum { OUT_QKV = 0, OUT_QKV_ROPE = 1, OUT_RESID = 2, OUT_GELU = 3, OUT_SWIGLU = 4, OUT_HEAD = 5 };
+
+constexpr int slices_for(int fmt_e, int K) { return K / fmt_e > 64 ? K / fmt_e / 64 : 1; }
+
+// the model shape
+template <int F_, int A_, int D_, int H_, int HK_, int HD_, int FF_, int V_>
+struct Shape {
+    static constexpr int F = F_, ARCH = A_, D = D_, H = H_, HK = HK_, HD = HD_, FF = FF_, V = V_;
+    static constexpr bool GPT2 = A_ == A_GPT2;
+    static constexpr int QD = H * HD, KD = HK * HD, QKV = QD + 2 * KD;
+    static constexpr int FCN = GPT2 ? FF : 2 * FF;   // FC rows (gate/up interleaved for Llama)
+    static constexpr int E = FmtT<F>::E;
+    // loads per lane of each phase: two row slots (or, for rows wider than a wave, one row per
+    // wave) for the K = d_model matrices, doubled for the interleaved gate/up rows and the head
+    static constexpr int NL_D = F == FMT_Q4_0 ? 2 : 4;
+    static constexpr int NL_FC = GPT2 ? NL_D : 2 * NL_D;
+    static constexpr int NL_HEAD = F == FMT_Q4_0 ? 4 : 8;
+    static constexpr int NL_O = slices_for(E, QD) == 1 ? 2 : slices_for(E, QD);
+    static constexpr int NL_F = slices_for(E, FF) == 1 ? 2 : slices_for(E, FF);
+    static_assert(QD <= MAX_K && D <= MAX_K && FF <= MAX_K, "reduction dimension held in LDS");
+    static_assert(slices_for(E, D) == 1, "d_model rows fit one wave");
+};
+
+// geometry of one GEMV phase: K-long rows, N of them, NL 16-byte loads per lane
+template <int F, int K, int N, int NL>
+struct Geo {
+    static constexpr int E = FmtT<F>::E, SPS = FmtT<F>::SLOTS_PER_SCALE, GS = FmtT<F>::SCALE_GROUP;
+    static constexpr int LPR = K / E;                       // 16-byte slots per row
+    static constexpr bool WIDE = LPR > 64;                  // a row spans several loads per lane
+    static constexpr int SPL = WIDE ? LPR / 64 : 1;         // loads per lane per row
+    static constexpr int RG = WIDE ? 1 : 64 / LPR;          // row groups per wave
+    static constexpr int NP = WIDE ? NL / SPL : NL;         // rows per lane
+    static constexpr int RPW = NP * RG;                     // rows per wave
+    static constexpr int RPT = NWAVE * RPW;                 // rows per tile
+    static constexpr int TILES = (N + RPT - 1) / RPT;
+    static constexpr int GW = WIDE ? 64 : LPR;              // lanes reduced per row
+    static constexpr size_t RB = F == FMT_Q4_0 ? (size_t)K / 2 : (size_t)K;   // payload bytes per row
+    static constexpr int SPR = K / GS;                      // scales per row
+    static_assert(K % E == 0 && (WIDE ? LPR % 64 == 0 : 64 % LPR == 0), "lanes map onto slots exactly");
+    static_assert(!WIDE || NL % SPL == 0, "whole rows per wave");
+};
+
+struct Smem {
+    float* xl;       // [MAX_K] phase input, swizzled for the weight format
+    float* red;      // [2 * NWAVE]
+    float* ml;       // [H * SG * 2] attention (m, l) of a group of chunks
+    int* abort;      // a wait of this workgroup timed out
+};
+
+struct Ctx {
+    int pos, tok, n_keys, S;
+    long long limit;
+};
+
+// ---- phase input -----------------------------------------------------------------------------
+// x[0..K) into LDS at the swizzled place of format F.  Thread t owns elements k = t + NT*j,
+// j < ceil(K / NT); every load is issued unconditionally (an element past K, when K is not a
+// multiple of NT, reads element K-1 and is discarded).
+//   IN_XCHG     exchange words src[k] (epoch ep)
+//   IN_NORM     the same, then LayerNorm (gain g, bias bt) or RMSNorm (gain g)
+//   IN_EMB_NORM the embedding row of the input token (+ the learned position row), then the norm
+//   IN_ATTN     the attention output, merged from the per-chunk partials src[(h*max_split+s)*(hd+2)]
+template <class C, int F, int K, int IN, bool LN>
+__device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const uint64_t* src, const uint32_t ep,
+                                         const float* g, const float* bt, Smem& sm)
+{
+    constexpr int E = FmtT<F>::E, LPR = K / E, J = (K + NT - 1) / NT;
+    constexpr bool NORM = IN == IN_NORM || IN == IN_EMB_NORM;
+    const int t = threadIdx.x;
+    auto elem = [&](int j) { return K % NT == 0 ? t + NT * j : min(t + NT * j, K - 1); };
+    float v[J], gg[J], bb[J];
+    bool ok = true;
+    if constexpr (NORM) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            gg[j] = glb(g)[elem(j)];
+            bb[j] = LN ? glb(bt)[elem(j)] : 0.f;
+        }
+    }
+    float x0 = 0.f;   // LayerNorm shift (see finish_x in the GEMV core)
+    if constexpr (IN == IN_EMB_NORM) {
+        const float* er = a.emb + (size_t)cx.tok * K;
+        const float* pr = a.wpe + (size_t)cx.pos * K;
+#pragma unroll
+        for (int j = 0; j < J; ++j) v[j] = glb(er)[elem(j)] + (C::GPT2 ? glb(pr)[elem(j)] : 0.f);
+    } else if constexpr (IN == IN_ATTN) {
+        // element k = h*HD + i; chunk s of head h published (o[0..HD), m, l) in the log2 domain
+        constexpr int HD = C::HD, H = K / HD, PS = HD + 2;
+        static_assert(H * SG * 2 <= NT, "one (m, l) word per thread");
+        float Mr[J], Lr[J], Or[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            Mr[j] = -INFINITY;
+            Lr[j] = 0.f;
+            Or[j] = 0.f;
+        }
+        for (int s0 = 0; s0 < cx.S; s0 += SG) {
+            const int ns = min(SG, cx.S - s0);
+            // word 0: this thread's (m or l) word of the group (table [h][u][m, l]);
+            // word 1 + j*SG + u: chunk s0+u's output for element j (chunks past the context
+            // re-read the group's last chunk and are not used)
+            const int nml = H * ns * 2;
+            const int tm = min(t, nml - 1);
+            const int mh = tm / (2 * ns), mr = tm - mh * 2 * ns;
+            const uint64_t* mp = src + ((size_t)mh * a.max_split + s0 + (mr >> 1)) * PS + HD + (mr & 1);
+            auto addr = [&](int q) -> const uint64_t* {
+                if (q == 0) return mp;
+                const int j = (q - 1) / SG, u = (q - 1) % SG;
+                const int k = elem(j), h = k / HD, i = k - h * HD;
+                return src + ((size_t)h * a.max_split + s0 + min(u, ns - 1)) * PS + i;
+            };
+            constexpr int NW = 1 + J * SG;
+            uint64_t wv[NW];
+#pragma unroll
+            for (int q = 0; q < NW; ++q) wv[q] = xchg::load(addr(q));
+            ok &= xchg::settle_n(wv, NW, addr, ep, cx.limit, a.abort_word);
+            lds_barrier();                                 // earlier readers of ml are done
+            if (t < nml) sm.ml[t] = xchg::value(wv[0]);
+            lds_barrier();
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const float* mlh = sm.ml + (elem(j) / HD) * ns * 2;
+                float M = Mr[j];
+#pragma unroll
+                for (int u = 0; u < SG; ++u)
+                    if (u < ns) M = fmaxf(M, mlh[2 * u]);
+                const float sc = exp2f(Mr[j] - M);          // rescale of the running sums (0 at start)
+                float L = Lr[j] * sc, O = Or[j] * sc;
+#pragma unroll
+                for (int u = 0; u < SG; ++u) {
+                    if (u < ns) {
+                        const float wgt = exp2f(mlh[2 * u] - M);
+                        L = fmaf(mlh[2 * u + 1], wgt, L);
+                        O = fmaf(xchg::value(wv[1 + j * SG + u]), wgt, O);
+                    }
+                }
+                Mr[j] = M;
+                Lr[j] = L;
+                Or[j] = O;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < J; ++j) v[j] = __fdividef(Or[j], Lr[j]);
+    } else {
+        // words 0..J-1: this thread's elements; word J: element 0 (the LayerNorm shift)
+        constexpr int NW = J + (LN ? 1 : 0);
+        auto addr = [&](int q) -> const uint64_t* { return q < J ? src + elem(q) : src; };
+        uint64_t w[NW];
+#pragma unroll
+        for (int q = 0; q < NW; ++q) w[q] = xchg::load(addr(q));
+        ok = xchg::settle_n(w, NW, addr, ep, cx.limit, a.abort_word);
+#pragma unroll
+        for (int j = 0; j < J; ++j) v[j] = xchg::value(w[j]);
+        if constexpr (LN) x0 = xchg::value(w[NW - 1]);
+    }
+    if (!ok) *sm.abort = 1;
+
+    if constexpr (NORM) {
+        constexpr float invK = 1.0f / (float)K;
+        float s1 = 0.f, q2 = 0.f;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const float dx = (K % NT == 0 || t + NT * j < K) ? v[j] - x0 : 0.f;
+            s1 += dx;
+            q2 = fmaf(dx, dx, q2);
+        }
+        float mean = 0.f, var;
+        if constexpr (LN) {
+            const float2 tot = block_sum2<NT>(s1, q2, sm.red);
+            const float ms = tot.x * invK;
+            mean = x0 + ms;
+            var = fmaxf(tot.y * invK - ms * ms, 0.f);
+        } else {
+            var = block_sum<NT>(q2, sm.red) * invK;
+        }
+        const float r = 1.0f / sqrtf(var + a.eps);
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            float y = (v[j] - mean) * r * gg[j];
+            if constexpr (LN) y += bb[j];
+            v[j] = y;
+        }
+    } else {
+        lds_barrier();   // the previous phase's readers of xl are done
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int k = t + NT * j;
+        if (K % NT == 0 || k < K) sm.xl[4 * swz<E>(k, LPR) + (k & 3)] = v[j];
+    }
+    lds_barrier();
+}
+
+// ---- one GEMV phase --------------------------------------------------------------------------
+struct PhaseIO {
+    const uint64_t* src;  // input words (IN_XCHG / IN_NORM / IN_ATTN)
+    uint32_t src_ep;
+    const float* g;       // norm gain / bias
+    const float* bt;
+    const float* bias;    // linear bias or null
+    uint64_t* dst;        // output words
+    uint32_t dst_ep;
+    const uint64_t* res;  // OUT_RESID: residual words, or null for the embedding row (first layer)
+    uint32_t res_ep;
+    __half* kc;           // OUT_QKV*: this layer's cache
+    __half* vc;
+};
+
+// 16-byte load through the global address space
+__device__ __forceinline__ uint4 ld16(const void* p)
+{
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u v = *(const TSD_GLOBAL v4u*)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// (cos, sin) pair load through the global address space
+__device__ __forceinline__ float2 ld8f(const float2* p)
+{
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    const v2f v = *(const TSD_GLOBAL v2f*)p;
+    return make_float2(v.x, v.y);
+}
+
+// fp16 store through the global address space
+__device__ __forceinline__ void st_half(__half* p, __half v) { *glb((unsigned short*)p) = __half_as_ushort(v); }
+
+// v[i] for a runtime i < N: a tree of selects on the bits of i (the opaque intermediates keep
+// the compiler from rebuilding it as an indexed load through scratch memory)
+template <int N>
+__device__ __forceinline__ float pick(const float (&v)[N], int i)
+{
+    static_assert((N & (N - 1)) == 0, "power of two");
+    if constexpr (N == 1) {
+        return v[0];
+    } else {
+        float lo[N / 2], hi[N / 2];
+#pragma unroll
+        for (int k = 0; k < N / 2; ++k) {
+            lo[k] = v[k];
+            hi[k] = v[k + N / 2];
+        }
+        float a = pick(lo, i & (N / 2 - 1)), b = pick(hi, i & (N / 2 - 1));
+        asm volatile("" : "+v"(a), "+v"(b));
+        return (i & (N / 2)) ? b : a;
+    }
+}
+
+template <class C, int K, int N, int NL, int IN, int OUT, bool LN>
+__device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, const PackedMat& W, const PhaseIO& io,
+                                           Smem& sm)
+{
+    constexpr int F = C::F, HD = C::HD;
+    using G = Geo<F, K, N, NL>;
+    constexpr int E = G::E, NP = G::NP;
+    constexpr bool PAIR = OUT == OUT_QKV_ROPE || OUT == OUT_SWIGLU;
+    constexpr bool HAS_BIAS = C::GPT2 && !PAIR && OUT != OUT_HEAD;
+    constexpr int QD = C::QD, KD = C::KD;
+    static_assert(!PAIR || NP % 2 == 0, "pair epilogues need an even number of rows per lane");
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int slot0 = G::WIDE ? lane : lane % G::LPR;   // this lane's slot (first slice)
+    const int sub = G::WIDE ? 0 : lane / G::LPR;         // its row group within the wave
+    // lane-parallel epilogue: lane `slot0` (< NOUT) of a row group finishes the group's output
+    // slot0 (a row, or a pair of rows)
+    constexpr int NOUT = PAIR ? NP / 2 : NP;
+    const int er = slot0 < NOUT ? slot0 : NOUT - 1;
+    const bool eon = slot0 < NOUT;
+
+    unsigned long long best = 0ull;
+    bool have_x = false;
+    for (int tile = blockIdx.x; tile < G::TILES; tile += gridDim.x) {
+        const int row0 = (tile * NWAVE + wave) * G::RPW + sub * NP;   // first row of this lane's group
+        // epilogue operands of the lane's own output row(s), issued before the weights
+        const int erow = row0 + (PAIR ? 2 * er : er);
+        const int erc = min(erow, N - 1);
+        float bv = 0.f, re = 0.f;
+        uint64_t rw = 0ull;
+        if constexpr (HAS_BIAS) bv = glb(io.bias)[erc];
+        if constexpr (OUT == OUT_RESID) {
+            if (io.res) rw = xchg::load(io.res + erc);
+            else re = glb(a.emb)[(size_t)cx.tok * N + erc] + (C::GPT2 ? glb(a.wpe)[(size_t)cx.pos * N + erc] : 0.f);
+        }
+        // every weight and raw scale of this lane (unconditional, clamped rows)
+        uint4 w[NL];
+        uint32_t sc_raw[NL], sb_raw[NL];
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int row = min(G::WIDE ? row0 + i / G::SPL : row0 + i, N - 1);
+            const int slot = G::WIDE ? (i % G::SPL) * 64 + lane : slot0;
+            w[i] = ld16(W.q + (size_t)row * G::RB + (size_t)slot * 16);
+            sc_raw[i] = *glb((const uint16_t*)W.s + (size_t)row * G::SPR + slot / G::SPS);
+            if constexpr (F == FMT_AFF8) sb_raw[i] = *glb((const uint16_t*)W.b + (size_t)row * G::SPR + slot / G::SPS);
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+
+        if (!have_x) {
+            gather_x<C, F, K, IN, LN>(a, cx, io.src, io.src_ep, io.g, io.bt, sm);
+            have_x = true;
+            if (*sm.abort) return false;
+        }
+
+        // this lane's x slices and their sums
+        float xs[G::SPL][E];
+        float sx[G::SPL];
+        const float4* xl4 = (const float4*)sm.xl;
+#pragma unroll
+        for (int j = 0; j < G::SPL; ++j) {
+            const int slot = G::WIDE ? j * 64 + lane : slot0;
+            float s = 0.f;
+#pragma unroll
+            for (int e4 = 0; e4 < E / 4; ++e4) {
+                const float4 v = xl4[e4 * G::LPR + slot];
+                xs[j][4 * e4 + 0] = v.x;
+                xs[j][4 * e4 + 1] = v.y;
+                xs[j][4 * e4 + 2] = v.z;
+                xs[j][4 * e4 + 3] = v.w;
+                s += (v.x + v.y) + (v.z + v.w);
+            }
+            sx[j] = s;
+        }
+
+        float part[NP];
+#pragma unroll
+        for (int r = 0; r < NP; ++r) part[r] = 0.f;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int j = G::WIDE ? i % G::SPL : 0;
+            const int r = G::WIDE ? i / G::SPL : i;
+            const float d = slot_dot<F>(w[i], xs[j]);
+            const float sc = __half2float(__ushort_as_half((unsigned short)sc_raw[i]));
+            float v;
+            if constexpr (F == FMT_Q4_0) v = sc * fmaf(-8.f, sx[j], d);
+            else if constexpr (F == FMT_Q8_0) v = sc * fmaf(-128.f, sx[j], d);
+            else v = fmaf(sc, d, __half2float(__ushort_as_half((unsigned short)sb_raw[i])) * sx[j]);
+            part[r] += v;
+        }
+#pragma unroll
+        for (int r = 0; r < NP; ++r) part[r] = group_sum(part[r], G::GW);
+
+        if constexpr (OUT == OUT_RESID) {
+            if (io.res) {
+                uint64_t rr[1] = {rw};
+                auto addr = [&](int) { return io.res + erc; };
+                if (!xchg::settle_n(rr, 1, addr, io.res_ep, cx.limit, a.abort_word)) *sm.abort = 1;
+                re = xchg::value(rr[0]);
+            }
+        }
+
+        if constexpr (OUT == OUT_HEAD) {
+            const float t = pick(part, er);
+            if (eon && erow < N) {
+                glb(a.logits)[erow] = t;
+                const unsigned long long key =
+                    ((unsigned long long)float_order_key(t) << 32) | (0xFFFFFFFFu - (uint32_t)erow);
+                best = key > best ? key : best;
+            }
+        } else if constexpr (PAIR) {
+            float pa[NP / 2], pb[NP / 2];
+#pragma unroll
+            for (int q = 0; q < NP / 2; ++q) {
+                pa[q] = part[2 * q];
+                pb[q] = part[2 * q + 1];
+            }
+            const float t0 = pick(pa, er), t1 = pick(pb, er);
+            if (eon && erow < N) {
+                if constexpr (OUT == OUT_SWIGLU) {
+                    xchg::store(io.dst + (erow >> 1), silu(t0) * t1, io.dst_ep);
+                } else {
+                    // rows (2m, 2m+1) = elements (i, i + hd/2) of a Q or K head, or (2m, 2m+1) of V
+                    constexpr int half = HD / 2;
+                    if (erow < QD + KD) {
+                        const bool isk = erow >= QD;
+                        const int m = (isk ? erow - QD : erow) >> 1;
+                        const int h = m / half, i = m - h * half;
+                        const float2 cs = ld8f(a.rope + (size_t)cx.pos * half + i);
+                        const float ra = t0 * cs.x - t1 * cs.y, rb = t0 * cs.y + t1 * cs.x;
+                        if (!isk) {
+                            xchg::store(io.dst + h * HD + i, ra, io.dst_ep);
+                            xchg::store(io.dst + h * HD + i + half, rb, io.dst_ep);
+                        } else {
+                            const __half ha = __float2half_rn(ra), hb = __float2half_rn(rb);
+                            __half* c = io.kc + ((size_t)h * a.n_ctx + cx.pos) * HD;
+                            st_half(c + i, ha);
+                            st_half(c + i + half, hb);
+                            xchg::store(io.dst + QD + h * HD + i, __half2float(ha), io.dst_ep);
+                            xchg::store(io.dst + QD + h * HD + i + half, __half2float(hb), io.dst_ep);
+                        }
+                    } else {
+                        const int rv = erow - QD - KD;
+                        const int h = rv / HD, i = rv - h * HD;
+                        const __half ha = __float2half_rn(t0), hb = __float2half_rn(t1);
+                        __half* c = io.vc + ((size_t)h * a.n_ctx + cx.pos) * HD;
+                        st_half(c + i, ha);
+                        st_half(c + i + 1, hb);
+                        xchg::store(io.dst + erow, __half2float(ha), io.dst_ep);
+                        xchg::store(io.dst + erow + 1, __half2float(hb), io.dst_ep);
+                    }
+                }
+            }
+        } else {
+            const float t = pick(part, er) + bv;
+            if (eon && erow < N) {
+                if constexpr (OUT == OUT_QKV) {
+                    if (erow < QD) {
+                        xchg::store(io.dst + erow, t, io.dst_ep);
+                    } else {
+                        const bool isk = erow < QD + KD;
+                        const int rv = isk ? erow - QD : erow - QD - KD;
+                        const int h = rv / HD, i = rv - h * HD;
+                        const __half hv = __float2half_rn(t);
+                        st_half((isk ? io.kc : io.vc) + ((size_t)h * a.n_ctx + cx.pos) * HD + i, hv);
+                        xchg::store(io.dst + erow, __half2float(hv), io.dst_ep);
+                    }
+                } else if constexpr (OUT == OUT_RESID) {
+                    xchg::store(io.dst + erow, t + re, io.dst_ep);
+                } else if constexpr (OUT == OUT_GELU) {
+                    xchg::store(io.dst + erow, gelu_tanh(t), io.dst_ep);
+                }
+            }
+        }
+    }
+
+    if constexpr (OUT == OUT_HEAD) {
+        // this workgroup's best (ordered logit, ~index) key, published as two words
+        if ((int)blockIdx.x < G::TILES) {
+            __shared__ unsigned long long bkey[NWAVE];
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const unsigned long long other = __shfl_xor(best, o, 64);
+                best = other > best ? other : best;
+            }
+            if (lane == 0) bkey[wave] = best;
+            lds_barrier();
+            if (threadIdx.x == 0) {
+                unsigned long long m = bkey[0];
+#pragma unroll
+                for (int i = 1; i < NWAVE; ++i) m = bkey[i] > m ? bkey[i] : m;
+                xchg::store_bits(io.dst + 2 * blockIdx.x, (uint32_t)(m >> 32), io.dst_ep);
+                xchg::store_bits(io.dst + 2 * blockIdx.x + 1, (uint32_t)m, io.dst_ep);
+            }
+        }
+    }
+    return true;
+}
+
+// ---- attention phase -------------------------------------------------------------------------
+// Work item (head h, chunk s) = keys [256 s, 256 s + 256) of query head h; the same math as
+// k_attn (attention.hip), with the query and the new position's key/value taken from the
+// exchange.  Items go to the highest-numbered workgroups, which the QKV phase leaves idle when
+// it has fewer tiles than the grid has workgroups.
+template <class C>
+__device__ __forceinline__ bool attn_phase(const StepArgs& a, const Ctx& cx, const __half* kcache, const __half* vcache,
+                                           const uint32_t ep_qkv, const uint32_t ep_part, Smem& sm)
+{
+    constexpr int HD = C::HD, H = C::H, HK = C::HK, QD = C::QD, KD = C::KD;
+    constexpr int LPK = HD / 8, KPI = 64 / LPK, R = KTILE / KPI, PS = HD + 2;
+    __shared__ float ow[NWAVE][HD];
+    __shared__ float mw[NWAVE], lw[NWAVE];
+    const int items = H * cx.S;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = lane % LPK, kq = lane / LPK;
+    const int n_keys = cx.n_keys;
+    const float qscale = 1.4426950408889634f / sqrtf((float)HD);
+
+    for (int item = (int)gridDim.x - 1 - (int)blockIdx.x; item < items; item += gridDim.x) {
+        const int h = item % H, s = item / H, g = h / (H / HK);
+        const int k0 = s * ATTN_CHUNK + wave * KTILE;
+        const size_t head_off = (size_t)g * a.n_ctx * HD;
+        const int klast = n_keys - 1;
+        uint4 kr[R], vr[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int key = min(k0 + r * KPI + kq, klast);
+            kr[r] = ld16(kcache + head_off + (size_t)key * HD + c * 8);
+            vr[r] = ld16(vcache + head_off + (size_t)key * HD + c * 8);
+        }
+        // words 0-7: query dims 8c..8c+7 of head h; 8-15 / 16-23: the new key / value of kv head g
+        const uint64_t* pq = a.x_qkv + h * HD + c * 8;
+        const uint64_t* pk = a.x_qkv + QD + g * HD + c * 8;
+        const uint64_t* pv = a.x_qkv + QD + KD + g * HD + c * 8;
+        auto addr = [&](int i) { return (i < 8 ? pq : i < 16 ? pk - 8 : pv - 16) + i; };
+        uint64_t wx[24];
+#pragma unroll
+        for (int i = 0; i < 24; ++i) wx[i] = xchg::load(addr(i));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        if (!xchg::settle_n(wx, 24, addr, ep_qkv, cx.limit, a.abort_word)) *sm.abort = 1;
+        // the new position's row (exact fp16 values) replaces whatever the cache held there
+        uint4 nk, nv;
+        {
+            __half2 hk[4], hv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hk[e] = __floats2half2_rn(xchg::value(wx[8 + 2 * e]), xchg::value(wx[8 + 2 * e + 1]));
+                hv[e] = __floats2half2_rn(xchg::value(wx[16 + 2 * e]), xchg::value(wx[16 + 2 * e + 1]));
+            }
+            nk = *(const uint4*)hk;
+            nv = *(const uint4*)hv;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (k0 + r * KPI + kq == cx.pos) {
+                kr[r] = nk;
+                vr[r] = nv;
+            }
+        float q[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[e] = xchg::value(wx[e]) * qscale;
+
+        float sc[R];
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const __half2* kh = (const __half2*)&kr[r];
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float2 f = __half22float2(kh[e]);
+                acc = fmaf(f.x, q[2 * e], acc);
+                acc = fmaf(f.y, q[2 * e + 1], acc);
+            }
+            acc = group_sum(acc, LPK);
+            sc[r] = k0 + r * KPI + kq < n_keys ? acc : -INFINITY;
+            mloc = fmaxf(mloc, sc[r]);
+        }
+        const float m = wave_max(mloc);
+        float lsum = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const bool valid = k0 + r * KPI + kq < n_keys;
+            const float p = valid ? exp2f(sc[r] - m) : 0.f;
+            lsum += p;
+            const uint4 vv = valid ? vr[r] : make_uint4(0u, 0u, 0u, 0u);
+            const __half2* vh = (const __half2*)&vv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float2 f = __half22float2(vh[e]);
+                o[2 * e] = fmaf(p, f.x, o[2 * e]);
+                o[2 * e + 1] = fmaf(p, f.y, o[2 * e + 1]);
+            }
+        }
+        const float l = wave_sum(lsum) * (1.0f / LPK);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = o[e];
+            if constexpr (LPK == 8) v += dpp_mov<0x128>(v);
+            v = swap16_sum(v);
+            v = swap32_sum(v);
+            o[e] = v;
+        }
+        lds_barrier();   // the previous item's readers of ow are done
+        if (kq == 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ow[wave][c * 8 + e] = o[e];
+        }
+        if (lane == 0) {
+            mw[wave] = k0 < n_keys ? m : -INFINITY;
+            lw[wave] = l;
+        }
+        lds_barrier();
+        if (*sm.abort) return false;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, mw[w]);
+        uint64_t* part = a.x_part + ((size_t)h * a.max_split + s) * PS;
+        if (threadIdx.x < HD) {
+            float acc = 0.f;
+#pragma unroll
+            for (int w = 0; w < NWAVE; ++w) acc = fmaf(ow[w][threadIdx.x], exp2f(mw[w] - M), acc);
+            xchg::store(part + threadIdx.x, acc, ep_part);
+        } else if (threadIdx.x == HD) {
+            float L = 0.f;
+#pragma unroll
+            for (int w = 0; w < NWAVE; ++w) L = fmaf(lw[w], exp2f(mw[w] - M), L);
+            xchg::store(part + HD, M, ep_part);
+            xchg::store(part + HD + 1, L, ep_part);
+        }
+    }
+    return true;
+}
+
+// ---- the step --------------------------------------------------------------------------------
+template <class T>
+__device__ __forceinline__ T* shift(T* p, long long bytes)
+{
+    return p ? (T*)((const char*)p + bytes) : nullptr;
+}
+
+__device__ __forceinline__ PackedMat shift(PackedMat m, long long bytes)
+{
+    m.q = shift(m.q, bytes);
+    m.s = shift(m.s, bytes);
+    m.b = shift(m.b, bytes);
+    return m;
+}
+
+// a workgroup that gave up tells every other one at once (their waits check the abort word)
+__device__ __forceinline__ void give_up(const StepArgs& a)
+{
+    if (threadIdx.x == 0) xchg::raise_abort(a.abort_word);
+}
+
+// The arguments live in device memory and every phase re-reads the ones it uses through an
+// opaque copy of their address (in the constant address space, so the fields are fetched with
+// scalar loads, which hit the scalar cache): no phase keeps another phase's pointers alive,
+// which held across the whole step would not fit the scalar registers.
+using ArgsPtr = const __attribute__((address_space(4))) StepArgs*;
+__device__ __forceinline__ const StepArgs& opaque(ArgsPtr p)
+{
+    asm volatile("" : "+s"(p));
+    return *(const StepArgs*)p;
+}
+
+template <class C>
+__global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
+{
+    constexpr int OUT_QKV_K = C::GPT2 ? OUT_QKV : OUT_QKV_ROPE;
+    constexpr int OUT_FC_K = C::GPT2 ? OUT_GELU : OUT_SWIGLU;
+    const ArgsPtr ap = (ArgsPtr)args;
+
+    __shared__ float xl[MAX_K];
+    __shared__ float red[2 * NWAVE];
+    __shared__ float ml[C::H * SG * 2];
+    __shared__ int s_abort;
+    Smem sm{xl, red, ml, &s_abort};
+
+    if (threadIdx.x == 0) s_abort = 0;
+    Ctx cx;
+    uint32_t ctr, ep0;
+    int n_layer;
+    {
+        const StepArgs& a = opaque(ap);
+        // a wait of an earlier launch timed out: the exchange state is not trusted, do nothing
+        if (ld_uniform((const int*)a.abort_word)) return;
+        cx.pos = ld_uniform(a.pos);
+        const int tok = ld_uniform(a.tok);
+        ctr = (uint32_t)ld_uniform((const int*)a.ctr);
+        cx.tok = tok < 0 ? 0 : (tok >= C::V ? C::V - 1 : tok);
+        cx.n_keys = cx.pos + 1;
+        cx.S = (cx.n_keys + ATTN_CHUNK - 1) / ATTN_CHUNK;
+        cx.limit = a.spin_limit;
+        n_layer = a.n_layer;
+        lds_barrier();
+        if (cx.pos < 0 || cx.pos >= a.n_ctx) {   // never index the cache outside the context
+            if (threadIdx.x == 0) xchg::raise_abort(a.abort_word);
+            return;
+        }
+        ep0 = ctr * (5u * (uint32_t)n_layer + 1u) + 1u;
+    }
+
+    for (int l = 0; l < n_layer; ++l) {
+        // this layer's tensors are layer 0's moved by l strides; each phase derives only its own
+        const uint32_t e = ep0 + 5u * (uint32_t)l;   // qkv e, partials e+1, attn-out stream e+2, h e+3, layer out e+4
+        {   // 1. norm + QKV (+bias | RoPE) + K/V append
+            const StepArgs& a = opaque(ap);
+            const long long o = a.lstride * l;
+            PhaseIO io{};
+            io.src = a.x_out;
+            io.src_ep = e - 1u;
+            io.g = shift(a.L0.n1g, o);
+            io.bt = shift(a.L0.n1b, o);
+            io.bias = shift(a.L0.bqkv, o);
+            io.dst = a.x_qkv;
+            io.dst_ep = e;
+            io.kc = a.L0.kc + a.kvstride * l;
+            io.vc = a.L0.vc + a.kvstride * l;
+            const PackedMat W = shift(a.L0.qkv, o);
+            const bool ok = l == 0
+                ? gemv_phase<C, C::D, C::QKV, C::NL_D, IN_EMB_NORM, OUT_QKV_K, C::GPT2>(a, cx, W, io, sm)
+                : gemv_phase<C, C::D, C::QKV, C::NL_D, IN_NORM, OUT_QKV_K, C::GPT2>(a, cx, W, io, sm);
+            if (!ok) return give_up(a);
+        }
+        {   // 2. attention partials
+            const StepArgs& a = opaque(ap);
+            if (!attn_phase<C>(a, cx, a.L0.kc + a.kvstride * l, a.L0.vc + a.kvstride * l, e, e + 1u, sm))
+                return give_up(a);
+        }
+        {   // 3. merge + output projection + bias + residual
+            const StepArgs& a = opaque(ap);
+            const long long o = a.lstride * l;
+            PhaseIO io{};
+            io.src = a.x_part;
+            io.src_ep = e + 1u;
+            io.bias = shift(a.L0.bo, o);
+            io.dst = a.x_attn;
+            io.dst_ep = e + 2u;
+            io.res = l == 0 ? nullptr : a.x_out;
+            io.res_ep = e - 1u;
+            if (!gemv_phase<C, C::QD, C::D, C::NL_O, IN_ATTN, OUT_RESID, false>(a, cx, shift(a.L0.o, o), io, sm))
+                return give_up(a);
+        }
+        {   // 4. norm + FC (+bias, GELU) | gate/up (SwiGLU)
+            const StepArgs& a = opaque(ap);
+            const long long o = a.lstride * l;
+            PhaseIO io{};
+            io.src = a.x_attn;
+            io.src_ep = e + 2u;
+            io.g = shift(a.L0.n2g, o);
+            io.bt = shift(a.L0.n2b, o);
+            io.bias = shift(a.L0.bfc, o);
+            io.dst = a.x_h;
+            io.dst_ep = e + 3u;
+            if (!gemv_phase<C, C::D, C::FCN, C::NL_FC, IN_NORM, OUT_FC_K, C::GPT2>(a, cx, shift(a.L0.fc, o), io, sm))
+                return give_up(a);
+        }
+        {   // 5. down projection + bias + residual
+            const StepArgs& a = opaque(ap);
+            const long long o = a.lstride * l;
+            PhaseIO io{};
+            io.src = a.x_h;
+            io.src_ep = e + 3u;
+            io.bias = shift(a.L0.bdown, o);
+            io.dst = a.x_out;
+            io.dst_ep = e + 4u;
+            io.res = a.x_attn;
+            io.res_ep = e + 2u;
+            if (!gemv_phase<C, C::FF, C::D, C::NL_F, IN_XCHG, OUT_RESID, false>(a, cx, shift(a.L0.down, o), io, sm))
+                return give_up(a);
+        }
+    }
+
+    const StepArgs& a = opaque(ap);
+    // final norm + head (logits, per-workgroup best)
+    const uint32_t eh = ep0 + 5u * (uint32_t)n_layer;
+    PhaseIO io{};
+    io.src = a.x_out;
+    io.src_ep = eh - 1u;
+    io.g = a.nfg;
+    io.bt = a.nfb;
+    io.dst = a.x_best;
+    io.dst_ep = eh;
+    if (!gemv_phase<C, C::D, C::V, C::NL_HEAD, IN_NORM, OUT_HEAD, C::GPT2>(a, cx, a.head, io, sm)) return give_up(a);
+
+    // greedy sampler, last stage (workgroup 0): the best of the per-workgroup keys; ties go to
+    // the lowest index because the key's low word is the inverted index
+    if (blockIdx.x != 0) return;
+    constexpr int HEAD_TILES = Geo<C::F, C::D, C::V, C::NL_HEAD>::TILES;
+    const int nb = min((int)gridDim.x, HEAD_TILES);
+    unsigned long long bk = 0ull;
+    bool ok = true;
+    for (int w = threadIdx.x; w < nb; w += NT) {
+        float hl[2];
+        ok &= xchg::wait_words<2>(a.x_best + 2 * w, 1, eh, hl, cx.limit, a.abort_word);
+        const unsigned long long key = ((unsigned long long)__float_as_uint(hl[0]) << 32) | __float_as_uint(hl[1]);
+        bk = key > bk ? key : bk;
+    }
+    if (!ok) s_abort = 1;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const unsigned long long other = __shfl_xor(bk, o, 64);
+        bk = other > bk ? other : bk;
+    }
+    __shared__ unsigned long long fkey[NWAVE];
+    if ((threadIdx.x & 63) == 0) fkey[threadIdx.x >> 6] = bk;
+    lds_barrier();
+    if (threadIdx.x == 0) {
+        if (s_abort) {
+            xchg::raise_abort(a.abort_word);
+            return;
+        }
+        unsigned long long m = fkey[0];
+#pragma unroll
+        for (int i = 1; i < NWAVE; ++i) m = fkey[i] > m ? fkey[i] : m;
+        const int id = (int)(0xFFFFFFFFu - (uint32_t)m);
+        *glb(a.tok) = id;
+        glb(a.hist)[cx.pos] = id;
+        *glb(a.pos) = cx.pos + 1;
+        *glb(a.ctr) = ctr + 1u;
+    }
+}
+
+// the shapes with a persistent kernel: the decoders of the pages at their real sizes, and the
+// small shapes the parity tests use; any other shape runs one launch per operator
+struct Entry {
+    int fmt, arch, d, h, hk, hd, ff, v;
+    const void* fn;
+};
+template <int F, int A, int D, int H, int HK, int HD, int FF, int V>
+Entry entry()
+{
+    return Entry{F, A, D, H, HK, HD, FF, V, (const void*)k_step<Shape<F, A, D, H, HK, HD, FF, V>>};
+}
+
+const Entry* entries(int& n)
+{
+    static const Entry tab[] = {
+        entry<FMT_Q4_0, A_GPT2, 1024, 16, 16, 64, 4096, 8192>(),    // GPT-2-Medium-shaped T3, Q4_0
+        entry<FMT_Q8_0, A_GPT2, 1024, 16, 16, 64, 4096, 8192>(),    //   and Q8_0
+        entry<FMT_Q8_0, A_LLAMA, 1024, 16, 16, 64, 4096, 8192>(),   // Llama-shaped ~520M T3, Q8_0
+        entry<FMT_Q4_0, A_LLAMA, 1024, 16, 16, 64, 4096, 8192>(),   //   and Q4_0
+        // test shapes
+        entry<FMT_Q4_0, A_GPT2, 128, 2, 2, 64, 256, 160>(),
+        entry<FMT_Q8_0, A_GPT2, 128, 2, 2, 64, 256, 160>(),
+        entry<FMT_AFF8, A_GPT2, 128, 2, 2, 64, 256, 160>(),
+        entry<FMT_Q4_0, A_LLAMA, 128, 2, 2, 64, 256, 160>(),
+        entry<FMT_Q8_0, A_LLAMA, 128, 2, 2, 64, 256, 160>(),
+        entry<FMT_AFF8, A_LLAMA, 128, 2, 2, 64, 256, 160>(),
+        entry<FMT_Q4_0, A_GPT2, 128, 2, 2, 64, 256, 1000>(),
+        entry<FMT_Q8_0, A_LLAMA, 256, 4, 2, 128, 256, 160>(),
+    };
+    n = (int)(sizeof(tab) / sizeof(tab[0]));
+    return tab;
+}
+
+}  // namespace
+
+const void* step_kernel_for(int fmt, int arch_llama, int d, int h, int hk, int hd, int ff, int vocab)
+{
+    int n = 0;
+    const Entry* t = entries(n);
+    const int arch = arch_llama ? A_LLAMA : A_GPT2;
+    for (int i = 0; i < n; ++i)
+        if (t[i].fmt == fmt && t[i].arch == arch && t[i].d == d && t[i].h == h && t[i].hk == hk && t[i].hd == hd &&
+            t[i].ff == ff && t[i].v == vocab)
+            return t[i].fn;
+    return nullptr;
+}
+
+hipError_t launch_step(const void* kernel, const StepArgs* d_args, int n_wg, hipStream_t st)
+{
+    void* args[] = {(void*)&d_args};
+    return hipLaunchKernel(kernel, dim3(n_wg), dim3(NT), args, 0, st);
+}
+
+}  // namespace tsd

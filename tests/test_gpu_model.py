@@ -1,6 +1,7 @@
 """GPU parity of the whole decode step (captured graph) against the CPU oracle, through the
-C ABI.  Logits: rel <= 2e-3 per step.  Greedy ids: teacher forced (both sides get the oracle's
-id as the next input) and equal except where the oracle's top-2 logits are within 1e-3."""
+C ABI, in both launch modes (one persistent launch per step; one launch per operator).
+Logits: rel <= 2e-3 per step.  Greedy ids: teacher forced (both sides get the oracle's id as
+the next input) and equal except where the oracle's top-2 logits are within 1e-3."""
 import sys
 
 import numpy as np
@@ -27,16 +28,22 @@ def dev(a):
     return torch_mod().from_numpy(np.ascontiguousarray(a)).to("cuda")
 
 
-def gpu_model(cfg, w):
+MODES = ["persistent", "per_operator"]
+
+
+def gpu_model(cfg, w, mode="persistent", n_wg=0):
     from quantized_gemv_kv_amd import Model
-    return Model(cfg, w)
+    m = Model(dict(cfg, launch_mode=mode, n_workgroups=n_wg), w)
+    # the launch mode asked for is the one that runs (the step kernel is timed only when it exists)
+    assert m.uses_persistent_step() == (mode == "persistent"), "persistent step not built for this shape"
+    return m
 
 
-def teacher_forced(cfg, w, n_prompt, n_steps, kv_pos=None, seed=3, check_ids=True):
+def teacher_forced(cfg, w, n_prompt, n_steps, kv_pos=None, seed=3, check_ids=True, mode="persistent", n_wg=0):
     """Run both sides n_steps past a prompt (or a loaded random cache) and compare."""
     torch = torch_mod()
     om = oracle.OracleModel(cfg, w)
-    gm = gpu_model(cfg, w)
+    gm = gpu_model(cfg, w, mode, n_wg)
     worst = 0.0
     if kv_pos is not None:
         k, v = synth.kv_cache(cfg, kv_pos, seed=seed)
@@ -64,6 +71,7 @@ def teacher_forced(cfg, w, n_prompt, n_steps, kv_pos=None, seed=3, check_ids=Tru
             assert ids_agree(g_ids[0, 0], lo), (s, g_ids, o_ids, top2_gap(lo))
         nxt = o_ids
     assert gm.n_past == om.n_past
+    gm.synchronize()
     gm.close()
     return worst
 
@@ -72,20 +80,32 @@ SMALL = [("gpt2", "q4_0"), ("gpt2", "q8_0"), ("gpt2", "aff8"), ("llama", "q8_0")
          ("llama", "aff8")]
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("arch,fmt", SMALL)
-def test_small_models_teacher_forced(arch, fmt):
+def test_small_models_teacher_forced(arch, fmt, mode):
     cfg = synth.small_config(arch, fmt, d_ff=256, n_ctx=64)
-    say(f"[model-small] {arch} {fmt}")
+    say(f"[model-small] {arch} {fmt} {mode}")
     w = synth.model_weights(cfg, 42, norm_std=0.5)
-    worst = teacher_forced(cfg, w, n_prompt=9, n_steps=30)
+    worst = teacher_forced(cfg, w, n_prompt=9, n_steps=30, mode=mode)
     say(f"  worst rel {worst:.2e}")
 
 
-def test_small_llama_gqa_head128():
+@pytest.mark.parametrize("mode", MODES)
+def test_small_llama_gqa_head128(mode):
     cfg = synth.small_config("llama", "q8_0", d_model=256, n_head=4, n_kv_head=2, head_dim=128, d_ff=256, n_ctx=96)
-    say("[model-small] llama gqa hd128")
+    say(f"[model-small] llama gqa hd128 {mode}")
     w = synth.model_weights(cfg, 7, norm_std=0.5)
-    teacher_forced(cfg, w, n_prompt=70, n_steps=20)     # crosses a 64-key tile boundary
+    teacher_forced(cfg, w, n_prompt=70, n_steps=20, mode=mode)     # crosses a 64-key tile boundary
+
+
+@pytest.mark.parametrize("n_wg", [1, 7, 37])
+def test_persistent_step_any_grid(n_wg):
+    """Grids smaller than the tile counts: workgroups take several tiles of a phase, attention
+    items wrap onto workgroups that also hold GEMV tiles, and a single workgroup runs it all."""
+    cfg = synth.small_config("gpt2", "q4_0", d_ff=256, n_ctx=320, vocab=1000)
+    say(f"[model-small] persistent grid {n_wg}")
+    w = synth.model_weights(cfg, 5, norm_std=0.5)
+    teacher_forced(cfg, w, n_prompt=0, n_steps=3, kv_pos=300, mode="persistent", n_wg=n_wg)   # two 256-key chunks
 
 
 def test_gpt2_medium_one_layer_after_512_positions():
@@ -112,14 +132,15 @@ def test_gpt2_medium_one_layer_after_512_positions():
     gm.close()
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("name,kv_pos", [("gpt2_medium_q4_0", 755), ("llama520m_q8_0", 899)])
-def test_full_size_step_over_long_cache(name, kv_pos):
+def test_full_size_step_over_long_cache(name, kv_pos, mode):
     """All layers at their real shapes, one teacher-forced step at the last position of the
     decode run (756 / 900 keys), and one more at the next position."""
     cfg = synth.config(name)
-    say(f"[model-full] {name} kv_pos={kv_pos}")
+    say(f"[model-full] {name} kv_pos={kv_pos} {mode}")
     w = synth.model_weights(cfg, 42)
-    worst = teacher_forced(cfg, w, n_prompt=0, n_steps=2, kv_pos=kv_pos)
+    worst = teacher_forced(cfg, w, n_prompt=0, n_steps=2, kv_pos=kv_pos, mode=mode)
     say(f"  worst rel {worst:.2e}")
 
 
@@ -130,12 +151,13 @@ def test_full_size_gpt2_prefill_then_decode():
     teacher_forced(cfg, w, n_prompt=6, n_steps=3)
 
 
-def test_free_running_greedy_matches_history():
+@pytest.mark.parametrize("mode", MODES)
+def test_free_running_greedy_matches_history(mode):
     """The benchmarked path: no input ids, the graph feeds its own samples forward."""
     torch = torch_mod()
     cfg = synth.small_config("gpt2", "q4_0", d_ff=256, n_ctx=64)
     w = synth.model_weights(cfg, 42, norm_std=0.5)
-    gm = gpu_model(cfg, w)
+    gm = gpu_model(cfg, w, mode)
     om = oracle.OracleModel(cfg, w)
     toks = synth.prompt_tokens(cfg, 5, seed=1)
     first = gm.prefill(dev(toks)).cpu().numpy()
@@ -180,3 +202,23 @@ def test_errors_leave_state_unchanged():
         gpu_model(cfg, w[:-1])                     # wrong number of weights
     with pytest.raises(TsdError):
         gpu_model(dict(cfg, d_model=130), w)       # K not a multiple of the block
+    with pytest.raises(TsdError) as e:
+        gpu_model(cfg, w, n_wg=100000)             # more workgroups than can be resident
+    assert e.value.status == 2
+
+
+def test_step_timing_kinds_follow_launch_mode():
+    from quantized_gemv_kv_amd import TsdError
+    cfg = synth.small_config("gpt2", "q4_0", d_ff=256, n_ctx=64)
+    w = synth.model_weights(cfg, 42, norm_std=0.5)
+    for mode, ok, bad in (("persistent", "step", "qkv"), ("per_operator", "qkv", "step")):
+        gm = gpu_model(cfg, w, mode)
+        gm.prefill(dev(synth.prompt_tokens(cfg, 4)))
+        us, n = gm.time_kernel(ok, 3)
+        assert us > 0 and n >= 1
+        before = gm.n_past
+        with pytest.raises(TsdError) as e:
+            gm.time_kernel(bad, 3)
+        assert e.value.status == 2 and gm.n_past == before
+        gm.synchronize()
+        gm.close()

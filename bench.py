@@ -50,6 +50,26 @@ def parse():
     return ap.parse_args()
 
 
+STEP_SOURCES = ["quantized_gemv_kv_amd/csrc/" + f for f in ("step.hip", "exchange.h", "gemv_core.h", "common.h", "kernels.h")]
+COUNTERS = os.path.join(ROOT, "profiles", "step_gpt2_medium_q4_0_counters.json")
+
+
+def counted_traffic(kernel):
+    """HBM-side bytes per launch of the step kernel from the committed FETCH_SIZE / WRITE_SIZE
+    summary (scaled by the copy calibration), or None when that summary was taken on other
+    kernel sources than the ones built now."""
+    import hashlib
+    if kernel != "step" or not os.path.exists(COUNTERS):
+        return None
+    h = hashlib.sha256()
+    for f in STEP_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    with open(COUNTERS) as fh:
+        d = json.load(fh)
+    return d["traffic_bytes_per_launch"] if d.get("sources_sha256_16") == h.hexdigest()[:16] else None
+
+
 def cpu_baseline(cfg, weights, seconds, seed):
     """The CPU oracle as it stands (single-threaded C, fp64), timed on this host: decode steps
     from position 256 over a random 256-position fp16 cache, until the time budget is spent."""
@@ -156,7 +176,7 @@ def main():
                    "d_model": 1024, "n_layer": 24, "n_head": 16, "d_ff": 4096, "vocab": 8192,
                    "prompt": PROMPT, "global_batch": 1, "launch_mode": mode, "workgroups": n_wg},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": roofline.HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / roofline.HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / roofline.HBM_PEAK_GBS, "traffic": counted_traffic(dom),
                      "kernel": dom, "launch_us": dom_us, "launches_per_step": dom_n,
                      "bytes_per_launch": dom_bytes},
         "kernel_us": {k: round(v[0], 3) for k, v in kinds.items()},

@@ -17,7 +17,7 @@
  *     device memory are valid once the caller synchronises that stream.
  *   - A model is not thread-safe; use one model per stream.
  *
- * Weight formats ([J] appendix A3 "Quantize T3" and §3.23; [F] §3 "Counting the bytes"):
+ * Weight formats ([J] appendix A3 "Quantize T3" and §3.23; [F] §3 "Predict first: the roofline"):
  *   TSD_W_Q4_0        rows of K/32 blocks, 18 bytes each: fp16 scale d (little endian), then 16
  *                     bytes; element j<16 is the low nibble of byte j, element j+16 its high
  *                     nibble; w = (q - 8) * d.

@@ -120,9 +120,34 @@ __device__ __forceinline__ float wave_max(float v)
     v = fmaxf(v, dpp_mov<0x4E>(v));
     v = fmaxf(v, dpp_mov<0x141>(v));
     v = fmaxf(v, dpp_mov<0x140>(v));
-    v = fmaxf(v, __shfl_xor(v, 16, 64));
-    v = fmaxf(v, __shfl_xor(v, 32, 64));
-    return v;
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// maximum of a 64-bit key over the wave (both halves moved by the same lane pattern)
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_mov64(unsigned long long v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, true);
+    return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long max64(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
+{
+    v = max64(v, dpp_mov64<0xB1>(v));
+    v = max64(v, dpp_mov64<0x4E>(v));
+    v = max64(v, dpp_mov64<0x141>(v));
+    v = max64(v, dpp_mov64<0x140>(v));
+    // the swaps return (own, partner) in a lane-dependent order, the same for both halves
+    auto a = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    auto b = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+    v = max64(((unsigned long long)b[0] << 32) | a[0], ((unsigned long long)b[1] << 32) | a[1]);
+    a = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    b = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+    return max64(((unsigned long long)b[0] << 32) | a[0], ((unsigned long long)b[1] << 32) | a[1]);
 }
 
 // global-address-space views of a pointer: loads and stores through them are global_* (vector

@@ -139,5 +139,28 @@ __device__ __forceinline__ bool settle_n(uint64_t (&w)[N], int n, Addr addr, uin
     }
 }
 
+// the same for the words w[i] with use(i) (a uniform predicate)
+template <int N, class Use, class Addr>
+__device__ __forceinline__ bool settle_if(uint64_t (&w)[N], Use use, Addr addr, uint32_t epoch, long long limit,
+                                          const uint32_t* abort_word)
+{
+    auto lane_ready = [&]() {
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            if (use(i)) ok &= ready(w[i], epoch);
+        return ok;
+    };
+    if (__builtin_amdgcn_ballot_w64(!lane_ready()) == 0) return true;
+    Deadline dl(limit, abort_word);
+    for (;;) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            if (use(i)) w[i] = load(addr(i));
+        if (__builtin_amdgcn_ballot_w64(!lane_ready()) == 0) return true;
+        if (dl.expired()) return false;
+    }
+}
+
 }  // namespace xchg
 }  // namespace tsd

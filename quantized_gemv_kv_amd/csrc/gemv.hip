@@ -211,11 +211,7 @@ __global__ __launch_bounds__(WG) void k_gemv(const PackedMat W, const ProArgs pa
     if constexpr (EPI == EPI_HEAD_ARGMAX) {
         // greedy sampler, first stage: the workgroup's best key (ordered logit, ~index: ties go
         // to the lowest index); one plain store per workgroup, reduced by the finalize kernel
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            const unsigned long long other = __shfl_xor(best, o, 64);
-            best = other > best ? other : best;
-        }
+        best = wave_max_u64(best);
         if (lane == 0) bkey[wave] = best;
         lds_barrier();
         if (threadIdx.x == 0) {
@@ -345,11 +341,7 @@ __global__ __launch_bounds__(256) void k_argmax_finalize(const unsigned long lon
     __shared__ unsigned long long bk[NWAVE];
     unsigned long long m = 0ull;
     for (int i = threadIdx.x; i < n; i += WG) m = best[i] > m ? best[i] : m;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        const unsigned long long other = __shfl_xor(m, o, 64);
-        m = other > m ? other : m;
-    }
+    m = wave_max_u64(m);
     if ((threadIdx.x & 63) == 0) bk[threadIdx.x >> 6] = m;
     __syncthreads();
     if (threadIdx.x == 0) {

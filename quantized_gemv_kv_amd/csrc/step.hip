@@ -157,11 +157,13 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
                 return src + ((size_t)h * a.max_split + s0 + min(u, ns - 1)) * PS + i;
             };
             constexpr int NW = 1 + J * SG;
+            auto use = [&](int q) { return q == 0 || (q - 1) % SG < ns; };
             uint64_t wv[NW];
 #pragma unroll
-            for (int q = 0; q < NW; ++q) wv[q] = xchg::load(addr(q));
-            ok &= xchg::settle_n(wv, NW, addr, ep, cx.limit, a.abort_word);
-            lds_barrier();                                 // earlier readers of ml are done
+            for (int q = 0; q < NW; ++q)
+                if (use(q)) wv[q] = xchg::load(addr(q));
+            ok &= xchg::settle_if(wv, use, addr, ep, cx.limit, a.abort_word);
+            if (s0 > 0) lds_barrier();                     // the previous group's readers of ml are done
             if (t < nml) sm.ml[t] = xchg::value(wv[0]);
             lds_barrier();
 #pragma unroll
@@ -473,11 +475,7 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
         // this workgroup's best (ordered logit, ~index) key, published as two words
         if ((int)blockIdx.x < G::TILES) {
             __shared__ unsigned long long bkey[NWAVE];
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                const unsigned long long other = __shfl_xor(best, o, 64);
-                best = other > best ? other : best;
-            }
+            best = wave_max_u64(best);
             if (lane == 0) bkey[wave] = best;
             lds_barrier();
             if (threadIdx.x == 0) {
@@ -794,11 +792,7 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
         bk = key > bk ? key : bk;
     }
     if (!ok) s_abort = 1;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        const unsigned long long other = __shfl_xor(bk, o, 64);
-        bk = other > bk ? other : bk;
-    }
+    bk = wave_max_u64(bk);
     __shared__ unsigned long long fkey[NWAVE];
     if ((threadIdx.x & 63) == 0) fkey[threadIdx.x >> 6] = bk;
     lds_barrier();

@@ -87,7 +87,8 @@ typedef struct {
  *         them, draw u in [0,1) as the top 24 bits of the first word of Philox4x64-10
  *         (Salmon et al. 2011) with key (seed, 0) and counter (position, row, pass, 0), and
  *         return the first index in descending order whose cumulative mass exceeds u * total.
- *         top_k <= 0 or > vocab means the whole vocabulary. */
+ *         top_k <= 0 or > vocab means the whole vocabulary.  Draws with k > 1024 (or a vocabulary
+ *         over 12288) are TSD_ERR_UNSUPPORTED; the temperature must be positive and finite. */
 typedef struct {
     int32_t mode;
     int32_t top_k;
@@ -190,6 +191,14 @@ tsd_status tsd_layer_forward(tsd_model* m, int layer, const float* d_x, int pos,
 tsd_status tsd_time_kernel(tsd_model* m, int kind, int n_steps, float* avg_us, int* launches_per_step);
 
 /* ---- standalone operators (same kernels as the step) ------------------------------------- */
+
+/* The step's top-k draw on d_logits[0..n) (fp32, device): the id is written to d_out[0] (device).
+ * k = top_k, or n when top_k <= 0 or > n; the uniform is drawn at counter (pos, row, pass, 0)
+ * with key (seed, 0) as in tsd_sampling.  TSD_ERR_UNSUPPORTED for k > 1024 or n > 12288;
+ * TSD_ERR_INVALID_ARGUMENT for null buffers, n <= 0, negative counters or a temperature that is
+ * not positive and finite. */
+tsd_status tsd_sample_topk(const float* d_logits, int n, int top_k, float temperature, uint64_t seed, int row,
+                           int pos, int pass, int32_t* d_out, void* stream);
 
 /* Bytes of the kernel layout of one W[N][K] matrix (tsd_gemv_pack's output). */
 tsd_status tsd_gemv_packed_bytes(int wfmt, int N, int K, size_t* out_bytes);

@@ -126,11 +126,24 @@ struct StepArgs {
     // (residual stream), MLP hidden, layer output (residual stream), per-workgroup argmax keys
     uint64_t *x_qkv, *x_part, *x_attn, *x_h, *x_out, *x_best;
     long long spin_limit;                     // ticks of the 100 MHz clock a wait may take
+    // sampler: mode 0 greedy, 1 top-k (the head also publishes its logits as exchange words)
+    int samp_mode, top_k;
+    float temperature;
+    unsigned long long seed;
+    uint64_t* x_logit;                        // [vocab] exchange words of the logits (top-k)
 };
 // the step kernel for a shape, or null when the shape has no instantiation
 const void* step_kernel_for(int fmt, int arch_llama, int d, int h, int hk, int hd, int ff, int vocab);
 // d_args: the arguments in device memory (read by every phase)
 hipError_t launch_step(const void* kernel, const StepArgs* d_args, int n_wg, hipStream_t st);
+
+// ---- top-k sampler (sampler.hip, sampler.h) ----------------------------------------------------
+// the id drawn from logits[0..n): k largest of logits / temperature, counter (pos, row, pass);
+// pos is *posp when posp is set (then the id is also written to hist[pos * hist_stride] and *posp
+// advanced), else pos_value.  k must be 1..min(n, 1024).
+bool topk_supported(int n, int k);
+hipError_t launch_topk(const float* logits, int n, int k, float temperature, unsigned long long seed, int row, int pass,
+                       int* posp, int pos_value, int* out, int* hist, int hist_stride, hipStream_t st);
 
 // ---- small state kernels ---------------------------------------------------------------------
 hipError_t launch_copy_i32(int* dst, const int* src, int n, hipStream_t st);

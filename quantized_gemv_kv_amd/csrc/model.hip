@@ -10,6 +10,7 @@
 // a Memory Read", §5.2: the random state and the sampled ids stay inside the compiled graph).
 #include <math.h>
 
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -92,6 +93,7 @@ struct tsd_model {
     // timing probes: events around every launch of one kernel kind
     std::vector<hipEvent_t> probe_ev[TSD_KERNEL_KINDS];
     int n_past = 0;
+    int top_k = 0;                    // effective k of the top-k sampler
     std::string err;
 };
 
@@ -254,7 +256,7 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     uint32_t* ctl = (uint32_t*)P.take(sizeof(uint32_t) * 64);
     StepArgs* d_sa = (StepArgs*)P.take(sizeof(StepArgs));
     const size_t n_part = (size_t)H * attn_max_split(c->n_ctx) * (hd + 2);
-    const size_t xw[6] = {(size_t)qkv_rows, n_part, (size_t)d, (size_t)ff, (size_t)d, 2 * (size_t)MAX_STEP_WG};
+    const size_t xw[7] = {(size_t)qkv_rows, n_part, (size_t)d, (size_t)ff, (size_t)d, 2 * (size_t)MAX_STEP_WG, (size_t)vmax};
     size_t xtot = 0;
     for (size_t n : xw) xtot += (n + 31) & ~(size_t)31;
     uint64_t* xbuf = (uint64_t*)P.take(sizeof(uint64_t) * xtot);
@@ -268,14 +270,15 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
         m->d_sa = d_sa;
         m->xbuf = xbuf;
         m->xbuf_words = xtot;
-        uint64_t* xp[6];
+        uint64_t* xp[7];
         uint64_t* q = xbuf;
-        for (int i = 0; i < 6; ++i) {
+        for (int i = 0; i < 7; ++i) {
             xp[i] = q;
             q += (xw[i] + 31) & ~(size_t)31;
         }
         StepArgs& a = m->sa;
         a.x_qkv = xp[0]; a.x_part = xp[1]; a.x_attn = xp[2]; a.x_h = xp[3]; a.x_out = xp[4]; a.x_best = xp[5];
+        a.x_logit = xp[6];
     }
     return align256(P.off);
 }
@@ -429,6 +432,9 @@ hipError_t enqueue_step(tsd_model* m, hipStream_t st, Probe* pr = nullptr)
     Bracket br(pr, KIND_HEAD, st);
     hipError_t e = launch_gemv(c.wfmt, c.arch == TSD_ARCH_GPT2 ? PRO_LN : PRO_RMS, EPI_HEAD_ARGMAX, m->head, ph, eh, st);
     if (e != hipSuccess) return e;
+    if (m->samp.mode == 1)
+        return launch_topk(m->logits, c.vocab, m->top_k, m->samp.temperature, m->samp.seed, 0, 0, m->pos, 0, m->tok,
+                           m->hist, c.batch * m->tpp, st);
     const int nblk = (c.vocab + gemv_rows_per_block(c.wfmt, c.d_model, EPI_HEAD_ARGMAX) - 1) /
                      gemv_rows_per_block(c.wfmt, c.d_model, EPI_HEAD_ARGMAX);
     return launch_argmax_finalize(m->best, nblk, m->tok, m->hist, c.batch * m->tpp, m->pos, st);
@@ -542,6 +548,10 @@ tsd_status setup_step(tsd_model* m)
     a.pos = m->pos; a.tok = m->tok; a.hist = m->hist; a.ctr = m->ctl; a.abort_word = m->ctl + 1;
     a.logits = m->logits;
     a.spin_limit = STEP_SPIN_LIMIT;
+    a.samp_mode = m->samp.mode;
+    a.top_k = m->top_k;
+    a.temperature = m->samp.temperature;
+    a.seed = m->samp.seed;
     const uint64_t nph = 5ull * c.n_layer + 1ull;
     m->max_launches = (0xFFFFFFF0ull - nph) / nph;
     return TSD_OK;
@@ -641,11 +651,20 @@ tsd_status tsd_model_create(const tsd_config* cfg, const tsd_tensor* weights, in
         if (!weights[i].ptr || weights[i].bytes != sz[i])
             return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "weight " + std::to_string(i) + ": " +
                         std::to_string(weights[i].bytes) + " bytes, expected " + std::to_string(sz[i]));
-    if (sampling && sampling->mode != 0) return fail(nullptr, TSD_ERR_UNSUPPORTED, "top-k sampling is not built yet");
+    int top_k = 0;
+    if (sampling && sampling->mode != 0) {
+        if (sampling->mode != 1) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "sampling mode must be 0 (greedy) or 1 (top-k)");
+        if (!(sampling->temperature > 0.f) || !std::isfinite(sampling->temperature))
+            return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "temperature must be positive and finite");
+        top_k = (sampling->top_k <= 0 || sampling->top_k > cfg->vocab) ? cfg->vocab : sampling->top_k;
+        if (!topk_supported(cfg->vocab, top_k))
+            return fail(nullptr, TSD_ERR_UNSUPPORTED, "top-k draws support k <= 1024 and vocabularies up to 12288");
+    }
     tsd_model* m = new (std::nothrow) tsd_model();
     if (!m) return fail(nullptr, TSD_ERR_OUT_OF_MEMORY, "host allocation");
     m->c = *cfg;
     if (sampling) m->samp = *sampling;
+    m->top_k = top_k;
     m->st = (hipStream_t)stream;
     m->ws = (uint8_t*)d_ws;
     m->ws_bytes = ws_bytes;
@@ -892,6 +911,20 @@ tsd_status tsd_gemv(int wfmt, const void* d_packed, int N, int K, int B, const f
         if (e != hipSuccess) return hip_fail(nullptr, e, "gemv");
     }
     return TSD_OK;
+}
+
+tsd_status tsd_sample_topk(const float* d_logits, int n, int top_k, float temperature, uint64_t seed, int row, int pos,
+                           int pass, int32_t* d_out, void* stream)
+{
+    if (!d_logits || !d_out) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null buffer");
+    if (n <= 0 || row < 0 || pos < 0 || pass < 0) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "bad size or counter");
+    if (!(temperature > 0.f) || !std::isfinite(temperature))
+        return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "temperature must be positive and finite");
+    const int k = (top_k <= 0 || top_k > n) ? n : top_k;
+    if (!topk_supported(n, k)) return fail(nullptr, TSD_ERR_UNSUPPORTED, "k <= 1024 and n <= 12288");
+    hipError_t e = launch_topk(d_logits, n, k, temperature, seed, row, pass, nullptr, pos, d_out, nullptr, 0,
+                               (hipStream_t)stream);
+    return e == hipSuccess ? TSD_OK : hip_fail(nullptr, e, "top-k");
 }
 
 tsd_status tsd_attention_scratch_bytes(int B, int H, int n_ctx, int hd, size_t* out)

@@ -33,6 +33,7 @@
 
 #include "exchange.h"
 #include "gemv_core.h"
+#include "sampler.h"
 
 namespace tsd {
 namespace {
@@ -401,6 +402,7 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
             const float t = pick(part, er);
             if (eon && erow < N) {
                 glb(a.logits)[erow] = t;
+                if (a.samp_mode) xchg::store(a.x_logit + erow, t, io.dst_ep);
                 const unsigned long long key =
                     ((unsigned long long)float_order_key(t) << 32) | (0xFFFFFFFFu - (uint32_t)erow);
                 best = key > best ? key : best;
@@ -665,11 +667,16 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
     constexpr int OUT_FC_K = C::GPT2 ? OUT_GELU : OUT_SWIGLU;
     const ArgsPtr ap = (ArgsPtr)args;
 
-    __shared__ float xl[MAX_K];
+    // the phase input buffer; after the head, workgroup 0 reuses it for the top-k draw
+    constexpr size_t KEYS_BYTES = ((size_t)C::V * 4 + 15) & ~(size_t)15;
+    constexpr size_t SAMP_BYTES = KEYS_BYTES + sizeof(samp::Scratch);
+    constexpr size_t RAW_BYTES = MAX_K * 4 > SAMP_BYTES ? MAX_K * 4 : SAMP_BYTES;
+    static_assert(RAW_BYTES <= 56 * 1024, "LDS of one workgroup");
+    __shared__ __align__(16) unsigned char raw[RAW_BYTES];
     __shared__ float red[2 * NWAVE];
     __shared__ float ml[C::H * SG * 2];
     __shared__ int s_abort;
-    Smem sm{xl, red, ml, &s_abort};
+    Smem sm{(float*)raw, red, ml, &s_abort};
 
     if (threadIdx.x == 0) s_abort = 0;
     Ctx cx;
@@ -778,9 +785,35 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
     io.dst_ep = eh;
     if (!gemv_phase<C, C::D, C::V, C::NL_HEAD, IN_NORM, OUT_HEAD, C::GPT2>(a, cx, a.head, io, sm)) return give_up(a);
 
+    if (blockIdx.x != 0) return;
+    if (a.samp_mode) {
+        // top-k draw (workgroup 0) over every logit, from the exchange words
+        const int t = threadIdx.x;
+        uint32_t* keys = (uint32_t*)raw;
+        samp::Scratch& S = *(samp::Scratch*)(raw + KEYS_BYTES);
+        constexpr int JV = (C::V + NT - 1) / NT;
+        auto addr = [&](int q) { return a.x_logit + min(t + NT * q, C::V - 1); };
+        uint64_t w[JV];
+#pragma unroll
+        for (int q = 0; q < JV; ++q) w[q] = xchg::load(addr(q));
+        if (!xchg::settle_n(w, JV, addr, eh, cx.limit, a.abort_word)) s_abort = 1;
+#pragma unroll
+        for (int q = 0; q < JV; ++q)
+            if (t + NT * q < C::V) keys[t + NT * q] = float_order_key(xchg::value(w[q]));
+        __syncthreads();
+        if (s_abort) return give_up(a);
+        const float u = samp::uniform24(a.seed, 0u, (uint32_t)cx.pos, 0u);
+        const int id = samp::topk_draw<NT>(keys, C::V, a.top_k, a.temperature, u, S);
+        if (t == 0) {
+            *glb(a.tok) = id;
+            glb(a.hist)[cx.pos] = id;
+            *glb(a.pos) = cx.pos + 1;
+            *glb(a.ctr) = ctr + 1u;
+        }
+        return;
+    }
     // greedy sampler, last stage (workgroup 0): the best of the per-workgroup keys; ties go to
     // the lowest index because the key's low word is the inverted index
-    if (blockIdx.x != 0) return;
     constexpr int HEAD_TILES = Geo<C::F, C::D, C::V, C::NL_HEAD>::TILES;
     const int nb = min((int)gridDim.x, HEAD_TILES);
     unsigned long long bk = 0ull;

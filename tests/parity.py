@@ -30,3 +30,26 @@ def ids_agree(got_id, ref_logits) -> bool:
     if int(got_id) == best:
         return True
     return top2_gap(ref_logits) < TIE_GAP and ref_logits[int(got_id)] >= ref_logits[best] - TIE_GAP
+
+
+DRAW_MARGIN = 1e-4
+
+
+def topk_draw_margins(logits, k, temperature, u):
+    """For the top-k draw (temperature, k largest with ties to the lower index, softmax, first
+    index in descending order whose cumulative mass exceeds u * total), in fp64:
+    (distance of u * total from the nearest cumulative boundary, relative to the total;
+     gap between the k-th and (k+1)-th largest logit, inf when k covers the vocabulary).
+    A fp32 draw may legitimately differ from the fp64 one when the first is below DRAW_MARGIN
+    or the second below TIE_GAP."""
+    v = np.asarray(logits, np.float64).ravel()
+    n = v.size
+    k = n if k <= 0 or k > n else k
+    order = sorted(range(n), key=lambda i: (-v[i], i))
+    top = order[:k]
+    z = np.exp(v[top] / temperature - v[top[0]] / temperature)
+    c = np.cumsum(z)
+    total = c[-1]
+    margin = float(np.min(np.abs(c - u * total)) / total)
+    gap = float(v[order[k - 1]] - v[order[k]]) if k < n else float("inf")
+    return margin, gap

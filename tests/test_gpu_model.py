@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import REL_TOL, ids_agree, rel_err, top2_gap
+from parity import DRAW_MARGIN, REL_TOL, TIE_GAP, ids_agree, rel_err, top2_gap, topk_draw_margins
 from quantized_gemv_kv_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -33,7 +33,10 @@ MODES = ["persistent", "per_operator"]
 
 def gpu_model(cfg, w, mode="persistent", n_wg=0):
     from quantized_gemv_kv_amd import Model
-    m = Model(dict(cfg, launch_mode=mode, n_workgroups=n_wg), w)
+    samp = None
+    if cfg.get("sample_mode", 0):
+        samp = dict(mode=1, top_k=cfg["top_k"], temperature=cfg["temperature"], seed=cfg["seed"])
+    m = Model(dict(cfg, launch_mode=mode, n_workgroups=n_wg), w, sampling=samp)
     # the launch mode asked for is the one that runs (the step kernel is timed only when it exists)
     assert m.uses_persistent_step() == (mode == "persistent"), "persistent step not built for this shape"
     return m
@@ -96,6 +99,37 @@ def test_small_llama_gqa_head128(mode):
     say(f"[model-small] llama gqa hd128 {mode}")
     w = synth.model_weights(cfg, 7, norm_std=0.5)
     teacher_forced(cfg, w, n_prompt=70, n_steps=20, mode=mode)     # crosses a 64-key tile boundary
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("arch,fmt", [("gpt2", "q4_0"), ("llama", "q8_0")])
+def test_small_models_topk_teacher_forced(arch, fmt, mode):
+    """Top-k sampling on the device: both sides get the oracle's sampled id as the next input;
+    the GPU's draw must equal the oracle's unless the oracle's u * total lies within 1e-4 of a
+    cumulative boundary or the k-th and (k+1)-th logits are within 1e-3."""
+    k, T, seed = 5, 0.8, 1234
+    cfg = synth.small_config(arch, fmt, d_ff=256, n_ctx=64, sample_mode=1, top_k=k, temperature=T, seed=seed)
+    say(f"[model-small] top-k {arch} {fmt} {mode}")
+    w = synth.model_weights(cfg, 42, norm_std=0.5)
+    om = oracle.OracleModel(cfg, w)
+    gm = gpu_model(cfg, w, mode)
+    toks = synth.prompt_tokens(cfg, 6, seed=2)
+    o_ids = om.prefill(toks)
+    g_ids = gm.prefill(dev(toks)).cpu().numpy()
+    checked = 0
+    for s in range(40):
+        pos = om.n_past - 1
+        lo, lg = om.logits()[0], gm.logits().cpu().numpy()[0]
+        assert rel_err(lg, lo) <= REL_TOL, (s, rel_err(lg, lo))
+        margin, gap = topk_draw_margins(lo, k, T, oracle.uniform24(seed, 0, pos, 0))
+        if margin >= DRAW_MARGIN and gap >= TIE_GAP:
+            assert int(g_ids[0, 0]) == int(o_ids[0, 0]), (s, g_ids, o_ids, margin, gap)
+            checked += 1
+        g_ids = gm.step(dev(o_ids)).cpu().numpy()
+        o_ids = om.step(o_ids)
+    assert checked >= 30
+    gm.synchronize()
+    gm.close()
 
 
 @pytest.mark.parametrize("n_wg", [1, 7, 37])

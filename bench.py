@@ -3,7 +3,11 @@
 Workload (the pages' T3 decoder at its real shape): a 24-layer GPT-2-Medium-shaped speech-token
 decoder, d 1024, 16 heads x 64, FFN 4096, learned positions, vocab 8192 head, Q4_0 weights,
 fp32 norms/embeddings ~N(0, 0.02), fp16 KV cache; 256-token prefill, then greedy decode steps at
-positions 256 .. 255+K, batch 1.  All inputs are seeded synthetic data.
+positions 256 .. 255+K, batch 1.  All inputs are seeded synthetic data.  --workload
+llama520m_q8_0 times the 30-layer Llama-shaped Q8_0 decoder instead (300-token prefill).
+
+The line also carries "gemv": the standalone quantized GEMV on one 524288 x 1024 Q8_0 matrix
+(~570 MB, more than the Infinity Cache holds), where a launch is amortised.
 
 One step = one replay of the captured decode graph (every layer, the head and the greedy
 sampler); by default the graph holds one persistent launch that runs the whole step.  W warm-up
@@ -26,6 +30,13 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+# workload name -> (prompt positions, default steps, description, dtype)
+WORKLOADS = {
+    "gpt2_medium_q4_0": (256, 500, "GPT-2-Medium-shaped 24-layer speech-token decoder, Q4_0, 256-token prefill then {K} "
+                                   "greedy decode steps, batch 1", "q4_0 weights, fp32 accumulate, fp16 kv"),
+    "llama520m_q8_0": (300, 600, "Llama-shaped ~520M 30-layer speech-token decoder, Q8_0, 300-token prefill then {K} "
+                                 "greedy decode steps, batch 1", "q8_0 weights, fp32 accumulate, fp16 kv"),
+}
 WORKLOAD = "gpt2_medium_q4_0"
 PROMPT = 256
 
@@ -33,11 +44,14 @@ PROMPT = 256
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--workload", default="gpt2_medium_q4_0", choices=sorted(WORKLOADS),
+                    help="the decoder timed (the default is the one the headline metric is quoted on)")
+    ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemv", action="store_true", help="skip the standalone tall-GEMV measurement")
     ap.add_argument("--eager", action="store_true",
                     help="enqueue each step kernel by kernel instead of replaying the graph (for counter "
                          "collection, which cannot follow graph launches); prefill is skipped: the cache "
@@ -54,12 +68,12 @@ STEP_SOURCES = ["quantized_gemv_kv_amd/csrc/" + f for f in ("step.hip", "exchang
 COUNTERS = os.path.join(ROOT, "profiles", "step_gpt2_medium_q4_0_counters.json")
 
 
-def counted_traffic(kernel):
+def counted_traffic(kernel, workload="gpt2_medium_q4_0"):
     """HBM-side bytes per launch of the step kernel from the committed FETCH_SIZE / WRITE_SIZE
     summary (scaled by the copy calibration), or None when that summary was taken on other
     kernel sources than the ones built now."""
     import hashlib
-    if kernel != "step" or not os.path.exists(COUNTERS):
+    if kernel != "step" or workload != "gpt2_medium_q4_0" or not os.path.exists(COUNTERS):
         return None
     h = hashlib.sha256()
     for f in STEP_SOURCES:
@@ -68,6 +82,47 @@ def counted_traffic(kernel):
     with open(COUNTERS) as fh:
         d = json.load(fh)
     return d["traffic_bytes_per_launch"] if d.get("sources_sha256_16") == h.hexdigest()[:16] else None
+
+
+TALL_N, TALL_K = 524288, 1024      # one Q8_0 GEMV of ~570 MB, larger than the 256 MB Infinity Cache
+
+
+def gemv_headline(seed, reps=7):
+    """The quantized GEMV alone at a size where a launch is amortised: y = W x with W a
+    524288 x 1024 Q8_0 matrix (the lone-GEMV law), x ~ N(0,1), batch 1; the median over `reps`
+    bursts of 10 back-to-back launches timed with HIP events.  Bytes = the stored matrix + x + y."""
+    import torch
+    from quantized_gemv_kv_amd import binding, roofline, synth
+    N, K = TALL_N, TALL_K
+    canon = torch.empty(roofline.matrix_bytes("q8_0", N, K), dtype=torch.uint8, device="cuda")
+    row_b = K // 32 * 34
+    for r0, blob in synth.q8_0_row_chunks(N, K, seed):
+        canon[r0 * row_b: r0 * row_b + blob.size].copy_(torch.from_numpy(blob))
+    packed = torch.empty(binding.tsd_gemv_packed_bytes("q8_0", N, K), dtype=torch.uint8, device="cuda")
+    binding.tsd_gemv_pack("q8_0", canon, N, K, packed)
+    del canon
+    x = torch.from_numpy(synth.normal_f32(synth.rng_for(seed, 1), (1, K))).cuda()
+    y = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        binding.tsd_gemv("q8_0", packed, N, K, 1, x, None, y)
+    # median over short bursts of back-to-back launches (about 1 ms each, timed with HIP events
+    # around the burst): long runs of full-bandwidth streaming are slowed by the board's power
+    # management, which would make the figure depend on the run length
+    burst, times = 10, []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(burst):
+            binding.tsd_gemv("q8_0", packed, N, K, 1, x, None, y)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / burst)
+    us = float(np.median(times))
+    nbytes = roofline.gemv_bytes("q8_0", N, K)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"shape": f"Q8_0 {N}x{K}, batch 1", "bytes": nbytes, "us": us, "gbs": gbs,
+            "frac": gbs / roofline.HBM_PEAK_GBS, "timing": f"median over {reps} bursts of {burst} back-to-back launches"}
 
 
 def cpu_baseline(cfg, weights, seconds, seed):
@@ -89,7 +144,7 @@ def cpu_baseline(cfg, weights, seconds, seed):
             break
     om.close()
     return {"value": n / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} decode steps of the same 24-layer model at positions {PROMPT}..{PROMPT + n - 1} "
+            "sample": f"{n} decode steps of the same {cfg['n_layer']}-layer model at positions {PROMPT}..{PROMPT + n - 1} "
                       f"over a random {PROMPT}-position fp16 cache, single-threaded fp64 oracle, {el:.1f} s"}
 
 
@@ -102,6 +157,11 @@ def main():
     import torch
     from quantized_gemv_kv_amd import Model, roofline, synth
 
+    global WORKLOAD, PROMPT
+    WORKLOAD = args.workload
+    PROMPT, default_steps, desc, dtype = WORKLOADS[WORKLOAD]
+    if args.steps is None:
+        args.steps = default_steps
     cfg = dict(synth.config(WORKLOAD), launch_mode=args.launch_mode)
     K, W = args.steps, args.warmup
     if PROMPT + max(K, W) > cfg["n_ctx"]:
@@ -169,14 +229,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q4_0 weights, fp32 accumulate, fp16 kv",
+        "dtype": dtype,
         "data": "synthetic (seeded random weights, prompt ids and values; no checkpoint)",
-        "config": {"workload": "GPT-2-Medium-shaped 24-layer speech-token decoder, Q4_0, 256-token prefill then "
-                               f"{K} greedy decode steps, batch 1",
-                   "d_model": 1024, "n_layer": 24, "n_head": 16, "d_ff": 4096, "vocab": 8192,
+        "config": {"workload": desc.format(K=K), "d_model": cfg["d_model"], "n_layer": cfg["n_layer"],
+                   "n_head": cfg["n_head"], "d_ff": cfg["d_ff"], "vocab": cfg["vocab"],
                    "prompt": PROMPT, "global_batch": 1, "launch_mode": mode, "workgroups": n_wg},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": roofline.HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / roofline.HBM_PEAK_GBS, "traffic": counted_traffic(dom),
+                     "frac": achieved / roofline.HBM_PEAK_GBS, "traffic": counted_traffic(dom, WORKLOAD),
                      "kernel": dom, "launch_us": dom_us, "launches_per_step": dom_n,
                      "bytes_per_launch": dom_bytes},
         "kernel_us": {k: round(v[0], 3) for k, v in kinds.items()},
@@ -193,6 +252,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         result["calibration_copy_bytes"] = 2 * n * 4
+    if not args.no_gemv:
+        result["gemv"] = gemv_headline(args.seed)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, weights, args.cpu_seconds, args.seed)
     model.close()

@@ -207,7 +207,8 @@ tsd_status tsd_gemv_pack(int wfmt, const void* d_w, size_t w_bytes, int N, int K
                          size_t packed_bytes, void* stream);
 /* Fused block-dequant GEMV on the packed layout: d_y[b][n] = sum_k W[n][k] d_x[b][k]
  * (+ d_bias[n] if not NULL) for b < B (1 <= B <= 4), fp32 accumulation
- * ([J] §3.15 mat-vec with the bias added in the same kernel). */
+ * ([J] §3.15 mat-vec with the bias added in the same kernel).  The matrix is read with
+ * non-temporal loads (it is streamed once per call). */
 tsd_status tsd_gemv(int wfmt, const void* d_packed, int N, int K, int B, const float* d_x,
                     const float* d_bias, float* d_y, void* stream);
 

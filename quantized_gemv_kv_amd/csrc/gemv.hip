@@ -90,7 +90,9 @@ __device__ __forceinline__ void epi_pair(const EpiArgs& e, int row, float t0, fl
 
 template <int EPI> struct EpiIsPair { static constexpr bool v = EPI == EPI_SWIGLU || EPI == EPI_QKV_ROPE; };
 
-template <int F, int SPL, int NLOAD, int PRO, int EPI>
+// STREAM: the weight loads carry the non-temporal hint (a matrix read once, larger than the
+// caches: the hint keeps it from displacing what stays resident and streams measurably faster)
+template <int F, int SPL, int NLOAD, int PRO, int EPI, bool STREAM = false>
 __global__ __launch_bounds__(WG) void k_gemv(const PackedMat W, const ProArgs pa, const EpiArgs ea)
 {
     constexpr int E = FmtT<F>::E, SPS = FmtT<F>::SLOTS_PER_SCALE, G = FmtT<F>::SCALE_GROUP;
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(WG) void k_gemv(const PackedMat W, const ProArgs pa
     static_assert(SPL == 1 || NLOAD % SPL == 0, "whole rows per wave");
     static_assert(!PAIR || NP % 2 == 0, "pair epilogues need an even number of rows per lane");
 
-    __shared__ float4 xl4[MAX_K / 4];
+    extern __shared__ float4 xl4[];   // [K / 4], sized at launch (a fixed MAX_K buffer would cost occupancy)
     __shared__ float red[2 * NWAVE];
     __shared__ unsigned long long bkey[NWAVE];
 
@@ -130,7 +132,14 @@ __global__ __launch_bounds__(WG) void k_gemv(const PackedMat W, const ProArgs pa
         const int slot = SPL == 1 ? slot0 : (i % SPL) * 64 + lane;
         ok[i] = row < N && slot < lpr;
         const int rr = row < N ? row : N - 1, ss = slot < lpr ? slot : lpr - 1;
-        w[i] = *(const uint4*)(W.q + (size_t)rr * rb + (size_t)ss * 16);
+        const uint4* wp = (const uint4*)(W.q + (size_t)rr * rb + (size_t)ss * 16);
+        if constexpr (STREAM) {
+            typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+            const v4u v = __builtin_nontemporal_load((const v4u*)wp);
+            w[i] = make_uint4(v.x, v.y, v.z, v.w);
+        } else {
+            w[i] = *wp;
+        }
         sc_raw[i] = __half_as_ushort(W.s[(size_t)rr * spr + ss / SPS]);
         if constexpr (F == FMT_AFF8) sb_raw[i] = __half_as_ushort(W.b[(size_t)rr * spr + ss / SPS]);
     }
@@ -241,24 +250,27 @@ int rows_per_block_impl(int fmt, int K)
     return NWAVE * rpw;
 }
 
-template <int F, int PRO, int EPI, int SPL>
+template <int F, int PRO, int EPI, int SPL, bool STREAM = false>
 hipError_t go(const PackedMat& W, const ProArgs& pa, const EpiArgs& ea, hipStream_t st)
 {
-    constexpr int NLOAD = nload_for<SPL>();
-    const int rpb = rows_per_block_impl(F, W.K);
+    // a streamed matrix keeps twice the loads in flight per lane when a row fits one wave
+    constexpr int NLOAD = STREAM && SPL == 1 ? 4 : nload_for<SPL>();
+    const int lpr = W.K / FmtT<F>::E;
+    const int rpb = NWAVE * (SPL == 1 ? NLOAD * (64 / lpr) : NLOAD / SPL);
     const int grid = (W.N + rpb - 1) / rpb;
-    hipLaunchKernelGGL((k_gemv<F, SPL, NLOAD, PRO, EPI>), dim3(grid), dim3(WG), 0, st, W, pa, ea);
+    hipLaunchKernelGGL((k_gemv<F, SPL, NLOAD, PRO, EPI, STREAM>), dim3(grid), dim3(WG), (size_t)W.K * sizeof(float), st, W, pa,
+                       ea);
     return hipGetLastError();
 }
 
-template <int F, int PRO, int EPI>
+template <int F, int PRO, int EPI, bool STREAM = false>
 hipError_t go_spl(const PackedMat& W, const ProArgs& pa, const EpiArgs& ea, hipStream_t st)
 {
     switch (spl_for(F, W.K)) {
-    case 1: return go<F, PRO, EPI, 1>(W, pa, ea, st);
-    case 2: return go<F, PRO, EPI, 2>(W, pa, ea, st);
-    case 3: return go<F, PRO, EPI, 3>(W, pa, ea, st);
-    case 4: return go<F, PRO, EPI, 4>(W, pa, ea, st);
+    case 1: return go<F, PRO, EPI, 1, STREAM>(W, pa, ea, st);
+    case 2: return go<F, PRO, EPI, 2, STREAM>(W, pa, ea, st);
+    case 3: return go<F, PRO, EPI, 3, STREAM>(W, pa, ea, st);
+    case 4: return go<F, PRO, EPI, 4, STREAM>(W, pa, ea, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -372,6 +384,90 @@ hipError_t launch_gemv(int fmt, int pro, int epi, const PackedMat& W, const ProA
     case FMT_Q4_0: return go_fmt<FMT_Q4_0>(pro, epi, W, pa, ea, st);
     case FMT_Q8_0: return go_fmt<FMT_Q8_0>(pro, epi, W, pa, ea, st);
     case FMT_AFF8: return go_fmt<FMT_AFF8>(pro, epi, W, pa, ea, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+namespace {
+// y = W x (+bias) for a matrix streamed once, rows of at most one wave (slots per row a power of
+// two <= 64): every lane issues its NL weight loads (non-temporal) and scale loads first, then x
+// is staged in LDS, then the lane dots its slot with each of its rows; lane r of a row group
+// writes the group's row r.
+template <int F, int NL>
+__global__ __launch_bounds__(WG) void k_gemv_stream(const PackedMat W, const float* __restrict__ x,
+                                                    const float* __restrict__ bias, float* __restrict__ y)
+{
+    constexpr int E = FmtT<F>::E, SPS = FmtT<F>::SLOTS_PER_SCALE, G = FmtT<F>::SCALE_GROUP;
+    extern __shared__ float4 xl4[];
+    const int K = W.K, N = W.N, lpr = K / E, spr = K / G;
+    const size_t rb = F == FMT_Q4_0 ? (size_t)K / 2 : (size_t)K;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int slot = lane & (lpr - 1), sub = lane / lpr;
+    const int row0 = ((blockIdx.x * NWAVE + wave) * (64 / lpr) + sub) * NL;
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    uint4 w[NL];
+    uint32_t sc[NL], sb[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int row = min(row0 + i, N - 1);
+        const v4u v = __builtin_nontemporal_load((const v4u*)(W.q + (size_t)row * rb + (size_t)slot * 16));
+        w[i] = make_uint4(v.x, v.y, v.z, v.w);
+        sc[i] = __half_as_ushort(W.s[(size_t)row * spr + slot / SPS]);
+        if constexpr (F == FMT_AFF8) sb[i] = __half_as_ushort(W.b[(size_t)row * spr + slot / SPS]);
+    }
+    const int er = min(row0 + (slot < NL ? slot : NL - 1), N - 1);
+    const float bv = bias ? bias[er] : 0.f;
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    for (int c = threadIdx.x; c < K / 4; c += WG) xl4[swz<E>(4 * c, lpr)] = ((const float4*)x)[c];
+    __syncthreads();
+    float xs[E];
+    float sx = 0.f;
+#pragma unroll
+    for (int e4 = 0; e4 < E / 4; ++e4) {
+        const float4 v = xl4[e4 * lpr + slot];
+        xs[4 * e4] = v.x;
+        xs[4 * e4 + 1] = v.y;
+        xs[4 * e4 + 2] = v.z;
+        xs[4 * e4 + 3] = v.w;
+        sx += (v.x + v.y) + (v.z + v.w);
+    }
+    float part[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const float d = slot_dot<F>(w[i], xs);
+        const float s = __half2float(__ushort_as_half((unsigned short)sc[i]));
+        float v;
+        if constexpr (F == FMT_Q4_0) v = s * fmaf(-8.f, sx, d);
+        else if constexpr (F == FMT_Q8_0) v = s * fmaf(-128.f, sx, d);
+        else v = fmaf(s, d, __half2float(__ushort_as_half((unsigned short)sb[i])) * sx);
+        part[i] = group_sum(v, lpr);
+    }
+    float t = part[0];
+#pragma unroll
+    for (int i = 1; i < NL; ++i) t = slot == i ? part[i] : t;
+    if (slot < NL && row0 + slot < N) y[row0 + slot] = t + bv;
+}
+}  // namespace
+
+hipError_t launch_gemv_stream(int fmt, const PackedMat& W, const ProArgs& pa, const EpiArgs& ea, hipStream_t st)
+{
+    if (W.K > MAX_K || !gemv_shape_ok(fmt, W.K) || W.N <= 0) return hipErrorInvalidValue;
+    const int lpr = W.K / fmt_elems_per_slot(fmt);
+    if (lpr <= 64 && lpr >= 4) {   // rows fit one wave and a row group holds at least NL lanes
+        constexpr int NL = 4;
+        const int rpb = NWAVE * (64 / lpr) * NL;
+        const dim3 grid((W.N + rpb - 1) / rpb);
+        const size_t lds = (size_t)W.K * sizeof(float);
+        if (fmt == FMT_Q4_0) hipLaunchKernelGGL((k_gemv_stream<FMT_Q4_0, NL>), grid, dim3(WG), lds, st, W, pa.src, ea.bias, ea.y);
+        else if (fmt == FMT_Q8_0) hipLaunchKernelGGL((k_gemv_stream<FMT_Q8_0, NL>), grid, dim3(WG), lds, st, W, pa.src, ea.bias, ea.y);
+        else hipLaunchKernelGGL((k_gemv_stream<FMT_AFF8, NL>), grid, dim3(WG), lds, st, W, pa.src, ea.bias, ea.y);
+        return hipGetLastError();
+    }
+    switch (fmt) {
+    case FMT_Q4_0: return go_spl<FMT_Q4_0, PRO_LOAD, EPI_STORE, true>(W, pa, ea, st);
+    case FMT_Q8_0: return go_spl<FMT_Q8_0, PRO_LOAD, EPI_STORE, true>(W, pa, ea, st);
+    case FMT_AFF8: return go_spl<FMT_AFF8, PRO_LOAD, EPI_STORE, true>(W, pa, ea, st);
     default: return hipErrorInvalidValue;
     }
 }

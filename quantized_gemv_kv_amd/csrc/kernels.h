@@ -64,6 +64,8 @@ struct EpiArgs {
 // Launch the fused GEMV y = epilogue(W . prologue(x)).  Returns hipSuccess or the launch error.
 hipError_t launch_gemv(int fmt, int pro, int epi, const PackedMat& W, const ProArgs& pa, const EpiArgs& ea,
                        hipStream_t st);
+// y = W x (+bias) with the weight loads marked non-temporal: for a matrix streamed once
+hipError_t launch_gemv_stream(int fmt, const PackedMat& W, const ProArgs& pa, const EpiArgs& ea, hipStream_t st);
 // the tile (rows per workgroup) the launcher uses for a shape; for byte/launch accounting
 int gemv_rows_per_block(int fmt, int K, int epi);
 

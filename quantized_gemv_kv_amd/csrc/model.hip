@@ -907,7 +907,7 @@ tsd_status tsd_gemv(int wfmt, const void* d_packed, int N, int K, int B, const f
         EpiArgs ea{};
         ea.y = d_y + (size_t)b * N;
         ea.bias = d_bias;
-        hipError_t e = launch_gemv(wfmt, PRO_LOAD, EPI_STORE, W, pa, ea, (hipStream_t)stream);
+        hipError_t e = launch_gemv_stream(wfmt, W, pa, ea, (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(nullptr, e, "gemv");
     }
     return TSD_OK;

@@ -44,6 +44,14 @@ def q8_0_matrix(rng, N, K, dscale=0.01):
     return blob.reshape(-1), {"q": q, "d": d}
 
 
+def q8_0_row_chunks(N, K, seed, chunk_rows=65536):
+    """A tall Q8_0 matrix in row chunks (the lone-GEMV law, each chunk from its own seeded
+    stream), so that hundreds of MB never sit in host memory at once: yields (row0, blob)."""
+    for r0 in range(0, N, chunk_rows):
+        n = min(chunk_rows, N - r0)
+        yield r0, q8_0_matrix(rng_for(seed, r0, K), n, K)[0]
+
+
 def q4_0_matrix(rng, N, K, dscale=0.02):
     """4-bit q uniform in 0..15, fp16 d = |N(0,1)| * dscale."""
     assert K % 32 == 0

@@ -73,6 +73,35 @@ def test_gemv_matches_oracle(fmt, N, K, B):
     assert np.all(np.abs(got - ref) <= 4 * K * 2.0 ** -24 * mag + 1e-30)
 
 
+def test_tall_gemv_sampled_rows():
+    """The tall Q8_0 GEMV the benchmark times (524288 x 1024, ~570 MB), in the same launch
+    configuration; 96 sampled rows checked against the oracle row by row."""
+    torch = _t()
+    from quantized_gemv_kv_amd import binding as tb
+    N, K, seed = 524288, 1024, 42
+    say("[gemv] tall q8_0 524288 x 1024")
+    row_b = K // 32 * 34
+    canon = torch.empty(N * row_b, dtype=torch.uint8, device="cuda")
+    rows = np.sort(synth.rng_for(5).choice(N, size=96, replace=False))
+    rows = np.concatenate([[0, N - 1], rows])
+    blobs = {}
+    for r0, blob in synth.q8_0_row_chunks(N, K, seed):
+        canon[r0 * row_b: r0 * row_b + blob.size].copy_(torch.from_numpy(blob))
+        for r in rows[(rows >= r0) & (rows < r0 + blob.size // row_b)]:
+            blobs[int(r)] = blob[(r - r0) * row_b:(r - r0 + 1) * row_b].copy()
+    packed = torch.empty(tb.tsd_gemv_packed_bytes("q8_0", N, K), dtype=torch.uint8, device="cuda")
+    tb.tsd_gemv_pack("q8_0", canon, N, K, packed)
+    del canon
+    x = synth.normal_f32(synth.rng_for(seed, 1), (1, K))
+    y = torch.full((1, N), float("nan"), dtype=torch.float32, device="cuda")
+    tb.tsd_gemv("q8_0", packed, N, K, 1, dev(x), None, y)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()[0]
+    assert np.all(np.isfinite(got))
+    ref = np.array([oracle.gemv_f32("q8_0", blobs[int(r)], 1, K, x, None)[0, 0] for r in rows])
+    assert rel_err(got[rows], ref) <= REL_TOL
+
+
 def test_gemv_rejects_bad_shapes():
     torch = _t()
     from quantized_gemv_kv_amd import binding as tb

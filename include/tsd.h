@@ -212,6 +212,19 @@ tsd_status tsd_gemv_pack(int wfmt, const void* d_w, size_t w_bytes, int N, int K
 tsd_status tsd_gemv(int wfmt, const void* d_packed, int N, int K, int B, const float* d_x,
                     const float* d_bias, float* d_y, void* stream);
 
+/* Batched GEMM on the matrix cores for the 8-bit affine layout ([F] §8: batched rollouts turn
+ * the memory-bound mat-vec into a skinny product; §3: affine groups of 64):
+ * d_y[b][n] = sum_k W[n][k] d_x[b][k] for b < B (1 <= B <= 16), W packed by tsd_gemv_pack
+ * (TSD_W_AFFINE8_G64), d_x [B][K] and d_y [B][N] fp32 (device, caller-owned, d_y is
+ * overwritten).  Each x is split into two fp16 numbers (hi, x - hi) and each weight enters
+ * exactly (1024 + q in fp16); products accumulate in fp32, the group's scale and bias are
+ * applied in fp32.  K must be a multiple of 64 and at most 4096.  `splits` (1..8, at most K/64)
+ * cuts K into slices run by separate workgroups and summed afterwards.  d_scratch (256-byte
+ * aligned, tsd_gemm_rows_scratch_bytes) holds the operand and the slices. */
+tsd_status tsd_gemm_rows_scratch_bytes(int N, int K, int splits, size_t* out_bytes);
+tsd_status tsd_gemm_rows(const void* d_packed, int N, int K, int B, const float* d_x, float* d_y,
+                         int splits, void* d_scratch, size_t scratch_bytes, void* stream);
+
 /* Split-KV flash-decode attention of one query per head over an fp16 cache
  * ([J] §3.13: cache laid out head-dim fastest, then position, then head; no mask for a single
  * new token): d_q [B][H][hd] fp32, d_k/d_v [B][Hkv][n_ctx][hd] fp16, attends keys

@@ -147,7 +147,81 @@ bool topk_supported(int n, int k);
 hipError_t launch_topk(const float* logits, int n, int k, float temperature, unsigned long long seed, int row, int pass,
                        int* posp, int pos_value, int* out, int* hist, int hist_stride, hipStream_t st);
 
+// ---- batched frame operators (frame.hip) -------------------------------------------------------
+// Up to MM_ROWS rows of activations go through the matrix cores together.  Every GEMM operand
+// buffer holds MM_ROWS rows; rows past the batch stay zero.
+constexpr int MM_ROWS = 16;
+constexpr int MM_MAX_SPLIT = 8;   // split-K slices of one GEMM, at most
+constexpr int MM_MAX_K = 4096;    // longest reduction dimension
+
+// a GEMM operand: x split into fp16 hi + lo (x - hi), and sum(hi + lo) over each group of 64
+struct Act16 {
+    __half* hi;        // [MM_ROWS][K]
+    __half* lo;        // [MM_ROWS][K]
+    float* gsum;       // [MM_ROWS][K / 64]
+};
+
+// prep: v = x[b] (+ sum over s < n_part of part[s][b]; then v is written back to x[b]);
+// y = v, or RMSNorm(v) * g; the operand of y; optionally y itself to norm_out[b]
+struct PrepArgs {
+    float* x;
+    int ldx;
+    const float* part;   // [n_part][MM_ROWS][ldx]
+    int n_part;
+    const float* g;      // null: no norm
+    float eps;
+    int K, rows;
+    Act16 a;
+    float* norm_out;     // [rows][K] or null
+};
+
+enum Mm16Epi : int { MM_STORE = 0, MM_SWIGLU = 1, MM_QKV_ROPE = 2 };
+struct Mm16Out {
+    float* y;            // STORE: y[split][b][n] at y + split * slice + b * ldy + n; SWIGLU: y[b][n/2]
+    int ldy;
+    long long slice;
+    int rows;            // activation rows b < rows are written
+    // QKV_ROPE: rows [0, qrows) and [qrows, qrows + krows) in RoPE pairs (2i, 2i+1) = (i, i+hd/2)
+    // of each head -> rotated q [b][qrows] and K cache; the rest -> V cache; caches
+    // [b][Hkv][n_ctx][hd] at slot pos (*posp, else pos_value)
+    int qrows, krows, hd, Hkv, n_ctx;
+    float* q;
+    __half *kc, *vc;
+    const float2* rope;
+    const int* posp;
+    int pos_value;
+};
+
+struct EmbedTabs {
+    const float* tab[16];
+    int rows[16];
+};
+
+// W: AFF8 (the only format with a matrix-core path), any N, K % 64 == 0, K <= MM_MAX_K
+bool mm16_supported(int fmt, int N, int K);
+hipError_t launch_prep16(const PrepArgs& p, hipStream_t st);
+hipError_t launch_mm16(int epi, const PackedMat& W, const Act16& a, int splits, const Mm16Out& o, hipStream_t st);
+// attention partials (launch_attention layout, max_split slots per head) of rows b < B merged into
+// the operand of [B][H * hd]; n_keys = *posp + 1, else n_keys_value
+hipError_t launch_merge_prep16(const float* part, int B, int H, int hd, int max_split, const int* posp, int n_keys_value,
+                               const Act16& a, hipStream_t st);
+// x[b] = sum over c < n_tab of tab[c][codes[b * ld_codes + c]] for b < B (ids clamped into each table)
+hipError_t launch_embed_sum16(const EmbedTabs& T, const int* codes, int ld_codes, int n_tab, int d, float* x, int B,
+                              hipStream_t st);
+// code[b * ld_code] = argmax of logits[b * ld_l + 0 .. n) for b < B (ties to the lowest index)
+hipError_t launch_argmax_rows(const float* logits, int ld_l, int n, int* code, int ld_code, int B, hipStream_t st);
+// y[i] = sum over s < S of part[s * slice + i] for i < n
+hipError_t launch_sum_slices(const float* part, int S, long long slice, float* y, long long n, hipStream_t st);
+// hist[*pos][0..n) = codes[0..n) (n may be 0), then *pos += 1
+hipError_t launch_frame_done(const int* codes, int n, int* hist, int* pos, hipStream_t st);
+
+// top-k draw for rows b < B: id of logits[b * ld_l ..] at counter (*posp, b, pass) -> out[b * ld_out]
+hipError_t launch_topk_rows(const float* logits, int ld_l, int n, int k, float temperature, unsigned long long seed,
+                            int pass, const int* posp, int* out, int ld_out, int B, hipStream_t st);
+
 // ---- small state kernels ---------------------------------------------------------------------
+// dst[r * cols + c] = src[r * src_stride + c]
+hipError_t launch_gather_i32(int* dst, const int* src, int rows, int cols, long long src_stride, hipStream_t st);
 hipError_t launch_copy_i32(int* dst, const int* src, int n, hipStream_t st);
 hipError_t launch_fill_i32(int* dst, int value, int n, hipStream_t st);
 hipError_t launch_fill_u32(unsigned int* dst, unsigned int value, int n, hipStream_t st);

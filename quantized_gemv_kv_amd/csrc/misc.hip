@@ -16,6 +16,13 @@ __global__ void k_fill(T* d, T v, size_t n)
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) d[i] = v;
 }
+__global__ void k_gather_i32(int* __restrict__ d, const int* __restrict__ s, int rows, int cols, long long stride)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= rows * cols) return;
+    const int r = i / cols, c = i - r * cols;
+    d[i] = s[r * stride + c];
+}
 __global__ void k_copy_bytes(uint8_t* __restrict__ d, const uint8_t* __restrict__ s, size_t n)
 {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -37,6 +44,13 @@ hipError_t launch_copy_i32(int* dst, const int* src, int n, hipStream_t st)
 {
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_copy_i32, dim3((n + 255) / 256), dim3(256), 0, st, dst, src, n);
+    return hipGetLastError();
+}
+hipError_t launch_gather_i32(int* dst, const int* src, int rows, int cols, long long src_stride, hipStream_t st)
+{
+    const int n = rows * cols;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_gather_i32, dim3((n + 255) / 256), dim3(256), 0, st, dst, src, rows, cols, src_stride);
     return hipGetLastError();
 }
 hipError_t launch_fill_i32(int* d, int v, int n, hipStream_t st) { return fill<int>(d, v, (size_t)n, st); }

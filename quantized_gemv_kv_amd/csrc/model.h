@@ -1,0 +1,153 @@
+// model.h — the model object behind the C ABI (internal; shared by model.hip, which runs the
+// batch-1 GPT2/LLAMA step, and talker.hip, which runs the batched Talker + code-predictor frame).
+#pragma once
+
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "tsd.h"
+
+namespace tsd {
+
+struct LayerW {
+    PackedMat qkv, o, fc, down;            // fc = fc (GPT-2) or interleaved gate/up (Llama, Talker)
+    float *n1g = nullptr, *n1b = nullptr, *n2g = nullptr, *n2b = nullptr;
+    float *bqkv = nullptr, *bo = nullptr, *bfc = nullptr, *bdown = nullptr;
+};
+
+// bump planner over the workspace: the same walk sizes it and lays it out
+struct Planner {
+    uint8_t* base;
+    size_t off = 0;
+    explicit Planner(uint8_t* b) : base(b) {}
+    void* take(size_t bytes)
+    {
+        off = align256(off);
+        void* p = base ? base + off : nullptr;
+        off += bytes;
+        return p;
+    }
+};
+
+inline PackedMat take_mat(Planner& P, int f, int N, int K)
+{
+    PackedLayout L = packed_layout(f, N, K);
+    void* p = P.take(L.total);
+    if (!p) {
+        PackedMat m{};
+        m.N = N;
+        m.K = K;
+        return m;
+    }
+    return packed_view(f, p, N, K);
+}
+
+// kernel kinds a timing probe can bracket
+enum { KIND_QKV = 0, KIND_ATTN = 1, KIND_OPROJ = 2, KIND_FC = 3, KIND_DOWN = 4, KIND_HEAD = 5, KIND_STEP = 6, TSD_KERNEL_KINDS = 7 };
+
+struct Probe {
+    int kind = -1;
+    hipEvent_t* ev = nullptr;   // quadruples, consumed in launch order: empty bracket, kernel bracket
+    int next = 0;
+};
+
+// brackets one launch with probe events when its kind is the probed one
+struct Bracket {
+    Probe* p;
+    hipStream_t st;
+    bool on;
+    Bracket(Probe* pr, int kind, hipStream_t s) : p(pr), st(s), on(pr && pr->kind == kind)
+    {
+        if (!on) return;
+        (void)hipEventRecord(p->ev[p->next], st);       // empty bracket: the cost of bracketing
+        (void)hipEventRecord(p->ev[p->next + 1], st);
+        (void)hipEventRecord(p->ev[p->next + 2], st);   // the kernel
+    }
+    ~Bracket()
+    {
+        if (on) (void)hipEventRecord(p->ev[p->next + 3], st), p->next += 4;
+    }
+};
+
+}  // namespace tsd
+
+struct tsd_model {
+    tsd_config c{};
+    tsd_sampling samp{};
+    hipStream_t st = nullptr;
+    uint8_t* ws = nullptr;
+    size_t ws_bytes = 0;
+    int tpp = 1;          // tokens per position
+    int vmax = 0;
+    int qkv_rows = 0;
+    std::vector<tsd::LayerW> L;
+    const float* emb[16] = {};
+    int emb_rows[16] = {};
+    const float* wpe = nullptr;
+    float *nfg = nullptr, *nfb = nullptr;
+    tsd::PackedMat head{};
+    __half *kc = nullptr, *vc = nullptr;
+    size_t kv_layer_elems = 0;
+    float *x = nullptr, *qkv = nullptr, *attn = nullptr, *h = nullptr, *logits = nullptr, *part = nullptr;
+    float2* rope = nullptr;
+    int rope_rows = 0;
+    unsigned long long* best = nullptr;   // per head-workgroup best keys
+    int *pos = nullptr, *tok = nullptr, *hist = nullptr, *dbg_pos = nullptr;
+    // persistent step: kernel (null: one launch per operator), grid, exchange state
+    const void* step_fn = nullptr;
+    int n_wg = 0;
+    tsd::StepArgs sa{};
+    tsd::StepArgs* d_sa = nullptr;    // sa in the workspace (the kernel reads it there)
+    uint64_t* xbuf = nullptr;
+    size_t xbuf_words = 0;
+    uint32_t* ctl = nullptr;          // [0] epoch base (launches), [1] abort word
+    uint64_t launches = 0, max_launches = 0;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    // TALKER_CP: batch rows through the matrix-core GEMM; the code predictor's own layers,
+    // norm, heads and cache; the graph of a frame without head and predictor (prefill)
+    std::vector<tsd::LayerW> Lc;
+    float* cp_nfg = nullptr;
+    tsd::PackedMat cp_head[16] = {};
+    __half *ckc = nullptr, *cvc = nullptr;
+    size_t ckv_layer_elems = 0;
+    float* xc = nullptr;              // predictor residual stream [16][d]
+    float* mmp = nullptr;             // split-K partial sums [MM_MAX_SPLIT][16][d]
+    tsd::Act16 act{};                 // GEMM operand [16][K] as fp16 hi/lo + group sums
+    int split_o = 1, split_down = 1;
+    hipGraph_t graph_talker = nullptr;
+    hipGraphExec_t exec_talker = nullptr;
+    int kind_launches[tsd::TSD_KERNEL_KINDS] = {};
+    // timing probes: events around every launch of one kernel kind
+    std::vector<hipEvent_t> probe_ev[tsd::TSD_KERNEL_KINDS];
+    int n_past = 0;
+    int top_k = 0;                    // effective k of the top-k sampler
+    std::string err;
+};
+
+namespace tsd {
+
+tsd_status fail(tsd_model* m, tsd_status s, const std::string& msg);
+tsd_status hip_fail(tsd_model* m, hipError_t e, const char* what);
+
+#define HIP_TRY(m, expr, what)                              \
+    do {                                                    \
+        hipError_t e_ = (expr);                             \
+        if (e_ != hipSuccess) return hip_fail(m, e_, what); \
+    } while (0)
+
+// ---- TALKER_CP (talker.hip) -------------------------------------------------------------------
+tsd_status talker_validate(const tsd_config* c, std::string& msg);
+void talker_canonical_sizes(const tsd_config* c, size_t (*matrix_bytes)(int, int, int), std::vector<size_t>& sz);
+size_t talker_plan(tsd_model* m, const tsd_config* c, uint8_t* base);
+tsd_status talker_pack(tsd_model* m, const tsd_tensor* w);
+// one frame: Talker layers, head and code c_0; with_cp: the predictor's passes for codes
+// 1..C-1 and the history append.  Without: only the Talker's cache is advanced (prefill).
+hipError_t talker_enqueue(tsd_model* m, hipStream_t st, bool with_cp, Probe* pr = nullptr);
+// Talker layer l on m->x at *pos (tsd_layer_forward)
+hipError_t talker_layer(tsd_model* m, int l, hipStream_t st, const int* pos);
+// launches of each kind in one frame
+void talker_kind_launches(const tsd_model* m, int* out);
+
+}  // namespace tsd

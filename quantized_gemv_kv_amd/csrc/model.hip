@@ -16,88 +16,13 @@
 #include <string>
 #include <vector>
 
-#include "kernels.h"
-#include "tsd.h"
+#include "model.h"
 
 using namespace tsd;
 
-namespace {
+namespace tsd {
 
 thread_local std::string g_err;
-constexpr int MAX_STEP_WG = 1024;          // workgroups of the persistent step, at most
-constexpr long long STEP_SPIN_LIMIT = 2000000;   // 20 ms of the 100 MHz clock per wait
-
-struct LayerW {
-    PackedMat qkv, o, fc, down;            // fc = fc (GPT-2) or interleaved gate/up (Llama)
-    float *n1g = nullptr, *n1b = nullptr, *n2g = nullptr, *n2b = nullptr;
-    float *bqkv = nullptr, *bo = nullptr, *bfc = nullptr, *bdown = nullptr;
-};
-
-// bump planner over the workspace: the same walk sizes it and lays it out
-struct Planner {
-    uint8_t* base;
-    size_t off = 0;
-    explicit Planner(uint8_t* b) : base(b) {}
-    void* take(size_t bytes)
-    {
-        off = align256(off);
-        void* p = base ? base + off : nullptr;
-        off += bytes;
-        return p;
-    }
-};
-
-}  // namespace
-
-// kernel kinds a timing probe can bracket
-enum { KIND_QKV = 0, KIND_ATTN = 1, KIND_OPROJ = 2, KIND_FC = 3, KIND_DOWN = 4, KIND_HEAD = 5, KIND_STEP = 6, TSD_KERNEL_KINDS = 7 };
-
-struct Probe {
-    int kind = -1;
-    hipEvent_t* ev = nullptr;   // quadruples, consumed in launch order: empty bracket, kernel bracket
-    int next = 0;
-};
-
-struct tsd_model {
-    tsd_config c{};
-    tsd_sampling samp{};
-    hipStream_t st = nullptr;
-    uint8_t* ws = nullptr;
-    size_t ws_bytes = 0;
-    int tpp = 1;          // tokens per position
-    int vmax = 0;
-    int qkv_rows = 0;
-    std::vector<LayerW> L;
-    const float* emb[16] = {};
-    int emb_rows[16] = {};
-    const float* wpe = nullptr;
-    float *nfg = nullptr, *nfb = nullptr;
-    PackedMat head{};
-    __half *kc = nullptr, *vc = nullptr;
-    size_t kv_layer_elems = 0;
-    float *x = nullptr, *qkv = nullptr, *attn = nullptr, *h = nullptr, *logits = nullptr, *part = nullptr;
-    float2* rope = nullptr;
-    unsigned long long* best = nullptr;   // per head-workgroup best keys
-    int *pos = nullptr, *tok = nullptr, *hist = nullptr, *dbg_pos = nullptr;
-    // persistent step: kernel (null: one launch per operator), grid, exchange state
-    const void* step_fn = nullptr;
-    int n_wg = 0;
-    StepArgs sa{};
-    StepArgs* d_sa = nullptr;         // sa in the workspace (the kernel reads it there)
-    uint64_t* xbuf = nullptr;
-    size_t xbuf_words = 0;
-    uint32_t* ctl = nullptr;          // [0] epoch base (launches), [1] abort word
-    uint64_t launches = 0, max_launches = 0;
-    hipGraph_t graph = nullptr;
-    hipGraphExec_t exec = nullptr;
-    // timing probes: events around every launch of one kernel kind
-    std::vector<hipEvent_t> probe_ev[TSD_KERNEL_KINDS];
-    int n_past = 0;
-    int top_k = 0;                    // effective k of the top-k sampler
-    std::string err;
-};
-
-namespace {
 
 tsd_status fail(tsd_model* m, tsd_status s, const std::string& msg)
 {
@@ -111,11 +36,12 @@ tsd_status hip_fail(tsd_model* m, hipError_t e, const char* what)
     return fail(m, TSD_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-#define HIP_TRY(m, expr, what)                          \
-    do {                                                \
-        hipError_t e_ = (expr);                         \
-        if (e_ != hipSuccess) return hip_fail(m, e_, what); \
-    } while (0)
+}  // namespace tsd
+
+namespace {
+
+constexpr int MAX_STEP_WG = 1024;          // workgroups of the persistent step, at most
+constexpr long long STEP_SPIN_LIMIT = 2000000;   // 20 ms of the 100 MHz clock per wait
 
 int group_of(int f) { return f == TSD_W_AFFINE8_G64 ? 64 : 32; }
 
@@ -146,7 +72,7 @@ tsd_status validate(const tsd_config* c, std::string& msg)
               std::to_string(g) + ")";
         return TSD_ERR_INVALID_ARGUMENT;
     }
-    if (c->arch == TSD_ARCH_TALKER_CP) { msg = "TALKER_CP is not built yet"; return TSD_ERR_UNSUPPORTED; }
+    if (c->arch == TSD_ARCH_TALKER_CP) return talker_validate(c, msg);
     if (c->batch != 1) { msg = "GPT2/LLAMA decode supports batch 1"; return TSD_ERR_UNSUPPORTED; }
     if (c->head_dim != 64 && c->head_dim != 128) { msg = "head_dim must be 64 or 128"; return TSD_ERR_UNSUPPORTED; }
     for (int K : {c->d_model, c->d_ff, qd})
@@ -167,6 +93,7 @@ int n_weights_of(const tsd_config* c)
 // expected canonical sizes in order; kinds: 0 fp32 tensor, 1 matrix
 void canonical_sizes(const tsd_config* c, std::vector<size_t>& sz)
 {
+    if (c->arch == TSD_ARCH_TALKER_CP) return talker_canonical_sizes(c, canonical_matrix_bytes, sz);
     const int d = c->d_model, ff = c->d_ff, f = c->wfmt, qd = c->n_head * c->head_dim, kd = c->n_kv_head * c->head_dim;
     auto F32 = [&](size_t n) { sz.push_back(n * 4); };
     auto MAT = [&](int N, int K) { sz.push_back(canonical_matrix_bytes(f, N, K)); };
@@ -188,21 +115,10 @@ void canonical_sizes(const tsd_config* c, std::vector<size_t>& sz)
     }
 }
 
-struct Layout {
-    size_t total = 0;
-};
-
-PackedMat take_mat(Planner& P, int f, int N, int K)
-{
-    PackedLayout L = packed_layout(f, N, K);
-    void* p = P.take(L.total);
-    if (!p) { PackedMat m{}; m.N = N; m.K = K; return m; }
-    return packed_view(f, p, N, K);
-}
-
 // walk the workspace; with base == nullptr it only sizes it
 size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
 {
+    if (c->arch == TSD_ARCH_TALKER_CP) return talker_plan(m, c, base);
     Planner P(base);
     const int d = c->d_model, H = c->n_head, Hk = c->n_kv_head, hd = c->head_dim, ff = c->d_ff, B = c->batch, f = c->wfmt;
     const int tpp = 1, vmax = c->vocab;
@@ -263,7 +179,7 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     if (m && base) {
         m->pos = pos; m->dbg_pos = pos + 1; m->tok = tok; m->best = best;
         m->hist = hist; m->x = x; m->qkv = qkv; m->attn = attn; m->h = h; m->logits = logits; m->part = part;
-        m->rope = rope; m->emb[0] = emb0; m->emb_rows[0] = c->vocab; m->wpe = wpe; m->L = Ls; m->nfg = nfg; m->nfb = nfb;
+        m->rope = rope; m->rope_rows = c->n_ctx; m->emb[0] = emb0; m->emb_rows[0] = c->vocab; m->wpe = wpe; m->L = Ls; m->nfg = nfg; m->nfb = nfb;
         m->head = head; m->kc = kc; m->vc = vc; m->kv_layer_elems = kv_layer; m->tpp = tpp; m->vmax = vmax;
         m->qkv_rows = qkv_rows;
         m->ctl = ctl;
@@ -284,24 +200,6 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
 }
 
 // ---- the step's kernels --------------------------------------------------------------------
-
-// brackets one launch with probe events when its kind is the probed one
-struct Bracket {
-    Probe* p;
-    hipStream_t st;
-    bool on;
-    Bracket(Probe* pr, int kind, hipStream_t s) : p(pr), st(s), on(pr && pr->kind == kind)
-    {
-        if (!on) return;
-        (void)hipEventRecord(p->ev[p->next], st);       // empty bracket: the cost of bracketing
-        (void)hipEventRecord(p->ev[p->next + 1], st);
-        (void)hipEventRecord(p->ev[p->next + 2], st);   // the kernel
-    }
-    ~Bracket()
-    {
-        if (on) (void)hipEventRecord(p->ev[p->next + 3], st), p->next += 4;
-    }
-};
 
 hipError_t enqueue_layer(tsd_model* m, int l, hipStream_t st, const int* pos, bool embed, Probe* pr = nullptr)
 {
@@ -412,6 +310,7 @@ hipError_t enqueue_layer(tsd_model* m, int l, hipStream_t st, const int* pos, bo
 hipError_t enqueue_step(tsd_model* m, hipStream_t st, Probe* pr = nullptr)
 {
     const tsd_config& c = m->c;
+    if (c.arch == TSD_ARCH_TALKER_CP) return talker_enqueue(m, st, true, pr);
     if (m->step_fn) {
         Bracket br(pr, KIND_STEP, st);
         return launch_step(m->step_fn, m->d_sa, m->n_wg, st);
@@ -443,6 +342,7 @@ hipError_t enqueue_step(tsd_model* m, hipStream_t st, Probe* pr = nullptr)
 tsd_status pack_weights(tsd_model* m, const tsd_tensor* w)
 {
     const tsd_config& c = m->c;
+    if (c.arch == TSD_ARCH_TALKER_CP) return talker_pack(m, w);
     const int d = c.d_model, H = c.n_head, Hk = c.n_kv_head, hd = c.head_dim, ff = c.d_ff, f = c.wfmt;
     hipStream_t st = m->st;
     int i = 0;
@@ -498,6 +398,7 @@ tsd_status setup_step(tsd_model* m)
     const tsd_config& c = m->c;
     if (c.launch_mode == TSD_LAUNCH_PER_OPERATOR) return TSD_OK;
     if (c.launch_mode != TSD_LAUNCH_PERSISTENT) return fail(m, TSD_ERR_INVALID_ARGUMENT, "unknown launch_mode");
+    if (c.arch == TSD_ARCH_TALKER_CP) return TSD_OK;   // the frame runs one launch per operator
     m->step_fn = step_kernel_for(c.wfmt, c.arch == TSD_ARCH_LLAMA, c.d_model, c.n_head, c.n_kv_head, c.head_dim, c.d_ff,
                                  c.vocab);
     if (!m->step_fn) return TSD_OK;   // this shape runs one launch per operator
@@ -579,8 +480,8 @@ tsd_status init_state(tsd_model* m)
     HIP_TRY(m, launch_fill_f32(m->logits, 0.f, (size_t)c.batch * m->tpp * m->vmax, st), "init");
     // RoPE table in fp64 on the host: angle = pos * theta^(-2i/hd)
     const int half = c.head_dim / 2;
-    std::vector<float2> tab((size_t)c.n_ctx * half);
-    for (int p = 0; p < c.n_ctx; ++p)
+    std::vector<float2> tab((size_t)m->rope_rows * half);
+    for (int p = 0; p < m->rope_rows; ++p)
         for (int i = 0; i < half; ++i) {
             const double a = (double)p * pow((double)c.rope_theta, -2.0 * i / c.head_dim);
             tab[(size_t)p * half + i] = make_float2((float)cos(a), (float)sin(a));
@@ -595,13 +496,28 @@ tsd_status init_state(tsd_model* m)
     return TSD_OK;
 }
 
-tsd_status capture(tsd_model* m, Probe* pr, hipGraph_t* out_g, hipGraphExec_t* out_x)
+// launches of each kind in one step (timing probes size their events from it)
+void count_launches(tsd_model* m)
+{
+    const tsd_config& c = m->c;
+    for (int k = 0; k < TSD_KERNEL_KINDS; ++k) m->kind_launches[k] = 0;
+    if (c.arch == TSD_ARCH_TALKER_CP) return talker_kind_launches(m, m->kind_launches);
+    if (m->step_fn) {
+        m->kind_launches[KIND_STEP] = 1;
+        return;
+    }
+    for (int k : {KIND_QKV, KIND_ATTN, KIND_OPROJ, KIND_FC, KIND_DOWN}) m->kind_launches[k] = c.n_layer;
+    m->kind_launches[KIND_HEAD] = 1;
+}
+
+// the step graph; talker_only: the TALKER_CP frame without head and predictor (prefill positions)
+tsd_status capture(tsd_model* m, bool talker_only, hipGraph_t* out_g, hipGraphExec_t* out_x)
 {
     hipStream_t cs;
     HIP_TRY(m, hipStreamCreateWithFlags(&cs, hipStreamNonBlocking), "capture stream");
     hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) { (void)hipStreamDestroy(cs); return hip_fail(m, e, "begin capture"); }
-    hipError_t le = enqueue_step(m, cs, pr);
+    hipError_t le = talker_only ? talker_enqueue(m, cs, false) : enqueue_step(m, cs);
     hipGraph_t g = nullptr;
     e = hipStreamEndCapture(cs, &g);
     (void)hipStreamDestroy(cs);
@@ -659,6 +575,11 @@ tsd_status tsd_model_create(const tsd_config* cfg, const tsd_tensor* weights, in
         top_k = (sampling->top_k <= 0 || sampling->top_k > cfg->vocab) ? cfg->vocab : sampling->top_k;
         if (!topk_supported(cfg->vocab, top_k))
             return fail(nullptr, TSD_ERR_UNSUPPORTED, "top-k draws support k <= 1024 and vocabularies up to 12288");
+        if (cfg->arch == TSD_ARCH_TALKER_CP) {
+            const int kc = (sampling->top_k <= 0 || sampling->top_k > cfg->cp_vocab) ? cfg->cp_vocab : sampling->top_k;
+            if (!topk_supported(cfg->cp_vocab, kc))
+                return fail(nullptr, TSD_ERR_UNSUPPORTED, "top-k draws support k <= 1024 and vocabularies up to 12288");
+        }
     }
     tsd_model* m = new (std::nothrow) tsd_model();
     if (!m) return fail(nullptr, TSD_ERR_OUT_OF_MEMORY, "host allocation");
@@ -672,7 +593,9 @@ tsd_status tsd_model_create(const tsd_config* cfg, const tsd_tensor* weights, in
     tsd_status r = setup_step(m);
     if (r == TSD_OK) r = pack_weights(m, weights);
     if (r == TSD_OK) r = init_state(m);
-    if (r == TSD_OK) r = capture(m, nullptr, &m->graph, &m->exec);
+    if (r == TSD_OK) r = capture(m, false, &m->graph, &m->exec);
+    if (r == TSD_OK && cfg->arch == TSD_ARCH_TALKER_CP) r = capture(m, true, &m->graph_talker, &m->exec_talker);
+    if (r == TSD_OK) count_launches(m);
     if (r != TSD_OK) {
         g_err = m->err;
         tsd_model_destroy(m);
@@ -687,6 +610,8 @@ tsd_status tsd_model_destroy(tsd_model* m)
     if (!m) return TSD_OK;
     if (m->exec) (void)hipGraphExecDestroy(m->exec);
     if (m->graph) (void)hipGraphDestroy(m->graph);
+    if (m->exec_talker) (void)hipGraphExecDestroy(m->exec_talker);
+    if (m->graph_talker) (void)hipGraphDestroy(m->graph_talker);
     for (int k = 0; k < TSD_KERNEL_KINDS; ++k)
         for (hipEvent_t ev : m->probe_ev[k]) (void)hipEventDestroy(ev);
     delete m;
@@ -728,9 +653,13 @@ tsd_status tsd_prefill(tsd_model* m, const int32_t* d_tokens, int n, int32_t* d_
     if (m->n_past + n > m->c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "prompt does not fit the context");
     const int nt = m->c.batch * m->tpp;
     for (int t = 0; t < n; ++t) {
-        HIP_TRY(m, launch_copy_i32(m->tok, d_tokens + (size_t)t * nt, nt, m->st), "set input");
+        // tokens are [batch][n][tokens per position]: position t of every row
+        HIP_TRY(m, launch_gather_i32(m->tok, d_tokens + (size_t)t * m->tpp, m->c.batch, m->tpp, (long long)n * m->tpp, m->st),
+                "set input");
         HIP_TRY(m, before_launch(m), "exchange restart");
-        HIP_TRY(m, hipGraphLaunch(m->exec, m->st), "graph launch");
+        // TALKER_CP prompt frames before the last need neither head nor predictor
+        hipGraphExec_t x = (m->exec_talker && t + 1 < n) ? m->exec_talker : m->exec;
+        HIP_TRY(m, hipGraphLaunch(x, m->st), "graph launch");
         m->n_past += 1;
     }
     if (d_next) HIP_TRY(m, launch_copy_i32(d_next, m->tok, nt, m->st), "copy ids");
@@ -826,7 +755,8 @@ tsd_status tsd_layer_forward(tsd_model* m, int layer, const float* d_x, int pos,
     const size_t xb = (size_t)c.batch * c.d_model * sizeof(float);
     HIP_TRY(m, hipMemcpyAsync(m->x, d_x, xb, hipMemcpyDeviceToDevice, m->st), "copy x");
     HIP_TRY(m, launch_fill_i32(m->dbg_pos, pos, 1, m->st), "set position");
-    HIP_TRY(m, enqueue_layer(m, layer, m->st, m->dbg_pos, false), "layer");
+    if (c.arch == TSD_ARCH_TALKER_CP) HIP_TRY(m, talker_layer(m, layer, m->st, m->dbg_pos), "layer");
+    else HIP_TRY(m, enqueue_layer(m, layer, m->st, m->dbg_pos, false), "layer");
     HIP_TRY(m, hipMemcpyAsync(d_out, m->x, xb, hipMemcpyDeviceToDevice, m->st), "copy out");
     return TSD_OK;
 }
@@ -838,7 +768,8 @@ tsd_status tsd_time_kernel(tsd_model* m, int kind, int n_steps, float* avg_us, i
     if (m->n_past + n_steps > m->c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "probe steps do not fit the context");
     if ((kind == KIND_STEP) != (m->step_fn != nullptr))
         return fail(m, TSD_ERR_UNSUPPORTED, "this model does not launch a kernel of that kind");
-    const int pairs_max = (kind == KIND_HEAD || kind == KIND_STEP) ? 1 : m->c.n_layer;
+    const int pairs_max = m->kind_launches[kind];
+    if (pairs_max == 0) return fail(m, TSD_ERR_UNSUPPORTED, "this step has no kernel of that kind");
     if (m->probe_ev[kind].empty()) {
         m->probe_ev[kind].resize(4 * pairs_max);
         for (auto& ev : m->probe_ev[kind]) HIP_TRY(m, hipEventCreate(&ev), "probe event");
@@ -911,6 +842,74 @@ tsd_status tsd_gemv(int wfmt, const void* d_packed, int N, int K, int B, const f
         if (e != hipSuccess) return hip_fail(nullptr, e, "gemv");
     }
     return TSD_OK;
+}
+
+// operand [16][K] hi, lo; group sums [16][K/64]; split-K slices [splits][16][N]
+size_t gemm_rows_layout(int N, int K, int splits, size_t* off_lo, size_t* off_gs, size_t* off_part)
+{
+    size_t o = 0;
+    o += align256((size_t)MM_ROWS * K * 2);
+    *off_lo = o;
+    o += align256((size_t)MM_ROWS * K * 2);
+    *off_gs = o;
+    o += align256((size_t)MM_ROWS * (K / 64) * 4);
+    *off_part = o;
+    o += (size_t)splits * MM_ROWS * N * 4;
+    return o;
+}
+
+tsd_status tsd_gemm_rows_scratch_bytes(int N, int K, int splits, size_t* out)
+{
+    if (!out || N <= 0 || !mm16_supported(FMT_AFF8, N, K) || splits < 1 || splits > MM_MAX_SPLIT || splits > K / 64)
+        return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "bad shape or split count");
+    size_t a, b, c;
+    *out = gemm_rows_layout(N, K, splits, &a, &b, &c);
+    return TSD_OK;
+}
+
+tsd_status tsd_gemm_rows(const void* d_packed, int N, int K, int B, const float* d_x, float* d_y, int splits,
+                         void* d_scratch, size_t scratch_bytes, void* stream)
+{
+    size_t need = 0;
+    tsd_status s = tsd_gemm_rows_scratch_bytes(N, K, splits, &need);
+    if (s != TSD_OK) return s;
+    if (B < 1 || B > MM_ROWS) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "B must be 1..16");
+    if (!d_packed || !d_x || !d_y || !d_scratch) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null buffer");
+    if ((uintptr_t)d_scratch % 256) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "scratch must be 256-byte aligned");
+    if (scratch_bytes < need) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "scratch too small");
+    hipStream_t st = (hipStream_t)stream;
+    size_t off_lo, off_gs, off_part;
+    gemm_rows_layout(N, K, splits, &off_lo, &off_gs, &off_part);
+    uint8_t* base = (uint8_t*)d_scratch;
+    Act16 a{(__half*)base, (__half*)(base + off_lo), (float*)(base + off_gs)};
+    hipError_t e = hipSuccess;
+    if (B < MM_ROWS) {   // rows past B enter the GEMM as zeros
+        const int rest = MM_ROWS - B;
+        e = launch_fill_u32((unsigned*)(a.hi + (size_t)B * K), 0u, rest * K / 2, st);
+        if (e == hipSuccess) e = launch_fill_u32((unsigned*)(a.lo + (size_t)B * K), 0u, rest * K / 2, st);
+        if (e == hipSuccess) e = launch_fill_f32(a.gsum + (size_t)B * (K / 64), 0.f, (size_t)rest * (K / 64), st);
+    }
+    PrepArgs p{};
+    p.x = (float*)d_x;   // read only: no partial slices to add
+    p.ldx = K;
+    p.K = K;
+    p.rows = B;
+    p.a = a;
+    if (e == hipSuccess) e = launch_prep16(p, st);
+    PackedMat W = packed_view(FMT_AFF8, (void*)d_packed, N, K);
+    Mm16Out o{};
+    o.rows = B;
+    o.ldy = N;
+    if (splits == 1) {
+        o.y = d_y;
+        if (e == hipSuccess) e = launch_mm16(MM_STORE, W, a, 1, o, st);
+    } else {
+        o.y = (float*)(base + off_part);
+        o.slice = (long long)MM_ROWS * N;
+        if (e == hipSuccess) e = launch_mm16(MM_STORE, W, a, splits, o, st);
+        if (e == hipSuccess) e = launch_sum_slices(o.y, splits, o.slice, d_y, (long long)B * N, st);
+    }
+    return e == hipSuccess ? TSD_OK : hip_fail(nullptr, e, "gemm rows");
 }
 
 tsd_status tsd_sample_topk(const float* d_logits, int n, int top_k, float temperature, uint64_t seed, int row, int pos,

@@ -39,3 +39,17 @@ def test_workspace_sizes_and_validation():
     with pytest.raises(binding.TsdError):
         binding.tsd_gemv_packed_bytes("q8_0", 8, 100)
     assert binding.tsd_gemv_packed_bytes("q4_0", 3072, 1024) >= 3072 * 512 + 3072 * 32 * 2
+
+
+def test_talker_workspace_and_validation():
+    c5 = synth.config("talker_cp_aff8")
+    n = binding.tsd_workspace_bytes(c5)
+    # ~0.6 GB of packed weights, 0.14 GB of embedding tables, 0.94 GB of fp16 Talker cache
+    assert 1.5e9 < n < 2.0e9
+    for bad, status in [(dict(c5, wfmt="q8_0"), 2), (dict(c5, batch=17), 2), (dict(c5, n_codebooks=1), 1),
+                        (dict(c5, n_codebooks=17), 1), (dict(c5, head_dim=96), 2), (dict(c5, cp_n_layer=0), 1),
+                        (dict(c5, d_ff=8192), 2)]:
+        with pytest.raises(binding.TsdError) as e:
+            binding.tsd_workspace_bytes(bad)
+        assert e.value.status == status, bad
+    assert binding.tsd_gemm_rows_scratch_bytes(1024, 3072, 4) >= 2 * 16 * 3072 * 2 + 4 * 16 * 1024 * 4

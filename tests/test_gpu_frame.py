@@ -1,0 +1,271 @@
+"""GPU parity of the batched Talker + code-predictor frame (TALKER_CP) and of its matrix-core
+GEMM against the CPU oracle, through the C ABI.
+
+Frames are teacher forced across frames (both sides get the oracle's codes as the next
+frame's input).  Inside a frame the predictor feeds its own codes forward, so for every row the
+codebooks are compared in order up to the first code where the two sides legitimately differ
+(oracle top-2 within 1e-3, or a top-k draw within 1e-4 of a cumulative boundary); logits of each
+compared head, taken together as the frame's output tensor: rel <= 2e-3.
+
+The small models use norm gains ~N(0, 0.1): with gains ~N(0, 0.5) these random networks amplify
+the fp16 rounding of cached keys and values (a value computed 1e-7 apart on two sides rounds to
+neighbouring fp16 numbers now and then) into logit differences of a few 1e-3 late in the
+predictor's chain, as much between two GPU runs whose embeddings differ by 2e-7 as between the
+GPU and the oracle."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from parity import DRAW_MARGIN, REL_TOL, TIE_GAP, ids_agree, rel_err, top2_gap, topk_draw_margins
+from quantized_gemv_kv_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+# The GEMM alone: x enters as fp16 hi + lo (about 2^-22 relative), the centred weights q - 128
+# exactly, products are exact and summed in fp32, then scaled per group in fp32: the bound is
+# that of an fp32 dot product, ~K 2^-24 sum|w x| at worst (1e-7 .. 1e-6 of max|y| measured).
+GEMM_TOL = 1e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def dev(a):
+    return torch_mod().from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+GEMM_CASES = [
+    # N, K, B, splits
+    (96, 128, 2, 1),
+    (160, 192, 16, 1),      # three groups: one wave of each slice idle
+    (1000, 1024, 16, 1),    # N not a multiple of the 16-row tile
+    (4096, 1024, 16, 1),    # Talker fused QKV
+    (6144, 1024, 16, 1),    # Talker gate/up (interleaved)
+    (1024, 2048, 16, 4),    # output projection, four K slices
+    (1024, 3072, 16, 4),    # down projection: three groups per wave
+    (1024, 3072, 7, 3),
+    (3072, 1024, 1, 1),     # Talker head, one row
+    (2048, 4096, 16, 8),
+    (48, 64, 16, 1),        # one group
+]
+
+
+@pytest.mark.parametrize("N,K,B,splits", GEMM_CASES)
+def test_gemm_rows_matches_oracle(N, K, B, splits):
+    torch = torch_mod()
+    from quantized_gemv_kv_amd import binding as tb
+    say(f"[gemm16] N={N} K={K} B={B} splits={splits}")
+    rng = synth.rng_for(21, N, K, B)
+    blob = synth.aff8_matrix(rng, N, K)[0]
+    x = synth.normal_f32(rng, (B, K))
+    x[:, : K // 8] *= 30.0          # a wide range of magnitudes inside each row
+    x[:, K // 8: K // 4] *= 1e-3
+    ref = oracle.gemv_f32("aff8", blob, N, K, x, None)
+    packed = torch.empty(tb.tsd_gemv_packed_bytes("aff8", N, K), dtype=torch.uint8, device="cuda")
+    tb.tsd_gemv_pack("aff8", dev(blob), N, K, packed)
+    scratch = torch.empty(tb.tsd_gemm_rows_scratch_bytes(N, K, splits), dtype=torch.uint8, device="cuda")
+    scratch.fill_(0xFF)             # NaN patterns: rows past B must not leak into the result
+    y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+    tb.tsd_gemm_rows(packed, N, K, B, dev(x), y, splits, scratch)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    r = max(rel_err(got[b], ref[b]) for b in range(B))
+    say(f"  worst row rel {r:.2e}")
+    assert r <= GEMM_TOL
+
+
+def test_gemm_rows_rejects_bad_arguments():
+    torch = torch_mod()
+    from quantized_gemv_kv_amd import binding as tb
+    with pytest.raises(tb.TsdError):
+        tb.tsd_gemm_rows_scratch_bytes(64, 96, 1)        # K not a multiple of 64
+    with pytest.raises(tb.TsdError):
+        tb.tsd_gemm_rows_scratch_bytes(64, 8192, 1)      # K above 4096
+    with pytest.raises(tb.TsdError):
+        tb.tsd_gemm_rows_scratch_bytes(64, 128, 3)       # more slices than groups
+    p = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
+    s = torch.empty(tb.tsd_gemm_rows_scratch_bytes(64, 128, 1), dtype=torch.uint8, device="cuda")
+    x = torch.zeros(17 * 128, dtype=torch.float32, device="cuda")
+    with pytest.raises(tb.TsdError):
+        tb.tsd_gemm_rows(p, 64, 128, 17, x, x, 1, s)     # more than 16 rows
+    with pytest.raises(tb.TsdError):
+        tb.tsd_gemm_rows(p, 64, 128, 2, x, x, 1, s[:100])  # scratch too small
+
+
+# ---- the frame ---------------------------------------------------------------------------------
+
+def gpu_model(cfg, w):
+    from quantized_gemv_kv_amd import Model
+    samp = None
+    if cfg.get("sample_mode", 0):
+        samp = dict(mode=1, top_k=cfg["top_k"], temperature=cfg["temperature"], seed=cfg["seed"])
+    m = Model(dict(cfg, launch_mode="per_operator"), w, sampling=samp)
+    assert not m.uses_persistent_step()
+    return m
+
+
+def compare_frame(cfg, lo, lg, o_ids, g_ids, pos):
+    """Logits [B][C][vmax] and codes [B][C] of one frame.  The frame's logits are one output
+    tensor: rel over every head compared (each row up to its first legitimate difference of
+    codes).  Returns (heads compared, rel)."""
+    B, C, V, Vc = cfg["batch"], cfg["n_codebooks"], cfg["vocab"], cfg["cp_vocab"]
+    topk = cfg.get("sample_mode", 0) == 1
+    got, ref = [], []
+    for b in range(B):
+        for j in range(C):
+            nv = V if j == 0 else Vc
+            got.append(lg[b, j, :nv])
+            ref.append(lo[b, j, :nv])
+            assert np.all(lg[b, j, nv:] == 0.0)
+            if int(g_ids[b, j]) == int(o_ids[b, j]):
+                continue
+            # a legitimate difference ends the comparison of this row's frame
+            if topk:
+                u = oracle.uniform24(cfg["seed"], b, pos, j)
+                margin, gap = topk_draw_margins(lo[b, j, :nv], cfg["top_k"], cfg["temperature"], u)
+                assert margin < DRAW_MARGIN or gap < TIE_GAP, (pos, b, j, g_ids[b, j], o_ids[b, j], margin, gap)
+            else:
+                assert ids_agree(g_ids[b, j], lo[b, j, :nv]), (pos, b, j, g_ids[b, j], o_ids[b, j],
+                                                                top2_gap(lo[b, j, :nv]))
+            break
+    r = rel_err(np.concatenate(got), np.concatenate(ref))
+    assert r <= REL_TOL, (pos, r)
+    return len(got), r
+
+
+def frame_parity(cfg, w, n_prompt, n_frames, seed=3, kv_pos=None):
+    om = oracle.OracleModel(cfg, w)
+    gm = gpu_model(cfg, w)
+    B, C = cfg["batch"], cfg["n_codebooks"]
+    heads, worst = 0, 0.0
+    if kv_pos is not None:
+        k, v = synth.kv_cache(cfg, kv_pos, seed=seed)
+        om.load_kv(k, v, kv_pos)
+        gm.load_kv(dev(k), dev(v), kv_pos)
+        o_ids = synth.prompt_tokens(cfg, 1, seed=seed + 1)[:, 0, :]
+    else:
+        toks = synth.prompt_tokens(cfg, n_prompt, seed=seed)
+        o_ids = om.prefill(toks)
+        g_ids = gm.prefill(dev(toks)).cpu().numpy()
+        n, r = compare_frame(cfg, om.logits(), gm.logits().cpu().numpy(), o_ids, g_ids, n_prompt - 1)
+        heads, worst = heads + n, max(worst, r)
+    for f in range(n_frames):
+        pos = om.n_past
+        nxt = o_ids
+        o_ids = om.step(nxt)
+        g_ids = gm.step(dev(nxt)).cpu().numpy()
+        n, r = compare_frame(cfg, om.logits(), gm.logits().cpu().numpy(), o_ids, g_ids, pos)
+        heads, worst = heads + n, max(worst, r)
+    assert gm.n_past == om.n_past
+    hist = gm.tokens(gm.n_past - 1, 1).cpu().numpy()[0]
+    assert hist.shape == (B, C)
+    gm.synchronize()
+    gm.close()
+    om.close()
+    return heads, worst
+
+
+def small_talker(**kw):
+    return synth.small_config("talker_cp", "aff8", **kw)
+
+
+@pytest.mark.parametrize("batch", [1, 2, 16])
+def test_small_frame_teacher_forced(batch):
+    cfg = small_talker(batch=batch, n_ctx=64)
+    say(f"[frame-small] batch {batch}")
+    w = synth.model_weights(cfg, 42, norm_std=0.1)
+    heads, worst = frame_parity(cfg, w, n_prompt=9, n_frames=6)
+    say(f"  heads compared {heads}, worst rel {worst:.2e}")
+    assert heads >= batch * cfg["n_codebooks"] * 4
+
+
+def test_small_frame_gqa_many_codebooks():
+    """16 codebooks, grouped-query attention 4/2 with head 128, three predictor layers."""
+    cfg = small_talker(d_model=256, n_head=4, n_kv_head=2, head_dim=128, d_ff=384, n_codebooks=16, cp_n_layer=3,
+                       cp_vocab=200, vocab=300, batch=5, n_ctx=80)
+    say("[frame-small] 16 codebooks, gqa")
+    w = synth.model_weights(cfg, 9, norm_std=0.1)
+    heads, worst = frame_parity(cfg, w, n_prompt=70, n_frames=4)   # crosses a 64-key tile
+    say(f"  heads compared {heads}, worst rel {worst:.2e}")
+
+
+def test_small_frame_topk_teacher_forced():
+    cfg = small_talker(batch=3, n_ctx=64, sample_mode=1, top_k=5, temperature=0.8, seed=99)
+    say("[frame-small] top-k")
+    w = synth.model_weights(cfg, 42, norm_std=0.1)
+    heads, worst = frame_parity(cfg, w, n_prompt=5, n_frames=8)
+    say(f"  heads compared {heads}, worst rel {worst:.2e}")
+    assert heads >= 3 * 4 * 5
+
+
+def test_talker_widths_over_two_attention_chunks():
+    """The Talker's real widths (d 1024, 16 q / 8 kv heads of 128, SwiGLU 3072, vocabularies
+    3072 / 2048, 16 codebooks) with two Talker layers and one predictor layer, after a random
+    cache of 290 positions (two 256-key chunks), four rows."""
+    cfg = dict(synth.config("talker_cp_aff8"), n_layer=2, cp_n_layer=1, batch=4, n_ctx=320)
+    say("[frame-mid] talker widths, 290 cached positions")
+    w = synth.model_weights(cfg, 42)
+    heads, worst = frame_parity(cfg, w, n_prompt=0, n_frames=2, kv_pos=290)
+    say(f"  heads compared {heads}, worst rel {worst:.2e}")
+
+
+def test_talker_layer_forward():
+    """One Talker layer at its real widths on 16 rows at position 100 over a random cache."""
+    cfg = dict(synth.config("talker_cp_aff8"), n_layer=1, cp_n_layer=1, n_ctx=128)
+    say("[frame-layer] talker layer, 16 rows")
+    w = synth.model_weights(cfg, 42)
+    k, v = synth.kv_cache(cfg, 100, seed=4)
+    x = synth.hidden(cfg, seed=4)
+    om = oracle.OracleModel(cfg, w)
+    om.load_kv(k, v, 100)
+    ref = om.layer_forward(0, x, 100)
+    gm = gpu_model(cfg, w)
+    gm.load_kv(dev(k), dev(v), 100)
+    got = gm.layer_forward(0, dev(x), 100).cpu().numpy()
+    r = max(rel_err(got[b], ref[b]) for b in range(cfg["batch"]))
+    say(f"  worst row rel {r:.2e}")
+    assert r <= REL_TOL
+    gm.close()
+
+
+def test_free_running_frames_match_history():
+    """No input codes: the graph feeds each frame's codes into the next."""
+    cfg = small_talker(batch=2, n_ctx=64)
+    w = synth.model_weights(cfg, 42, norm_std=0.1)
+    gm = gpu_model(cfg, w)
+    toks = synth.prompt_tokens(cfg, 4, seed=1)
+    frames = [gm.prefill(dev(toks)).cpu().numpy().copy()]
+    for _ in range(6):
+        frames.append(gm.step(None).cpu().numpy().copy())
+    hist = gm.tokens(3, 7).cpu().numpy()
+    assert np.array_equal(hist, np.stack(frames))
+    gm.close()
+
+
+def test_talker_errors():
+    from quantized_gemv_kv_amd import TsdError
+    cfg = small_talker(batch=2, n_ctx=8)
+    w = synth.model_weights(cfg, 1)
+    gm = gpu_model(cfg, w)
+    gm.prefill(dev(synth.prompt_tokens(cfg, 6)))
+    with pytest.raises(TsdError) as e:
+        gm.prefill(dev(synth.prompt_tokens(cfg, 3)))
+    assert e.value.status == 4 and gm.n_past == 6
+    gm.step()
+    gm.step()
+    with pytest.raises(TsdError) as e:
+        gm.step()
+    assert e.value.status == 4
+    gm.close()
+    with pytest.raises(TsdError):
+        gpu_model(cfg, w[:-1])

@@ -4,7 +4,11 @@ Workload (the pages' T3 decoder at its real shape): a 24-layer GPT-2-Medium-shap
 decoder, d 1024, 16 heads x 64, FFN 4096, learned positions, vocab 8192 head, Q4_0 weights,
 fp32 norms/embeddings ~N(0, 0.02), fp16 KV cache; 256-token prefill, then greedy decode steps at
 positions 256 .. 255+K, batch 1.  All inputs are seeded synthetic data.  --workload
-llama520m_q8_0 times the 30-layer Llama-shaped Q8_0 decoder instead (300-token prefill).
+llama520m_q8_0 times the 30-layer Llama-shaped Q8_0 decoder instead (300-token prefill), and
+--workload talker_cp_aff8 the Qwen3-TTS-shaped Talker (28 layers) + code predictor (5 layers,
+15 passes) frame loop with 8-bit affine weights at batch 16 (170 prompt frames, then K frames);
+its line also carries "gemm_rows", the batched matrix-core GEMM alone on a matrix larger than
+the Infinity Cache.
 
 The line also carries "gemv": the standalone quantized GEMV on one 524288 x 1024 Q8_0 matrix
 (~570 MB, more than the Infinity Cache holds), where a launch is amortised.
@@ -36,6 +40,10 @@ WORKLOADS = {
                                    "greedy decode steps, batch 1", "q4_0 weights, fp32 accumulate, fp16 kv"),
     "llama520m_q8_0": (300, 600, "Llama-shaped ~520M 30-layer speech-token decoder, Q8_0, 300-token prefill then {K} "
                                  "greedy decode steps, batch 1", "q8_0 weights, fp32 accumulate, fp16 kv"),
+    "talker_cp_aff8": (170, 200, "Talker (28 layers, d 1024, 16 q / 8 kv heads of 128, SwiGLU 3072) + code predictor "
+                                 "(5 layers, 15 sequential passes, vocab 2048), 8-bit affine group-64 weights, "
+                                 "170 prompt frames then {K} greedy frames of 16 codes, batch 16",
+                       "aff8 weights, fp16 hi/lo x fp16 weight MFMA with fp32 accumulate, fp16 kv"),
 }
 WORKLOAD = "gpt2_medium_q4_0"
 PROMPT = 256
@@ -148,6 +156,84 @@ def cpu_baseline(cfg, weights, seconds, seed):
                       f"over a random {PROMPT}-position fp16 cache, single-threaded fp64 oracle, {el:.1f} s"}
 
 
+def cpu_baseline_frames(cfg, weights, seconds, seed):
+    """The CPU oracle on one batch row of the frame loop (rows are independent, so a 16-row frame
+    costs 16 row-frames): frames at positions 170.. over a random 170-position Talker cache."""
+    import oracle
+    from quantized_gemv_kv_amd import synth
+    c1 = dict(cfg, batch=1)
+    om = oracle.OracleModel(c1, weights)
+    k, v = synth.kv_cache(c1, PROMPT, seed=seed)
+    om.load_kv(k, v, PROMPT)
+    codes = synth.prompt_tokens(c1, 1, seed=seed)[:, 0, :]
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        codes = om.step(codes)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 16:
+            break
+    om.close()
+    rows = cfg["batch"]
+    return {"value": n / el / rows, "unit": "frames/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} frames of one batch row (Talker {cfg['n_layer']} layers + {cfg['n_codebooks'] - 1} predictor "
+                      f"passes) at positions {PROMPT}..{PROMPT + n - 1} over a random {PROMPT}-position fp16 cache, "
+                      f"single-threaded fp64 oracle, {el:.1f} s; the {rows}-row rate is that rate / {rows}"}
+
+
+GEMM_N, GEMM_K = 131072, 2048   # one 8-bit affine matrix of ~270 MB, larger than the Infinity Cache
+
+
+def gemm_rows_headline(seed, reps=7):
+    """The batched matrix-core GEMM alone at a size where a launch is amortised: Y = W X for 16
+    rows, W 131072 x 2048 in 8-bit affine groups of 64 (the frame's weight law), X ~ N(0,1);
+    median over bursts of back-to-back calls (operand interleave, GEMM).  Bytes = the stored
+    matrix (tiled: quants, then one scale/bias word per row and group) + X read + Y written."""
+    import torch
+    from quantized_gemv_kv_amd import binding, roofline, synth
+    N, K, B = GEMM_N, GEMM_K, 16
+    canon = torch.empty(roofline.matrix_bytes("aff8", N, K), dtype=torch.uint8, device="cuda")
+    chunk = 16384
+    qs, ss, bs = [], [], []
+    for r0 in range(0, N, chunk):
+        blob = synth.aff8_matrix(synth.rng_for(seed, r0, K), chunk, K)[0]
+        nq, ng = chunk * K, chunk * (K // 64)
+        qs.append(torch.from_numpy(blob[:nq]))
+        ss.append(torch.from_numpy(blob[nq:nq + 2 * ng]))
+        bs.append(torch.from_numpy(blob[nq + 2 * ng:]))
+    nq = N * K
+    canon[:nq].copy_(torch.cat(qs))
+    canon[nq:nq + N * (K // 64) * 2].copy_(torch.cat(ss))
+    canon[nq + N * (K // 64) * 2:].copy_(torch.cat(bs))
+    del qs, ss, bs
+    packed = torch.empty(binding.tsd_gemm_rows_packed_bytes(N, K), dtype=torch.uint8, device="cuda")
+    binding.tsd_gemm_rows_pack(canon, N, K, packed)
+    del canon
+    x = torch.from_numpy(synth.normal_f32(synth.rng_for(seed, 2), (B, K))).cuda()
+    y = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    scratch = torch.empty(binding.tsd_gemm_rows_scratch_bytes(N, K, 1), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        binding.tsd_gemm_rows(packed, N, K, B, x, y, 1, scratch)
+    burst, times = 10, []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(burst):
+            binding.tsd_gemm_rows(packed, N, K, B, x, y, 1, scratch)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / burst)
+    us = float(np.median(times))
+    nbytes = roofline.matrix_bytes("aff8", N, K) + 4 * B * (K + N)   # the tiled layout stores the same bytes
+    gbs = nbytes / (us * 1e-6) / 1e9
+    flops = 2.0 * N * K * B
+    return {"shape": f"aff8 {N}x{K}, 16 rows", "bytes": nbytes, "us": us, "gbs": gbs,
+            "frac": gbs / roofline.HBM_PEAK_GBS, "tflops": flops / (us * 1e-6) / 1e12,
+            "timing": f"median over {reps} bursts of {burst} back-to-back calls (operand split + GEMM)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -163,6 +249,7 @@ def main():
     if args.steps is None:
         args.steps = default_steps
     cfg = dict(synth.config(WORKLOAD), launch_mode=args.launch_mode)
+    frames = cfg["arch"] == "talker_cp"
     K, W = args.steps, args.warmup
     if PROMPT + max(K, W) > cfg["n_ctx"]:
         print(f"steps/warmup exceed the {cfg['n_ctx']}-position context", file=sys.stderr)
@@ -194,7 +281,10 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1)
-    ids = model.tokens(PROMPT, K).cpu().numpy().reshape(-1)
+    ids = model.tokens(PROMPT, K).cpu().numpy()
+    if frames:
+        assert ids[..., 1:].max() < cfg["cp_vocab"], "sampled codes out of range"
+    ids = ids.reshape(-1)
     assert ids.min() >= 0 and ids.max() < cfg["vocab"], "sampled ids out of range"
 
     # dominant kernel: every kind timed inside real steps (event records around each launch on
@@ -219,9 +309,10 @@ def main():
     ms_step = ms / K
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     result = {
-        "metric": "decode tokens/sec at batch 1 + achieved HBM GB/s (% of peak) per step",
+        "metric": ("Talker + code-predictor frames/sec at batch 16 + achieved HBM GB/s (% of peak) per frame" if frames
+                   else "decode tokens/sec at batch 1 + achieved HBM GB/s (% of peak) per step"),
         "value": K / (ms * 1e-3),
-        "unit": "tokens/s",
+        "unit": "frames/s" if frames else "tokens/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
@@ -233,7 +324,7 @@ def main():
         "data": "synthetic (seeded random weights, prompt ids and values; no checkpoint)",
         "config": {"workload": desc.format(K=K), "d_model": cfg["d_model"], "n_layer": cfg["n_layer"],
                    "n_head": cfg["n_head"], "d_ff": cfg["d_ff"], "vocab": cfg["vocab"],
-                   "prompt": PROMPT, "global_batch": 1, "launch_mode": mode, "workgroups": n_wg},
+                   "prompt": PROMPT, "global_batch": cfg["batch"], "launch_mode": mode, "workgroups": n_wg},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": roofline.HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / roofline.HBM_PEAK_GBS, "traffic": counted_traffic(dom, WORKLOAD),
                      "kernel": dom, "launch_us": dom_us, "launches_per_step": dom_n,
@@ -252,10 +343,16 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         result["calibration_copy_bytes"] = 2 * n * 4
+    if frames:
+        result["codes_per_s"] = result["value"] * cfg["batch"] * cfg["n_codebooks"]
     if not args.no_gemv:
-        result["gemv"] = gemv_headline(args.seed)
+        if frames:
+            result["gemm_rows"] = gemm_rows_headline(args.seed)
+        else:
+            result["gemv"] = gemv_headline(args.seed)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, weights, args.cpu_seconds, args.seed)
+        result["cpu_baseline"] = (cpu_baseline_frames if frames else cpu_baseline)(cfg, weights, args.cpu_seconds,
+                                                                                    args.seed)
     model.close()
     print(json.dumps(result), flush=True)
 

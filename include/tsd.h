@@ -212,15 +212,21 @@ tsd_status tsd_gemv_pack(int wfmt, const void* d_w, size_t w_bytes, int N, int K
 tsd_status tsd_gemv(int wfmt, const void* d_packed, int N, int K, int B, const float* d_x,
                     const float* d_bias, float* d_y, void* stream);
 
-/* Batched GEMM on the matrix cores for the 8-bit affine layout ([F] §8: batched rollouts turn
+/* Batched GEMM on the matrix cores for the 8-bit affine format ([F] §8: batched rollouts turn
  * the memory-bound mat-vec into a skinny product; §3: affine groups of 64):
- * d_y[b][n] = sum_k W[n][k] d_x[b][k] for b < B (1 <= B <= 16), W packed by tsd_gemv_pack
- * (TSD_W_AFFINE8_G64), d_x [B][K] and d_y [B][N] fp32 (device, caller-owned, d_y is
- * overwritten).  Each x is split into two fp16 numbers (hi, x - hi) and each weight enters
- * exactly (1024 + q in fp16); products accumulate in fp32, the group's scale and bias are
- * applied in fp32.  K must be a multiple of 64 and at most 4096.  `splits` (1..8, at most K/64)
- * cuts K into slices run by separate workgroups and summed afterwards.  d_scratch (256-byte
- * aligned, tsd_gemm_rows_scratch_bytes) holds the operand and the slices. */
+ * d_y[b][n] = sum_k W[n][k] d_x[b][k] for b < B (1 <= B <= 16), d_x [B][K] and d_y [B][N] fp32
+ * row-major (device, caller-owned, d_y is overwritten).  W is first repacked by
+ * tsd_gemm_rows_pack from the canonical TSD_W_AFFINE8_G64 matrix into the batched path's own
+ * layout (16-row tiles of 1 KB blocks, one per group of 64, in the order the matrix cores read
+ * them; tsd_gemm_rows_packed_bytes, 256-byte aligned).  Each x is split into two fp16 numbers
+ * (hi, x - hi) and each weight enters exactly (q - 128 in fp16); products accumulate in fp32,
+ * the group's scale and bias are applied in fp32.  K must be a multiple of 64 and at most 4096.
+ * `splits` (1..8, at most K/64) cuts K into slices run by separate workgroups and summed
+ * afterwards.  d_scratch (256-byte aligned, tsd_gemm_rows_scratch_bytes) holds the operand rows
+ * and the slices. */
+tsd_status tsd_gemm_rows_packed_bytes(int N, int K, size_t* out_bytes);
+tsd_status tsd_gemm_rows_pack(const void* d_w, size_t w_bytes, int N, int K, void* d_packed,
+                              size_t packed_bytes, void* stream);
 tsd_status tsd_gemm_rows_scratch_bytes(int N, int K, int splits, size_t* out_bytes);
 tsd_status tsd_gemm_rows(const void* d_packed, int N, int K, int B, const float* d_x, float* d_y,
                          int splits, void* d_scratch, size_t scratch_bytes, void* stream);

@@ -25,7 +25,8 @@ EXPORTS = ["tsd_workspace_bytes", "tsd_model_create", "tsd_prefill", "tsd_step",
            "tsd_n_past", "tsd_model_destroy", "tsd_last_error", "tsd_get_logits", "tsd_get_tokens", "tsd_load_kv",
            "tsd_layer_forward", "tsd_gemv_packed_bytes", "tsd_gemv_pack", "tsd_gemv",
            "tsd_attention_scratch_bytes", "tsd_attention", "tsd_time_kernel", "tsd_synchronize",
-           "tsd_model_info", "tsd_sample_topk", "tsd_gemm_rows_scratch_bytes", "tsd_gemm_rows"]
+           "tsd_model_info", "tsd_sample_topk", "tsd_gemm_rows_packed_bytes", "tsd_gemm_rows_pack",
+           "tsd_gemm_rows_scratch_bytes", "tsd_gemm_rows"]
 KERNEL_KINDS = {"qkv": 0, "attn": 1, "oproj": 2, "fc": 3, "down": 4, "head": 5, "step": 6}
 
 
@@ -88,6 +89,8 @@ def lib():
             "tsd_synchronize": [_P],
             "tsd_model_info": [_P, _P, _P],
             "tsd_sample_topk": [_P, _I, _I, ctypes.c_float, ctypes.c_uint64, _I, _I, _I, _P, _P],
+            "tsd_gemm_rows_packed_bytes": [_I, _I, ctypes.POINTER(_SZ)],
+            "tsd_gemm_rows_pack": [_P, _SZ, _I, _I, _P, _SZ, _P],
             "tsd_gemm_rows_scratch_bytes": [_I, _I, _I, ctypes.POINTER(_SZ)],
             "tsd_gemm_rows": [_P, _I, _I, _I, _P, _P, _I, _P, _SZ, _P],
         }
@@ -155,6 +158,17 @@ def tsd_gemv(fmt, packed, N, K, B, x, bias, y, stream=None):
 def tsd_sample_topk(logits, top_k, temperature, seed, row, pos, pss, out, stream=None):
     _check(lib().tsd_sample_topk(_ptr(logits), logits.numel(), top_k, temperature, seed, row, pos, pss, _ptr(out),
                                  _stream(stream)))
+
+
+def tsd_gemm_rows_packed_bytes(N, K) -> int:
+    out = _SZ()
+    _check(lib().tsd_gemm_rows_packed_bytes(N, K, ctypes.byref(out)))
+    return out.value
+
+
+def tsd_gemm_rows_pack(w, N, K, packed, stream=None):
+    _check(lib().tsd_gemm_rows_pack(_ptr(w), w.numel() * w.element_size(), N, K, _ptr(packed),
+                                    packed.numel() * packed.element_size(), _stream(stream)))
 
 
 def tsd_gemm_rows_scratch_bytes(N, K, splits=1) -> int:

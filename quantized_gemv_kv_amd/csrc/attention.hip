@@ -18,7 +18,9 @@
 //       M = max m_i,  L = sum l_i 2^(m_i - M),  o = sum o_i 2^(m_i - M) / L
 //     by whoever consumes the attention output: in the decode step that is the prologue of the
 //     output-projection GEMV (so the merge costs neither a launch nor a device-wide fence);
-//     the standalone operator runs a small merge kernel;
+//     the standalone operator runs a small merge kernel; when a cache fits one chunk (the code
+//     predictor's) the workgroup normalises its own result and writes it as the fp16 hi/lo
+//     operand of the batched output projection;
 //   * the grid is sized for the full context and chunks past the current length exit at once,
 //     so one launch configuration serves every position (the step is replayed from a graph).
 #include <math.h>
@@ -131,6 +133,23 @@ __global__ __launch_bounds__(256) void k_attn(const AttnArgs a)
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, mw[w]);
+    if (a.act_hi) {   // the only chunk: normalise here and write the next GEMM's operand
+        float L = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWAVE; ++w) L = fmaf(lw[w], exp2f(mw[w] - M), L);
+        const float inv = 1.0f / L;
+        for (int i = threadIdx.x; i < HD; i += 256) {
+            float acc = 0.f;
+#pragma unroll
+            for (int w = 0; w < NWAVE; ++w) acc = fmaf(ow[w][i], exp2f(mw[w] - M), acc);
+            const float y = acc * inv;
+            const _Float16 hi = (_Float16)y;
+            const size_t idx = il_act(b, h * HD + i);
+            ((TSD_GLOBAL _Float16*)a.act_hi)[idx] = hi;
+            ((TSD_GLOBAL _Float16*)a.act_lo)[idx] = (_Float16)(y - (float)hi);
+        }
+        return;
+    }
     float* part = a.part + (((size_t)b * a.H + h) * attn_max_split(a.n_ctx) + s) * PS;
     for (int i = threadIdx.x; i < HD; i += 256) {
         float acc = 0.f;
@@ -176,6 +195,7 @@ size_t attn_part_bytes(int B, int H, int n_ctx, int hd)
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st)
 {
+    if (a.act_hi && (attn_max_split(a.n_ctx) != 1 || !a.act_lo)) return hipErrorInvalidValue;
     dim3 grid(attn_max_split(a.n_ctx), a.H, a.B);
     if (a.hd == 64) hipLaunchKernelGGL(k_attn<64>, grid, dim3(256), 0, st, a);
     else if (a.hd == 128) hipLaunchKernelGGL(k_attn<128>, grid, dim3(256), 0, st, a);

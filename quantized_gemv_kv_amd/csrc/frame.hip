@@ -13,11 +13,17 @@
 //     each, which carries about 22 bits of x;
 //   * each group of 64 along K is scaled in fp32 after its MFMAs:
 //       sum_k (s q_k + b) x_k = s P + (b + 128 s) X,   P = sum_k (q_k - 128) x_k,  X = sum_k x_k
-//     with X computed once per row and group by the kernel that produced the operand.
+//     and X comes from the same operand fragments multiplied by a fragment of ones (four more
+//     MFMAs per group, shared by every weight tile of the workgroup).
 // Operand roles: A = the 16 activation rows (lane l holds row l % 16), B = 16 weight rows (lane
 // l holds row n0 + l % 16), so a lane's four results share one weight row and so one (s, b) per
 // group.  Within a group, lane group j = l / 16 supplies K positions 16 j .. 16 j + 15 to two
 // MFMAs (the same K permutation on both operands), i.e. one 16-byte load of weights per lane.
+//
+// The operand is either ready (fp16 hi/lo, written by the attention or by the SwiGLU epilogue)
+// or the fp32 residual stream itself: the GEMM then gathers, scales by the norm gain and splits
+// the rows in registers, sums their squares across the workgroup and applies the RMSNorm's
+// 1 / rms to its results, so that no separate normalisation kernel runs between layers.
 #include <math.h>
 
 #include "gemv_core.h"
@@ -28,72 +34,25 @@ namespace {
 
 using core::silu;
 
-constexpr int NT = 256;
-constexpr int PT = MM_MAX_K / NT;   // prep: elements per thread
-
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void put_hilo(const Act16& a, size_t idx, float y, float& sum)
+__device__ __forceinline__ void put_hilo(const Act16& a, size_t idx, float y)
 {
     const _Float16 h = (_Float16)y;
-    const _Float16 l = (_Float16)(y - (float)h);
     ((TSD_GLOBAL _Float16*)a.hi)[idx] = h;
-    ((TSD_GLOBAL _Float16*)a.lo)[idx] = l;
-    sum = (float)h + (float)l;
+    ((TSD_GLOBAL _Float16*)a.lo)[idx] = (_Float16)(y - (float)h);
 }
 
-// ---- operand preparation: residual add, RMSNorm, fp16 hi/lo split, group sums --------------
-// one workgroup per row; thread t holds elements t + 256 i, so wave w holds the whole group
-// 4 i + w of its i-th element (K % 64 == 0): a group sum is a wave sum
-__global__ __launch_bounds__(NT) void k_prep16(const PrepArgs p)
+// ---- attention partials merged into the operand of the output projection -------------------
+// one thread per output element
+__global__ __launch_bounds__(256) void k_merge16(const float* __restrict__ part, int H, int hd, int max_split,
+                                                 const int* posp, int n_keys_value, int n, const Act16 a)
 {
-    const int b = blockIdx.x, t = threadIdx.x, K = p.K, G = K >> 6;
-    TSD_GLOBAL float* xr = glb(p.x) + (size_t)b * p.ldx;
-    __shared__ float red[NT / 64];
-    float v[PT];
-    float q2 = 0.f;
-#pragma unroll
-    for (int i = 0; i < PT; ++i) {
-        const int k = t + i * NT;
-        v[i] = 0.f;
-        if (k < K) {
-            float a = xr[k];
-            for (int s = 0; s < p.n_part; ++s) a += glb(p.part)[((size_t)s * MM_ROWS + b) * p.ldx + k];
-            if (p.n_part > 0) xr[k] = a;
-            v[i] = a;
-            q2 = fmaf(a, a, q2);
-        }
-    }
-    float r = 1.f;
-    if (p.g) {
-        q2 = wave_sum(q2);
-        if ((t & 63) == 0) red[t >> 6] = q2;
-        __syncthreads();
-        r = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)K + p.eps);
-    }
-#pragma unroll
-    for (int i = 0; i < PT; ++i) {
-        const int k0 = i * NT + (t & ~63);   // first element of this wave's group (uniform)
-        if (k0 >= K) break;
-        const int k = t + i * NT;
-        const float y = p.g ? v[i] * r * glb(p.g)[k] : v[i];
-        float s;
-        put_hilo(p.a, (size_t)b * K + k, y, s);
-        if (p.norm_out) glb(p.norm_out)[(size_t)b * K + k] = y;
-        s = wave_sum(s);
-        if ((t & 63) == 0) glb(p.a.gsum)[(size_t)b * G + (k0 >> 6)] = s;
-    }
-}
-
-// ---- attention partials merged straight into the operand of the output projection ----------
-// one 64-thread workgroup per group of 64 output elements (a head of 64 or half a head of 128)
-__global__ __launch_bounds__(64) void k_merge_prep16(const float* __restrict__ part, int H, int hd, int max_split,
-                                                     const int* posp, int n_keys_value, const Act16 a)
-{
-    const int e = blockIdx.x * 64 + threadIdx.x;
-    const int i = e % hd, bh = e / hd, b = bh / H, h = bh - b * H;
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= n) return;
+    const int i = e % hd, bh = e / hd;
     const int n_keys = posp ? ld_uniform(posp) + 1 : n_keys_value;
     const int n_split = (n_keys + ATTN_CHUNK - 1) / ATTN_CHUNK;
     const int PS = hd + 4;
@@ -106,11 +65,8 @@ __global__ __launch_bounds__(64) void k_merge_prep16(const float* __restrict__ p
         L = fmaf(pb[(size_t)t * PS + hd + 1], w, L);
         O = fmaf(pb[(size_t)t * PS + i], w, O);
     }
-    const int K = H * hd;
-    float s;
-    put_hilo(a, (size_t)b * K + h * hd + i, O / L, s);
-    s = wave_sum(s);
-    if (threadIdx.x == 0) glb(a.gsum)[(size_t)b * (K >> 6) + ((h * hd + i) >> 6)] = s;
+    const int b = bh / H, h = bh - b * H;
+    put_hilo(a, il_act(b, h * hd + i), O / L);
 }
 
 // ---- the skinny GEMM -------------------------------------------------------------------------
@@ -134,89 +90,40 @@ __device__ __forceinline__ half8 q8_to_half8(uint32_t w0, uint32_t w1)
     return __builtin_bit_cast(half8, u) - (_Float16)1152.0f;   // q - 128, exact
 }
 
-constexpr int MM_U = 4;   // groups per wave whose loads are issued together
-
-// Y = W X for the 16 operand rows: one workgroup per 16-row tile of W (blockIdx.x) and K slice
-// (blockIdx.y of gridDim.y); the four waves take the slice's groups round robin, add their
-// results in LDS, and wave 0 runs the epilogue.
-template <int EPI>
-__global__ __launch_bounds__(NT) void k_mm16(const PackedMat W, const Act16 a, const Mm16Out o)
+// fp32 values -> fp16 hi, lo
+__device__ __forceinline__ void split8(const float (&v)[8], half8& h, half8& l)
 {
-    const int K = W.K, G = K >> 6, N = W.N;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane >> 4, c16 = lane & 15;
-    const int n = blockIdx.x * 16 + c16;
-    const int nl = n < N ? n : N - 1;   // rows past N load row N-1 and store nothing
-    const int S = gridDim.y, sl = blockIdx.y;
-    const int g_lo = (int)((long long)G * sl / S), g_hi = (int)((long long)G * (sl + 1) / S);
-    const int gw = g_hi - g_lo > wave ? (g_hi - g_lo - wave + 3) >> 2 : 0;   // this wave's groups
-
-    const TSD_GLOBAL uint8_t* wr = glb(W.q) + (size_t)nl * K + 16 * j;
-    const TSD_GLOBAL _Float16* sr = (const TSD_GLOBAL _Float16*)glb(W.s) + (size_t)nl * G;
-    const TSD_GLOBAL _Float16* br = (const TSD_GLOBAL _Float16*)glb(W.b) + (size_t)nl * G;
-    const TSD_GLOBAL _Float16* ah = (const TSD_GLOBAL _Float16*)glb(a.hi) + (size_t)c16 * K + 16 * j;
-    const TSD_GLOBAL _Float16* al = (const TSD_GLOBAL _Float16*)glb(a.lo) + (size_t)c16 * K + 16 * j;
-    const TSD_GLOBAL float* gs = glb(a.gsum) + (size_t)(4 * j) * G;
-
-    float4v acc = {0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < gw; c += MM_U) {
-        u32x4 wq[MM_U];
-        half8 h0[MM_U], h1[MM_U], l0[MM_U], l1[MM_U];
-        float sc[MM_U], bi[MM_U], xs[MM_U][4];
 #pragma unroll
-        for (int u = 0; u < MM_U; ++u) {   // every load of the chunk first (clamped, masked below)
-            const int gi = c + u < gw ? c + u : gw - 1;
-            const int grp = g_lo + wave + 4 * gi, k0 = grp * 64;
-            wq[u] = *(const TSD_GLOBAL u32x4*)(wr + k0);
-            h0[u] = *(const TSD_GLOBAL half8*)(ah + k0);
-            h1[u] = *(const TSD_GLOBAL half8*)(ah + k0 + 8);
-            l0[u] = *(const TSD_GLOBAL half8*)(al + k0);
-            l1[u] = *(const TSD_GLOBAL half8*)(al + k0 + 8);
-            sc[u] = (float)sr[grp];
-            bi[u] = (float)br[grp];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) xs[u][i] = gs[(size_t)i * G + grp];
-        }
-#pragma unroll
-        for (int u = 0; u < MM_U; ++u) {
-            const half8 w0 = q8_to_half8(wq[u].x, wq[u].y), w1 = q8_to_half8(wq[u].z, wq[u].w);
-            float4v pz = {0.f, 0.f, 0.f, 0.f};
-            pz = __builtin_amdgcn_mfma_f32_16x16x32_f16(h0[u], w0, pz, 0, 0, 0);
-            pz = __builtin_amdgcn_mfma_f32_16x16x32_f16(h1[u], w1, pz, 0, 0, 0);
-            pz = __builtin_amdgcn_mfma_f32_16x16x32_f16(l0[u], w0, pz, 0, 0, 0);
-            pz = __builtin_amdgcn_mfma_f32_16x16x32_f16(l1[u], w1, pz, 0, 0, 0);
-            const bool valid = c + u < gw;
-            const float s = valid ? sc[u] : 0.f;
-            const float c0 = valid ? fmaf(128.f, sc[u], bi[u]) : 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = fmaf(s, pz[i], fmaf(c0, xs[u][i], acc[i]));
-        }
+    for (int e = 0; e < 8; ++e) {
+        const _Float16 t = (_Float16)v[e];
+        h[e] = t;
+        l[e] = (_Float16)(v[e] - (float)t);
     }
+}
 
-    __shared__ float4v red[3][64];
-    if (wave > 0) red[wave - 1][lane] = acc;
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int w = 0; w < 3; ++w) {
-        const float4v r = red[w][lane];
-        acc[0] += r[0];
-        acc[1] += r[1];
-        acc[2] += r[2];
-        acc[3] += r[3];
-    }
-    // lane (j, c16) holds Y[4 j + i][n] for i < 4
+// lane (j, c16) holds Y[4 j + i][n] for i < 4
+template <int EPI>
+__device__ __forceinline__ void epilogue(const Mm16Out& o, int n, int N, int j, int c16, int sl, const float4v& acc)
+{
     if constexpr (EPI == MM_STORE) {
         TSD_GLOBAL float* y = glb(o.y) + sl * o.slice;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (4 * j + i < o.rows && n < N) y[(size_t)(4 * j + i) * o.ldy + n] = acc[i];
+    } else if constexpr (EPI == MM_RESID) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * j + i < o.rows && n < N) {
+                TSD_GLOBAL float* y = glb(o.y) + il_x(4 * j + i, n);
+                *y = *y + acc[i];
+            }
     } else if constexpr (EPI == MM_SWIGLU) {
         // rows (2m, 2m+1) = (gate_m, up_m): the up value sits in the neighbouring lane
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float up = __shfl_xor(acc[i], 1, 64);
             if ((c16 & 1) == 0 && 4 * j + i < o.rows && n < N)
-                glb(o.y)[(size_t)(4 * j + i) * o.ldy + (n >> 1)] = silu(acc[i]) * up;
+                put_hilo(o.act, il_act(4 * j + i, n >> 1), silu(acc[i]) * up);
         }
     } else {
         const int pos = o.posp ? ld_uniform(o.posp) : o.pos_value;
@@ -234,9 +141,9 @@ __global__ __launch_bounds__(NT) void k_mm16(const PackedMat W, const Act16 a, c
                 const float2 cs = o.rope[(size_t)pos * half + e];
                 const float ra = acc[i] * cs.x - partner * cs.y, rb = acc[i] * cs.y + partner * cs.x;
                 if (!isk) {
-                    TSD_GLOBAL float* q = glb(o.q) + (size_t)b * o.qrows + h * o.hd;
-                    q[e] = ra;
-                    q[e + half] = rb;
+                    TSD_GLOBAL float* qr = glb(o.q) + (size_t)b * o.qrows + h * o.hd;
+                    qr[e] = ra;
+                    qr[e + half] = rb;
                 } else {
                     TSD_GLOBAL _Float16* kr =
                         (TSD_GLOBAL _Float16*)glb(o.kc) + (((size_t)b * o.Hkv + h) * o.n_ctx + pos) * o.hd;
@@ -244,11 +151,231 @@ __global__ __launch_bounds__(NT) void k_mm16(const PackedMat W, const Act16 a, c
                     kr[e + half] = (_Float16)rb;
                 }
             } else {
-                const int r = n - o.qrows - o.krows, h = r / o.hd, e = r - h * o.hd;
+                const int rr = n - o.qrows - o.krows, h = rr / o.hd, e = rr - h * o.hd;
                 ((TSD_GLOBAL _Float16*)glb(o.vc))[(((size_t)b * o.Hkv + h) * o.n_ctx + pos) * o.hd + e] = (_Float16)acc[i];
             }
         }
     }
+}
+
+// Y = W X for the 16 operand rows: a workgroup of NW waves takes T consecutive 16-row tiles of W
+// (blockIdx.x) over one K slice (blockIdx.y of gridDim.y).  Each wave reduces a contiguous share
+// of the slice's groups: per chunk of U groups it issues every load first (weights of the T
+// tiles, then its operand fragment, which serves all T tiles), then converts and runs the MFMAs;
+// the waves add their results in LDS and wave 0 runs the epilogue.
+template <int EPI, int PRO, int T, int NW, int U>
+__global__ __launch_bounds__(64 * NW) void k_mm16(const TiledMat W, const MmIn in, const Mm16Out o)
+{
+    constexpr bool PX = PRO == MP_X;
+    const int K = W.K, G = K >> 6, N = W.N, tiles = (N + 15) >> 4;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane >> 4, c16 = lane & 15;
+    const int S = gridDim.y, sl = blockIdx.y;
+    const int g_lo = (int)((long long)G * sl / S), g_hi = (int)((long long)G * (sl + 1) / S);
+    const int cnt = g_hi - g_lo, q = cnt / NW, r = cnt - q * NW;
+    const int w_lo = g_lo + wave * q + (wave < r ? wave : r), w_n = q + (wave < r ? 1 : 0);
+    const bool lead = blockIdx.x == 0 && blockIdx.y == 0;
+
+    const TSD_GLOBAL u32x4* wr[T];
+    const TSD_GLOBAL uint32_t* sbr[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        int tile = blockIdx.x * T + t;
+        tile = tile < tiles ? tile : tiles - 1;   // tiles past the matrix reload the last one and store nothing
+        wr[t] = (const TSD_GLOBAL u32x4*)glb(W.q) + (size_t)tile * G * 64 + lane;
+        sbr[t] = glb(W.sb) + (size_t)tile * G * 16 + c16;
+    }
+    // this lane's operand row c16
+    const TSD_GLOBAL float4v* x4 = nullptr;   // il_x rows
+    const TSD_GLOBAL float* tr = nullptr;     // gathered row-major embedding row
+    bool rv = true;
+    if constexpr (PX) {
+        if (in.tab) {
+            rv = c16 < in.rows;
+            int id = rv ? in.codes[(size_t)c16 * in.ld_codes] : 0;
+            id = id < 0 ? 0 : (id >= in.tab_rows ? in.tab_rows - 1 : id);
+            tr = glb(in.tab) + (size_t)id * K + 8 * j;
+        } else {
+            x4 = (const TSD_GLOBAL float4v*)glb(in.x) + 2 * j * MM_ROWS + c16;
+        }
+    }
+    const TSD_GLOBAL half8* ah = (const TSD_GLOBAL half8*)glb(in.a.hi) + j * MM_ROWS + c16;
+    const TSD_GLOBAL half8* al = (const TSD_GLOBAL half8*)glb(in.a.lo) + j * MM_ROWS + c16;
+    const TSD_GLOBAL float4v* g4 = in.g ? (const TSD_GLOBAL float4v*)(glb(in.g) + 8 * j) : nullptr;
+    half8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
+
+    float4v acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = (float4v){0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f;   // sum of squares of this lane's x (row c16)
+    for (int c = 0; c < w_n; c += U) {
+        u32x4 wq[T][U];
+        uint32_t sb[T][U];
+        half8 h0[U], h1[U], l0[U], l1[U];
+        float4v xv[PX ? U : 1][4], gv[PX ? U : 1][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {   // clamped to the wave's last group, masked below
+            const int grp = w_lo + (c + u < w_n ? c + u : w_n - 1);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                wq[t][u] = wr[t][grp * 64];
+                sb[t][u] = sbr[t][grp * 16];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int grp = w_lo + (c + u < w_n ? c + u : w_n - 1);
+            if constexpr (PX) {
+                // K offsets 8j .. 8j+7 (first MFMA) and 32 + 8j .. (second) of the group
+                if (in.tab) {
+                    const TSD_GLOBAL float4v* p = (const TSD_GLOBAL float4v*)(tr + grp * 64);
+                    const float4v z = {0.f, 0.f, 0.f, 0.f};
+                    xv[u][0] = rv ? p[0] : z;
+                    xv[u][1] = rv ? p[1] : z;
+                    xv[u][2] = rv ? p[8] : z;
+                    xv[u][3] = rv ? p[9] : z;
+                } else {
+                    const int q4 = grp * 16 * MM_ROWS;   // float4 index of the group's first quad of rows
+                    xv[u][0] = x4[q4];
+                    xv[u][1] = x4[q4 + MM_ROWS];
+                    xv[u][2] = x4[q4 + 8 * MM_ROWS];
+                    xv[u][3] = x4[q4 + 9 * MM_ROWS];
+                }
+                if (g4) {
+                    gv[u][0] = g4[grp * 16];
+                    gv[u][1] = g4[grp * 16 + 1];
+                    gv[u][2] = g4[grp * 16 + 8];
+                    gv[u][3] = g4[grp * 16 + 9];
+                } else {
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) gv[u][p] = (float4v){1.f, 1.f, 1.f, 1.f};
+                }
+            } else {
+                h0[u] = ah[grp * 8 * MM_ROWS];
+                h1[u] = ah[(grp * 8 + 4) * MM_ROWS];
+                l0[u] = al[grp * 8 * MM_ROWS];
+                l1[u] = al[(grp * 8 + 4) * MM_ROWS];
+            }
+        }
+        // every load of the chunk is in flight before the first use
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool valid = c + u < w_n;
+            if constexpr (PX) {
+                float v0[8], v1[8];
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float xe = xv[u][p][e];
+                        ss = fmaf(valid ? xe : 0.f, xe, ss);
+                        const float ye = xe * gv[u][p][e];
+                        if (p < 2) v0[4 * p + e] = ye;
+                        else v1[4 * (p - 2) + e] = ye;
+                    }
+                if (lead && in.x_out && in.tab && rv && valid) {   // the gathered rows, for later residual adds
+                    TSD_GLOBAL float4v* xo = (TSD_GLOBAL float4v*)glb(in.x_out) + 2 * j * MM_ROWS + c16 +
+                                             (w_lo + c + u) * 16 * MM_ROWS;
+                    xo[0] = xv[u][0];
+                    xo[MM_ROWS] = xv[u][1];
+                    xo[8 * MM_ROWS] = xv[u][2];
+                    xo[9 * MM_ROWS] = xv[u][3];
+                }
+                split8(v0, h0[u], l0[u]);
+                split8(v1, h1[u], l1[u]);
+            }
+            // X: the group sums of the operand rows, from the same fragments
+            float4v xz = {0.f, 0.f, 0.f, 0.f};
+            xz = __builtin_amdgcn_mfma_f32_16x16x32_f16(h0[u], ones, xz, 0, 0, 0);
+            xz = __builtin_amdgcn_mfma_f32_16x16x32_f16(h1[u], ones, xz, 0, 0, 0);
+            xz = __builtin_amdgcn_mfma_f32_16x16x32_f16(l0[u], ones, xz, 0, 0, 0);
+            xz = __builtin_amdgcn_mfma_f32_16x16x32_f16(l1[u], ones, xz, 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const half8 w0 = q8_to_half8(wq[t][u].x, wq[t][u].y), w1 = q8_to_half8(wq[t][u].z, wq[t][u].w);
+                float4v pz = {0.f, 0.f, 0.f, 0.f};
+                pz = __builtin_amdgcn_mfma_f32_16x16x32_f16(h0[u], w0, pz, 0, 0, 0);
+                pz = __builtin_amdgcn_mfma_f32_16x16x32_f16(h1[u], w1, pz, 0, 0, 0);
+                pz = __builtin_amdgcn_mfma_f32_16x16x32_f16(l0[u], w0, pz, 0, 0, 0);
+                pz = __builtin_amdgcn_mfma_f32_16x16x32_f16(l1[u], w1, pz, 0, 0, 0);
+                const float sv = (float)__builtin_bit_cast(_Float16, (uint16_t)(sb[t][u] & 0xFFFFu));
+                const float bv = (float)__builtin_bit_cast(_Float16, (uint16_t)(sb[t][u] >> 16));
+                const float s1 = valid ? sv : 0.f;
+                const float c0 = valid ? fmaf(128.f, sv, bv) : 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[t][i] = fmaf(s1, pz[i], fmaf(c0, xz[i], acc[t][i]));
+            }
+        }
+    }
+
+    __shared__ float4v red[NW - 1][T][64];
+    __shared__ float ssw[NW][16];
+    __shared__ float rrow[16];
+    if (wave > 0)
+#pragma unroll
+        for (int t = 0; t < T; ++t) red[wave - 1][t][lane] = acc[t];
+    const bool norm = PX && in.norm;
+    if (norm) {
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        if (j == 0) ssw[wave][c16] = ss;
+    }
+    __syncthreads();
+    if (norm) {
+        if (threadIdx.x < 16) {
+            float tsum = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) tsum += ssw[w][threadIdx.x];
+            rrow[threadIdx.x] = 1.0f / sqrtf(tsum / (float)K + in.eps);
+        }
+        __syncthreads();
+        if (lead && in.norm_out) {   // RMSNorm(x) * g of every row, for a consumer of the normed state
+            for (int idx = threadIdx.x; idx < MM_ROWS * K; idx += 64 * NW) {
+                const int b = (idx >> 2) & (MM_ROWS - 1), k = (idx >> 6) * 4 + (idx & 3);
+                if (b < in.rows) glb(in.norm_out)[idx] = glb(in.x)[idx] * (in.g ? glb(in.g)[k] : 1.f) * rrow[b];
+            }
+        }
+    }
+    if (wave != 0) return;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+#pragma unroll
+        for (int w = 0; w < NW - 1; ++w) {
+            const float4v v = red[w][t][lane];
+            acc[t][0] += v[0];
+            acc[t][1] += v[1];
+            acc[t][2] += v[2];
+            acc[t][3] += v[3];
+        }
+        if (norm)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][i] *= rrow[4 * j + i];
+        epilogue<EPI>(o, (blockIdx.x * T + t) * 16 + c16, N, j, c16, sl, acc[t]);
+    }
+}
+
+// ---- repack a canonical 8-bit affine matrix into the tiled layout --------------------------
+// one thread per (source row, group)
+__global__ void k_pack_tiled(const uint8_t* __restrict__ src, int N, int K, uint8_t* __restrict__ dq,
+                             uint32_t* __restrict__ dsb, int mode, int hd, int row0)
+{
+    const int G = K / 64;
+    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (long long)N * G) return;
+    const int r = (int)(idx / G), g = (int)(idx - (long long)r * G);
+    const int dr = place_row(r, mode, hd, row0), t = dr >> 4, c = dr & 15;
+    const uint8_t* qs = src + (size_t)r * K + (size_t)g * 64;
+    uint8_t* blk = dq + ((size_t)t * G + g) * 1024;
+    for (int kk = 0; kk < 64; ++kk) {
+        const int jj = (kk & 31) >> 3, e = 8 * (kk >> 5) + (kk & 7);
+        blk[(jj * 16 + c) * 16 + e] = qs[kk];
+    }
+    const uint8_t* s = src + (size_t)N * K + ((size_t)r * G + g) * 2;
+    const uint8_t* b = src + (size_t)N * K + (size_t)N * G * 2 + ((size_t)r * G + g) * 2;
+    dsb[((size_t)t * G + g) * 16 + c] = (uint32_t)(s[0] | (s[1] << 8)) | ((uint32_t)(b[0] | (b[1] << 8)) << 16);
 }
 
 // ---- embeddings ----------------------------------------------------------------------------
@@ -263,27 +390,43 @@ __global__ void k_embed_sum16(const EmbedTabs T, const int* __restrict__ codes, 
         id = id < 0 ? 0 : (id >= T.rows[c] ? T.rows[c] - 1 : id);
         s += T.tab[c][(size_t)id * d + k];
     }
-    x[(size_t)b * d + k] = s;
+    x[il_x(b, k)] = s;
+}
+
+// row-major rows <-> the il_x layout
+__global__ void k_rows_to_il(const float* __restrict__ src, int B, int K, float* __restrict__ dst)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= MM_ROWS * K) return;
+    const int b = i / K, k = i - b * K;
+    dst[il_x(b, k)] = b < B ? src[i] : 0.f;
+}
+__global__ void k_il_to_rows(const float* __restrict__ src, int B, int K, float* __restrict__ dst)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= B * K) return;
+    const int b = i / K, k = i - b * K;
+    dst[i] = src[il_x(b, k)];
 }
 
 // ---- per-row greedy pick ---------------------------------------------------------------------
-__global__ __launch_bounds__(NT) void k_argmax_rows(const float* __restrict__ logits, int ld_l, int n, int* code,
-                                                    int ld_code)
+__global__ __launch_bounds__(256) void k_argmax_rows(const float* __restrict__ logits, int ld_l, int n, int* code,
+                                                     int ld_code)
 {
     const int b = blockIdx.x, t = threadIdx.x;
     const float* l = logits + (size_t)b * ld_l;
     unsigned long long best = 0ull;
-    for (int i = t; i < n; i += NT) {
+    for (int i = t; i < n; i += 256) {
         const unsigned long long key = ((unsigned long long)float_order_key(l[i]) << 32) | (0xFFFFFFFFu - (uint32_t)i);
         best = key > best ? key : best;
     }
     best = wave_max_u64(best);
-    __shared__ unsigned long long bk[NT / 64];
+    __shared__ unsigned long long bk[4];
     if ((t & 63) == 0) bk[t >> 6] = best;
     __syncthreads();
     if (t == 0) {
         unsigned long long m = bk[0];
-        for (int i = 1; i < NT / 64; ++i) m = bk[i] > m ? bk[i] : m;
+        for (int i = 1; i < 4; ++i) m = bk[i] > m ? bk[i] : m;
         code[(size_t)b * ld_code] = (int)(0xFFFFFFFFu - (uint32_t)m);
     }
 }
@@ -307,39 +450,90 @@ __global__ void k_frame_done(const int* __restrict__ codes, int n, int* hist, in
     if (threadIdx.x == 0) *pos = p + 1;
 }
 
+template <int EPI, int PRO, int T, int NW, int U>
+hipError_t go(const TiledMat& W, const MmIn& in, int splits, const Mm16Out& o, hipStream_t st)
+{
+    const int tiles = (W.N + 15) / 16;
+    const dim3 grid((tiles + T - 1) / T, splits);
+    hipLaunchKernelGGL((k_mm16<EPI, PRO, T, NW, U>), grid, dim3(64 * NW), 0, st, W, in, o);
+    return hipGetLastError();
+}
+
+// The launch shape: a tall matrix takes four tiles per workgroup (its operand fragment serves
+// all four); otherwise one tile, with enough waves that each reduces at most four groups of its
+// slice in one round of loads (the in-register split of an fp32 operand needs more registers
+// than a wave has beyond eight waves per workgroup).
+template <int EPI, int PRO>
+hipError_t launch_e(const TiledMat& W, const MmIn& in, int splits, const Mm16Out& o, hipStream_t st)
+{
+    const int tiles = (W.N + 15) / 16, gs = W.K / 64 / splits;
+    if (tiles >= 1024) return go<EPI, PRO, 4, 8, 2>(W, in, splits, o, st);
+    if (gs <= 16) return go<EPI, PRO, 1, 4, 4>(W, in, splits, o, st);
+    if (gs <= 32 || PRO == MP_X) return go<EPI, PRO, 1, 8, 4>(W, in, splits, o, st);
+    if constexpr (PRO == MP_ACT) {
+        if (gs <= 48) return go<EPI, PRO, 1, 12, 4>(W, in, splits, o, st);
+        return go<EPI, PRO, 1, 16, 4>(W, in, splits, o, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
-bool mm16_supported(int fmt, int N, int K) { return fmt == FMT_AFF8 && N > 0 && K > 0 && K % 64 == 0 && K <= MM_MAX_K; }
+bool mm16_supported(int N, int K) { return N > 0 && K > 0 && K % 64 == 0 && K <= MM_MAX_K; }
 
-hipError_t launch_prep16(const PrepArgs& p, hipStream_t st)
+hipError_t launch_mm16(int epi, int pro, const TiledMat& W, const MmIn& in, int splits, const Mm16Out& o, hipStream_t st)
 {
-    if (p.K <= 0 || p.K % 64 || p.K > MM_MAX_K || p.rows <= 0 || p.rows > MM_ROWS || p.n_part < 0 ||
-        p.n_part > MM_MAX_SPLIT || (p.n_part > 0 && !p.part))
+    if (!mm16_supported(W.N, W.K) || splits < 1 || splits > MM_MAX_SPLIT || splits > W.K / 64 || o.rows < 1 ||
+        o.rows > MM_ROWS || in.rows < 1 || in.rows > MM_ROWS)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_prep16, dim3(p.rows), dim3(NT), 0, st, p);
-    return hipGetLastError();
-}
-
-hipError_t launch_mm16(int epi, const PackedMat& W, const Act16& a, int splits, const Mm16Out& o, hipStream_t st)
-{
-    if (!mm16_supported(FMT_AFF8, W.N, W.K) || !W.b || splits < 1 || splits > MM_MAX_SPLIT || splits > W.K / 64 ||
-        o.rows < 1 || o.rows > MM_ROWS)
-        return hipErrorInvalidValue;
-    if (epi != MM_STORE && splits != 1) return hipErrorInvalidValue;   // nonlinear epilogues need the whole sum
+    if (epi != MM_STORE && splits != 1) return hipErrorInvalidValue;        // the other epilogues need the whole sum
+    if (pro == MP_X && in.norm && splits != 1) return hipErrorInvalidValue;  // the norm needs the whole row
+    if (pro == MP_X && !in.x && !in.tab) return hipErrorInvalidValue;
+    if (pro == MP_X && in.norm_out && (!in.norm || in.tab)) return hipErrorInvalidValue;
+    if (pro == MP_X && in.x_out && !in.tab) return hipErrorInvalidValue;
     if ((epi == MM_SWIGLU || epi == MM_QKV_ROPE) && W.N % 2) return hipErrorInvalidValue;
-    const dim3 grid((W.N + 15) / 16, splits);
-    if (epi == MM_STORE) hipLaunchKernelGGL(k_mm16<MM_STORE>, grid, dim3(NT), 0, st, W, a, o);
-    else if (epi == MM_SWIGLU) hipLaunchKernelGGL(k_mm16<MM_SWIGLU>, grid, dim3(NT), 0, st, W, a, o);
-    else if (epi == MM_QKV_ROPE) hipLaunchKernelGGL(k_mm16<MM_QKV_ROPE>, grid, dim3(NT), 0, st, W, a, o);
-    else return hipErrorInvalidValue;
+#define TSD_MM(E)                                                                \
+    if (epi == E) return pro == MP_X ? launch_e<E, MP_X>(W, in, splits, o, st)   \
+                                     : launch_e<E, MP_ACT>(W, in, splits, o, st);
+    TSD_MM(MM_STORE)
+    TSD_MM(MM_RESID)
+    TSD_MM(MM_SWIGLU)
+    TSD_MM(MM_QKV_ROPE)
+#undef TSD_MM
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_pack_tiled(const void* src, int N, int K, void* dst_base, int dst_N, int dst_row0, int mode, int hd,
+                             hipStream_t st)
+{
+    if (K % 64 || N <= 0) return hipErrorInvalidValue;
+    TiledMat T = tiled_view(dst_base, dst_N, K);
+    const long long n = (long long)N * (K / 64);
+    hipLaunchKernelGGL(k_pack_tiled, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (const uint8_t*)src, N, K,
+                       (uint8_t*)T.q, (uint32_t*)T.sb, mode, hd, dst_row0);
     return hipGetLastError();
 }
 
-hipError_t launch_merge_prep16(const float* part, int B, int H, int hd, int max_split, const int* posp, int n_keys_value,
-                               const Act16& a, hipStream_t st)
+hipError_t launch_rows_to_il(const float* src, int B, int K, float* dst, hipStream_t st)
 {
-    if (hd % 64 || B < 1 || B > MM_ROWS) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_merge_prep16, dim3(B * H * hd / 64), dim3(64), 0, st, part, H, hd, max_split, posp, n_keys_value, a);
+    const int n = MM_ROWS * K;
+    hipLaunchKernelGGL(k_rows_to_il, dim3((n + 255) / 256), dim3(256), 0, st, src, B, K, dst);
+    return hipGetLastError();
+}
+
+hipError_t launch_il_to_rows(const float* src, int B, int K, float* dst, hipStream_t st)
+{
+    const int n = B * K;
+    hipLaunchKernelGGL(k_il_to_rows, dim3((n + 255) / 256), dim3(256), 0, st, src, B, K, dst);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge16(const float* part, int B, int H, int hd, int max_split, const int* posp, int n_keys_value,
+                          const Act16& a, hipStream_t st)
+{
+    if (B < 1 || B > MM_ROWS) return hipErrorInvalidValue;
+    const int n = B * H * hd;
+    hipLaunchKernelGGL(k_merge16, dim3((n + 255) / 256), dim3(256), 0, st, part, H, hd, max_split, posp, n_keys_value, n, a);
     return hipGetLastError();
 }
 
@@ -354,7 +548,7 @@ hipError_t launch_embed_sum16(const EmbedTabs& T, const int* codes, int ld_codes
 hipError_t launch_argmax_rows(const float* logits, int ld_l, int n, int* code, int ld_code, int B, hipStream_t st)
 {
     if (n < 1 || B < 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_argmax_rows, dim3(B), dim3(NT), 0, st, logits, ld_l, n, code, ld_code);
+    hipLaunchKernelGGL(k_argmax_rows, dim3(B), dim3(256), 0, st, logits, ld_l, n, code, ld_code);
     return hipGetLastError();
 }
 

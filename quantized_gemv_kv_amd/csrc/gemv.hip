@@ -299,20 +299,7 @@ hipError_t go_fmt(int pro, int epi, const PackedMat& W, const ProArgs& pa, const
 
 // ---- repack canonical blocks into the kernel layout ----------------------------------------
 // one thread per (source row, scale group); `mode` places source row r at destination row
-//   IDENTITY: row0 + r
-//   ROPE_PAIRS: within each head of hd rows, element i < hd/2 -> 2i, i >= hd/2 -> 2(i-hd/2)+1
-//   INTERLEAVE_EVEN / _ODD: row0 + 2r (+1)
-__device__ __forceinline__ int place_row(int r, int mode, int hd, int row0)
-{
-    if (mode == PACK_ROPE_PAIRS) {
-        const int h = r / hd, i = r - h * hd, half = hd / 2;
-        return row0 + h * hd + (i < half ? 2 * i : 2 * (i - half) + 1);
-    }
-    if (mode == PACK_INTERLEAVE_EVEN) return row0 + 2 * r;
-    if (mode == PACK_INTERLEAVE_ODD) return row0 + 2 * r + 1;
-    return row0 + r;
-}
-
+// place_row(r, mode, hd, row0) (kernels.h)
 __global__ void k_pack(int fmt, const uint8_t* __restrict__ src, int N, int K, uint8_t* dq, __half* ds,
                        __half* db, int mode, int hd, int row0)
 {

@@ -71,8 +71,22 @@ int gemv_rows_per_block(int fmt, int K, int epi);
 
 hipError_t launch_pack(int fmt, const void* src, int N, int K, void* dst_base, int dst_N,
                        int dst_row0, int mode, int hd, hipStream_t st);
-// row placement modes for launch_pack
+// row placement modes for launch_pack (and launch_pack_tiled)
 enum PackMode : int { PACK_IDENTITY = 0, PACK_ROPE_PAIRS = 1, PACK_INTERLEAVE_EVEN = 2, PACK_INTERLEAVE_ODD = 3 };
+// destination row of source row r:
+//   IDENTITY: row0 + r
+//   ROPE_PAIRS: within each head of hd rows, element i < hd/2 -> 2i, i >= hd/2 -> 2(i-hd/2)+1
+//   INTERLEAVE_EVEN / _ODD: row0 + 2r (+1)
+__host__ __device__ inline int place_row(int r, int mode, int hd, int row0)
+{
+    if (mode == PACK_ROPE_PAIRS) {
+        const int h = r / hd, i = r - h * hd, half = hd / 2;
+        return row0 + h * hd + (i < half ? 2 * i : 2 * (i - half) + 1);
+    }
+    if (mode == PACK_INTERLEAVE_EVEN) return row0 + 2 * r;
+    if (mode == PACK_INTERLEAVE_ODD) return row0 + 2 * r + 1;
+    return row0 + r;
+}
 
 // ---- attention -------------------------------------------------------------------------------
 struct AttnArgs {
@@ -87,6 +101,11 @@ struct AttnArgs {
     const int* pos;      // n_keys = *pos + 1 + pos_add when pos != null
     int pos_add;
     int n_keys;          // used when pos == null
+    // when the cache fits one chunk (n_ctx <= ATTN_CHUNK) and act_hi is set, o is written straight
+    // into the batched GEMM operand (row b, column h * hd + i, il_act layout) as fp16 hi and lo
+    // (x - hi) instead of partials
+    __half* act_hi;
+    __half* act_lo;
 };
 size_t attn_part_bytes(int B, int H, int n_ctx, int hd);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
@@ -148,41 +167,86 @@ hipError_t launch_topk(const float* logits, int n, int k, float temperature, uns
                        int* posp, int pos_value, int* out, int* hist, int hist_stride, hipStream_t st);
 
 // ---- batched frame operators (frame.hip) -------------------------------------------------------
-// Up to MM_ROWS rows of activations go through the matrix cores together.  Every GEMM operand
-// buffer holds MM_ROWS rows; rows past the batch stay zero.
+// Up to MM_ROWS rows of activations go through the matrix cores together.  The batched path keeps
+// its data in layouts made for the MFMA operand fragments, so that one load instruction of a
+// wave reads 1 KB of consecutive bytes:
+//   * tiled weights (8-bit affine): for each 16-row tile t and group g of 64 along K, a 1 KB
+//     block of 64 lanes x 16 bytes; lane (j, c) (j = lane / 16, c = lane % 16) holds row 16 t + c
+//     at K offsets 64 g + kappa(j, e), e = 0..15, kappa(j, e) = 32 (e / 8) + 8 j + e % 8; then
+//     one 32-bit (scale | bias << 16) word per (t, g, c);
+//   * the fp32 rows x[b][k] (the residual stream) at il_x(b, k) = ((k / 4) 16 + b) 4 + k % 4;
+//   * the fp16 hi/lo operand of a GEMM at il_act(b, k) = ((k / 8) 16 + b) 8 + k % 8.
+// Every such buffer holds MM_ROWS rows; rows past the batch stay zero.
 constexpr int MM_ROWS = 16;
 constexpr int MM_MAX_SPLIT = 8;   // split-K slices of one GEMM, at most
 constexpr int MM_MAX_K = 4096;    // longest reduction dimension
 
-// a GEMM operand: x split into fp16 hi + lo (x - hi), and sum(hi + lo) over each group of 64
+__host__ __device__ inline size_t il_x(int b, int k) { return ((size_t)(k >> 2) * MM_ROWS + b) * 4 + (k & 3); }
+__host__ __device__ inline size_t il_act(int b, int k) { return ((size_t)(k >> 3) * MM_ROWS + b) * 8 + (k & 7); }
+
+struct TiledMat {
+    const uint8_t* q;     // [tiles][G][64 lanes][16]
+    const uint32_t* sb;   // [tiles][G][16]
+    int N, K;
+};
+inline size_t tiled_q_bytes(int N, int K) { return (size_t)((N + 15) / 16) * (K / 64) * 1024; }
+inline size_t tiled_bytes(int N, int K) { return align256(tiled_q_bytes(N, K)) + (size_t)((N + 15) / 16) * (K / 64) * 64; }
+inline TiledMat tiled_view(void* base, int N, int K)
+{
+    TiledMat m;
+    m.q = (const uint8_t*)base;
+    m.sb = (const uint32_t*)((uint8_t*)base + align256(tiled_q_bytes(N, K)));
+    m.N = N;
+    m.K = K;
+    return m;
+}
+// canonical 8-bit affine matrix [N][K] -> rows place_row(r, ...) of a tiled matrix of dst_N rows
+// (the destination must be zeroed first when some of its rows are not written)
+hipError_t launch_pack_tiled(const void* src, int N, int K, void* dst_base, int dst_N, int dst_row0, int mode, int hd,
+                             hipStream_t st);
+
+// a GEMM operand as two fp16 numbers per element, hi = fp16(x) and lo = fp16(x - hi), il_act layout
 struct Act16 {
-    __half* hi;        // [MM_ROWS][K]
-    __half* lo;        // [MM_ROWS][K]
-    float* gsum;       // [MM_ROWS][K / 64]
+    __half* hi;
+    __half* lo;
 };
 
-// prep: v = x[b] (+ sum over s < n_part of part[s][b]; then v is written back to x[b]);
-// y = v, or RMSNorm(v) * g; the operand of y; optionally y itself to norm_out[b]
-struct PrepArgs {
-    float* x;
-    int ldx;
-    const float* part;   // [n_part][MM_ROWS][ldx]
-    int n_part;
-    const float* g;      // null: no norm
+// where a GEMM's operand comes from
+enum MmPro : int {
+    MP_ACT = 0,   // a ready fp16 hi/lo operand
+    MP_X = 1      // fp32 rows, split into hi/lo by the GEMM itself (optionally gathered, scaled, normed)
+};
+struct MmIn {
+    Act16 a;                 // MP_ACT
+    // MP_X: the rows x (il_x layout, MM_ROWS rows), or with tab the embedding rows
+    // tab[codes[b * ld_codes]] (row-major [tab_rows][K], ids clamped) for b < rows; times g[k]
+    // when g is set; with norm, RMSNorm over K (the rows' 1/rms is applied to the results, so the
+    // workgroup must cover all of K: one slice)
+    const float* x;
+    const float* tab;
+    const int* codes;
+    int ld_codes, tab_rows;
+    const float* g;
+    int norm;
     float eps;
-    int K, rows;
-    Act16 a;
-    float* norm_out;     // [rows][K] or null
+    float* x_out;            // MP_X with tab: workgroup 0 also stores the gathered rows to x_out (il_x)
+    float* norm_out;         // MP_X with norm: workgroup 0 also stores RMSNorm(x) * g to norm_out (il_x)
+    int rows;                // rows b < rows are real
 };
 
-enum Mm16Epi : int { MM_STORE = 0, MM_SWIGLU = 1, MM_QKV_ROPE = 2 };
+enum Mm16Epi : int { MM_STORE = 0, MM_SWIGLU = 1, MM_QKV_ROPE = 2, MM_RESID = 3 };
 struct Mm16Out {
-    float* y;            // STORE: y[split][b][n] at y + split * slice + b * ldy + n; SWIGLU: y[b][n/2]
+    // STORE: y[split][b][n] at y + split * slice + b * ldy + n (row-major).
+    // RESID: y[il_x(b, n)] += result (the residual stream).
+    float* y;
     int ldy;
     long long slice;
+    // SWIGLU: rows (2m, 2m+1) = (gate_m, up_m); silu(gate) * up is written as the next GEMM's
+    // operand act at il_act(b, m)
+    Act16 act;
     int rows;            // activation rows b < rows are written
     // QKV_ROPE: rows [0, qrows) and [qrows, qrows + krows) in RoPE pairs (2i, 2i+1) = (i, i+hd/2)
-    // of each head -> rotated q [b][qrows] and K cache; the rest -> V cache; caches
+    // of each head -> rotated q [b][qrows] (row-major) and K cache; the rest -> V cache; caches
     // [b][Hkv][n_ctx][hd] at slot pos (*posp, else pos_value)
     int qrows, krows, hd, Hkv, n_ctx;
     float* q;
@@ -197,17 +261,18 @@ struct EmbedTabs {
     int rows[16];
 };
 
-// W: AFF8 (the only format with a matrix-core path), any N, K % 64 == 0, K <= MM_MAX_K
-bool mm16_supported(int fmt, int N, int K);
-hipError_t launch_prep16(const PrepArgs& p, hipStream_t st);
-hipError_t launch_mm16(int epi, const PackedMat& W, const Act16& a, int splits, const Mm16Out& o, hipStream_t st);
+bool mm16_supported(int N, int K);   // any N, K % 64 == 0, K <= MM_MAX_K
+hipError_t launch_mm16(int epi, int pro, const TiledMat& W, const MmIn& in, int splits, const Mm16Out& o, hipStream_t st);
 // attention partials (launch_attention layout, max_split slots per head) of rows b < B merged into
-// the operand of [B][H * hd]; n_keys = *posp + 1, else n_keys_value
-hipError_t launch_merge_prep16(const float* part, int B, int H, int hd, int max_split, const int* posp, int n_keys_value,
-                               const Act16& a, hipStream_t st);
-// x[b] = sum over c < n_tab of tab[c][codes[b * ld_codes + c]] for b < B (ids clamped into each table)
+// the operand [B][H * hd]; n_keys = *posp + 1, else n_keys_value
+hipError_t launch_merge16(const float* part, int B, int H, int hd, int max_split, const int* posp, int n_keys_value,
+                          const Act16& a, hipStream_t st);
+// x[il_x(b, k)] = sum over c < n_tab of tab[c][codes[b * ld_codes + c]][k] for b < B (ids clamped)
 hipError_t launch_embed_sum16(const EmbedTabs& T, const int* codes, int ld_codes, int n_tab, int d, float* x, int B,
                               hipStream_t st);
+// row-major [B][K] <-> il_x (rows past B of the interleaved side written as zeros)
+hipError_t launch_rows_to_il(const float* src, int B, int K, float* dst, hipStream_t st);
+hipError_t launch_il_to_rows(const float* src, int B, int K, float* dst, hipStream_t st);
 // code[b * ld_code] = argmax of logits[b * ld_l + 0 .. n) for b < B (ties to the lowest index)
 hipError_t launch_argmax_rows(const float* logits, int ld_l, int n, int* code, int ld_code, int B, hipStream_t st);
 // y[i] = sum over s < S of part[s * slice + i] for i < n

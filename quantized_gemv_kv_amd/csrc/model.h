@@ -30,6 +30,25 @@ struct Planner {
     }
 };
 
+// a LLAMA-shaped layer of the batched frame: tiled matrices (qkv rows in RoPE pairs, gate/up
+// interleaved), RMSNorm gains
+struct TLayerW {
+    TiledMat qkv, o, fc, down;
+    float *n1g = nullptr, *n2g = nullptr;
+};
+
+inline TiledMat take_tiled(Planner& P, int N, int K)
+{
+    void* p = P.take(tiled_bytes(N, K));
+    if (!p) {
+        TiledMat m{};
+        m.N = N;
+        m.K = K;
+        return m;
+    }
+    return tiled_view(p, N, K);
+}
+
 inline PackedMat take_mat(Planner& P, int f, int N, int K)
 {
     PackedLayout L = packed_layout(f, N, K);
@@ -107,15 +126,14 @@ struct tsd_model {
     hipGraphExec_t exec = nullptr;
     // TALKER_CP: batch rows through the matrix-core GEMM; the code predictor's own layers,
     // norm, heads and cache; the graph of a frame without head and predictor (prefill)
-    std::vector<tsd::LayerW> Lc;
+    std::vector<tsd::TLayerW> Lt, Lc;   // Talker and predictor layers
+    tsd::TiledMat t_head{};
     float* cp_nfg = nullptr;
-    tsd::PackedMat cp_head[16] = {};
+    tsd::TiledMat cp_head[16] = {};
     __half *ckc = nullptr, *cvc = nullptr;
     size_t ckv_layer_elems = 0;
     float* xc = nullptr;              // predictor residual stream [16][d]
-    float* mmp = nullptr;             // split-K partial sums [MM_MAX_SPLIT][16][d]
-    tsd::Act16 act{};                 // GEMM operand [16][K] as fp16 hi/lo + group sums
-    int split_o = 1, split_down = 1;
+    tsd::Act16 act{};                 // GEMM operand, fp16 hi/lo of 16 rows (il_act layout)
     hipGraph_t graph_talker = nullptr;
     hipGraphExec_t exec_talker = nullptr;
     int kind_launches[tsd::TSD_KERNEL_KINDS] = {};

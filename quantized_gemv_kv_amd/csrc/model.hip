@@ -752,11 +752,16 @@ tsd_status tsd_layer_forward(tsd_model* m, int layer, const float* d_x, int pos,
     const tsd_config& c = m->c;
     if (layer < 0 || layer >= c.n_layer) return fail(m, TSD_ERR_INVALID_ARGUMENT, "layer out of range");
     if (pos < 0 || pos >= c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "position outside the context");
+    HIP_TRY(m, launch_fill_i32(m->dbg_pos, pos, 1, m->st), "set position");
+    if (c.arch == TSD_ARCH_TALKER_CP) {   // the batched frame keeps its rows interleaved
+        HIP_TRY(m, launch_rows_to_il(d_x, c.batch, c.d_model, m->x, m->st), "copy x");
+        HIP_TRY(m, talker_layer(m, layer, m->st, m->dbg_pos), "layer");
+        HIP_TRY(m, launch_il_to_rows(m->x, c.batch, c.d_model, d_out, m->st), "copy out");
+        return TSD_OK;
+    }
     const size_t xb = (size_t)c.batch * c.d_model * sizeof(float);
     HIP_TRY(m, hipMemcpyAsync(m->x, d_x, xb, hipMemcpyDeviceToDevice, m->st), "copy x");
-    HIP_TRY(m, launch_fill_i32(m->dbg_pos, pos, 1, m->st), "set position");
-    if (c.arch == TSD_ARCH_TALKER_CP) HIP_TRY(m, talker_layer(m, layer, m->st, m->dbg_pos), "layer");
-    else HIP_TRY(m, enqueue_layer(m, layer, m->st, m->dbg_pos, false), "layer");
+    HIP_TRY(m, enqueue_layer(m, layer, m->st, m->dbg_pos, false), "layer");
     HIP_TRY(m, hipMemcpyAsync(d_out, m->x, xb, hipMemcpyDeviceToDevice, m->st), "copy out");
     return TSD_OK;
 }
@@ -844,26 +849,34 @@ tsd_status tsd_gemv(int wfmt, const void* d_packed, int N, int K, int B, const f
     return TSD_OK;
 }
 
-// operand [16][K] hi, lo; group sums [16][K/64]; split-K slices [splits][16][N]
-size_t gemm_rows_layout(int N, int K, int splits, size_t* off_lo, size_t* off_gs, size_t* off_part)
+tsd_status tsd_gemm_rows_packed_bytes(int N, int K, size_t* out)
 {
-    size_t o = 0;
-    o += align256((size_t)MM_ROWS * K * 2);
-    *off_lo = o;
-    o += align256((size_t)MM_ROWS * K * 2);
-    *off_gs = o;
-    o += align256((size_t)MM_ROWS * (K / 64) * 4);
-    *off_part = o;
-    o += (size_t)splits * MM_ROWS * N * 4;
-    return o;
+    if (!out || !mm16_supported(N, K)) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "bad shape");
+    *out = tiled_bytes(N, K);
+    return TSD_OK;
+}
+
+tsd_status tsd_gemm_rows_pack(const void* d_w, size_t w_bytes, int N, int K, void* d_packed, size_t packed_bytes,
+                              void* stream)
+{
+    size_t need = 0;
+    tsd_status s = tsd_gemm_rows_packed_bytes(N, K, &need);
+    if (s != TSD_OK) return s;
+    if (!d_w || !d_packed) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null buffer");
+    if ((uintptr_t)d_packed % 256) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "packed buffer must be 256-byte aligned");
+    if (w_bytes != canonical_matrix_bytes(TSD_W_AFFINE8_G64, N, K))
+        return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "canonical size mismatch");
+    if (packed_bytes < need) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "packed buffer too small");
+    hipError_t e = launch_pack_tiled(d_w, N, K, d_packed, N, 0, PACK_IDENTITY, 64, (hipStream_t)stream);
+    return e == hipSuccess ? TSD_OK : hip_fail(nullptr, e, "pack");
 }
 
 tsd_status tsd_gemm_rows_scratch_bytes(int N, int K, int splits, size_t* out)
 {
-    if (!out || N <= 0 || !mm16_supported(FMT_AFF8, N, K) || splits < 1 || splits > MM_MAX_SPLIT || splits > K / 64)
+    if (!out || !mm16_supported(N, K) || splits < 1 || splits > MM_MAX_SPLIT || splits > K / 64)
         return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "bad shape or split count");
-    size_t a, b, c;
-    *out = gemm_rows_layout(N, K, splits, &a, &b, &c);
+    // the interleaved operand rows, then the split-K slices
+    *out = align256((size_t)MM_ROWS * K * 4) + (splits == 1 ? 0 : (size_t)splits * MM_ROWS * N * 4);
     return TSD_OK;
 }
 
@@ -875,38 +888,26 @@ tsd_status tsd_gemm_rows(const void* d_packed, int N, int K, int B, const float*
     if (s != TSD_OK) return s;
     if (B < 1 || B > MM_ROWS) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "B must be 1..16");
     if (!d_packed || !d_x || !d_y || !d_scratch) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null buffer");
-    if ((uintptr_t)d_scratch % 256) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "scratch must be 256-byte aligned");
+    if ((uintptr_t)d_scratch % 256 || (uintptr_t)d_packed % 256)
+        return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "packed matrix and scratch must be 256-byte aligned");
     if (scratch_bytes < need) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "scratch too small");
     hipStream_t st = (hipStream_t)stream;
-    size_t off_lo, off_gs, off_part;
-    gemm_rows_layout(N, K, splits, &off_lo, &off_gs, &off_part);
-    uint8_t* base = (uint8_t*)d_scratch;
-    Act16 a{(__half*)base, (__half*)(base + off_lo), (float*)(base + off_gs)};
-    hipError_t e = hipSuccess;
-    if (B < MM_ROWS) {   // rows past B enter the GEMM as zeros
-        const int rest = MM_ROWS - B;
-        e = launch_fill_u32((unsigned*)(a.hi + (size_t)B * K), 0u, rest * K / 2, st);
-        if (e == hipSuccess) e = launch_fill_u32((unsigned*)(a.lo + (size_t)B * K), 0u, rest * K / 2, st);
-        if (e == hipSuccess) e = launch_fill_f32(a.gsum + (size_t)B * (K / 64), 0.f, (size_t)rest * (K / 64), st);
-    }
-    PrepArgs p{};
-    p.x = (float*)d_x;   // read only: no partial slices to add
-    p.ldx = K;
-    p.K = K;
-    p.rows = B;
-    p.a = a;
-    if (e == hipSuccess) e = launch_prep16(p, st);
-    PackedMat W = packed_view(FMT_AFF8, (void*)d_packed, N, K);
+    TiledMat W = tiled_view((void*)d_packed, N, K);
+    float* xi = (float*)d_scratch;
+    hipError_t e = launch_rows_to_il(d_x, B, K, xi, st);
+    MmIn in{};
+    in.x = xi;
+    in.rows = B;
     Mm16Out o{};
     o.rows = B;
     o.ldy = N;
     if (splits == 1) {
         o.y = d_y;
-        if (e == hipSuccess) e = launch_mm16(MM_STORE, W, a, 1, o, st);
+        if (e == hipSuccess) e = launch_mm16(MM_STORE, MP_X, W, in, 1, o, st);
     } else {
-        o.y = (float*)(base + off_part);
+        o.y = (float*)((uint8_t*)d_scratch + align256((size_t)MM_ROWS * K * 4));
         o.slice = (long long)MM_ROWS * N;
-        if (e == hipSuccess) e = launch_mm16(MM_STORE, W, a, splits, o, st);
+        if (e == hipSuccess) e = launch_mm16(MM_STORE, MP_X, W, in, splits, o, st);
         if (e == hipSuccess) e = launch_sum_slices(o.y, splits, o.slice, d_y, (long long)B * N, st);
     }
     return e == hipSuccess ? TSD_OK : hip_fail(nullptr, e, "gemm rows");

@@ -11,11 +11,13 @@
 // How: every linear is the batched matrix-core GEMM of frame.hip over all rows at once; one
 // launch per operator, recorded into the step graph (a frame of the 28 + 5 x 16 layers is about
 // a thousand launches, replayed with one graph launch).  Per layer:
-//   prep(residual add + RMSNorm) -> QKV GEMM with RoPE and fp16 K/V append in its epilogue ->
-//   split-KV attention -> merge into the O-proj operand -> O-proj GEMM (split-K partials) ->
-//   prep(residual add + RMSNorm) -> gate/up GEMM with SwiGLU -> prep -> down GEMM (partials).
-// A GEMM with few 16-row tiles is cut along K into slices whose partial sums the next prep adds
-// into the residual stream, so that every GEMM has about one workgroup per compute unit.
+//   QKV GEMM (RMSNorm of the fp32 residual rows in its prologue; RoPE and the fp16 K/V append
+//   in its epilogue) -> split-KV attention (a one-chunk cache, the predictor's, writes the next
+//   operand itself; the Talker's two chunks are merged by a small kernel) -> O-proj GEMM adding
+//   into the residual -> gate/up GEMM (RMSNorm prologue, SwiGLU epilogue writing the next
+//   operand) -> down GEMM adding into the residual: five or six launches per layer.
+// The O and down projections have few 16-row tiles and a long K: sixteen waves of one
+// workgroup share the K range, so every result has a single writer and adds deterministically.
 #include <algorithm>
 #include <string>
 
@@ -24,48 +26,42 @@
 namespace tsd {
 namespace {
 
-// split-K slices for an N x K GEMM: double while the 16-row tiles do not cover the compute units
-// and every wave of a slice still has a group of 64 to reduce
-int splits_for(int N, int K)
-{
-    constexpr int n_cu = 256;
-    const int tiles = (N + 15) / 16, G = K / 64;
-    int s = 1;
-    while (tiles * s < n_cu && s * 2 <= MM_MAX_SPLIT && G / (s * 2) >= 4) s *= 2;
-    return s;
-}
-
-hipError_t prep(tsd_model* m, hipStream_t st, float* x, int ldx, int n_part, const float* g, int K, float* norm_out)
-{
-    PrepArgs p{};
-    p.x = x;
-    p.ldx = ldx;
-    p.part = m->mmp;
-    p.n_part = n_part;
-    p.g = g;
-    p.eps = m->c.norm_eps;
-    p.K = K;
-    p.rows = m->c.batch;
-    p.a = m->act;
-    p.norm_out = norm_out;
-    return launch_prep16(p, st);
-}
-
 #define TRY(expr)                            \
     do {                                     \
         hipError_t e_ = (expr);              \
         if (e_ != hipSuccess) return e_;     \
     } while (0)
 
+// embedding rows gathered by the first predictor layer (its input is E_{j-1}(c_{j-1}))
+struct Gather {
+    const float* tab;
+    int rows;
+    const int* codes;
+};
+
 // One LLAMA-shaped layer on the residual stream x[rows][d] whose cache (kc, vc: [rows][Hkv]
-// [n_ctx][hd]) gets slot pos = *posp (Talker) or pos_value (predictor).  n_in partial slices of
-// the previous down projection are still to be added into x; *n_out receives this layer's.
-hipError_t layer16(tsd_model* m, const LayerW& w, float* x, int n_in, __half* kc, __half* vc, int n_ctx,
-                   const int* posp, int pos_value, hipStream_t st, Probe* pr, int* n_out)
+// [n_ctx][hd]) gets slot pos = *posp (Talker) or pos_value (predictor).  With gather, the
+// layer's input rows are embedding rows, which the QKV GEMM also stores to x.
+hipError_t layer16(tsd_model* m, const TLayerW& w, float* x, __half* kc, __half* vc, int n_ctx, const int* posp,
+                   int pos_value, hipStream_t st, Probe* pr, const Gather* gather = nullptr)
 {
     const tsd_config& c = m->c;
     const int d = c.d_model, H = c.n_head, Hk = c.n_kv_head, hd = c.head_dim, ff = c.d_ff, B = c.batch;
-    TRY(prep(m, st, x, d, n_in, w.n1g, d, nullptr));
+    // norm + fused QKV, RoPE and the K/V append
+    MmIn iq{};
+    iq.x = x;
+    iq.g = w.n1g;
+    iq.norm = 1;
+    iq.eps = c.norm_eps;
+    iq.rows = B;
+    if (gather) {
+        iq.x = nullptr;
+        iq.tab = gather->tab;
+        iq.tab_rows = gather->rows;
+        iq.codes = gather->codes;
+        iq.ld_codes = c.n_codebooks;
+        iq.x_out = x;
+    }
     Mm16Out oq{};
     oq.rows = B;
     oq.qrows = H * hd;
@@ -81,8 +77,10 @@ hipError_t layer16(tsd_model* m, const LayerW& w, float* x, int n_in, __half* kc
     oq.pos_value = pos_value;
     {
         Bracket br(pr, KIND_QKV, st);
-        TRY(launch_mm16(MM_QKV_ROPE, w.qkv, m->act, 1, oq, st));
+        TRY(launch_mm16(MM_QKV_ROPE, MP_X, w.qkv, iq, 1, oq, st));
     }
+    // attention; a cache of one chunk writes the output projection's operand directly
+    const bool direct = attn_max_split(n_ctx) == 1;
     AttnArgs aa{};
     aa.q = m->qkv;
     aa.ldq = H * hd;
@@ -97,53 +95,68 @@ hipError_t layer16(tsd_model* m, const LayerW& w, float* x, int n_in, __half* kc
     aa.n_ctx = n_ctx;
     aa.pos = posp;
     aa.n_keys = pos_value + 1;
+    aa.act_hi = direct ? m->act.hi : nullptr;
+    aa.act_lo = direct ? m->act.lo : nullptr;
     {
         Bracket br(pr, KIND_ATTN, st);
         TRY(launch_attention(aa, st));
     }
-    TRY(launch_merge_prep16(m->part, B, H, hd, attn_max_split(n_ctx), posp, pos_value + 1, m->act, st));
-    Mm16Out oo{};
-    oo.y = m->mmp;
-    oo.ldy = d;
-    oo.slice = (long long)MM_ROWS * d;
-    oo.rows = B;
+    if (!direct) TRY(launch_merge16(m->part, B, H, hd, attn_max_split(n_ctx), posp, pos_value + 1, m->act, st));
+    // output projection + residual
+    MmIn ia{};
+    ia.a = m->act;
+    ia.rows = B;
+    Mm16Out orr{};
+    orr.y = x;
+    orr.rows = B;
     {
         Bracket br(pr, KIND_OPROJ, st);
-        TRY(launch_mm16(MM_STORE, w.o, m->act, m->split_o, oo, st));
+        TRY(launch_mm16(MM_RESID, MP_ACT, w.o, ia, 1, orr, st));
     }
-    TRY(prep(m, st, x, d, m->split_o, w.n2g, d, nullptr));
+    // norm + gate/up + SwiGLU, written as the down projection's operand
+    MmIn ig{};
+    ig.x = x;
+    ig.g = w.n2g;
+    ig.norm = 1;
+    ig.eps = c.norm_eps;
+    ig.rows = B;
     Mm16Out of{};
-    of.y = m->h;
-    of.ldy = ff;
+    of.act = m->act;
     of.rows = B;
     {
         Bracket br(pr, KIND_FC, st);
-        TRY(launch_mm16(MM_SWIGLU, w.fc, m->act, 1, of, st));
+        TRY(launch_mm16(MM_SWIGLU, MP_X, w.fc, ig, 1, of, st));
     }
-    TRY(prep(m, st, m->h, ff, 0, nullptr, ff, nullptr));
+    // down projection + residual
     {
         Bracket br(pr, KIND_DOWN, st);
-        TRY(launch_mm16(MM_STORE, w.down, m->act, m->split_down, oo, st));
+        TRY(launch_mm16(MM_RESID, MP_ACT, w.down, ia, 1, orr, st));
     }
-    *n_out = m->split_down;
+    (void)ff;
     return hipSuccess;
 }
 
-// final RMSNorm (adding the pending partials), head j into logits[b][j][..], and code j of every
-// row into tok[b][j]; norm_out receives the normed hidden state (or null)
-hipError_t head16(tsd_model* m, hipStream_t st, Probe* pr, float* x, int n_in, const float* g, const PackedMat& W, int j,
-                  int vocab, float* norm_out)
+// final RMSNorm + head j into logits[b][j][..], and code j of every row into tok[b][j];
+// norm_out receives the normed hidden state (or null)
+hipError_t head16(tsd_model* m, hipStream_t st, Probe* pr, float* x, const float* g, const TiledMat& W, int j, int vocab,
+                  float* norm_out)
 {
     const tsd_config& c = m->c;
     const int C = c.n_codebooks, B = c.batch;
-    TRY(prep(m, st, x, c.d_model, n_in, g, c.d_model, norm_out));
+    MmIn ih{};
+    ih.x = x;
+    ih.g = g;
+    ih.norm = 1;
+    ih.eps = c.norm_eps;
+    ih.rows = B;
+    ih.norm_out = norm_out;
     Mm16Out oh{};
     oh.y = m->logits + (size_t)j * m->vmax;
     oh.ldy = C * m->vmax;
     oh.rows = B;
     {
         Bracket br(pr, KIND_HEAD, st);
-        TRY(launch_mm16(MM_STORE, W, m->act, 1, oh, st));
+        TRY(launch_mm16(MM_STORE, MP_X, W, ih, 1, oh, st));
     }
     const float* lg = m->logits + (size_t)j * m->vmax;
     if (m->samp.mode == 1) {
@@ -208,7 +221,7 @@ size_t talker_plan(tsd_model* m, const tsd_config* c, uint8_t* base)
 {
     Planner P(base);
     const int d = c->d_model, H = c->n_head, Hk = c->n_kv_head, hd = c->head_dim, ff = c->d_ff, B = c->batch;
-    const int C = c->n_codebooks, V = c->vocab, Vc = c->cp_vocab, f = c->wfmt;
+    const int C = c->n_codebooks, V = c->vocab, Vc = c->cp_vocab;
     const int qd = H * hd, kd = Hk * hd, vmax = std::max(V, Vc), kmax = std::max(d, std::max(qd, ff));
     const int rope_rows = std::max(c->n_ctx, C);
     int* pos = (int*)P.take(4 * sizeof(int));
@@ -219,8 +232,6 @@ size_t talker_plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     float* xc = (float*)P.take(sizeof(float) * MM_ROWS * d);
     __half* hi = (__half*)P.take(2 * (size_t)MM_ROWS * kmax);
     __half* lo = (__half*)P.take(2 * (size_t)MM_ROWS * kmax);
-    float* gsum = (float*)P.take(sizeof(float) * MM_ROWS * (kmax / 64));
-    float* mmp = (float*)P.take(sizeof(float) * (size_t)MM_MAX_SPLIT * MM_ROWS * d);
     float* q = (float*)P.take(sizeof(float) * MM_ROWS * qd);
     float* h = (float*)P.take(sizeof(float) * MM_ROWS * (size_t)ff);
     float* logits = (float*)P.take(sizeof(float) * (size_t)B * C * vmax);
@@ -230,24 +241,24 @@ size_t talker_plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     emb[0] = (float*)P.take(sizeof(float) * (size_t)V * d);
     for (int k = 1; k < C; ++k) emb[k] = (float*)P.take(sizeof(float) * (size_t)Vc * d);
     auto layers = [&](int n) {
-        std::vector<LayerW> Ls(n);
-        for (LayerW& w : Ls) {
-            w.qkv = take_mat(P, f, qd + 2 * kd, d);
-            w.o = take_mat(P, f, d, qd);
-            w.fc = take_mat(P, f, 2 * ff, d);
-            w.down = take_mat(P, f, d, ff);
+        std::vector<TLayerW> Ls(n);
+        for (TLayerW& w : Ls) {
+            w.qkv = take_tiled(P, qd + 2 * kd, d);
+            w.o = take_tiled(P, d, qd);
+            w.fc = take_tiled(P, 2 * ff, d);
+            w.down = take_tiled(P, d, ff);
             w.n1g = (float*)P.take(4 * d);
             w.n2g = (float*)P.take(4 * d);
         }
         return Ls;
     };
-    std::vector<LayerW> Lt = layers(c->n_layer);
+    std::vector<TLayerW> Lt = layers(c->n_layer);
     float* nfg = (float*)P.take(4 * d);
-    PackedMat head = take_mat(P, f, V, d);
-    std::vector<LayerW> Lc = layers(c->cp_n_layer);
+    TiledMat head = take_tiled(P, V, d);
+    std::vector<TLayerW> Lc = layers(c->cp_n_layer);
     float* cp_nfg = (float*)P.take(4 * d);
-    PackedMat cp_head[16] = {};
-    for (int k = 1; k < C; ++k) cp_head[k] = take_mat(P, f, Vc, d);
+    TiledMat cp_head[16] = {};
+    for (int k = 1; k < C; ++k) cp_head[k] = take_tiled(P, Vc, d);
     const size_t kv_layer = (size_t)B * Hk * c->n_ctx * hd;
     const size_t ckv_layer = (size_t)B * Hk * C * hd;
     __half* kc = (__half*)P.take(2 * kv_layer * c->n_layer);
@@ -256,21 +267,19 @@ size_t talker_plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     __half* cvc = (__half*)P.take(2 * ckv_layer * c->cp_n_layer);
     if (m && base) {
         m->pos = pos; m->dbg_pos = pos + 1; m->tok = tok; m->hist = hist; m->ctl = ctl;
-        m->x = x; m->xc = xc; m->mmp = mmp; m->qkv = q; m->h = h; m->logits = logits; m->part = part;
-        m->act.hi = hi; m->act.lo = lo; m->act.gsum = gsum;
+        m->x = x; m->xc = xc; m->qkv = q; m->h = h; m->logits = logits; m->part = part;
+        m->act.hi = hi; m->act.lo = lo;
         m->rope = rope; m->rope_rows = rope_rows;
         for (int k = 0; k < C; ++k) {
             m->emb[k] = emb[k];
             m->emb_rows[k] = k == 0 ? V : Vc;
         }
-        m->L = Lt; m->nfg = nfg; m->head = head;
+        m->Lt = Lt; m->nfg = nfg; m->t_head = head;
         m->Lc = Lc; m->cp_nfg = cp_nfg;
         for (int k = 0; k < 16; ++k) m->cp_head[k] = cp_head[k];
         m->kc = kc; m->vc = vc; m->kv_layer_elems = kv_layer;
         m->ckc = ckc; m->cvc = cvc; m->ckv_layer_elems = ckv_layer;
         m->tpp = C; m->vmax = vmax; m->qkv_rows = qd + 2 * kd;
-        m->split_o = splits_for(d, qd);
-        m->split_down = splits_for(d, ff);
     }
     return align256(P.off);
 }
@@ -278,18 +287,18 @@ size_t talker_plan(tsd_model* m, const tsd_config* c, uint8_t* base)
 tsd_status talker_pack(tsd_model* m, const tsd_tensor* w)
 {
     const tsd_config& c = m->c;
-    const int d = c.d_model, H = c.n_head, Hk = c.n_kv_head, hd = c.head_dim, ff = c.d_ff, f = c.wfmt, C = c.n_codebooks;
+    const int d = c.d_model, H = c.n_head, Hk = c.n_kv_head, hd = c.head_dim, ff = c.d_ff, C = c.n_codebooks;
     hipStream_t st = m->st;
     int i = 0;
     auto cp = [&](const void* dst, int idx) {
         return hipMemcpyAsync((void*)dst, w[idx].ptr, w[idx].bytes, hipMemcpyDeviceToDevice, st);
     };
-    auto pk = [&](const PackedMat& dst, int idx, int N, int K, int row0, int mode) {
-        return launch_pack(f, w[idx].ptr, N, K, (void*)dst.q, dst.N, row0, mode, hd, st);
+    auto pk = [&](const TiledMat& dst, int idx, int N, int K, int row0, int mode) {
+        return launch_pack_tiled(w[idx].ptr, N, K, (void*)dst.q, dst.N, row0, mode, hd, st);
     };
     for (int k = 0; k < C; ++k) HIP_TRY(m, cp(m->emb[k], i++), "copy embedding");
-    auto layers = [&](std::vector<LayerW>& Ls) -> tsd_status {
-        for (LayerW& L : Ls) {
+    auto layers = [&](std::vector<TLayerW>& Ls) -> tsd_status {
+        for (TLayerW& L : Ls) {
             HIP_TRY(m, cp(L.n1g, i++), "copy");
             HIP_TRY(m, pk(L.qkv, i++, H * hd, d, 0, PACK_ROPE_PAIRS), "pack q");
             HIP_TRY(m, pk(L.qkv, i++, Hk * hd, d, H * hd, PACK_ROPE_PAIRS), "pack k");
@@ -302,10 +311,10 @@ tsd_status talker_pack(tsd_model* m, const tsd_tensor* w)
         }
         return TSD_OK;
     };
-    tsd_status s = layers(m->L);
+    tsd_status s = layers(m->Lt);
     if (s != TSD_OK) return s;
     HIP_TRY(m, cp(m->nfg, i++), "copy");
-    HIP_TRY(m, pk(m->head, i++, c.vocab, d, 0, PACK_IDENTITY), "pack head");
+    HIP_TRY(m, pk(m->t_head, i++, c.vocab, d, 0, PACK_IDENTITY), "pack head");
     s = layers(m->Lc);
     if (s != TSD_OK) return s;
     HIP_TRY(m, cp(m->cp_nfg, i++), "copy");
@@ -314,7 +323,6 @@ tsd_status talker_pack(tsd_model* m, const tsd_tensor* w)
     const int kmax = std::max(d, std::max(H * hd, ff));
     HIP_TRY(m, launch_fill_u32((unsigned*)m->act.hi, 0u, MM_ROWS * kmax / 2, st), "init");
     HIP_TRY(m, launch_fill_u32((unsigned*)m->act.lo, 0u, MM_ROWS * kmax / 2, st), "init");
-    HIP_TRY(m, launch_fill_f32(m->act.gsum, 0.f, (size_t)MM_ROWS * (kmax / 64), st), "init");
     HIP_TRY(m, launch_fill_f32(m->x, 0.f, (size_t)MM_ROWS * d, st), "init");
     HIP_TRY(m, launch_fill_f32(m->xc, 0.f, (size_t)MM_ROWS * d, st), "init");
     return TSD_OK;
@@ -330,25 +338,19 @@ hipError_t talker_enqueue(tsd_model* m, hipStream_t st, bool with_cp, Probe* pr)
         T.rows[k] = m->emb_rows[k];
     }
     TRY(launch_embed_sum16(T, m->tok, C, C, d, m->x, B, st));
-    int np = 0;
     for (int l = 0; l < c.n_layer; ++l)
-        TRY(layer16(m, m->L[l], m->x, np, m->kc + m->kv_layer_elems * l, m->vc + m->kv_layer_elems * l, c.n_ctx, m->pos, 0,
-                    st, pr, &np));
+        TRY(layer16(m, m->Lt[l], m->x, m->kc + m->kv_layer_elems * l, m->vc + m->kv_layer_elems * l, c.n_ctx, m->pos, 0,
+                    st, pr));
     if (!with_cp) return launch_frame_done(m->tok, 0, m->hist, m->pos, st);   // advance the position only
     // code 0; the Talker's final-normed hidden state is the predictor's position 0
-    TRY(head16(m, st, pr, m->x, np, m->nfg, m->head, 0, c.vocab, m->xc));
+    TRY(head16(m, st, pr, m->x, m->nfg, m->t_head, 0, c.vocab, m->xc));
     for (int cpos = 0; cpos < C; ++cpos) {
-        if (cpos > 0) {
-            EmbedTabs E{};
-            E.tab[0] = m->emb[cpos - 1];
-            E.rows[0] = m->emb_rows[cpos - 1];
-            TRY(launch_embed_sum16(E, m->tok + (cpos - 1), C, 1, d, m->xc, B, st));
-        }
-        np = 0;
+        Gather g{};
+        if (cpos > 0) g = Gather{m->emb[cpos - 1], m->emb_rows[cpos - 1], m->tok + (cpos - 1)};
         for (int l = 0; l < c.cp_n_layer; ++l)
-            TRY(layer16(m, m->Lc[l], m->xc, np, m->ckc + m->ckv_layer_elems * l, m->cvc + m->ckv_layer_elems * l, C,
-                        nullptr, cpos, st, pr, &np));
-        if (cpos > 0) TRY(head16(m, st, pr, m->xc, np, m->cp_nfg, m->cp_head[cpos], cpos, c.cp_vocab, nullptr));
+            TRY(layer16(m, m->Lc[l], m->xc, m->ckc + m->ckv_layer_elems * l, m->cvc + m->ckv_layer_elems * l, C,
+                        nullptr, cpos, st, pr, (cpos > 0 && l == 0) ? &g : nullptr));
+        if (cpos > 0) TRY(head16(m, st, pr, m->xc, m->cp_nfg, m->cp_head[cpos], cpos, c.cp_vocab, nullptr));
     }
     return launch_frame_done(m->tok, B * C, m->hist, m->pos, st);
 }
@@ -356,10 +358,8 @@ hipError_t talker_enqueue(tsd_model* m, hipStream_t st, bool with_cp, Probe* pr)
 hipError_t talker_layer(tsd_model* m, int l, hipStream_t st, const int* pos)
 {
     const tsd_config& c = m->c;
-    int np = 0;
-    TRY(layer16(m, m->L[l], m->x, 0, m->kc + m->kv_layer_elems * l, m->vc + m->kv_layer_elems * l, c.n_ctx, pos, 0, st,
-                nullptr, &np));
-    return prep(m, st, m->x, c.d_model, np, nullptr, c.d_model, nullptr);   // the pending partials into x
+    return layer16(m, m->Lt[l], m->x, m->kc + m->kv_layer_elems * l, m->vc + m->kv_layer_elems * l, c.n_ctx, pos, 0, st,
+                   nullptr);
 }
 
 void talker_kind_launches(const tsd_model* m, int* out)

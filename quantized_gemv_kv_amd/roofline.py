@@ -127,5 +127,39 @@ def kernel_bytes(c, kind: str, pos: int) -> int:
     raise KeyError(kind)
 
 
+def frame_kernel_bytes(c, kind: str, pos: int) -> float:
+    """Mean algorithmic bytes of one launch of a kind in the batched Talker + predictor frame
+    at Talker position pos: the matrix in its stored format (the same for Talker and predictor
+    layers, which share their widths), the fp16 hi/lo operand of all 16 GEMM rows and its group
+    sums, and what the epilogue writes for the batch rows; attention: the fp16 keys and values
+    each launch reads (the Talker's 0..pos, the predictor's 0..cpos) averaged over the frame's
+    launches, plus queries and partials."""
+    d, f, H, Hk, hd, ff, B = (c[k] for k in ("d_model", "wfmt", "n_head", "n_kv_head", "head_dim", "d_ff", "batch"))
+    C, L, Lc = c["n_codebooks"], c["n_layer"], c["cp_n_layer"]
+    qd, kd, rows = H * hd, Hk * hd, 16
+
+    def operand(K):
+        return rows * K * 4 + rows * (K // 64) * 4
+
+    if kind == "qkv":
+        return matrix_bytes(f, qd + 2 * kd, d) + operand(d) + B * (qd * 4 + 2 * kd * 2)
+    if kind == "oproj":
+        return matrix_bytes(f, d, qd) + operand(qd) + B * d * 4 * 4      # up to four K slices
+    if kind == "fc":
+        return matrix_bytes(f, 2 * ff, d) + operand(d) + B * ff * 4
+    if kind == "down":
+        return matrix_bytes(f, d, ff) + operand(ff) + B * d * 4 * 4
+    if kind == "head":
+        mats = matrix_bytes(f, c["vocab"], d) + (C - 1) * matrix_bytes(f, c["cp_vocab"], d)
+        return mats / C + operand(d) + B * 4 * (c["vocab"] + (C - 1) * c["cp_vocab"]) / C
+    if kind == "attn":
+        keys = L * (pos + 1) + Lc * sum(j + 1 for j in range(C))
+        n_launch = L + Lc * C
+        return (B * keys * 2 * kd * 2 + n_launch * B * (qd * 4 + H * 2 * (hd + 4) * 4)) / n_launch
+    raise KeyError(kind)
+
+
 def mean_kernel_bytes(c, kind: str, first_pos: int, n_steps: int) -> float:
+    if c["arch"] == "talker_cp":
+        return sum(frame_kernel_bytes(c, kind, p) for p in range(first_pos, first_pos + n_steps)) / n_steps
     return sum(kernel_bytes(c, kind, p) for p in range(first_pos, first_pos + n_steps)) / n_steps

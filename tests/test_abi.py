@@ -52,4 +52,4 @@ def test_talker_workspace_and_validation():
         with pytest.raises(binding.TsdError) as e:
             binding.tsd_workspace_bytes(bad)
         assert e.value.status == status, bad
-    assert binding.tsd_gemm_rows_scratch_bytes(1024, 3072, 4) >= 2 * 16 * 3072 * 2 + 4 * 16 * 1024 * 4
+    assert binding.tsd_gemm_rows_scratch_bytes(1024, 3072, 4) >= 4 * 16 * 1024 * 4      # the split-K slices

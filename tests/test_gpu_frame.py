@@ -70,8 +70,8 @@ def test_gemm_rows_matches_oracle(N, K, B, splits):
     x[:, : K // 8] *= 30.0          # a wide range of magnitudes inside each row
     x[:, K // 8: K // 4] *= 1e-3
     ref = oracle.gemv_f32("aff8", blob, N, K, x, None)
-    packed = torch.empty(tb.tsd_gemv_packed_bytes("aff8", N, K), dtype=torch.uint8, device="cuda")
-    tb.tsd_gemv_pack("aff8", dev(blob), N, K, packed)
+    packed = torch.empty(tb.tsd_gemm_rows_packed_bytes(N, K), dtype=torch.uint8, device="cuda")
+    tb.tsd_gemm_rows_pack(dev(blob), N, K, packed)
     scratch = torch.empty(tb.tsd_gemm_rows_scratch_bytes(N, K, splits), dtype=torch.uint8, device="cuda")
     scratch.fill_(0xFF)             # NaN patterns: rows past B must not leak into the result
     y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
@@ -100,6 +100,8 @@ def test_gemm_rows_rejects_bad_arguments():
         tb.tsd_gemm_rows(p, 64, 128, 17, x, x, 1, s)     # more than 16 rows
     with pytest.raises(tb.TsdError):
         tb.tsd_gemm_rows(p, 64, 128, 2, x, x, 1, s[:100])  # scratch too small
+    with pytest.raises(tb.TsdError):
+        tb.tsd_gemm_rows_pack(p, 64, 128, p)                # canonical size mismatch
 
 
 # ---- the frame ---------------------------------------------------------------------------------

@@ -20,14 +20,17 @@
 // group.  Within a group, lane group j = l / 16 supplies K positions 16 j .. 16 j + 15 to two
 // MFMAs (the same K permutation on both operands), i.e. one 16-byte load of weights per lane.
 //
-// The operand is either ready (fp16 hi/lo, written by the attention or by the SwiGLU epilogue)
-// or the fp32 residual stream itself: the GEMM then gathers, scales by the norm gain and splits
-// the rows in registers, sums their squares across the workgroup and applies the RMSNorm's
-// 1 / rms to its results, so that no separate normalisation kernel runs between layers.
+// Every operand is produced ready by the kernel before: the attention (or its merge) and the
+// SwiGLU epilogue write fp16 hi/lo rows; the epilogue that adds a projection into the residual
+// stream also writes the next norm's input, hi/lo of x * g, and per 16-column tile the rows'
+// partial sums of x^2.  The GEMM that consumes a norm's input sums those partials in a fixed
+// order and applies the RMSNorm's 1 / rms to its results, so no normalisation kernel runs
+// between layers and the residual stream is never re-read to build an operand.
 #include <math.h>
 
 #include "gemv_core.h"
 #include "kernels.h"
+#include "sampler.h"
 
 namespace tsd {
 namespace {
@@ -43,6 +46,16 @@ __device__ __forceinline__ void put_hilo(const Act16& a, size_t idx, float y)
     const _Float16 h = (_Float16)y;
     ((TSD_GLOBAL _Float16*)a.hi)[idx] = h;
     ((TSD_GLOBAL _Float16*)a.lo)[idx] = (_Float16)(y - (float)h);
+}
+
+// sum over the 256 threads of a workgroup in a fixed order; every thread gets it
+__device__ __forceinline__ float block_sum256(float v, float* red)
+{
+    v = wave_sum(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return ((red[0] + red[1]) + red[2]) + red[3];
 }
 
 // ---- attention partials merged into the operand of the output projection -------------------
@@ -90,21 +103,39 @@ __device__ __forceinline__ half8 q8_to_half8(uint32_t w0, uint32_t w1)
     return __builtin_bit_cast(half8, u) - (_Float16)1152.0f;   // q - 128, exact
 }
 
-// fp32 values -> fp16 hi, lo
-__device__ __forceinline__ void split8(const float (&v)[8], half8& h, half8& l)
+// what an epilogue reads besides the results, loaded before the main loop so that its latency
+// hides behind the weight stream: the residual values it adds to and the next norm's gain
+// (RESID), the position and the lane's rotation (QKV_ROPE)
+struct Pre {
+    float xo[4];
+    float gn;
+    float2 cs;
+};
+
+template <int EPI>
+__device__ __forceinline__ void prefetch(const Mm16Out& o, int tile, int N, int j, int c16, int pos, Pre& p)
 {
+    const int n = tile * 16 + c16;
+    if constexpr (EPI == MM_RESID) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const _Float16 t = (_Float16)v[e];
-        h[e] = t;
-        l[e] = (_Float16)(v[e] - (float)t);
+        for (int i = 0; i < 4; ++i) p.xo[i] = (4 * j + i < o.rows && n < N) ? glb(o.y)[il_x(4 * j + i, n)] : 0.f;
+        p.gn = (o.next.hi && n < N) ? glb(o.g_next)[n] : 0.f;
+    } else if constexpr (EPI == MM_QKV_ROPE) {
+        p.cs = make_float2(1.f, 0.f);
+        if (n < o.qrows + o.krows && (c16 & 1) == 0) {
+            const int half = o.hd >> 1;
+            const int m = (n >= o.qrows ? n - o.qrows : n) >> 1;
+            p.cs = o.rope[(size_t)pos * half + (m - (m / half) * half)];
+        }
     }
 }
 
-// lane (j, c16) holds Y[4 j + i][n] for i < 4
+// lane (j, c16) holds Y[4 j + i][n] for i < 4; tile = the 16-row tile of W
 template <int EPI>
-__device__ __forceinline__ void epilogue(const Mm16Out& o, int n, int N, int j, int c16, int sl, const float4v& acc)
+__device__ __forceinline__ void epilogue(const Mm16Out& o, int tile, int N, int j, int c16, int sl, int pos,
+                                         const Pre& pre, const float4v& acc)
 {
+    const int n = tile * 16 + c16;
     if constexpr (EPI == MM_STORE) {
         TSD_GLOBAL float* y = glb(o.y) + sl * o.slice;
 #pragma unroll
@@ -112,21 +143,28 @@ __device__ __forceinline__ void epilogue(const Mm16Out& o, int n, int N, int j, 
             if (4 * j + i < o.rows && n < N) y[(size_t)(4 * j + i) * o.ldy + n] = acc[i];
     } else if constexpr (EPI == MM_RESID) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (4 * j + i < o.rows && n < N) {
-                TSD_GLOBAL float* y = glb(o.y) + il_x(4 * j + i, n);
-                *y = *y + acc[i];
+        for (int i = 0; i < 4; ++i) {
+            const int b = 4 * j + i;
+            float sq = 0.f;
+            if (b < o.rows && n < N) {
+                const float v = pre.xo[i] + acc[i];
+                glb(o.y)[il_x(b, n)] = v;
+                if (o.next.hi) put_hilo(o.next, il_act(b, n), v * pre.gn);
+                sq = v * v;
             }
+            if (o.ssq_out) {   // the tile's part of the row's sum of squares (same order every time)
+                sq = group_sum(sq, 16);
+                if (c16 == 0 && b < o.rows) glb(o.ssq_out)[(size_t)tile * MM_ROWS + b] = sq;
+            }
+        }
     } else if constexpr (EPI == MM_SWIGLU) {
         // rows (2m, 2m+1) = (gate_m, up_m): the up value sits in the neighbouring lane
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float up = __shfl_xor(acc[i], 1, 64);
-            if ((c16 & 1) == 0 && 4 * j + i < o.rows && n < N)
-                put_hilo(o.act, il_act(4 * j + i, n >> 1), silu(acc[i]) * up);
+            if ((c16 & 1) == 0 && 4 * j + i < o.rows && n < N) put_hilo(o.act, il_act(4 * j + i, n >> 1), silu(acc[i]) * up);
         }
     } else {
-        const int pos = o.posp ? ld_uniform(o.posp) : o.pos_value;
         const int half = o.hd >> 1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -138,7 +176,7 @@ __device__ __forceinline__ void epilogue(const Mm16Out& o, int n, int N, int j, 
                 const bool isk = n >= o.qrows;
                 const int m = (isk ? n - o.qrows : n) >> 1;
                 const int h = m / half, e = m - h * half;
-                const float2 cs = o.rope[(size_t)pos * half + e];
+                const float2 cs = pre.cs;
                 const float ra = acc[i] * cs.x - partner * cs.y, rb = acc[i] * cs.y + partner * cs.x;
                 if (!isk) {
                     TSD_GLOBAL float* qr = glb(o.q) + (size_t)b * o.qrows + h * o.hd;
@@ -163,17 +201,15 @@ __device__ __forceinline__ void epilogue(const Mm16Out& o, int n, int N, int j, 
 // of the slice's groups: per chunk of U groups it issues every load first (weights of the T
 // tiles, then its operand fragment, which serves all T tiles), then converts and runs the MFMAs;
 // the waves add their results in LDS and wave 0 runs the epilogue.
-template <int EPI, int PRO, int T, int NW, int U>
+template <int EPI, int T, int NW, int U>
 __global__ __launch_bounds__(64 * NW) void k_mm16(const TiledMat W, const MmIn in, const Mm16Out o)
 {
-    constexpr bool PX = PRO == MP_X;
     const int K = W.K, G = K >> 6, N = W.N, tiles = (N + 15) >> 4;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane >> 4, c16 = lane & 15;
     const int S = gridDim.y, sl = blockIdx.y;
     const int g_lo = (int)((long long)G * sl / S), g_hi = (int)((long long)G * (sl + 1) / S);
     const int cnt = g_hi - g_lo, q = cnt / NW, r = cnt - q * NW;
     const int w_lo = g_lo + wave * q + (wave < r ? wave : r), w_n = q + (wave < r ? 1 : 0);
-    const bool lead = blockIdx.x == 0 && blockIdx.y == 0;
 
     const TSD_GLOBAL u32x4* wr[T];
     const TSD_GLOBAL uint32_t* sbr[T];
@@ -184,23 +220,22 @@ __global__ __launch_bounds__(64 * NW) void k_mm16(const TiledMat W, const MmIn i
         wr[t] = (const TSD_GLOBAL u32x4*)glb(W.q) + (size_t)tile * G * 64 + lane;
         sbr[t] = glb(W.sb) + (size_t)tile * G * 16 + c16;
     }
-    // this lane's operand row c16
-    const TSD_GLOBAL float4v* x4 = nullptr;   // il_x rows
-    const TSD_GLOBAL float* tr = nullptr;     // gathered row-major embedding row
-    bool rv = true;
-    if constexpr (PX) {
-        if (in.tab) {
-            rv = c16 < in.rows;
-            int id = rv ? in.codes[(size_t)c16 * in.ld_codes] : 0;
-            id = id < 0 ? 0 : (id >= in.tab_rows ? in.tab_rows - 1 : id);
-            tr = glb(in.tab) + (size_t)id * K + 8 * j;
-        } else {
-            x4 = (const TSD_GLOBAL float4v*)glb(in.x) + 2 * j * MM_ROWS + c16;
-        }
-    }
     const TSD_GLOBAL half8* ah = (const TSD_GLOBAL half8*)glb(in.a.hi) + j * MM_ROWS + c16;
     const TSD_GLOBAL half8* al = (const TSD_GLOBAL half8*)glb(in.a.lo) + j * MM_ROWS + c16;
-    const TSD_GLOBAL float4v* g4 = in.g ? (const TSD_GLOBAL float4v*)(glb(in.g) + 8 * j) : nullptr;
+    // a norm's operand: the rows' partial sums of squares, loaded now, summed after the main loop
+    const bool norm = in.ssq != nullptr;
+    const int sb_row = threadIdx.x & 15, sb_part = threadIdx.x >> 4;   // 16 parts of 16 threads
+    float sp[4] = {0.f, 0.f, 0.f, 0.f};
+    if (norm && threadIdx.x < 256)
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            if (sb_part + 16 * p < in.n_ssq) sp[p] = glb(in.ssq)[(size_t)(sb_part + 16 * p) * MM_ROWS + sb_row];
+    // the epilogue's own inputs (wave 0 runs it)
+    const int pos = EPI == MM_QKV_ROPE ? (o.posp ? ld_uniform(o.posp) : o.pos_value) : 0;
+    Pre pre[T];
+    if (wave == 0)
+#pragma unroll
+        for (int t = 0; t < T; ++t) prefetch<EPI>(o, blockIdx.x * T + t, N, j, c16, pos, pre[t]);
     half8 ones;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
@@ -208,12 +243,10 @@ __global__ __launch_bounds__(64 * NW) void k_mm16(const TiledMat W, const MmIn i
     float4v acc[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = (float4v){0.f, 0.f, 0.f, 0.f};
-    float ss = 0.f;   // sum of squares of this lane's x (row c16)
     for (int c = 0; c < w_n; c += U) {
         u32x4 wq[T][U];
         uint32_t sb[T][U];
         half8 h0[U], h1[U], l0[U], l1[U];
-        float4v xv[PX ? U : 1][4], gv[PX ? U : 1][4];
 #pragma unroll
         for (int u = 0; u < U; ++u) {   // clamped to the wave's last group, masked below
             const int grp = w_lo + (c + u < w_n ? c + u : w_n - 1);
@@ -225,38 +258,12 @@ __global__ __launch_bounds__(64 * NW) void k_mm16(const TiledMat W, const MmIn i
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            // K offsets 8j .. 8j+7 (first MFMA) and 32 + 8j .. (second) of the group
             const int grp = w_lo + (c + u < w_n ? c + u : w_n - 1);
-            if constexpr (PX) {
-                // K offsets 8j .. 8j+7 (first MFMA) and 32 + 8j .. (second) of the group
-                if (in.tab) {
-                    const TSD_GLOBAL float4v* p = (const TSD_GLOBAL float4v*)(tr + grp * 64);
-                    const float4v z = {0.f, 0.f, 0.f, 0.f};
-                    xv[u][0] = rv ? p[0] : z;
-                    xv[u][1] = rv ? p[1] : z;
-                    xv[u][2] = rv ? p[8] : z;
-                    xv[u][3] = rv ? p[9] : z;
-                } else {
-                    const int q4 = grp * 16 * MM_ROWS;   // float4 index of the group's first quad of rows
-                    xv[u][0] = x4[q4];
-                    xv[u][1] = x4[q4 + MM_ROWS];
-                    xv[u][2] = x4[q4 + 8 * MM_ROWS];
-                    xv[u][3] = x4[q4 + 9 * MM_ROWS];
-                }
-                if (g4) {
-                    gv[u][0] = g4[grp * 16];
-                    gv[u][1] = g4[grp * 16 + 1];
-                    gv[u][2] = g4[grp * 16 + 8];
-                    gv[u][3] = g4[grp * 16 + 9];
-                } else {
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) gv[u][p] = (float4v){1.f, 1.f, 1.f, 1.f};
-                }
-            } else {
-                h0[u] = ah[grp * 8 * MM_ROWS];
-                h1[u] = ah[(grp * 8 + 4) * MM_ROWS];
-                l0[u] = al[grp * 8 * MM_ROWS];
-                l1[u] = al[(grp * 8 + 4) * MM_ROWS];
-            }
+            h0[u] = ah[grp * 8 * MM_ROWS];
+            h1[u] = ah[(grp * 8 + 4) * MM_ROWS];
+            l0[u] = al[grp * 8 * MM_ROWS];
+            l1[u] = al[(grp * 8 + 4) * MM_ROWS];
         }
         // every load of the chunk is in flight before the first use
         asm volatile("" ::: "memory");
@@ -264,29 +271,6 @@ __global__ __launch_bounds__(64 * NW) void k_mm16(const TiledMat W, const MmIn i
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const bool valid = c + u < w_n;
-            if constexpr (PX) {
-                float v0[8], v1[8];
-#pragma unroll
-                for (int p = 0; p < 4; ++p)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float xe = xv[u][p][e];
-                        ss = fmaf(valid ? xe : 0.f, xe, ss);
-                        const float ye = xe * gv[u][p][e];
-                        if (p < 2) v0[4 * p + e] = ye;
-                        else v1[4 * (p - 2) + e] = ye;
-                    }
-                if (lead && in.x_out && in.tab && rv && valid) {   // the gathered rows, for later residual adds
-                    TSD_GLOBAL float4v* xo = (TSD_GLOBAL float4v*)glb(in.x_out) + 2 * j * MM_ROWS + c16 +
-                                             (w_lo + c + u) * 16 * MM_ROWS;
-                    xo[0] = xv[u][0];
-                    xo[MM_ROWS] = xv[u][1];
-                    xo[8 * MM_ROWS] = xv[u][2];
-                    xo[9 * MM_ROWS] = xv[u][3];
-                }
-                split8(v0, h0[u], l0[u]);
-                split8(v1, h1[u], l1[u]);
-            }
             // X: the group sums of the operand rows, from the same fragments
             float4v xz = {0.f, 0.f, 0.f, 0.f};
             xz = __builtin_amdgcn_mfma_f32_16x16x32_f16(h0[u], ones, xz, 0, 0, 0);
@@ -312,34 +296,28 @@ __global__ __launch_bounds__(64 * NW) void k_mm16(const TiledMat W, const MmIn i
     }
 
     __shared__ float4v red[NW - 1][T][64];
-    __shared__ float ssw[NW][16];
+    __shared__ float ssp[16][16];
     __shared__ float rrow[16];
     if (wave > 0)
 #pragma unroll
         for (int t = 0; t < T; ++t) red[wave - 1][t][lane] = acc[t];
-    const bool norm = PX && in.norm;
-    if (norm) {
-        ss += __shfl_xor(ss, 16, 64);
-        ss += __shfl_xor(ss, 32, 64);
-        if (j == 0) ssw[wave][c16] = ss;
+    if (norm && threadIdx.x < 256) {
+        float v = ((sp[0] + sp[1]) + sp[2]) + sp[3];
+        for (int p = sb_part + 64; p < in.n_ssq; p += 16) v += glb(in.ssq)[(size_t)p * MM_ROWS + sb_row];
+        ssp[sb_part][sb_row] = v;
     }
     __syncthreads();
+    if (wave != 0) return;
     if (norm) {
-        if (threadIdx.x < 16) {
+        if (lane < 16) {
             float tsum = 0.f;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) tsum += ssw[w][threadIdx.x];
-            rrow[threadIdx.x] = 1.0f / sqrtf(tsum / (float)K + in.eps);
+            for (int p = 0; p < 16; ++p) tsum += ssp[p][lane];
+            rrow[lane] = 1.0f / sqrtf(tsum / (float)K + in.eps);
         }
-        __syncthreads();
-        if (lead && in.norm_out) {   // RMSNorm(x) * g of every row, for a consumer of the normed state
-            for (int idx = threadIdx.x; idx < MM_ROWS * K; idx += 64 * NW) {
-                const int b = (idx >> 2) & (MM_ROWS - 1), k = (idx >> 6) * 4 + (idx & 3);
-                if (b < in.rows) glb(in.norm_out)[idx] = glb(in.x)[idx] * (in.g ? glb(in.g)[k] : 1.f) * rrow[b];
-            }
-        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // this wave's LDS writes (lgkmcnt 0) before reading rrow
+        __builtin_amdgcn_wave_barrier();
     }
-    if (wave != 0) return;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
 #pragma unroll
@@ -353,7 +331,7 @@ __global__ __launch_bounds__(64 * NW) void k_mm16(const TiledMat W, const MmIn i
         if (norm)
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[t][i] *= rrow[4 * j + i];
-        epilogue<EPI>(o, (blockIdx.x * T + t) * 16 + c16, N, j, c16, sl, acc[t]);
+        epilogue<EPI>(o, blockIdx.x * T + t, N, j, c16, sl, pos, pre[t], acc[t]);
     }
 }
 
@@ -378,57 +356,121 @@ __global__ void k_pack_tiled(const uint8_t* __restrict__ src, int N, int K, uint
     dsb[((size_t)t * G + g) * 16 + c] = (uint32_t)(s[0] | (s[1] << 8)) | ((uint32_t)(b[0] | (b[1] << 8)) << 16);
 }
 
-// ---- embeddings ----------------------------------------------------------------------------
-__global__ void k_embed_sum16(const EmbedTabs T, const int* __restrict__ codes, int ld_codes, int n_tab, int d,
-                              float* __restrict__ x)
+// ---- a norm's input, one row per 256-thread workgroup ------------------------------------------
+constexpr int RP = MM_MAX_K / 256;   // elements per thread
+
+// id0 >= 0: the id of table 0 (ROW_EMB), else read from codes.  Rows b >= B write zeros.
+// red: 4 floats of LDS; ids: 16 ints of LDS
+__device__ void row_prep(const RowPrep& p, int b, int id0, float* red, int* ids)
 {
-    const int b = blockIdx.y, k = blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= d) return;
-    float s = 0.f;
-    for (int c = 0; c < n_tab; ++c) {
-        int id = codes[(size_t)b * ld_codes + c];
-        id = id < 0 ? 0 : (id >= T.rows[c] ? T.rows[c] - 1 : id);
-        s += T.tab[c][(size_t)id * d + k];
+    const int t = threadIdx.x, K = p.K;
+    const bool live = b < p.B;
+    float v[RP];
+#pragma unroll
+    for (int i = 0; i < RP; ++i) v[i] = 0.f;
+    if (p.src == ROW_EMB) {   // uniform over the workgroup
+        if (live && t < p.n_tab) {
+            const int id = (t == 0 && id0 >= 0) ? id0 : p.codes[(size_t)b * p.ld_codes + t];
+            ids[t] = id < 0 ? 0 : (id >= p.tab_rows[t] ? p.tab_rows[t] - 1 : id);
+        }
+        __syncthreads();
     }
-    x[il_x(b, k)] = s;
+    if (live) {
+        if (p.src == ROW_EMB) {
+#pragma unroll
+            for (int i = 0; i < RP; ++i) {
+                const int k = t + 256 * i;
+                if (k < K) {
+                    float s = 0.f;
+                    for (int c = 0; c < p.n_tab; ++c) s += glb(p.tab[c])[(size_t)ids[c] * K + k];
+                    v[i] = s;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < RP; ++i) {
+                const int k = t + 256 * i;
+                if (k < K) v[i] = p.src == ROW_MAJOR ? glb(p.rows_src)[(size_t)b * K + k] : glb(p.rows_src)[il_x(b, k)];
+            }
+        }
+    }
+    if (p.src == ROW_NORMED) {   // uniform over the workgroup
+        float q2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < RP; ++i) q2 = fmaf(v[i], v[i], q2);
+        const float r = 1.0f / sqrtf(block_sum256(q2, red) / (float)K + p.eps);
+#pragma unroll
+        for (int i = 0; i < RP; ++i) {
+            const int k = t + 256 * i;
+            if (k < K) v[i] *= glb(p.g_src)[k] * r;
+        }
+    }
+    float q2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < RP; ++i) {
+        const int k = t + 256 * i;
+        if (k >= K) continue;
+        if (p.x && live) glb(p.x)[il_x(b, k)] = v[i];
+        put_hilo(p.act, il_act(b, k), p.g ? v[i] * glb(p.g)[k] : v[i]);
+        q2 = fmaf(v[i], v[i], q2);
+    }
+    if (p.ssq) {
+        q2 = block_sum256(q2, red);
+        if (t == 0 && live) glb(p.ssq)[b] = q2;
+    }
 }
 
-// row-major rows <-> the il_x layout
-__global__ void k_rows_to_il(const float* __restrict__ src, int B, int K, float* __restrict__ dst)
+__global__ __launch_bounds__(256) void k_row_prep(const RowPrep p)
 {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= MM_ROWS * K) return;
-    const int b = i / K, k = i - b * K;
-    dst[il_x(b, k)] = b < B ? src[i] : 0.f;
+    __shared__ float red[4];
+    __shared__ int ids[16];
+    row_prep(p, blockIdx.x, -1, red, ids);
 }
+
+// ---- the code of every row, then that row's next input ----------------------------------------
+__global__ __launch_bounds__(256) void k_pick(const PickArgs a)
+{
+    extern __shared__ uint32_t keys[];   // top-k only: the row's logits as ordered keys
+    __shared__ samp::Scratch S;
+    __shared__ unsigned long long bk[4];
+    __shared__ float red[4];
+    __shared__ int ids[16];
+    __shared__ int picked;
+    const int b = blockIdx.x, t = threadIdx.x;
+    const float* l = a.logits + (size_t)b * a.ld_l;
+    if (a.top_k > 0) {
+        for (int i = t; i < a.n; i += 256) keys[i] = float_order_key(l[i]);
+        __syncthreads();
+        const float u = samp::uniform24(a.seed, (uint32_t)b, (uint32_t)*a.posp, (uint32_t)a.pass);
+        const int id = samp::topk_draw<256>(keys, a.n, a.top_k, a.temperature, u, S);
+        if (t == 0) picked = id;
+    } else {
+        unsigned long long best = 0ull;
+        for (int i = t; i < a.n; i += 256) {
+            const unsigned long long key = ((unsigned long long)float_order_key(l[i]) << 32) | (0xFFFFFFFFu - (uint32_t)i);
+            best = key > best ? key : best;
+        }
+        best = wave_max_u64(best);
+        if ((t & 63) == 0) bk[t >> 6] = best;
+        __syncthreads();
+        if (t == 0) {
+            unsigned long long m = bk[0];
+            for (int i = 1; i < 4; ++i) m = bk[i] > m ? bk[i] : m;
+            picked = (int)(0xFFFFFFFFu - (uint32_t)m);
+        }
+    }
+    __syncthreads();
+    const int id = picked;
+    if (t == 0) a.code[(size_t)b * a.ld_code] = id;
+    if (a.prep.src >= 0) row_prep(a.prep, b, id, red, ids);
+}
+
 __global__ void k_il_to_rows(const float* __restrict__ src, int B, int K, float* __restrict__ dst)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= B * K) return;
     const int b = i / K, k = i - b * K;
     dst[i] = src[il_x(b, k)];
-}
-
-// ---- per-row greedy pick ---------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_argmax_rows(const float* __restrict__ logits, int ld_l, int n, int* code,
-                                                     int ld_code)
-{
-    const int b = blockIdx.x, t = threadIdx.x;
-    const float* l = logits + (size_t)b * ld_l;
-    unsigned long long best = 0ull;
-    for (int i = t; i < n; i += 256) {
-        const unsigned long long key = ((unsigned long long)float_order_key(l[i]) << 32) | (0xFFFFFFFFu - (uint32_t)i);
-        best = key > best ? key : best;
-    }
-    best = wave_max_u64(best);
-    __shared__ unsigned long long bk[4];
-    if ((t & 63) == 0) bk[t >> 6] = best;
-    __syncthreads();
-    if (t == 0) {
-        unsigned long long m = bk[0];
-        for (int i = 1; i < 4; ++i) m = bk[i] > m ? bk[i] : m;
-        code[(size_t)b * ld_code] = (int)(0xFFFFFFFFu - (uint32_t)m);
-    }
 }
 
 // y[b][n] = sum over s of part[s][b][n] (the standalone GEMM's split-K slices)
@@ -450,56 +492,45 @@ __global__ void k_frame_done(const int* __restrict__ codes, int n, int* hist, in
     if (threadIdx.x == 0) *pos = p + 1;
 }
 
-template <int EPI, int PRO, int T, int NW, int U>
+template <int EPI, int T, int NW, int U>
 hipError_t go(const TiledMat& W, const MmIn& in, int splits, const Mm16Out& o, hipStream_t st)
 {
     const int tiles = (W.N + 15) / 16;
     const dim3 grid((tiles + T - 1) / T, splits);
-    hipLaunchKernelGGL((k_mm16<EPI, PRO, T, NW, U>), grid, dim3(64 * NW), 0, st, W, in, o);
+    hipLaunchKernelGGL((k_mm16<EPI, T, NW, U>), grid, dim3(64 * NW), 0, st, W, in, o);
     return hipGetLastError();
 }
 
 // The launch shape: a tall matrix takes four tiles per workgroup (its operand fragment serves
-// all four); otherwise one tile, with enough waves that each reduces at most four groups of its
-// slice in one round of loads (the in-register split of an fp32 operand needs more registers
-// than a wave has beyond eight waves per workgroup).
-template <int EPI, int PRO>
+// all four); otherwise one tile, with enough waves (up to twelve) that each reduces at most four
+// groups of its slice in one round of loads.
+template <int EPI>
 hipError_t launch_e(const TiledMat& W, const MmIn& in, int splits, const Mm16Out& o, hipStream_t st)
 {
     const int tiles = (W.N + 15) / 16, gs = W.K / 64 / splits;
-    if (tiles >= 1024) return go<EPI, PRO, 4, 8, 2>(W, in, splits, o, st);
-    if (gs <= 16) return go<EPI, PRO, 1, 4, 4>(W, in, splits, o, st);
-    if (gs <= 32 || PRO == MP_X) return go<EPI, PRO, 1, 8, 4>(W, in, splits, o, st);
-    if constexpr (PRO == MP_ACT) {
-        if (gs <= 48) return go<EPI, PRO, 1, 12, 4>(W, in, splits, o, st);
-        return go<EPI, PRO, 1, 16, 4>(W, in, splits, o, st);
-    }
-    return hipErrorInvalidValue;
+    if (tiles >= 1024) return go<EPI, 4, 8, 2>(W, in, splits, o, st);
+    if (gs <= 16) return go<EPI, 1, 4, 4>(W, in, splits, o, st);
+    if (gs <= 32) return go<EPI, 1, 8, 4>(W, in, splits, o, st);
+    return go<EPI, 1, 12, 4>(W, in, splits, o, st);   // (beyond 48 groups a wave takes two rounds)
 }
 
 }  // namespace
 
 bool mm16_supported(int N, int K) { return N > 0 && K > 0 && K % 64 == 0 && K <= MM_MAX_K; }
 
-hipError_t launch_mm16(int epi, int pro, const TiledMat& W, const MmIn& in, int splits, const Mm16Out& o, hipStream_t st)
+hipError_t launch_mm16(int epi, const TiledMat& W, const MmIn& in, int splits, const Mm16Out& o, hipStream_t st)
 {
     if (!mm16_supported(W.N, W.K) || splits < 1 || splits > MM_MAX_SPLIT || splits > W.K / 64 || o.rows < 1 ||
-        o.rows > MM_ROWS || in.rows < 1 || in.rows > MM_ROWS)
+        o.rows > MM_ROWS || in.rows < 1 || in.rows > MM_ROWS || !in.a.hi || !in.a.lo)
         return hipErrorInvalidValue;
-    if (epi != MM_STORE && splits != 1) return hipErrorInvalidValue;        // the other epilogues need the whole sum
-    if (pro == MP_X && in.norm && splits != 1) return hipErrorInvalidValue;  // the norm needs the whole row
-    if (pro == MP_X && !in.x && !in.tab) return hipErrorInvalidValue;
-    if (pro == MP_X && in.norm_out && (!in.norm || in.tab)) return hipErrorInvalidValue;
-    if (pro == MP_X && in.x_out && !in.tab) return hipErrorInvalidValue;
+    if (epi != MM_STORE && splits != 1) return hipErrorInvalidValue;       // the other epilogues need the whole sum
+    if (in.ssq && (splits != 1 || in.n_ssq < 1 || in.n_ssq > MM_MAX_SSQ)) return hipErrorInvalidValue;
+    if (epi == MM_RESID && o.next.hi && (!o.g_next || !o.next.lo)) return hipErrorInvalidValue;
     if ((epi == MM_SWIGLU || epi == MM_QKV_ROPE) && W.N % 2) return hipErrorInvalidValue;
-#define TSD_MM(E)                                                                \
-    if (epi == E) return pro == MP_X ? launch_e<E, MP_X>(W, in, splits, o, st)   \
-                                     : launch_e<E, MP_ACT>(W, in, splits, o, st);
-    TSD_MM(MM_STORE)
-    TSD_MM(MM_RESID)
-    TSD_MM(MM_SWIGLU)
-    TSD_MM(MM_QKV_ROPE)
-#undef TSD_MM
+    if (epi == MM_STORE) return launch_e<MM_STORE>(W, in, splits, o, st);
+    if (epi == MM_RESID) return launch_e<MM_RESID>(W, in, splits, o, st);
+    if (epi == MM_SWIGLU) return launch_e<MM_SWIGLU>(W, in, splits, o, st);
+    if (epi == MM_QKV_ROPE) return launch_e<MM_QKV_ROPE>(W, in, splits, o, st);
     return hipErrorInvalidValue;
 }
 
@@ -514,10 +545,26 @@ hipError_t launch_pack_tiled(const void* src, int N, int K, void* dst_base, int 
     return hipGetLastError();
 }
 
-hipError_t launch_rows_to_il(const float* src, int B, int K, float* dst, hipStream_t st)
+static bool row_prep_ok(const RowPrep& p)
 {
-    const int n = MM_ROWS * K;
-    hipLaunchKernelGGL(k_rows_to_il, dim3((n + 255) / 256), dim3(256), 0, st, src, B, K, dst);
+    return p.K > 0 && p.K % 64 == 0 && p.K <= MM_MAX_K && p.B >= 1 && p.B <= MM_ROWS && p.act.hi && p.act.lo &&
+           (p.src != ROW_EMB || (p.n_tab >= 1 && p.n_tab <= 16)) && (p.src != ROW_NORMED || p.g_src) &&
+           (p.src == ROW_EMB || p.rows_src);
+}
+
+hipError_t launch_row_prep(const RowPrep& p, hipStream_t st)
+{
+    if (!row_prep_ok(p)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_row_prep, dim3(MM_ROWS), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_pick(const PickArgs& a, hipStream_t st)
+{
+    if (a.n < 1 || a.B < 1 || a.B > MM_ROWS || (a.prep.src >= 0 && (!row_prep_ok(a.prep) || a.prep.B != a.B)))
+        return hipErrorInvalidValue;
+    if (a.top_k > 0 && (!topk_supported(a.n, a.top_k) || !a.posp)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_pick, dim3(a.B), dim3(256), a.top_k > 0 ? (size_t)a.n * 4 : 0, st, a);
     return hipGetLastError();
 }
 
@@ -534,21 +581,6 @@ hipError_t launch_merge16(const float* part, int B, int H, int hd, int max_split
     if (B < 1 || B > MM_ROWS) return hipErrorInvalidValue;
     const int n = B * H * hd;
     hipLaunchKernelGGL(k_merge16, dim3((n + 255) / 256), dim3(256), 0, st, part, H, hd, max_split, posp, n_keys_value, n, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_embed_sum16(const EmbedTabs& T, const int* codes, int ld_codes, int n_tab, int d, float* x, int B,
-                              hipStream_t st)
-{
-    if (n_tab < 1 || n_tab > 16 || B < 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_embed_sum16, dim3((d + 255) / 256, B), dim3(256), 0, st, T, codes, ld_codes, n_tab, d, x);
-    return hipGetLastError();
-}
-
-hipError_t launch_argmax_rows(const float* logits, int ld_l, int n, int* code, int ld_code, int B, hipStream_t st)
-{
-    if (n < 1 || B < 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_argmax_rows, dim3(B), dim3(256), 0, st, logits, ld_l, n, code, ld_code);
     return hipGetLastError();
 }
 

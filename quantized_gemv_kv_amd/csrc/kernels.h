@@ -210,37 +210,32 @@ struct Act16 {
     __half* hi;
     __half* lo;
 };
+constexpr int MM_MAX_SSQ = 256;   // partial row sums of squares a normed operand can come with
 
-// where a GEMM's operand comes from
-enum MmPro : int {
-    MP_ACT = 0,   // a ready fp16 hi/lo operand
-    MP_X = 1      // fp32 rows, split into hi/lo by the GEMM itself (optionally gathered, scaled, normed)
-};
+// The operand of a GEMM: ready fp16 hi/lo rows.  When it is a norm's input, a = hi/lo of x * g
+// (x the residual rows, g the norm gain) and ssq holds n_ssq partial sums of x^2 per row
+// ([n_ssq][MM_ROWS]); the GEMM then applies the RMSNorm's 1 / sqrt(sum / K + eps) to its results
+// (summing the partials in a fixed order).
 struct MmIn {
-    Act16 a;                 // MP_ACT
-    // MP_X: the rows x (il_x layout, MM_ROWS rows), or with tab the embedding rows
-    // tab[codes[b * ld_codes]] (row-major [tab_rows][K], ids clamped) for b < rows; times g[k]
-    // when g is set; with norm, RMSNorm over K (the rows' 1/rms is applied to the results, so the
-    // workgroup must cover all of K: one slice)
-    const float* x;
-    const float* tab;
-    const int* codes;
-    int ld_codes, tab_rows;
-    const float* g;
-    int norm;
+    Act16 a;
+    const float* ssq;
+    int n_ssq;
     float eps;
-    float* x_out;            // MP_X with tab: workgroup 0 also stores the gathered rows to x_out (il_x)
-    float* norm_out;         // MP_X with norm: workgroup 0 also stores RMSNorm(x) * g to norm_out (il_x)
-    int rows;                // rows b < rows are real
+    int rows;            // rows b < rows are real (the others are zero)
 };
 
 enum Mm16Epi : int { MM_STORE = 0, MM_SWIGLU = 1, MM_QKV_ROPE = 2, MM_RESID = 3 };
 struct Mm16Out {
     // STORE: y[split][b][n] at y + split * slice + b * ldy + n (row-major).
-    // RESID: y[il_x(b, n)] += result (the residual stream).
+    // RESID: x[il_x(b, n)] += result (the residual stream); with next.hi set, also the next
+    // norm's operand next[il_act(b, n)] = hi/lo of x * g_next[n] and, per 16-column tile t,
+    // ssq_out[t][b] = sum over the tile of x^2.
     float* y;
     int ldy;
     long long slice;
+    Act16 next;
+    const float* g_next;
+    float* ssq_out;
     // SWIGLU: rows (2m, 2m+1) = (gate_m, up_m); silu(gate) * up is written as the next GEMM's
     // operand act at il_act(b, m)
     Act16 act;
@@ -256,33 +251,64 @@ struct Mm16Out {
     int pos_value;
 };
 
+// A norm's input prepared one row per workgroup: the rows (rows b < B) come from
+//   ROW_EMB:  sum over c < n_tab of tab[c][codes[b * ld_codes + c]] (ids clamped into rows[c]),
+//   ROW_MAJOR: src[b][K] row-major,
+//   ROW_NORMED: RMSNorm(src_il rows) * g_src (src in il_x layout),
+// and are written to x (il_x, unless null), with the operand act = hi/lo of x * g (x alone when
+// g is null) and ssq[0][b] = sum of x^2 (unless null).
+enum RowSrc : int { ROW_EMB = 0, ROW_MAJOR = 1, ROW_NORMED = 2 };
+struct RowPrep {
+    int src;
+    const float* tab[16];
+    int tab_rows[16];
+    const int* codes;
+    int ld_codes, n_tab;
+    const float* rows_src;   // ROW_MAJOR [B][K] / ROW_NORMED il_x
+    const float* g_src;      // ROW_NORMED gain
+    float eps;
+    int K, B;
+    float* x;
+    Act16 act;
+    const float* g;
+    float* ssq;
+};
+
 struct EmbedTabs {
     const float* tab[16];
     int rows[16];
 };
 
 bool mm16_supported(int N, int K);   // any N, K % 64 == 0, K <= MM_MAX_K
-hipError_t launch_mm16(int epi, int pro, const TiledMat& W, const MmIn& in, int splits, const Mm16Out& o, hipStream_t st);
+hipError_t launch_mm16(int epi, const TiledMat& W, const MmIn& in, int splits, const Mm16Out& o, hipStream_t st);
+hipError_t launch_row_prep(const RowPrep& p, hipStream_t st);
 // attention partials (launch_attention layout, max_split slots per head) of rows b < B merged into
 // the operand [B][H * hd]; n_keys = *posp + 1, else n_keys_value
 hipError_t launch_merge16(const float* part, int B, int H, int hd, int max_split, const int* posp, int n_keys_value,
                           const Act16& a, hipStream_t st);
-// x[il_x(b, k)] = sum over c < n_tab of tab[c][codes[b * ld_codes + c]][k] for b < B (ids clamped)
-hipError_t launch_embed_sum16(const EmbedTabs& T, const int* codes, int ld_codes, int n_tab, int d, float* x, int B,
-                              hipStream_t st);
-// row-major [B][K] <-> il_x (rows past B of the interleaved side written as zeros)
-hipError_t launch_rows_to_il(const float* src, int B, int K, float* dst, hipStream_t st);
+// il_x rows -> row-major [B][K]
 hipError_t launch_il_to_rows(const float* src, int B, int K, float* dst, hipStream_t st);
-// code[b * ld_code] = argmax of logits[b * ld_l + 0 .. n) for b < B (ties to the lowest index)
-hipError_t launch_argmax_rows(const float* logits, int ld_l, int n, int* code, int ld_code, int B, hipStream_t st);
+// The code of every row b < B from logits[b * ld_l .. + n): greedy argmax (ties to the lowest
+// index) when top_k == 0, else the top-k draw at counter (*posp, b, pass); written to
+// code[b * ld_code].  Then, when prep.src >= 0, that row's next input is prepared as launch_row_prep
+// does (ROW_EMB with the drawn code as the id of table 0, or ROW_NORMED).
+struct PickArgs {
+    const float* logits;
+    int ld_l, n, B;
+    int top_k;
+    float temperature;
+    unsigned long long seed;
+    int pass;
+    const int* posp;
+    int* code;
+    int ld_code;
+    RowPrep prep;        // prep.src = -1: none
+};
+hipError_t launch_pick(const PickArgs& a, hipStream_t st);
 // y[i] = sum over s < S of part[s * slice + i] for i < n
 hipError_t launch_sum_slices(const float* part, int S, long long slice, float* y, long long n, hipStream_t st);
 // hist[*pos][0..n) = codes[0..n) (n may be 0), then *pos += 1
 hipError_t launch_frame_done(const int* codes, int n, int* hist, int* pos, hipStream_t st);
-
-// top-k draw for rows b < B: id of logits[b * ld_l ..] at counter (*posp, b, pass) -> out[b * ld_out]
-hipError_t launch_topk_rows(const float* logits, int ld_l, int n, int k, float temperature, unsigned long long seed,
-                            int pass, const int* posp, int* out, int ld_out, int B, hipStream_t st);
 
 // ---- small state kernels ---------------------------------------------------------------------
 // dst[r * cols + c] = src[r * src_stride + c]

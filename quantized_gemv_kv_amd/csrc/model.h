@@ -133,7 +133,9 @@ struct tsd_model {
     __half *ckc = nullptr, *cvc = nullptr;
     size_t ckv_layer_elems = 0;
     float* xc = nullptr;              // predictor residual stream [16][d]
-    tsd::Act16 act{};                 // GEMM operand, fp16 hi/lo of 16 rows (il_act layout)
+    tsd::Act16 act{}, act2{};         // GEMM operands, fp16 hi/lo of 16 rows (il_act layout): two,
+                                      // so that an epilogue can write the next while others read one
+    float* ssq = nullptr;             // partial row sums of squares of a norm's input [MM_MAX_SSQ][16]
     hipGraph_t graph_talker = nullptr;
     hipGraphExec_t exec_talker = nullptr;
     int kind_launches[tsd::TSD_KERNEL_KINDS] = {};
@@ -163,8 +165,9 @@ tsd_status talker_pack(tsd_model* m, const tsd_tensor* w);
 // one frame: Talker layers, head and code c_0; with_cp: the predictor's passes for codes
 // 1..C-1 and the history append.  Without: only the Talker's cache is advanced (prefill).
 hipError_t talker_enqueue(tsd_model* m, hipStream_t st, bool with_cp, Probe* pr = nullptr);
-// Talker layer l on m->x at *pos (tsd_layer_forward)
-hipError_t talker_layer(tsd_model* m, int l, hipStream_t st, const int* pos);
+// Talker layer l on the rows d_x ([batch][d] row-major) at *pos, the result left in m->x
+// (tsd_layer_forward)
+hipError_t talker_layer(tsd_model* m, int l, hipStream_t st, const float* d_x, const int* pos);
 // launches of each kind in one frame
 void talker_kind_launches(const tsd_model* m, int* out);
 

@@ -754,8 +754,7 @@ tsd_status tsd_layer_forward(tsd_model* m, int layer, const float* d_x, int pos,
     if (pos < 0 || pos >= c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "position outside the context");
     HIP_TRY(m, launch_fill_i32(m->dbg_pos, pos, 1, m->st), "set position");
     if (c.arch == TSD_ARCH_TALKER_CP) {   // the batched frame keeps its rows interleaved
-        HIP_TRY(m, launch_rows_to_il(d_x, c.batch, c.d_model, m->x, m->st), "copy x");
-        HIP_TRY(m, talker_layer(m, layer, m->st, m->dbg_pos), "layer");
+        HIP_TRY(m, talker_layer(m, layer, m->st, d_x, m->dbg_pos), "layer");
         HIP_TRY(m, launch_il_to_rows(m->x, c.batch, c.d_model, d_out, m->st), "copy out");
         return TSD_OK;
     }
@@ -875,7 +874,7 @@ tsd_status tsd_gemm_rows_scratch_bytes(int N, int K, int splits, size_t* out)
 {
     if (!out || !mm16_supported(N, K) || splits < 1 || splits > MM_MAX_SPLIT || splits > K / 64)
         return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "bad shape or split count");
-    // the interleaved operand rows, then the split-K slices
+    // the operand rows (fp16 hi and lo), then the split-K slices
     *out = align256((size_t)MM_ROWS * K * 4) + (splits == 1 ? 0 : (size_t)splits * MM_ROWS * N * 4);
     return TSD_OK;
 }
@@ -893,21 +892,27 @@ tsd_status tsd_gemm_rows(const void* d_packed, int N, int K, int B, const float*
     if (scratch_bytes < need) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "scratch too small");
     hipStream_t st = (hipStream_t)stream;
     TiledMat W = tiled_view((void*)d_packed, N, K);
-    float* xi = (float*)d_scratch;
-    hipError_t e = launch_rows_to_il(d_x, B, K, xi, st);
+    RowPrep p{};
+    p.src = ROW_MAJOR;
+    p.rows_src = d_x;
+    p.K = K;
+    p.B = B;
+    p.act.hi = (__half*)d_scratch;
+    p.act.lo = (__half*)d_scratch + (size_t)MM_ROWS * K;
+    hipError_t e = launch_row_prep(p, st);   // rows past B are written as zeros
     MmIn in{};
-    in.x = xi;
+    in.a = p.act;
     in.rows = B;
     Mm16Out o{};
     o.rows = B;
     o.ldy = N;
     if (splits == 1) {
         o.y = d_y;
-        if (e == hipSuccess) e = launch_mm16(MM_STORE, MP_X, W, in, 1, o, st);
+        if (e == hipSuccess) e = launch_mm16(MM_STORE, W, in, 1, o, st);
     } else {
         o.y = (float*)((uint8_t*)d_scratch + align256((size_t)MM_ROWS * K * 4));
         o.slice = (long long)MM_ROWS * N;
-        if (e == hipSuccess) e = launch_mm16(MM_STORE, MP_X, W, in, splits, o, st);
+        if (e == hipSuccess) e = launch_mm16(MM_STORE, W, in, splits, o, st);
         if (e == hipSuccess) e = launch_sum_slices(o.y, splits, o.slice, d_y, (long long)B * N, st);
     }
     return e == hipSuccess ? TSD_OK : hip_fail(nullptr, e, "gemm rows");

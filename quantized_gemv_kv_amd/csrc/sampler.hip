@@ -30,22 +30,6 @@ __global__ __launch_bounds__(NT) void k_topk(const float* __restrict__ logits, i
     }
 }
 
-// one workgroup per batch row b: the draw of logits[b * ld_l ..] at counter (*posp, b, pass)
-__global__ __launch_bounds__(NT) void k_topk_rows(const float* __restrict__ logits, int ld_l, int n, int k,
-                                                  float temperature, unsigned long long seed, int pass,
-                                                  const int* posp, int* out, int ld_out)
-{
-    extern __shared__ uint32_t keys[];
-    __shared__ samp::Scratch S;
-    const int b = blockIdx.x;
-    const float* l = logits + (size_t)b * ld_l;
-    for (int i = threadIdx.x; i < n; i += NT) keys[i] = float_order_key(l[i]);
-    __syncthreads();
-    const float u = samp::uniform24(seed, (uint32_t)b, (uint32_t)*posp, (uint32_t)pass);
-    const int id = samp::topk_draw<NT>(keys, n, k, temperature, u, S);
-    if (threadIdx.x == 0) out[(size_t)b * ld_out] = id;
-}
-
 }  // namespace
 
 size_t topk_lds_bytes(int n) { return (size_t)n * sizeof(uint32_t); }
@@ -58,15 +42,6 @@ hipError_t launch_topk(const float* logits, int n, int k, float temperature, uns
     if (!topk_supported(n, k)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_topk, dim3(1), dim3(NT), topk_lds_bytes(n), st, logits, n, k, temperature, seed, row, pass, posp,
                        pos_value, out, hist, hist_stride);
-    return hipGetLastError();
-}
-
-hipError_t launch_topk_rows(const float* logits, int ld_l, int n, int k, float temperature, unsigned long long seed,
-                            int pass, const int* posp, int* out, int ld_out, int B, hipStream_t st)
-{
-    if (!topk_supported(n, k) || B <= 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_topk_rows, dim3(B), dim3(NT), topk_lds_bytes(n), st, logits, ld_l, n, k, temperature, seed, pass,
-                       posp, out, ld_out);
     return hipGetLastError();
 }
 

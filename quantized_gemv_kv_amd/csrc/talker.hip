@@ -11,13 +11,15 @@
 // How: every linear is the batched matrix-core GEMM of frame.hip over all rows at once; one
 // launch per operator, recorded into the step graph (a frame of the 28 + 5 x 16 layers is about
 // a thousand launches, replayed with one graph launch).  Per layer:
-//   QKV GEMM (RMSNorm of the fp32 residual rows in its prologue; RoPE and the fp16 K/V append
-//   in its epilogue) -> split-KV attention (a one-chunk cache, the predictor's, writes the next
-//   operand itself; the Talker's two chunks are merged by a small kernel) -> O-proj GEMM adding
-//   into the residual -> gate/up GEMM (RMSNorm prologue, SwiGLU epilogue writing the next
-//   operand) -> down GEMM adding into the residual: five or six launches per layer.
-// The O and down projections have few 16-row tiles and a long K: sixteen waves of one
+//   QKV GEMM (the first norm applied to its results; RoPE and the fp16 K/V append in its
+//   epilogue) -> split-KV attention (a one-chunk cache, the predictor's, writes the next operand
+//   itself; the Talker's chunks are merged by a small kernel) -> O-proj GEMM adding into the
+//   residual and writing the second norm's input -> gate/up GEMM (norm applied, SwiGLU
+//   epilogue writing the next operand) -> down GEMM adding into the residual and writing the
+//   next layer's norm input: five or six launches per layer.
+// The O and down projections have few 16-row tiles and a long K: up to sixteen waves of one
 // workgroup share the K range, so every result has a single writer and adds deterministically.
+// The sampler of each head also prepares the predictor's next input row.
 #include <algorithm>
 #include <string>
 
@@ -32,36 +34,23 @@ namespace {
         if (e_ != hipSuccess) return e_;     \
     } while (0)
 
-// embedding rows gathered by the first predictor layer (its input is E_{j-1}(c_{j-1}))
-struct Gather {
-    const float* tab;
-    int rows;
-    const int* codes;
-};
-
-// One LLAMA-shaped layer on the residual stream x[rows][d] whose cache (kc, vc: [rows][Hkv]
-// [n_ctx][hd]) gets slot pos = *posp (Talker) or pos_value (predictor).  With gather, the
-// layer's input rows are embedding rows, which the QKV GEMM also stores to x.
-hipError_t layer16(tsd_model* m, const TLayerW& w, float* x, __half* kc, __half* vc, int n_ctx, const int* posp,
-                   int pos_value, hipStream_t st, Probe* pr, const Gather* gather = nullptr)
+// One LLAMA-shaped layer on the residual stream x (il_x rows) whose cache (kc, vc: [rows][Hkv]
+// [n_ctx][hd]) gets slot pos = *posp (Talker) or pos_value (predictor).  On entry act2 holds
+// hi/lo of x * n1g with n_ssq partial row sums of x^2 in ssq; on exit the same for the next norm,
+// whose gain is g_after.
+hipError_t layer16(tsd_model* m, const TLayerW& w, float* x, int n_ssq, const float* g_after, __half* kc, __half* vc,
+                   int n_ctx, const int* posp, int pos_value, hipStream_t st, Probe* pr)
 {
     const tsd_config& c = m->c;
-    const int d = c.d_model, H = c.n_head, Hk = c.n_kv_head, hd = c.head_dim, ff = c.d_ff, B = c.batch;
+    const int d = c.d_model, H = c.n_head, Hk = c.n_kv_head, hd = c.head_dim, B = c.batch;
+    const int tiles_d = (d + 15) / 16;
     // norm + fused QKV, RoPE and the K/V append
     MmIn iq{};
-    iq.x = x;
-    iq.g = w.n1g;
-    iq.norm = 1;
+    iq.a = m->act2;
+    iq.ssq = m->ssq;
+    iq.n_ssq = n_ssq;
     iq.eps = c.norm_eps;
     iq.rows = B;
-    if (gather) {
-        iq.x = nullptr;
-        iq.tab = gather->tab;
-        iq.tab_rows = gather->rows;
-        iq.codes = gather->codes;
-        iq.ld_codes = c.n_codebooks;
-        iq.x_out = x;
-    }
     Mm16Out oq{};
     oq.rows = B;
     oq.qrows = H * hd;
@@ -77,7 +66,7 @@ hipError_t layer16(tsd_model* m, const TLayerW& w, float* x, __half* kc, __half*
     oq.pos_value = pos_value;
     {
         Bracket br(pr, KIND_QKV, st);
-        TRY(launch_mm16(MM_QKV_ROPE, MP_X, w.qkv, iq, 1, oq, st));
+        TRY(launch_mm16(MM_QKV_ROPE, w.qkv, iq, 1, oq, st));
     }
     // attention; a cache of one chunk writes the output projection's operand directly
     const bool direct = attn_max_split(n_ctx) == 1;
@@ -102,22 +91,25 @@ hipError_t layer16(tsd_model* m, const TLayerW& w, float* x, __half* kc, __half*
         TRY(launch_attention(aa, st));
     }
     if (!direct) TRY(launch_merge16(m->part, B, H, hd, attn_max_split(n_ctx), posp, pos_value + 1, m->act, st));
-    // output projection + residual
+    // output projection into the residual, which also prepares the second norm's input
     MmIn ia{};
     ia.a = m->act;
     ia.rows = B;
     Mm16Out orr{};
     orr.y = x;
     orr.rows = B;
+    orr.next = m->act2;
+    orr.g_next = w.n2g;
+    orr.ssq_out = m->ssq;
     {
         Bracket br(pr, KIND_OPROJ, st);
-        TRY(launch_mm16(MM_RESID, MP_ACT, w.o, ia, 1, orr, st));
+        TRY(launch_mm16(MM_RESID, w.o, ia, 1, orr, st));
     }
     // norm + gate/up + SwiGLU, written as the down projection's operand
     MmIn ig{};
-    ig.x = x;
-    ig.g = w.n2g;
-    ig.norm = 1;
+    ig.a = m->act2;
+    ig.ssq = m->ssq;
+    ig.n_ssq = tiles_d;
     ig.eps = c.norm_eps;
     ig.rows = B;
     Mm16Out of{};
@@ -125,46 +117,74 @@ hipError_t layer16(tsd_model* m, const TLayerW& w, float* x, __half* kc, __half*
     of.rows = B;
     {
         Bracket br(pr, KIND_FC, st);
-        TRY(launch_mm16(MM_SWIGLU, MP_X, w.fc, ig, 1, of, st));
+        TRY(launch_mm16(MM_SWIGLU, w.fc, ig, 1, of, st));
     }
-    // down projection + residual
+    // down projection into the residual, preparing the next norm's input
+    orr.g_next = g_after;
     {
         Bracket br(pr, KIND_DOWN, st);
-        TRY(launch_mm16(MM_RESID, MP_ACT, w.down, ia, 1, orr, st));
+        TRY(launch_mm16(MM_RESID, w.down, ia, 1, orr, st));
     }
-    (void)ff;
     return hipSuccess;
 }
 
-// final RMSNorm + head j into logits[b][j][..], and code j of every row into tok[b][j];
-// norm_out receives the normed hidden state (or null)
-hipError_t head16(tsd_model* m, hipStream_t st, Probe* pr, float* x, const float* g, const TiledMat& W, int j, int vocab,
-                  float* norm_out)
+// final RMSNorm (act2 and ssq as left by the last layer) + head j into logits[b][j][..]
+hipError_t head16(tsd_model* m, hipStream_t st, Probe* pr, const TiledMat& W, int j)
 {
     const tsd_config& c = m->c;
-    const int C = c.n_codebooks, B = c.batch;
     MmIn ih{};
-    ih.x = x;
-    ih.g = g;
-    ih.norm = 1;
+    ih.a = m->act2;
+    ih.ssq = m->ssq;
+    ih.n_ssq = (c.d_model + 15) / 16;
     ih.eps = c.norm_eps;
-    ih.rows = B;
-    ih.norm_out = norm_out;
+    ih.rows = c.batch;
     Mm16Out oh{};
     oh.y = m->logits + (size_t)j * m->vmax;
-    oh.ldy = C * m->vmax;
-    oh.rows = B;
-    {
-        Bracket br(pr, KIND_HEAD, st);
-        TRY(launch_mm16(MM_STORE, MP_X, W, ih, 1, oh, st));
-    }
-    const float* lg = m->logits + (size_t)j * m->vmax;
-    if (m->samp.mode == 1) {
-        const int k = (m->samp.top_k <= 0 || m->samp.top_k > vocab) ? vocab : m->samp.top_k;
-        return launch_topk_rows(lg, C * m->vmax, vocab, k, m->samp.temperature, m->samp.seed, j, m->pos, m->tok + j, C, B,
-                                st);
-    }
-    return launch_argmax_rows(lg, C * m->vmax, vocab, m->tok + j, C, B, st);
+    oh.ldy = c.n_codebooks * m->vmax;
+    oh.rows = c.batch;
+    Bracket br(pr, KIND_HEAD, st);
+    return launch_mm16(MM_STORE, W, ih, 1, oh, st);
+}
+
+// code j of every row from head j's logits into tok[b][j], then the row's next input
+hipError_t pick16(tsd_model* m, hipStream_t st, int j, int vocab, const RowPrep* prep)
+{
+    const tsd_config& c = m->c;
+    PickArgs a{};
+    a.logits = m->logits + (size_t)j * m->vmax;
+    a.ld_l = c.n_codebooks * m->vmax;
+    a.n = vocab;
+    a.B = c.batch;
+    a.top_k = m->samp.mode == 1 ? ((m->samp.top_k <= 0 || m->samp.top_k > vocab) ? vocab : m->samp.top_k) : 0;
+    a.temperature = m->samp.temperature;
+    a.seed = m->samp.seed;
+    a.pass = j;
+    a.posp = m->pos;
+    a.code = m->tok + j;
+    a.ld_code = c.n_codebooks;
+    a.prep.src = -1;
+    if (prep) a.prep = *prep;
+    return launch_pick(a, st);
+}
+
+// the predictor's input rows (xc, act2, ssq): an embedding row (id from codes, or the picked code)
+RowPrep cp_input_emb(tsd_model* m, int table, const int* codes)
+{
+    const tsd_config& c = m->c;
+    RowPrep p{};
+    p.src = ROW_EMB;
+    p.tab[0] = m->emb[table];
+    p.tab_rows[0] = m->emb_rows[table];
+    p.codes = codes;
+    p.ld_codes = c.n_codebooks;
+    p.n_tab = 1;
+    p.K = c.d_model;
+    p.B = c.batch;
+    p.x = m->xc;
+    p.act = m->act2;
+    p.g = m->Lc[0].n1g;
+    p.ssq = m->ssq;
+    return p;
 }
 
 }  // namespace
@@ -232,6 +252,9 @@ size_t talker_plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     float* xc = (float*)P.take(sizeof(float) * MM_ROWS * d);
     __half* hi = (__half*)P.take(2 * (size_t)MM_ROWS * kmax);
     __half* lo = (__half*)P.take(2 * (size_t)MM_ROWS * kmax);
+    __half* hi2 = (__half*)P.take(2 * (size_t)MM_ROWS * kmax);
+    __half* lo2 = (__half*)P.take(2 * (size_t)MM_ROWS * kmax);
+    float* ssq = (float*)P.take(sizeof(float) * MM_MAX_SSQ * MM_ROWS);
     float* q = (float*)P.take(sizeof(float) * MM_ROWS * qd);
     float* h = (float*)P.take(sizeof(float) * MM_ROWS * (size_t)ff);
     float* logits = (float*)P.take(sizeof(float) * (size_t)B * C * vmax);
@@ -268,7 +291,7 @@ size_t talker_plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     if (m && base) {
         m->pos = pos; m->dbg_pos = pos + 1; m->tok = tok; m->hist = hist; m->ctl = ctl;
         m->x = x; m->xc = xc; m->qkv = q; m->h = h; m->logits = logits; m->part = part;
-        m->act.hi = hi; m->act.lo = lo;
+        m->act.hi = hi; m->act.lo = lo; m->act2.hi = hi2; m->act2.lo = lo2; m->ssq = ssq;
         m->rope = rope; m->rope_rows = rope_rows;
         for (int k = 0; k < C; ++k) {
             m->emb[k] = emb[k];
@@ -321,8 +344,9 @@ tsd_status talker_pack(tsd_model* m, const tsd_tensor* w)
     for (int k = 1; k < C; ++k) HIP_TRY(m, pk(m->cp_head[k], i++, c.cp_vocab, d, 0, PACK_IDENTITY), "pack predictor head");
     // operand rows past the batch are read by the GEMM and must stay finite: zero everything once
     const int kmax = std::max(d, std::max(H * hd, ff));
-    HIP_TRY(m, launch_fill_u32((unsigned*)m->act.hi, 0u, MM_ROWS * kmax / 2, st), "init");
-    HIP_TRY(m, launch_fill_u32((unsigned*)m->act.lo, 0u, MM_ROWS * kmax / 2, st), "init");
+    for (__half* a : {m->act.hi, m->act.lo, m->act2.hi, m->act2.lo})
+        HIP_TRY(m, launch_fill_u32((unsigned*)a, 0u, MM_ROWS * kmax / 2, st), "init");
+    HIP_TRY(m, launch_fill_f32(m->ssq, 0.f, (size_t)MM_MAX_SSQ * MM_ROWS, st), "init");
     HIP_TRY(m, launch_fill_f32(m->x, 0.f, (size_t)MM_ROWS * d, st), "init");
     HIP_TRY(m, launch_fill_f32(m->xc, 0.f, (size_t)MM_ROWS * d, st), "init");
     return TSD_OK;
@@ -331,35 +355,81 @@ tsd_status talker_pack(tsd_model* m, const tsd_tensor* w)
 hipError_t talker_enqueue(tsd_model* m, hipStream_t st, bool with_cp, Probe* pr)
 {
     const tsd_config& c = m->c;
-    const int d = c.d_model, B = c.batch, C = c.n_codebooks;
-    EmbedTabs T{};
+    const int d = c.d_model, B = c.batch, C = c.n_codebooks, L = c.n_layer, Lc = c.cp_n_layer;
+    const int tiles_d = (d + 15) / 16;
+    // the Talker's input: the sum of the frame's code embeddings
+    RowPrep e{};
+    e.src = ROW_EMB;
     for (int k = 0; k < C; ++k) {
-        T.tab[k] = m->emb[k];
-        T.rows[k] = m->emb_rows[k];
+        e.tab[k] = m->emb[k];
+        e.tab_rows[k] = m->emb_rows[k];
     }
-    TRY(launch_embed_sum16(T, m->tok, C, C, d, m->x, B, st));
-    for (int l = 0; l < c.n_layer; ++l)
-        TRY(layer16(m, m->Lt[l], m->x, m->kc + m->kv_layer_elems * l, m->vc + m->kv_layer_elems * l, c.n_ctx, m->pos, 0,
-                    st, pr));
+    e.codes = m->tok;
+    e.ld_codes = C;
+    e.n_tab = C;
+    e.K = d;
+    e.B = B;
+    e.x = m->x;
+    e.act = m->act2;
+    e.g = m->Lt[0].n1g;
+    e.ssq = m->ssq;
+    TRY(launch_row_prep(e, st));
+    int n_ssq = 1;
+    for (int l = 0; l < L; ++l) {
+        TRY(layer16(m, m->Lt[l], m->x, n_ssq, l + 1 < L ? m->Lt[l + 1].n1g : m->nfg, m->kc + m->kv_layer_elems * l,
+                    m->vc + m->kv_layer_elems * l, c.n_ctx, m->pos, 0, st, pr));
+        n_ssq = tiles_d;
+    }
     if (!with_cp) return launch_frame_done(m->tok, 0, m->hist, m->pos, st);   // advance the position only
     // code 0; the Talker's final-normed hidden state is the predictor's position 0
-    TRY(head16(m, st, pr, m->x, m->nfg, m->t_head, 0, c.vocab, m->xc));
+    TRY(head16(m, st, pr, m->t_head, 0));
+    RowPrep h{};
+    h.src = ROW_NORMED;
+    h.rows_src = m->x;
+    h.g_src = m->nfg;
+    h.eps = c.norm_eps;
+    h.K = d;
+    h.B = B;
+    h.x = m->xc;
+    h.act = m->act2;
+    h.g = m->Lc[0].n1g;
+    h.ssq = m->ssq;
+    TRY(pick16(m, st, 0, c.vocab, &h));
     for (int cpos = 0; cpos < C; ++cpos) {
-        Gather g{};
-        if (cpos > 0) g = Gather{m->emb[cpos - 1], m->emb_rows[cpos - 1], m->tok + (cpos - 1)};
-        for (int l = 0; l < c.cp_n_layer; ++l)
-            TRY(layer16(m, m->Lc[l], m->xc, m->ckc + m->ckv_layer_elems * l, m->cvc + m->ckv_layer_elems * l, C,
-                        nullptr, cpos, st, pr, (cpos > 0 && l == 0) ? &g : nullptr));
-        if (cpos > 0) TRY(head16(m, st, pr, m->xc, m->cp_nfg, m->cp_head[cpos], cpos, c.cp_vocab, nullptr));
+        if (cpos == 1) {   // position 1 consumes E_0(c_0)
+            const RowPrep p = cp_input_emb(m, 0, m->tok);
+            TRY(launch_row_prep(p, st));
+        }
+        n_ssq = 1;
+        for (int l = 0; l < Lc; ++l) {
+            TRY(layer16(m, m->Lc[l], m->xc, n_ssq, l + 1 < Lc ? m->Lc[l + 1].n1g : m->cp_nfg,
+                        m->ckc + m->ckv_layer_elems * l, m->cvc + m->ckv_layer_elems * l, C, nullptr, cpos, st, pr));
+            n_ssq = tiles_d;
+        }
+        if (cpos == 0) continue;
+        TRY(head16(m, st, pr, m->cp_head[cpos], cpos));
+        // code cpos, and position cpos + 1's input E_cpos(c_cpos)
+        const RowPrep p = cp_input_emb(m, cpos, nullptr);
+        TRY(pick16(m, st, cpos, c.cp_vocab, cpos + 1 < C ? &p : nullptr));
     }
     return launch_frame_done(m->tok, B * C, m->hist, m->pos, st);
 }
 
-hipError_t talker_layer(tsd_model* m, int l, hipStream_t st, const int* pos)
+hipError_t talker_layer(tsd_model* m, int l, hipStream_t st, const float* d_x, const int* pos)
 {
     const tsd_config& c = m->c;
-    return layer16(m, m->Lt[l], m->x, m->kc + m->kv_layer_elems * l, m->vc + m->kv_layer_elems * l, c.n_ctx, pos, 0, st,
-                   nullptr);
+    RowPrep p{};
+    p.src = ROW_MAJOR;
+    p.rows_src = d_x;
+    p.K = c.d_model;
+    p.B = c.batch;
+    p.x = m->x;
+    p.act = m->act2;
+    p.g = m->Lt[l].n1g;
+    p.ssq = m->ssq;
+    TRY(launch_row_prep(p, st));
+    return layer16(m, m->Lt[l], m->x, 1, m->Lt[l].n1g, m->kc + m->kv_layer_elems * l, m->vc + m->kv_layer_elems * l,
+                   c.n_ctx, pos, 0, st, nullptr);
 }
 
 void talker_kind_launches(const tsd_model* m, int* out)

@@ -271,3 +271,41 @@ def test_talker_errors():
     gm.close()
     with pytest.raises(TsdError):
         gpu_model(cfg, w[:-1])
+
+
+def test_full_size_frames_sampled_rows():
+    """The frame the benchmark times (Talker 28 layers + predictor 5 layers, 16 codebooks,
+    batch 16, 512-position context) after a random 170-position cache, two frames; rows 0 and
+    15 checked against the oracle row by row (rows are independent: the oracle runs each as a
+    batch of one over that row's cache), teacher forced across the two frames."""
+    cfg = synth.config("talker_cp_aff8")
+    say("[frame-full] talker_cp_aff8, 170 cached positions, rows 0 and 15")
+    w = synth.model_weights(cfg, 42)
+    P, rows = 170, (0, 15)
+    k, v = synth.kv_cache(cfg, P, seed=7)
+    gm = gpu_model(cfg, w)
+    gm.load_kv(dev(k), dev(v), P)
+    c1 = dict(cfg, batch=1)
+    om = oracle.OracleModel(c1, w)
+    codes = synth.prompt_tokens(cfg, 1, seed=8)[:, 0, :]
+    want = {b: codes[b:b + 1] for b in rows}
+    kv_b = {b: (np.ascontiguousarray(k[:, b:b + 1]), np.ascontiguousarray(v[:, b:b + 1])) for b in rows}
+    hist = {b: [] for b in rows}
+    for f in range(2):
+        g_ids = gm.step(dev(codes)).cpu().numpy()
+        lg = gm.logits().cpu().numpy()
+        for b in rows:
+            om.load_kv(*kv_b[b], P)          # the row's cache before this run of frames
+            for past in hist[b]:
+                om.step(past)
+            o_ids = om.step(want[b])
+            n, r = compare_frame(c1, om.logits(), lg[b:b + 1], o_ids, g_ids[b:b + 1], P + f)
+            say(f"  frame {f} row {b}: {n} heads compared, rel {r:.2e}")
+            assert n >= 4
+            hist[b].append(want[b])
+            want[b] = o_ids
+        codes = g_ids.copy()
+        for b in rows:
+            codes[b] = want[b][0]
+    om.close()
+    gm.close()

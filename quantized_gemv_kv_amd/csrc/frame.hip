@@ -29,7 +29,7 @@
 #include <math.h>
 
 #include "gemv_core.h"
-#include "kernels.h"
+#include "frame.h"
 #include "sampler.h"
 
 namespace tsd {

@@ -5,7 +5,7 @@
 #include <string>
 #include <vector>
 
-#include "kernels.h"
+#include "frame.h"
 #include "tsd.h"
 
 namespace tsd {

@@ -72,7 +72,22 @@ def parse():
     return ap.parse_args()
 
 
-STEP_SOURCES = ["quantized_gemv_kv_amd/csrc/" + f for f in ("step.hip", "exchange.h", "gemv_core.h", "common.h", "kernels.h")]
+# what the step kernel is compiled from: its sources, and the step-argument block of kernels.h
+STEP_SOURCES = ["quantized_gemv_kv_amd/csrc/" + f for f in ("step.hip", "exchange.h", "gemv_core.h", "common.h")]
+STEP_DECLS = ("quantized_gemv_kv_amd/csrc/kernels.h", "// ---- persistent decode step", "// ---- top-k sampler")
+
+
+def step_sources_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in STEP_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    path, a, b = STEP_DECLS
+    with open(os.path.join(ROOT, path)) as fh:
+        text = fh.read()
+    h.update(text[text.index(a):text.index(b)].encode())
+    return h.hexdigest()[:16]
 COUNTERS = os.path.join(ROOT, "profiles", "step_gpt2_medium_q4_0_counters.json")
 
 
@@ -80,16 +95,11 @@ def counted_traffic(kernel, workload="gpt2_medium_q4_0"):
     """HBM-side bytes per launch of the step kernel from the committed FETCH_SIZE / WRITE_SIZE
     summary (scaled by the copy calibration), or None when that summary was taken on other
     kernel sources than the ones built now."""
-    import hashlib
     if kernel != "step" or workload != "gpt2_medium_q4_0" or not os.path.exists(COUNTERS):
         return None
-    h = hashlib.sha256()
-    for f in STEP_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
     with open(COUNTERS) as fh:
         d = json.load(fh)
-    return d["traffic_bytes_per_launch"] if d.get("sources_sha256_16") == h.hexdigest()[:16] else None
+    return d["traffic_bytes_per_launch"] if d.get("sources_sha256_16") == step_sources_hash() else None
 
 
 TALL_N, TALL_K = 524288, 1024      # one Q8_0 GEMV of ~570 MB, larger than the 256 MB Infinity Cache

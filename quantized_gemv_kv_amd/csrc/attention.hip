@@ -7,7 +7,8 @@
 //
 // Mapping onto CDNA4:
 //   * the keys of a head are cut into chunks of 256 positions, one 4-wave workgroup per
-//     (chunk, head, row), one 64-key tile per wave;
+//     (chunk, head, row), one 64-key tile per wave; a cache of at most 512 positions can instead
+//     be covered by one workgroup (16-key tiles up to 64 positions, eight waves beyond 256);
 //   * lane layout: hd/8 lanes share a key and each holds 8 of its dims (16 bytes), so every load
 //     instruction reads 1 KB of consecutive K (or V) rows; the score is a DPP reduction inside
 //     the key's lane group and the weighted sum stays in VGPRs, reduced across key groups with a
@@ -30,8 +31,6 @@
 namespace tsd {
 namespace {
 
-constexpr int TILE = 64;
-constexpr int NWAVE = 4;
 
 // sum over the lanes that hold the same dims of different keys (key groups of LPK lanes)
 template <int LPK>
@@ -43,19 +42,22 @@ __device__ __forceinline__ float keygroup_sum(float v)
     return v;
 }
 
-template <int HD>
-__global__ __launch_bounds__(256) void k_attn(const AttnArgs a)
+// NWAVE waves per workgroup, TILE keys per wave: one workgroup covers a chunk of NWAVE * TILE
+// positions (ATTN_CHUNK for the split form; the whole cache for the operand-writing form)
+template <int HD, int NWAVE, int TILE>
+__global__ __launch_bounds__(64 * NWAVE) void k_attn(const AttnArgs a)
 {
     constexpr int LPK = HD / 8;           // lanes per key, 8 dims (16 bytes) each
     constexpr int KPI = 64 / LPK;         // keys per load instruction (1 KB contiguous)
-    constexpr int R = TILE / KPI;         // load rounds per 64-key tile
+    constexpr int R = TILE / KPI;         // load rounds per tile
     constexpr int PS = HD + 4;            // partial stride (16-byte aligned)
+    constexpr int CHUNK = NWAVE * TILE;
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n_keys = a.pos ? ld_uniform(a.pos) + 1 + a.pos_add : a.n_keys;
-    if (s * ATTN_CHUNK >= n_keys) return;
+    if (s * CHUNK >= n_keys) return;
     const int g = h / (a.H / a.Hkv);
-    const int k0 = s * ATTN_CHUNK + wave * TILE;          // first key of this wave's tile
+    const int k0 = s * CHUNK + wave * TILE;               // first key of this wave's tile
     const int c = lane % LPK, kq = lane / LPK;            // dims 8c..8c+7 of key k0 + r*KPI + kq
     const size_t head_off = ((size_t)b * a.Hkv + g) * a.n_ctx * HD;
 
@@ -138,7 +140,7 @@ __global__ __launch_bounds__(256) void k_attn(const AttnArgs a)
 #pragma unroll
         for (int w = 0; w < NWAVE; ++w) L = fmaf(lw[w], exp2f(mw[w] - M), L);
         const float inv = 1.0f / L;
-        for (int i = threadIdx.x; i < HD; i += 256) {
+        for (int i = threadIdx.x; i < HD; i += 64 * NWAVE) {
             float acc = 0.f;
 #pragma unroll
             for (int w = 0; w < NWAVE; ++w) acc = fmaf(ow[w][i], exp2f(mw[w] - M), acc);
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(256) void k_attn(const AttnArgs a)
         return;
     }
     float* part = a.part + (((size_t)b * a.H + h) * attn_max_split(a.n_ctx) + s) * PS;
-    for (int i = threadIdx.x; i < HD; i += 256) {
+    for (int i = threadIdx.x; i < HD; i += 64 * NWAVE) {
         float acc = 0.f;
 #pragma unroll
         for (int w = 0; w < NWAVE; ++w) acc = fmaf(ow[w][i], exp2f(mw[w] - M), acc);
@@ -193,14 +195,26 @@ size_t attn_part_bytes(int B, int H, int n_ctx, int hd)
     return (size_t)B * H * attn_max_split(n_ctx) * (hd + 4) * sizeof(float);
 }
 
+template <int HD>
+hipError_t launch_hd(const AttnArgs& a, hipStream_t st)
+{
+    const dim3 one(1, a.H, a.B);
+    if (a.act_hi) {   // one workgroup covers the whole cache
+        if (a.n_ctx <= 64) hipLaunchKernelGGL((k_attn<HD, 4, 16>), one, dim3(256), 0, st, a);
+        else if (a.n_ctx <= 256) hipLaunchKernelGGL((k_attn<HD, 4, 64>), one, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((k_attn<HD, 8, 64>), one, dim3(512), 0, st, a);
+    } else {
+        hipLaunchKernelGGL((k_attn<HD, 4, 64>), dim3(attn_max_split(a.n_ctx), a.H, a.B), dim3(256), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st)
 {
-    if (a.act_hi && (attn_max_split(a.n_ctx) != 1 || !a.act_lo)) return hipErrorInvalidValue;
-    dim3 grid(attn_max_split(a.n_ctx), a.H, a.B);
-    if (a.hd == 64) hipLaunchKernelGGL(k_attn<64>, grid, dim3(256), 0, st, a);
-    else if (a.hd == 128) hipLaunchKernelGGL(k_attn<128>, grid, dim3(256), 0, st, a);
-    else return hipErrorInvalidValue;
-    return hipGetLastError();
+    if (a.act_hi && (!attn_direct_fits(a.n_ctx) || !a.act_lo)) return hipErrorInvalidValue;
+    if (a.hd == 64) return launch_hd<64>(a, st);
+    if (a.hd == 128) return launch_hd<128>(a, st);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_attention_merge(const AttnArgs& a, int n_keys, hipStream_t st)

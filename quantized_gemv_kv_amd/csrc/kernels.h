@@ -14,6 +14,8 @@ enum ProKind : int { PRO_LOAD = 0, PRO_LN = 1, PRO_RMS = 2, PRO_LN_EMB = 3, PRO_
 // attention works on chunks of ATTN_CHUNK cached positions (one workgroup each)
 constexpr int ATTN_CHUNK = 256;
 __host__ __device__ inline int attn_max_split(int n_ctx) { return (n_ctx + ATTN_CHUNK - 1) / ATTN_CHUNK; }
+// caches one workgroup can cover whole (then the attention can write the batched GEMM operand)
+__host__ __device__ inline bool attn_direct_fits(int n_ctx) { return n_ctx <= 512; }
 
 struct ProArgs {
     const float* src;   // [NB][ld_src] input (ignored when n_emb > 0)
@@ -101,7 +103,7 @@ struct AttnArgs {
     const int* pos;      // n_keys = *pos + 1 + pos_add when pos != null
     int pos_add;
     int n_keys;          // used when pos == null
-    // when the cache fits one chunk (n_ctx <= ATTN_CHUNK) and act_hi is set, o is written straight
+    // when attn_direct_fits(n_ctx) and act_hi is set, o is written straight
     // into the batched GEMM operand (row b, column h * hd + i, il_act layout) as fp16 hi and lo
     // (x - hi) instead of partials
     __half* act_hi;

@@ -12,11 +12,12 @@
 // launch per operator, recorded into the step graph (a frame of the 28 + 5 x 16 layers is about
 // a thousand launches, replayed with one graph launch).  Per layer:
 //   QKV GEMM (the first norm applied to its results; RoPE and the fp16 K/V append in its
-//   epilogue) -> split-KV attention (a one-chunk cache, the predictor's, writes the next operand
-//   itself; the Talker's chunks are merged by a small kernel) -> O-proj GEMM adding into the
+//   epilogue) -> attention (a cache of up to 512 positions is covered by one workgroup per head
+//   and row, which writes the next operand itself; longer Talker caches are split and merged by
+//   a small kernel) -> O-proj GEMM adding into the
 //   residual and writing the second norm's input -> gate/up GEMM (norm applied, SwiGLU
 //   epilogue writing the next operand) -> down GEMM adding into the residual and writing the
-//   next layer's norm input: five or six launches per layer.
+//   next layer's norm input: five launches per layer (six with a merge).
 // The O and down projections have few 16-row tiles and a long K: up to sixteen waves of one
 // workgroup share the K range, so every result has a single writer and adds deterministically.
 // The sampler of each head also prepares the predictor's next input row.
@@ -69,7 +70,7 @@ hipError_t layer16(tsd_model* m, const TLayerW& w, float* x, int n_ssq, const fl
         TRY(launch_mm16(MM_QKV_ROPE, w.qkv, iq, 1, oq, st));
     }
     // attention; a cache of one chunk writes the output projection's operand directly
-    const bool direct = attn_max_split(n_ctx) == 1;
+    const bool direct = attn_direct_fits(n_ctx);
     AttnArgs aa{};
     aa.q = m->qkv;
     aa.ldq = H * hd;

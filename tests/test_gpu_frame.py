@@ -221,6 +221,16 @@ def test_talker_widths_over_two_attention_chunks():
     say(f"  heads compared {heads}, worst rel {worst:.2e}")
 
 
+def test_small_frame_long_cache_split_attention():
+    """A Talker cache longer than one attention workgroup covers (600 positions): the split
+    attention and its merge into the output projection's operand, after 530 cached positions."""
+    cfg = small_talker(batch=3, n_ctx=600)
+    say("[frame-small] 530 cached positions, split attention")
+    w = synth.model_weights(cfg, 11, norm_std=0.1)
+    heads, worst = frame_parity(cfg, w, n_prompt=0, n_frames=3, kv_pos=530)
+    say(f"  heads compared {heads}, worst rel {worst:.2e}")
+
+
 def test_talker_layer_forward():
     """One Talker layer at its real widths on 16 rows at position 100 over a random cache."""
     cfg = dict(synth.config("talker_cp_aff8"), n_layer=1, cp_n_layer=1, n_ctx=128)

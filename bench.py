@@ -102,13 +102,27 @@ def counted_traffic(kernel, workload="gpt2_medium_q4_0"):
     return d["traffic_bytes_per_launch"] if d.get("sources_sha256_16") == step_sources_hash() else None
 
 
+def warm(call, seconds=0.25):
+    """Back-to-back launches for about `seconds` before a timed measurement: on a GPU that has
+    been idle the board's power management first runs a launch at full speed, then slows the
+    next ~100 ms while it changes state, so bursts timed straight away are mixed."""
+    import time
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            call()
+        torch.cuda.synchronize()
+
+
 TALL_N, TALL_K = 524288, 1024      # one Q8_0 GEMV of ~570 MB, larger than the 256 MB Infinity Cache
 
 
 def gemv_headline(seed, reps=7):
     """The quantized GEMV alone at a size where a launch is amortised: y = W x with W a
-    524288 x 1024 Q8_0 matrix (the lone-GEMV law), x ~ N(0,1), batch 1; the median over `reps`
-    bursts of 10 back-to-back launches timed with HIP events.  Bytes = the stored matrix + x + y."""
+    524288 x 1024 Q8_0 matrix (the lone-GEMV law), x ~ N(0,1), batch 1; after a quarter second of
+    warm-up launches, the median over `reps` bursts of 10 back-to-back launches timed with HIP
+    events.  Bytes = the stored matrix + x + y."""
     import torch
     from quantized_gemv_kv_amd import binding, roofline, synth
     N, K = TALL_N, TALL_K
@@ -121,8 +135,7 @@ def gemv_headline(seed, reps=7):
     del canon
     x = torch.from_numpy(synth.normal_f32(synth.rng_for(seed, 1), (1, K))).cuda()
     y = torch.empty((1, N), dtype=torch.float32, device="cuda")
-    for _ in range(3):
-        binding.tsd_gemv("q8_0", packed, N, K, 1, x, None, y)
+    warm(lambda: binding.tsd_gemv("q8_0", packed, N, K, 1, x, None, y))
     # median over short bursts of back-to-back launches (about 1 ms each, timed with HIP events
     # around the burst): long runs of full-bandwidth streaming are slowed by the board's power
     # management, which would make the figure depend on the run length
@@ -140,7 +153,7 @@ def gemv_headline(seed, reps=7):
     nbytes = roofline.gemv_bytes("q8_0", N, K)
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"shape": f"Q8_0 {N}x{K}, batch 1", "bytes": nbytes, "us": us, "gbs": gbs,
-            "frac": gbs / roofline.HBM_PEAK_GBS, "timing": f"median over {reps} bursts of {burst} back-to-back launches"}
+            "frac": gbs / roofline.HBM_PEAK_GBS, "timing": f"median over {reps} bursts of {burst} back-to-back launches, after 0.25 s of warm-up launches"}
 
 
 def cpu_baseline(cfg, weights, seconds, seed):
@@ -223,8 +236,7 @@ def gemm_rows_headline(seed, reps=7):
     x = torch.from_numpy(synth.normal_f32(synth.rng_for(seed, 2), (B, K))).cuda()
     y = torch.empty((B, N), dtype=torch.float32, device="cuda")
     scratch = torch.empty(binding.tsd_gemm_rows_scratch_bytes(N, K, 1), dtype=torch.uint8, device="cuda")
-    for _ in range(3):
-        binding.tsd_gemm_rows(packed, N, K, B, x, y, 1, scratch)
+    warm(lambda: binding.tsd_gemm_rows(packed, N, K, B, x, y, 1, scratch))
     burst, times = 10, []
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -241,7 +253,7 @@ def gemm_rows_headline(seed, reps=7):
     flops = 2.0 * N * K * B
     return {"shape": f"aff8 {N}x{K}, 16 rows", "bytes": nbytes, "us": us, "gbs": gbs,
             "frac": gbs / roofline.HBM_PEAK_GBS, "tflops": flops / (us * 1e-6) / 1e12,
-            "timing": f"median over {reps} bursts of {burst} back-to-back calls (operand split + GEMM)"}
+            "timing": f"median over {reps} bursts of {burst} back-to-back calls (operand split + GEMM), after 0.25 s of warm-up calls"}
 
 
 def main():

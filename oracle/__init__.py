@@ -35,7 +35,17 @@ class _Cfg(ctypes.Structure):
         ("norm_eps", ctypes.c_double), ("rope_theta", ctypes.c_double),
         ("cp_n_layer", ctypes.c_int), ("n_codebooks", ctypes.c_int), ("cp_vocab", ctypes.c_int),
         ("sample_mode", ctypes.c_int), ("top_k", ctypes.c_int), ("temperature", ctypes.c_double),
-        ("seed", ctypes.c_uint64)]
+        ("seed", ctypes.c_uint64), ("top_p", ctypes.c_double), ("min_p", ctypes.c_double),
+        ("rep_penalty", ctypes.c_double), ("sample_order", ctypes.c_int)]
+
+
+class _Samp(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int), ("top_k", ctypes.c_int), ("temperature", ctypes.c_double),
+                ("top_p", ctypes.c_double), ("min_p", ctypes.c_double), ("rep_penalty", ctypes.c_double),
+                ("order", ctypes.c_int)]
+
+
+ORDERS = {"t3": 0, "mtl": 1}
 
 
 _lib = None
@@ -65,6 +75,7 @@ def lib():
             "orc_attend": (None, [_P, _P, _P, i, i, _P]),
             "orc_argmax": (i, [_P, i]),
             "orc_sample_topk": (i, [_P, i, i, d, d]),
+            "orc_sample_chain": (i, [_P, i, _P, _P, i, d, _P]),
             "orc_n_weights": (i, [_P]),
             "orc_model_create": (_P, [_P, _P, _P, i]),
             "orc_last_error": (ctypes.c_char_p, []),
@@ -203,16 +214,34 @@ def sample_topk(logits, k, temperature, u):
     return lib().orc_sample_topk(_ptr(v), v.size, k, temperature, u)
 
 
+def sample_chain(logits, u, mode=1, top_k=0, temperature=1.0, top_p=0.0, min_p=0.0, rep_penalty=1.0,
+                 order="t3", hist=()):
+    """The sampler chain (tsd_oracle.c orc_sample_chain).  Returns (id, margins) with margins =
+    {draw, top_p, min_p, top_k, greedy} distances to the nearest decision boundary."""
+    v = _c(logits, np.float64)
+    h = _c(list(hist) if len(hist) else [0], np.int32)
+    s = _Samp(mode, top_k, temperature, top_p, min_p, rep_penalty, ORDERS.get(order, order))
+    m = np.zeros(5, np.float64)
+    i = lib().orc_sample_chain(_ptr(v), v.size, ctypes.byref(s), _ptr(h), len(hist), float(u), _ptr(m))
+    return i, dict(zip(("draw", "top_p", "min_p", "top_k", "greedy"), m.tolist()))
+
+
 # ---- models -----------------------------------------------------------------------------------
+
+# sampler-chain fields a config may leave out: every filter off, the T3 order
+CHAIN_DEFAULTS = {"top_p": 0.0, "min_p": 0.0, "rep_penalty": 1.0, "sample_order": "t3"}
+
 
 def _cfg_struct(cfg: dict) -> _Cfg:
     s = _Cfg()
     for name, _ in _Cfg._fields_:
-        v = cfg[name]
+        v = cfg.get(name, CHAIN_DEFAULTS.get(name)) if name in CHAIN_DEFAULTS else cfg[name]
         if name == "arch":
             v = ARCHS[v]
         elif name == "wfmt":
             v = FORMATS[v]
+        elif name == "sample_order":
+            v = ORDERS.get(v, v)
         setattr(s, name, v)
     return s
 

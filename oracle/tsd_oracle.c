@@ -312,6 +312,152 @@ int orc_sample_topk(const double* logits, int n, int k, double temperature, doub
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* The sampler chain, as processors on a full-vocabulary vector v[n] in which a removed entry is
+ * -inf.  Two orders appear on the pages:
+ *   [J] §3.2 (the T3 port, mirroring HF's processor list): temperature, top-k, top-p, then the
+ *       repetition penalty;
+ *   [J] §3.19 (the multilingual T3): repetition penalty, temperature, min-p, top-p, top-k, then
+ *       the draw.
+ * The repetition penalty ([J] §3.2 issue 7) divides a positive logit by theta and multiplies a
+ * negative one, for every token id present in the history (once per id, however often it
+ * occurs).  top-p keeps, in descending order, every entry whose preceding mass is below p
+ * (HF's warper removes an entry whose ascending cumulative mass is <= 1 - p, which is the same
+ * set); min-p keeps the entries whose probability is at least min_p times the largest.
+ * READING (order of the draw): the survivors are walked in descending order of their final
+ * values (ties by lower index), as in orc_sample_topk.  READING (greedy with a penalty): the
+ * argmax of the penalized logits (HF applies processors, not warpers, when not sampling). */
+
+typedef struct { double v; int i; } orc_vi;
+static int cmp_desc(const void* a, const void* b)
+{
+    const orc_vi *x = (const orc_vi*)a, *y = (const orc_vi*)b;
+    if (x->v > y->v) return -1;
+    if (x->v < y->v) return 1;
+    return x->i < y->i ? -1 : (x->i > y->i);
+}
+
+/* the finite entries of v in descending order (ties by lower index); returns their count */
+static int rank_desc(const double* v, int n, orc_vi* out)
+{
+    int m = 0;
+    for (int i = 0; i < n; ++i) if (isfinite(v[i])) { out[m].v = v[i]; out[m].i = i; ++m; }
+    qsort(out, (size_t)m, sizeof(orc_vi), cmp_desc);
+    return m;
+}
+
+/* probabilities of the finite entries (softmax, max-subtracted); removed entries get 0 */
+static void probs_of(const double* v, int n, double* p)
+{
+    double mx = -INFINITY, z = 0.0;
+    for (int i = 0; i < n; ++i) if (v[i] > mx) mx = v[i];
+    for (int i = 0; i < n; ++i) { p[i] = isfinite(v[i]) ? exp(v[i] - mx) : 0.0; z += p[i]; }
+    for (int i = 0; i < n; ++i) p[i] /= z;
+}
+
+static void proc_penalty(double* v, int n, const char* seen, double theta)
+{
+    for (int i = 0; i < n; ++i)
+        if (seen[i] && isfinite(v[i])) v[i] = v[i] < 0.0 ? v[i] * theta : v[i] / theta;
+}
+
+static void proc_temperature(double* v, int n, double T)
+{
+    for (int i = 0; i < n; ++i) v[i] /= T;
+}
+
+/* keep the k largest (ties by lower index); gap = distance between the k-th and (k+1)-th */
+static void proc_top_k(double* v, int n, int k, orc_vi* r, double* gap)
+{
+    int m = rank_desc(v, n, r);
+    if (k >= m) return;
+    double g = r[k - 1].v - r[k].v;
+    if (g < *gap) *gap = g;
+    for (int j = k; j < m; ++j) v[r[j].i] = -INFINITY;
+}
+
+static void proc_top_p(double* v, int n, double top_p, orc_vi* r, double* p, double* margin)
+{
+    int m = rank_desc(v, n, r);
+    probs_of(v, n, p);
+    double before = 0.0;
+    for (int j = 0; j < m; ++j) {
+        double dist = fabs(before - top_p);
+        if (j > 0 && dist < *margin) *margin = dist;
+        if (before >= top_p) v[r[j].i] = -INFINITY;
+        before += p[r[j].i];
+    }
+}
+
+static void proc_min_p(double* v, int n, double min_p, double* p, double* margin)
+{
+    probs_of(v, n, p);
+    double pmax = 0.0;
+    for (int i = 0; i < n; ++i) if (p[i] > pmax) pmax = p[i];
+    for (int i = 0; i < n; ++i) {
+        if (!isfinite(v[i])) continue;
+        double dist = fabs(p[i] / pmax - min_p);
+        if (dist < *margin) *margin = dist;
+        if (p[i] < min_p * pmax) v[i] = -INFINITY;
+    }
+}
+
+/* margins (optional, 5 values): [0] distance of u from the nearest cumulative boundary of the
+ * draw, relative to the total mass; [1] top-p: smallest |preceding mass - p|; [2] min-p:
+ * smallest |p_i / p_max - min_p|; [3] top-k: gap between the k-th and (k+1)-th value at that
+ * stage; [4] greedy: gap between the two largest penalized logits.  Unused ones are +inf. */
+int orc_sample_chain(const double* logits, int n, const orc_sampling* s, const int32_t* hist, int n_hist,
+                     double u, double* margins)
+{
+    if (n <= 0) return -1;
+    double mg[5] = {INFINITY, INFINITY, INFINITY, INFINITY, INFINITY};
+    double* v = (double*)malloc(sizeof(double) * (size_t)n);
+    double* p = (double*)malloc(sizeof(double) * (size_t)n);
+    char* seen = (char*)calloc((size_t)n, 1);
+    orc_vi* r = (orc_vi*)malloc(sizeof(orc_vi) * (size_t)n);
+    memcpy(v, logits, sizeof(double) * (size_t)n);
+    for (int j = 0; j < n_hist; ++j) if (hist[j] >= 0 && hist[j] < n) seen[hist[j]] = 1;
+    int pen = s->rep_penalty > 0.0 && s->rep_penalty != 1.0;
+    int k = (s->top_k <= 0 || s->top_k > n) ? n : s->top_k;
+    int use_p = s->top_p > 0.0 && s->top_p < 1.0, use_min = s->min_p > 0.0;
+    int pick;
+    if (s->mode == 0) {
+        if (pen) proc_penalty(v, n, seen, s->rep_penalty);
+        int m = rank_desc(v, n, r);
+        pick = r[0].i;
+        if (m > 1) mg[4] = r[0].v - r[1].v;
+    } else {
+        if (s->order == ORC_ORDER_MTL) {
+            if (pen) proc_penalty(v, n, seen, s->rep_penalty);
+            proc_temperature(v, n, s->temperature);
+            if (use_min) proc_min_p(v, n, s->min_p, p, &mg[2]);
+            if (use_p) proc_top_p(v, n, s->top_p, r, p, &mg[1]);
+            proc_top_k(v, n, k, r, &mg[3]);
+        } else {
+            proc_temperature(v, n, s->temperature);
+            proc_top_k(v, n, k, r, &mg[3]);
+            if (use_p) proc_top_p(v, n, s->top_p, r, p, &mg[1]);
+            if (pen) proc_penalty(v, n, seen, s->rep_penalty);
+        }
+        /* the draw: softmax over the survivors, walked in descending order */
+        int m = rank_desc(v, n, r);
+        double total = 0.0;
+        for (int j = 0; j < m; ++j) total += exp(r[j].v - r[0].v);
+        double thr = u * total, c = 0.0;
+        pick = r[m - 1].i;
+        int found = 0;
+        for (int j = 0; j < m; ++j) {
+            c += exp(r[j].v - r[0].v);
+            double dist = fabs(c - thr) / total;
+            if (dist < mg[0]) mg[0] = dist;
+            if (!found && c > thr) { pick = r[j].i; found = 1; }
+        }
+    }
+    if (margins) memcpy(margins, mg, sizeof(mg));
+    free(v); free(p); free(seen); free(r);
+    return pick;
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* Models.
  * GPT-2-Medium-shaped T3 ([J] §3.2; appendix A3 lists the quantized linears c_attn, c_proj,
  * c_fc, mlp.c_proj and speech_head; biases, norms and embeddings stay fp32).
@@ -360,6 +506,8 @@ struct orc_model {
     int vmax;
     double* logits;              /* [B][C or 1][vmax] */
     int32_t* last;               /* [B][C or 1] last sampled */
+    int32_t* seq;                /* [n_ctx][B] token consumed at each position (code 0 for
+                                    TALKER_CP): the repetition penalty's history; -1 = unknown */
 };
 
 int orc_n_weights(const orc_config* c)
@@ -416,7 +564,7 @@ void orc_model_destroy(orc_model* m)
     if (!m) return;
     for (int i = 0; i < m->n_own; ++i) free(m->own[i]);
     free(m->own); free(m->L); free(m->Lc); free(m->kc); free(m->vc); free(m->ckc); free(m->cvc);
-    free(m->logits); free(m->last); free(m);
+    free(m->logits); free(m->last); free(m->seq); free(m);
 }
 
 static size_t cache_elems(const orc_config* c)
@@ -537,6 +685,8 @@ orc_model* orc_model_create(const orc_config* c, const void* const* w, const siz
     if (c->arch == ORC_TALKER_CP && c->cp_vocab > m->vmax) m->vmax = c->cp_vocab;
     m->logits = (double*)calloc((size_t)c->batch * m->n_in * m->vmax, sizeof(double));
     m->last = (int32_t*)calloc((size_t)c->batch * m->n_in, sizeof(int32_t));
+    m->seq = (int32_t*)malloc(sizeof(int32_t) * (size_t)c->n_ctx * c->batch);
+    for (size_t i = 0; i < (size_t)c->n_ctx * c->batch; ++i) m->seq[i] = -1;
     if (!m->kc || !m->vc || !m->logits || !m->last) { set_err("out of memory"); orc_model_destroy(m); return NULL; }
     return m;
 }
@@ -626,12 +776,22 @@ static void final_norm(const orc_model* m, const double* x, const double* g, con
     else orc_rmsnorm(x, m->c.d_model, g, m->c.norm_eps, y);
 }
 
+/* READING (which heads the penalty covers): the main head (GPT2/LLAMA token, Talker code 0),
+ * over the tokens the row consumed at positions 0..pos; the code predictor's heads use the rest
+ * of the chain without it. */
 static int pick(const orc_model* m, const double* logits, int n, int row, int pos, int pass)
 {
-    if (m->c.sample_mode == 1)
-        return orc_sample_topk(logits, n, m->c.top_k, m->c.temperature,
-                               orc_uniform24(m->c.seed, (uint32_t)row, (uint32_t)pos, (uint32_t)pass));
-    return orc_argmax(logits, n);
+    const orc_config* c = &m->c;
+    orc_sampling s = {c->sample_mode, c->top_k, c->temperature, c->top_p, c->min_p, c->rep_penalty, c->sample_order};
+    if (pass > 0) s.rep_penalty = 1.0;
+    int pen = s.rep_penalty > 0.0 && s.rep_penalty != 1.0;
+    if (s.mode == 0 && !pen) return orc_argmax(logits, n);
+    int32_t* hist = (int32_t*)malloc(sizeof(int32_t) * (size_t)(pos + 1));
+    for (int p = 0; p <= pos; ++p) hist[p] = m->seq[(size_t)p * c->batch + row];
+    int id = orc_sample_chain(logits, n, &s, hist, pen ? pos + 1 : 0,
+                              orc_uniform24(c->seed, (uint32_t)row, (uint32_t)pos, (uint32_t)pass), NULL);
+    free(hist);
+    return id;
 }
 
 /* the input embedding of one position */
@@ -669,6 +829,7 @@ static int forward_position(orc_model* m, const int32_t* tok_in, int32_t* tok_ou
     /* validate every token before touching state */
     for (int b = 0; b < c->batch; ++b)
         if (embed(m, tok_in + (size_t)b * C, pos, x)) { set_err("token out of range"); free(x); free(h); free(lg); return -1; }
+    for (int b = 0; b < c->batch; ++b) m->seq[(size_t)pos * c->batch + b] = tok_in[(size_t)b * C];
     for (int b = 0; b < c->batch; ++b) {
         embed(m, tok_in + (size_t)b * C, pos, x);
         for (int l = 0; l < c->n_layer; ++l) layer_forward(m, &m->L[l], l, b, x, pos, m->kc, m->vc, c->n_ctx);
@@ -751,6 +912,7 @@ int orc_load_kv(orc_model* m, const uint16_t* k, const uint16_t* v, int n_pos)
                     memcpy(cache_at(m->kc, c, c->n_ctx, l, b, g, p), k + src, hd * 2);
                     memcpy(cache_at(m->vc, c, c->n_ctx, l, b, g, p), v + src, hd * 2);
                 }
+    for (size_t i = 0; i < (size_t)n_pos * c->batch; ++i) m->seq[i] = -1;   /* tokens unknown */
     m->n_past = n_pos;
     return 0;
 }

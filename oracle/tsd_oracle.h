@@ -34,11 +34,23 @@ typedef struct {
     int n_layer, d_model, n_head, n_kv_head, head_dim, d_ff, vocab, n_ctx, batch;
     double norm_eps, rope_theta;
     int cp_n_layer, n_codebooks, cp_vocab; /* TALKER_CP only */
-    int sample_mode;                       /* 0 greedy, 1 top-k */
+    int sample_mode;                       /* 0 greedy, 1 draw */
     int top_k;
     double temperature;
     uint64_t seed;
+    double top_p, min_p, rep_penalty;      /* off: 0 (or >= 1), 0, 0 (or 1) */
+    int sample_order;                      /* ORC_ORDER_T3 or ORC_ORDER_MTL */
 } orc_config;
+
+/* sampler chain orders ([J] §3.2 and §3.19) */
+enum { ORC_ORDER_T3 = 0, ORC_ORDER_MTL = 1 };
+
+typedef struct {
+    int mode;                              /* 0 greedy (penalty, then argmax), 1 draw */
+    int top_k;                             /* <= 0 or > n: the whole vocabulary */
+    double temperature, top_p, min_p, rep_penalty;
+    int order;
+} orc_sampling;
 
 typedef struct orc_model orc_model;
 
@@ -67,6 +79,10 @@ void orc_attend(const double* q, const uint16_t* kc, const uint16_t* vc, int n_k
                 double* o); /* kc/vc: [n_keys][hd] fp16 rows */
 int  orc_argmax(const double* v, int n);
 int  orc_sample_topk(const double* logits, int n, int k, double temperature, double u);
+/* the sampler chain over logits[n] with the history's token ids (out-of-range ids ignored);
+ * margins: NULL or 5 doubles (see tsd_oracle.c) */
+int  orc_sample_chain(const double* logits, int n, const orc_sampling* s, const int32_t* hist,
+                      int n_hist, double u, double* margins);
 
 /* ---- models ---- */
 int  orc_n_weights(const orc_config* c);

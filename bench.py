@@ -74,7 +74,7 @@ def parse():
 
 # what the step kernel is compiled from: its sources, and the step-argument block of kernels.h
 STEP_SOURCES = ["quantized_gemv_kv_amd/csrc/" + f for f in ("step.hip", "exchange.h", "gemv_core.h", "common.h")]
-STEP_DECLS = ("quantized_gemv_kv_amd/csrc/kernels.h", "// ---- persistent decode step", "// ---- top-k sampler")
+STEP_DECLS = ("quantized_gemv_kv_amd/csrc/kernels.h", "// ---- persistent decode step", "// ---- sampler chain")
 
 
 def step_sources_hash():

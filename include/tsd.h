@@ -81,19 +81,38 @@ typedef struct {
                              resident at once is TSD_ERR_UNSUPPORTED */
 } tsd_config;
 
-/* Sampler ([J] §3.2: temperature then top-k, in that order).
- * mode 0: greedy argmax, ties to the lowest index.
- * mode 1: keep the top_k largest of logits/temperature (ties by lower index), softmax over
- *         them, draw u in [0,1) as the top 24 bits of the first word of Philox4x64-10
- *         (Salmon et al. 2011) with key (seed, 0) and counter (position, row, pass, 0), and
- *         return the first index in descending order whose cumulative mass exceeds u * total.
- *         top_k <= 0 or > vocab means the whole vocabulary.  Draws with k > 1024 (or a vocabulary
- *         over 12288) are TSD_ERR_UNSUPPORTED; the temperature must be positive and finite. */
+/* Sampler chain ([J] §3.2: the T3 port's order, temperature, top-k, top-p, repetition penalty;
+ * [J] §3.19: the multilingual order, repetition penalty, temperature, min-p, top-p, top-k; [F]
+ * §5.2 and §5.5: the random state and the penalty's history on the device).
+ * mode 0: greedy argmax, ties to the lowest index; with rep_penalty on, the argmax of the
+ *         penalized logits (processors, no warpers, as when not sampling).
+ * mode 1: the chain in `order`, then a draw: u in [0,1) is the top 24 bits of the first word of
+ *         Philox4x64-10 (Salmon et al. 2011) with key (seed, 0) and counter (position, row,
+ *         pass, 0); the survivors are walked in descending order of their final values (ties by
+ *         lower index) and the first whose cumulative mass exceeds u * total is returned.
+ * The steps:
+ *   temperature  logits / temperature (positive, finite);
+ *   top_k        the k largest, ties by lower index; <= 0 or > vocab means the whole vocabulary;
+ *   top_p        keep, in descending order, every entry whose preceding mass is below top_p
+ *                (measured over what survives the steps before it); 0 or 1 is off;
+ *   min_p        keep the entries whose probability is at least min_p times the largest; 0 is
+ *                off; only in TSD_ORDER_MTL;
+ *   rep_penalty  every id present in the row's history (counted once) gets logit / theta if the
+ *                logit is >= 0, logit * theta if negative; 0 or 1 is off.  The history is the
+ *                tokens the row consumed at positions 0..n_past (prompt included; for TALKER_CP
+ *                code 0 of every frame); tsd_load_kv leaves the loaded positions without one.
+ *                TALKER_CP: the Talker's code-0 head only, never the code predictor's heads.
+ * Draws with k > 1024 (or a vocabulary over 12288) are TSD_ERR_UNSUPPORTED. */
+typedef enum { TSD_ORDER_T3 = 0, TSD_ORDER_MTL = 1 } tsd_sampler_order;
 typedef struct {
     int32_t mode;
     int32_t top_k;
     float temperature;
     uint64_t seed;
+    float top_p;
+    float min_p;
+    float rep_penalty;
+    int32_t order; /* tsd_sampler_order */
 } tsd_sampling;
 
 typedef struct {
@@ -199,6 +218,15 @@ tsd_status tsd_time_kernel(tsd_model* m, int kind, int n_steps, float* avg_us, i
  * not positive and finite. */
 tsd_status tsd_sample_topk(const float* d_logits, int n, int top_k, float temperature, uint64_t seed, int row,
                            int pos, int pass, int32_t* d_out, void* stream);
+
+/* The step's sampler chain (tsd_sampling, any mode and order) on d_logits[0..n) (fp32, device)
+ * with the history d_hist[0..n_hist) (int32 token ids, device; ids outside [0, n) are ignored;
+ * may be NULL when n_hist is 0): the id is written to d_out[0] (device).  The uniform is drawn
+ * at counter (pos, row, pass, 0) with key (s->seed, 0).  TSD_ERR_INVALID_ARGUMENT for null
+ * buffers, n <= 0, negative counters or n_hist, and parameters outside the ranges of
+ * tsd_sampling; TSD_ERR_UNSUPPORTED for k > 1024 or n > 12288. */
+tsd_status tsd_sample(const float* d_logits, int n, const tsd_sampling* s, const int32_t* d_hist, int n_hist,
+                      int row, int pos, int pass, int32_t* d_out, void* stream);
 
 /* Bytes of the kernel layout of one W[N][K] matrix (tsd_gemv_pack's output). */
 tsd_status tsd_gemv_packed_bytes(int wfmt, int N, int K, size_t* out_bytes);

@@ -217,13 +217,13 @@ def sample_topk(logits, k, temperature, u):
 def sample_chain(logits, u, mode=1, top_k=0, temperature=1.0, top_p=0.0, min_p=0.0, rep_penalty=1.0,
                  order="t3", hist=()):
     """The sampler chain (tsd_oracle.c orc_sample_chain).  Returns (id, margins) with margins =
-    {draw, top_p, min_p, top_k, greedy} distances to the nearest decision boundary."""
+    {draw, top_p, min_p, top_k, greedy, order} distances to the nearest decision boundary."""
     v = _c(logits, np.float64)
     h = _c(list(hist) if len(hist) else [0], np.int32)
     s = _Samp(mode, top_k, temperature, top_p, min_p, rep_penalty, ORDERS.get(order, order))
-    m = np.zeros(5, np.float64)
+    m = np.zeros(6, np.float64)
     i = lib().orc_sample_chain(_ptr(v), v.size, ctypes.byref(s), _ptr(h), len(hist), float(u), _ptr(m))
-    return i, dict(zip(("draw", "top_p", "min_p", "top_k", "greedy"), m.tolist()))
+    return i, dict(zip(("draw", "top_p", "min_p", "top_k", "greedy", "order"), m.tolist()))
 
 
 # ---- models -----------------------------------------------------------------------------------

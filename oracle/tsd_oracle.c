@@ -401,15 +401,18 @@ static void proc_min_p(double* v, int n, double min_p, double* p, double* margin
     }
 }
 
-/* margins (optional, 5 values): [0] distance of u from the nearest cumulative boundary of the
+/* margins (optional, 6 values): [0] distance of u from the nearest cumulative boundary of the
  * draw, relative to the total mass; [1] top-p: smallest |preceding mass - p|; [2] min-p:
  * smallest |p_i / p_max - min_p|; [3] top-k: gap between the k-th and (k+1)-th value at that
- * stage; [4] greedy: gap between the two largest penalized logits.  Unused ones are +inf. */
+ * stage; [4] greedy: gap between the two largest penalized logits; [5] order: gap between the
+ * drawn entry's final value and its neighbours' in the walk (two nearly equal values may be
+ * walked in the other order by a computation that rounds differently, which moves the
+ * crossing to the other id).  Unused ones are +inf. */
 int orc_sample_chain(const double* logits, int n, const orc_sampling* s, const int32_t* hist, int n_hist,
                      double u, double* margins)
 {
     if (n <= 0) return -1;
-    double mg[5] = {INFINITY, INFINITY, INFINITY, INFINITY, INFINITY};
+    double mg[6] = {INFINITY, INFINITY, INFINITY, INFINITY, INFINITY, INFINITY};
     double* v = (double*)malloc(sizeof(double) * (size_t)n);
     double* p = (double*)malloc(sizeof(double) * (size_t)n);
     char* seen = (char*)calloc((size_t)n, 1);
@@ -445,12 +448,15 @@ int orc_sample_chain(const double* logits, int n, const orc_sampling* s, const i
         double thr = u * total, c = 0.0;
         pick = r[m - 1].i;
         int found = 0;
+        int at = m - 1;
         for (int j = 0; j < m; ++j) {
             c += exp(r[j].v - r[0].v);
             double dist = fabs(c - thr) / total;
             if (dist < mg[0]) mg[0] = dist;
-            if (!found && c > thr) { pick = r[j].i; found = 1; }
+            if (!found && c > thr) { pick = r[j].i; at = j; found = 1; }
         }
+        if (at > 0 && r[at - 1].v - r[at].v < mg[5]) mg[5] = r[at - 1].v - r[at].v;
+        if (at + 1 < m && r[at].v - r[at + 1].v < mg[5]) mg[5] = r[at].v - r[at + 1].v;
     }
     if (margins) memcpy(margins, mg, sizeof(mg));
     free(v); free(p); free(seen); free(r);

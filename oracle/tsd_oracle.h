@@ -80,7 +80,7 @@ void orc_attend(const double* q, const uint16_t* kc, const uint16_t* vc, int n_k
 int  orc_argmax(const double* v, int n);
 int  orc_sample_topk(const double* logits, int n, int k, double temperature, double u);
 /* the sampler chain over logits[n] with the history's token ids (out-of-range ids ignored);
- * margins: NULL or 5 doubles (see tsd_oracle.c) */
+ * margins: NULL or 6 doubles (see tsd_oracle.c) */
 int  orc_sample_chain(const double* logits, int n, const orc_sampling* s, const int32_t* hist,
                       int n_hist, double u, double* margins);
 

@@ -25,7 +25,7 @@ EXPORTS = ["tsd_workspace_bytes", "tsd_model_create", "tsd_prefill", "tsd_step",
            "tsd_n_past", "tsd_model_destroy", "tsd_last_error", "tsd_get_logits", "tsd_get_tokens", "tsd_load_kv",
            "tsd_layer_forward", "tsd_gemv_packed_bytes", "tsd_gemv_pack", "tsd_gemv",
            "tsd_attention_scratch_bytes", "tsd_attention", "tsd_time_kernel", "tsd_synchronize",
-           "tsd_model_info", "tsd_sample_topk", "tsd_gemm_rows_packed_bytes", "tsd_gemm_rows_pack",
+           "tsd_model_info", "tsd_sample_topk", "tsd_sample", "tsd_gemm_rows_packed_bytes", "tsd_gemm_rows_pack",
            "tsd_gemm_rows_scratch_bytes", "tsd_gemm_rows"]
 KERNEL_KINDS = {"qkv": 0, "attn": 1, "oproj": 2, "fc": 3, "down": 4, "head": 5, "step": 6}
 
@@ -46,7 +46,18 @@ class tsd_config(ctypes.Structure):
 
 class tsd_sampling(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("top_k", ctypes.c_int32), ("temperature", ctypes.c_float),
-                ("seed", ctypes.c_uint64)]
+                ("seed", ctypes.c_uint64), ("top_p", ctypes.c_float), ("min_p", ctypes.c_float),
+                ("rep_penalty", ctypes.c_float), ("order", ctypes.c_int32)]
+
+
+ORDERS = {"t3": 0, "mtl": 1}
+
+
+def make_sampling(d: dict) -> tsd_sampling:
+    """tsd_sampling from a dict (missing fields: greedy, every filter off, the T3 order)."""
+    return tsd_sampling(d.get("mode", 0), d.get("top_k", 0), d.get("temperature", 1.0), d.get("seed", 0),
+                        d.get("top_p", 0.0), d.get("min_p", 0.0), d.get("rep_penalty", 0.0),
+                        ORDERS.get(d.get("order", "t3"), d.get("order", 0)))
 
 
 class tsd_tensor(ctypes.Structure):
@@ -89,6 +100,7 @@ def lib():
             "tsd_synchronize": [_P],
             "tsd_model_info": [_P, _P, _P],
             "tsd_sample_topk": [_P, _I, _I, ctypes.c_float, ctypes.c_uint64, _I, _I, _I, _P, _P],
+            "tsd_sample": [_P, _I, ctypes.POINTER(tsd_sampling), _P, _I, _I, _I, _I, _P, _P],
             "tsd_gemm_rows_packed_bytes": [_I, _I, ctypes.POINTER(_SZ)],
             "tsd_gemm_rows_pack": [_P, _SZ, _I, _I, _P, _SZ, _P],
             "tsd_gemm_rows_scratch_bytes": [_I, _I, _I, ctypes.POINTER(_SZ)],
@@ -160,6 +172,13 @@ def tsd_sample_topk(logits, top_k, temperature, seed, row, pos, pss, out, stream
                                  _stream(stream)))
 
 
+def tsd_sample(logits, sampling: dict, hist, row, pos, pss, out, stream=None):
+    """hist: an int32 device tensor of token ids, or None."""
+    s = make_sampling(sampling)
+    _check(lib().tsd_sample(_ptr(logits), logits.numel(), ctypes.byref(s), _ptr(hist),
+                            0 if hist is None else hist.numel(), row, pos, pss, _ptr(out), _stream(stream)))
+
+
 def tsd_gemm_rows_packed_bytes(N, K) -> int:
     out = _SZ()
     _check(lib().tsd_gemm_rows_packed_bytes(N, K, ctypes.byref(out)))
@@ -215,8 +234,7 @@ class Model:
         arr = (tsd_tensor * len(dev))(*[tsd_tensor(t.data_ptr(), t.numel()) for t in dev])
         samp = None
         if sampling is not None:
-            samp = tsd_sampling(sampling.get("mode", 0), sampling.get("top_k", 0),
-                                sampling.get("temperature", 1.0), sampling.get("seed", 0))
+            samp = make_sampling(sampling)
         h = _P()
         torch.cuda.synchronize()
         _check(lib().tsd_model_create(ctypes.byref(self._c), arr, len(dev), _ptr(self.workspace), nbytes,

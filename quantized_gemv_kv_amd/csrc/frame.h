@@ -131,19 +131,24 @@ hipError_t launch_il_to_rows(const float* src, int B, int K, float* dst, hipStre
 struct PickArgs {
     const float* logits;
     int ld_l, n, B;
-    int top_k;
-    float temperature;
+    int draw;            // 0: the greedy argmax; 1: the chain's draw
+    SampChain ch;
     unsigned long long seed;
     int pass;
     const int* posp;
-    int* code;
+    int* code;           // code[b * ld_code]: the row's code, overwritten by the pick
     int ld_code;
+    // the penalty's history and the consumed-token record (null: none): seq[p * B + b] for
+    // p < *posp, then the code this position consumed (code[b * ld_code] before the pick), which
+    // is also written to seq[*posp * B + b]
+    int* seq;
     RowPrep prep;        // prep.src = -1: none
 };
 hipError_t launch_pick(const PickArgs& a, hipStream_t st);
 // y[i] = sum over s < S of part[s * slice + i] for i < n
 hipError_t launch_sum_slices(const float* part, int S, long long slice, float* y, long long n, hipStream_t st);
-// hist[*pos][0..n) = codes[0..n) (n may be 0), then *pos += 1
-hipError_t launch_frame_done(const int* codes, int n, int* hist, int* pos, hipStream_t st);
+// hist[*pos][0..n) = codes[0..n) (n may be 0), with seq: seq[*pos * B + b] = codes[b * C] for
+// b < B (the consumed code 0 of a frame no pick ran on); then *pos += 1
+hipError_t launch_frame_done(const int* codes, int n, int* hist, int* pos, int* seq, int B, int C, hipStream_t st);
 
 }  // namespace tsd

@@ -430,7 +430,8 @@ __global__ __launch_bounds__(256) void k_row_prep(const RowPrep p)
 // ---- the code of every row, then that row's next input ----------------------------------------
 __global__ __launch_bounds__(256) void k_pick(const PickArgs a)
 {
-    extern __shared__ uint32_t keys[];   // top-k only: the row's logits as ordered keys
+    extern __shared__ uint32_t keys[];   // draw only: the row's logits as ordered keys, then the
+                                         // history's bit set
     __shared__ samp::Scratch S;
     __shared__ unsigned long long bk[4];
     __shared__ float red[4];
@@ -438,11 +439,17 @@ __global__ __launch_bounds__(256) void k_pick(const PickArgs a)
     __shared__ int picked;
     const int b = blockIdx.x, t = threadIdx.x;
     const float* l = a.logits + (size_t)b * a.ld_l;
-    if (a.top_k > 0) {
-        for (int i = t; i < a.n; i += 256) keys[i] = float_order_key(l[i]);
+    const int pos = *a.posp;
+    const int cur = a.seq ? a.code[(size_t)b * a.ld_code] : -1;   // read before the pick overwrites it
+    if (a.draw) {
+        uint32_t* seen = keys + a.n;
+        const bool pen = a.seq && a.ch.penalty != 1.f;
+        if (pen) samp::build_seen<256>(seen, a.n, a.seq + b, a.B, pos, cur);
+        const uint32_t* sp = pen ? seen : nullptr;
+        for (int i = t; i < a.n; i += 256) keys[i] = samp::chain_key(l[i], i, a.ch, sp);
         __syncthreads();
-        const float u = samp::uniform24(a.seed, (uint32_t)b, (uint32_t)*a.posp, (uint32_t)a.pass);
-        const int id = samp::topk_draw<256>(keys, a.n, a.top_k, a.temperature, u, S);
+        const float u = samp::uniform24(a.seed, (uint32_t)b, (uint32_t)pos, (uint32_t)a.pass);
+        const int id = samp::chain_draw<256>(keys, a.n, a.ch, u, S, sp);
         if (t == 0) picked = id;
     } else {
         unsigned long long best = 0ull;
@@ -461,7 +468,10 @@ __global__ __launch_bounds__(256) void k_pick(const PickArgs a)
     }
     __syncthreads();
     const int id = picked;
-    if (t == 0) a.code[(size_t)b * a.ld_code] = id;
+    if (t == 0) {
+        if (a.seq) a.seq[(size_t)pos * a.B + b] = cur;
+        a.code[(size_t)b * a.ld_code] = id;
+    }
     if (a.prep.src >= 0) row_prep(a.prep, b, id, red, ids);
 }
 
@@ -484,10 +494,12 @@ __global__ void k_sum_slices(const float* __restrict__ part, int S, long long sl
 }
 
 // the frame's codes appended to the history at *pos, and the position advanced
-__global__ void k_frame_done(const int* __restrict__ codes, int n, int* hist, int* pos)
+__global__ void k_frame_done(const int* __restrict__ codes, int n, int* hist, int* pos, int* seq, int B, int C)
 {
     const int p = *pos;
     for (int i = threadIdx.x; i < n; i += blockDim.x) hist[(size_t)p * n + i] = codes[i];
+    if (seq)
+        for (int b = threadIdx.x; b < B; b += blockDim.x) seq[(size_t)p * B + b] = codes[(size_t)b * C];
     __syncthreads();
     if (threadIdx.x == 0) *pos = p + 1;
 }
@@ -564,8 +576,8 @@ hipError_t launch_pick(const PickArgs& a, hipStream_t st)
 {
     if (a.n < 1 || a.B < 1 || a.B > MM_ROWS || (a.prep.src >= 0 && (!row_prep_ok(a.prep) || a.prep.B != a.B)))
         return hipErrorInvalidValue;
-    if (a.top_k > 0 && (!topk_supported(a.n, a.top_k) || !a.posp)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_pick, dim3(a.B), dim3(256), a.top_k > 0 ? (size_t)a.n * 4 : 0, st, a);
+    if (!a.posp || (a.draw && (!sample_supported(a.n, a.ch.k) || !(a.ch.temperature > 0.f)))) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_pick, dim3(a.B), dim3(256), a.draw ? sample_lds_bytes(a.n) : 0, st, a);
     return hipGetLastError();
 }
 
@@ -592,9 +604,9 @@ hipError_t launch_sum_slices(const float* part, int S, long long slice, float* y
     return hipGetLastError();
 }
 
-hipError_t launch_frame_done(const int* codes, int n, int* hist, int* pos, hipStream_t st)
+hipError_t launch_frame_done(const int* codes, int n, int* hist, int* pos, int* seq, int B, int C, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_frame_done, dim3(1), dim3(256), 0, st, codes, n, hist, pos);
+    hipLaunchKernelGGL(k_frame_done, dim3(1), dim3(256), 0, st, codes, n, hist, pos, seq, B, C);
     return hipGetLastError();
 }
 

@@ -335,7 +335,7 @@ int gemv_rows_per_block(int fmt, int K, int) { return rows_per_block_impl(fmt, K
 
 namespace {
 __global__ __launch_bounds__(256) void k_argmax_finalize(const unsigned long long* __restrict__ best, int n, int* tok,
-                                                         int* hist, int hist_stride, int* pos)
+                                                         int* hist, int* seq, int hist_stride, int* pos)
 {
     __shared__ unsigned long long bk[NWAVE];
     unsigned long long m = 0ull;
@@ -348,6 +348,7 @@ __global__ __launch_bounds__(256) void k_argmax_finalize(const unsigned long lon
         for (int i = 1; i < NWAVE; ++i) b = bk[i] > b ? bk[i] : b;
         const int id = (int)(0xFFFFFFFFu - (uint32_t)(b & 0xFFFFFFFFull));
         const int p = *pos;
+        if (seq) seq[(size_t)p * hist_stride] = *tok;
         *tok = id;
         if (hist) hist[(size_t)p * hist_stride] = id;
         *pos = p + 1;
@@ -355,10 +356,10 @@ __global__ __launch_bounds__(256) void k_argmax_finalize(const unsigned long lon
 }
 }  // namespace
 
-hipError_t launch_argmax_finalize(const unsigned long long* best, int n, int* tok, int* hist, int hist_stride, int* pos,
-                                  hipStream_t st)
+hipError_t launch_argmax_finalize(const unsigned long long* best, int n, int* tok, int* hist, int* seq, int hist_stride,
+                                  int* pos, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_argmax_finalize, dim3(1), dim3(WG), 0, st, best, n, tok, hist, hist_stride, pos);
+    hipLaunchKernelGGL(k_argmax_finalize, dim3(1), dim3(WG), 0, st, best, n, tok, hist, seq, hist_stride, pos);
     return hipGetLastError();
 }
 

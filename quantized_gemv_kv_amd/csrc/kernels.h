@@ -117,7 +117,9 @@ hipError_t launch_attention_merge(const AttnArgs& a, int n_keys, hipStream_t st)
 // ---- sampler finalize --------------------------------------------------------------------------
 // greedy: reduce the head's per-workgroup keys [n], publish the id into tok, append it to the
 // history at the current position and advance the position (one workgroup)
-hipError_t launch_argmax_finalize(const unsigned long long* best, int n, int* tok, int* hist, int hist_stride, int* pos,
+// seq: when set, seq[*pos * hist_stride] = the token consumed at this position (*tok before it is
+// overwritten by the id)
+hipError_t launch_argmax_finalize(const unsigned long long* best, int n, int* tok, int* hist, int* seq, int hist_stride, int* pos,
                                   hipStream_t st);
 
 // ---- persistent decode step (step.hip) ---------------------------------------------------------
@@ -129,6 +131,18 @@ struct StepLayer {
     const float *n1g, *n1b, *n2g, *n2b;       // norm gains / LayerNorm biases (null for RMSNorm)
     const float *bqkv, *bo, *bfc, *bdown;     // linear biases (null without)
     __half *kc, *vc;                          // this layer's cache [Hkv][n_ctx][hd]
+};
+// the sampler chain's parameters (sampler.h): temperature, k largest, nucleus, min-p, repetition
+// penalty, and which of the two orders runs
+constexpr int SAMP_ORDER_T3 = 0, SAMP_ORDER_MTL = 1;
+struct SampChain {
+    float temperature;   // > 0
+    int k;               // 1 <= k <= min(vocabulary, 1024)
+    float top_p;         // filters when 0 < top_p < 1
+    float min_p;         // filters when 0 < min_p < 1 (SAMP_ORDER_MTL only)
+    float penalty;       // applies when != 1
+    int order;           // SAMP_ORDER_T3: temperature, top-k, top-p, penalty; SAMP_ORDER_MTL: penalty,
+                         // temperature, min-p, top-p, top-k
 };
 struct StepArgs {
     StepLayer L0;                             // layer 0; layer l is layer 0 moved by l strides
@@ -142,6 +156,7 @@ struct StepArgs {
     PackedMat head;
     const float2* rope;                       // [n_ctx][hd/2] (cos, sin), Llama
     int *pos, *tok, *hist;                    // step state (read at launch start, advanced at its end)
+    int* seq;                                 // [n_ctx] the token consumed at each position
     uint32_t* ctr;                            // launches completed: the epoch base
     uint32_t* abort_word;                     // sticky: a wait gave up
     float* logits;                            // [vocab]
@@ -149,24 +164,43 @@ struct StepArgs {
     // (residual stream), MLP hidden, layer output (residual stream), per-workgroup argmax keys
     uint64_t *x_qkv, *x_part, *x_attn, *x_h, *x_out, *x_best;
     long long spin_limit;                     // ticks of the 100 MHz clock a wait may take
-    // sampler: mode 0 greedy, 1 top-k (the head also publishes its logits as exchange words)
-    int samp_mode, top_k;
-    float temperature;
+    // sampler: mode 0 the greedy argmax of the head's per-workgroup keys, 1 the chain's draw on
+    // workgroup 0 (the head then also publishes its logits as exchange words)
+    int samp_mode;
+    SampChain chain;
     unsigned long long seed;
-    uint64_t* x_logit;                        // [vocab] exchange words of the logits (top-k)
+    uint64_t* x_logit;                        // [vocab] exchange words of the logits (draw)
 };
 // the step kernel for a shape, or null when the shape has no instantiation
 const void* step_kernel_for(int fmt, int arch_llama, int d, int h, int hk, int hd, int ff, int vocab);
 // d_args: the arguments in device memory (read by every phase)
 hipError_t launch_step(const void* kernel, const StepArgs* d_args, int n_wg, hipStream_t st);
 
-// ---- top-k sampler (sampler.hip, sampler.h) ----------------------------------------------------
-// the id drawn from logits[0..n): k largest of logits / temperature, counter (pos, row, pass);
-// pos is *posp when posp is set (then the id is also written to hist[pos * hist_stride] and *posp
-// advanced), else pos_value.  k must be 1..min(n, 1024).
-bool topk_supported(int n, int k);
-hipError_t launch_topk(const float* logits, int n, int k, float temperature, unsigned long long seed, int row, int pass,
-                       int* posp, int pos_value, int* out, int* hist, int hist_stride, hipStream_t st);
+// ---- sampler chain (sampler.hip, sampler.h) --------------------------------------------------
+// the id drawn from logits[0..n) by the chain ch with the uniform of counter (pos, row, pass); pos
+// is *posp when posp is set (then the id is also written to hist[pos * hist_stride], the consumed
+// token *cur to seq_out[pos * seq_stride], and *posp advanced), else pos_value.  The penalty's
+// history is seq[p * seq_stride] for p < n_seq (n_seq < 0: p < pos), then *cur when cur is set.
+struct SampleArgs {
+    const float* logits;
+    int n;
+    SampChain ch;
+    unsigned long long seed;
+    int row, pass;
+    int* posp;
+    int pos_value;
+    int* out;
+    int* hist;
+    int hist_stride;
+    const int* seq;
+    long long seq_stride;
+    int n_seq;
+    const int* cur;
+    int* seq_out;
+};
+bool sample_supported(int n, int k);
+size_t sample_lds_bytes(int n);
+hipError_t launch_sample(const SampleArgs& a, hipStream_t st);
 
 // ---- the batched path's row-interleaved layouts (frame.h has the rest) ---------------------------
 // fp32 rows x[b][k] at il_x(b, k); fp16 GEMM operands at il_act(b, k); MM_ROWS rows each

@@ -142,7 +142,12 @@ struct tsd_model {
     // timing probes: events around every launch of one kernel kind
     std::vector<hipEvent_t> probe_ev[tsd::TSD_KERNEL_KINDS];
     int n_past = 0;
-    int top_k = 0;                    // effective k of the top-k sampler
+    int top_k = 0;                    // effective k of the main head's draw
+    // the sampler chain as the kernels run it: the main head (token, or Talker code 0) and the
+    // code predictor's heads (no repetition penalty); draw 0 = the greedy argmax
+    tsd::SampChain chain{}, cp_chain{};
+    int draw = 0, cp_draw = 0;
+    int* seq = nullptr;               // [n_ctx][batch] the token (code 0) consumed at each position
     std::string err;
 };
 

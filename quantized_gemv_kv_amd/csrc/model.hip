@@ -129,6 +129,7 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     const int head_blocks = (c->vocab + gemv_rows_per_block(f, d, EPI_HEAD_ARGMAX) - 1) / gemv_rows_per_block(f, d, EPI_HEAD_ARGMAX);
     unsigned long long* best = (unsigned long long*)P.take(sizeof(unsigned long long) * B * tpp * head_blocks);
     int* hist = (int*)P.take(sizeof(int) * (size_t)c->n_ctx * B * tpp);
+    int* seq = (int*)P.take(sizeof(int) * (size_t)c->n_ctx * B);
     // activations
     float* x = (float*)P.take(sizeof(float) * B * d);
     float* qkv = (float*)P.take(sizeof(float) * B * qkv_rows);
@@ -178,7 +179,7 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     uint64_t* xbuf = (uint64_t*)P.take(sizeof(uint64_t) * xtot);
     if (m && base) {
         m->pos = pos; m->dbg_pos = pos + 1; m->tok = tok; m->best = best;
-        m->hist = hist; m->x = x; m->qkv = qkv; m->attn = attn; m->h = h; m->logits = logits; m->part = part;
+        m->hist = hist; m->seq = seq; m->x = x; m->qkv = qkv; m->attn = attn; m->h = h; m->logits = logits; m->part = part;
         m->rope = rope; m->rope_rows = c->n_ctx; m->emb[0] = emb0; m->emb_rows[0] = c->vocab; m->wpe = wpe; m->L = Ls; m->nfg = nfg; m->nfb = nfb;
         m->head = head; m->kc = kc; m->vc = vc; m->kv_layer_elems = kv_layer; m->tpp = tpp; m->vmax = vmax;
         m->qkv_rows = qkv_rows;
@@ -331,12 +332,26 @@ hipError_t enqueue_step(tsd_model* m, hipStream_t st, Probe* pr = nullptr)
     Bracket br(pr, KIND_HEAD, st);
     hipError_t e = launch_gemv(c.wfmt, c.arch == TSD_ARCH_GPT2 ? PRO_LN : PRO_RMS, EPI_HEAD_ARGMAX, m->head, ph, eh, st);
     if (e != hipSuccess) return e;
-    if (m->samp.mode == 1)
-        return launch_topk(m->logits, c.vocab, m->top_k, m->samp.temperature, m->samp.seed, 0, 0, m->pos, 0, m->tok,
-                           m->hist, c.batch * m->tpp, st);
+    if (m->draw) {
+        SampleArgs s{};
+        s.logits = m->logits;
+        s.n = c.vocab;
+        s.ch = m->chain;
+        s.seed = m->samp.seed;
+        s.posp = m->pos;
+        s.out = m->tok;
+        s.hist = m->hist;
+        s.hist_stride = c.batch * m->tpp;
+        s.seq = m->seq;
+        s.seq_stride = c.batch;
+        s.n_seq = -1;
+        s.cur = m->tok;
+        s.seq_out = m->seq;
+        return launch_sample(s, st);
+    }
     const int nblk = (c.vocab + gemv_rows_per_block(c.wfmt, c.d_model, EPI_HEAD_ARGMAX) - 1) /
                      gemv_rows_per_block(c.wfmt, c.d_model, EPI_HEAD_ARGMAX);
-    return launch_argmax_finalize(m->best, nblk, m->tok, m->hist, c.batch * m->tpp, m->pos, st);
+    return launch_argmax_finalize(m->best, nblk, m->tok, m->hist, m->seq, c.batch * m->tpp, m->pos, st);
 }
 
 tsd_status pack_weights(tsd_model* m, const tsd_tensor* w)
@@ -446,12 +461,11 @@ tsd_status setup_step(tsd_model* m)
     a.max_split = attn_max_split(c.n_ctx);
     a.eps = c.norm_eps;
     a.emb = m->emb[0]; a.wpe = m->wpe; a.nfg = m->nfg; a.nfb = m->nfb; a.head = m->head; a.rope = m->rope;
-    a.pos = m->pos; a.tok = m->tok; a.hist = m->hist; a.ctr = m->ctl; a.abort_word = m->ctl + 1;
+    a.pos = m->pos; a.tok = m->tok; a.hist = m->hist; a.seq = m->seq; a.ctr = m->ctl; a.abort_word = m->ctl + 1;
     a.logits = m->logits;
     a.spin_limit = STEP_SPIN_LIMIT;
-    a.samp_mode = m->samp.mode;
-    a.top_k = m->top_k;
-    a.temperature = m->samp.temperature;
+    a.samp_mode = m->draw;
+    a.chain = m->chain;
     a.seed = m->samp.seed;
     const uint64_t nph = 5ull * c.n_layer + 1ull;
     m->max_launches = (0xFFFFFFF0ull - nph) / nph;
@@ -477,6 +491,7 @@ tsd_status init_state(tsd_model* m)
     HIP_TRY(m, launch_fill_i32(m->pos, 0, 4, st), "init");
     HIP_TRY(m, launch_fill_i32(m->tok, 0, c.batch * m->tpp, st), "init");
     HIP_TRY(m, launch_fill_i32(m->hist, 0, c.n_ctx * c.batch * m->tpp, st), "init");
+    HIP_TRY(m, launch_fill_i32(m->seq, -1, c.n_ctx * c.batch, st), "init");
     HIP_TRY(m, launch_fill_f32(m->logits, 0.f, (size_t)c.batch * m->tpp * m->vmax, st), "init");
     // RoPE table in fp64 on the host: angle = pos * theta^(-2i/hd)
     const int half = c.head_dim / 2;
@@ -547,6 +562,47 @@ tsd_status tsd_workspace_bytes(const tsd_config* cfg, size_t* out)
     return TSD_OK;
 }
 
+// the sampling parameters' ranges: mode 0 or 1; a positive finite temperature (mode 1); top_p in
+// [0, 1] (0 and 1 off); min_p in [0, 1), only in the multilingual order; rep_penalty 0 (off) or
+// positive and finite; order T3 or MTL
+tsd_status check_sampling(const tsd_sampling* s, std::string& msg)
+{
+    if (s->mode != 0 && s->mode != 1) return msg = "sampling mode must be 0 (greedy) or 1 (draw)", TSD_ERR_INVALID_ARGUMENT;
+    if (s->mode == 1 && (!(s->temperature > 0.f) || !std::isfinite(s->temperature)))
+        return msg = "temperature must be positive and finite", TSD_ERR_INVALID_ARGUMENT;
+    if (!(s->top_p >= 0.f && s->top_p <= 1.f)) return msg = "top_p must lie in [0, 1]", TSD_ERR_INVALID_ARGUMENT;
+    if (!(s->min_p >= 0.f && s->min_p < 1.f)) return msg = "min_p must lie in [0, 1)", TSD_ERR_INVALID_ARGUMENT;
+    if (!(s->rep_penalty >= 0.f) || !std::isfinite(s->rep_penalty))
+        return msg = "rep_penalty must be 0 (off) or positive and finite", TSD_ERR_INVALID_ARGUMENT;
+    if (s->order != TSD_ORDER_T3 && s->order != TSD_ORDER_MTL) return msg = "unknown sampler order", TSD_ERR_INVALID_ARGUMENT;
+    if (s->min_p > 0.f && s->order != TSD_ORDER_MTL)
+        return msg = "min_p is a step of the multilingual order (TSD_ORDER_MTL)", TSD_ERR_INVALID_ARGUMENT;
+    return TSD_OK;
+}
+
+// the chain the kernels run for a head of n ids (with_penalty: the head the penalty covers);
+// greedy with a penalty is the draw of the single largest penalized logit
+bool chain_of(const tsd_sampling* s, int n, bool with_penalty, SampChain* ch, int* draw)
+{
+    const bool pen = with_penalty && s->rep_penalty > 0.f && s->rep_penalty != 1.f;
+    *ch = SampChain{1.f, 1, 0.f, 0.f, 1.f, SAMP_ORDER_MTL};
+    *draw = 0;
+    if (s->mode == 0) {
+        if (!pen) return true;
+        ch->penalty = s->rep_penalty;
+        *draw = 1;
+        return sample_supported(n, 1);
+    }
+    ch->temperature = s->temperature;
+    ch->k = (s->top_k <= 0 || s->top_k > n) ? n : s->top_k;
+    ch->top_p = s->top_p;
+    ch->min_p = s->min_p;
+    ch->penalty = pen ? s->rep_penalty : 1.f;
+    ch->order = s->order == TSD_ORDER_MTL ? SAMP_ORDER_MTL : SAMP_ORDER_T3;
+    *draw = 1;
+    return sample_supported(n, ch->k);
+}
+
 tsd_status tsd_model_create(const tsd_config* cfg, const tsd_tensor* weights, int n_weights, void* d_ws,
                             size_t ws_bytes, void* stream, const tsd_sampling* sampling, tsd_model** out)
 {
@@ -567,25 +623,26 @@ tsd_status tsd_model_create(const tsd_config* cfg, const tsd_tensor* weights, in
         if (!weights[i].ptr || weights[i].bytes != sz[i])
             return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "weight " + std::to_string(i) + ": " +
                         std::to_string(weights[i].bytes) + " bytes, expected " + std::to_string(sz[i]));
-    int top_k = 0;
-    if (sampling && sampling->mode != 0) {
-        if (sampling->mode != 1) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "sampling mode must be 0 (greedy) or 1 (top-k)");
-        if (!(sampling->temperature > 0.f) || !std::isfinite(sampling->temperature))
-            return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "temperature must be positive and finite");
-        top_k = (sampling->top_k <= 0 || sampling->top_k > cfg->vocab) ? cfg->vocab : sampling->top_k;
-        if (!topk_supported(cfg->vocab, top_k))
-            return fail(nullptr, TSD_ERR_UNSUPPORTED, "top-k draws support k <= 1024 and vocabularies up to 12288");
-        if (cfg->arch == TSD_ARCH_TALKER_CP) {
-            const int kc = (sampling->top_k <= 0 || sampling->top_k > cfg->cp_vocab) ? cfg->cp_vocab : sampling->top_k;
-            if (!topk_supported(cfg->cp_vocab, kc))
-                return fail(nullptr, TSD_ERR_UNSUPPORTED, "top-k draws support k <= 1024 and vocabularies up to 12288");
-        }
-    }
+    tsd_sampling sv{};
+    if (sampling) sv = *sampling;
+    std::string smsg;
+    s = check_sampling(&sv, smsg);
+    if (s != TSD_OK) return fail(nullptr, s, smsg);
+    SampChain ch{}, cch{};
+    int draw = 0, cdraw = 0;
+    if (!chain_of(&sv, cfg->vocab, true, &ch, &draw))
+        return fail(nullptr, TSD_ERR_UNSUPPORTED, "draws support k <= 1024 and vocabularies up to 12288");
+    if (cfg->arch == TSD_ARCH_TALKER_CP && !chain_of(&sv, cfg->cp_vocab, false, &cch, &cdraw))
+        return fail(nullptr, TSD_ERR_UNSUPPORTED, "draws support k <= 1024 and vocabularies up to 12288");
     tsd_model* m = new (std::nothrow) tsd_model();
     if (!m) return fail(nullptr, TSD_ERR_OUT_OF_MEMORY, "host allocation");
     m->c = *cfg;
-    if (sampling) m->samp = *sampling;
-    m->top_k = top_k;
+    m->samp = sv;
+    m->chain = ch;
+    m->cp_chain = cch;
+    m->draw = draw;
+    m->cp_draw = cdraw;
+    m->top_k = ch.k;
     m->st = (hipStream_t)stream;
     m->ws = (uint8_t*)d_ws;
     m->ws_bytes = ws_bytes;
@@ -692,6 +749,7 @@ tsd_status tsd_reset(tsd_model* m)
     if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
     HIP_TRY(m, launch_fill_i32(m->pos, 0, 1, m->st), "reset");
     HIP_TRY(m, launch_fill_i32(m->hist, 0, m->c.n_ctx * m->c.batch * m->tpp, m->st), "reset");
+    HIP_TRY(m, launch_fill_i32(m->seq, -1, m->c.n_ctx * m->c.batch, m->st), "reset");
     if (m->step_fn) HIP_TRY(m, reset_exchange(m), "reset");
     m->n_past = 0;
     return TSD_OK;
@@ -742,6 +800,7 @@ tsd_status tsd_load_kv(tsd_model* m, const uint16_t* d_k, const uint16_t* d_v, i
         HIP_TRY(m, hipMemcpy2DAsync(m->vc, dp, d_v, w, w, rows, hipMemcpyDeviceToDevice, m->st), "load v");
     }
     HIP_TRY(m, launch_fill_i32(m->pos, n_pos, 1, m->st), "set position");
+    HIP_TRY(m, launch_fill_i32(m->seq, -1, m->c.n_ctx * m->c.batch, m->st), "load kv");   // tokens unknown
     m->n_past = n_pos;
     return TSD_OK;
 }
@@ -925,11 +984,41 @@ tsd_status tsd_sample_topk(const float* d_logits, int n, int top_k, float temper
     if (n <= 0 || row < 0 || pos < 0 || pass < 0) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "bad size or counter");
     if (!(temperature > 0.f) || !std::isfinite(temperature))
         return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "temperature must be positive and finite");
-    const int k = (top_k <= 0 || top_k > n) ? n : top_k;
-    if (!topk_supported(n, k)) return fail(nullptr, TSD_ERR_UNSUPPORTED, "k <= 1024 and n <= 12288");
-    hipError_t e = launch_topk(d_logits, n, k, temperature, seed, row, pass, nullptr, pos, d_out, nullptr, 0,
-                               (hipStream_t)stream);
-    return e == hipSuccess ? TSD_OK : hip_fail(nullptr, e, "top-k");
+    tsd_sampling sv{};
+    sv.mode = 1;
+    sv.top_k = top_k;
+    sv.temperature = temperature;
+    sv.seed = seed;
+    return tsd_sample(d_logits, n, &sv, nullptr, 0, row, pos, pass, d_out, stream);
+}
+
+tsd_status tsd_sample(const float* d_logits, int n, const tsd_sampling* s, const int32_t* d_hist, int n_hist, int row,
+                      int pos, int pass, int32_t* d_out, void* stream)
+{
+    if (!d_logits || !d_out || !s) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null argument");
+    if (n <= 0 || row < 0 || pos < 0 || pass < 0) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "bad size or counter");
+    if (n_hist < 0 || (n_hist > 0 && !d_hist)) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "bad history");
+    std::string msg;
+    tsd_status st = check_sampling(s, msg);
+    if (st != TSD_OK) return fail(nullptr, st, msg);
+    SampChain ch{};
+    int draw = 0;
+    if (!chain_of(s, n, true, &ch, &draw)) return fail(nullptr, TSD_ERR_UNSUPPORTED, "k <= 1024 and n <= 12288");
+    if (!draw) ch = SampChain{1.f, 1, 0.f, 0.f, 1.f, SAMP_ORDER_T3};   // greedy: the largest logit
+    SampleArgs a{};
+    a.logits = d_logits;
+    a.n = n;
+    a.ch = ch;
+    a.seed = s->seed;
+    a.row = row;
+    a.pass = pass;
+    a.pos_value = pos;
+    a.out = d_out;
+    a.seq = d_hist;
+    a.seq_stride = 1;
+    a.n_seq = n_hist;
+    hipError_t e = launch_sample(a, (hipStream_t)stream);
+    return e == hipSuccess ? TSD_OK : hip_fail(nullptr, e, "sample");
 }
 
 tsd_status tsd_attention_scratch_bytes(int B, int H, int n_ctx, int hd, size_t* out)

@@ -1,23 +1,32 @@
-// sampler.h — the top-k draw of the decode step, as block-wide device code (internal).
+// sampler.h — the sampler chain's draw, as block-wide device code (internal).
 //
 // What it computes ("Chatterbox -> ggml Port: Development Journal", §3.2 and §3.9: temperature,
-// then top-k, in that order; "Every Frame Is a Memory Read", §5.2: the random state stays on the
-// device): keep the k largest of logits / T (equal logits: the lower index first), take
-// z_r = exp(l_r / T - l_0 / T) in descending order, and return the first index whose running sum
-// exceeds u * sum(z), where u is the top 24 bits of the first word of Philox4x64-10 (Salmon,
-// Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011) with key
-// (seed, 0) and counter (position, row, pass, 0).
+// then top-k, then top-p, then the repetition penalty; §3.19: the multilingual order, penalty,
+// temperature, min-p, top-p, top-k; "Every Frame Is a Memory Read", §5.2 and §5.5: the random
+// state and the penalty's history stay on the device):
+//   * the penalty divides a positive logit by theta and multiplies a negative one, for every id
+//     in the row's history (a bit set);
+//   * top-k keeps the k largest (equal values: the lower index first); top-p keeps, in
+//     descending order, every survivor whose preceding mass is below p; min-p keeps the
+//     survivors whose probability is at least min_p times the largest;
+//   * the draw takes z_r = exp(v_r - v_0) of the final values in descending order and returns
+//     the first index whose running sum exceeds u * sum(z), where u is the top 24 bits of the
+//     first word of Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+//     easy as 1, 2, 3", SC 2011) with key (seed, 0) and counter (position, row, pass, 0).
 //
-// How, on one workgroup: logits arrive as monotone 32-bit keys in LDS; a four-pass radix select
-// (8-bit digits, most significant first, LDS histograms) finds the k-th largest key; the
-// survivors are gathered as 64-bit (key, ~index) words — the same ordering as the greedy
-// argmax — bitonic-sorted in descending order, and an inclusive scan of their weights finds the
-// crossing.
+// How, on one workgroup: logits arrive as monotone 32-bit keys in LDS (penalized first in the
+// multilingual order); a four-pass radix select (8-bit digits, most significant first, LDS
+// histograms) finds the k-th largest key; the survivors are gathered as 64-bit (key, ~index)
+// words, the same ordering as the greedy argmax, and bitonic-sorted in descending order; one
+// scan of their weights gives the masses the top-p and min-p cuts compare against (in the
+// multilingual order top-p is measured against the whole vocabulary's mass, a block sum);
+// after a penalty that comes last the survivors are re-keyed and sorted again; a second scan
+// finds the crossing.
 #pragma once
 
 #include <math.h>
 
-#include "common.h"
+#include "kernels.h"
 
 namespace tsd {
 namespace samp {
@@ -103,13 +112,77 @@ __device__ __forceinline__ float block_scan_f32(float v, float* buf)
     return r;
 }
 
-// The draw over keys[0..n) (LDS; float_order_key of the logits), 1 <= k <= min(n, KMAX).
-// Every thread of the (NT = 256) workgroup calls it; every thread gets the index.
+// the chain's parameters (kernels.h)
+constexpr int ORDER_T3 = SAMP_ORDER_T3, ORDER_MTL = SAMP_ORDER_MTL;
+using Chain = SampChain;
+
+__device__ __forceinline__ float penalize(float l, float theta) { return l < 0.f ? l * theta : l / theta; }
+__device__ __forceinline__ bool seen_bit(const uint32_t* seen, int i) { return (seen[i >> 5] >> (i & 31)) & 1u; }
+
+// the history's ids as a bit set over [0, n) in LDS: entries hist[0], hist[stride], ...,
+// hist[(count-1)*stride], then cur; ids outside [0, n) are ignored
 template <int NT>
-__device__ int topk_draw(const uint32_t* keys, int n, int k, float temperature, float u, Scratch& S)
+__device__ void build_seen(uint32_t* seen, int n, const int* hist, long long stride, int count, int cur)
+{
+    const int nw = (n + 31) >> 5;
+    for (int i = threadIdx.x; i < nw; i += NT) seen[i] = 0u;
+    __syncthreads();
+    for (int p = threadIdx.x; p <= count; p += NT) {
+        const int id = p < count ? hist[(long long)p * stride] : cur;
+        if ((unsigned)id < (unsigned)n) atomicOr(&seen[id >> 5], 1u << (id & 31));
+    }
+    __syncthreads();
+}
+
+// the key of logit l of id i, penalized first when the order asks for it
+__device__ __forceinline__ uint32_t chain_key(float l, int i, const Chain& ch, const uint32_t* seen)
+{
+    if (seen && ch.order == ORDER_MTL && seen_bit(seen, i)) l = penalize(l, ch.penalty);
+    return float_order_key(l);
+}
+
+template <int NT>
+__device__ __forceinline__ float block_sum_f32(float v, float* buf)
+{
+    v = wave_sum(v);
+    if ((threadIdx.x & 63) == 0) buf[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = 0.f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) r += buf[w];
+    __syncthreads();
+    return r;
+}
+
+// bitonic sort of S.cand[0..P) in descending order (P a power of two)
+template <int NT>
+__device__ __forceinline__ void sort_desc(unsigned long long* cand, int P)
+{
+    const int t = threadIdx.x;
+    for (int size = 2; size <= P; size <<= 1)
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = t; i < P / 2; i += NT) {
+                const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
+                const bool desc = (lo & size) == 0;
+                const unsigned long long a = cand[lo], b = cand[hi];
+                if ((a < b) == desc) {
+                    cand[lo] = b;
+                    cand[hi] = a;
+                }
+            }
+            __syncthreads();
+        }
+}
+
+// The chain's draw over keys[0..n) (LDS, chain_key of the logits); seen: the history's bit set
+// in LDS, or null (no penalty).  Every thread of the (NT = 256) workgroup calls it; every thread
+// gets the index.
+template <int NT>
+__device__ int chain_draw(const uint32_t* keys, int n, const Chain& ch, float u, Scratch& S, const uint32_t* seen)
 {
     static_assert(NT == 256, "one histogram bin per thread");
     const int t = threadIdx.x;
+    const int k = ch.k;
     const int per = (n + NT - 1) / NT;            // thread t owns elements [t*per, t*per + per)
     const int i0 = t * per, i1 = min(n, i0 + per);
 
@@ -168,40 +241,97 @@ __device__ int topk_draw(const uint32_t* keys, int n, int k, float temperature, 
     __syncthreads();
 
     // 3. bitonic sort, descending
-    for (int size = 2; size <= P; size <<= 1)
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = t; i < P / 2; i += NT) {
-                const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
-                const bool desc = (lo & size) == 0;
-                const unsigned long long a = S.cand[lo], b = S.cand[hi];
-                if ((a < b) == desc) {
-                    S.cand[lo] = b;
-                    S.cand[hi] = a;
-                }
-            }
-            __syncthreads();
-        }
+    sort_desc<NT>(S.cand, P);
 
-    // 4. weights in descending order, their running sum, the crossing
-    const float l0 = key_to_float((uint32_t)(S.cand[0] >> 32)) / temperature;
+    // 4. weights of the survivors (values / T, descending) and the cuts
+    const float temp = ch.temperature;
+    const float l0 = key_to_float((uint32_t)(S.cand[0] >> 32)) / temp;
     const int per_r = P / NT > 0 ? P / NT : 1;   // thread t owns ranks [t*per_r, t*per_r + per_r)
+    const bool mtl = ch.order == ORDER_MTL;
+    const bool use_p = ch.top_p > 0.f && ch.top_p < 1.f, use_min = mtl && ch.min_p > 0.f && ch.min_p < 1.f;
+    int L = k;
+    if (use_p || use_min) {
+        float loc = 0.f;
+        for (int q = 0; q < per_r; ++q) {
+            const int rr = t * per_r + q;
+            float zv = 0.f;
+            if (rr < k) zv = expf(key_to_float((uint32_t)(S.cand[rr] >> 32)) / temp - l0);
+            if (rr < P) S.z[rr] = zv;
+            loc += zv;
+        }
+        // the mass top-p compares against: the k survivors (T3: top-k came first), or the whole
+        // vocabulary's min-p survivors (MTL: top-k comes last)
+        float Z;
+        if (mtl) {
+            float a = 0.f;
+            for (int i = i0; i < i1; ++i) {
+                const float zv = expf(key_to_float(keys[i]) / temp - l0);
+                a += (!use_min || zv >= ch.min_p) ? zv : 0.f;
+            }
+            Z = block_sum_f32<NT>(a, (float*)S.scan);
+        }
+        const float incl = block_scan_f32<NT>(loc, (float*)S.scan);
+        if (t == NT - 1) ((float*)S.misc)[3] = incl;
+        __syncthreads();
+        if (!mtl) Z = ((float*)S.misc)[3];
+        const float cut = ch.top_p * Z;
+        int kept = 0;
+        float before = incl - loc;
+        for (int q = 0; q < per_r; ++q) {
+            const int rr = t * per_r + q;
+            if (rr >= k) break;
+            const float zv = S.z[rr];
+            kept += (!use_p || before < cut) && (!use_min || zv >= ch.min_p);
+            before += zv;
+        }
+        // both cuts keep a prefix of the descending order, so the count is its length
+        L = (int)block_sum_f32<NT>((float)kept, (float*)S.scan);
+        L = max(L, 1);
+    }
+
+    // 5. a penalty that comes last re-weights the survivors and can reorder them
+    bool rekeyed = false;
+    if (seen && !mtl && ch.penalty != 1.f) {
+        int P2 = 1;
+        while (P2 < L) P2 <<= 1;
+        for (int rr = t; rr < P; rr += NT) {
+            const unsigned long long c = S.cand[rr];
+            unsigned long long nc = 0ull;
+            if (rr < L) {
+                const uint32_t lo = (uint32_t)c, idx = 0xFFFFFFFFu - lo;
+                float v = key_to_float((uint32_t)(c >> 32)) / temp;
+                if (seen_bit(seen, (int)idx)) v = penalize(v, ch.penalty);
+                nc = ((unsigned long long)float_order_key(v) << 32) | lo;
+            }
+            S.cand[rr] = nc;
+        }
+        __syncthreads();
+        sort_desc<NT>(S.cand, P2);
+        rekeyed = true;
+    }
+
+    // 6. the draw over the first L: weights in descending order, their running sum, the crossing
+    const float v0 = rekeyed ? key_to_float((uint32_t)(S.cand[0] >> 32)) : l0;
     float loc = 0.f;
     for (int q = 0; q < per_r; ++q) {
         const int rr = t * per_r + q;
         float zv = 0.f;
-        if (rr < k) zv = expf(key_to_float((uint32_t)(S.cand[rr] >> 32)) / temperature - l0);
+        if (rr < L) {
+            const float v = key_to_float((uint32_t)(S.cand[rr] >> 32));
+            zv = expf((rekeyed ? v : v / temp) - v0);
+        }
         if (rr < P) S.z[rr] = zv;
         loc += zv;
     }
     const float incl = block_scan_f32<NT>(loc, (float*)S.scan);
     if (t == NT - 1) ((float*)S.misc)[3] = incl;   // the total
-    if (t == 0) S.misc[0] = (int)(0xFFFFFFFFu - (uint32_t)S.cand[k - 1]);   // if nothing crosses
+    if (t == 0) S.misc[0] = (int)(0xFFFFFFFFu - (uint32_t)S.cand[L - 1]);   // if nothing crosses
     __syncthreads();
     const float thr = u * ((float*)S.misc)[3];
     float run = incl - loc;
     for (int q = 0; q < per_r; ++q) {
         const int rr = t * per_r + q;
-        if (rr >= k) break;
+        if (rr >= L) break;
         const float before = run;
         run += S.z[rr];
         if (run > thr && before <= thr) S.misc[0] = (int)(0xFFFFFFFFu - (uint32_t)S.cand[rr]);

@@ -1,5 +1,6 @@
-// sampler.hip — the top-k draw as its own one-workgroup kernel: the sampler of the per-operator
-// step (after the head GEMV) and the standalone tsd_sample_topk.  The draw itself is sampler.h.
+// sampler.hip — the sampler chain as its own one-workgroup kernel: the sampler of the
+// per-operator step (after the head GEMV) and the standalone tsd_sample / tsd_sample_topk.  The
+// draw itself is sampler.h.
 #include "kernels.h"
 #include "sampler.h"
 
@@ -8,40 +9,45 @@ namespace {
 
 constexpr int NT = 256;
 
-// logits[0..n) -> id.  The position of the counter is *posp (the step's device position) or
-// pos_value; with hist, the id is also appended at hist[pos * hist_stride] and *posp advanced.
-__global__ __launch_bounds__(NT) void k_topk(const float* __restrict__ logits, int n, int k, float temperature,
-                                             unsigned long long seed, int row, int pass, int* posp, int pos_value,
-                                             int* out, int* hist, int hist_stride)
+__global__ __launch_bounds__(NT) void k_sample(const SampleArgs a)
 {
-    extern __shared__ uint32_t keys[];
+    extern __shared__ uint32_t lds[];   // keys [n], then the history's bit set [(n + 31) / 32]
     __shared__ samp::Scratch S;
-    for (int i = threadIdx.x; i < n; i += NT) keys[i] = float_order_key(logits[i]);
+    const int n = a.n;
+    uint32_t* keys = lds;
+    uint32_t* seen = lds + n;
+    const int pos = a.posp ? *a.posp : a.pos_value;
+    const int cur = a.cur ? *a.cur : -1;
+    const bool pen = a.ch.penalty != 1.f;
+    if (pen) samp::build_seen<NT>(seen, n, a.seq, a.seq_stride, a.n_seq < 0 ? pos : a.n_seq, cur);
+    const uint32_t* sp = pen ? seen : nullptr;
+    for (int i = threadIdx.x; i < n; i += NT) keys[i] = samp::chain_key(a.logits[i], i, a.ch, sp);
     __syncthreads();
-    const int pos = posp ? *posp : pos_value;
-    const float u = samp::uniform24(seed, (uint32_t)row, (uint32_t)pos, (uint32_t)pass);
-    const int id = samp::topk_draw<NT>(keys, n, k, temperature, u, S);
+    const float u = samp::uniform24(a.seed, (uint32_t)a.row, (uint32_t)pos, (uint32_t)a.pass);
+    const int id = samp::chain_draw<NT>(keys, n, a.ch, u, S, sp);
     if (threadIdx.x == 0) {
-        out[0] = id;
-        if (hist) {
-            hist[(size_t)pos * hist_stride] = id;
-            *posp = pos + 1;
+        a.out[0] = id;
+        if (a.posp) {
+            if (a.seq_out && a.cur) a.seq_out[(size_t)pos * a.seq_stride] = cur;
+            if (a.hist) a.hist[(size_t)pos * a.hist_stride] = id;
+            *a.posp = pos + 1;
         }
     }
 }
 
 }  // namespace
 
-size_t topk_lds_bytes(int n) { return (size_t)n * sizeof(uint32_t); }
+size_t sample_lds_bytes(int n) { return (size_t)n * sizeof(uint32_t) + (size_t)((n + 31) / 32) * sizeof(uint32_t); }
 
-bool topk_supported(int n, int k) { return n > 0 && k >= 1 && k <= n && k <= samp::KMAX && topk_lds_bytes(n) + sizeof(samp::Scratch) <= 64 * 1024; }
-
-hipError_t launch_topk(const float* logits, int n, int k, float temperature, unsigned long long seed, int row, int pass,
-                       int* posp, int pos_value, int* out, int* hist, int hist_stride, hipStream_t st)
+bool sample_supported(int n, int k)
 {
-    if (!topk_supported(n, k)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_topk, dim3(1), dim3(NT), topk_lds_bytes(n), st, logits, n, k, temperature, seed, row, pass, posp,
-                       pos_value, out, hist, hist_stride);
+    return n > 0 && k >= 1 && k <= n && k <= samp::KMAX && sample_lds_bytes(n) + sizeof(samp::Scratch) <= 64 * 1024;
+}
+
+hipError_t launch_sample(const SampleArgs& a, hipStream_t st)
+{
+    if (!sample_supported(a.n, a.ch.k) || !(a.ch.temperature > 0.f)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_sample, dim3(1), dim3(NT), sample_lds_bytes(a.n), st, a);
     return hipGetLastError();
 }
 

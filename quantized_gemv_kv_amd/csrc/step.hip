@@ -667,9 +667,11 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
     constexpr int OUT_FC_K = C::GPT2 ? OUT_GELU : OUT_SWIGLU;
     const ArgsPtr ap = (ArgsPtr)args;
 
-    // the phase input buffer; after the head, workgroup 0 reuses it for the top-k draw
+    // the phase input buffer; after the head, workgroup 0 reuses it for the chain's draw (keys,
+    // the history's bit set, the draw's scratch)
     constexpr size_t KEYS_BYTES = ((size_t)C::V * 4 + 15) & ~(size_t)15;
-    constexpr size_t SAMP_BYTES = KEYS_BYTES + sizeof(samp::Scratch);
+    constexpr size_t SEEN_BYTES = ((size_t)(C::V + 31) / 32 * 4 + 15) & ~(size_t)15;
+    constexpr size_t SAMP_BYTES = KEYS_BYTES + SEEN_BYTES + sizeof(samp::Scratch);
     constexpr size_t RAW_BYTES = MAX_K * 4 > SAMP_BYTES ? MAX_K * 4 : SAMP_BYTES;
     static_assert(RAW_BYTES <= 56 * 1024, "LDS of one workgroup");
     __shared__ __align__(16) unsigned char raw[RAW_BYTES];
@@ -786,11 +788,18 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
     if (!gemv_phase<C, C::D, C::V, C::NL_HEAD, IN_NORM, OUT_HEAD, C::GPT2>(a, cx, a.head, io, sm)) return give_up(a);
 
     if (blockIdx.x != 0) return;
+    // the token this step consumed (read before the sampler overwrites it): recorded at seq[pos]
+    // for the repetition penalty of later steps
+    const int cur = *glb(a.tok);
     if (a.samp_mode) {
-        // top-k draw (workgroup 0) over every logit, from the exchange words
+        // the chain's draw (workgroup 0) over every logit, from the exchange words
         const int t = threadIdx.x;
         uint32_t* keys = (uint32_t*)raw;
-        samp::Scratch& S = *(samp::Scratch*)(raw + KEYS_BYTES);
+        uint32_t* seen = (uint32_t*)(raw + KEYS_BYTES);
+        samp::Scratch& S = *(samp::Scratch*)(raw + KEYS_BYTES + SEEN_BYTES);
+        const bool pen = a.chain.penalty != 1.f;
+        if (pen) samp::build_seen<NT>(seen, C::V, a.seq, 1, cx.pos, cur);
+        const uint32_t* sp = pen ? seen : nullptr;
         constexpr int JV = (C::V + NT - 1) / NT;
         auto addr = [&](int q) { return a.x_logit + min(t + NT * q, C::V - 1); };
         uint64_t w[JV];
@@ -799,12 +808,13 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
         if (!xchg::settle_n(w, JV, addr, eh, cx.limit, a.abort_word)) s_abort = 1;
 #pragma unroll
         for (int q = 0; q < JV; ++q)
-            if (t + NT * q < C::V) keys[t + NT * q] = float_order_key(xchg::value(w[q]));
+            if (t + NT * q < C::V) keys[t + NT * q] = samp::chain_key(xchg::value(w[q]), t + NT * q, a.chain, sp);
         __syncthreads();
         if (s_abort) return give_up(a);
         const float u = samp::uniform24(a.seed, 0u, (uint32_t)cx.pos, 0u);
-        const int id = samp::topk_draw<NT>(keys, C::V, a.top_k, a.temperature, u, S);
+        const int id = samp::chain_draw<NT>(keys, C::V, a.chain, u, S, sp);
         if (t == 0) {
+            glb(a.seq)[cx.pos] = cur;
             *glb(a.tok) = id;
             glb(a.hist)[cx.pos] = id;
             *glb(a.pos) = cx.pos + 1;
@@ -838,6 +848,7 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
 #pragma unroll
         for (int i = 1; i < NWAVE; ++i) m = fkey[i] > m ? fkey[i] : m;
         const int id = (int)(0xFFFFFFFFu - (uint32_t)m);
+        glb(a.seq)[cx.pos] = cur;
         *glb(a.tok) = id;
         glb(a.hist)[cx.pos] = id;
         *glb(a.pos) = cx.pos + 1;

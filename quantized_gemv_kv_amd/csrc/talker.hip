@@ -156,8 +156,9 @@ hipError_t pick16(tsd_model* m, hipStream_t st, int j, int vocab, const RowPrep*
     a.ld_l = c.n_codebooks * m->vmax;
     a.n = vocab;
     a.B = c.batch;
-    a.top_k = m->samp.mode == 1 ? ((m->samp.top_k <= 0 || m->samp.top_k > vocab) ? vocab : m->samp.top_k) : 0;
-    a.temperature = m->samp.temperature;
+    a.draw = j == 0 ? m->draw : m->cp_draw;
+    a.ch = j == 0 ? m->chain : m->cp_chain;
+    a.seq = j == 0 ? m->seq : nullptr;   // the penalty and the consumed-token record: code 0 only
     a.seed = m->samp.seed;
     a.pass = j;
     a.posp = m->pos;
@@ -248,6 +249,7 @@ size_t talker_plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     int* pos = (int*)P.take(4 * sizeof(int));
     int* tok = (int*)P.take(sizeof(int) * B * C);
     int* hist = (int*)P.take(sizeof(int) * (size_t)c->n_ctx * B * C);
+    int* seq = (int*)P.take(sizeof(int) * (size_t)c->n_ctx * B);
     uint32_t* ctl = (uint32_t*)P.take(sizeof(uint32_t) * 64);
     float* x = (float*)P.take(sizeof(float) * MM_ROWS * d);
     float* xc = (float*)P.take(sizeof(float) * MM_ROWS * d);
@@ -290,7 +292,7 @@ size_t talker_plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     __half* ckc = (__half*)P.take(2 * ckv_layer * c->cp_n_layer);
     __half* cvc = (__half*)P.take(2 * ckv_layer * c->cp_n_layer);
     if (m && base) {
-        m->pos = pos; m->dbg_pos = pos + 1; m->tok = tok; m->hist = hist; m->ctl = ctl;
+        m->pos = pos; m->dbg_pos = pos + 1; m->tok = tok; m->hist = hist; m->seq = seq; m->ctl = ctl;
         m->x = x; m->xc = xc; m->qkv = q; m->h = h; m->logits = logits; m->part = part;
         m->act.hi = hi; m->act.lo = lo; m->act2.hi = hi2; m->act2.lo = lo2; m->ssq = ssq;
         m->rope = rope; m->rope_rows = rope_rows;
@@ -381,7 +383,8 @@ hipError_t talker_enqueue(tsd_model* m, hipStream_t st, bool with_cp, Probe* pr)
                     m->vc + m->kv_layer_elems * l, c.n_ctx, m->pos, 0, st, pr));
         n_ssq = tiles_d;
     }
-    if (!with_cp) return launch_frame_done(m->tok, 0, m->hist, m->pos, st);   // advance the position only
+    if (!with_cp)   // advance the position and record the consumed code 0 only
+        return launch_frame_done(m->tok, 0, m->hist, m->pos, m->seq, c.batch, c.n_codebooks, st);
     // code 0; the Talker's final-normed hidden state is the predictor's position 0
     TRY(head16(m, st, pr, m->t_head, 0));
     RowPrep h{};
@@ -413,7 +416,7 @@ hipError_t talker_enqueue(tsd_model* m, hipStream_t st, bool with_cp, Probe* pr)
         const RowPrep p = cp_input_emb(m, cpos, nullptr);
         TRY(pick16(m, st, cpos, c.cp_vocab, cpos + 1 < C ? &p : nullptr));
     }
-    return launch_frame_done(m->tok, B * C, m->hist, m->pos, st);
+    return launch_frame_done(m->tok, B * C, m->hist, m->pos, nullptr, B, C, st);
 }
 
 hipError_t talker_layer(tsd_model* m, int l, hipStream_t st, const float* d_x, const int* pos)

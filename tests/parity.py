@@ -53,3 +53,41 @@ def topk_draw_margins(logits, k, temperature, u):
     margin = float(np.min(np.abs(c - u * total)) / total)
     gap = float(v[order[k - 1]] - v[order[k]]) if k < n else float("inf")
     return margin, gap
+
+
+# ---- the sampler chain ------------------------------------------------------------------------
+
+def sampling_of(cfg):
+    """The GPU model's sampling dict for a config (None: plain greedy)."""
+    mode = cfg.get("sample_mode", 0)
+    pen = cfg.get("rep_penalty", 1.0)
+    if mode == 0 and pen in (0.0, 1.0):
+        return None
+    return dict(mode=mode, top_k=cfg.get("top_k", 0), temperature=cfg.get("temperature", 1.0), seed=cfg.get("seed", 0),
+                top_p=cfg.get("top_p", 0.0), min_p=cfg.get("min_p", 0.0), rep_penalty=pen,
+                order=cfg.get("sample_order", "t3"))
+
+
+def uses_chain(cfg) -> bool:
+    return sampling_of(cfg) is not None
+
+
+def chain_margins(logits, cfg, u, hist=(), penalty=True):
+    """The oracle's id and decision margins for one head (penalty False: a head the repetition
+    penalty does not cover)."""
+    import oracle
+    return oracle.sample_chain(logits, u, mode=cfg.get("sample_mode", 0), top_k=cfg.get("top_k", 0),
+                               temperature=cfg.get("temperature", 1.0), top_p=cfg.get("top_p", 0.0),
+                               min_p=cfg.get("min_p", 0.0),
+                               rep_penalty=cfg.get("rep_penalty", 1.0) if penalty else 1.0,
+                               order=cfg.get("sample_order", "t3"), hist=hist)
+
+
+def chain_near_boundary(margins, mass_tol=DRAW_MARGIN, gap_tol=TIE_GAP) -> bool:
+    """True when a fp32 run may take another decision than the fp64 oracle: the draw, the top-p
+    or the min-p cut lies within mass_tol of its boundary, or the top-k cut, the greedy argmax or
+    the walk order around the drawn id is decided by a logit gap below gap_tol (an exact tie,
+    gap 0, is decided by index on both sides and does not count)."""
+    return (margins["draw"] < mass_tol or margins["top_p"] < mass_tol or margins["min_p"] < mass_tol
+            or 0.0 < margins["top_k"] < gap_tol or margins["greedy"] < gap_tol
+            or 0.0 < margins["order"] < gap_tol)

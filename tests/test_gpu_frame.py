@@ -18,7 +18,8 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import DRAW_MARGIN, REL_TOL, TIE_GAP, ids_agree, rel_err, top2_gap, topk_draw_margins
+from parity import (DRAW_MARGIN, REL_TOL, TIE_GAP, chain_margins, chain_near_boundary, ids_agree, rel_err,
+                    sampling_of, top2_gap, topk_draw_margins, uses_chain)
 from quantized_gemv_kv_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -108,20 +109,18 @@ def test_gemm_rows_rejects_bad_arguments():
 
 def gpu_model(cfg, w):
     from quantized_gemv_kv_amd import Model
-    samp = None
-    if cfg.get("sample_mode", 0):
-        samp = dict(mode=1, top_k=cfg["top_k"], temperature=cfg["temperature"], seed=cfg["seed"])
-    m = Model(dict(cfg, launch_mode="per_operator"), w, sampling=samp)
+    m = Model(dict(cfg, launch_mode="per_operator"), w, sampling=sampling_of(cfg))
     assert not m.uses_persistent_step()
     return m
 
 
-def compare_frame(cfg, lo, lg, o_ids, g_ids, pos):
+def compare_frame(cfg, lo, lg, o_ids, g_ids, pos, hist0=None):
     """Logits [B][C][vmax] and codes [B][C] of one frame.  The frame's logits are one output
     tensor: rel over every head compared (each row up to its first legitimate difference of
-    codes).  Returns (heads compared, rel)."""
+    codes).  hist0[b]: the code 0 row b consumed at positions 0..pos (the repetition penalty's
+    history).  Returns (heads compared, rel)."""
     B, C, V, Vc = cfg["batch"], cfg["n_codebooks"], cfg["vocab"], cfg["cp_vocab"]
-    topk = cfg.get("sample_mode", 0) == 1
+    chain = uses_chain(cfg)
     got, ref = [], []
     for b in range(B):
         for j in range(C):
@@ -132,10 +131,11 @@ def compare_frame(cfg, lo, lg, o_ids, g_ids, pos):
             if int(g_ids[b, j]) == int(o_ids[b, j]):
                 continue
             # a legitimate difference ends the comparison of this row's frame
-            if topk:
+            if chain:
                 u = oracle.uniform24(cfg["seed"], b, pos, j)
-                margin, gap = topk_draw_margins(lo[b, j, :nv], cfg["top_k"], cfg["temperature"], u)
-                assert margin < DRAW_MARGIN or gap < TIE_GAP, (pos, b, j, g_ids[b, j], o_ids[b, j], margin, gap)
+                ref_id, mg = chain_margins(lo[b, j, :nv], cfg, u, hist0[b] if j == 0 else (), penalty=j == 0)
+                assert ref_id == int(o_ids[b, j])
+                assert chain_near_boundary(mg), (pos, b, j, g_ids[b, j], o_ids[b, j], mg)
             else:
                 assert ids_agree(g_ids[b, j], lo[b, j, :nv]), (pos, b, j, g_ids[b, j], o_ids[b, j],
                                                                 top2_gap(lo[b, j, :nv]))
@@ -155,18 +155,22 @@ def frame_parity(cfg, w, n_prompt, n_frames, seed=3, kv_pos=None):
         om.load_kv(k, v, kv_pos)
         gm.load_kv(dev(k), dev(v), kv_pos)
         o_ids = synth.prompt_tokens(cfg, 1, seed=seed + 1)[:, 0, :]
+        hist0 = [[] for _ in range(B)]                 # the loaded positions carry no tokens
     else:
         toks = synth.prompt_tokens(cfg, n_prompt, seed=seed)
+        hist0 = [list(toks[b, :, 0]) for b in range(B)]
         o_ids = om.prefill(toks)
         g_ids = gm.prefill(dev(toks)).cpu().numpy()
-        n, r = compare_frame(cfg, om.logits(), gm.logits().cpu().numpy(), o_ids, g_ids, n_prompt - 1)
+        n, r = compare_frame(cfg, om.logits(), gm.logits().cpu().numpy(), o_ids, g_ids, n_prompt - 1, hist0)
         heads, worst = heads + n, max(worst, r)
     for f in range(n_frames):
         pos = om.n_past
         nxt = o_ids
+        for b in range(B):
+            hist0[b].append(int(nxt[b, 0]))
         o_ids = om.step(nxt)
         g_ids = gm.step(dev(nxt)).cpu().numpy()
-        n, r = compare_frame(cfg, om.logits(), gm.logits().cpu().numpy(), o_ids, g_ids, pos)
+        n, r = compare_frame(cfg, om.logits(), gm.logits().cpu().numpy(), o_ids, g_ids, pos, hist0)
         heads, worst = heads + n, max(worst, r)
     assert gm.n_past == om.n_past
     hist = gm.tokens(gm.n_past - 1, 1).cpu().numpy()[0]
@@ -199,6 +203,22 @@ def test_small_frame_gqa_many_codebooks():
     w = synth.model_weights(cfg, 9, norm_std=0.1)
     heads, worst = frame_parity(cfg, w, n_prompt=70, n_frames=4)   # crosses a 64-key tile
     say(f"  heads compared {heads}, worst rel {worst:.2e}")
+
+
+@pytest.mark.parametrize("chain", [
+    dict(sample_mode=1, top_k=20, temperature=0.9, top_p=0.9, rep_penalty=1.3, sample_order="t3"),
+    dict(sample_mode=1, top_k=40, temperature=0.9, min_p=0.05, top_p=0.95, rep_penalty=1.05, sample_order="mtl"),
+    dict(sample_mode=0, rep_penalty=1.5),
+], ids=["t3", "mtl", "greedy-penalty"])
+def test_small_frame_chain_teacher_forced(chain):
+    """The sampler chain on every head of the frame; the repetition penalty on the Talker's code 0
+    over the codes 0 each row consumed (prompt frames included)."""
+    cfg = small_talker(batch=3, n_ctx=64, seed=77, **chain)
+    say(f"[frame-small] chain {chain}")
+    w = synth.model_weights(cfg, 42, norm_std=0.1)
+    heads, worst = frame_parity(cfg, w, n_prompt=5, n_frames=8)
+    say(f"  heads compared {heads}, worst rel {worst:.2e}")
+    assert heads >= cfg["batch"] * cfg["n_codebooks"] * 4
 
 
 def test_small_frame_topk_teacher_forced():

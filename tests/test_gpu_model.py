@@ -8,7 +8,8 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import DRAW_MARGIN, REL_TOL, TIE_GAP, ids_agree, rel_err, top2_gap, topk_draw_margins
+from parity import (DRAW_MARGIN, REL_TOL, TIE_GAP, chain_margins, chain_near_boundary, ids_agree, rel_err,
+                    sampling_of, top2_gap, topk_draw_margins)
 from quantized_gemv_kv_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -33,10 +34,7 @@ MODES = ["persistent", "per_operator"]
 
 def gpu_model(cfg, w, mode="persistent", n_wg=0):
     from quantized_gemv_kv_amd import Model
-    samp = None
-    if cfg.get("sample_mode", 0):
-        samp = dict(mode=1, top_k=cfg["top_k"], temperature=cfg["temperature"], seed=cfg["seed"])
-    m = Model(dict(cfg, launch_mode=mode, n_workgroups=n_wg), w, sampling=samp)
+    m = Model(dict(cfg, launch_mode=mode, n_workgroups=n_wg), w, sampling=sampling_of(cfg))
     # the launch mode asked for is the one that runs (the step kernel is timed only when it exists)
     assert m.uses_persistent_step() == (mode == "persistent"), "persistent step not built for this shape"
     return m
@@ -106,7 +104,8 @@ def test_small_llama_gqa_head128(mode):
 def test_small_models_topk_teacher_forced(arch, fmt, mode):
     """Top-k sampling on the device: both sides get the oracle's sampled id as the next input;
     the GPU's draw must equal the oracle's unless the oracle's u * total lies within 1e-4 of a
-    cumulative boundary or the k-th and (k+1)-th logits are within 1e-3."""
+    cumulative boundary, or the k-th and (k+1)-th logits, or the drawn one and a neighbour in
+    the walk, are within 1e-3."""
     k, T, seed = 5, 0.8, 1234
     cfg = synth.small_config(arch, fmt, d_ff=256, n_ctx=64, sample_mode=1, top_k=k, temperature=T, seed=seed)
     say(f"[model-small] top-k {arch} {fmt} {mode}")
@@ -121,13 +120,55 @@ def test_small_models_topk_teacher_forced(arch, fmt, mode):
         pos = om.n_past - 1
         lo, lg = om.logits()[0], gm.logits().cpu().numpy()[0]
         assert rel_err(lg, lo) <= REL_TOL, (s, rel_err(lg, lo))
-        margin, gap = topk_draw_margins(lo, k, T, oracle.uniform24(seed, 0, pos, 0))
-        if margin >= DRAW_MARGIN and gap >= TIE_GAP:
-            assert int(g_ids[0, 0]) == int(o_ids[0, 0]), (s, g_ids, o_ids, margin, gap)
+        ref, mg = chain_margins(lo, cfg, oracle.uniform24(seed, 0, pos, 0))
+        assert ref == int(o_ids[0, 0])
+        if not chain_near_boundary(mg):
+            assert int(g_ids[0, 0]) == int(o_ids[0, 0]), (s, g_ids, o_ids, mg)
             checked += 1
         g_ids = gm.step(dev(o_ids)).cpu().numpy()
         o_ids = om.step(o_ids)
     assert checked >= 30
+    gm.synchronize()
+    gm.close()
+
+
+CHAINS = {
+    "t3": dict(sample_mode=1, top_k=50, temperature=0.8, top_p=0.9, rep_penalty=1.3, sample_order="t3"),
+    "mtl": dict(sample_mode=1, top_k=100, temperature=0.9, min_p=0.05, top_p=0.9, rep_penalty=1.2, sample_order="mtl"),
+    "greedy-penalty": dict(sample_mode=0, rep_penalty=1.5),
+}
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("chain", list(CHAINS))
+@pytest.mark.parametrize("arch,fmt", [("gpt2", "q4_0"), ("llama", "q8_0")])
+def test_small_models_chain_teacher_forced(arch, fmt, chain, mode):
+    """The sampler chain on the device, teacher forced: the repetition penalty's history is every
+    token consumed so far (the prompt included); the GPU's id must equal the oracle's unless one
+    of the chain's decisions lies within the tolerance of its boundary."""
+    cfg = synth.small_config(arch, fmt, d_ff=256, n_ctx=80, seed=4321, **CHAINS[chain])
+    say(f"[model-small] chain {chain} {arch} {fmt} {mode}")
+    w = synth.model_weights(cfg, 42, norm_std=0.5)
+    om = oracle.OracleModel(cfg, w)
+    gm = gpu_model(cfg, w, mode)
+    toks = synth.prompt_tokens(cfg, 6, seed=2)
+    consumed = [int(t) for t in toks.ravel()]
+    o_ids = om.prefill(toks)
+    g_ids = gm.prefill(dev(toks)).cpu().numpy()
+    checked = 0
+    for s in range(60):
+        pos = om.n_past - 1
+        lo, lg = om.logits()[0], gm.logits().cpu().numpy()[0]
+        assert rel_err(lg, lo) <= REL_TOL, (s, rel_err(lg, lo))
+        ref, mg = chain_margins(lo, cfg, oracle.uniform24(cfg["seed"], 0, pos, 0), consumed)
+        assert ref == int(o_ids[0, 0])
+        if not chain_near_boundary(mg):
+            assert int(g_ids[0, 0]) == int(o_ids[0, 0]), (s, g_ids, o_ids, mg)
+            checked += 1
+        consumed.append(int(o_ids[0, 0]))
+        g_ids = gm.step(dev(o_ids)).cpu().numpy()
+        o_ids = om.step(o_ids)
+    assert checked >= 30                      # at least half of the steps decide clearly
     gm.synchronize()
     gm.close()
 

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import DRAW_MARGIN, topk_draw_margins
+from parity import DRAW_MARGIN, chain_near_boundary, topk_draw_margins
 
 pytestmark = pytest.mark.gpu
 
@@ -86,4 +86,88 @@ def test_rejects_bad_arguments():
     assert e.value.status == 1
     with pytest.raises(TsdError) as e:
         gpu_draw(np.zeros(4096, np.float32), 2000, 1.0, 1, 0, 0, 0)
+    assert e.value.status == 2
+
+
+# ---- the sampler chain (tsd_sample) -------------------------------------------------------------
+
+def gpu_chain(logits, samp, hist, row, pos, pss):
+    import torch
+    from quantized_gemv_kv_amd import binding
+    x = torch.from_numpy(np.ascontiguousarray(logits, np.float32)).cuda()
+    h = torch.from_numpy(np.ascontiguousarray(hist, np.int32)).cuda() if len(hist) else None
+    out = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    binding.tsd_sample(x, samp, h, row, pos, pss, out)
+    torch.cuda.synchronize()
+    return int(out.item())
+
+
+CHAIN_CASES = [
+    # n, sampling, history length
+    (160, dict(mode=1, top_k=50, temperature=0.8, top_p=0.9, rep_penalty=1.3, order="t3"), 30),
+    (1000, dict(mode=1, top_k=1000, temperature=0.8, top_p=0.95, rep_penalty=1.2, order="t3"), 200),
+    (8192, dict(mode=1, top_k=1000, temperature=0.8, top_p=0.95, rep_penalty=1.2, order="t3"), 700),
+    (8192, dict(mode=1, top_k=50, temperature=0.9, top_p=0.95, rep_penalty=1.05, order="t3"), 300),
+    (8192, dict(mode=1, top_k=1000, temperature=0.8, min_p=0.05, top_p=0.95, rep_penalty=2.0, order="mtl"), 700),
+    (3072, dict(mode=1, top_k=200, temperature=1.1, min_p=0.02, top_p=0.8, rep_penalty=1.3, order="mtl"), 100),
+    (2048, dict(mode=1, top_k=300, temperature=0.7, top_p=0.5, order="t3"), 0),
+    (2048, dict(mode=1, top_k=1000, temperature=1.0, min_p=0.1, order="mtl"), 0),
+    (8192, dict(mode=0, rep_penalty=1.5), 500),
+    (12288, dict(mode=1, top_k=64, temperature=0.9, top_p=0.9, rep_penalty=1.1, order="mtl"), 1000),
+]
+
+
+@pytest.mark.parametrize("n,samp,nh", CHAIN_CASES)
+def test_chain_draw_matches_oracle(n, samp, nh):
+    say(f"[sampler] chain n={n} {samp} history {nh}")
+    seed = 4242 + n + nh
+    samp = dict(samp, seed=seed)
+    rng = np.random.default_rng(seed)
+    checked = 0
+    for pos in range(30):
+        v = crafted_logits(n, seed + 7 * pos)   # fresh logits: a cut near its boundary stays one case
+        # a history drawn mostly from the largest logits, so the penalty reorders the top
+        top = np.argsort(-v, kind="stable")[:64]
+        hist = np.concatenate([rng.choice(top, size=nh // 2), rng.integers(0, n, nh - nh // 2)]).astype(np.int32) \
+            if nh else np.zeros(0, np.int32)
+        hist[: min(3, nh)] = [-1, n, n + 5][: min(3, nh)]          # out-of-range ids are ignored
+        u = oracle.uniform24(seed, 2, pos, 1)
+        ref, mg = oracle.sample_chain(v, u, mode=samp["mode"], top_k=samp.get("top_k", 0),
+                                      temperature=samp.get("temperature", 1.0), top_p=samp.get("top_p", 0.0),
+                                      min_p=samp.get("min_p", 0.0), rep_penalty=samp.get("rep_penalty", 1.0),
+                                      order=samp.get("order", "t3"), hist=hist)
+        got = gpu_chain(v, samp, hist, 2, pos, 1)
+        # identical fp32 inputs on both sides: only fp32 rounding of the scans separates them
+        if chain_near_boundary(mg, mass_tol=2e-5, gap_tol=1e-5):
+            continue
+        assert got == ref, (pos, got, ref, mg)
+        checked += 1
+    assert checked >= 20
+
+
+def test_chain_penalty_changes_the_pick():
+    """One logit far above the rest: without a history it is always drawn; once it is in the
+    history a huge penalty sends its (positive) logit to about 0, below the others."""
+    n = 512
+    v = np.full(n, 1.0, np.float32)
+    v[100] = 40.0
+    samp = dict(mode=1, top_k=n, temperature=1.0, rep_penalty=1e4, order="t3", seed=1)
+    for pos in range(10):
+        assert gpu_chain(v, samp, [], 0, pos, 0) == 100
+        assert gpu_chain(v, samp, [100, 100, 7], 0, pos, 0) != 100
+    g = dict(mode=0, rep_penalty=1e4)
+    assert gpu_chain(v, g, [], 0, 0, 0) == 100
+    assert gpu_chain(v, g, [100], 0, 0, 0) == 0       # every other logit ties at 1: lowest index
+
+
+def test_chain_rejects_bad_arguments():
+    from quantized_gemv_kv_amd import TsdError
+    v = np.zeros(64, np.float32)
+    for bad in (dict(mode=1, top_p=1.5), dict(mode=1, min_p=0.1, order="t3"), dict(mode=1, min_p=1.0, order="mtl"),
+                dict(mode=1, rep_penalty=-1.0), dict(mode=1, order=7), dict(mode=2), dict(mode=1, temperature=0.0)):
+        with pytest.raises(TsdError) as e:
+            gpu_chain(v, dict(dict(temperature=1.0), **bad), [], 0, 0, 0)
+        assert e.value.status == 1, bad
+    with pytest.raises(TsdError) as e:
+        gpu_chain(np.zeros(4096, np.float32), dict(mode=1, top_k=2000, temperature=1.0), [], 0, 0, 0)
     assert e.value.status == 2

@@ -133,6 +133,10 @@ def test_margins_locate_the_boundaries():
     assert m["min_p"] < 1e-12
     _, m = oracle.sample_chain(np.array([1.0, 3.0, 2.0]), 0.3, top_k=2)
     assert m["top_k"] == pytest.approx(1.0)
+    # the drawn entry's neighbours in the walk: 1.0001 and 1.0 are nearly equal, the crossing
+    # lands on rank 1 (index 0, value 1.0) whose neighbours are 1.0001 above and 0 below
+    i, m = oracle.sample_chain(np.array([1.0, 1.0001, 0.0]), 0.6)
+    assert i == 0 and m["order"] == pytest.approx(1e-4, rel=1e-6)
 
 
 def test_model_records_the_consumed_tokens_for_the_penalty():

@@ -37,16 +37,34 @@ sys.path.insert(0, ROOT)
 # workload name -> (prompt positions, default steps, description, dtype)
 WORKLOADS = {
     "gpt2_medium_q4_0": (256, 500, "GPT-2-Medium-shaped 24-layer speech-token decoder, Q4_0, 256-token prefill then {K} "
-                                   "greedy decode steps, batch 1", "q4_0 weights, fp32 accumulate, fp16 kv"),
+                                   "{S} decode steps, batch 1", "q4_0 weights, fp32 accumulate, fp16 kv"),
     "llama520m_q8_0": (300, 600, "Llama-shaped ~520M 30-layer speech-token decoder, Q8_0, 300-token prefill then {K} "
-                                 "greedy decode steps, batch 1", "q8_0 weights, fp32 accumulate, fp16 kv"),
+                                 "{S} decode steps, batch 1", "q8_0 weights, fp32 accumulate, fp16 kv"),
     "talker_cp_aff8": (170, 200, "Talker (28 layers, d 1024, 16 q / 8 kv heads of 128, SwiGLU 3072) + code predictor "
                                  "(5 layers, 15 sequential passes, vocab 2048), 8-bit affine group-64 weights, "
-                                 "170 prompt frames then {K} greedy frames of 16 codes, batch 16",
+                                 "170 prompt frames then {K} {S} frames of 16 codes, batch 16",
                        "aff8 weights, fp16 hi/lo x fp16 weight MFMA with fp32 accumulate, fp16 kv"),
 }
 WORKLOAD = "gpt2_medium_q4_0"
 PROMPT = 256
+
+# sampler presets: greedy (the headline and the parity reference); the T3 port's defaults
+# ("Chatterbox -> ggml Port: Development Journal", §3.9 table: top-k 1000, top-p 0.95,
+# temperature 0.8, repetition penalty 1.2); the Qwen3-TTS harness's settings ("Every Frame Is a
+# Memory Read", the baseline table: temperature 0.9, top-p 0.95, top-k 50, repetition penalty 1.05)
+SAMPLERS = {
+    "greedy": None,
+    "t3": dict(mode=1, top_k=1000, temperature=0.8, top_p=0.95, rep_penalty=1.2, order="t3"),
+    "qwen": dict(mode=1, top_k=50, temperature=0.9, top_p=0.95, rep_penalty=1.05, order="t3"),
+}
+
+
+def with_sampler(cfg, samp):
+    """The oracle's config fields for a sampler preset."""
+    if samp is None:
+        return cfg
+    return dict(cfg, sample_mode=samp["mode"], top_k=samp["top_k"], temperature=samp["temperature"],
+                seed=samp["seed"], top_p=samp["top_p"], rep_penalty=samp["rep_penalty"], sample_order=samp["order"])
 
 
 def parse():
@@ -57,6 +75,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=42)
+    ap.add_argument("--sampler", default="greedy", choices=sorted(SAMPLERS),
+                    help="greedy, or a sampler-chain preset (t3: the T3 port's defaults; qwen: the Qwen3-TTS settings)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemv", action="store_true", help="skip the standalone tall-GEMV measurement")
@@ -278,7 +298,10 @@ def main():
         sys.exit(2)
     weights = synth.model_weights(cfg, args.seed)
     stream = torch.cuda.Stream()
-    model = Model(cfg, weights, stream=stream)
+    samp = SAMPLERS[args.sampler]
+    if samp is not None:
+        samp = dict(samp, seed=args.seed)
+    model = Model(cfg, weights, stream=stream, sampling=samp)
     prompt = torch.from_numpy(synth.prompt_tokens(cfg, PROMPT, seed=args.seed)).to("cuda")
     step = model.step_eager if args.eager else model.step
     with torch.cuda.stream(stream):
@@ -344,9 +367,10 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic (seeded random weights, prompt ids and values; no checkpoint)",
-        "config": {"workload": desc.format(K=K), "d_model": cfg["d_model"], "n_layer": cfg["n_layer"],
+        "config": {"workload": desc.format(K=K, S="greedy" if samp is None else "sampled"), "d_model": cfg["d_model"], "n_layer": cfg["n_layer"],
                    "n_head": cfg["n_head"], "d_ff": cfg["d_ff"], "vocab": cfg["vocab"],
-                   "prompt": PROMPT, "global_batch": cfg["batch"], "launch_mode": mode, "workgroups": n_wg},
+                   "prompt": PROMPT, "global_batch": cfg["batch"], "launch_mode": mode, "workgroups": n_wg,
+                   "sampler": args.sampler if samp is None else dict(samp, preset=args.sampler)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": roofline.HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / roofline.HBM_PEAK_GBS, "traffic": counted_traffic(dom, WORKLOAD),
                      "kernel": dom, "launch_us": dom_us, "launches_per_step": dom_n,
@@ -373,8 +397,8 @@ def main():
         else:
             result["gemv"] = gemv_headline(args.seed)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = (cpu_baseline_frames if frames else cpu_baseline)(cfg, weights, args.cpu_seconds,
-                                                                                    args.seed)
+        result["cpu_baseline"] = (cpu_baseline_frames if frames else cpu_baseline)(with_sampler(cfg, samp), weights,
+                                                                                    args.cpu_seconds, args.seed)
     model.close()
     print(json.dumps(result), flush=True)
 

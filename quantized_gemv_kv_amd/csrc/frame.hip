@@ -442,20 +442,29 @@ __global__ __launch_bounds__(256) void k_pick(const PickArgs a)
     const int pos = *a.posp;
     const int cur = a.seq ? a.code[(size_t)b * a.ld_code] : -1;   // read before the pick overwrites it
     if (a.draw) {
-        uint32_t* seen = keys + a.n;
+        uint32_t* seen = keys + samp::key_words(a.n);
         const bool pen = a.seq && a.ch.penalty != 1.f;
         if (pen) samp::build_seen<256>(seen, a.n, a.seq + b, a.B, pos, cur);
         const uint32_t* sp = pen ? seen : nullptr;
-        for (int i = t; i < a.n; i += 256) keys[i] = samp::chain_key(l[i], i, a.ch, sp);
+        samp::load_keys<256>(keys, l, a.n, a.ch, sp);
         __syncthreads();
         const float u = samp::uniform24(a.seed, (uint32_t)b, (uint32_t)pos, (uint32_t)a.pass);
         const int id = samp::chain_draw<256>(keys, a.n, a.ch, u, S, sp);
         if (t == 0) picked = id;
     } else {
+        // the loads of a round are all issued (clamped addresses) before the first is used
+        constexpr int R = 8;
         unsigned long long best = 0ull;
-        for (int i = t; i < a.n; i += 256) {
-            const unsigned long long key = ((unsigned long long)float_order_key(l[i]) << 32) | (0xFFFFFFFFu - (uint32_t)i);
-            best = key > best ? key : best;
+        for (int base = 0; base < a.n; base += 256 * R) {
+            float v[R];
+#pragma unroll
+            for (int j = 0; j < R; ++j) v[j] = l[min(base + j * 256 + t, a.n - 1)];
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const int i = base + j * 256 + t;
+                const unsigned long long key = ((unsigned long long)float_order_key(v[j]) << 32) | (0xFFFFFFFFu - (uint32_t)i);
+                best = (i < a.n && key > best) ? key : best;
+            }
         }
         best = wave_max_u64(best);
         if ((t & 63) == 0) bk[t >> 6] = best;

@@ -69,48 +69,57 @@ __device__ __forceinline__ float key_to_float(uint32_t k)
 }
 
 // LDS the draw needs besides the n keys
+constexpr int HIST_COPIES = 8;   // the radix histogram is kept 8 times (lane % 8 picks one):
+                                 // logits cluster in a few digits, and one copy would serialise
+                                 // their atomic adds
 struct Scratch {
-    uint32_t hist[256];
-    uint32_t scan[256];
-    unsigned long long cand[KMAX];
-    float z[KMAX];
+    union {
+        uint32_t hist[256 * HIST_COPIES];   // digit d, copy c at d * HIST_COPIES + c (step 1 only)
+        unsigned long long cand[KMAX];      // the survivors (from step 2 on)
+    };
+    float z[KMAX];                          // their weights
+    uint32_t scan[8];                       // the scans' wave totals
     int misc[4];
 };
 
-// inclusive scan over the NT threads' values (one per thread); every thread gets its prefix
-template <int NT>
-__device__ __forceinline__ uint32_t block_scan_u32(uint32_t v, uint32_t* buf)
+// LDS position of key i: one word of padding after every 32, so that both the draw's per-thread
+// ranges (thread t reads element t * per + j, per a multiple of 32 for the large vocabularies)
+// and a writer's round-robin stores (element t + NT * q) spread over the 32 banks
+__host__ __device__ constexpr int key_at(int i) { return i + (i >> 5); }
+__host__ __device__ constexpr int key_words(int n) { return n + (n >> 5) + 1; }
+
+// inclusive scans over the NT threads' values (one per thread): a shuffle scan inside each wave,
+// then the wave totals through LDS; every thread gets its prefix
+template <class T>
+__device__ __forceinline__ T wave_incl_scan(T v)
 {
-    const int t = threadIdx.x;
-    buf[t] = v;
-    __syncthreads();
-    for (int o = 1; o < NT; o <<= 1) {
-        const uint32_t add = t >= o ? buf[t - o] : 0u;
-        __syncthreads();
-        buf[t] += add;
-        __syncthreads();
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const T u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
     }
-    const uint32_t r = buf[t];
+    return v;
+}
+
+template <int NT, class T>
+__device__ __forceinline__ T block_scan(T v, T* buf)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const T w = wave_incl_scan(v);
+    if (lane == 63) buf[wave] = w;
     __syncthreads();
-    return r;
+    T off = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) off += i < wave ? buf[i] : (T)0;
+    __syncthreads();
+    return w + off;
 }
 
 template <int NT>
-__device__ __forceinline__ float block_scan_f32(float v, float* buf)
-{
-    const int t = threadIdx.x;
-    buf[t] = v;
-    __syncthreads();
-    for (int o = 1; o < NT; o <<= 1) {
-        const float add = t >= o ? buf[t - o] : 0.f;
-        __syncthreads();
-        buf[t] += add;
-        __syncthreads();
-    }
-    const float r = buf[t];
-    __syncthreads();
-    return r;
-}
+__device__ __forceinline__ uint32_t block_scan_u32(uint32_t v, uint32_t* buf) { return block_scan<NT, uint32_t>(v, buf); }
+template <int NT>
+__device__ __forceinline__ float block_scan_f32(float v, float* buf) { return block_scan<NT, float>(v, buf); }
 
 // the chain's parameters (kernels.h)
 constexpr int ORDER_T3 = SAMP_ORDER_T3, ORDER_MTL = SAMP_ORDER_MTL;
@@ -120,16 +129,25 @@ __device__ __forceinline__ float penalize(float l, float theta) { return l < 0.f
 __device__ __forceinline__ bool seen_bit(const uint32_t* seen, int i) { return (seen[i >> 5] >> (i & 31)) & 1u; }
 
 // the history's ids as a bit set over [0, n) in LDS: entries hist[0], hist[stride], ...,
-// hist[(count-1)*stride], then cur; ids outside [0, n) are ignored
+// hist[(count-1)*stride], then cur; ids outside [0, n) are ignored.  The loads of a round are
+// all issued before the first is used (one memory round trip per 8 * NT entries).
 template <int NT>
 __device__ void build_seen(uint32_t* seen, int n, const int* hist, long long stride, int count, int cur)
 {
+    constexpr int R = 8;
     const int nw = (n + 31) >> 5;
     for (int i = threadIdx.x; i < nw; i += NT) seen[i] = 0u;
     __syncthreads();
-    for (int p = threadIdx.x; p <= count; p += NT) {
-        const int id = p < count ? hist[(long long)p * stride] : cur;
-        if ((unsigned)id < (unsigned)n) atomicOr(&seen[id >> 5], 1u << (id & 31));
+    for (int base = 0; base <= count; base += NT * R) {
+        int id[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int p = base + j * NT + (int)threadIdx.x;
+            id[j] = p < count ? hist[(long long)p * stride] : (p == count ? cur : -1);
+        }
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+            if ((unsigned)id[j] < (unsigned)n) atomicOr(&seen[id[j] >> 5], 1u << (id[j] & 31));
     }
     __syncthreads();
 }
@@ -139,6 +157,25 @@ __device__ __forceinline__ uint32_t chain_key(float l, int i, const Chain& ch, c
 {
     if (seen && ch.order == ORDER_MTL && seen_bit(seen, i)) l = penalize(l, ch.penalty);
     return float_order_key(l);
+}
+
+// keys[key_at(i)] = chain_key(l[i], i) for i < n (l in global memory): the loads of a round
+// are all issued (from clamped addresses) before the first is used
+template <int NT>
+__device__ void load_keys(uint32_t* keys, const float* __restrict__ l, int n, const Chain& ch, const uint32_t* seen)
+{
+    constexpr int R = 16;
+    const int t = threadIdx.x;
+    for (int base = 0; base < n; base += NT * R) {
+        float v[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) v[j] = l[min(base + j * NT + t, n - 1)];
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int i = base + j * NT + t;
+            if (i < n) keys[key_at(i)] = chain_key(v[j], i, ch, seen);
+        }
+    }
 }
 
 template <int NT>
@@ -154,27 +191,57 @@ __device__ __forceinline__ float block_sum_f32(float v, float* buf)
     return r;
 }
 
-// bitonic sort of S.cand[0..P) in descending order (P a power of two)
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m)
+{
+    const uint32_t lo = __shfl_xor((uint32_t)v, m, 64), hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// bitonic sort of cand[0..P) in descending order (P a power of two <= KMAX = 4 NT): thread t
+// holds elements 4t..4t+3 in registers; partners inside a thread or a wave are reached by
+// shuffles, only the strides that cross waves go through LDS.  Elements at P and beyond only
+// ever meet each other.
 template <int NT>
 __device__ __forceinline__ void sort_desc(unsigned long long* cand, int P)
 {
+    static_assert(KMAX == 4 * NT, "four elements per thread");
     const int t = threadIdx.x;
+    unsigned long long v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = 4 * t + e < P ? cand[4 * t + e] : 0ull;
     for (int size = 2; size <= P; size <<= 1)
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = t; i < P / 2; i += NT) {
-                const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
-                const bool desc = (lo & size) == 0;
-                const unsigned long long a = cand[lo], b = cand[hi];
-                if ((a < b) == desc) {
-                    cand[lo] = b;
-                    cand[hi] = a;
-                }
+            unsigned long long o[4];
+            if (stride >= 256) {   // partner in another wave
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cand[4 * t + e] = v[e];
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = cand[(4 * t + e) ^ stride];
+            } else if (stride >= 4) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = shfl_xor_u64(v[e], stride >> 2);
+            } else if (stride == 2) {   // partners inside the thread (constant register indices)
+                o[0] = v[2]; o[1] = v[3]; o[2] = v[0]; o[3] = v[1];
+            } else {
+                o[0] = v[1]; o[1] = v[0]; o[2] = v[3]; o[3] = v[2];
             }
-            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * t + e;
+                const bool take_max = ((i & stride) == 0) == ((i & size) == 0);
+                const bool gt = v[e] > o[e];
+                v[e] = take_max == gt ? v[e] : o[e];
+            }
         }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cand[4 * t + e] = v[e];
+    __syncthreads();
 }
 
-// The chain's draw over keys[0..n) (LDS, chain_key of the logits); seen: the history's bit set
+// The chain's draw over keys[0..n) (LDS, key i at key_at(i), chain_key of the logits); seen: the history's bit set
 // in LDS, or null (no penalty).  Every thread of the (NT = 256) workgroup calls it; every thread
 // gets the index.
 template <int NT>
@@ -185,21 +252,35 @@ __device__ int chain_draw(const uint32_t* keys, int n, const Chain& ch, float u,
     const int k = ch.k;
     const int per = (n + NT - 1) / NT;            // thread t owns elements [t*per, t*per + per)
     const int i0 = t * per, i1 = min(n, i0 + per);
+    // the thread's keys KCH at a time, every read of a chunk issued before the first is used
+    // (clamped: past the end a chunk rereads the last key, which the callers skip)
+    constexpr int KCH = 8;
+    auto load_chunk = [&](uint32_t* kk, int c) {
+#pragma unroll
+        for (int j = 0; j < KCH; ++j) kk[j] = keys[key_at(min(i0 + c + j, n - 1))];
+    };
 
     // 1. radix select of the k-th largest key
     uint32_t prefix = 0u, mask = 0u;
     int remaining = k;
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-        S.hist[t] = 0u;
+        for (int i = t; i < 256 * HIST_COPIES; i += NT) S.hist[i] = 0u;
         __syncthreads();
-        for (int i = i0; i < i1; ++i) {
-            const uint32_t key = keys[i];
-            if ((key & mask) == prefix) atomicAdd(&S.hist[(key >> shift) & 255u], 1u);
+        const uint32_t copy = (uint32_t)(t % HIST_COPIES);
+        for (int c = 0; c < per; c += KCH) {
+            uint32_t kk[KCH];
+            load_chunk(kk, c);
+#pragma unroll
+            for (int j = 0; j < KCH; ++j)
+                if (i0 + c + j < i1 && (kk[j] & mask) == prefix)
+                    atomicAdd(&S.hist[((kk[j] >> shift) & 255u) * HIST_COPIES + copy], 1u);
         }
         __syncthreads();
         // running count from the highest digit down: thread t holds digit 255 - t
-        const uint32_t c = S.hist[255 - t];
+        uint32_t c = 0u;
+#pragma unroll
+        for (int r = 0; r < HIST_COPIES; ++r) c += S.hist[(255 - t) * HIST_COPIES + r];
         const uint32_t cum = block_scan_u32<NT>(c, S.scan);
         if (cum >= (uint32_t)remaining && cum - c < (uint32_t)remaining) {
             S.misc[0] = 255 - t;              // the digit of the k-th largest
@@ -216,25 +297,29 @@ __device__ int chain_draw(const uint32_t* keys, int n, const Chain& ch, float u,
     const int n_eq = remaining;           // how many keys equal to T survive (the lowest indices)
     const int n_gt = k - n_eq;
 
-    // 2. gather the survivors as (key, ~index)
-    if (t == 0) S.misc[2] = 0;
-    __syncthreads();
-    uint32_t my_eq = 0u;
-    for (int i = i0; i < i1; ++i) {
-        const uint32_t key = keys[i];
-        if (key > T) {
-            const int p = atomicAdd(&S.misc[2], 1);
-            S.cand[p] = ((unsigned long long)key << 32) | (0xFFFFFFFFu - (uint32_t)i);
-        }
-        my_eq += key == T;
+    // 2. gather the survivors as (key, ~index), in index order: each thread counts its larger
+    //    and its equal keys (packed: equal << 16 | larger), one scan gives its offsets
+    uint32_t my = 0u;
+    for (int c = 0; c < per; c += KCH) {
+        uint32_t kk[KCH];
+        load_chunk(kk, c);
+#pragma unroll
+        for (int j = 0; j < KCH; ++j)
+            if (i0 + c + j < i1) my += kk[j] > T ? 1u : (kk[j] == T ? 0x10000u : 0u);
     }
-    const uint32_t eq_end = block_scan_u32<NT>(my_eq, S.scan);   // equal keys in index order
-    uint32_t r = eq_end - my_eq;
-    for (int i = i0; i < i1 && r < (uint32_t)n_eq; ++i)
-        if (keys[i] == T) {
-            S.cand[n_gt + r] = ((unsigned long long)T << 32) | (0xFFFFFFFFu - (uint32_t)i);
-            ++r;
+    const uint32_t end = block_scan_u32<NT>(my, S.scan);
+    uint32_t rg = (end - my) & 0xFFFFu, re = (end - my) >> 16;
+    for (int c = 0; c < per && (my & 0xFFFFu) + (my >> 16) > 0u; c += KCH) {
+        uint32_t kk[KCH];
+        load_chunk(kk, c);
+#pragma unroll
+        for (int j = 0; j < KCH; ++j) {
+            const int i = i0 + c + j;
+            const unsigned long long cv = ((unsigned long long)kk[j] << 32) | (0xFFFFFFFFu - (uint32_t)i);
+            if (i < i1 && kk[j] > T) S.cand[rg++] = cv;
+            else if (i < i1 && kk[j] == T && re < (uint32_t)n_eq) S.cand[n_gt + re++] = cv;
         }
+    }
     int P = 1;
     while (P < k) P <<= 1;
     for (int i = k + t; i < P; i += NT) S.cand[i] = 0ull;   // below every survivor
@@ -264,9 +349,14 @@ __device__ int chain_draw(const uint32_t* keys, int n, const Chain& ch, float u,
         float Z;
         if (mtl) {
             float a = 0.f;
-            for (int i = i0; i < i1; ++i) {
-                const float zv = expf(key_to_float(keys[i]) / temp - l0);
-                a += (!use_min || zv >= ch.min_p) ? zv : 0.f;
+            for (int c = 0; c < per; c += KCH) {
+                uint32_t kk[KCH];
+                load_chunk(kk, c);
+#pragma unroll
+                for (int j = 0; j < KCH; ++j) {
+                    const float zv = expf(key_to_float(kk[j]) / temp - l0);
+                    a += (i0 + c + j < i1 && (!use_min || zv >= ch.min_p)) ? zv : 0.f;
+                }
             }
             Z = block_sum_f32<NT>(a, (float*)S.scan);
         }

@@ -11,17 +11,17 @@ constexpr int NT = 256;
 
 __global__ __launch_bounds__(NT) void k_sample(const SampleArgs a)
 {
-    extern __shared__ uint32_t lds[];   // keys [n], then the history's bit set [(n + 31) / 32]
+    extern __shared__ uint32_t lds[];   // keys [key_words(n)], then the history's bit set [(n + 31) / 32]
     __shared__ samp::Scratch S;
     const int n = a.n;
     uint32_t* keys = lds;
-    uint32_t* seen = lds + n;
+    uint32_t* seen = lds + samp::key_words(n);
     const int pos = a.posp ? *a.posp : a.pos_value;
     const int cur = a.cur ? *a.cur : -1;
     const bool pen = a.ch.penalty != 1.f;
     if (pen) samp::build_seen<NT>(seen, n, a.seq, a.seq_stride, a.n_seq < 0 ? pos : a.n_seq, cur);
     const uint32_t* sp = pen ? seen : nullptr;
-    for (int i = threadIdx.x; i < n; i += NT) keys[i] = samp::chain_key(a.logits[i], i, a.ch, sp);
+    samp::load_keys<NT>(keys, a.logits, n, a.ch, sp);
     __syncthreads();
     const float u = samp::uniform24(a.seed, (uint32_t)a.row, (uint32_t)pos, (uint32_t)a.pass);
     const int id = samp::chain_draw<NT>(keys, n, a.ch, u, S, sp);
@@ -37,7 +37,10 @@ __global__ __launch_bounds__(NT) void k_sample(const SampleArgs a)
 
 }  // namespace
 
-size_t sample_lds_bytes(int n) { return (size_t)n * sizeof(uint32_t) + (size_t)((n + 31) / 32) * sizeof(uint32_t); }
+size_t sample_lds_bytes(int n)
+{
+    return (size_t)samp::key_words(n) * sizeof(uint32_t) + (size_t)((n + 31) / 32) * sizeof(uint32_t);
+}
 
 bool sample_supported(int n, int k)
 {

@@ -669,7 +669,7 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
 
     // the phase input buffer; after the head, workgroup 0 reuses it for the chain's draw (keys,
     // the history's bit set, the draw's scratch)
-    constexpr size_t KEYS_BYTES = ((size_t)C::V * 4 + 15) & ~(size_t)15;
+    constexpr size_t KEYS_BYTES = ((size_t)samp::key_words(C::V) * 4 + 15) & ~(size_t)15;
     constexpr size_t SEEN_BYTES = ((size_t)(C::V + 31) / 32 * 4 + 15) & ~(size_t)15;
     constexpr size_t SAMP_BYTES = KEYS_BYTES + SEEN_BYTES + sizeof(samp::Scratch);
     constexpr size_t RAW_BYTES = MAX_K * 4 > SAMP_BYTES ? MAX_K * 4 : SAMP_BYTES;
@@ -808,7 +808,8 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
         if (!xchg::settle_n(w, JV, addr, eh, cx.limit, a.abort_word)) s_abort = 1;
 #pragma unroll
         for (int q = 0; q < JV; ++q)
-            if (t + NT * q < C::V) keys[t + NT * q] = samp::chain_key(xchg::value(w[q]), t + NT * q, a.chain, sp);
+            if (t + NT * q < C::V)
+                keys[samp::key_at(t + NT * q)] = samp::chain_key(xchg::value(w[q]), t + NT * q, a.chain, sp);
         __syncthreads();
         if (s_abort) return give_up(a);
         const float u = samp::uniform24(a.seed, 0u, (uint32_t)cx.pos, 0u);

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "tsd_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-FORMATS = {"q4_0": 0, "q8_0": 1, "aff8": 2}
+FORMATS = {"q4_0": 0, "q8_0": 1, "aff8": 2, "q5_0": 3, "aff4_g64": 4, "aff4_g32": 5}
 ARCHS = {"gpt2": 0, "llama": 1, "talker_cp": 2}
 
 

@@ -125,6 +125,9 @@ size_t orc_matrix_bytes(int fmt, int N, int K)
     case ORC_Q4_0: return K % 32 ? 0 : (size_t)N * (K / 32) * 18;
     case ORC_Q8_0: return K % 32 ? 0 : (size_t)N * (K / 32) * 34;
     case ORC_AFF8: return K % 64 ? 0 : (size_t)N * K + (size_t)N * (K / 64) * 4;
+    case ORC_Q5_0: return K % 32 ? 0 : (size_t)N * (K / 32) * 22;
+    case ORC_AFF4_G64: return K % 64 ? 0 : (size_t)N * K / 2 + (size_t)N * (K / 64) * 4;
+    case ORC_AFF4_G32: return K % 32 ? 0 : (size_t)N * K / 2 + (size_t)N * (K / 32) * 4;
     default: return 0;
     }
 }
@@ -149,6 +152,40 @@ int orc_dequant_row(int fmt, const uint8_t* blob, int N, int K, int n, double* w
             for (int j = 0; j < 16; ++j) {
                 w[b * 32 + j] = ((double)(blk[2 + j] & 15) - 8.0) * d;
                 w[b * 32 + j + 16] = ((double)(blk[2 + j] >> 4) - 8.0) * d;
+            }
+        }
+    } else if (fmt == ORC_Q5_0) {
+        /* READING (Q5_0, the GGUF block the journal's --quant q5_0 writes, [J] A3): fp16 d, a
+         * 32-bit word of fifth bits (bit j for element j), then the 16 nibble bytes in Q4_0's
+         * order; w = (q - 16) d with q = nibble | fifth bit << 4 */
+        const uint8_t* row = blob + (size_t)n * (K / 32) * 22;
+        for (int b = 0; b < K / 32; ++b) {
+            const uint8_t* blk = row + (size_t)b * 22;
+            double d = orc_half_to_double(rd16(blk));
+            uint32_t qh = (uint32_t)blk[2] | ((uint32_t)blk[3] << 8) | ((uint32_t)blk[4] << 16) | ((uint32_t)blk[5] << 24);
+            for (int j = 0; j < 16; ++j) {
+                int lo = blk[6 + j] & 15, hi = blk[6 + j] >> 4;
+                lo |= (int)((qh >> j) & 1u) << 4;
+                hi |= (int)((qh >> (j + 16)) & 1u) << 4;
+                w[b * 32 + j] = ((double)lo - 16.0) * d;
+                w[b * 32 + j + 16] = ((double)hi - 16.0) * d;
+            }
+        }
+    } else if (fmt == ORC_AFF4_G64 || fmt == ORC_AFF4_G32) {
+        /* READING (4-bit affine, the MLX layout [F] §5.8 quantises to, groups of 64 or 32 along
+         * K): q packed two per byte, element 2i in the low nibble of byte i and 2i+1 in the high
+         * one (the little-endian uint32 words of eight); then fp16 scales, then fp16 biases, one
+         * per group; w = s q + b */
+        const int G = fmt == ORC_AFF4_G64 ? 64 : 32, ng = K / G;
+        const uint8_t* q = blob + (size_t)n * (K / 2);
+        const uint8_t* s = blob + (size_t)N * (K / 2) + (size_t)n * ng * 2;
+        const uint8_t* bb = blob + (size_t)N * (K / 2) + (size_t)N * ng * 2 + (size_t)n * ng * 2;
+        for (int g = 0; g < ng; ++g) {
+            double sc = orc_half_to_double(rd16(s + 2 * g)), bi = orc_half_to_double(rd16(bb + 2 * g));
+            for (int j = 0; j < G; ++j) {
+                int k = g * G + j;
+                int v = (k & 1) ? q[k >> 1] >> 4 : q[k >> 1] & 15;
+                w[k] = sc * (double)v + bi;
             }
         }
     } else {

@@ -25,7 +25,7 @@ extern "C" {
 #endif
 
 /* weight formats (values are this library's own; the Python side maps names) */
-enum { ORC_Q4_0 = 0, ORC_Q8_0 = 1, ORC_AFF8 = 2 };
+enum { ORC_Q4_0 = 0, ORC_Q8_0 = 1, ORC_AFF8 = 2, ORC_Q5_0 = 3, ORC_AFF4_G64 = 4, ORC_AFF4_G32 = 5 };
 /* architectures */
 enum { ORC_GPT2 = 0, ORC_LLAMA = 1, ORC_TALKER_CP = 2 };
 

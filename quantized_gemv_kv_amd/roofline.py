@@ -26,6 +26,12 @@ def matrix_bytes(fmt: str, N: int, K: int) -> int:
         return N * (K // 32) * 34
     if fmt == "aff8":
         return N * K + N * (K // 64) * 4
+    if fmt == "q5_0":
+        return N * (K // 32) * 22
+    if fmt == "aff4_g64":
+        return N * K // 2 + N * (K // 64) * 4
+    if fmt == "aff4_g32":
+        return N * K // 2 + N * (K // 32) * 4
     raise ValueError(fmt)
 
 

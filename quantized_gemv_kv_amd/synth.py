@@ -15,12 +15,16 @@ Canonical storage formats (little endian):
          low nibble of byte j, element j+16 its high nibble.
   q8_0 : per row, K/32 blocks of 34 bytes = fp16 scale d, then 32 int8.
   aff8 : planar q[N][K] uint8, then scales[N][K/64] fp16, then biases[N][K/64] fp16.
+  q5_0 : per row, K/32 blocks of 22 bytes = fp16 scale d, a 32-bit word whose bit j is element
+         j's fifth bit, then the 16 nibble bytes ordered as in q4_0; w = (q - 16) d.
+  aff4_g64 / aff4_g32 : planar q[N][K/2] bytes (element 2i in the low nibble of byte i, 2i+1 in
+         the high one), then scales[N][K/G] fp16, then biases[N][K/G] fp16; w = s q + b.
 """
 from __future__ import annotations
 
 import numpy as np
 
-FORMATS = {"q4_0": 0, "q8_0": 1, "aff8": 2}
+FORMATS = {"q4_0": 0, "q8_0": 1, "aff8": 2, "q5_0": 3, "aff4_g64": 4, "aff4_g32": 5}
 ARCHS = {"gpt2": 0, "llama": 1, "talker_cp": 2}
 
 
@@ -75,6 +79,34 @@ def aff8_matrix(rng, N, K, sscale=0.01):
     return blob, {"q": q, "s": s, "b": b}
 
 
+def q5_0_matrix(rng, N, K, dscale=0.02):
+    """5-bit q uniform in 0..31, fp16 d = |N(0,1)| * dscale."""
+    assert K % 32 == 0
+    q = rng.integers(0, 32, size=(N, K), dtype=np.uint8)
+    d = (np.abs(rng.standard_normal((N, K // 32))) * dscale).astype(np.float16)
+    qb = q.reshape(N, K // 32, 32)
+    lo = qb & 15
+    hbits = ((qb >> 4) & 1).astype(np.uint32)
+    qh = (hbits << np.arange(32, dtype=np.uint32)).sum(axis=2).astype(np.uint32)
+    blob = np.empty((N, K // 32, 22), np.uint8)
+    blob[:, :, 0:2] = d.view(np.uint8).reshape(N, K // 32, 2)
+    blob[:, :, 2:6] = qh.astype("<u4").view(np.uint8).reshape(N, K // 32, 4)
+    blob[:, :, 6:] = lo[:, :, :16] | (lo[:, :, 16:] << 4)
+    return blob.reshape(-1), {"q": q, "d": d}
+
+
+def aff4_matrix(rng, N, K, group=64, sscale=0.02):
+    """4-bit q uniform in 0..15; fp16 scale s = |N(0,1)| * sscale; fp16 bias around -8 s (centred
+    weights) plus 0.01 N(0,1)."""
+    assert K % group == 0
+    q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    s = (np.abs(rng.standard_normal((N, K // group))) * sscale).astype(np.float16)
+    b = (-8.0 * s.astype(np.float64) + 0.01 * rng.standard_normal((N, K // group))).astype(np.float16)
+    packed = q[:, 0::2] | (q[:, 1::2] << 4)
+    blob = np.concatenate([packed.reshape(-1), s.view(np.uint8).reshape(-1), b.view(np.uint8).reshape(-1)])
+    return blob, {"q": q, "s": s, "b": b}
+
+
 def matrix(fmt, rng, N, K, scale=None):
     if fmt == "q4_0":
         return q4_0_matrix(rng, N, K, *(() if scale is None else (scale,)))[0]
@@ -82,6 +114,11 @@ def matrix(fmt, rng, N, K, scale=None):
         return q8_0_matrix(rng, N, K, *(() if scale is None else (scale,)))[0]
     if fmt == "aff8":
         return aff8_matrix(rng, N, K, *(() if scale is None else (scale,)))[0]
+    if fmt == "q5_0":
+        return q5_0_matrix(rng, N, K, *(() if scale is None else (scale,)))[0]
+    if fmt in ("aff4_g64", "aff4_g32"):
+        g = 64 if fmt == "aff4_g64" else 32
+        return aff4_matrix(rng, N, K, g, *(() if scale is None else (scale,)))[0]
     raise ValueError(fmt)
 
 

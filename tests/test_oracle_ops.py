@@ -14,10 +14,10 @@ def _blob(fmt, N, K, seed=0):
 
 # ---- GEMV ------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "aff8"])
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "aff8", "q5_0", "aff4_g64", "aff4_g32"])
 @pytest.mark.parametrize("N,K", [(32, 64), (96, 128), (5, 1024), (64, 192)])
 def test_gemv_matches_dense_matmul(orc, fmt, N, K):
-    if fmt == "aff8" and K % 64:
+    if fmt in ("aff8", "aff4_g64") and K % 64:
         pytest.skip("affine groups are 64 wide")
     blob = _blob(fmt, N, K)
     W = orc.dequant(fmt, blob, N, K)
@@ -28,7 +28,7 @@ def test_gemv_matches_dense_matmul(orc, fmt, N, K):
     np.testing.assert_allclose(y, ref.numpy(), rtol=1e-12, atol=1e-12 * np.abs(W).sum())
 
 
-@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "aff8"])
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "aff8", "q5_0", "aff4_g64", "aff4_g32"])
 def test_gemv_one_hot_selects_a_column_exactly(orc, fmt):
     N, K = 40, 128
     blob = _blob(fmt, N, K, 3)

@@ -149,7 +149,70 @@ def test_aff8_hand_built_group(orc):
     assert np.array_equal(orc.dequant("aff8", blob, N, K)[1], np.r_[np.full(64, 1.0), np.full(64, 0.5)])
 
 
-@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "aff8"])
+def test_new_format_block_sizes(orc):
+    # Q5_0: 2 + 4 + 16 bytes per 32 weights (5.5 bits); 4-bit affine: K/2 bytes plus a scale and
+    # a bias per group (4.5 bits at group 64, 5 at group 32, the "~0.5 bit per weight more" of
+    # the finer groups)
+    assert orc.matrix_bytes("q5_0", 1, 32) == 22
+    assert orc.matrix_bytes("q5_0", 1, 1024) == 704
+    assert orc.matrix_bytes("aff4_g64", 1, 1024) * 8 / 1024 == 4.5
+    assert orc.matrix_bytes("aff4_g32", 1, 1024) * 8 / 1024 == 5.0
+    assert orc.matrix_bytes("q5_0", 2, 48) == 0
+    assert orc.matrix_bytes("aff4_g64", 2, 96) == 0
+    assert orc.matrix_bytes("aff4_g32", 2, 96) == 2 * 48 + 2 * 3 * 4
+
+
+def _q5_block(dbits, qh, qs):
+    return np.concatenate([np.array([dbits & 0xFF, dbits >> 8], np.uint8),
+                           np.array([qh & 0xFF, (qh >> 8) & 0xFF, (qh >> 16) & 0xFF, qh >> 24], np.uint8),
+                           np.asarray(qs, np.uint8)])
+
+
+@pytest.mark.parametrize("dbits", sorted(HALF))
+def test_q5_0_hand_built_block(orc, dbits):
+    lo = np.arange(16, dtype=np.uint8)                 # low nibbles of elements 0..15
+    hi = (15 - np.arange(16)).astype(np.uint8)         # of elements 16..31
+    qh = 0xA5C3F00F                                    # fifth bits: bit j for element j
+    w = orc.dequant("q5_0", _q5_block(dbits, qh, lo | (hi << 4)), 1, 32)[0]
+    five = np.array([(qh >> j) & 1 for j in range(32)], np.float64) * 16
+    expect = HALF[dbits] * (np.concatenate([lo, hi]).astype(np.float64) + five - 16.0)
+    assert np.array_equal(w, expect)
+    # all bits clear: -16 d; every bit set: 15 d
+    assert np.array_equal(orc.dequant("q5_0", _q5_block(dbits, 0, np.zeros(16)), 1, 32)[0], np.full(32, -16 * HALF[dbits]))
+    assert np.array_equal(orc.dequant("q5_0", _q5_block(dbits, 0xFFFFFFFF, np.full(16, 0xFF)), 1, 32)[0],
+                          np.full(32, 15 * HALF[dbits]))
+
+
+def test_q5_0_fifth_bit_order_single_element(orc):
+    # q = 16 is zero: nibbles 0 with every fifth bit set; clearing bit j moves element j alone to -16
+    for j in range(32):
+        w = orc.dequant("q5_0", _q5_block(0x3C00, 0xFFFFFFFF & ~(1 << j), np.zeros(16)), 1, 32)[0]
+        assert list(np.nonzero(w)[0]) == [j] and w[j] == -16.0
+
+
+def test_aff4_nibble_order_and_groups(orc):
+    for fmt, G in (("aff4_g64", 64), ("aff4_g32", 32)):
+        N, K = 2, 128
+        q = np.zeros((N, K), np.uint8)
+        q[0, 5] = 9                                    # byte 2's high nibble
+        q[0, 6] = 3                                    # byte 3's low nibble
+        q[1, :] = np.arange(K) % 16
+        ng = K // G
+        s = np.full((N, ng), 0x3C00, np.uint16)        # 1
+        s[1, :] = 0x3800                               # 0.5
+        b = np.zeros((N, ng), np.uint16)
+        b[1, -1] = 0xC000                              # -2 on row 1's last group
+        packed = q[:, 0::2] | (q[:, 1::2] << 4)
+        assert packed[0, 2] == 0x90 and packed[0, 3] == 0x03
+        blob = np.concatenate([packed.reshape(-1), s.reshape(-1).view(np.uint8), b.reshape(-1).view(np.uint8)])
+        W = orc.dequant(fmt, blob, N, K)
+        assert list(np.nonzero(W[0])[0]) == [5, 6] and W[0, 5] == 9.0 and W[0, 6] == 3.0
+        expect = 0.5 * (np.arange(K) % 16).astype(np.float64)
+        expect[K - G:] -= 2.0
+        assert np.array_equal(W[1], expect)
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "aff8", "q5_0", "aff4_g64", "aff4_g32"])
 def test_generator_blobs_decode_to_their_draws(orc, fmt):
     """The generator's packing, decoded by the oracle, reproduces the raw draws exactly."""
     from quantized_gemv_kv_amd import synth
@@ -161,6 +224,14 @@ def test_generator_blobs_decode_to_their_draws(orc, fmt):
     elif fmt == "q8_0":
         blob, raw = synth.q8_0_matrix(rng, N, K)
         expect = raw["q"].astype(np.float64) * np.repeat(raw["d"].astype(np.float64), 32, axis=1)
+    elif fmt == "q5_0":
+        blob, raw = synth.q5_0_matrix(rng, N, K)
+        expect = (raw["q"].astype(np.float64) - 16) * np.repeat(raw["d"].astype(np.float64), 32, axis=1)
+    elif fmt.startswith("aff4"):
+        g = 64 if fmt == "aff4_g64" else 32
+        blob, raw = synth.aff4_matrix(rng, N, K, g)
+        expect = (raw["q"].astype(np.float64) * np.repeat(raw["s"].astype(np.float64), g, axis=1)
+                  + np.repeat(raw["b"].astype(np.float64), g, axis=1))
     else:
         blob, raw = synth.aff8_matrix(rng, N, K)
         expect = (raw["q"].astype(np.float64) * np.repeat(raw["s"].astype(np.float64), 64, axis=1)

@@ -1,5 +1,7 @@
 """The byte counter against the figures the pages print (CPU only)."""
 import os
+
+import pytest
 import sys
 
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
@@ -79,3 +81,10 @@ def test_parity_metric_reproduces_page_rows():
         ref = np.array([0.3 * max_ref, -max_ref, 0.5 * max_ref])
         got = ref + np.array([0.0, 0.2 * max_abs, -max_abs])
         assert abs(rel_err(got, ref) - rel) / rel < 0.06, row
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "aff8", "q5_0", "aff4_g64", "aff4_g32"])
+def test_matrix_bytes_agree_with_the_oracle(orc, fmt):
+    for N, K in [(1, 1024), (3072, 1024), (1024, 4096), (7, 192)]:
+        if orc.matrix_bytes(fmt, N, K):
+            assert roofline.matrix_bytes(fmt, N, K) == orc.matrix_bytes(fmt, N, K)

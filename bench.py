@@ -38,6 +38,8 @@ sys.path.insert(0, ROOT)
 WORKLOADS = {
     "gpt2_medium_q4_0": (256, 500, "GPT-2-Medium-shaped 24-layer speech-token decoder, Q4_0, 256-token prefill then {K} "
                                    "{S} decode steps, batch 1", "q4_0 weights, fp32 accumulate, fp16 kv"),
+    "gpt2_medium_q5_0": (256, 500, "GPT-2-Medium-shaped 24-layer speech-token decoder, Q5_0, 256-token prefill then {K} "
+                                   "{S} decode steps, batch 1", "q5_0 weights, fp32 accumulate, fp16 kv"),
     "llama520m_q8_0": (300, 600, "Llama-shaped ~520M 30-layer speech-token decoder, Q8_0, 300-token prefill then {K} "
                                  "{S} decode steps, batch 1", "q8_0 weights, fp32 accumulate, fp16 kv"),
     "talker_cp_aff8": (170, 200, "Talker (28 layers, d 1024, 16 q / 8 kv heads of 128, SwiGLU 3072) + code predictor "
@@ -80,6 +82,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemv", action="store_true", help="skip the standalone tall-GEMV measurement")
+    ap.add_argument("--gemv-format", default="q8_0", choices=["q8_0", "q4_0", "q5_0", "aff8", "aff4_g64", "aff4_g32"],
+                    help="weight format of the standalone tall GEMV (q8_0: the lone-GEMV workload's)")
     ap.add_argument("--eager", action="store_true",
                     help="enqueue each step kernel by kernel instead of replaying the graph (for counter "
                          "collection, which cannot follow graph launches); prefill is skipped: the cache "
@@ -138,7 +142,7 @@ def warm(call, seconds=0.25):
 TALL_N, TALL_K = 524288, 1024      # one Q8_0 GEMV of ~570 MB, larger than the 256 MB Infinity Cache
 
 
-def gemv_headline(seed, reps=7):
+def gemv_headline(seed, reps=7, fmt="q8_0"):
     """The quantized GEMV alone at a size where a launch is amortised: y = W x with W a
     524288 x 1024 Q8_0 matrix (the lone-GEMV law), x ~ N(0,1), batch 1; after a quarter second of
     warm-up launches, the median over `reps` bursts of 10 back-to-back launches timed with HIP
@@ -146,16 +150,19 @@ def gemv_headline(seed, reps=7):
     import torch
     from quantized_gemv_kv_amd import binding, roofline, synth
     N, K = TALL_N, TALL_K
-    canon = torch.empty(roofline.matrix_bytes("q8_0", N, K), dtype=torch.uint8, device="cuda")
-    row_b = K // 32 * 34
-    for r0, blob in synth.q8_0_row_chunks(N, K, seed):
-        canon[r0 * row_b: r0 * row_b + blob.size].copy_(torch.from_numpy(blob))
-    packed = torch.empty(binding.tsd_gemv_packed_bytes("q8_0", N, K), dtype=torch.uint8, device="cuda")
-    binding.tsd_gemv_pack("q8_0", canon, N, K, packed)
+    canon = torch.empty(roofline.matrix_bytes(fmt, N, K), dtype=torch.uint8, device="cuda")
+    if fmt == "q8_0":
+        row_b = K // 32 * 34
+        for r0, blob in synth.q8_0_row_chunks(N, K, seed):
+            canon[r0 * row_b: r0 * row_b + blob.size].copy_(torch.from_numpy(blob))
+    else:
+        synth.matrix_into(fmt, N, K, seed, canon)
+    packed = torch.empty(binding.tsd_gemv_packed_bytes(fmt, N, K), dtype=torch.uint8, device="cuda")
+    binding.tsd_gemv_pack(fmt, canon, N, K, packed)
     del canon
     x = torch.from_numpy(synth.normal_f32(synth.rng_for(seed, 1), (1, K))).cuda()
     y = torch.empty((1, N), dtype=torch.float32, device="cuda")
-    warm(lambda: binding.tsd_gemv("q8_0", packed, N, K, 1, x, None, y))
+    warm(lambda: binding.tsd_gemv(fmt, packed, N, K, 1, x, None, y))
     # median over short bursts of back-to-back launches (about 1 ms each, timed with HIP events
     # around the burst): long runs of full-bandwidth streaming are slowed by the board's power
     # management, which would make the figure depend on the run length
@@ -165,14 +172,14 @@ def gemv_headline(seed, reps=7):
         torch.cuda.synchronize()
         e0.record()
         for _ in range(burst):
-            binding.tsd_gemv("q8_0", packed, N, K, 1, x, None, y)
+            binding.tsd_gemv(fmt, packed, N, K, 1, x, None, y)
         e1.record()
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1) * 1e3 / burst)
     us = float(np.median(times))
-    nbytes = roofline.gemv_bytes("q8_0", N, K)
+    nbytes = roofline.gemv_bytes(fmt, N, K)
     gbs = nbytes / (us * 1e-6) / 1e9
-    return {"shape": f"Q8_0 {N}x{K}, batch 1", "bytes": nbytes, "us": us, "gbs": gbs,
+    return {"shape": f"{fmt.upper()} {N}x{K}, batch 1", "bytes": nbytes, "us": us, "gbs": gbs,
             "frac": gbs / roofline.HBM_PEAK_GBS, "timing": f"median over {reps} bursts of {burst} back-to-back launches, after 0.25 s of warm-up launches"}
 
 
@@ -395,7 +402,7 @@ def main():
         if frames:
             result["gemm_rows"] = gemm_rows_headline(args.seed)
         else:
-            result["gemv"] = gemv_headline(args.seed)
+            result["gemv"] = gemv_headline(args.seed, fmt=args.gemv_format)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = (cpu_baseline_frames if frames else cpu_baseline)(with_sampler(cfg, samp), weights,
                                                                                     args.cpu_seconds, args.seed)

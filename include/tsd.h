@@ -24,8 +24,16 @@
  *   TSD_W_Q8_0        rows of K/32 blocks, 34 bytes each: fp16 d, then 32 int8 q; w = d * q.
  *   TSD_W_AFFINE8_G64 planar: q[N][K] uint8, then s[N][K/64] fp16, then b[N][K/64] fp16;
  *                     w = s * q + b for each group of 64 along K.
+ *   TSD_W_Q5_0        ([J] appendix A3's third legacy block) rows of K/32 blocks, 22 bytes each:
+ *                     fp16 d, a little-endian 32-bit word whose bit j is element j's fifth bit,
+ *                     then 16 nibble bytes ordered as in Q4_0; w = (q - 16) * d with
+ *                     q = nibble | fifth bit << 4.
+ *   TSD_W_AFFINE4_G64, TSD_W_AFFINE4_G32 ([F] §5.8's 4-bit variants, groups of 64 and 32)
+ *                     planar: q[N][K/2] bytes, element 2i in the low nibble of byte i and 2i+1
+ *                     in the high one, then s[N][K/G] fp16, then b[N][K/G] fp16; w = s * q + b.
  *   All matrices are W[N][K]: N output rows, each contiguous along the reduction axis K
- *   ([J] §3.2 issue 5).  K must be a multiple of 32 (Q4_0, Q8_0) or 64 (affine).
+ *   ([J] §3.2 issue 5).  K must be a multiple of the group: 32 (Q4_0, Q8_0, Q5_0, AFFINE4_G32)
+ *   or 64 (AFFINE8_G64, AFFINE4_G64).  TALKER_CP takes TSD_W_AFFINE8_G64 only.
  */
 #ifndef TSD_H
 #define TSD_H
@@ -49,7 +57,14 @@ typedef enum {
 } tsd_status;
 
 typedef enum { TSD_ARCH_GPT2 = 0, TSD_ARCH_LLAMA = 1, TSD_ARCH_TALKER_CP = 2 } tsd_arch;
-typedef enum { TSD_W_Q4_0 = 0, TSD_W_Q8_0 = 1, TSD_W_AFFINE8_G64 = 2 } tsd_wfmt;
+typedef enum {
+    TSD_W_Q4_0 = 0,
+    TSD_W_Q8_0 = 1,
+    TSD_W_AFFINE8_G64 = 2,
+    TSD_W_Q5_0 = 3,
+    TSD_W_AFFINE4_G64 = 4,
+    TSD_W_AFFINE4_G32 = 5
+} tsd_wfmt;
 
 /* How a step is launched.
  *   PERSISTENT (default): batch-1 GPT2/LLAMA steps run as ONE launch of one workgroup per

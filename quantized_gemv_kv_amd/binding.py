@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtsd.so")
 
 ARCHS = {"gpt2": 0, "llama": 1, "talker_cp": 2}
-FORMATS = {"q4_0": 0, "q8_0": 1, "aff8": 2}
+FORMATS = {"q4_0": 0, "q8_0": 1, "aff8": 2, "q5_0": 3, "aff4_g64": 4, "aff4_g32": 5}
 STATUS = {0: "TSD_OK", 1: "TSD_ERR_INVALID_ARGUMENT", 2: "TSD_ERR_UNSUPPORTED", 3: "TSD_ERR_OUT_OF_MEMORY",
           4: "TSD_ERR_CONTEXT_FULL", 5: "TSD_ERR_HIP", 6: "TSD_ERR_STATE", 7: "TSD_ERR_TIMEOUT"}
 LAUNCH_MODES = {"persistent": 0, "per_operator": 1}

@@ -18,29 +18,42 @@ namespace tsd {
 //   Q8_0: slot = half a block (16 elements); bytes stored as q + 128 (unsigned), so that the
 //         byte-to-float conversions need no sign handling; the -128 is folded into the sum.
 //   AFF8: slot = a quarter of a 64-group (16 elements); q stored as is.
-enum Fmt : int { FMT_Q4_0 = 0, FMT_Q8_0 = 1, FMT_AFF8 = 2 };
+//   Q5_0: slot = one block's 16 nibble bytes in Q4_0's order; the block's 32 fifth bits (bit j
+//         for element j) in a separate array of 32-bit words; w = (q - 16) d.
+//   AFF4_G64 / AFF4_G32: slot = 32 elements of a 64 (32) group, repacked into Q4_0's nibble
+//         order (byte b: element b low, element b + 16 high); w = s q + b.
+enum Fmt : int { FMT_Q4_0 = 0, FMT_Q8_0 = 1, FMT_AFF8 = 2, FMT_Q5_0 = 3, FMT_AFF4_G64 = 4, FMT_AFF4_G32 = 5 };
+constexpr int FMT_COUNT = 6;
 
 template <int F> struct FmtT;
 template <> struct FmtT<FMT_Q4_0> { static constexpr int E = 32, SLOTS_PER_SCALE = 1, SCALE_GROUP = 32; };
 template <> struct FmtT<FMT_Q8_0> { static constexpr int E = 16, SLOTS_PER_SCALE = 2, SCALE_GROUP = 32; };
 template <> struct FmtT<FMT_AFF8> { static constexpr int E = 16, SLOTS_PER_SCALE = 4, SCALE_GROUP = 64; };
+template <> struct FmtT<FMT_Q5_0> { static constexpr int E = 32, SLOTS_PER_SCALE = 1, SCALE_GROUP = 32; };
+template <> struct FmtT<FMT_AFF4_G64> { static constexpr int E = 32, SLOTS_PER_SCALE = 2, SCALE_GROUP = 64; };
+template <> struct FmtT<FMT_AFF4_G32> { static constexpr int E = 32, SLOTS_PER_SCALE = 1, SCALE_GROUP = 32; };
 
-__host__ __device__ inline int fmt_elems_per_slot(int f) { return f == FMT_Q4_0 ? 32 : 16; }
-__host__ __device__ inline int fmt_group(int f) { return f == FMT_AFF8 ? 64 : 32; }
-__host__ __device__ inline size_t fmt_row_bytes(int f, int K) { return f == FMT_Q4_0 ? (size_t)K / 2 : (size_t)K; }
+// formats whose slot holds 32 four-bit codes in Q4_0's nibble order
+__host__ __device__ constexpr bool fmt_nibbles(int f) { return f == FMT_Q4_0 || f == FMT_Q5_0 || f == FMT_AFF4_G64 || f == FMT_AFF4_G32; }
+// formats with a per-group bias (w = s q + b)
+__host__ __device__ constexpr bool fmt_affine(int f) { return f == FMT_AFF8 || f == FMT_AFF4_G64 || f == FMT_AFF4_G32; }
+__host__ __device__ inline int fmt_elems_per_slot(int f) { return fmt_nibbles(f) ? 32 : 16; }
+__host__ __device__ inline int fmt_group(int f) { return f == FMT_AFF8 || f == FMT_AFF4_G64 ? 64 : 32; }
+__host__ __device__ inline size_t fmt_row_bytes(int f, int K) { return fmt_nibbles(f) ? (size_t)K / 2 : (size_t)K; }
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct PackedMat {
-    const uint8_t* q;   // [N][row_bytes]
-    const __half* s;    // [N][K/group]
-    const __half* b;    // [N][K/group] affine biases (AFF8), else null
+    const uint8_t* q;    // [N][row_bytes]
+    const __half* s;     // [N][K/group]
+    const __half* b;     // [N][K/group] affine biases, else null
+    const uint32_t* h;   // [N][K/32] Q5_0 fifth bits, else null
     int N, K;
 };
 
 // byte layout of one packed matrix inside a buffer
 struct PackedLayout {
-    size_t q_off, s_off, b_off, total;
+    size_t q_off, s_off, b_off, h_off, total;
 };
 inline PackedLayout packed_layout(int f, int N, int K)
 {
@@ -49,7 +62,8 @@ inline PackedLayout packed_layout(int f, int N, int K)
     L.s_off = align256((size_t)N * fmt_row_bytes(f, K));
     size_t sb = align256((size_t)N * (K / fmt_group(f)) * 2);
     L.b_off = L.s_off + sb;
-    L.total = L.b_off + (f == FMT_AFF8 ? sb : 0);
+    L.h_off = L.b_off + (fmt_affine(f) ? sb : 0);
+    L.total = L.h_off + (f == FMT_Q5_0 ? align256((size_t)N * (K / 32) * 4) : 0);
     return L;
 }
 inline PackedMat packed_view(int f, void* base, int N, int K)
@@ -59,7 +73,8 @@ inline PackedMat packed_view(int f, void* base, int N, int K)
     PackedMat m;
     m.q = p + L.q_off;
     m.s = (const __half*)(p + L.s_off);
-    m.b = f == FMT_AFF8 ? (const __half*)(p + L.b_off) : nullptr;
+    m.b = fmt_affine(f) ? (const __half*)(p + L.b_off) : nullptr;
+    m.h = f == FMT_Q5_0 ? (const uint32_t*)(p + L.h_off) : nullptr;
     m.N = N;
     m.K = K;
     return m;

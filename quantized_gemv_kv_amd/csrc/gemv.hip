@@ -107,7 +107,7 @@ __global__ __launch_bounds__(WG) void k_gemv(const PackedMat W, const ProArgs pa
     __shared__ unsigned long long bkey[NWAVE];
 
     const int K = W.K, N = W.N, lpr = K / E;
-    const size_t rb = F == FMT_Q4_0 ? (size_t)K / 2 : (size_t)K;
+    const size_t rb = fmt_row_bytes(F, K);
     const int spr = K / G;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int slot0 = SPL == 1 ? (lane & (lpr - 1)) : lane;
@@ -125,6 +125,7 @@ __global__ __launch_bounds__(WG) void k_gemv(const PackedMat W, const ProArgs pa
     //    out-of-range slots get a zero scale)
     uint4 w[NLOAD];
     uint32_t sc_raw[NLOAD], sb_raw[NLOAD];   // 32-bit: 16-bit elements would be packed, forcing a wait per load
+    uint32_t h_raw[NLOAD];                   // Q5_0 fifth bits
     bool ok[NLOAD];
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i) {
@@ -141,7 +142,10 @@ __global__ __launch_bounds__(WG) void k_gemv(const PackedMat W, const ProArgs pa
             w[i] = *wp;
         }
         sc_raw[i] = __half_as_ushort(W.s[(size_t)rr * spr + ss / SPS]);
-        if constexpr (F == FMT_AFF8) sb_raw[i] = __half_as_ushort(W.b[(size_t)rr * spr + ss / SPS]);
+        sb_raw[i] = 0u;
+        h_raw[i] = 0u;
+        if constexpr (fmt_affine(F)) sb_raw[i] = __half_as_ushort(W.b[(size_t)rr * spr + ss / SPS]);
+        if constexpr (F == FMT_Q5_0) h_raw[i] = W.h[(size_t)rr * (K / 32) + ss];
     }
 
     asm volatile("" ::: "memory");   // keep every load above: all in flight before any wait
@@ -179,16 +183,10 @@ __global__ __launch_bounds__(WG) void k_gemv(const PackedMat W, const ProArgs pa
     for (int i = 0; i < NLOAD; ++i) {
         const int j = SPL == 1 ? 0 : i % SPL;
         const int r = SPL == 1 ? i : i / SPL;
-        const float d = slot_dot<F>(w[i], xs[j]);
+        const float d = slot_dot<F>(w[i], xs[j], h_raw[i]);
         const float sc = ok[i] ? __half2float(__ushort_as_half((unsigned short)sc_raw[i])) : 0.f;
-        float v;
-        if constexpr (F == FMT_Q4_0) v = sc * fmaf(-8.f, sx[j], d);
-        else if constexpr (F == FMT_Q8_0) v = sc * fmaf(-128.f, sx[j], d);
-        else {
-            const float sb = ok[i] ? __half2float(__ushort_as_half((unsigned short)sb_raw[i])) : 0.f;
-            v = fmaf(sc, d, sb * sx[j]);
-        }
-        part[r] += v;
+        const float sb = ok[i] ? __half2float(__ushort_as_half((unsigned short)sb_raw[i])) : 0.f;
+        part[r] += slot_value<F>(d, sx[j], sc, sb);
     }
 
     // 6. reduce over the lanes sharing a row
@@ -301,7 +299,7 @@ hipError_t go_fmt(int pro, int epi, const PackedMat& W, const ProArgs& pa, const
 // one thread per (source row, scale group); `mode` places source row r at destination row
 // place_row(r, mode, hd, row0) (kernels.h)
 __global__ void k_pack(int fmt, const uint8_t* __restrict__ src, int N, int K, uint8_t* dq, __half* ds,
-                       __half* db, int mode, int hd, int row0)
+                       __half* db, uint32_t* dh, int mode, int hd, int row0)
 {
     const int G = fmt_group(fmt), gpr = K / G;
     const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -318,6 +316,25 @@ __global__ void k_pack(int fmt, const uint8_t* __restrict__ src, int N, int K, u
         uint8_t* o = dq + (size_t)dr * K + (size_t)g * 32;
         for (int j = 0; j < 32; ++j) o[j] = (uint8_t)(blk[2 + j] ^ 0x80u);   // int8 q -> q + 128
         ds[(size_t)dr * gpr + g] = __ushort_as_half((unsigned short)(blk[0] | (blk[1] << 8)));
+    } else if (fmt == FMT_Q5_0) {
+        const uint8_t* blk = src + ((size_t)r * gpr + g) * 22;
+        uint8_t* o = dq + (size_t)dr * (K / 2) + (size_t)g * 16;
+        for (int j = 0; j < 16; ++j) o[j] = blk[6 + j];
+        ds[(size_t)dr * gpr + g] = __ushort_as_half((unsigned short)(blk[0] | (blk[1] << 8)));
+        dh[(size_t)dr * gpr + g] = (uint32_t)blk[2] | ((uint32_t)blk[3] << 8) | ((uint32_t)blk[4] << 16) | ((uint32_t)blk[5] << 24);
+    } else if (fmt == FMT_AFF4_G64 || fmt == FMT_AFF4_G32) {
+        // canonical: element 2i low / 2i+1 high nibble of byte i; packed: per 32-element slot,
+        // byte b holds element b (low) and b + 16 (high)
+        const uint8_t* q = src + (size_t)r * (K / 2) + (size_t)g * (G / 2);
+        const uint8_t* s = src + (size_t)N * (K / 2) + ((size_t)r * gpr + g) * 2;
+        const uint8_t* b = src + (size_t)N * (K / 2) + (size_t)N * gpr * 2 + ((size_t)r * gpr + g) * 2;
+        uint8_t* o = dq + (size_t)dr * (K / 2) + (size_t)g * (G / 2);
+        auto nib = [&](int e) { return (q[e >> 1] >> (4 * (e & 1))) & 15; };
+        for (int sl = 0; sl < G / 32; ++sl)
+            for (int j = 0; j < 16; ++j)
+                o[sl * 16 + j] = (uint8_t)(nib(sl * 32 + j) | (nib(sl * 32 + j + 16) << 4));
+        ds[(size_t)dr * gpr + g] = __ushort_as_half((unsigned short)(s[0] | (s[1] << 8)));
+        db[(size_t)dr * gpr + g] = __ushort_as_half((unsigned short)(b[0] | (b[1] << 8)));
     } else {
         const uint8_t* q = src + (size_t)r * K + (size_t)g * 64;
         const uint8_t* s = src + (size_t)N * K + ((size_t)r * gpr + g) * 2;
@@ -372,6 +389,9 @@ hipError_t launch_gemv(int fmt, int pro, int epi, const PackedMat& W, const ProA
     case FMT_Q4_0: return go_fmt<FMT_Q4_0>(pro, epi, W, pa, ea, st);
     case FMT_Q8_0: return go_fmt<FMT_Q8_0>(pro, epi, W, pa, ea, st);
     case FMT_AFF8: return go_fmt<FMT_AFF8>(pro, epi, W, pa, ea, st);
+    case FMT_Q5_0: return go_fmt<FMT_Q5_0>(pro, epi, W, pa, ea, st);
+    case FMT_AFF4_G64: return go_fmt<FMT_AFF4_G64>(pro, epi, W, pa, ea, st);
+    case FMT_AFF4_G32: return go_fmt<FMT_AFF4_G32>(pro, epi, W, pa, ea, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -388,20 +408,23 @@ __global__ __launch_bounds__(WG) void k_gemv_stream(const PackedMat W, const flo
     constexpr int E = FmtT<F>::E, SPS = FmtT<F>::SLOTS_PER_SCALE, G = FmtT<F>::SCALE_GROUP;
     extern __shared__ float4 xl4[];
     const int K = W.K, N = W.N, lpr = K / E, spr = K / G;
-    const size_t rb = F == FMT_Q4_0 ? (size_t)K / 2 : (size_t)K;
+    const size_t rb = fmt_row_bytes(F, K);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int slot = lane & (lpr - 1), sub = lane / lpr;
     const int row0 = ((blockIdx.x * NWAVE + wave) * (64 / lpr) + sub) * NL;
     typedef unsigned int v4u __attribute__((ext_vector_type(4)));
     uint4 w[NL];
-    uint32_t sc[NL], sb[NL];
+    uint32_t sc[NL], sb[NL], hb[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
         const int row = min(row0 + i, N - 1);
         const v4u v = __builtin_nontemporal_load((const v4u*)(W.q + (size_t)row * rb + (size_t)slot * 16));
         w[i] = make_uint4(v.x, v.y, v.z, v.w);
         sc[i] = __half_as_ushort(W.s[(size_t)row * spr + slot / SPS]);
-        if constexpr (F == FMT_AFF8) sb[i] = __half_as_ushort(W.b[(size_t)row * spr + slot / SPS]);
+        sb[i] = 0u;
+        hb[i] = 0u;
+        if constexpr (fmt_affine(F)) sb[i] = __half_as_ushort(W.b[(size_t)row * spr + slot / SPS]);
+        if constexpr (F == FMT_Q5_0) hb[i] = W.h[(size_t)row * (K / 32) + slot];
     }
     const int er = min(row0 + (slot < NL ? slot : NL - 1), N - 1);
     const float bv = bias ? bias[er] : 0.f;
@@ -423,12 +446,9 @@ __global__ __launch_bounds__(WG) void k_gemv_stream(const PackedMat W, const flo
     float part[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-        const float d = slot_dot<F>(w[i], xs);
-        const float s = __half2float(__ushort_as_half((unsigned short)sc[i]));
-        float v;
-        if constexpr (F == FMT_Q4_0) v = s * fmaf(-8.f, sx, d);
-        else if constexpr (F == FMT_Q8_0) v = s * fmaf(-128.f, sx, d);
-        else v = fmaf(s, d, __half2float(__ushort_as_half((unsigned short)sb[i])) * sx);
+        const float d = slot_dot<F>(w[i], xs, hb[i]);
+        const float v = slot_value<F>(d, sx, __half2float(__ushort_as_half((unsigned short)sc[i])),
+                                      __half2float(__ushort_as_half((unsigned short)sb[i])));
         part[i] = group_sum(v, lpr);
     }
     float t = part[0];
@@ -447,15 +467,20 @@ hipError_t launch_gemv_stream(int fmt, const PackedMat& W, const ProArgs& pa, co
         const int rpb = NWAVE * (64 / lpr) * NL;
         const dim3 grid((W.N + rpb - 1) / rpb);
         const size_t lds = (size_t)W.K * sizeof(float);
-        if (fmt == FMT_Q4_0) hipLaunchKernelGGL((k_gemv_stream<FMT_Q4_0, NL>), grid, dim3(WG), lds, st, W, pa.src, ea.bias, ea.y);
-        else if (fmt == FMT_Q8_0) hipLaunchKernelGGL((k_gemv_stream<FMT_Q8_0, NL>), grid, dim3(WG), lds, st, W, pa.src, ea.bias, ea.y);
-        else hipLaunchKernelGGL((k_gemv_stream<FMT_AFF8, NL>), grid, dim3(WG), lds, st, W, pa.src, ea.bias, ea.y);
+#define TSD_STREAM(F_) \
+    if (fmt == F_) hipLaunchKernelGGL((k_gemv_stream<F_, NL>), grid, dim3(WG), lds, st, W, pa.src, ea.bias, ea.y);
+        TSD_STREAM(FMT_Q4_0) TSD_STREAM(FMT_Q8_0) TSD_STREAM(FMT_AFF8) TSD_STREAM(FMT_Q5_0) TSD_STREAM(FMT_AFF4_G64)
+        TSD_STREAM(FMT_AFF4_G32)
+#undef TSD_STREAM
         return hipGetLastError();
     }
     switch (fmt) {
     case FMT_Q4_0: return go_spl<FMT_Q4_0, PRO_LOAD, EPI_STORE, true>(W, pa, ea, st);
     case FMT_Q8_0: return go_spl<FMT_Q8_0, PRO_LOAD, EPI_STORE, true>(W, pa, ea, st);
     case FMT_AFF8: return go_spl<FMT_AFF8, PRO_LOAD, EPI_STORE, true>(W, pa, ea, st);
+    case FMT_Q5_0: return go_spl<FMT_Q5_0, PRO_LOAD, EPI_STORE, true>(W, pa, ea, st);
+    case FMT_AFF4_G64: return go_spl<FMT_AFF4_G64, PRO_LOAD, EPI_STORE, true>(W, pa, ea, st);
+    case FMT_AFF4_G32: return go_spl<FMT_AFF4_G32, PRO_LOAD, EPI_STORE, true>(W, pa, ea, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -469,7 +494,8 @@ hipError_t launch_pack(int fmt, const void* src, int N, int K, void* dst_base, i
     const int threads = 256;
     const long long blocks = (n + threads - 1) / threads;
     hipLaunchKernelGGL(k_pack, dim3((unsigned)blocks), dim3(threads), 0, st, fmt, (const uint8_t*)src, N, K,
-                       base + L.q_off, (__half*)(base + L.s_off), fmt == FMT_AFF8 ? (__half*)(base + L.b_off) : nullptr,
+                       base + L.q_off, (__half*)(base + L.s_off), fmt_affine(fmt) ? (__half*)(base + L.b_off) : nullptr,
+                       fmt == FMT_Q5_0 ? (uint32_t*)(base + L.h_off) : nullptr,
                        mode, hd, dst_row0);
     return hipGetLastError();
 }

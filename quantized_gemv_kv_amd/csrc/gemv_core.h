@@ -24,15 +24,25 @@ __device__ __forceinline__ float ubyte(uint32_t v)
     return r;
 }
 
+// bits 0..3 of v moved to bit 4 of bytes 0..3 (copies at shifts 0, 7, 14, 21 do not overlap,
+// so one 24-bit multiply places every bit k at 8k; the mask keeps those)
+__device__ __forceinline__ uint32_t spread4(uint32_t v) { return (__umul24(v & 0xFu, 0x00204081u) & 0x01010101u) << 4; }
+
+// sum over the slot's elements of code * x: the codes as stored (Q8_0 offset by 128, Q4_0 and
+// Q5_0 unsigned; h: the Q5_0 block's fifth bits, ignored by the other formats)
 template <int F>
-__device__ __forceinline__ float slot_dot(const uint4 w, const float* __restrict__ x)
+__device__ __forceinline__ float slot_dot(const uint4 w, const float* __restrict__ x, uint32_t h = 0u)
 {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    if constexpr (F == FMT_Q4_0) {
+    if constexpr (fmt_nibbles(F)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint32_t lo = ws[j] & 0x0F0F0F0Fu, hi = (ws[j] >> 4) & 0x0F0F0F0Fu;
+            uint32_t lo = ws[j] & 0x0F0F0F0Fu, hi = (ws[j] >> 4) & 0x0F0F0F0Fu;
+            if constexpr (F == FMT_Q5_0) {
+                lo |= spread4(h >> (4 * j));
+                hi |= spread4(h >> (16 + 4 * j));
+            }
             float& al = (j & 1) ? a1 : a0;
             float& ah = (j & 1) ? a3 : a2;
             al = fmaf(ubyte<0>(lo), x[4 * j + 0], al);
@@ -55,6 +65,17 @@ __device__ __forceinline__ float slot_dot(const uint4 w, const float* __restrict
         }
     }
     return (a0 + a1) + (a2 + a3);
+}
+
+// one slot's contribution to its row: d = slot_dot, sx = the slot's sum of x, sc / sb the raw
+// fp16 scale / bias of its group (zero scale for a slot outside the matrix)
+template <int F>
+__device__ __forceinline__ float slot_value(float d, float sx, float sc, float sb)
+{
+    if constexpr (F == FMT_Q4_0) return sc * fmaf(-8.f, sx, d);
+    else if constexpr (F == FMT_Q8_0) return sc * fmaf(-128.f, sx, d);
+    else if constexpr (F == FMT_Q5_0) return sc * fmaf(-16.f, sx, d);
+    else return fmaf(sc, d, sb * sx);
 }
 
 // two sums in one pass (one pair of barriers)

@@ -43,19 +43,22 @@ namespace {
 constexpr int MAX_STEP_WG = 1024;          // workgroups of the persistent step, at most
 constexpr long long STEP_SPIN_LIMIT = 2000000;   // 20 ms of the 100 MHz clock per wait
 
-int group_of(int f) { return f == TSD_W_AFFINE8_G64 ? 64 : 32; }
+int group_of(int f) { return f == TSD_W_AFFINE8_G64 || f == TSD_W_AFFINE4_G64 ? 64 : 32; }
+bool known_format(int f) { return f >= 0 && f < FMT_COUNT; }
 
 size_t canonical_matrix_bytes(int f, int N, int K)
 {
     if (f == TSD_W_Q4_0) return (size_t)N * (K / 32) * 18;
     if (f == TSD_W_Q8_0) return (size_t)N * (K / 32) * 34;
+    if (f == TSD_W_Q5_0) return (size_t)N * (K / 32) * 22;
+    if (f == TSD_W_AFFINE4_G64 || f == TSD_W_AFFINE4_G32) return (size_t)N * K / 2 + (size_t)N * (K / group_of(f)) * 4;
     return (size_t)N * K + (size_t)N * (K / 64) * 4;
 }
 
 tsd_status validate(const tsd_config* c, std::string& msg)
 {
     if (!c) { msg = "null config"; return TSD_ERR_INVALID_ARGUMENT; }
-    if (c->arch < 0 || c->arch > 2 || c->wfmt < 0 || c->wfmt > 2) { msg = "unknown arch or weight format"; return TSD_ERR_INVALID_ARGUMENT; }
+    if (c->arch < 0 || c->arch > 2 || !known_format(c->wfmt)) { msg = "unknown arch or weight format"; return TSD_ERR_INVALID_ARGUMENT; }
     if (c->n_layer <= 0 || c->d_model <= 0 || c->n_head <= 0 || c->n_kv_head <= 0 || c->head_dim <= 0 || c->d_ff <= 0 ||
         c->vocab <= 0 || c->n_ctx <= 0 || c->batch <= 0 || c->n_head % c->n_kv_head) {
         msg = "dimensions must be positive and n_head a multiple of n_kv_head";
@@ -868,7 +871,7 @@ tsd_status tsd_time_kernel(tsd_model* m, int kind, int n_steps, float* avg_us, i
 
 tsd_status tsd_gemv_packed_bytes(int wfmt, int N, int K, size_t* out)
 {
-    if (!out || wfmt < 0 || wfmt > 2 || N <= 0 || K <= 0 || K % group_of(wfmt))
+    if (!out || !known_format(wfmt) || N <= 0 || K <= 0 || K % group_of(wfmt))
         return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "bad format or shape");
     *out = packed_layout(wfmt, N, K).total;
     return TSD_OK;
@@ -890,7 +893,7 @@ tsd_status tsd_gemv_pack(int wfmt, const void* d_w, size_t w_bytes, int N, int K
 tsd_status tsd_gemv(int wfmt, const void* d_packed, int N, int K, int B, const float* d_x, const float* d_bias,
                     float* d_y, void* stream)
 {
-    if (wfmt < 0 || wfmt > 2 || N <= 0 || K <= 0 || K % group_of(wfmt) || B < 1 || B > 4)
+    if (!known_format(wfmt) || N <= 0 || K <= 0 || K % group_of(wfmt) || B < 1 || B > 4)
         return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "bad format or shape");
     if (!d_packed || !d_x || !d_y) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null buffer");
     if (K > 4096 || !gemv_shape_ok(wfmt, K)) return fail(nullptr, TSD_ERR_UNSUPPORTED, "K has no GEMV lane mapping");

@@ -60,9 +60,9 @@ struct Shape {
     static constexpr int E = FmtT<F>::E;
     // loads per lane of each phase: two row slots (or, for rows wider than a wave, one row per
     // wave) for the K = d_model matrices, doubled for the interleaved gate/up rows and the head
-    static constexpr int NL_D = F == FMT_Q4_0 ? 2 : 4;
+    static constexpr int NL_D = fmt_nibbles(F) ? 2 : 4;
     static constexpr int NL_FC = GPT2 ? NL_D : 2 * NL_D;
-    static constexpr int NL_HEAD = F == FMT_Q4_0 ? 4 : 8;
+    static constexpr int NL_HEAD = fmt_nibbles(F) ? 4 : 8;
     static constexpr int NL_O = slices_for(E, QD) == 1 ? 2 : slices_for(E, QD);
     static constexpr int NL_F = slices_for(E, FF) == 1 ? 2 : slices_for(E, FF);
     static_assert(QD <= MAX_K && D <= MAX_K && FF <= MAX_K, "reduction dimension held in LDS");
@@ -82,7 +82,7 @@ struct Geo {
     static constexpr int RPT = NWAVE * RPW;                 // rows per tile
     static constexpr int TILES = (N + RPT - 1) / RPT;
     static constexpr int GW = WIDE ? 64 : LPR;              // lanes reduced per row
-    static constexpr size_t RB = F == FMT_Q4_0 ? (size_t)K / 2 : (size_t)K;   // payload bytes per row
+    static constexpr size_t RB = fmt_nibbles(F) ? (size_t)K / 2 : (size_t)K;   // payload bytes per row
     static constexpr int SPR = K / GS;                      // scales per row
     static_assert(K % E == 0 && (WIDE ? LPR % 64 == 0 : 64 % LPR == 0), "lanes map onto slots exactly");
     static_assert(!WIDE || NL % SPL == 0, "whole rows per wave");
@@ -333,14 +333,17 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
         }
         // every weight and raw scale of this lane (unconditional, clamped rows)
         uint4 w[NL];
-        uint32_t sc_raw[NL], sb_raw[NL];
+        uint32_t sc_raw[NL], sb_raw[NL], h_raw[NL];
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int row = min(G::WIDE ? row0 + i / G::SPL : row0 + i, N - 1);
             const int slot = G::WIDE ? (i % G::SPL) * 64 + lane : slot0;
             w[i] = ld16(W.q + (size_t)row * G::RB + (size_t)slot * 16);
             sc_raw[i] = *glb((const uint16_t*)W.s + (size_t)row * G::SPR + slot / G::SPS);
-            if constexpr (F == FMT_AFF8) sb_raw[i] = *glb((const uint16_t*)W.b + (size_t)row * G::SPR + slot / G::SPS);
+            sb_raw[i] = 0u;
+            h_raw[i] = 0u;
+            if constexpr (fmt_affine(F)) sb_raw[i] = *glb((const uint16_t*)W.b + (size_t)row * G::SPR + slot / G::SPS);
+            if constexpr (F == FMT_Q5_0) h_raw[i] = *glb(W.h + (size_t)row * (K / 32) + slot);
         }
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
@@ -378,13 +381,9 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
         for (int i = 0; i < NL; ++i) {
             const int j = G::WIDE ? i % G::SPL : 0;
             const int r = G::WIDE ? i / G::SPL : i;
-            const float d = slot_dot<F>(w[i], xs[j]);
-            const float sc = __half2float(__ushort_as_half((unsigned short)sc_raw[i]));
-            float v;
-            if constexpr (F == FMT_Q4_0) v = sc * fmaf(-8.f, sx[j], d);
-            else if constexpr (F == FMT_Q8_0) v = sc * fmaf(-128.f, sx[j], d);
-            else v = fmaf(sc, d, __half2float(__ushort_as_half((unsigned short)sb_raw[i])) * sx[j]);
-            part[r] += v;
+            const float d = slot_dot<F>(w[i], xs[j], h_raw[i]);
+            part[r] += slot_value<F>(d, sx[j], __half2float(__ushort_as_half((unsigned short)sc_raw[i])),
+                                     __half2float(__ushort_as_half((unsigned short)sb_raw[i])));
         }
 #pragma unroll
         for (int r = 0; r < NP; ++r) part[r] = group_sum(part[r], G::GW);
@@ -640,6 +639,7 @@ __device__ __forceinline__ PackedMat shift(PackedMat m, long long bytes)
     m.q = shift(m.q, bytes);
     m.s = shift(m.s, bytes);
     m.b = shift(m.b, bytes);
+    m.h = shift(m.h, bytes);
     return m;
 }
 
@@ -876,6 +876,7 @@ const Entry* entries(int& n)
         entry<FMT_Q8_0, A_GPT2, 1024, 16, 16, 64, 4096, 8192>(),    //   and Q8_0
         entry<FMT_Q8_0, A_LLAMA, 1024, 16, 16, 64, 4096, 8192>(),   // Llama-shaped ~520M T3, Q8_0
         entry<FMT_Q4_0, A_LLAMA, 1024, 16, 16, 64, 4096, 8192>(),   //   and Q4_0
+        entry<FMT_Q5_0, A_GPT2, 1024, 16, 16, 64, 4096, 8192>(),    // the T3 in the journal's Q5_0
         // test shapes
         entry<FMT_Q4_0, A_GPT2, 128, 2, 2, 64, 256, 160>(),
         entry<FMT_Q8_0, A_GPT2, 128, 2, 2, 64, 256, 160>(),
@@ -885,6 +886,12 @@ const Entry* entries(int& n)
         entry<FMT_AFF8, A_LLAMA, 128, 2, 2, 64, 256, 160>(),
         entry<FMT_Q4_0, A_GPT2, 128, 2, 2, 64, 256, 1000>(),
         entry<FMT_Q8_0, A_LLAMA, 256, 4, 2, 128, 256, 160>(),
+        entry<FMT_Q5_0, A_GPT2, 128, 2, 2, 64, 256, 160>(),
+        entry<FMT_Q5_0, A_LLAMA, 128, 2, 2, 64, 256, 160>(),
+        entry<FMT_AFF4_G64, A_GPT2, 128, 2, 2, 64, 256, 160>(),
+        entry<FMT_AFF4_G64, A_LLAMA, 128, 2, 2, 64, 256, 160>(),
+        entry<FMT_AFF4_G32, A_GPT2, 128, 2, 2, 64, 256, 160>(),
+        entry<FMT_AFF4_G32, A_LLAMA, 128, 2, 2, 64, 256, 160>(),
     };
     n = (int)(sizeof(tab) / sizeof(tab[0]));
     return tab;

@@ -48,6 +48,32 @@ def q8_0_matrix(rng, N, K, dscale=0.01):
     return blob.reshape(-1), {"q": q, "d": d}
 
 
+PLANAR = ("aff8", "aff4_g64", "aff4_g32")   # formats stored as planes (q, then s, then b)
+
+
+def matrix_into(fmt, N, K, seed, out, chunk_rows=65536):
+    """A tall matrix in `fmt`, drawn in row chunks (each from its own seeded stream) straight into
+    the canonical byte buffer `out` (any array with slice assignment from numpy uint8, e.g. a
+    torch uint8 tensor on the device), so that hundreds of MB never sit in host memory at once."""
+    import torch
+    for r0 in range(0, N, chunk_rows):
+        n = min(chunk_rows, N - r0)
+        blob = matrix(fmt, rng_for(seed, r0, K), n, K)
+        if fmt in PLANAR:
+            qb = n * (K if fmt == "aff8" else K // 2)
+            g = 64 if fmt in ("aff8", "aff4_g64") else 32
+            sb = n * (K // g) * 2
+            qrow = qb // n
+            Q = N * qrow
+            parts = [(r0 * qrow, blob[:qb]), (Q + r0 * (K // g) * 2, blob[qb:qb + sb]),
+                     (Q + N * (K // g) * 2 + r0 * (K // g) * 2, blob[qb + sb:])]
+        else:
+            rowb = blob.size // n
+            parts = [(r0 * rowb, blob)]
+        for off, part in parts:
+            out[off:off + part.size].copy_(torch.from_numpy(part))
+
+
 def q8_0_row_chunks(N, K, seed, chunk_rows=65536):
     """A tall Q8_0 matrix in row chunks (the lone-GEMV law, each chunk from its own seeded
     stream), so that hundreds of MB never sit in host memory at once: yields (row0, blob)."""
@@ -139,6 +165,9 @@ def config(name: str) -> dict:
                 sample_mode=0, top_k=0, temperature=1.0, seed=42)
     if name == "gpt2_medium_q4_0":      # 24-layer T3 Turbo shape
         base.update(arch="gpt2", wfmt="q4_0", n_layer=24, d_model=1024, n_head=16, n_kv_head=16,
+                    head_dim=64, d_ff=4096, vocab=8192, n_ctx=1024)
+    elif name == "gpt2_medium_q5_0":    # the same decoder in the journal's Q5_0 (appendix A3)
+        base.update(arch="gpt2", wfmt="q5_0", n_layer=24, d_model=1024, n_head=16, n_kv_head=16,
                     head_dim=64, d_ff=4096, vocab=8192, n_ctx=1024)
     elif name == "gpt2_layer_q4_0":     # one GPT-2-Medium layer
         base.update(arch="gpt2", wfmt="q4_0", n_layer=1, d_model=1024, n_head=16, n_kv_head=16,

@@ -41,6 +41,23 @@ def test_workspace_sizes_and_validation():
     assert binding.tsd_gemv_packed_bytes("q4_0", 3072, 1024) >= 3072 * 512 + 3072 * 32 * 2
 
 
+def test_new_formats_workspace_and_validation():
+    c3 = synth.config("gpt2_medium_q4_0")
+    n4 = binding.tsd_workspace_bytes(c3)
+    # Q5_0 adds a fifth-bit word per 32 weights; 4-bit affine adds a bias per group
+    n5 = binding.tsd_workspace_bytes(dict(c3, wfmt="q5_0"))
+    assert n4 < n5 < n4 * 1.2
+    for f in ("aff4_g64", "aff4_g32"):
+        assert n4 <= binding.tsd_workspace_bytes(dict(c3, wfmt=f)) < n4 * 1.2
+    assert binding.tsd_gemv_packed_bytes("q5_0", 3072, 1024) >= 3072 * (512 + 32 * 2 + 32 * 4)
+    assert binding.tsd_gemv_packed_bytes("aff4_g32", 3072, 1024) >= 3072 * (512 + 32 * 4)
+    with pytest.raises(binding.TsdError):
+        binding.tsd_gemv_packed_bytes("aff4_g64", 8, 96)       # K not a multiple of the group
+    with pytest.raises(binding.TsdError) as e:
+        binding.tsd_workspace_bytes(dict(synth.config("talker_cp_aff8"), wfmt="aff4_g64"))
+    assert e.value.status == 2                                 # the batched frame is affine-8 only
+
+
 def test_talker_workspace_and_validation():
     c5 = synth.config("talker_cp_aff8")
     n = binding.tsd_workspace_bytes(c5)

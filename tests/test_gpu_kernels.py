@@ -46,6 +46,15 @@ GEMV_CASES = [
     ("aff8", 3, 64, 1),
     ("q4_0", 1, 32, 1),          # one slot per row, 128 rows per wave, one real row
     ("q4_0", 130, 256, 1),
+    ("q5_0", 3072, 1024, 1),     # the journal's third T3 quantisation
+    ("q5_0", 1024, 4096, 2),     # rows spanning two loads
+    ("q5_0", 40, 128, 1),
+    ("aff4_g64", 4096, 1024, 1), # 4-bit affine, groups of 64
+    ("aff4_g64", 1024, 3072, 1),
+    ("aff4_g64", 3, 64, 3),
+    ("aff4_g32", 4096, 1024, 1), # and of 32
+    ("aff4_g32", 1024, 2048, 4),
+    ("aff4_g32", 5, 32, 1),
 ]
 
 

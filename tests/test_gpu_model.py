@@ -78,7 +78,8 @@ def teacher_forced(cfg, w, n_prompt, n_steps, kv_pos=None, seed=3, check_ids=Tru
 
 
 SMALL = [("gpt2", "q4_0"), ("gpt2", "q8_0"), ("gpt2", "aff8"), ("llama", "q8_0"), ("llama", "q4_0"),
-         ("llama", "aff8")]
+         ("llama", "aff8"), ("gpt2", "q5_0"), ("llama", "q5_0"), ("gpt2", "aff4_g64"), ("llama", "aff4_g64"),
+         ("gpt2", "aff4_g32"), ("llama", "aff4_g32")]
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -216,6 +217,17 @@ def test_full_size_step_over_long_cache(name, kv_pos, mode):
     say(f"[model-full] {name} kv_pos={kv_pos} {mode}")
     w = synth.model_weights(cfg, 42)
     worst = teacher_forced(cfg, w, n_prompt=0, n_steps=2, kv_pos=kv_pos, mode=mode)
+    say(f"  worst rel {worst:.2e}")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_full_size_gpt2_q5_0_step_over_long_cache(mode):
+    """The GPT-2-Medium-shaped T3 in Q5_0 (q ~ U{0..31}, d = |N| 0.02) at the decode run's last
+    position."""
+    cfg = dict(synth.config("gpt2_medium_q4_0"), wfmt="q5_0")
+    say(f"[model-full] gpt2_medium q5_0 kv_pos=755 {mode}")
+    w = synth.model_weights(cfg, 42)
+    worst = teacher_forced(cfg, w, n_prompt=0, n_steps=2, kv_pos=755, mode=mode)
     say(f"  worst rel {worst:.2e}")
 
 

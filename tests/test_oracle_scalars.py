@@ -238,3 +238,19 @@ def test_generator_blobs_decode_to_their_draws(orc, fmt):
                   + np.repeat(raw["b"].astype(np.float64), 64, axis=1))
     assert blob.size == orc.matrix_bytes(fmt, N, K)
     assert np.array_equal(orc.dequant(fmt, blob, N, K), expect)
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q5_0", "aff8", "aff4_g64", "aff4_g32"])
+def test_chunked_generator_assembles_the_planes(orc, fmt):
+    """The tall-matrix generator writes each row chunk into its place in the canonical layout:
+    decoded whole, the matrix is the chunks' own decodes stacked."""
+    import torch
+    from quantized_gemv_kv_amd import synth
+    N, K, ch = 10, 128, 4
+    out = torch.zeros(orc.matrix_bytes(fmt, N, K), dtype=torch.uint8)
+    synth.matrix_into(fmt, N, K, 5, out, chunk_rows=ch)
+    W = orc.dequant(fmt, out.numpy(), N, K)
+    for r0 in range(0, N, ch):
+        n = min(ch, N - r0)
+        part = synth.matrix(fmt, synth.rng_for(5, r0, K), n, K)
+        assert np.array_equal(W[r0:r0 + n], orc.dequant(fmt, part, n, K))

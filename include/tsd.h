@@ -85,6 +85,8 @@ typedef enum { TSD_LAUNCH_PERSISTENT = 0, TSD_LAUNCH_PER_OPERATOR = 1 } tsd_laun
  *   TALKER_CP: Talker + code predictor frame loop ([F] §1): LLAMA-shaped Talker of n_layer,
  *          then a LLAMA-shaped predictor of cp_n_layer (same widths) running n_codebooks-1
  *          sequential passes.  One step is one frame of n_codebooks codes.
+ * batch: GPT2/LLAMA 1 or 2 (two rows read every weight once per step: two streams, or a
+ * guided pair, see tsd_sampling.cfg; batch 2 runs PER_OPERATOR); TALKER_CP 1..16.
  * norm_eps is used by every LayerNorm/RMSNorm. */
 typedef struct {
     int32_t arch, wfmt;
@@ -117,6 +119,11 @@ typedef struct {
  *                tokens the row consumed at positions 0..n_past (prompt included; for TALKER_CP
  *                code 0 of every frame); tsd_load_kv leaves the loaded positions without one.
  *                TALKER_CP: the Talker's code-0 head only, never the code predictor's heads.
+ * Classifier-free guidance ([J] §3.19 "Sampling path", §3.21 phase 1: cond and uncond as two
+ * rows of one batch-2 forward, combined at the logits): with cfg = 1 the model's two rows run
+ * the same tokens after their own prompts; the logits that enter the chain (first, before the
+ * penalty) are l_0 + cfg_weight * (l_0 - l_1); the draw uses row 0's counter and history, and
+ * both rows get the id.  cfg_weight 0 is the conditioned row alone.
  * Draws with k > 1024 (or a vocabulary over 12288) are TSD_ERR_UNSUPPORTED. */
 typedef enum { TSD_ORDER_T3 = 0, TSD_ORDER_MTL = 1 } tsd_sampler_order;
 typedef struct {
@@ -127,7 +134,9 @@ typedef struct {
     float top_p;
     float min_p;
     float rep_penalty;
-    int32_t order; /* tsd_sampler_order */
+    int32_t order;    /* tsd_sampler_order */
+    int32_t cfg;      /* 1: classifier-free guidance over the two rows of a batch-2 GPT2/LLAMA model */
+    float cfg_weight; /* w: the draw (or argmax) is over cond + w (cond - uncond), row 0 = cond */
 } tsd_sampling;
 
 typedef struct {

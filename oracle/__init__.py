@@ -36,7 +36,8 @@ class _Cfg(ctypes.Structure):
         ("cp_n_layer", ctypes.c_int), ("n_codebooks", ctypes.c_int), ("cp_vocab", ctypes.c_int),
         ("sample_mode", ctypes.c_int), ("top_k", ctypes.c_int), ("temperature", ctypes.c_double),
         ("seed", ctypes.c_uint64), ("top_p", ctypes.c_double), ("min_p", ctypes.c_double),
-        ("rep_penalty", ctypes.c_double), ("sample_order", ctypes.c_int)]
+        ("rep_penalty", ctypes.c_double), ("sample_order", ctypes.c_int), ("cfg", ctypes.c_int),
+        ("cfg_weight", ctypes.c_double)]
 
 
 class _Samp(ctypes.Structure):
@@ -229,7 +230,7 @@ def sample_chain(logits, u, mode=1, top_k=0, temperature=1.0, top_p=0.0, min_p=0
 # ---- models -----------------------------------------------------------------------------------
 
 # sampler-chain fields a config may leave out: every filter off, the T3 order
-CHAIN_DEFAULTS = {"top_p": 0.0, "min_p": 0.0, "rep_penalty": 1.0, "sample_order": "t3"}
+CHAIN_DEFAULTS = {"top_p": 0.0, "min_p": 0.0, "rep_penalty": 1.0, "sample_order": "t3", "cfg": 0, "cfg_weight": 0.0}
 
 
 def _cfg_struct(cfg: dict) -> _Cfg:

@@ -632,6 +632,7 @@ orc_model* orc_model_create(const orc_config* c, const void* const* w, const siz
     if (nw < 0) { set_err("unknown arch"); return NULL; }
     if (c->n_layer <= 0 || c->d_model <= 0 || c->n_head <= 0 || c->n_kv_head <= 0 || c->head_dim <= 0 ||
         c->d_ff <= 0 || c->vocab <= 0 || c->n_ctx <= 0 || c->batch <= 0 || c->n_head % c->n_kv_head ||
+        (c->cfg && (c->batch != 2 || c->arch == ORC_TALKER_CP)) ||
         c->head_dim % 2) { set_err("bad dimensions"); return NULL; }
     if (c->arch == ORC_GPT2 && (c->n_head * c->head_dim != c->d_model || c->n_kv_head != c->n_head)) {
         set_err("GPT2 needs n_head*head_dim == d_model and n_kv_head == n_head"); return NULL;
@@ -881,6 +882,7 @@ static int forward_position(orc_model* m, const int32_t* tok_in, int32_t* tok_ou
         orc_gemv(c->wfmt, m->head, c->vocab, d, h, NULL, lg);
         double* dst = m->logits + (size_t)b * C * m->vmax;
         memcpy(dst, lg, sizeof(double) * c->vocab);
+        if (c->cfg) continue;                   /* guided: one pick after both rows, below */
         int c0 = pick(m, lg, c->vocab, b, pos, 0);
         m->last[(size_t)b * C] = c0;
         if (c->arch != ORC_TALKER_CP) continue;
@@ -903,6 +905,17 @@ static int forward_position(orc_model* m, const int32_t* tok_in, int32_t* tok_ou
             prev = pick(m, lg, c->cp_vocab, b, pos, j);
             m->last[(size_t)b * C + j] = prev;
         }
+    }
+    if (c->cfg && with_head) {
+        /* READING (classifier-free guidance, [J] §3.19: cond and uncond forwards combined at the
+         * logits before the rest of the chain): l = l_cond + w (l_cond - l_uncond), row 0 the
+         * conditioned one; the pick uses row 0's counter and history and both rows take it */
+        const double* l0 = m->logits;
+        const double* l1 = m->logits + (size_t)C * m->vmax;
+        for (int i = 0; i < c->vocab; ++i) lg[i] = l0[i] + c->cfg_weight * (l0[i] - l1[i]);
+        int id = pick(m, lg, c->vocab, 0, pos, 0);
+        m->last[0] = id;
+        m->last[C] = id;
     }
     free(x); free(h); free(lg);
     m->n_past = pos + 1;

@@ -40,6 +40,8 @@ typedef struct {
     uint64_t seed;
     double top_p, min_p, rep_penalty;      /* off: 0 (or >= 1), 0, 0 (or 1) */
     int sample_order;                      /* ORC_ORDER_T3 or ORC_ORDER_MTL */
+    int cfg;                               /* 1: rows 0 (cond) and 1 (uncond) guided together */
+    double cfg_weight;
 } orc_config;
 
 /* sampler chain orders ([J] §3.2 and §3.19) */

@@ -47,7 +47,8 @@ class tsd_config(ctypes.Structure):
 class tsd_sampling(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("top_k", ctypes.c_int32), ("temperature", ctypes.c_float),
                 ("seed", ctypes.c_uint64), ("top_p", ctypes.c_float), ("min_p", ctypes.c_float),
-                ("rep_penalty", ctypes.c_float), ("order", ctypes.c_int32)]
+                ("rep_penalty", ctypes.c_float), ("order", ctypes.c_int32), ("cfg", ctypes.c_int32),
+                ("cfg_weight", ctypes.c_float)]
 
 
 ORDERS = {"t3": 0, "mtl": 1}
@@ -57,7 +58,7 @@ def make_sampling(d: dict) -> tsd_sampling:
     """tsd_sampling from a dict (missing fields: greedy, every filter off, the T3 order)."""
     return tsd_sampling(d.get("mode", 0), d.get("top_k", 0), d.get("temperature", 1.0), d.get("seed", 0),
                         d.get("top_p", 0.0), d.get("min_p", 0.0), d.get("rep_penalty", 0.0),
-                        ORDERS.get(d.get("order", "t3"), d.get("order", 0)))
+                        ORDERS.get(d.get("order", "t3"), d.get("order", 0)), d.get("cfg", 0), d.get("cfg_weight", 0.0))
 
 
 class tsd_tensor(ctypes.Structure):

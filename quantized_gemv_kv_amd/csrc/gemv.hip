@@ -93,8 +93,23 @@ template <int EPI> struct EpiIsPair { static constexpr bool v = EPI == EPI_SWIGL
 // STREAM: the weight loads carry the non-temporal hint (a matrix read once, larger than the
 // caches: the hint keeps it from displacing what stays resident and streams measurably faster)
 template <int F, int SPL, int NLOAD, int PRO, int EPI, bool STREAM = false>
-__global__ __launch_bounds__(WG) void k_gemv(const PackedMat W, const ProArgs pa, const EpiArgs ea)
+__global__ __launch_bounds__(WG) void k_gemv(const PackedMat W, const ProArgs pa0, const EpiArgs ea0)
 {
+    // batch row blockIdx.y: its input, output, cache and key pointers
+    ProArgs pa = pa0;
+    EpiArgs ea = ea0;
+    if (blockIdx.y) {
+        const long long b = blockIdx.y;
+        if (pa.src) pa.src += b * pa.rs_src;
+        if (pa.x_out) pa.x_out += b * pa.rs_src;
+        if (pa.tok) pa.tok += b * pa.rs_tok;
+        if (pa.part) pa.part += b * pa.rs_part;
+        if (ea.y) ea.y += b * ea.rs_y;
+        if (ea.q) ea.q += b * ea.rs_q;
+        if (ea.kc) ea.kc += b * ea.rs_kv;
+        if (ea.vc) ea.vc += b * ea.rs_kv;
+        if (ea.best) ea.best += b * gridDim.x;
+    }
     constexpr int E = FmtT<F>::E, SPS = FmtT<F>::SLOTS_PER_SCALE, G = FmtT<F>::SCALE_GROUP;
     constexpr int RWS = SPL == 1 ? 1 : NLOAD / SPL;       // rows per wave when rows span loads
     constexpr int NP = SPL == 1 ? NLOAD : RWS;             // partial sums per lane
@@ -249,35 +264,35 @@ int rows_per_block_impl(int fmt, int K)
 }
 
 template <int F, int PRO, int EPI, int SPL, bool STREAM = false>
-hipError_t go(const PackedMat& W, const ProArgs& pa, const EpiArgs& ea, hipStream_t st)
+hipError_t go(const PackedMat& W, const ProArgs& pa, const EpiArgs& ea, hipStream_t st, int B = 1)
 {
     // a streamed matrix keeps twice the loads in flight per lane when a row fits one wave
     constexpr int NLOAD = STREAM && SPL == 1 ? 4 : nload_for<SPL>();
     const int lpr = W.K / FmtT<F>::E;
     const int rpb = NWAVE * (SPL == 1 ? NLOAD * (64 / lpr) : NLOAD / SPL);
     const int grid = (W.N + rpb - 1) / rpb;
-    hipLaunchKernelGGL((k_gemv<F, SPL, NLOAD, PRO, EPI, STREAM>), dim3(grid), dim3(WG), (size_t)W.K * sizeof(float), st, W, pa,
-                       ea);
+    hipLaunchKernelGGL((k_gemv<F, SPL, NLOAD, PRO, EPI, STREAM>), dim3(grid, B), dim3(WG), (size_t)W.K * sizeof(float), st, W,
+                       pa, ea);
     return hipGetLastError();
 }
 
 template <int F, int PRO, int EPI, bool STREAM = false>
-hipError_t go_spl(const PackedMat& W, const ProArgs& pa, const EpiArgs& ea, hipStream_t st)
+hipError_t go_spl(const PackedMat& W, const ProArgs& pa, const EpiArgs& ea, hipStream_t st, int B = 1)
 {
     switch (spl_for(F, W.K)) {
-    case 1: return go<F, PRO, EPI, 1, STREAM>(W, pa, ea, st);
-    case 2: return go<F, PRO, EPI, 2, STREAM>(W, pa, ea, st);
-    case 3: return go<F, PRO, EPI, 3, STREAM>(W, pa, ea, st);
-    case 4: return go<F, PRO, EPI, 4, STREAM>(W, pa, ea, st);
+    case 1: return go<F, PRO, EPI, 1, STREAM>(W, pa, ea, st, B);
+    case 2: return go<F, PRO, EPI, 2, STREAM>(W, pa, ea, st, B);
+    case 3: return go<F, PRO, EPI, 3, STREAM>(W, pa, ea, st, B);
+    case 4: return go<F, PRO, EPI, 4, STREAM>(W, pa, ea, st, B);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <int F>
-hipError_t go_fmt(int pro, int epi, const PackedMat& W, const ProArgs& pa, const EpiArgs& ea, hipStream_t st)
+hipError_t go_fmt(int pro, int epi, const PackedMat& W, const ProArgs& pa, const EpiArgs& ea, hipStream_t st, int B)
 {
 #define TSD_CASE(PRO_, EPI_) \
-    if (pro == PRO_ && epi == EPI_) return go_spl<F, PRO_, EPI_>(W, pa, ea, st);
+    if (pro == PRO_ && epi == EPI_) return go_spl<F, PRO_, EPI_>(W, pa, ea, st, B);
     TSD_CASE(PRO_LOAD, EPI_STORE)
     TSD_CASE(PRO_LOAD, EPI_RESID)
     TSD_CASE(PRO_ATTN, EPI_RESID)
@@ -351,47 +366,50 @@ __global__ void k_pack(int fmt, const uint8_t* __restrict__ src, int N, int K, u
 int gemv_rows_per_block(int fmt, int K, int) { return rows_per_block_impl(fmt, K); }
 
 namespace {
-__global__ __launch_bounds__(256) void k_argmax_finalize(const unsigned long long* __restrict__ best, int n, int* tok,
+__global__ __launch_bounds__(256) void k_argmax_finalize(const unsigned long long* __restrict__ best, int n, int B, int* tok,
                                                          int* hist, int* seq, int hist_stride, int* pos)
 {
     __shared__ unsigned long long bk[NWAVE];
-    unsigned long long m = 0ull;
-    for (int i = threadIdx.x; i < n; i += WG) m = best[i] > m ? best[i] : m;
-    m = wave_max_u64(m);
-    if ((threadIdx.x & 63) == 0) bk[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned long long b = bk[0];
-        for (int i = 1; i < NWAVE; ++i) b = bk[i] > b ? bk[i] : b;
-        const int id = (int)(0xFFFFFFFFu - (uint32_t)(b & 0xFFFFFFFFull));
-        const int p = *pos;
-        if (seq) seq[(size_t)p * hist_stride] = *tok;
-        *tok = id;
-        if (hist) hist[(size_t)p * hist_stride] = id;
-        *pos = p + 1;
+    const int p = *pos;   // every row is read before the position advances (one workgroup)
+    for (int r = 0; r < B; ++r) {
+        unsigned long long m = 0ull;
+        for (int i = threadIdx.x; i < n; i += WG) m = best[(size_t)r * n + i] > m ? best[(size_t)r * n + i] : m;
+        m = wave_max_u64(m);
+        if ((threadIdx.x & 63) == 0) bk[threadIdx.x >> 6] = m;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            unsigned long long b = bk[0];
+            for (int i = 1; i < NWAVE; ++i) b = bk[i] > b ? bk[i] : b;
+            const int id = (int)(0xFFFFFFFFu - (uint32_t)(b & 0xFFFFFFFFull));
+            if (seq) seq[(size_t)p * hist_stride + r] = tok[r];
+            tok[r] = id;
+            if (hist) hist[(size_t)p * hist_stride + r] = id;
+        }
+        __syncthreads();
     }
+    if (threadIdx.x == 0) *pos = p + 1;
 }
 }  // namespace
 
-hipError_t launch_argmax_finalize(const unsigned long long* best, int n, int* tok, int* hist, int* seq, int hist_stride,
+hipError_t launch_argmax_finalize(const unsigned long long* best, int n, int B, int* tok, int* hist, int* seq, int hist_stride,
                                   int* pos, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_argmax_finalize, dim3(1), dim3(WG), 0, st, best, n, tok, hist, seq, hist_stride, pos);
+    hipLaunchKernelGGL(k_argmax_finalize, dim3(1), dim3(WG), 0, st, best, n, B, tok, hist, seq, hist_stride, pos);
     return hipGetLastError();
 }
 
 hipError_t launch_gemv(int fmt, int pro, int epi, const PackedMat& W, const ProArgs& pa, const EpiArgs& ea,
-                       hipStream_t st)
+                       hipStream_t st, int B)
 {
-    if (W.K > MAX_K || !gemv_shape_ok(fmt, W.K) || W.N <= 0) return hipErrorInvalidValue;
+    if (W.K > MAX_K || !gemv_shape_ok(fmt, W.K) || W.N <= 0 || B < 1 || B > 65535) return hipErrorInvalidValue;
     if (pro == PRO_ATTN && W.K > 4 * NJA * WG) return hipErrorInvalidValue;
     switch (fmt) {
-    case FMT_Q4_0: return go_fmt<FMT_Q4_0>(pro, epi, W, pa, ea, st);
-    case FMT_Q8_0: return go_fmt<FMT_Q8_0>(pro, epi, W, pa, ea, st);
-    case FMT_AFF8: return go_fmt<FMT_AFF8>(pro, epi, W, pa, ea, st);
-    case FMT_Q5_0: return go_fmt<FMT_Q5_0>(pro, epi, W, pa, ea, st);
-    case FMT_AFF4_G64: return go_fmt<FMT_AFF4_G64>(pro, epi, W, pa, ea, st);
-    case FMT_AFF4_G32: return go_fmt<FMT_AFF4_G32>(pro, epi, W, pa, ea, st);
+    case FMT_Q4_0: return go_fmt<FMT_Q4_0>(pro, epi, W, pa, ea, st, B);
+    case FMT_Q8_0: return go_fmt<FMT_Q8_0>(pro, epi, W, pa, ea, st, B);
+    case FMT_AFF8: return go_fmt<FMT_AFF8>(pro, epi, W, pa, ea, st, B);
+    case FMT_Q5_0: return go_fmt<FMT_Q5_0>(pro, epi, W, pa, ea, st, B);
+    case FMT_AFF4_G64: return go_fmt<FMT_AFF4_G64>(pro, epi, W, pa, ea, st, B);
+    case FMT_AFF4_G32: return go_fmt<FMT_AFF4_G32>(pro, epi, W, pa, ea, st, B);
     default: return hipErrorInvalidValue;
     }
 }

@@ -36,6 +36,10 @@ struct ProArgs {
     // a_chunk positions
     const float* part;
     int a_hd, a_max_split, a_chunk, pos_add;
+    // batch rows (blockIdx.y = row b): src and x_out move by b * rs_src, tok by b * rs_tok, part
+    // by b * rs_part elements
+    long long rs_src, rs_part;
+    int rs_tok;
 };
 
 enum EpiKind : int {
@@ -61,11 +65,15 @@ struct EpiArgs {
     const int* pos;      // device position (K/V slot, RoPE angle)
     // head / argmax: best key of workgroup i -> best[i]
     unsigned long long* best;
+    // batch rows (blockIdx.y = row b): y moves by b * rs_y, q by b * rs_q, the caches by
+    // b * rs_kv elements, best by b * (workgroups per row)
+    long long rs_y, rs_q, rs_kv;
 };
 
-// Launch the fused GEMV y = epilogue(W . prologue(x)).  Returns hipSuccess or the launch error.
+// Launch the fused GEMV y = epilogue(W . prologue(x)) for B batch rows (one grid row each, the
+// row strides in pa / ea).  Returns hipSuccess or the launch error.
 hipError_t launch_gemv(int fmt, int pro, int epi, const PackedMat& W, const ProArgs& pa, const EpiArgs& ea,
-                       hipStream_t st);
+                       hipStream_t st, int B = 1);
 // y = W x (+bias) with the weight loads marked non-temporal: for a matrix streamed once
 hipError_t launch_gemv_stream(int fmt, const PackedMat& W, const ProArgs& pa, const EpiArgs& ea, hipStream_t st);
 // the tile (rows per workgroup) the launcher uses for a shape; for byte/launch accounting
@@ -119,7 +127,8 @@ hipError_t launch_attention_merge(const AttnArgs& a, int n_keys, hipStream_t st)
 // history at the current position and advance the position (one workgroup)
 // seq: when set, seq[*pos * hist_stride] = the token consumed at this position (*tok before it is
 // overwritten by the id)
-hipError_t launch_argmax_finalize(const unsigned long long* best, int n, int* tok, int* hist, int* seq, int hist_stride, int* pos,
+// B rows: row b's keys at best + b * n, its id to tok[b], hist[*pos * hist_stride + b] (and seq)
+hipError_t launch_argmax_finalize(const unsigned long long* best, int n, int B, int* tok, int* hist, int* seq, int hist_stride, int* pos,
                                   hipStream_t st);
 
 // ---- persistent decode step (step.hip) ---------------------------------------------------------
@@ -181,6 +190,10 @@ hipError_t launch_step(const void* kernel, const StepArgs* d_args, int n_wg, hip
 // is *posp when posp is set (then the id is also written to hist[pos * hist_stride], the consumed
 // token *cur to seq_out[pos * seq_stride], and *posp advanced), else pos_value.  The penalty's
 // history is seq[p * seq_stride] for p < n_seq (n_seq < 0: p < pos), then *cur when cur is set.
+// rows > 1: row r (counter row + r) draws from logits + r * ld_logits with history seq + r and
+// consumed token cur[r], writing out[r], hist[.. + r], seq_out[.. + r].  cfg: rows must be 2 and
+// one draw is made from the guided logits l0 + cfg_weight (l0 - l1) with row 0's counter and
+// history; both rows get the id.
 struct SampleArgs {
     const float* logits;
     int n;
@@ -197,6 +210,10 @@ struct SampleArgs {
     int n_seq;
     const int* cur;
     int* seq_out;
+    int rows;
+    long long ld_logits;
+    int cfg;
+    float cfg_weight;
 };
 bool sample_supported(int n, int k);
 size_t sample_lds_bytes(int n);

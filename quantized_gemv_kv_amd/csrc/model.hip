@@ -76,7 +76,7 @@ tsd_status validate(const tsd_config* c, std::string& msg)
         return TSD_ERR_INVALID_ARGUMENT;
     }
     if (c->arch == TSD_ARCH_TALKER_CP) return talker_validate(c, msg);
-    if (c->batch != 1) { msg = "GPT2/LLAMA decode supports batch 1"; return TSD_ERR_UNSUPPORTED; }
+    if (c->batch != 1 && c->batch != 2) { msg = "GPT2/LLAMA decode supports batch 1 or 2"; return TSD_ERR_UNSUPPORTED; }
     if (c->head_dim != 64 && c->head_dim != 128) { msg = "head_dim must be 64 or 128"; return TSD_ERR_UNSUPPORTED; }
     for (int K : {c->d_model, c->d_ff, qd})
         if (K > 4096 || !gemv_shape_ok(c->wfmt, K)) {
@@ -208,11 +208,12 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
 hipError_t enqueue_layer(tsd_model* m, int l, hipStream_t st, const int* pos, bool embed, Probe* pr = nullptr)
 {
     const tsd_config& c = m->c;
-    const int d = c.d_model, H = c.n_head, Hk = c.n_kv_head, hd = c.head_dim;
+    const int d = c.d_model, H = c.n_head, Hk = c.n_kv_head, hd = c.head_dim, B = c.batch;
     const LayerW& w = m->L[l];
     const bool gpt2 = c.arch == TSD_ARCH_GPT2;
     __half* kc = m->kc + m->kv_layer_elems * l;
     __half* vc = m->vc + m->kv_layer_elems * l;
+    const long long kv_row = (long long)Hk * c.n_ctx * hd;   // one batch row's slab of a layer's cache
     hipError_t e;
 
     // norm + fused QKV (+bias | +RoPE) + K/V append
@@ -241,10 +242,14 @@ hipError_t enqueue_layer(tsd_model* m, int l, hipStream_t st, const int* pos, bo
     ea.vc = vc;
     ea.rope = m->rope;
     ea.pos = pos;
+    pa.rs_src = d;
+    pa.rs_tok = m->tpp;
+    ea.rs_q = m->qkv_rows;
+    ea.rs_kv = kv_row;
     const int pro = embed ? (gpt2 ? PRO_LN_EMB : PRO_RMS_EMB) : (gpt2 ? PRO_LN : PRO_RMS);
     {
         Bracket br(pr, KIND_QKV, st);
-        e = launch_gemv(c.wfmt, pro, gpt2 ? EPI_QKV : EPI_QKV_ROPE, w.qkv, pa, ea, st);
+        e = launch_gemv(c.wfmt, pro, gpt2 ? EPI_QKV : EPI_QKV_ROPE, w.qkv, pa, ea, st, B);
     }
     if (e != hipSuccess) return e;
 
@@ -257,7 +262,7 @@ hipError_t enqueue_layer(tsd_model* m, int l, hipStream_t st, const int* pos, bo
     aa.out = m->attn;
     aa.ldo = H * hd;
     aa.part = m->part;
-    aa.B = 1;
+    aa.B = B;
     aa.H = H;
     aa.Hkv = Hk;
     aa.hd = hd;
@@ -276,12 +281,14 @@ hipError_t enqueue_layer(tsd_model* m, int l, hipStream_t st, const int* pos, bo
     po.a_chunk = ATTN_CHUNK;
     po.a_max_split = (c.n_ctx + po.a_chunk - 1) / po.a_chunk;
     po.pos = pos;
+    po.rs_part = (long long)H * po.a_max_split * (hd + 4);
     EpiArgs eo{};
     eo.y = m->x;
     eo.bias = w.bo;
+    eo.rs_y = d;
     {
         Bracket br(pr, KIND_OPROJ, st);
-        e = launch_gemv(c.wfmt, PRO_ATTN, EPI_RESID, w.o, po, eo, st);
+        e = launch_gemv(c.wfmt, PRO_ATTN, EPI_RESID, w.o, po, eo, st, B);
     }
     if (e != hipSuccess) return e;
 
@@ -291,24 +298,27 @@ hipError_t enqueue_layer(tsd_model* m, int l, hipStream_t st, const int* pos, bo
     pf.g = w.n2g;
     pf.beta = w.n2b;
     pf.eps = c.norm_eps;
+    pf.rs_src = d;
     EpiArgs ef{};
     ef.y = m->h;
     ef.bias = w.bfc;
+    ef.rs_y = c.d_ff;
     {
         Bracket br(pr, KIND_FC, st);
-        e = launch_gemv(c.wfmt, gpt2 ? PRO_LN : PRO_RMS, gpt2 ? EPI_GELU : EPI_SWIGLU, w.fc, pf, ef, st);
+        e = launch_gemv(c.wfmt, gpt2 ? PRO_LN : PRO_RMS, gpt2 ? EPI_GELU : EPI_SWIGLU, w.fc, pf, ef, st, B);
     }
     if (e != hipSuccess) return e;
 
     // down projection + bias + residual
     ProArgs pd{};
     pd.src = m->h;
+    pd.rs_src = c.d_ff;
     EpiArgs ed{};
     ed.y = m->x;
     ed.bias = w.bdown;
-    (void)d;
+    ed.rs_y = d;
     Bracket br(pr, KIND_DOWN, st);
-    return launch_gemv(c.wfmt, PRO_LOAD, EPI_RESID, w.down, pd, ed, st);
+    return launch_gemv(c.wfmt, PRO_LOAD, EPI_RESID, w.down, pd, ed, st, B);
 }
 
 hipError_t enqueue_step(tsd_model* m, hipStream_t st, Probe* pr = nullptr)
@@ -328,15 +338,22 @@ hipError_t enqueue_step(tsd_model* m, hipStream_t st, Probe* pr = nullptr)
     ph.g = m->nfg;
     ph.beta = m->nfb;
     ph.eps = c.norm_eps;
+    ph.rs_src = c.d_model;
     EpiArgs eh{};
     eh.y = m->logits;
     eh.ldy = c.vocab;
     eh.best = m->best;
+    eh.rs_y = c.vocab;
     Bracket br(pr, KIND_HEAD, st);
-    hipError_t e = launch_gemv(c.wfmt, c.arch == TSD_ARCH_GPT2 ? PRO_LN : PRO_RMS, EPI_HEAD_ARGMAX, m->head, ph, eh, st);
+    hipError_t e = launch_gemv(c.wfmt, c.arch == TSD_ARCH_GPT2 ? PRO_LN : PRO_RMS, EPI_HEAD_ARGMAX, m->head, ph, eh, st,
+                               c.batch);
     if (e != hipSuccess) return e;
     if (m->draw) {
         SampleArgs s{};
+        s.rows = c.batch;
+        s.ld_logits = c.vocab;
+        s.cfg = m->samp.cfg;
+        s.cfg_weight = m->samp.cfg_weight;
         s.logits = m->logits;
         s.n = c.vocab;
         s.ch = m->chain;
@@ -354,7 +371,7 @@ hipError_t enqueue_step(tsd_model* m, hipStream_t st, Probe* pr = nullptr)
     }
     const int nblk = (c.vocab + gemv_rows_per_block(c.wfmt, c.d_model, EPI_HEAD_ARGMAX) - 1) /
                      gemv_rows_per_block(c.wfmt, c.d_model, EPI_HEAD_ARGMAX);
-    return launch_argmax_finalize(m->best, nblk, m->tok, m->hist, m->seq, c.batch * m->tpp, m->pos, st);
+    return launch_argmax_finalize(m->best, nblk, c.batch, m->tok, m->hist, m->seq, c.batch * m->tpp, m->pos, st);
 }
 
 tsd_status pack_weights(tsd_model* m, const tsd_tensor* w)
@@ -417,6 +434,7 @@ tsd_status setup_step(tsd_model* m)
     if (c.launch_mode == TSD_LAUNCH_PER_OPERATOR) return TSD_OK;
     if (c.launch_mode != TSD_LAUNCH_PERSISTENT) return fail(m, TSD_ERR_INVALID_ARGUMENT, "unknown launch_mode");
     if (c.arch == TSD_ARCH_TALKER_CP) return TSD_OK;   // the frame runs one launch per operator
+    if (c.batch != 1) return TSD_OK;                    // two rows run one launch per operator
     m->step_fn = step_kernel_for(c.wfmt, c.arch == TSD_ARCH_LLAMA, c.d_model, c.n_head, c.n_kv_head, c.head_dim, c.d_ff,
                                  c.vocab);
     if (!m->step_fn) return TSD_OK;   // this shape runs one launch per operator
@@ -580,6 +598,8 @@ tsd_status check_sampling(const tsd_sampling* s, std::string& msg)
     if (s->order != TSD_ORDER_T3 && s->order != TSD_ORDER_MTL) return msg = "unknown sampler order", TSD_ERR_INVALID_ARGUMENT;
     if (s->min_p > 0.f && s->order != TSD_ORDER_MTL)
         return msg = "min_p is a step of the multilingual order (TSD_ORDER_MTL)", TSD_ERR_INVALID_ARGUMENT;
+    if (s->cfg != 0 && s->cfg != 1) return msg = "cfg must be 0 or 1", TSD_ERR_INVALID_ARGUMENT;
+    if (!std::isfinite(s->cfg_weight)) return msg = "cfg_weight must be finite", TSD_ERR_INVALID_ARGUMENT;
     return TSD_OK;
 }
 
@@ -591,7 +611,11 @@ bool chain_of(const tsd_sampling* s, int n, bool with_penalty, SampChain* ch, in
     *ch = SampChain{1.f, 1, 0.f, 0.f, 1.f, SAMP_ORDER_MTL};
     *draw = 0;
     if (s->mode == 0) {
-        if (!pen) return true;
+        if (!pen && !s->cfg) return true;   // greedy over guided logits is the draw's k = 1
+        if (!pen) {
+            *draw = 1;
+            return sample_supported(n, 1);
+        }
         ch->penalty = s->rep_penalty;
         *draw = 1;
         return sample_supported(n, 1);
@@ -631,6 +655,9 @@ tsd_status tsd_model_create(const tsd_config* cfg, const tsd_tensor* weights, in
     std::string smsg;
     s = check_sampling(&sv, smsg);
     if (s != TSD_OK) return fail(nullptr, s, smsg);
+    if (sv.cfg && (cfg->arch == TSD_ARCH_TALKER_CP || cfg->batch != 2))
+        return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "classifier-free guidance needs a GPT2/LLAMA model of batch 2 "
+                                                       "(row 0 conditioned, row 1 unconditioned)");
     SampChain ch{}, cch{};
     int draw = 0, cdraw = 0;
     if (!chain_of(&sv, cfg->vocab, true, &ch, &draw))
@@ -1004,6 +1031,7 @@ tsd_status tsd_sample(const float* d_logits, int n, const tsd_sampling* s, const
     std::string msg;
     tsd_status st = check_sampling(s, msg);
     if (st != TSD_OK) return fail(nullptr, st, msg);
+    if (s->cfg) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "guidance combines a model's two rows: not a standalone draw");
     SampChain ch{};
     int draw = 0;
     if (!chain_of(s, n, true, &ch, &draw)) return fail(nullptr, TSD_ERR_UNSUPPORTED, "k <= 1024 and n <= 12288");

@@ -179,6 +179,43 @@ def test_batch_rows_are_independent(orc):
         assert np.array_equal(m1.logits()[0], m2.logits()[b])
 
 
+@pytest.mark.parametrize("arch,fmt", [("gpt2", "q4_0"), ("llama", "q8_0")])
+def test_guidance_reduces_to_the_conditioned_row(orc, arch, fmt):
+    """Classifier-free guidance over two rows: with w = 0 the draws are those of a batch-1 model
+    on the conditioned prompt (the same counters, the same history), and both rows receive them;
+    with identical prompts the guided logits are the conditioned ones for any w."""
+    base = dict(sample_mode=1, top_k=20, temperature=0.9, top_p=0.9, rep_penalty=1.3, sample_order="mtl", seed=77)
+    cfg1 = synth.small_config(arch, fmt, batch=1, **base)
+    w = synth.model_weights(cfg1, 42, norm_std=0.5)
+    toks = synth.prompt_tokens(dict(cfg1, batch=2), 6, seed=3)
+    for weight, prompts in [(0.0, toks), (2.5, np.stack([toks[0], toks[0]]))]:
+        m2 = orc.OracleModel(dict(cfg1, batch=2, cfg=1, cfg_weight=weight), w)
+        m1 = orc.OracleModel(cfg1, w)
+        a, b = m2.prefill(prompts), m1.prefill(prompts[:1])
+        for _ in range(10):
+            assert a[0, 0] == a[1, 0] == b[0, 0]
+            a, b = m2.step(), m1.step()
+        m1.close()
+        m2.close()
+
+
+def test_guidance_combines_cond_and_uncond_logits(orc):
+    """Greedy under guidance takes the argmax of l_cond + w (l_cond - l_uncond): row 0 is the
+    conditioned row (swapping the prompts changes the pick where the combination says so)."""
+    cfg = synth.small_config("llama", "q8_0", batch=2, cfg=1, cfg_weight=1.5)
+    w = synth.model_weights(cfg, 42, norm_std=0.5)
+    toks = synth.prompt_tokens(cfg, 6, seed=4)
+    m = orc.OracleModel(cfg, w)
+    nxt = m.prefill(toks)
+    for _ in range(8):
+        lg = m.logits()
+        guided = lg[0] + 1.5 * (lg[0] - lg[1])
+        assert nxt[0, 0] == nxt[1, 0] == int(np.argmax(guided))
+        nxt = m.step()
+    with pytest.raises(ValueError):
+        orc.OracleModel(dict(cfg, batch=1), w)           # guidance needs the two rows
+
+
 def test_errors_leave_state_unchanged(orc):
     cfg = synth.small_config("gpt2", "q4_0")
     m, w = make(orc, cfg)

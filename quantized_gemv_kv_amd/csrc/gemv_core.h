@@ -243,7 +243,7 @@ __device__ __forceinline__ void finish_x(const ProArgs& p, const int K, float4 (
     constexpr bool EMB = PRO == PRO_LN_EMB || PRO == PRO_RMS_EMB;
     constexpr bool LN = PRO == PRO_LN || PRO == PRO_LN_EMB;
     const int lpr = K / E, nch = K / 4, t = threadIdx.x;
-    if (EMB && blockIdx.x == 0 && blockIdx.y == 0) {
+    if (EMB && blockIdx.x == 0) {   // the first workgroup of each batch row (x_out is per row)
 #pragma unroll
         for (int j = 0; j < (MAX_K / 4 / NT); ++j)
             if (t + j * NT < nch) ((float4*)p.x_out)[t + j * NT] = v[j];

@@ -61,11 +61,11 @@ def sampling_of(cfg):
     """The GPU model's sampling dict for a config (None: plain greedy)."""
     mode = cfg.get("sample_mode", 0)
     pen = cfg.get("rep_penalty", 1.0)
-    if mode == 0 and pen in (0.0, 1.0):
+    if mode == 0 and pen in (0.0, 1.0) and not cfg.get("cfg", 0):
         return None
     return dict(mode=mode, top_k=cfg.get("top_k", 0), temperature=cfg.get("temperature", 1.0), seed=cfg.get("seed", 0),
                 top_p=cfg.get("top_p", 0.0), min_p=cfg.get("min_p", 0.0), rep_penalty=pen,
-                order=cfg.get("sample_order", "t3"))
+                order=cfg.get("sample_order", "t3"), cfg=cfg.get("cfg", 0), cfg_weight=cfg.get("cfg_weight", 0.0))
 
 
 def uses_chain(cfg) -> bool:

@@ -32,7 +32,7 @@ def test_workspace_sizes_and_validation():
     # packed weights + fp16 cache + embedding tables fit in a few hundred MB
     assert 300e6 < n < 340e6
     for bad, status in [(dict(c3, d_model=1000), 1), (dict(c3, n_head=15), 1), (dict(c3, head_dim=32, n_head=32, n_kv_head=32), 2),
-                        (dict(c3, batch=2), 2), (dict(c3, wfmt="aff8", d_ff=4000), 1)]:
+                        (dict(c3, batch=3), 2), (dict(c3, wfmt="aff8", d_ff=4000), 1)]:
         with pytest.raises(binding.TsdError) as e:
             binding.tsd_workspace_bytes(bad)
         assert e.value.status == status, bad

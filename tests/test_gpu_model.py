@@ -174,6 +174,58 @@ def test_small_models_chain_teacher_forced(arch, fmt, chain, mode):
     gm.close()
 
 
+BATCH2 = {
+    "greedy": dict(),
+    "chain": dict(sample_mode=1, top_k=50, temperature=0.8, top_p=0.9, rep_penalty=1.3, sample_order="t3"),
+    "cfg-greedy": dict(cfg=1, cfg_weight=1.5),
+    "cfg-chain": dict(cfg=1, cfg_weight=0.5, sample_mode=1, top_k=100, temperature=0.9, min_p=0.05, top_p=0.9,
+                      rep_penalty=1.2, sample_order="mtl"),
+}
+
+
+@pytest.mark.parametrize("variant", list(BATCH2))
+@pytest.mark.parametrize("arch,fmt", [("gpt2", "q4_0"), ("llama", "q8_0")])
+def test_batch2_teacher_forced(arch, fmt, variant):
+    """Two rows in one step (each weight read once for both): two independent streams, or a
+    classifier-free-guided pair (row 0 conditioned, row 1 not) whose one draw both rows take.
+    Both rows' logits are one tensor at rel <= 2e-3; ids as in the other teacher-forced tests."""
+    cfg = synth.small_config(arch, fmt, batch=2, d_ff=256, n_ctx=80, seed=99, **BATCH2[variant])
+    say(f"[model-small] batch 2 {variant} {arch} {fmt}")
+    w = synth.model_weights(cfg, 42, norm_std=0.5)
+    om = oracle.OracleModel(cfg, w)
+    gm = gpu_model(cfg, w, "per_operator")
+    toks = synth.prompt_tokens(cfg, 6, seed=2)                  # a different prompt per row
+    consumed = [[int(t) for t in toks[b, :, 0]] for b in range(2)]
+    o_ids = om.prefill(toks)
+    g_ids = gm.prefill(dev(toks)).cpu().numpy()
+    guided = cfg.get("cfg", 0) == 1
+    checked = 0
+    for s in range(40):
+        pos = om.n_past - 1
+        lo, lg = om.logits(), gm.logits().cpu().numpy()
+        assert rel_err(lg, lo) <= REL_TOL, (s, rel_err(lg, lo))
+        if guided:
+            assert int(g_ids[0, 0]) == int(g_ids[1, 0]) and int(o_ids[0, 0]) == int(o_ids[1, 0])
+            gl = lo[0] + cfg["cfg_weight"] * (lo[0] - lo[1])
+            cases = [(0, gl)]
+        else:
+            cases = [(b, lo[b]) for b in range(2)]
+        for b, l in cases:
+            ref, mg = chain_margins(l, cfg, oracle.uniform24(cfg["seed"], b, pos, 0), consumed[b])
+            assert ref == int(o_ids[b, 0])
+            if not chain_near_boundary(mg):
+                assert int(g_ids[b, 0]) == int(o_ids[b, 0]), (s, b, g_ids, o_ids, mg)
+                checked += 1
+        for b in range(2):
+            consumed[b].append(int(o_ids[b, 0]))
+        g_ids = gm.step(dev(o_ids)).cpu().numpy()
+        o_ids = om.step(o_ids)
+    assert checked >= (20 if guided else 40)
+    assert not gm.uses_persistent_step()
+    gm.synchronize()
+    gm.close()
+
+
 @pytest.mark.parametrize("n_wg", [1, 7, 37])
 def test_persistent_step_any_grid(n_wg):
     """Grids smaller than the tile counts: workgroups take several tiles of a phase, attention

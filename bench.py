@@ -62,11 +62,13 @@ SAMPLERS = {
 
 
 def with_sampler(cfg, samp):
-    """The oracle's config fields for a sampler preset."""
+    """The oracle's config fields for a sampling dict (None: greedy)."""
     if samp is None:
         return cfg
-    return dict(cfg, sample_mode=samp["mode"], top_k=samp["top_k"], temperature=samp["temperature"],
-                seed=samp["seed"], top_p=samp["top_p"], rep_penalty=samp["rep_penalty"], sample_order=samp["order"])
+    return dict(cfg, sample_mode=samp.get("mode", 0), top_k=samp.get("top_k", 0), temperature=samp.get("temperature", 1.0),
+                seed=samp.get("seed", 0), top_p=samp.get("top_p", 0.0), min_p=samp.get("min_p", 0.0),
+                rep_penalty=samp.get("rep_penalty", 1.0), sample_order=samp.get("order", "t3"), cfg=samp.get("cfg", 0),
+                cfg_weight=samp.get("cfg_weight", 0.0))
 
 
 def parse():
@@ -77,6 +79,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=42)
+    ap.add_argument("--cfg", type=float, default=None, metavar="W",
+                    help="classifier-free guidance with weight W: two rows (conditioned, unconditioned prompts) "
+                         "per step, one token drawn from cond + W (cond - uncond)")
     ap.add_argument("--sampler", default="greedy", choices=sorted(SAMPLERS),
                     help="greedy, or a sampler-chain preset (t3: the T3 port's defaults; qwen: the Qwen3-TTS settings)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
@@ -299,6 +304,11 @@ def main():
         args.steps = default_steps
     cfg = dict(synth.config(WORKLOAD), launch_mode=args.launch_mode)
     frames = cfg["arch"] == "talker_cp"
+    if args.cfg is not None:
+        if frames:
+            print("--cfg applies to the GPT2/LLAMA workloads", file=sys.stderr)
+            sys.exit(2)
+        cfg["batch"] = 2
     K, W = args.steps, args.warmup
     if PROMPT + max(K, W) > cfg["n_ctx"]:
         print(f"steps/warmup exceed the {cfg['n_ctx']}-position context", file=sys.stderr)
@@ -308,6 +318,8 @@ def main():
     samp = SAMPLERS[args.sampler]
     if samp is not None:
         samp = dict(samp, seed=args.seed)
+    if args.cfg is not None:
+        samp = dict(samp or {"mode": 0, "seed": args.seed}, cfg=1, cfg_weight=args.cfg)
     model = Model(cfg, weights, stream=stream, sampling=samp)
     prompt = torch.from_numpy(synth.prompt_tokens(cfg, PROMPT, seed=args.seed)).to("cuda")
     step = model.step_eager if args.eager else model.step
@@ -374,10 +386,13 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic (seeded random weights, prompt ids and values; no checkpoint)",
-        "config": {"workload": desc.format(K=K, S="greedy" if samp is None else "sampled"), "d_model": cfg["d_model"], "n_layer": cfg["n_layer"],
+        "config": {"workload": desc.format(K=K, S="greedy" if samp is None or samp.get("mode", 0) == 0 else "sampled")
+                   + ("" if args.cfg is None else f"; classifier-free guidance: a conditioned and an unconditioned row "
+                                                  f"per step (batch 2), one token from cond + {args.cfg} (cond - uncond)"), "d_model": cfg["d_model"], "n_layer": cfg["n_layer"],
                    "n_head": cfg["n_head"], "d_ff": cfg["d_ff"], "vocab": cfg["vocab"],
                    "prompt": PROMPT, "global_batch": cfg["batch"], "launch_mode": mode, "workgroups": n_wg,
-                   "sampler": args.sampler if samp is None else dict(samp, preset=args.sampler)},
+                   "sampler": args.sampler if samp is None else dict(samp, preset=args.sampler),
+                   "cfg": args.cfg},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": roofline.HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / roofline.HBM_PEAK_GBS, "traffic": counted_traffic(dom, WORKLOAD),
                      "kernel": dom, "launch_us": dom_us, "launches_per_step": dom_n,

@@ -316,6 +316,15 @@ def test_free_running_greedy_matches_history(mode):
     assert ids[:len(o_ids)] == o_ids
 
 
+def test_guidance_needs_a_two_row_model():
+    from quantized_gemv_kv_amd import Model, TsdError
+    cfg = synth.small_config("llama", "q8_0")
+    w = synth.model_weights(cfg, 1)
+    with pytest.raises(TsdError) as e:
+        Model(cfg, w, sampling=dict(mode=0, cfg=1, cfg_weight=1.0))
+    assert e.value.status == 1
+
+
 def test_errors_leave_state_unchanged():
     torch = torch_mod()
     from quantized_gemv_kv_amd import TsdError, binding

@@ -164,7 +164,8 @@ def test_chain_rejects_bad_arguments():
     from quantized_gemv_kv_amd import TsdError
     v = np.zeros(64, np.float32)
     for bad in (dict(mode=1, top_p=1.5), dict(mode=1, min_p=0.1, order="t3"), dict(mode=1, min_p=1.0, order="mtl"),
-                dict(mode=1, rep_penalty=-1.0), dict(mode=1, order=7), dict(mode=2), dict(mode=1, temperature=0.0)):
+                dict(mode=1, rep_penalty=-1.0), dict(mode=1, order=7), dict(mode=2), dict(mode=1, temperature=0.0),
+                dict(mode=1, cfg=1, cfg_weight=0.5), dict(mode=1, cfg=2)):
         with pytest.raises(TsdError) as e:
             gpu_chain(v, dict(dict(temperature=1.0), **bad), [], 0, 0, 0)
         assert e.value.status == 1, bad

@@ -131,6 +131,52 @@ def counted_traffic(kernel, workload="gpt2_medium_q4_0"):
     return d["traffic_bytes_per_launch"] if d.get("sources_sha256_16") == step_sources_hash() else None
 
 
+class DeviceState:
+    """amd-smi samples (socket power, graphics and memory clocks, temperatures) taken by a
+    background thread while the benchmark runs; summary() reports those that fall inside the
+    timed region (and the run's maximum power), or null fields where amd-smi is unavailable."""
+
+    def __init__(self):
+        import threading
+        self.samples, self.stop = [], threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+        self.thread.start()
+
+    @staticmethod
+    def _one():
+        import subprocess
+        out = subprocess.run(["/opt/rocm/bin/amd-smi", "metric", "-g", "0", "-p", "-t", "-c", "--json"],
+                             capture_output=True, text=True, timeout=20).stdout
+        d = json.loads(out)
+        g = d["gpu_data"][0] if isinstance(d, dict) and "gpu_data" in d else d[0]
+        num = lambda v: v["value"] if isinstance(v, dict) and isinstance(v.get("value"), (int, float)) else None
+        gfx = [num(c["clk"]) for k, c in g["clock"].items() if k.startswith("gfx_")]
+        gfx = [v for v in gfx if v is not None]
+        return {"power_w": num(g["power"]["socket_power"]), "gfx_mhz_max": max(gfx) if gfx else None,
+                "gfx_mhz_mean": sum(gfx) / len(gfx) if gfx else None, "mem_mhz": num(g["clock"]["mem_0"]["clk"]),
+                "hotspot_c": num(g["temperature"]["hotspot"]), "mem_c": num(g["temperature"]["mem"])}
+
+    def _run(self):
+        while not self.stop.is_set():
+            t0 = time.perf_counter()
+            try:
+                v = self._one()
+            except Exception:
+                return
+            self.samples.append((t0, time.perf_counter(), v))
+
+    LAG = 0.5   # seconds by which amd-smi's metrics trail the device (measured on this board)
+
+    def summary(self, t_begin, t_end):
+        self.stop.set()
+        inside = [v for a, b, v in self.samples if t_begin + self.LAG <= b <= t_end + self.LAG + 0.1]
+        powers = [v["power_w"] for _, _, v in self.samples if v["power_w"] is not None]
+        return {"samples_in_timed_region": inside, "samples_total": len(self.samples),
+                "max_power_w": max(powers) if powers else None,
+                "tool": "amd-smi metric -p -t -c, sampled in a background thread; a reading trails the device by "
+                        "about 0.5 s, so the timed region's samples are those read 0.5 s after it"}
+
+
 def warm(call, seconds=0.25):
     """Back-to-back launches for about `seconds` before a timed measurement: on a GPU that has
     been idle the board's power management first runs a launch at full speed, then slows the
@@ -322,6 +368,7 @@ def main():
         samp = dict(samp or {"mode": 0, "seed": args.seed}, cfg=1, cfg_weight=args.cfg)
     model = Model(cfg, weights, stream=stream, sampling=samp)
     prompt = torch.from_numpy(synth.prompt_tokens(cfg, PROMPT, seed=args.seed)).to("cuda")
+    dev_state = DeviceState()
     step = model.step_eager if args.eager else model.step
     with torch.cuda.stream(stream):
         if args.eager:
@@ -343,7 +390,8 @@ def main():
         e1.record(stream)
         stream.synchronize()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+        t1 = time.perf_counter()
+        wall = t1 - t0
     ms = e0.elapsed_time(e1)
     ids = model.tokens(PROMPT, K).cpu().numpy()
     if frames:
@@ -418,6 +466,7 @@ def main():
             result["gemm_rows"] = gemm_rows_headline(args.seed)
         else:
             result["gemv"] = gemv_headline(args.seed, fmt=args.gemv_format)
+    result["device_state"] = dev_state.summary(t0, t1)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = (cpu_baseline_frames if frames else cpu_baseline)(with_sampler(cfg, samp), weights,
                                                                                     args.cpu_seconds, args.seed)

@@ -168,13 +168,22 @@ tsd_status tsd_model_create(const tsd_config* cfg, const tsd_tensor* weights, in
                             void* d_workspace, size_t workspace_bytes, void* stream,
                             const tsd_sampling* sampling, tsd_model** out);
 
-/* Prefill: the decode step run at every prompt position, so that prefill and decode agree
- * exactly ([J] §3.2 prompt/step split over one persistent KV cache).  d_tokens is
- * [batch][n][tokens per position] (1, or n_codebooks for TALKER_CP); d_next (may be NULL)
- * receives [batch][tokens per step], the ids sampled after the last prompt position.
- * TSD_ERR_CONTEXT_FULL if n_past + n > n_ctx.  Tokens are not range-checked on the device:
- * an id outside its vocabulary is clamped into range. */
+/* Prefill ([J] §3.2: a prompt graph and a decode graph over one persistent KV cache; §3.11: the
+ * prompt graph masks every key after its query's position).  GPT2/LLAMA: positions
+ * n_past .. n_past + n - 2 run as one causal prompt pass (matrix-core products over all their
+ * rows, chunks of up to 512 rows of batch x positions), the last position as one decode step
+ * (head, sampler, history).  TALKER_CP: the decode step at every position (tsd_prefill_stepwise).
+ * d_tokens is [batch][n][tokens per position] (1, or n_codebooks for TALKER_CP); d_next (may be
+ * NULL) receives [batch][tokens per step], the ids sampled after the last prompt position.  The
+ * token history (tsd_get_tokens) at a prompt position before the last holds the next prompt id.
+ * The cached keys and values agree with tsd_prefill_stepwise's to fp32 rounding (the sums run
+ * in another order), not bit for bit.  TSD_ERR_CONTEXT_FULL if n_past + n > n_ctx.  Tokens are
+ * not range-checked on the device: an id outside its vocabulary is clamped into range. */
 tsd_status tsd_prefill(tsd_model* m, const int32_t* d_tokens, int n, int32_t* d_next);
+/* Prefill by the decode step at every prompt position (identical kernels, so the cache matches
+ * what decoding the prompt one id at a time writes, bit for bit); arguments as tsd_prefill.
+ * The history at a prompt position holds the id the step sampled there. */
+tsd_status tsd_prefill_stepwise(tsd_model* m, const int32_t* d_tokens, int n, int32_t* d_next);
 
 /* One decode step (one frame for TALKER_CP) at position n_past: replays the captured graph.
  * d_in is [batch][tokens per position] or NULL for "the ids sampled by the previous step";
@@ -214,6 +223,10 @@ tsd_status tsd_get_tokens(tsd_model* m, int first, int n, int32_t* d_out);
 /* Replace the (Talker) KV cache by d_k/d_v given as [n_layer][batch][n_kv_head][n_pos]
  * [head_dim] fp16 and set n_past = n_pos (used to start from a given context). */
 tsd_status tsd_load_kv(tsd_model* m, const uint16_t* d_k, const uint16_t* d_v, int n_pos);
+
+/* Copy the (Talker) KV cache of positions 0..n_pos-1 (n_pos <= n_past) out to d_k/d_v, laid out
+ * as tsd_load_kv takes it: [n_layer][batch][n_kv_head][n_pos][head_dim] fp16 (device). */
+tsd_status tsd_get_kv(tsd_model* m, uint16_t* d_k, uint16_t* d_v, int n_pos);
 
 /* One main decoder layer on hidden states d_x [batch][d_model] at position pos: writes that
  * layer's K/V at pos, attends to positions 0..pos, writes the residual stream after the
@@ -263,6 +276,19 @@ tsd_status tsd_gemv_pack(int wfmt, const void* d_w, size_t w_bytes, int N, int K
  * non-temporal loads (it is streamed once per call). */
 tsd_status tsd_gemv(int wfmt, const void* d_packed, int N, int K, int B, const float* d_x,
                     const float* d_bias, float* d_y, void* stream);
+
+/* Prompt-pass product on the matrix cores from the GEMV layout (tsd_gemv_pack's output, 256-byte
+ * aligned): d_y[m][n] = sum_k W[n][k] d_x[m][k] (+ d_bias[n] if not NULL) for m < M, d_x [M][K]
+ * and d_y [M][N] fp32 row-major (device, caller-owned; d_y is overwritten).  Each block of 32
+ * weights enters as exact fp16 integers (its codes minus their zero point) and each x as two
+ * fp16 numbers (hi, x - hi); products accumulate in fp32 per block and the block's scale (and
+ * affine bias times the block's sum of x) is applied in fp32 ([J] §3.2 prompt graph: the same
+ * weights as the step's mat-vecs, all prompt rows at once).  Any format; K a multiple of the
+ * format's group (and of 32).  d_scratch (256-byte aligned, tsd_gemm_scratch_bytes) holds the
+ * operand rows. */
+tsd_status tsd_gemm_scratch_bytes(int M, int K, size_t* out_bytes);
+tsd_status tsd_gemm(int wfmt, const void* d_packed, int N, int K, int M, const float* d_x, const float* d_bias,
+                    float* d_y, void* d_scratch, size_t scratch_bytes, void* stream);
 
 /* Batched GEMM on the matrix cores for the 8-bit affine format ([F] §8: batched rollouts turn
  * the memory-bound mat-vec into a skinny product; §3: affine groups of 64):

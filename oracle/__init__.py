@@ -88,6 +88,7 @@ def lib():
             "orc_prefill": (i, [_P, _P, i, _P]),
             "orc_get_logits": (i, [_P, _P, sz]),
             "orc_load_kv": (i, [_P, _P, _P, i]),
+            "orc_get_kv": (i, [_P, _P, _P, i]),
             "orc_layer_forward": (i, [_P, i, _P, i, _P]),
             "orc_forward_sequence": (i, [_P, _P, i, _P, _P]),
         }
@@ -307,6 +308,15 @@ class OracleModel:
     def load_kv(self, k, v, n_pos):
         k, v = _c(k, np.uint16), _c(v, np.uint16)
         self._check(lib().orc_load_kv(self._h, _ptr(k), _ptr(v), n_pos))
+
+    def get_kv(self, n_pos=None):
+        """The cache of positions 0..n_pos-1 as fp16 bit patterns [L][B][Hkv][n_pos][hd]."""
+        c = self.cfg
+        n = self.n_past if n_pos is None else n_pos
+        shape = (c["n_layer"], c["batch"], c["n_kv_head"], n, c["head_dim"])
+        k, v = np.empty(shape, np.uint16), np.empty(shape, np.uint16)
+        self._check(lib().orc_get_kv(self._h, _ptr(k), _ptr(v), n))
+        return k, v
 
     def layer_forward(self, layer, x, pos):
         x = _c(x, np.float64).reshape(self.cfg["batch"], self.cfg["d_model"])

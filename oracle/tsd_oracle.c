@@ -973,6 +973,23 @@ int orc_load_kv(orc_model* m, const uint16_t* k, const uint16_t* v, int n_pos)
     return 0;
 }
 
+/* Copy the main cache of positions 0..n_pos-1 out as [L][B][Hkv][n_pos][hd] fp16 (read-out only). */
+int orc_get_kv(const orc_model* m, uint16_t* k, uint16_t* v, int n_pos)
+{
+    const orc_config* c = &m->c;
+    if (n_pos < 0 || n_pos > m->n_past) { set_err("n_pos out of range"); return -1; }
+    size_t hd = c->head_dim;
+    for (int l = 0; l < c->n_layer; ++l)
+        for (int b = 0; b < c->batch; ++b)
+            for (int g = 0; g < c->n_kv_head; ++g)
+                for (int p = 0; p < n_pos; ++p) {
+                    size_t dst = ((((size_t)l * c->batch + b) * c->n_kv_head + g) * n_pos + p) * hd;
+                    memcpy(k + dst, cache_at(m->kc, c, c->n_ctx, l, b, g, p), hd * 2);
+                    memcpy(v + dst, cache_at(m->vc, c, c->n_ctx, l, b, g, p), hd * 2);
+                }
+    return 0;
+}
+
 /* One main layer on x[B][d] at position pos (writes that layer's K/V at pos, attends 0..pos),
  * out[B][d] = the residual stream after the layer.  n_past is not changed. */
 int orc_layer_forward(orc_model* m, int layer, const double* x, int pos, double* out)

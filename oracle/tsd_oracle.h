@@ -100,6 +100,7 @@ int  orc_prefill(orc_model* m, const int32_t* toks, int n, int32_t* tok_out);
 /* logits of the last step: [batch][vocab] (head 0) — for TALKER_CP [batch][n_codebooks][vocab_j] */
 int  orc_get_logits(const orc_model* m, double* out, size_t n_out);
 int  orc_load_kv(orc_model* m, const uint16_t* k, const uint16_t* v, int n_pos);
+int  orc_get_kv(const orc_model* m, uint16_t* k, uint16_t* v, int n_pos);
 int  orc_layer_forward(orc_model* m, int layer, const double* x, int pos, double* out);
 /* full-sequence causal forward from scratch, no cache reuse: logits [n][vocab] and optionally
  * the final-normed hidden states [n][d] (GPT2/LLAMA) */

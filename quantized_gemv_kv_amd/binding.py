@@ -26,7 +26,8 @@ EXPORTS = ["tsd_workspace_bytes", "tsd_model_create", "tsd_prefill", "tsd_step",
            "tsd_layer_forward", "tsd_gemv_packed_bytes", "tsd_gemv_pack", "tsd_gemv",
            "tsd_attention_scratch_bytes", "tsd_attention", "tsd_time_kernel", "tsd_synchronize",
            "tsd_model_info", "tsd_sample_topk", "tsd_sample", "tsd_gemm_rows_packed_bytes", "tsd_gemm_rows_pack",
-           "tsd_gemm_rows_scratch_bytes", "tsd_gemm_rows"]
+           "tsd_gemm_rows_scratch_bytes", "tsd_gemm_rows", "tsd_prefill_stepwise", "tsd_gemm_scratch_bytes", "tsd_gemm",
+           "tsd_get_kv"]
 KERNEL_KINDS = {"qkv": 0, "attn": 1, "oproj": 2, "fc": 3, "down": 4, "head": 5, "step": 6}
 
 
@@ -82,6 +83,7 @@ def lib():
             "tsd_model_create": [ctypes.POINTER(tsd_config), ctypes.POINTER(tsd_tensor), _I, _P, _SZ, _P,
                                  ctypes.POINTER(tsd_sampling), ctypes.POINTER(_P)],
             "tsd_prefill": [_P, _P, _I, _P],
+            "tsd_prefill_stepwise": [_P, _P, _I, _P],
             "tsd_step": [_P, _P, _P],
             "tsd_step_eager": [_P, _P, _P],
             "tsd_reset": [_P],
@@ -91,6 +93,7 @@ def lib():
             "tsd_get_logits": [_P, _P],
             "tsd_get_tokens": [_P, _I, _I, _P],
             "tsd_load_kv": [_P, _P, _P, _I],
+            "tsd_get_kv": [_P, _P, _P, _I],
             "tsd_layer_forward": [_P, _I, _P, _I, _P],
             "tsd_gemv_packed_bytes": [_I, _I, _I, ctypes.POINTER(_SZ)],
             "tsd_gemv_pack": [_I, _P, _SZ, _I, _I, _P, _SZ, _P],
@@ -106,6 +109,8 @@ def lib():
             "tsd_gemm_rows_pack": [_P, _SZ, _I, _I, _P, _SZ, _P],
             "tsd_gemm_rows_scratch_bytes": [_I, _I, _I, ctypes.POINTER(_SZ)],
             "tsd_gemm_rows": [_P, _I, _I, _I, _P, _P, _I, _P, _SZ, _P],
+            "tsd_gemm_scratch_bytes": [_I, _I, ctypes.POINTER(_SZ)],
+            "tsd_gemm": [_I, _P, _I, _I, _I, _P, _P, _P, _P, _SZ, _P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -202,6 +207,17 @@ def tsd_gemm_rows(packed, N, K, B, x, y, splits, scratch, stream=None):
                                _stream(stream)))
 
 
+def tsd_gemm_scratch_bytes(M, K) -> int:
+    out = _SZ()
+    _check(lib().tsd_gemm_scratch_bytes(M, K, ctypes.byref(out)))
+    return out.value
+
+
+def tsd_gemm(fmt, packed, N, K, M, x, bias, y, scratch, stream=None):
+    _check(lib().tsd_gemm(FORMATS.get(fmt, fmt), _ptr(packed), N, K, M, _ptr(x), _ptr(bias), _ptr(y), _ptr(scratch),
+                          scratch.numel(), _stream(stream)))
+
+
 def tsd_attention_scratch_bytes(B, H, n_ctx, hd) -> int:
     out = _SZ()
     _check(lib().tsd_attention_scratch_bytes(B, H, n_ctx, hd, ctypes.byref(out)))
@@ -268,6 +284,12 @@ class Model:
         self._chk(lib().tsd_prefill(self.h, _ptr(t), t.shape[1], _ptr(self._next)))
         return self._next
 
+    def prefill_stepwise(self, tokens):
+        """As prefill, by the decode step at every prompt position."""
+        t = tokens.reshape(self.cfg["batch"], -1, self.tpp).contiguous()
+        self._chk(lib().tsd_prefill_stepwise(self.h, _ptr(t), t.shape[1], _ptr(self._next)))
+        return self._next
+
     def step(self, tokens=None, out=True):
         t = None if tokens is None else tokens.reshape(self.cfg["batch"], self.tpp).contiguous()
         self._chk(lib().tsd_step(self.h, _ptr(t), _ptr(self._next) if out else None))
@@ -319,6 +341,18 @@ class Model:
 
     def load_kv(self, k, v, n_pos):
         self._chk(lib().tsd_load_kv(self.h, _ptr(k), _ptr(v), n_pos))
+
+    def get_kv(self, n_pos=None):
+        """The cache of positions 0..n_pos-1 as two device fp16 tensors [L][B][Hkv][n_pos][hd]."""
+        torch = self.torch
+        c = self.cfg
+        n = self.n_past if n_pos is None else n_pos
+        shape = (c["n_layer"], c["batch"], c["n_kv_head"], n, c["head_dim"])
+        k = torch.empty(shape, dtype=torch.float16, device="cuda")
+        v = torch.empty(shape, dtype=torch.float16, device="cuda")
+        self._chk(lib().tsd_get_kv(self.h, _ptr(k), _ptr(v), n))
+        self.stream.synchronize()
+        return k, v
 
     def layer_forward(self, layer, x, pos):
         out = self.torch.empty_like(x)

@@ -148,6 +148,11 @@ struct tsd_model {
     tsd::SampChain chain{}, cp_chain{};
     int draw = 0, cp_draw = 0;
     int* seq = nullptr;               // [n_ctx][batch] the token (code 0) consumed at each position
+    // prompt pass (GPT2/LLAMA): row buffers for up to pf_rows rows (batch rows x positions)
+    int pf_rows = 0;
+    float *pf_x = nullptr, *pf_q = nullptr;          // residual stream [rows][d], queries [rows][H hd]
+    __half *pf_ahi = nullptr, *pf_alo = nullptr;     // operand [rows][max(d, H hd)]
+    __half *pf_hhi = nullptr, *pf_hlo = nullptr;     // operand [rows][d_ff]
     std::string err;
 };
 

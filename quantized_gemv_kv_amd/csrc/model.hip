@@ -10,6 +10,7 @@
 // a Memory Read", §5.2: the random state and the sampled ids stay inside the compiled graph).
 #include <math.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -17,6 +18,7 @@
 #include <vector>
 
 #include "model.h"
+#include "prefill.h"
 
 using namespace tsd;
 
@@ -180,7 +182,18 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     size_t xtot = 0;
     for (size_t n : xw) xtot += (n + 31) & ~(size_t)31;
     uint64_t* xbuf = (uint64_t*)P.take(sizeof(uint64_t) * xtot);
+    // prompt pass rows
+    const int pf_rows = (int)std::min<long long>(PF_MAX_ROWS, ((long long)B * c->n_ctx + PF_TILE - 1) / PF_TILE * PF_TILE);
+    const int qd = H * hd, amax = std::max(d, qd);
+    float* pf_x = (float*)P.take(sizeof(float) * (size_t)pf_rows * d);
+    float* pf_q = (float*)P.take(sizeof(float) * (size_t)pf_rows * qd);
+    __half* pf_ahi = (__half*)P.take(2 * (size_t)pf_rows * amax);
+    __half* pf_alo = (__half*)P.take(2 * (size_t)pf_rows * amax);
+    __half* pf_hhi = (__half*)P.take(2 * (size_t)pf_rows * ff);
+    __half* pf_hlo = (__half*)P.take(2 * (size_t)pf_rows * ff);
     if (m && base) {
+        m->pf_rows = pf_rows;
+        m->pf_x = pf_x; m->pf_q = pf_q; m->pf_ahi = pf_ahi; m->pf_alo = pf_alo; m->pf_hhi = pf_hhi; m->pf_hlo = pf_hlo;
         m->pos = pos; m->dbg_pos = pos + 1; m->tok = tok; m->best = best;
         m->hist = hist; m->seq = seq; m->x = x; m->qkv = qkv; m->attn = attn; m->h = h; m->logits = logits; m->part = part;
         m->rope = rope; m->rope_rows = c->n_ctx; m->emb[0] = emb0; m->emb_rows[0] = c->vocab; m->wpe = wpe; m->L = Ls; m->nfg = nfg; m->nfb = nfb;
@@ -546,6 +559,64 @@ void count_launches(tsd_model* m)
     m->kind_launches[KIND_HEAD] = 1;
 }
 
+// ---- the prompt pass (GPT2/LLAMA) -----------------------------------------------------------
+// Prompt positions t0 .. t0 + np - 1 of every batch row (ids d_tokens[b][n_prompt]) at cache
+// positions m->n_past .. m->n_past + np - 1: the embedding rows, then per layer norm, QKV product
+// (queries, RoPE, K/V into the cache), causal attention, output projection into the residual
+// stream, norm, FC / gate-up product and down projection.  No head: the last prompt position
+// goes through the decode step.
+hipError_t pf_enqueue(tsd_model* m, const int32_t* d_tokens, int n_prompt, int t0, int np, hipStream_t st)
+{
+    const tsd_config& c = m->c;
+    const int d = c.d_model, H = c.n_head, Hk = c.n_kv_head, hd = c.head_dim, ff = c.d_ff, B = c.batch, f = c.wfmt;
+    const bool gpt2 = c.arch == TSD_ARCH_GPT2;
+    const int M = B * np, qd = H * hd, amax = std::max(d, qd);
+    const int pos0 = m->n_past;
+    PfRowArgs ra{};
+    ra.M = M; ra.d = d; ra.n_pos = np; ra.pos0 = pos0;
+    ra.tok = d_tokens; ra.tok_stride = n_prompt; ra.t0 = t0; ra.vocab = c.vocab; ra.n_prompt = n_prompt;
+    ra.emb = m->emb[0]; ra.wpe = m->wpe; ra.seq = m->seq; ra.hist = m->hist; ra.B = B;
+    ra.x = m->pf_x; ra.x_out = m->pf_x; ra.eps = c.norm_eps;
+    ra.ahi = m->pf_ahi; ra.alo = m->pf_alo; ra.lda = amax;
+    PfGemmArgs ga{};
+    ga.M = M;
+    ga.n_ctx = c.n_ctx; ga.n_pos = np; ga.pos0 = pos0;
+    ga.kv_row = (long long)Hk * c.n_ctx * hd;
+    PfAttnArgs aa{};
+    aa.q = m->pf_q; aa.ldq = qd; aa.kv_row = ga.kv_row;
+    aa.M = M; aa.H = H; aa.Hkv = Hk; aa.hd = hd; aa.n_ctx = c.n_ctx; aa.n_pos = np; aa.pos0 = pos0;
+    aa.ohi = m->pf_ahi; aa.olo = m->pf_alo; aa.ldo = amax;
+    hipError_t e = hipSuccess;
+    for (int l = 0; l < c.n_layer && e == hipSuccess; ++l) {
+        const LayerW& w = m->L[l];
+        __half* kc = m->kc + m->kv_layer_elems * l;
+        __half* vc = m->vc + m->kv_layer_elems * l;
+        ra.g = w.n1g; ra.bn = w.n1b;
+        e = l == 0 ? launch_pf_embed(ra, st) : launch_pf_norm(ra, st);
+        // Q/K/V: queries (after RoPE) to pf_q, keys and values into the cache
+        PfGemmArgs q = ga;
+        q.W = w.qkv; q.ahi = m->pf_ahi; q.alo = m->pf_alo; q.lda = amax; q.bias = w.bqkv;
+        q.q = m->pf_q; q.ldq = qd; q.qrows = qd; q.krows = Hk * hd; q.hd = hd; q.rope = gpt2 ? 0 : 1;
+        q.rope_tab = m->rope; q.kc = kc; q.vc = vc;
+        if (e == hipSuccess) e = launch_pf_gemm(f, PF_QKV, q, st);
+        aa.kc = kc; aa.vc = vc;
+        if (e == hipSuccess) e = launch_pf_attention(aa, st);
+        PfGemmArgs o = ga;
+        o.W = w.o; o.ahi = m->pf_ahi; o.alo = m->pf_alo; o.lda = amax; o.bias = w.bo; o.y = m->pf_x; o.ldy = d;
+        if (e == hipSuccess) e = launch_pf_gemm(f, PF_RESID, o, st);
+        ra.g = w.n2g; ra.bn = w.n2b;
+        if (e == hipSuccess) e = launch_pf_norm(ra, st);
+        PfGemmArgs u = ga;
+        u.W = w.fc; u.ahi = m->pf_ahi; u.alo = m->pf_alo; u.lda = amax; u.bias = w.bfc;
+        u.ohi = m->pf_hhi; u.olo = m->pf_hlo; u.ldo = ff;
+        if (e == hipSuccess) e = launch_pf_gemm(f, gpt2 ? PF_GELU : PF_SWIGLU, u, st);
+        PfGemmArgs dn = ga;
+        dn.W = w.down; dn.ahi = m->pf_hhi; dn.alo = m->pf_hlo; dn.lda = ff; dn.bias = w.bdown; dn.y = m->pf_x; dn.ldy = d;
+        if (e == hipSuccess) e = launch_pf_gemm(f, PF_RESID, dn, st);
+    }
+    return e;
+}
+
 // the step graph; talker_only: the TALKER_CP frame without head and predictor (prefill positions)
 tsd_status capture(tsd_model* m, bool talker_only, hipGraph_t* out_g, hipGraphExec_t* out_x)
 {
@@ -738,6 +809,31 @@ tsd_status tsd_prefill(tsd_model* m, const int32_t* d_tokens, int n, int32_t* d_
     if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
     if (!d_tokens || n <= 0) return fail(m, TSD_ERR_INVALID_ARGUMENT, "empty prompt");
     if (m->n_past + n > m->c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "prompt does not fit the context");
+    if (m->c.arch == TSD_ARCH_TALKER_CP) return tsd_prefill_stepwise(m, d_tokens, n, d_next);
+    const int nt = m->c.batch * m->tpp;
+    // every position but the last through the prompt pass, in chunks of pf_rows rows
+    const int chunk = m->pf_rows / m->c.batch;
+    for (int t0 = 0; t0 < n - 1; t0 += chunk) {
+        const int np = std::min(chunk, n - 1 - t0);
+        HIP_TRY(m, pf_enqueue(m, d_tokens, n, t0, np, m->st), "prompt pass");
+        m->n_past += np;
+    }
+    if (n > 1) HIP_TRY(m, launch_fill_i32(m->pos, m->n_past, 1, m->st), "set position");
+    // the last position: one decode step (head, sampler, history)
+    HIP_TRY(m, launch_gather_i32(m->tok, d_tokens + (size_t)(n - 1) * m->tpp, m->c.batch, m->tpp, (long long)n * m->tpp, m->st),
+            "set input");
+    HIP_TRY(m, before_launch(m), "exchange restart");
+    HIP_TRY(m, hipGraphLaunch(m->exec, m->st), "graph launch");
+    m->n_past += 1;
+    if (d_next) HIP_TRY(m, launch_copy_i32(d_next, m->tok, nt, m->st), "copy ids");
+    return TSD_OK;
+}
+
+tsd_status tsd_prefill_stepwise(tsd_model* m, const int32_t* d_tokens, int n, int32_t* d_next)
+{
+    if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
+    if (!d_tokens || n <= 0) return fail(m, TSD_ERR_INVALID_ARGUMENT, "empty prompt");
+    if (m->n_past + n > m->c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "prompt does not fit the context");
     const int nt = m->c.batch * m->tpp;
     for (int t = 0; t < n; ++t) {
         // tokens are [batch][n][tokens per position]: position t of every row
@@ -835,6 +931,20 @@ tsd_status tsd_load_kv(tsd_model* m, const uint16_t* d_k, const uint16_t* d_v, i
     return TSD_OK;
 }
 
+tsd_status tsd_get_kv(tsd_model* m, uint16_t* d_k, uint16_t* d_v, int n_pos)
+{
+    if (!m || !d_k || !d_v) return fail(m, TSD_ERR_INVALID_ARGUMENT, "null argument");
+    const tsd_config& c = m->c;
+    if (n_pos < 0 || n_pos > m->n_past) return fail(m, TSD_ERR_INVALID_ARGUMENT, "n_pos outside 0..n_past");
+    if (n_pos > 0) {
+        const size_t w = (size_t)n_pos * c.head_dim * 2, sp = (size_t)c.n_ctx * c.head_dim * 2;
+        const size_t rows = (size_t)c.n_layer * c.batch * c.n_kv_head;
+        HIP_TRY(m, hipMemcpy2DAsync(d_k, w, m->kc, sp, w, rows, hipMemcpyDeviceToDevice, m->st), "get k");
+        HIP_TRY(m, hipMemcpy2DAsync(d_v, w, m->vc, sp, w, rows, hipMemcpyDeviceToDevice, m->st), "get v");
+    }
+    return TSD_OK;
+}
+
 tsd_status tsd_layer_forward(tsd_model* m, int layer, const float* d_x, int pos, float* d_out)
 {
     if (!m || !d_x || !d_out) return fail(m, TSD_ERR_INVALID_ARGUMENT, "null argument");
@@ -895,6 +1005,42 @@ tsd_status tsd_time_kernel(tsd_model* m, int kind, int n_steps, float* avg_us, i
 }
 
 // ---- standalone operators -------------------------------------------------------------------
+
+tsd_status tsd_gemm_scratch_bytes(int M, int K, size_t* out)
+{
+    if (!out || M <= 0 || K <= 0 || K % 32) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "bad shape");
+    *out = 2 * align256((size_t)M * K * 2);   // the operand rows, fp16 hi then lo
+    return TSD_OK;
+}
+
+tsd_status tsd_gemm(int wfmt, const void* d_packed, int N, int K, int M, const float* d_x, const float* d_bias,
+                    float* d_y, void* d_scratch, size_t scratch_bytes, void* stream)
+{
+    size_t need = 0;
+    if (!known_format(wfmt) || N <= 0 || M <= 0 || K <= 0 || K % group_of(wfmt) || !pf_gemm_ok(wfmt, K))
+        return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "bad format or shape");
+    tsd_status s = tsd_gemm_scratch_bytes(M, K, &need);
+    if (s != TSD_OK) return s;
+    if (!d_packed || !d_x || !d_y || !d_scratch) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null buffer");
+    if ((uintptr_t)d_scratch % 256 || (uintptr_t)d_packed % 256)
+        return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "packed matrix and scratch must be 256-byte aligned");
+    if (scratch_bytes < need) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "scratch too small");
+    hipStream_t st = (hipStream_t)stream;
+    __half* hi = (__half*)d_scratch;
+    __half* lo = (__half*)((uint8_t*)d_scratch + need / 2);
+    hipError_t e = launch_pf_split(d_x, M, K, hi, lo, st);
+    PfGemmArgs a{};
+    a.W = packed_view(wfmt, (void*)d_packed, N, K);
+    a.M = M;
+    a.ahi = hi;
+    a.alo = lo;
+    a.lda = K;
+    a.bias = d_bias;
+    a.y = d_y;
+    a.ldy = N;
+    if (e == hipSuccess) e = launch_pf_gemm(wfmt, PF_STORE, a, st);
+    return e == hipSuccess ? TSD_OK : hip_fail(nullptr, e, "gemm");
+}
 
 tsd_status tsd_gemv_packed_bytes(int wfmt, int N, int K, size_t* out)
 {

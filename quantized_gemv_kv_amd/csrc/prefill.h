@@ -1,0 +1,91 @@
+// prefill.h — the prompt pass of the GPT2/LLAMA decoders (internal; prefill.hip).
+//
+// A prompt of n positions is one causal forward over n rows ([J] §3.2: the prompt graph and the
+// decode graph share one KV cache; §3.11: the prompt graph masks keys after each query's
+// position).  With n rows every weight byte feeds n multiply-adds, so the linears are matrix
+// products on the matrix cores; the activations of all rows sit in row-major buffers:
+//   X  [rows][d]  fp32 residual stream
+//   A  [rows][K]  fp16 hi / lo operand of the next product (hi = fp16(x), lo = fp16(x - hi))
+//   Q  [rows][H hd] fp32 queries after RoPE
+// Row r is batch row b = r / n_pos, position pos0 + r % n_pos.
+#pragma once
+
+#include "kernels.h"
+
+namespace tsd {
+
+constexpr int PF_TILE = 64;            // rows and columns of a product tile (one workgroup)
+constexpr int PF_MAX_ROWS = 512;       // rows one pass of the prompt holds (larger prompts are chunked)
+
+enum PfEpi : int {
+    PF_STORE = 0,    // y[r][n] = acc (+ bias[n])
+    PF_QKV = 1,      // queries to Q, keys/values to the cache at the row's position (RoPE pairs when rope)
+    PF_RESID = 2,    // x[r][n] += acc (+ bias[n])
+    PF_GELU = 3,     // operand (hi/lo) [r][n] = gelu(acc + bias[n])
+    PF_SWIGLU = 4,   // rows 2i/2i+1 = gate/up: operand [r][i] = silu(gate) * up
+};
+
+struct PfGemmArgs {
+    PackedMat W;                 // packed GEMV layout, N rows of K
+    int M;                       // operand rows
+    const __half* ahi;           // [M][lda] operand
+    const __half* alo;
+    int lda;
+    const float* bias;           // [N] or null
+    float* y;                    // PF_STORE / PF_RESID: [M][ldy] fp32
+    int ldy;
+    __half* ohi;                 // PF_GELU / PF_SWIGLU: next operand [M][ldo]
+    __half* olo;
+    int ldo;
+    // PF_QKV
+    float* q;                    // [M][ldq]
+    int ldq;
+    int qrows, krows, hd, rope;  // rope: q and k rows are in RoPE pairs (row 2i: element i, 2i+1: i + hd/2)
+    const float2* rope_tab;      // [n_ctx][hd/2] (cos, sin)
+    __half *kc, *vc;             // layer cache [B][Hkv][n_ctx][hd]
+    long long kv_row;            // elements of one batch row's slab
+    int n_ctx, n_pos, pos0;
+};
+
+struct PfRowArgs {
+    int M, d, n_pos, pos0;
+    // embedding rows: ids tok[b * tok_stride + t0 + t] (clamped into [0, vocab))
+    const int* tok;
+    long long tok_stride;
+    int t0, vocab, n_prompt;     // n_prompt: prompt length (for the history of the next id)
+    const float* emb;            // [vocab][d]
+    const float* wpe;            // [n_ctx][d] learned positions or null
+    int* seq;                    // [n_ctx][B] consumed ids
+    int* hist;                   // [n_ctx][B] next ids
+    int B;
+    // norm
+    const float* x;              // [M][d]
+    float* x_out;
+    const float* g;              // gain
+    const float* bn;             // LayerNorm bias (null: RMSNorm)
+    float eps;
+    __half *ahi, *alo;           // operand [M][lda]
+    int lda;
+};
+
+struct PfAttnArgs {
+    const float* q;              // [M][ldq] after RoPE
+    int ldq;
+    const __half *kc, *vc;       // layer cache [B][Hkv][n_ctx][hd]
+    long long kv_row;
+    int M, H, Hkv, hd, n_ctx, n_pos, pos0;
+    __half *ohi, *olo;           // operand [M][ldo], head h at column h hd
+    int ldo;
+};
+
+// supported when the reduction dimension is a multiple of 32 and the operand rows fit
+bool pf_gemm_ok(int fmt, int K);
+hipError_t launch_pf_gemm(int fmt, int epi, const PfGemmArgs& a, hipStream_t st);
+// X rows from the embeddings (and the history words), then the first norm into the operand
+hipError_t launch_pf_embed(const PfRowArgs& a, hipStream_t st);
+hipError_t launch_pf_norm(const PfRowArgs& a, hipStream_t st);
+// fp32 rows x [M][K] -> operand hi/lo (standalone product)
+hipError_t launch_pf_split(const float* x, int M, int K, __half* hi, __half* lo, hipStream_t st);
+hipError_t launch_pf_attention(const PfAttnArgs& a, hipStream_t st);
+
+}  // namespace tsd

@@ -1,0 +1,481 @@
+// prefill.hip — the prompt pass: every prompt position of a GPT2/LLAMA decoder in one causal
+// forward ([J] §3.2: prompt and decode graphs over one persistent KV cache; §3.11: the prompt
+// graph's causal mask), instead of one decode step per position.
+//
+// The linears are matrix products on the matrix cores (v_mfma_f32_16x16x32_f16) straight from
+// the packed GEMV layout, with the weights kept exact:
+//   * every block of 32 weights enters as fp16 integers (its codes minus their zero point:
+//     q - 8 for Q4_0 and 4-bit affine, q - 16 for Q5_0, the signed byte for Q8_0, q - 128 for
+//     8-bit affine; a byte permute builds 1024 + code and one packed subtract removes the
+//     offset), and one MFMA pair covers the block;
+//   * an activation enters as two fp16 numbers, hi = fp16(x) and lo = fp16(x - hi);
+//   * the block's (or group's) scale is applied in fp32 after its MFMAs:
+//       sum_k w_k x_k = d P                     (Q4_0, Q5_0, Q8_0: w = d (q - zero))
+//       sum_k w_k x_k = s P + (b + zero s) X    (affine: w = s q + b; X = sum_k x_k from the same
+//                                                 operand fragments against a fragment of ones)
+// Operand roles: A = 16 activation rows (lane l holds row l % 16), B = 16 weight rows (lane l
+// holds row l % 16); lane group j = l / 16 supplies K positions 8 j .. 8 j + 7 of the block to
+// both operands, so a lane's four results share one weight row (and so one scale).  A workgroup
+// computes a 64 x 64 tile; each of its four waves a 32 x 32 quarter (2 x 2 MFMA tiles).
+//
+// Epilogues write what the next kernel consumes: queries (after RoPE) and the fp16 K/V cache
+// entries at each row's position, the residual add, or the next product's hi/lo operand through
+// GELU or SwiGLU.  Attention is causal over the cache: row r at position p reads keys 0..p.
+#include <math.h>
+
+#include <type_traits>
+
+#include "gemv_core.h"
+#include "prefill.h"
+
+namespace tsd {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void put_hilo(__half* hi, __half* lo, size_t idx, float y)
+{
+    const _Float16 h = (_Float16)y;
+    ((TSD_GLOBAL _Float16*)hi)[idx] = h;
+    ((TSD_GLOBAL _Float16*)lo)[idx] = (_Float16)(y - (float)h);
+}
+
+// the eight byte codes u of (w0, w1) (each < 2048 - 1024) as fp16 (1024 + u) - off: byte permutes
+// put 0x64 above each code byte, which is the fp16 bit pattern of 1024 + u
+__device__ __forceinline__ half8 codes_h8(uint32_t w0, uint32_t w1, _Float16 off)
+{
+    u32x4 u;
+    u.x = __builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u);
+    u.y = __builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u);
+    u.z = __builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u);
+    u.w = __builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u);
+    return __builtin_bit_cast(half8, u) - off;
+}
+
+// per-format access to one 32-weight block of a packed row, for lane group j
+template <int F> struct PfFmt {
+    static constexpr bool NIB = fmt_nibbles(F);
+    static constexpr bool AFF = fmt_affine(F);
+    static constexpr int GB = (F == FMT_AFF8 || F == FMT_AFF4_G64) ? 2 : 1;   // blocks per scale group
+    // byte offset of lane group j's eight codes inside row n, and the stride between blocks
+    __device__ static size_t row_off(int n, int K, int j)
+    {
+        return NIB ? (size_t)n * (K / 2) + 8 * (j & 1) : (size_t)n * K + 8 * j;
+    }
+    static constexpr int BLOCK_BYTES = NIB ? 16 : 32;
+    // zero point entered with the code (w = scale (q - zero) [+ bias'])
+    static constexpr float ZERO = F == FMT_Q4_0 || F == FMT_AFF4_G64 || F == FMT_AFF4_G32 ? 8.f
+                                  : F == FMT_Q5_0                                         ? 16.f
+                                                                                           : 128.f;
+    // raw 8 bytes -> eight fp16 (q - zero); h: the block's Q5_0 fifth-bit word
+    __device__ static half8 codes(u32x2 r, int j, uint32_t h)
+    {
+        uint32_t a = r.x, b = r.y;
+        if constexpr (NIB) {
+            const int sh = (j & 2) ? 4 : 0;   // lane groups 2, 3: elements 16..31 = high nibbles
+            a = (a >> sh) & 0x0F0F0F0Fu;
+            b = (b >> sh) & 0x0F0F0F0Fu;
+            if constexpr (F == FMT_Q5_0) {
+                const uint32_t hb = (h >> (8 * j)) & 0xFFu;   // fifth bits of elements 8j..8j+7
+                a |= core::spread4(hb);
+                b |= core::spread4(hb >> 4);
+            }
+        }
+        return codes_h8(a, b, (_Float16)(1024.f + ZERO));
+    }
+};
+
+__device__ __forceinline__ float4v mfma(half8 a, half8 b, float4v c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+template <int F, int EPI>
+__global__ __launch_bounds__(256) void k_pf_gemm(const PfGemmArgs a)
+{
+    using T = PfFmt<F>;
+    constexpr int GB = T::GB;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int c = lane & 15, j = lane >> 4;
+    const int m0 = blockIdx.y * PF_TILE + (w & 1) * 32;
+    const int n0 = blockIdx.x * PF_TILE + (w >> 1) * 32;
+    const int N = a.W.N, K = a.W.K, M = a.M;
+    const int ngrp = K / (32 * GB);
+
+    const TSD_GLOBAL half8* ah[2];
+    const TSD_GLOBAL half8* al[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int r = min(m0 + 16 * s + c, M - 1);   // rows past M repeat row M-1 (never stored)
+        ah[s] = (const TSD_GLOBAL half8*)(glb(a.ahi) + (size_t)r * a.lda + 8 * j);
+        al[s] = (const TSD_GLOBAL half8*)(glb(a.alo) + (size_t)r * a.lda + 8 * j);
+    }
+    const TSD_GLOBAL uint8_t* wp[2];
+    const TSD_GLOBAL _Float16* sp[2];
+    const TSD_GLOBAL _Float16* bp[2];
+    const TSD_GLOBAL uint32_t* hp[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int n = min(n0 + 16 * u + c, N - 1);
+        wp[u] = glb(a.W.q) + T::row_off(n, K, j);
+        sp[u] = (const TSD_GLOBAL _Float16*)glb(a.W.s) + (size_t)n * ngrp;
+        bp[u] = T::AFF ? (const TSD_GLOBAL _Float16*)glb(a.W.b) + (size_t)n * ngrp : nullptr;
+        hp[u] = F == FMT_Q5_0 ? glb(a.W.h) + (size_t)n * (K / 32) : nullptr;
+    }
+
+    half8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
+
+    float4v acc[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) acc[s][u] = float4v{0.f, 0.f, 0.f, 0.f};
+
+    // one stage: NG scale groups (NG * GB blocks), all loads issued before the first MFMA
+    auto stage = [&](int g0, auto ng_tag) {
+        constexpr int NG = decltype(ng_tag)::value;
+        constexpr int NB = NG * GB;
+        half8 xh[NB][2], xl[NB][2];
+        u32x2 wr[NB][2];
+        uint32_t hb[NB][2];
+        float sc[NG][2], bi[NG][2];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int blk = g0 * GB + b;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                xh[b][s] = ah[s][blk * 4];   // 32 halves = 4 half8 per block
+                xl[b][s] = al[s][blk * 4];
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                wr[b][u] = *(const TSD_GLOBAL u32x2*)(wp[u] + (size_t)blk * T::BLOCK_BYTES);
+                hb[b][u] = F == FMT_Q5_0 ? hp[u][blk] : 0u;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < NG; ++q)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                sc[q][u] = (float)sp[u][g0 + q];
+                bi[q][u] = T::AFF ? (float)bp[u][g0 + q] : 0.f;
+            }
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+            float4v P[2][2], X[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                X[s] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int u = 0; u < 2; ++u) P[s][u] = float4v{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int bb = 0; bb < GB; ++bb) {
+                const int b = q * GB + bb;
+                half8 wv[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) wv[u] = T::codes(wr[b][u], j, hb[b][u]);
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const half8 hi = xh[b][s];
+                    const half8 lo = xl[b][s];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        P[s][u] = mfma(hi, wv[u], P[s][u]);
+                        P[s][u] = mfma(lo, wv[u], P[s][u]);
+                    }
+                    if constexpr (T::AFF) {
+                        X[s] = mfma(hi, ones, X[s]);
+                        X[s] = mfma(lo, ones, X[s]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const float d = sc[q][u];
+                const float b2 = T::AFF ? fmaf(T::ZERO, d, bi[q][u]) : 0.f;   // b + zero * s
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float v = fmaf(d, P[s][u][i], acc[s][u][i]);
+                        if constexpr (T::AFF) v = fmaf(b2, X[s][i], v);
+                        acc[s][u][i] = v;
+                    }
+            }
+        }
+    };
+    int g = 0;
+    for (; g + 4 <= ngrp; g += 4) stage(g, std::integral_constant<int, 4>{});
+    for (; g < ngrp; ++g) stage(g, std::integral_constant<int, 1>{});
+
+    // epilogue: lane holds weight row n = n0 + 16u + c for activation rows m0 + 16s + 4j + i
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int n = n0 + 16 * u + c;
+        const float bias = (a.bias && n < N) ? a.bias[n] : 0.f;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = m0 + 16 * s + 4 * j + i;
+                const float v = acc[s][u][i] + bias;
+                float partner = 0.f;
+                if constexpr (EPI == PF_SWIGLU || EPI == PF_QKV) partner = dpp_mov<0xB1>(v);   // column n ^ 1
+                if (r >= M || n >= N) continue;
+                if constexpr (EPI == PF_STORE) {
+                    a.y[(size_t)r * a.ldy + n] = v;
+                } else if constexpr (EPI == PF_RESID) {
+                    a.y[(size_t)r * a.ldy + n] += v;
+                } else if constexpr (EPI == PF_GELU) {
+                    put_hilo(a.ohi, a.olo, (size_t)r * a.ldo + n, core::gelu_tanh(v));
+                } else if constexpr (EPI == PF_SWIGLU) {
+                    if ((n & 1) == 0) put_hilo(a.ohi, a.olo, (size_t)r * a.ldo + (n >> 1), core::silu(v) * partner);
+                } else {   // PF_QKV
+                    const int b = r / a.n_pos, p = a.pos0 + (r - b * a.n_pos);
+                    if (n < a.qrows + a.krows) {
+                        const bool isk = n >= a.qrows;
+                        const int nn = isk ? n - a.qrows : n, h = nn / a.hd, rr = nn - h * a.hd;
+                        float out = v;
+                        int e = rr;
+                        if (a.rope) {
+                            const int half = a.hd >> 1, ip = rr >> 1;
+                            const float2 cs = a.rope_tab[(size_t)p * half + ip];
+                            // row 2i holds element i, row 2i+1 element i + hd/2 (its partner lane)
+                            out = (rr & 1) ? fmaf(partner, cs.y, v * cs.x) : fmaf(v, cs.x, -partner * cs.y);
+                            e = (rr & 1) ? ip + half : ip;
+                        }
+                        if (!isk)
+                            a.q[(size_t)r * a.ldq + h * a.hd + e] = out;
+                        else
+                            a.kc[b * a.kv_row + ((size_t)h * a.n_ctx + p) * a.hd + e] = __float2half_rn(out);
+                    } else {
+                        const int nn = n - a.qrows - a.krows, h = nn / a.hd, e = nn - h * a.hd;
+                        a.vc[b * a.kv_row + ((size_t)h * a.n_ctx + p) * a.hd + e] = __float2half_rn(v);
+                    }
+                }
+            }
+    }
+}
+
+// ---- rows: embedding, norms, the standalone split ---------------------------------------------
+constexpr int PF_NT = 256;
+constexpr int PF_MAXV = core::MAX_K / PF_NT;   // row values per thread
+
+__device__ __forceinline__ float row_sum(float v, float* red)
+{
+    v = wave_sum(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+// LayerNorm (bn set) or RMSNorm of the row held in v, written to the operand row r
+__device__ void norm_to_operand(const PfRowArgs& a, int r, const float (&v)[PF_MAXV], float* red)
+{
+    const int t = threadIdx.x, d = a.d;
+    const float invd = 1.0f / (float)d;
+    float mean = 0.f, s2 = 0.f;
+    if (a.bn) {
+        float s1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < PF_MAXV; ++i)
+            if (t + i * PF_NT < d) s1 += v[i];
+        mean = row_sum(s1, red) * invd;
+    }
+#pragma unroll
+    for (int i = 0; i < PF_MAXV; ++i)
+        if (t + i * PF_NT < d) s2 = fmaf(v[i] - mean, v[i] - mean, s2);
+    const float rs = 1.0f / sqrtf(row_sum(s2, red) * invd + a.eps);
+#pragma unroll
+    for (int i = 0; i < PF_MAXV; ++i) {
+        const int k = t + i * PF_NT;
+        if (k < d) {
+            float y = (v[i] - mean) * rs * a.g[k];
+            if (a.bn) y += a.bn[k];
+            put_hilo(a.ahi, a.alo, (size_t)r * a.lda + k, y);
+        }
+    }
+}
+
+__global__ __launch_bounds__(PF_NT) void k_pf_embed(const PfRowArgs a)
+{
+    __shared__ float red[4];
+    const int r = blockIdx.x, t = threadIdx.x, d = a.d;
+    const int b = r / a.n_pos, tt = r - b * a.n_pos, p = a.pos0 + tt;
+    const int* tr = a.tok + b * a.tok_stride + a.t0 + tt;
+    const int id = min(max(tr[0], 0), a.vocab - 1);
+    if (t == 0) {
+        a.seq[(size_t)p * a.B + b] = id;
+        // the history at a prompt position holds the id that follows it (the next prompt id)
+        if (a.t0 + tt + 1 < a.n_prompt) a.hist[(size_t)p * a.B + b] = min(max(tr[1], 0), a.vocab - 1);
+    }
+    float v[PF_MAXV];
+#pragma unroll
+    for (int i = 0; i < PF_MAXV; ++i) {
+        const int k = t + i * PF_NT;
+        v[i] = 0.f;
+        if (k < d) {
+            v[i] = a.emb[(size_t)id * d + k];
+            if (a.wpe) v[i] += a.wpe[(size_t)p * d + k];
+            a.x_out[(size_t)r * d + k] = v[i];
+        }
+    }
+    norm_to_operand(a, r, v, red);
+}
+
+__global__ __launch_bounds__(PF_NT) void k_pf_norm(const PfRowArgs a)
+{
+    __shared__ float red[4];
+    const int r = blockIdx.x, t = threadIdx.x, d = a.d;
+    float v[PF_MAXV];
+#pragma unroll
+    for (int i = 0; i < PF_MAXV; ++i) {
+        const int k = t + i * PF_NT;
+        v[i] = k < d ? a.x[(size_t)r * d + k] : 0.f;
+    }
+    norm_to_operand(a, r, v, red);
+}
+
+__global__ __launch_bounds__(256) void k_pf_split(const float* __restrict__ x, size_t n, __half* hi, __half* lo)
+{
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) put_hilo(hi, lo, i, x[i]);
+}
+
+// ---- causal attention over the cache ---------------------------------------------------------
+// one wave per (row, head): keys in chunks of 64 (one per lane) with a running max and sum;
+// the value rows are read coalesced, one key at a time, each lane owning hd / 64 output dims
+template <int HD>
+__global__ __launch_bounds__(256) void k_pf_attn(const PfAttnArgs a)
+{
+    __shared__ float qs[4][HD];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r = blockIdx.x * 4 + w, h = blockIdx.y;
+    if (r >= a.M) return;   // whole waves only; no workgroup barrier follows
+    const int b = r / a.n_pos, p = a.pos0 + (r - b * a.n_pos), n_keys = p + 1;
+    const int g = h / (a.H / a.Hkv);
+    const TSD_GLOBAL _Float16* Kc = (const TSD_GLOBAL _Float16*)glb(a.kc) + b * a.kv_row + (size_t)g * a.n_ctx * HD;
+    const TSD_GLOBAL _Float16* Vc = (const TSD_GLOBAL _Float16*)glb(a.vc) + b * a.kv_row + (size_t)g * a.n_ctx * HD;
+    // scores in the log2 domain: q . k / sqrt(hd) * log2(e)
+    const float qscale = 1.4426950408889634f / sqrtf((float)HD);
+#pragma unroll
+    for (int i = lane; i < HD; i += 64) qs[w][i] = a.q[(size_t)r * a.ldq + h * HD + i] * qscale;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    constexpr int OD = HD / 64;   // output dims per lane: lane * OD .. lane * OD + OD - 1
+    float o[OD];
+#pragma unroll
+    for (int e = 0; e < OD; ++e) o[e] = 0.f;
+    float mx = -INFINITY, l = 0.f;
+    for (int c0 = 0; c0 < n_keys; c0 += 64) {
+        const int key = c0 + lane;
+        float s = -INFINITY;
+        if (key < n_keys) {
+            const TSD_GLOBAL half8* kr = (const TSD_GLOBAL half8*)(Kc + (size_t)key * HD);
+            float acc = 0.f;
+#pragma unroll
+            for (int v8 = 0; v8 < HD / 8; ++v8) {
+                const half8 kv = kr[v8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = fmaf(qs[w][v8 * 8 + e], (float)kv[e], acc);
+            }
+            s = acc;
+        }
+        const float mn = fmaxf(mx, wave_max(s));   // finite: key c0 is always valid
+        const float alpha = exp2f(mx - mn);         // 0 on the first chunk
+        const float pj = key < n_keys ? exp2f(s - mn) : 0.f;
+        l = fmaf(l, alpha, wave_sum(pj));
+#pragma unroll
+        for (int e = 0; e < OD; ++e) o[e] *= alpha;
+        mx = mn;
+        const int nk = min(64, n_keys - c0);
+        for (int jj = 0; jj < nk; ++jj) {
+            const float pw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), jj));   // key c0 + jj's weight
+            const TSD_GLOBAL _Float16* vr = Vc + (size_t)(c0 + jj) * HD + lane * OD;
+#pragma unroll
+            for (int e = 0; e < OD; ++e) o[e] = fmaf(pw, (float)vr[e], o[e]);
+        }
+    }
+    const float il = 1.0f / l;
+#pragma unroll
+    for (int e = 0; e < OD; ++e) put_hilo(a.ohi, a.olo, (size_t)r * a.ldo + h * HD + lane * OD + e, o[e] * il);
+}
+
+template <int F>
+hipError_t gemm_epi(int epi, const PfGemmArgs& a, dim3 grid, hipStream_t st)
+{
+    switch (epi) {
+    case PF_STORE: k_pf_gemm<F, PF_STORE><<<grid, 256, 0, st>>>(a); break;
+    case PF_QKV: k_pf_gemm<F, PF_QKV><<<grid, 256, 0, st>>>(a); break;
+    case PF_RESID: k_pf_gemm<F, PF_RESID><<<grid, 256, 0, st>>>(a); break;
+    case PF_GELU: k_pf_gemm<F, PF_GELU><<<grid, 256, 0, st>>>(a); break;
+    case PF_SWIGLU: k_pf_gemm<F, PF_SWIGLU><<<grid, 256, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool pf_gemm_ok(int fmt, int K)
+{
+    return fmt >= 0 && fmt < FMT_COUNT && K > 0 && K % fmt_group(fmt) == 0 && K % 32 == 0;
+}
+
+hipError_t launch_pf_gemm(int fmt, int epi, const PfGemmArgs& a, hipStream_t st)
+{
+    if (!pf_gemm_ok(fmt, a.W.K) || a.M <= 0 || a.W.N <= 0 || a.lda % 8) return hipErrorInvalidValue;
+    if ((epi == PF_SWIGLU || epi == PF_QKV) && a.W.N % 2) return hipErrorInvalidValue;
+    const dim3 grid((a.W.N + PF_TILE - 1) / PF_TILE, (a.M + PF_TILE - 1) / PF_TILE);
+    switch (fmt) {
+    case FMT_Q4_0: return gemm_epi<FMT_Q4_0>(epi, a, grid, st);
+    case FMT_Q8_0: return gemm_epi<FMT_Q8_0>(epi, a, grid, st);
+    case FMT_AFF8: return gemm_epi<FMT_AFF8>(epi, a, grid, st);
+    case FMT_Q5_0: return gemm_epi<FMT_Q5_0>(epi, a, grid, st);
+    case FMT_AFF4_G64: return gemm_epi<FMT_AFF4_G64>(epi, a, grid, st);
+    case FMT_AFF4_G32: return gemm_epi<FMT_AFF4_G32>(epi, a, grid, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_pf_embed(const PfRowArgs& a, hipStream_t st)
+{
+    if (a.M <= 0 || a.d > core::MAX_K) return hipErrorInvalidValue;
+    k_pf_embed<<<a.M, PF_NT, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_pf_norm(const PfRowArgs& a, hipStream_t st)
+{
+    if (a.M <= 0 || a.d > core::MAX_K) return hipErrorInvalidValue;
+    k_pf_norm<<<a.M, PF_NT, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_pf_split(const float* x, int M, int K, __half* hi, __half* lo, hipStream_t st)
+{
+    const size_t n = (size_t)M * K;
+    if (!n) return hipSuccess;
+    k_pf_split<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(x, n, hi, lo);
+    return hipGetLastError();
+}
+
+hipError_t launch_pf_attention(const PfAttnArgs& a, hipStream_t st)
+{
+    if (a.M <= 0 || a.Hkv <= 0 || a.H % a.Hkv) return hipErrorInvalidValue;
+    const dim3 grid((a.M + 3) / 4, a.H);
+    if (a.hd == 64) k_pf_attn<64><<<grid, 256, 0, st>>>(a);
+    else if (a.hd == 128) k_pf_attn<128><<<grid, 256, 0, st>>>(a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace tsd

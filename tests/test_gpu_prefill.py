@@ -1,0 +1,271 @@
+"""GPU parity of the prompt pass (tsd_prefill for GPT2/LLAMA: matrix-core products over all
+prompt rows, causal attention over the cache, the last position through the decode step)
+against the CPU oracle, through the C ABI.
+
+* the standalone product tsd_gemm against the oracle's fp64 mat-vec of every row, for every
+  weight format, at shapes spanning several 64 x 64 tiles with ragged row and column tails and
+  reduction lengths that leave a partial stage: rel <= 1e-5 per tensor, and per element within
+  1e-5 of sum_k |w_k x_k| (the scale the rounding works on);
+* the cache a prompt writes (every layer, every position) against the oracle's prefill, which
+  runs the decode step at every position ([J] §3.2: prompt and decode share one cache): rel <=
+  2e-3 per layer for keys and values; then the logits after the prompt and a few teacher-forced
+  steps (rel <= 2e-3, ids as in the other model tests);
+* the causal mask ([J] §3.11): changing the ids after position i leaves every cached key and
+  value at positions <= i bit for bit unchanged;
+* prompts longer than one pass (chunks of 512 rows), prompts after decoded positions, one-id
+  prompts, two batch rows, and the prompt pass against the stepwise prefill at full size.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from parity import REL_TOL, ids_agree, rel_err, top2_gap
+from quantized_gemv_kv_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+GEMM_TOL = 1e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def dev(a):
+    return torch_mod().from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+FORMATS = ["q4_0", "q8_0", "aff8", "q5_0", "aff4_g64", "aff4_g32"]
+# (N, K, M): one tile; ragged rows/columns over several tiles with a partial stage of blocks;
+# tall K; a single row
+SHAPES = [(5, 64, 3), (200, 192, 37), (256, 1024, 130), (96, 4096, 65), (130, 320, 1)]
+
+
+@pytest.mark.parametrize("N,K,M", SHAPES)
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_gemm_matches_oracle(fmt, N, K, M):
+    from quantized_gemv_kv_amd import binding
+    torch = torch_mod()
+    say(f"[gemm] {fmt} N={N} K={K} M={M}")
+    rng = synth.rng_for(11, N, K, M)
+    blob = synth.matrix(fmt, rng, N, K)
+    x = synth.normal_f32(rng, (M, K))
+    bias = synth.normal_f32(rng, (N,), 0.1) if M % 2 else None
+    packed = torch.empty(binding.tsd_gemv_packed_bytes(fmt, N, K), dtype=torch.uint8, device="cuda")
+    binding.tsd_gemv_pack(fmt, dev(blob), N, K, packed)
+    scratch = torch.empty(binding.tsd_gemm_scratch_bytes(M, K), dtype=torch.uint8, device="cuda")
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    binding.tsd_gemm(fmt, packed, N, K, M, dev(x), None if bias is None else dev(bias), y, scratch)
+    got = y.cpu().numpy().astype(np.float64)
+    ref = np.stack([oracle.gemv(fmt, blob, N, K, x[m].astype(np.float64),
+                                None if bias is None else bias.astype(np.float64)) for m in range(M)])
+    W = oracle.dequant(fmt, blob, N, K)
+    scale = np.abs(x.astype(np.float64)) @ np.abs(W).T + (0 if bias is None else np.abs(bias.astype(np.float64)))
+    r = rel_err(got, ref)
+    worst = float(np.max(np.abs(got - ref) / np.maximum(scale, 1e-30)))
+    say(f"  rel {r:.2e}  elementwise {worst:.2e}")
+    assert np.all(np.isfinite(got))
+    assert r <= GEMM_TOL
+    assert worst <= GEMM_TOL
+
+
+def test_gemm_rejects_bad_arguments():
+    from quantized_gemv_kv_amd import TsdError, binding
+    torch = torch_mod()
+    packed = torch.zeros(binding.tsd_gemv_packed_bytes("q4_0", 64, 128), dtype=torch.uint8, device="cuda")
+    scratch = torch.zeros(binding.tsd_gemm_scratch_bytes(4, 128), dtype=torch.uint8, device="cuda")
+    x = torch.zeros((4, 128), dtype=torch.float32, device="cuda")
+    y = torch.zeros((4, 64), dtype=torch.float32, device="cuda")
+    for args in [("q4_0", packed, 64, 100, 4), ("q4_0", packed, 64, 128, 0), ("aff8", packed, 64, 96, 4),
+                 ("q4_0", packed, 64, 128, 5)]:   # K not a block multiple / no rows / K % 64 / scratch too small
+        with pytest.raises(TsdError) as e:
+            binding.tsd_gemm(args[0], args[1], args[2], args[3], args[4], x, None, y, scratch)
+        assert e.value.status == 1
+
+
+def kv_rel(gk, gv, ok, ov, n):
+    """Worst per-layer rel error of the GPU cache (fp16 tensors) against the oracle's (fp16 bits)."""
+    gk = gk.cpu().numpy().astype(np.float64)[:, :, :, :n]
+    gv = gv.cpu().numpy().astype(np.float64)[:, :, :, :n]
+    ok = ok.view(np.float16).astype(np.float64)[:, :, :, :n]
+    ov = ov.view(np.float16).astype(np.float64)[:, :, :, :n]
+    return max(max(rel_err(gk[l], ok[l]), rel_err(gv[l], ov[l])) for l in range(gk.shape[0]))
+
+
+def gpu_model(cfg, w, mode="persistent"):
+    from quantized_gemv_kv_amd import Model
+    return Model(dict(cfg, launch_mode=mode), w)
+
+
+def check_prompt(cfg, w, prompts, n_steps=3, mode="persistent", check_ids=True):
+    """Prefill each prompt in turn (a later prompt continues after the earlier ones and the
+    decoded steps between them), compare the cache and the logits, then n_steps teacher-forced
+    steps after each prompt."""
+    om = oracle.OracleModel(cfg, w)
+    gm = gpu_model(cfg, w, mode)
+    worst = 0.0
+    for i, n in enumerate(prompts):
+        toks = synth.prompt_tokens(cfg, n, seed=30 + i)
+        o_ids = om.prefill(toks)
+        g_ids = gm.prefill(dev(toks)).cpu().numpy()
+        assert gm.n_past == om.n_past
+        gk, gv = gm.get_kv()
+        ok, ov = om.get_kv()
+        r = kv_rel(gk, gv, ok, ov, om.n_past)
+        lo, lg = om.logits(), gm.logits().cpu().numpy()
+        rl = rel_err(lg, lo)
+        say(f"  prompt {n} at {om.n_past - n}: cache rel {r:.2e}, logits rel {rl:.2e}")
+        assert r <= REL_TOL and rl <= REL_TOL
+        worst = max(worst, r, rl)
+        for b in range(cfg["batch"]):
+            if check_ids:
+                assert ids_agree(g_ids[b, 0], lo[b]), (b, g_ids, o_ids, top2_gap(lo[b]))
+        nxt = o_ids
+        for s in range(n_steps):
+            o_ids = om.step(nxt)
+            g_ids = gm.step(dev(nxt)).cpu().numpy()
+            lo, lg = om.logits(), gm.logits().cpu().numpy()
+            assert rel_err(lg, lo) <= REL_TOL, (s, rel_err(lg, lo))
+            for b in range(cfg["batch"]):
+                if check_ids:
+                    assert ids_agree(g_ids[b, 0], lo[b]), (s, b, g_ids, o_ids, top2_gap(lo[b]))
+            nxt = o_ids
+    gm.synchronize()
+    gm.close()
+    return worst
+
+
+PROMPT_CASES = [("gpt2", "q4_0"), ("gpt2", "q8_0"), ("gpt2", "aff8"), ("gpt2", "q5_0"), ("llama", "q8_0"),
+                ("llama", "q4_0"), ("llama", "aff4_g64"), ("llama", "aff4_g32")]
+
+
+@pytest.mark.parametrize("arch,fmt", PROMPT_CASES)
+def test_prompt_pass_matches_oracle(arch, fmt):
+    """A 70-id prompt (two 64-row tiles, the second ragged) on a small model."""
+    cfg = synth.small_config(arch, fmt, d_ff=256, n_ctx=96)
+    say(f"[prefill] {arch} {fmt}")
+    w = synth.model_weights(cfg, 42, norm_std=0.5)
+    check_prompt(cfg, w, [70])
+
+
+def test_prompt_pass_gqa_head128():
+    cfg = synth.small_config("llama", "q8_0", d_model=256, n_head=4, n_kv_head=2, head_dim=128, d_ff=512, n_ctx=96)
+    say("[prefill] llama gqa hd 128")
+    w = synth.model_weights(cfg, 42, norm_std=0.5)
+    check_prompt(cfg, w, [40])
+
+
+@pytest.mark.parametrize("mode", ["persistent", "per_operator"])
+def test_prompt_continues_after_decoding(mode):
+    """A prompt, three decoded steps, a second prompt, three steps, a one-id prompt (only the
+    decode step runs), a two-id prompt (one prompt-pass row)."""
+    cfg = synth.small_config("gpt2", "q4_0", d_ff=256, n_ctx=160)
+    say(f"[prefill] continued prompts {mode}")
+    w = synth.model_weights(cfg, 7, norm_std=0.5)
+    check_prompt(cfg, w, [33, 45, 1, 2], mode=mode)
+
+
+def test_prompt_longer_than_one_pass():
+    """600 ids: a 512-row pass, an 87-row pass, the decode step."""
+    cfg = synth.small_config("llama", "q4_0", d_ff=256, n_ctx=640, vocab=500)
+    say("[prefill] 600 ids in two passes")
+    w = synth.model_weights(cfg, 3, norm_std=0.5)
+    check_prompt(cfg, w, [600], n_steps=2)
+
+
+@pytest.mark.parametrize("arch,fmt", [("gpt2", "q4_0"), ("llama", "q8_0")])
+def test_prompt_two_rows(arch, fmt):
+    """Batch 2, a different prompt per row, 300 positions each: 600 rows in passes of 256
+    positions."""
+    cfg = synth.small_config(arch, fmt, batch=2, d_ff=256, n_ctx=320, vocab=500)
+    say(f"[prefill] batch 2 {arch} {fmt}")
+    w = synth.model_weights(cfg, 5, norm_std=0.5)
+    check_prompt(cfg, w, [300], n_steps=2, mode="per_operator")
+
+
+def test_causal_mask_leaves_earlier_positions_unchanged():
+    """Two 90-id prompts that agree on their first 41 ids: the caches agree bit for bit at
+    positions 0..40, and differ after."""
+    cfg = synth.small_config("llama", "q4_0", d_ff=256, n_ctx=96)
+    say("[prefill] causal mask")
+    w = synth.model_weights(cfg, 9, norm_std=0.5)
+    a = synth.prompt_tokens(cfg, 90, seed=1)
+    b = a.copy()
+    b[:, 41:, :] = synth.prompt_tokens(cfg, 49, seed=2)
+    assert not np.array_equal(a[:, 41:], b[:, 41:])
+    caches = []
+    for t in (a, b):
+        gm = gpu_model(cfg, w)
+        gm.prefill(dev(t))
+        k, v = gm.get_kv()
+        caches.append((k.cpu().numpy().view(np.uint16), v.cpu().numpy().view(np.uint16)))
+        gm.close()
+    (ka, va), (kb, vb) = caches
+    assert np.array_equal(ka[:, :, :, :41], kb[:, :, :, :41]) and np.array_equal(va[:, :, :, :41], vb[:, :, :, :41])
+    assert not np.array_equal(ka[:, :, :, 41:], kb[:, :, :, 41:])
+
+
+def test_prompt_history_and_consumed_ids():
+    """The history holds the next prompt id at every prompt position but the last, and the
+    sampled id there; the penalty's consumed ids are the prompt."""
+    cfg = synth.small_config("gpt2", "q8_0", d_ff=256, n_ctx=64)
+    w = synth.model_weights(cfg, 4, norm_std=0.5)
+    gm = gpu_model(cfg, w)
+    toks = synth.prompt_tokens(cfg, 20, seed=6)
+    nxt = gm.prefill(dev(toks)).cpu().numpy()
+    hist = gm.tokens(0, 20).cpu().numpy()[:, 0, 0]
+    assert list(hist[:19]) == [int(t) for t in toks[0, 1:, 0]]
+    assert int(hist[19]) == int(nxt[0, 0])
+    gm.close()
+
+
+@pytest.mark.parametrize("name", ["gpt2_medium_q4_0", "llama520m_q8_0"])
+def test_full_size_prompt_pass(name):
+    """The benchmark's prompt (256 ids for GPT-2-Medium, 300 for Llama-520M) at the real shapes:
+    the prompt pass against the stepwise prefill (cache per layer and logits rel <= 2e-3, same
+    next id unless near-tied), and the first layer's cached keys and values at sampled positions
+    against the oracle's layer run on the same embedding rows."""
+    torch = torch_mod()
+    cfg = synth.config(name)
+    n = 256 if cfg["arch"] == "gpt2" else 300
+    say(f"[prefill-full] {name} {n} ids")
+    w = synth.model_weights(cfg, 42)
+    toks = synth.prompt_tokens(cfg, n, seed=42)
+    gm = gpu_model(cfg, w)
+    g_ids = gm.prefill(dev(toks)).cpu().numpy()
+    gk, gv = gm.get_kv()
+    lg = gm.logits().cpu().numpy()
+    gm.close()
+    sm = gpu_model(cfg, w)
+    s_ids = sm.prefill_stepwise(dev(toks)).cpu().numpy()
+    sk, sv = sm.get_kv()
+    ls = sm.logits().cpu().numpy()
+    sm.close()
+    r = max(max(rel_err(gk[l].cpu().numpy(), sk[l].cpu().numpy()), rel_err(gv[l].cpu().numpy(), sv[l].cpu().numpy()))
+            for l in range(cfg["n_layer"]))
+    say(f"  against stepwise: cache rel {r:.2e}, logits rel {rel_err(lg, ls):.2e}")
+    assert r <= REL_TOL and rel_err(lg, ls) <= REL_TOL
+    assert ids_agree(g_ids[0, 0], ls[0])
+    # layer 0 at sampled positions: the oracle runs the layer on the embedding row and writes its
+    # own key and value there (the cache below is the GPU's, loaded so that attention has keys)
+    om = oracle.OracleModel(cfg, w)
+    om.load_kv(gk.cpu().numpy().view(np.uint16), gv.cpu().numpy().view(np.uint16), n)
+    emb = w[0].reshape(cfg["vocab"], cfg["d_model"]).astype(np.float64)
+    wpe = w[1].reshape(cfg["n_ctx"], cfg["d_model"]).astype(np.float64) if cfg["arch"] == "gpt2" else None
+    for p in (0, 1, 127, n - 2):
+        x = emb[int(toks[0, p, 0])] + (wpe[p] if wpe is not None else 0.0)
+        om.layer_forward(0, x, p)
+    ok, ov = om.get_kv()
+    for p in (0, 1, 127, n - 2):
+        rk = rel_err(gk[0, :, :, p].cpu().numpy(), ok[0, :, :, p].view(np.float16))
+        rv = rel_err(gv[0, :, :, p].cpu().numpy(), ov[0, :, :, p].view(np.float16))
+        say(f"  layer 0 position {p}: k rel {rk:.2e} v rel {rv:.2e}")
+        assert rk <= REL_TOL and rv <= REL_TOL

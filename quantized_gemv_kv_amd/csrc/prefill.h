@@ -14,7 +14,7 @@
 
 namespace tsd {
 
-constexpr int PF_TILE = 64;            // rows and columns of a product tile (one workgroup)
+constexpr int PF_TILE = 32;            // rows and columns of a product tile (one workgroup)
 constexpr int PF_MAX_ROWS = 512;       // rows one pass of the prompt holds (larger prompts are chunked)
 
 enum PfEpi : int {

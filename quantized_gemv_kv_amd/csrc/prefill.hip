@@ -16,11 +16,15 @@
 // Operand roles: A = 16 activation rows (lane l holds row l % 16), B = 16 weight rows (lane l
 // holds row l % 16); lane group j = l / 16 supplies K positions 8 j .. 8 j + 7 of the block to
 // both operands, so a lane's four results share one weight row (and so one scale).  A workgroup
-// computes a 64 x 64 tile; each of its four waves a 32 x 32 quarter (2 x 2 MFMA tiles).
+// computes a 32 x 32 tile (2 x 2 MFMA tiles per wave); its four (eight, for reductions of 2048
+// and more) waves each take a contiguous share of the scale groups along K, and the partial tiles
+// are summed through LDS in wave order, so results do not depend on timing.  The small tile
+// and the split keep ~1000 waves in flight for the 1024-wide projections of a 256-row prompt.
 //
 // Epilogues write what the next kernel consumes: queries (after RoPE) and the fp16 K/V cache
 // entries at each row's position, the residual add, or the next product's hi/lo operand through
-// GELU or SwiGLU.  Attention is causal over the cache: row r at position p reads keys 0..p.
+// GELU or SwiGLU.  Attention is causal over the cache (row r at position p reads keys 0..p) and
+// runs on the matrix cores too, in the flash form (a running max and sum per query).
 #include <math.h>
 
 #include <type_traits>
@@ -93,17 +97,20 @@ __device__ __forceinline__ float4v mfma(half8 a, half8 b, float4v c)
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-template <int F, int EPI>
-__global__ __launch_bounds__(256) void k_pf_gemm(const PfGemmArgs a)
+template <int F, int EPI, int KS>
+__global__ __launch_bounds__(64 * KS) void k_pf_gemm(const PfGemmArgs a)
 {
     using T = PfFmt<F>;
     constexpr int GB = T::GB;
+    __shared__ float red[KS][16][64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int c = lane & 15, j = lane >> 4;
-    const int m0 = blockIdx.y * PF_TILE + (w & 1) * 32;
-    const int n0 = blockIdx.x * PF_TILE + (w >> 1) * 32;
+    const int m0 = blockIdx.y * PF_TILE;
+    const int n0 = blockIdx.x * PF_TILE;
     const int N = a.W.N, K = a.W.K, M = a.M;
     const int ngrp = K / (32 * GB);
+    // wave w reduces over scale groups [g_begin, g_end): the K range is split KS ways
+    const int g_begin = ngrp * w / KS, g_end = ngrp * (w + 1) / KS;
 
     const TSD_GLOBAL half8* ah[2];
     const TSD_GLOBAL half8* al[2];
@@ -210,21 +217,33 @@ __global__ __launch_bounds__(256) void k_pf_gemm(const PfGemmArgs a)
             }
         }
     };
-    int g = 0;
-    for (; g + 4 <= ngrp; g += 4) stage(g, std::integral_constant<int, 4>{});
-    for (; g < ngrp; ++g) stage(g, std::integral_constant<int, 1>{});
+    int g = g_begin;
+    for (; g + 4 <= g_end; g += 4) stage(g, std::integral_constant<int, 4>{});
+    for (; g < g_end; ++g) stage(g, std::integral_constant<int, 1>{});
 
-    // epilogue: lane holds weight row n = n0 + 16u + c for activation rows m0 + 16s + 4j + i
+    // the KS partial tiles summed in wave order (deterministic); wave w < 4 then finishes the
+    // 16 x 16 sub-tile (s, u) = (w & 1, w >> 1)
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[w][(s * 2 + u) * 4 + i][lane] = acc[s][u][i];
+    __syncthreads();
+    if (w >= 4) return;   // whole waves; no barrier follows
+    const int s = w & 1, u = w >> 1;
+    // epilogue: lane holds weight row n = n0 + 16u + c for activation rows m0 + 16s + 4j + i
+    {
         const int n = n0 + 16 * u + c;
         const float bias = (a.bias && n < N) ? a.bias[n] : 0.f;
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
+        {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
+                float sum = red[0][(s * 2 + u) * 4 + i][lane];
+#pragma unroll
+                for (int q = 1; q < KS; ++q) sum += red[q][(s * 2 + u) * 4 + i][lane];
                 const int r = m0 + 16 * s + 4 * j + i;
-                const float v = acc[s][u][i] + bias;
+                const float v = sum + bias;
                 float partner = 0.f;
                 if constexpr (EPI == PF_SWIGLU || EPI == PF_QKV) partner = dpp_mov<0xB1>(v);   // column n ^ 1
                 if (r >= M || n >= N) continue;
@@ -260,6 +279,7 @@ __global__ __launch_bounds__(256) void k_pf_gemm(const PfGemmArgs a)
                     }
                 }
             }
+        }
     }
 }
 
@@ -349,78 +369,147 @@ __global__ __launch_bounds__(256) void k_pf_split(const float* __restrict__ x, s
     if (i < n) put_hilo(hi, lo, i, x[i]);
 }
 
-// ---- causal attention over the cache ---------------------------------------------------------
-// one wave per (row, head): keys in chunks of 64 (one per lane) with a running max and sum;
-// the value rows are read coalesced, one key at a time, each lane owning hd / 64 output dims
-template <int HD>
-__global__ __launch_bounds__(256) void k_pf_attn(const PfAttnArgs a)
+// ---- causal attention over the cache (matrix cores) -------------------------------------------
+// One wave per (batch row, 16 consecutive queries, head).  Per block of 32 keys:
+//   S^T = K Q^T          A = 16 keys (lane row = key), B = Q^T (lane column = query c), K-dim =
+//                        head dims; q enters as fp16 hi/lo (scaled to the log2 domain), keys exact
+//   running max / sum    per query c over its 8 keys in the lane and the 4 lane groups
+//   O^T += V^T P^T       B = P^T is exactly the lane's 8 probabilities (hi/lo), A = V^T with row
+//                        c of dim tile dt holding dim c * DT + dt, so a lane reads DT consecutive
+//                        dims of each of its 8 keys
+// The result O^T leaves the lane with query c's dims (4 j + i) DT + dt: 4 DT consecutive values.
+__device__ __forceinline__ float group4_max(float v)   // over lanes c, c + 16, c + 32, c + 48
 {
-    __shared__ float qs[4][HD];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int r = blockIdx.x * 4 + w, h = blockIdx.y;
-    if (r >= a.M) return;   // whole waves only; no workgroup barrier follows
-    const int b = r / a.n_pos, p = a.pos0 + (r - b * a.n_pos), n_keys = p + 1;
-    const int g = h / (a.H / a.Hkv);
-    const TSD_GLOBAL _Float16* Kc = (const TSD_GLOBAL _Float16*)glb(a.kc) + b * a.kv_row + (size_t)g * a.n_ctx * HD;
-    const TSD_GLOBAL _Float16* Vc = (const TSD_GLOBAL _Float16*)glb(a.vc) + b * a.kv_row + (size_t)g * a.n_ctx * HD;
-    // scores in the log2 domain: q . k / sqrt(hd) * log2(e)
-    const float qscale = 1.4426950408889634f / sqrtf((float)HD);
-#pragma unroll
-    for (int i = lane; i < HD; i += 64) qs[w][i] = a.q[(size_t)r * a.ldq + h * HD + i] * qscale;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    constexpr int OD = HD / 64;   // output dims per lane: lane * OD .. lane * OD + OD - 1
-    float o[OD];
-#pragma unroll
-    for (int e = 0; e < OD; ++e) o[e] = 0.f;
-    float mx = -INFINITY, l = 0.f;
-    for (int c0 = 0; c0 < n_keys; c0 += 64) {
-        const int key = c0 + lane;
-        float s = -INFINITY;
-        if (key < n_keys) {
-            const TSD_GLOBAL half8* kr = (const TSD_GLOBAL half8*)(Kc + (size_t)key * HD);
-            float acc = 0.f;
-#pragma unroll
-            for (int v8 = 0; v8 < HD / 8; ++v8) {
-                const half8 kv = kr[v8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc = fmaf(qs[w][v8 * 8 + e], (float)kv[e], acc);
-            }
-            s = acc;
-        }
-        const float mn = fmaxf(mx, wave_max(s));   // finite: key c0 is always valid
-        const float alpha = exp2f(mx - mn);         // 0 on the first chunk
-        const float pj = key < n_keys ? exp2f(s - mn) : 0.f;
-        l = fmaf(l, alpha, wave_sum(pj));
-#pragma unroll
-        for (int e = 0; e < OD; ++e) o[e] *= alpha;
-        mx = mn;
-        const int nk = min(64, n_keys - c0);
-        for (int jj = 0; jj < nk; ++jj) {
-            const float pw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), jj));   // key c0 + jj's weight
-            const TSD_GLOBAL _Float16* vr = Vc + (size_t)(c0 + jj) * HD + lane * OD;
-#pragma unroll
-            for (int e = 0; e < OD; ++e) o[e] = fmaf(pw, (float)vr[e], o[e]);
-        }
-    }
-    const float il = 1.0f / l;
-#pragma unroll
-    for (int e = 0; e < OD; ++e) put_hilo(a.ohi, a.olo, (size_t)r * a.ldo + h * HD + lane * OD + e, o[e] * il);
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float group4_sum(float v)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int F>
-hipError_t gemm_epi(int epi, const PfGemmArgs& a, dim3 grid, hipStream_t st)
+template <int HD>
+__global__ __launch_bounds__(64) void k_pf_fattn(const PfAttnArgs a)
+{
+    constexpr int NC = HD / 32;   // K-dim chunks of S^T
+    constexpr int DT = HD / 16;   // dim tiles of O^T
+    typedef _Float16 halfDT __attribute__((ext_vector_type(DT)));
+    const int lane = threadIdx.x, c = lane & 15, j = lane >> 4;
+    const int ntile = (a.n_pos + 15) / 16;
+    const int b = blockIdx.x / ntile, t0 = (blockIdx.x - b * ntile) * 16;
+    const int h = blockIdx.y, g = h / (a.H / a.Hkv);
+    const int tq = min(t0 + c, a.n_pos - 1);              // query of lane column c (clamped; never stored)
+    const int r = b * a.n_pos + tq;
+    const int pq = a.pos0 + tq;                            // it attends keys 0..pq
+    const int plast = a.pos0 + min(t0 + 15, a.n_pos - 1);  // the tile's last position
+    const TSD_GLOBAL _Float16* Kc = (const TSD_GLOBAL _Float16*)glb(a.kc) + b * a.kv_row + (size_t)g * a.n_ctx * HD;
+    const TSD_GLOBAL _Float16* Vc = (const TSD_GLOBAL _Float16*)glb(a.vc) + b * a.kv_row + (size_t)g * a.n_ctx * HD;
+
+    // Q^T fragments: lane (j, c) holds query c's dims 32 kk + 8 j .. + 7
+    const float qscale = 1.4426950408889634f / sqrtf((float)HD);
+    half8 qh[NC], ql[NC];
+    const TSD_GLOBAL float* qr = glb(a.q) + (size_t)r * a.ldq + h * HD + 8 * j;
+#pragma unroll
+    for (int kk = 0; kk < NC; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = qr[32 * kk + e] * qscale;
+            const _Float16 hi = (_Float16)x;
+            qh[kk][e] = hi;
+            ql[kk][e] = (_Float16)(x - (float)hi);
+        }
+    float4v o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = float4v{0.f, 0.f, 0.f, 0.f};
+    float mx = -INFINITY, l = 0.f;   // query c's running max and sum (the same in its 4 lanes)
+
+    for (int k0 = 0; k0 <= plast; k0 += 32) {
+        // keys of this lane's operand rows / probability slots (clamped reads, masked below)
+        float4v st[2];
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const int key = min(k0 + 16 * sub + c, plast);
+            const TSD_GLOBAL half8* kr = (const TSD_GLOBAL half8*)(Kc + (size_t)key * HD) + j;
+            st[sub] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < NC; ++kk) {
+                const half8 kf = kr[4 * kk];
+                st[sub] = mfma(kf, qh[kk], st[sub]);
+                st[sub] = mfma(kf, ql[kk], st[sub]);
+            }
+        }
+        halfDT vr[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int key = min(k0 + 16 * (e >> 2) + 4 * j + (e & 3), plast);
+            vr[e] = *(const TSD_GLOBAL halfDT*)(Vc + (size_t)key * HD + c * DT);
+        }
+        // lane holds S^T[key k0 + 16 (e / 4) + 4 j + e % 4][query c] at slot e
+        float sv[8];
+        float ml = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int key = k0 + 16 * (e >> 2) + 4 * j + (e & 3);
+            sv[e] = key <= pq ? st[e >> 2][e & 3] : -INFINITY;
+            ml = fmaxf(ml, sv[e]);
+        }
+        const float mn = fmaxf(mx, group4_max(ml));   // finite: key 0 is in the first block
+        const float alpha = exp2f(mx - mn);          // 0 on the first block
+        half8 ph, pl;
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float p = exp2f(sv[e] - mn);
+            ps += p;
+            const _Float16 hi = (_Float16)p;
+            ph[e] = hi;
+            pl[e] = (_Float16)(p - (float)hi);
+        }
+        l = fmaf(l, alpha, group4_sum(ps));
+        mx = mn;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            half8 va;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) va[e] = vr[e][dt];
+            o[dt] = o[dt] * alpha;
+            o[dt] = mfma(va, ph, o[dt]);
+            o[dt] = mfma(va, pl, o[dt]);
+        }
+    }
+    if (t0 + c >= a.n_pos) return;
+    const float il = 1.0f / l;
+    const size_t base = (size_t)r * a.ldo + h * HD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) put_hilo(a.ohi, a.olo, base + (4 * j + i) * DT + dt, o[dt][i] * il);
+}
+
+template <int F, int KS>
+hipError_t gemm_epi_ks(int epi, const PfGemmArgs& a, dim3 grid, hipStream_t st)
 {
     switch (epi) {
-    case PF_STORE: k_pf_gemm<F, PF_STORE><<<grid, 256, 0, st>>>(a); break;
-    case PF_QKV: k_pf_gemm<F, PF_QKV><<<grid, 256, 0, st>>>(a); break;
-    case PF_RESID: k_pf_gemm<F, PF_RESID><<<grid, 256, 0, st>>>(a); break;
-    case PF_GELU: k_pf_gemm<F, PF_GELU><<<grid, 256, 0, st>>>(a); break;
-    case PF_SWIGLU: k_pf_gemm<F, PF_SWIGLU><<<grid, 256, 0, st>>>(a); break;
+    case PF_STORE: k_pf_gemm<F, PF_STORE, KS><<<grid, 64 * KS, 0, st>>>(a); break;
+    case PF_QKV: k_pf_gemm<F, PF_QKV, KS><<<grid, 64 * KS, 0, st>>>(a); break;
+    case PF_RESID: k_pf_gemm<F, PF_RESID, KS><<<grid, 64 * KS, 0, st>>>(a); break;
+    case PF_GELU: k_pf_gemm<F, PF_GELU, KS><<<grid, 64 * KS, 0, st>>>(a); break;
+    case PF_SWIGLU: k_pf_gemm<F, PF_SWIGLU, KS><<<grid, 64 * KS, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// long reductions split eight ways, the rest four ways
+template <int F>
+hipError_t gemm_epi(int epi, const PfGemmArgs& a, dim3 grid, hipStream_t st)
+{
+    return a.W.K >= 2048 ? gemm_epi_ks<F, 8>(epi, a, grid, st) : gemm_epi_ks<F, 4>(epi, a, grid, st);
 }
 
 }  // namespace
@@ -471,9 +560,10 @@ hipError_t launch_pf_split(const float* x, int M, int K, __half* hi, __half* lo,
 hipError_t launch_pf_attention(const PfAttnArgs& a, hipStream_t st)
 {
     if (a.M <= 0 || a.Hkv <= 0 || a.H % a.Hkv) return hipErrorInvalidValue;
-    const dim3 grid((a.M + 3) / 4, a.H);
-    if (a.hd == 64) k_pf_attn<64><<<grid, 256, 0, st>>>(a);
-    else if (a.hd == 128) k_pf_attn<128><<<grid, 256, 0, st>>>(a);
+    if (a.M % a.n_pos) return hipErrorInvalidValue;
+    const dim3 grid((a.M / a.n_pos) * ((a.n_pos + 15) / 16), a.H);
+    if (a.hd == 64) k_pf_fattn<64><<<grid, 64, 0, st>>>(a);
+    else if (a.hd == 128) k_pf_fattn<128><<<grid, 64, 0, st>>>(a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

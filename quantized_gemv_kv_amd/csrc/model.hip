@@ -559,23 +559,30 @@ void count_launches(tsd_model* m)
     m->kind_launches[KIND_HEAD] = 1;
 }
 
-// ---- the prompt pass (GPT2/LLAMA) -----------------------------------------------------------
-// Prompt positions t0 .. t0 + np - 1 of every batch row (ids d_tokens[b][n_prompt]) at cache
-// positions m->n_past .. m->n_past + np - 1: the embedding rows, then per layer norm, QKV product
-// (queries, RoPE, K/V into the cache), causal attention, output projection into the residual
-// stream, norm, FC / gate-up product and down projection.  No head: the last prompt position
-// goes through the decode step.
+// ---- the prompt pass -------------------------------------------------------------------------
+// Prompt positions t0 .. t0 + np - 1 of every batch row (ids d_tokens[b][n_prompt][tokens per
+// position]) at cache positions m->n_past .. m->n_past + np - 1: the embedding rows (the sum of
+// the frame's code embeddings for the Talker), then per layer norm, QKV product (queries, RoPE,
+// K/V into the cache), causal attention, output projection into the residual stream, norm,
+// FC / gate-up product and down projection.  No head: the last prompt position goes through the
+// decode step (the whole frame for TALKER_CP).
 hipError_t pf_enqueue(tsd_model* m, const int32_t* d_tokens, int n_prompt, int t0, int np, hipStream_t st)
 {
     const tsd_config& c = m->c;
     const int d = c.d_model, H = c.n_head, Hk = c.n_kv_head, hd = c.head_dim, ff = c.d_ff, B = c.batch, f = c.wfmt;
-    const bool gpt2 = c.arch == TSD_ARCH_GPT2;
+    const bool gpt2 = c.arch == TSD_ARCH_GPT2, talker = c.arch == TSD_ARCH_TALKER_CP;
     const int M = B * np, qd = H * hd, amax = std::max(d, qd);
     const int pos0 = m->n_past;
     PfRowArgs ra{};
     ra.M = M; ra.d = d; ra.n_pos = np; ra.pos0 = pos0;
-    ra.tok = d_tokens; ra.tok_stride = n_prompt; ra.t0 = t0; ra.vocab = c.vocab; ra.n_prompt = n_prompt;
-    ra.emb = m->emb[0]; ra.wpe = m->wpe; ra.seq = m->seq; ra.hist = m->hist; ra.B = B;
+    ra.tok = d_tokens; ra.tok_stride = n_prompt; ra.t0 = t0; ra.n_prompt = n_prompt;
+    ra.n_tab = m->tpp;
+    for (int k = 0; k < m->tpp; ++k) {
+        ra.tab[k] = m->emb[k];
+        ra.tab_rows[k] = m->emb_rows[k];
+    }
+    ra.wpe = m->wpe; ra.seq = m->seq; ra.B = B;
+    ra.hist = talker ? nullptr : m->hist;   // the Talker's prompt frames leave their history alone, as its frames do
     ra.x = m->pf_x; ra.x_out = m->pf_x; ra.eps = c.norm_eps;
     ra.ahi = m->pf_ahi; ra.alo = m->pf_alo; ra.lda = amax;
     PfGemmArgs ga{};
@@ -586,33 +593,47 @@ hipError_t pf_enqueue(tsd_model* m, const int32_t* d_tokens, int n_prompt, int t
     aa.q = m->pf_q; aa.ldq = qd; aa.kv_row = ga.kv_row;
     aa.M = M; aa.H = H; aa.Hkv = Hk; aa.hd = hd; aa.n_ctx = c.n_ctx; aa.n_pos = np; aa.pos0 = pos0;
     aa.ohi = m->pf_ahi; aa.olo = m->pf_alo; aa.ldo = amax;
+    // one product: the packed matrix (GPT2/LLAMA) or the tiled one (Talker)
+    auto gemm = [&](PfGemmArgs g, int epi, const PackedMat* P, const TiledMat* T) {
+        if (T) {
+            g.T = *T;
+            g.W.N = T->N;
+            g.W.K = T->K;
+            return launch_pf_gemm_tiled(epi, g, st);
+        }
+        g.W = *P;
+        return launch_pf_gemm(f, epi, g, st);
+    };
     hipError_t e = hipSuccess;
     for (int l = 0; l < c.n_layer && e == hipSuccess; ++l) {
-        const LayerW& w = m->L[l];
+        const LayerW* w = talker ? nullptr : &m->L[l];
+        const TLayerW* tw = talker ? &m->Lt[l] : nullptr;
         __half* kc = m->kc + m->kv_layer_elems * l;
         __half* vc = m->vc + m->kv_layer_elems * l;
-        ra.g = w.n1g; ra.bn = w.n1b;
+        ra.g = talker ? tw->n1g : w->n1g;
+        ra.bn = talker ? nullptr : w->n1b;
         e = l == 0 ? launch_pf_embed(ra, st) : launch_pf_norm(ra, st);
         // Q/K/V: queries (after RoPE) to pf_q, keys and values into the cache
         PfGemmArgs q = ga;
-        q.W = w.qkv; q.ahi = m->pf_ahi; q.alo = m->pf_alo; q.lda = amax; q.bias = w.bqkv;
+        q.ahi = m->pf_ahi; q.alo = m->pf_alo; q.lda = amax; q.bias = talker ? nullptr : w->bqkv;
         q.q = m->pf_q; q.ldq = qd; q.qrows = qd; q.krows = Hk * hd; q.hd = hd; q.rope = gpt2 ? 0 : 1;
         q.rope_tab = m->rope; q.kc = kc; q.vc = vc;
-        if (e == hipSuccess) e = launch_pf_gemm(f, PF_QKV, q, st);
+        if (e == hipSuccess) e = gemm(q, PF_QKV, talker ? nullptr : &w->qkv, talker ? &tw->qkv : nullptr);
         aa.kc = kc; aa.vc = vc;
         if (e == hipSuccess) e = launch_pf_attention(aa, st);
         PfGemmArgs o = ga;
-        o.W = w.o; o.ahi = m->pf_ahi; o.alo = m->pf_alo; o.lda = amax; o.bias = w.bo; o.y = m->pf_x; o.ldy = d;
-        if (e == hipSuccess) e = launch_pf_gemm(f, PF_RESID, o, st);
-        ra.g = w.n2g; ra.bn = w.n2b;
+        o.ahi = m->pf_ahi; o.alo = m->pf_alo; o.lda = amax; o.bias = talker ? nullptr : w->bo; o.y = m->pf_x; o.ldy = d;
+        if (e == hipSuccess) e = gemm(o, PF_RESID, talker ? nullptr : &w->o, talker ? &tw->o : nullptr);
+        ra.g = talker ? tw->n2g : w->n2g;
+        ra.bn = talker ? nullptr : w->n2b;
         if (e == hipSuccess) e = launch_pf_norm(ra, st);
         PfGemmArgs u = ga;
-        u.W = w.fc; u.ahi = m->pf_ahi; u.alo = m->pf_alo; u.lda = amax; u.bias = w.bfc;
+        u.ahi = m->pf_ahi; u.alo = m->pf_alo; u.lda = amax; u.bias = talker ? nullptr : w->bfc;
         u.ohi = m->pf_hhi; u.olo = m->pf_hlo; u.ldo = ff;
-        if (e == hipSuccess) e = launch_pf_gemm(f, gpt2 ? PF_GELU : PF_SWIGLU, u, st);
+        if (e == hipSuccess) e = gemm(u, gpt2 ? PF_GELU : PF_SWIGLU, talker ? nullptr : &w->fc, talker ? &tw->fc : nullptr);
         PfGemmArgs dn = ga;
-        dn.W = w.down; dn.ahi = m->pf_hhi; dn.alo = m->pf_hlo; dn.lda = ff; dn.bias = w.bdown; dn.y = m->pf_x; dn.ldy = d;
-        if (e == hipSuccess) e = launch_pf_gemm(f, PF_RESID, dn, st);
+        dn.ahi = m->pf_hhi; dn.alo = m->pf_hlo; dn.lda = ff; dn.bias = talker ? nullptr : w->bdown; dn.y = m->pf_x; dn.ldy = d;
+        if (e == hipSuccess) e = gemm(dn, PF_RESID, talker ? nullptr : &w->down, talker ? &tw->down : nullptr);
     }
     return e;
 }
@@ -809,7 +830,6 @@ tsd_status tsd_prefill(tsd_model* m, const int32_t* d_tokens, int n, int32_t* d_
     if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
     if (!d_tokens || n <= 0) return fail(m, TSD_ERR_INVALID_ARGUMENT, "empty prompt");
     if (m->n_past + n > m->c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "prompt does not fit the context");
-    if (m->c.arch == TSD_ARCH_TALKER_CP) return tsd_prefill_stepwise(m, d_tokens, n, d_next);
     const int nt = m->c.batch * m->tpp;
     // every position but the last through the prompt pass, in chunks of pf_rows rows
     const int chunk = m->pf_rows / m->c.batch;
@@ -819,7 +839,7 @@ tsd_status tsd_prefill(tsd_model* m, const int32_t* d_tokens, int n, int32_t* d_
         m->n_past += np;
     }
     if (n > 1) HIP_TRY(m, launch_fill_i32(m->pos, m->n_past, 1, m->st), "set position");
-    // the last position: one decode step (head, sampler, history)
+    // the last position: one decode step (head, sampler, history; the whole frame for TALKER_CP)
     HIP_TRY(m, launch_gather_i32(m->tok, d_tokens + (size_t)(n - 1) * m->tpp, m->c.batch, m->tpp, (long long)n * m->tpp, m->st),
             "set input");
     HIP_TRY(m, before_launch(m), "exchange restart");

@@ -10,6 +10,7 @@
 // Row r is batch row b = r / n_pos, position pos0 + r % n_pos.
 #pragma once
 
+#include "frame.h"
 #include "kernels.h"
 
 namespace tsd {
@@ -25,8 +26,11 @@ enum PfEpi : int {
     PF_SWIGLU = 4,   // rows 2i/2i+1 = gate/up: operand [r][i] = silu(gate) * up
 };
 
+constexpr int PF_TILED8 = 100;   // weight source: the batched path's tiled 8-bit affine layout
+
 struct PfGemmArgs {
-    PackedMat W;                 // packed GEMV layout, N rows of K
+    PackedMat W;                 // packed GEMV layout, N rows of K (W.N / W.K give the shape for either source)
+    TiledMat T;                  // tiled 8-bit affine layout (launch_pf_gemm_tiled)
     int M;                       // operand rows
     const __half* ahi;           // [M][lda] operand
     const __half* alo;
@@ -49,14 +53,18 @@ struct PfGemmArgs {
 
 struct PfRowArgs {
     int M, d, n_pos, pos0;
-    // embedding rows: ids tok[b * tok_stride + t0 + t] (clamped into [0, vocab))
+    // embedding rows: the sum over c < n_tab of tab[c][id_c], id_c = tok[(b * tok_stride + t0 + t)
+    // * n_tab + c] clamped into [0, tab_rows[c]) (one table for GPT2/LLAMA, one per codebook for
+    // the Talker)
     const int* tok;
     long long tok_stride;
-    int t0, vocab, n_prompt;     // n_prompt: prompt length (for the history of the next id)
-    const float* emb;            // [vocab][d]
+    int t0, n_prompt;            // n_prompt: prompt length (for the history of the next id)
+    int n_tab;
+    const float* tab[16];
+    int tab_rows[16];
     const float* wpe;            // [n_ctx][d] learned positions or null
-    int* seq;                    // [n_ctx][B] consumed ids
-    int* hist;                   // [n_ctx][B] next ids
+    int* seq;                    // [n_ctx][B] consumed id (code 0)
+    int* hist;                   // [n_ctx][B] next ids, or null
     int B;
     // norm
     const float* x;              // [M][d]
@@ -81,6 +89,8 @@ struct PfAttnArgs {
 // supported when the reduction dimension is a multiple of 32 and the operand rows fit
 bool pf_gemm_ok(int fmt, int K);
 hipError_t launch_pf_gemm(int fmt, int epi, const PfGemmArgs& a, hipStream_t st);
+// the same product with a.T (tiled 8-bit affine) as the weights; a.W.N / a.W.K carry the shape
+hipError_t launch_pf_gemm_tiled(int epi, const PfGemmArgs& a, hipStream_t st);
 // X rows from the embeddings (and the history words), then the first norm into the operand
 hipError_t launch_pf_embed(const PfRowArgs& a, hipStream_t st);
 hipError_t launch_pf_norm(const PfRowArgs& a, hipStream_t st);

@@ -60,10 +60,12 @@ __device__ __forceinline__ half8 codes_h8(uint32_t w0, uint32_t w1, _Float16 off
 }
 
 // per-format access to one 32-weight block of a packed row, for lane group j
+// (PF_TILED8: the batched path's tiled 8-bit affine matrices, one 16-byte load per lane covering
+// both blocks of a 64-group in the same lane order)
 template <int F> struct PfFmt {
     static constexpr bool NIB = fmt_nibbles(F);
-    static constexpr bool AFF = fmt_affine(F);
-    static constexpr int GB = (F == FMT_AFF8 || F == FMT_AFF4_G64) ? 2 : 1;   // blocks per scale group
+    static constexpr bool AFF = fmt_affine(F) || F == PF_TILED8;
+    static constexpr int GB = (F == FMT_AFF8 || F == FMT_AFF4_G64 || F == PF_TILED8) ? 2 : 1;   // blocks per scale group
     // byte offset of lane group j's eight codes inside row n, and the stride between blocks
     __device__ static size_t row_off(int n, int K, int j)
     {
@@ -124,13 +126,21 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(const PfGemmArgs a)
     const TSD_GLOBAL _Float16* sp[2];
     const TSD_GLOBAL _Float16* bp[2];
     const TSD_GLOBAL uint32_t* hp[2];
+    const TSD_GLOBAL u32x4* tq[2];     // PF_TILED8: lane's 16 bytes of group 0 of its 16-row tile
+    const TSD_GLOBAL uint32_t* tsb[2]; // PF_TILED8: its (scale | bias << 16) word of group 0
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int n = min(n0 + 16 * u + c, N - 1);
-        wp[u] = glb(a.W.q) + T::row_off(n, K, j);
-        sp[u] = (const TSD_GLOBAL _Float16*)glb(a.W.s) + (size_t)n * ngrp;
-        bp[u] = T::AFF ? (const TSD_GLOBAL _Float16*)glb(a.W.b) + (size_t)n * ngrp : nullptr;
-        hp[u] = F == FMT_Q5_0 ? glb(a.W.h) + (size_t)n * (K / 32) : nullptr;
+        if constexpr (F == PF_TILED8) {
+            const int t = min((n0 + 16 * u) / 16, (N - 1) / 16);   // lane row c of tile t (rows past N never stored)
+            tq[u] = (const TSD_GLOBAL u32x4*)glb(a.T.q) + (size_t)t * ngrp * 64 + lane;
+            tsb[u] = glb(a.T.sb) + (size_t)t * ngrp * 16 + c;
+        } else {
+            const int n = min(n0 + 16 * u + c, N - 1);
+            wp[u] = glb(a.W.q) + T::row_off(n, K, j);
+            sp[u] = (const TSD_GLOBAL _Float16*)glb(a.W.s) + (size_t)n * ngrp;
+            bp[u] = T::AFF ? (const TSD_GLOBAL _Float16*)glb(a.W.b) + (size_t)n * ngrp : nullptr;
+            hp[u] = F == FMT_Q5_0 ? glb(a.W.h) + (size_t)n * (K / 32) : nullptr;
+        }
     }
 
     half8 ones;
@@ -159,18 +169,37 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(const PfGemmArgs a)
                 xh[b][s] = ah[s][blk * 4];   // 32 halves = 4 half8 per block
                 xl[b][s] = al[s][blk * 4];
             }
+            if constexpr (F != PF_TILED8) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                wr[b][u] = *(const TSD_GLOBAL u32x2*)(wp[u] + (size_t)blk * T::BLOCK_BYTES);
-                hb[b][u] = F == FMT_Q5_0 ? hp[u][blk] : 0u;
+                for (int u = 0; u < 2; ++u) {
+                    wr[b][u] = *(const TSD_GLOBAL u32x2*)(wp[u] + (size_t)blk * T::BLOCK_BYTES);
+                    hb[b][u] = F == FMT_Q5_0 ? hp[u][blk] : 0u;
+                }
             }
+        }
+        if constexpr (F == PF_TILED8) {   // one 16-byte load per group: bytes 0-7 block 2g, 8-15 block 2g+1
+#pragma unroll
+            for (int q = 0; q < NG; ++q)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const u32x4 v = tq[u][(size_t)(g0 + q) * 64];
+                    wr[2 * q][u] = u32x2{v.x, v.y};
+                    wr[2 * q + 1][u] = u32x2{v.z, v.w};
+                    hb[2 * q][u] = hb[2 * q + 1][u] = 0u;
+                }
         }
 #pragma unroll
         for (int q = 0; q < NG; ++q)
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                sc[q][u] = (float)sp[u][g0 + q];
-                bi[q][u] = T::AFF ? (float)bp[u][g0 + q] : 0.f;
+                if constexpr (F == PF_TILED8) {
+                    const uint32_t sb = tsb[u][(size_t)(g0 + q) * 16];
+                    sc[q][u] = (float)__builtin_bit_cast(_Float16, (uint16_t)(sb & 0xFFFFu));
+                    bi[q][u] = (float)__builtin_bit_cast(_Float16, (uint16_t)(sb >> 16));
+                } else {
+                    sc[q][u] = (float)sp[u][g0 + q];
+                    bi[q][u] = T::AFF ? (float)bp[u][g0 + q] : 0.f;
+                }
             }
 #pragma unroll
         for (int q = 0; q < NG; ++q) {
@@ -217,8 +246,9 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(const PfGemmArgs a)
             }
         }
     };
+    constexpr int SG = 4 / GB;   // groups per stage: four blocks of 32
     int g = g_begin;
-    for (; g + 4 <= g_end; g += 4) stage(g, std::integral_constant<int, 4>{});
+    for (; g + SG <= g_end; g += SG) stage(g, std::integral_constant<int, SG>{});
     for (; g < g_end; ++g) stage(g, std::integral_constant<int, 1>{});
 
     // the KS partial tiles summed in wave order (deterministic); wave w < 4 then finishes the
@@ -327,22 +357,24 @@ __device__ void norm_to_operand(const PfRowArgs& a, int r, const float (&v)[PF_M
 __global__ __launch_bounds__(PF_NT) void k_pf_embed(const PfRowArgs a)
 {
     __shared__ float red[4];
+    __shared__ int ids[16];
     const int r = blockIdx.x, t = threadIdx.x, d = a.d;
     const int b = r / a.n_pos, tt = r - b * a.n_pos, p = a.pos0 + tt;
-    const int* tr = a.tok + b * a.tok_stride + a.t0 + tt;
-    const int id = min(max(tr[0], 0), a.vocab - 1);
+    const int* tr = a.tok + (b * a.tok_stride + a.t0 + tt) * a.n_tab;   // this position's ids
+    if (t < a.n_tab) ids[t] = min(max(tr[t], 0), a.tab_rows[t] - 1);
     if (t == 0) {
-        a.seq[(size_t)p * a.B + b] = id;
+        a.seq[(size_t)p * a.B + b] = min(max(tr[0], 0), a.tab_rows[0] - 1);
         // the history at a prompt position holds the id that follows it (the next prompt id)
-        if (a.t0 + tt + 1 < a.n_prompt) a.hist[(size_t)p * a.B + b] = min(max(tr[1], 0), a.vocab - 1);
+        if (a.hist && a.t0 + tt + 1 < a.n_prompt) a.hist[(size_t)p * a.B + b] = min(max(tr[a.n_tab], 0), a.tab_rows[0] - 1);
     }
+    __syncthreads();
     float v[PF_MAXV];
 #pragma unroll
     for (int i = 0; i < PF_MAXV; ++i) {
         const int k = t + i * PF_NT;
         v[i] = 0.f;
         if (k < d) {
-            v[i] = a.emb[(size_t)id * d + k];
+            for (int c = 0; c < a.n_tab; ++c) v[i] += a.tab[c][(size_t)ids[c] * d + k];
             if (a.wpe) v[i] += a.wpe[(size_t)p * d + k];
             a.x_out[(size_t)r * d + k] = v[i];
         }
@@ -535,9 +567,18 @@ hipError_t launch_pf_gemm(int fmt, int epi, const PfGemmArgs& a, hipStream_t st)
     }
 }
 
+hipError_t launch_pf_gemm_tiled(int epi, const PfGemmArgs& a, hipStream_t st)
+{
+    if (a.M <= 0 || a.W.N <= 0 || a.W.K <= 0 || a.W.K % 64 || a.lda % 8 || a.T.N != a.W.N || a.T.K != a.W.K)
+        return hipErrorInvalidValue;
+    if ((epi == PF_SWIGLU || epi == PF_QKV) && a.W.N % 2) return hipErrorInvalidValue;
+    const dim3 grid((a.W.N + PF_TILE - 1) / PF_TILE, (a.M + PF_TILE - 1) / PF_TILE);
+    return gemm_epi<PF_TILED8>(epi, a, grid, st);
+}
+
 hipError_t launch_pf_embed(const PfRowArgs& a, hipStream_t st)
 {
-    if (a.M <= 0 || a.d > core::MAX_K) return hipErrorInvalidValue;
+    if (a.M <= 0 || a.d > core::MAX_K || a.n_tab < 1 || a.n_tab > 16) return hipErrorInvalidValue;
     k_pf_embed<<<a.M, PF_NT, 0, st>>>(a);
     return hipGetLastError();
 }

@@ -25,6 +25,7 @@
 #include <string>
 
 #include "model.h"
+#include "prefill.h"
 
 namespace tsd {
 namespace {
@@ -285,6 +286,15 @@ size_t talker_plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     float* cp_nfg = (float*)P.take(4 * d);
     TiledMat cp_head[16] = {};
     for (int k = 1; k < C; ++k) cp_head[k] = take_tiled(P, Vc, d);
+    // prompt pass rows (row-major, batch rows x positions)
+    const int pf_rows = (int)std::min<long long>(PF_MAX_ROWS, ((long long)B * c->n_ctx + PF_TILE - 1) / PF_TILE * PF_TILE);
+    const int amax = std::max(d, qd);
+    float* pf_x = (float*)P.take(sizeof(float) * (size_t)pf_rows * d);
+    float* pf_q = (float*)P.take(sizeof(float) * (size_t)pf_rows * qd);
+    __half* pf_ahi = (__half*)P.take(2 * (size_t)pf_rows * amax);
+    __half* pf_alo = (__half*)P.take(2 * (size_t)pf_rows * amax);
+    __half* pf_hhi = (__half*)P.take(2 * (size_t)pf_rows * ff);
+    __half* pf_hlo = (__half*)P.take(2 * (size_t)pf_rows * ff);
     const size_t kv_layer = (size_t)B * Hk * c->n_ctx * hd;
     const size_t ckv_layer = (size_t)B * Hk * C * hd;
     __half* kc = (__half*)P.take(2 * kv_layer * c->n_layer);
@@ -306,6 +316,8 @@ size_t talker_plan(tsd_model* m, const tsd_config* c, uint8_t* base)
         m->kc = kc; m->vc = vc; m->kv_layer_elems = kv_layer;
         m->ckc = ckc; m->cvc = cvc; m->ckv_layer_elems = ckv_layer;
         m->tpp = C; m->vmax = vmax; m->qkv_rows = qd + 2 * kd;
+        m->pf_rows = pf_rows;
+        m->pf_x = pf_x; m->pf_q = pf_q; m->pf_ahi = pf_ahi; m->pf_alo = pf_alo; m->pf_hhi = pf_hhi; m->pf_hlo = pf_hlo;
     }
     return align256(P.off);
 }

@@ -1,9 +1,9 @@
-"""GPU parity of the prompt pass (tsd_prefill for GPT2/LLAMA: matrix-core products over all
-prompt rows, causal attention over the cache, the last position through the decode step)
-against the CPU oracle, through the C ABI.
+"""GPU parity of the prompt pass (tsd_prefill: matrix-core products over all prompt rows, causal
+attention over the cache, the last position through the decode step; the Talker's prompt frames
+likewise on its tiled weights) against the CPU oracle, through the C ABI.
 
 * the standalone product tsd_gemm against the oracle's fp64 mat-vec of every row, for every
-  weight format, at shapes spanning several 64 x 64 tiles with ragged row and column tails and
+  weight format, at shapes spanning several 32 x 32 tiles with ragged row and column tails and
   reduction lengths that leave a partial stage: rel <= 1e-5 per tensor, and per element within
   1e-5 of sum_k |w_k x_k| (the scale the rounding works on);
 * the cache a prompt writes (every layer, every position) against the oracle's prefill, which
@@ -13,7 +13,8 @@ against the CPU oracle, through the C ABI.
 * the causal mask ([J] §3.11): changing the ids after position i leaves every cached key and
   value at positions <= i bit for bit unchanged;
 * prompts longer than one pass (chunks of 512 rows), prompts after decoded positions, one-id
-  prompts, two batch rows, and the prompt pass against the stepwise prefill at full size.
+  prompts, two batch rows, the Talker at batch 2 and 16, and the prompt pass against the
+  stepwise prefill at full size (C3, C4, C5).
 """
 import sys
 
@@ -269,3 +270,55 @@ def test_full_size_prompt_pass(name):
         rv = rel_err(gv[0, :, :, p].cpu().numpy(), ov[0, :, :, p].view(np.float16))
         say(f"  layer 0 position {p}: k rel {rk:.2e} v rel {rv:.2e}")
         assert rk <= REL_TOL and rv <= REL_TOL
+
+
+@pytest.mark.parametrize("batch", [2, 16])
+def test_talker_prompt_pass_matches_oracle(batch):
+    """The Talker's prompt frames (each row's input the sum of its 4 code embeddings) through
+    the prompt pass on the tiled 8-bit affine weights: its cache against the oracle's prefill
+    (every layer and position) and the last frame's code-0 logits (the predictor's heads follow
+    from its own codes, compared in the frame tests)."""
+    cfg = synth.small_config("talker_cp", "aff8", batch=batch, n_ctx=64)
+    say(f"[prefill] talker batch {batch}")
+    w = synth.model_weights(cfg, 42, norm_std=0.1)
+    om = oracle.OracleModel(cfg, w)
+    gm = gpu_model(cfg, w)
+    toks = synth.prompt_tokens(cfg, 37, seed=5)
+    o_ids = om.prefill(toks)
+    g_ids = gm.prefill(dev(toks)).cpu().numpy()
+    gk, gv = gm.get_kv()
+    ok, ov = om.get_kv()
+    r = kv_rel(gk, gv, ok, ov, 37)
+    V = cfg["vocab"]
+    lo, lg = om.logits()[:, 0, :V], gm.logits().cpu().numpy()[:, 0, :V]
+    say(f"  cache rel {r:.2e}, code-0 logits rel {rel_err(lg, lo):.2e}")
+    assert r <= REL_TOL and rel_err(lg, lo) <= REL_TOL
+    for b in range(batch):
+        assert ids_agree(g_ids[b, 0], lo[b]), (b, g_ids[b, 0], o_ids[b, 0])
+    gm.close()
+
+
+def test_full_size_talker_prompt_pass():
+    """The batched frame's 170 prompt frames at batch 16 (2,720 rows in six passes of 32
+    positions) at the real Talker shape, against the frame-by-frame prefill: the Talker cache
+    per layer and the last frame's code-0 logits at rel <= 2e-3."""
+    cfg = synth.config("talker_cp_aff8")
+    n = 170
+    say(f"[prefill-full] talker_cp_aff8 {n} frames")
+    w = synth.model_weights(cfg, 42)
+    toks = synth.prompt_tokens(cfg, n, seed=42)
+    V = cfg["vocab"]
+    out = []
+    for kind in ("prefill", "prefill_stepwise"):
+        gm = gpu_model(cfg, w)
+        ids = getattr(gm, kind)(dev(toks)).cpu().numpy()
+        k, v = gm.get_kv()
+        out.append((ids, k.cpu().numpy().astype(np.float32), v.cpu().numpy().astype(np.float32),
+                    gm.logits().cpu().numpy()[:, 0, :V]))
+        gm.close()
+    (gi, gk, gv, gl), (si, sk, sv, sl) = out
+    r = max(max(rel_err(gk[l], sk[l]), rel_err(gv[l], sv[l])) for l in range(cfg["n_layer"]))
+    say(f"  against frame by frame: cache rel {r:.2e}, code-0 logits rel {rel_err(gl, sl):.2e}")
+    assert r <= REL_TOL and rel_err(gl, sl) <= REL_TOL
+    for b in range(cfg["batch"]):
+        assert ids_agree(gi[b, 0], sl[b])

@@ -376,7 +376,7 @@ def main():
             model.load_kv(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), PROMPT)
         else:
             # the prompt, once untimed (first launches of its kernels), then again from a reset
-            # model under events: the prompt pass (GPT2/LLAMA) or one frame per prompt position
+            # model under events
             model.prefill(prompt)
             stream.synchronize()
             model.reset()
@@ -479,9 +479,9 @@ def main():
     if not args.eager:
         result["prefill"] = {"positions": PROMPT, "rows": PROMPT * cfg["batch"], "ms": prefill_ms,
                              "positions_per_s": PROMPT / (prefill_ms * 1e-3),
-                             "path": ("decode step per prompt position" if frames else
-                                      "prompt pass (matrix-core products over all prompt rows, causal flash "
-                                      "attention), last position through the decode step")}
+                             "path": "prompt pass (matrix-core products over all prompt rows, causal flash "
+                                     "attention), the last position through the decode step"
+                                     + (" (the whole frame)" if frames else "")}
     result["device_state"] = dev_state.summary(t0, t1)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = (cpu_baseline_frames if frames else cpu_baseline)(with_sampler(cfg, samp), weights,

@@ -169,20 +169,22 @@ tsd_status tsd_model_create(const tsd_config* cfg, const tsd_tensor* weights, in
                             const tsd_sampling* sampling, tsd_model** out);
 
 /* Prefill ([J] §3.2: a prompt graph and a decode graph over one persistent KV cache; §3.11: the
- * prompt graph masks every key after its query's position).  GPT2/LLAMA: positions
- * n_past .. n_past + n - 2 run as one causal prompt pass (matrix-core products over all their
- * rows, chunks of up to 512 rows of batch x positions), the last position as one decode step
- * (head, sampler, history).  TALKER_CP: the decode step at every position (tsd_prefill_stepwise).
- * d_tokens is [batch][n][tokens per position] (1, or n_codebooks for TALKER_CP); d_next (may be
- * NULL) receives [batch][tokens per step], the ids sampled after the last prompt position.  The
- * token history (tsd_get_tokens) at a prompt position before the last holds the next prompt id.
- * The cached keys and values agree with tsd_prefill_stepwise's to fp32 rounding (the sums run
- * in another order), not bit for bit.  TSD_ERR_CONTEXT_FULL if n_past + n > n_ctx.  Tokens are
+ * prompt graph masks every key after its query's position).  Positions n_past .. n_past + n - 2
+ * run as one causal prompt pass (matrix-core products over all their rows, chunks of up to 512
+ * rows of batch x positions; for TALKER_CP the Talker only, on the sums of each frame's code
+ * embeddings), the last position as one decode step (head, sampler, history; for TALKER_CP the
+ * whole frame).  d_tokens is [batch][n][tokens per position] (1, or n_codebooks for TALKER_CP);
+ * d_next (may be NULL) receives [batch][tokens per step], the ids sampled after the last prompt
+ * position.  The token history (tsd_get_tokens) at a GPT2/LLAMA prompt position before the last
+ * holds the next prompt id (TALKER_CP prompt frames leave it alone).  The cached keys and values
+ * agree with tsd_prefill_stepwise's to fp32 rounding (the sums run in another order), not bit
+ * for bit.  TSD_ERR_CONTEXT_FULL if n_past + n > n_ctx.  Tokens are
  * not range-checked on the device: an id outside its vocabulary is clamped into range. */
 tsd_status tsd_prefill(tsd_model* m, const int32_t* d_tokens, int n, int32_t* d_next);
 /* Prefill by the decode step at every prompt position (identical kernels, so the cache matches
- * what decoding the prompt one id at a time writes, bit for bit); arguments as tsd_prefill.
- * The history at a prompt position holds the id the step sampled there. */
+ * what decoding the prompt one id at a time writes, bit for bit; TALKER_CP prompt frames run the
+ * Talker only); arguments as tsd_prefill.  The GPT2/LLAMA history at a prompt position holds
+ * the id the step sampled there. */
 tsd_status tsd_prefill_stepwise(tsd_model* m, const int32_t* d_tokens, int n, int32_t* d_next);
 
 /* One decode step (one frame for TALKER_CP) at position n_past: replays the captured graph.

@@ -527,6 +527,12 @@ tsd_status init_state(tsd_model* m)
     HIP_TRY(m, launch_fill_i32(m->hist, 0, c.n_ctx * c.batch * m->tpp, st), "init");
     HIP_TRY(m, launch_fill_i32(m->seq, -1, c.n_ctx * c.batch, st), "init");
     HIP_TRY(m, launch_fill_f32(m->logits, 0.f, (size_t)c.batch * m->tpp * m->vmax, st), "init");
+    // the prompt pass's operands: rows past a prompt's last row are read (never stored), keep them finite
+    const size_t amax = (size_t)std::max(c.d_model, c.n_head * c.head_dim);
+    for (__half* a : {m->pf_ahi, m->pf_alo})
+        HIP_TRY(m, launch_fill_u32((unsigned*)a, 0u, (int)(m->pf_rows * amax / 2), st), "init");
+    for (__half* a : {m->pf_hhi, m->pf_hlo})
+        HIP_TRY(m, launch_fill_u32((unsigned*)a, 0u, (int)((size_t)m->pf_rows * c.d_ff / 2), st), "init");
     // RoPE table in fp64 on the host: angle = pos * theta^(-2i/hd)
     const int half = c.head_dim / 2;
     std::vector<float2> tab((size_t)m->rope_rows * half);
@@ -571,7 +577,7 @@ hipError_t pf_enqueue(tsd_model* m, const int32_t* d_tokens, int n_prompt, int t
     const tsd_config& c = m->c;
     const int d = c.d_model, H = c.n_head, Hk = c.n_kv_head, hd = c.head_dim, ff = c.d_ff, B = c.batch, f = c.wfmt;
     const bool gpt2 = c.arch == TSD_ARCH_GPT2, talker = c.arch == TSD_ARCH_TALKER_CP;
-    const int M = B * np, qd = H * hd, amax = std::max(d, qd);
+    const int M = B * np, qd = H * hd;
     const int pos0 = m->n_past;
     PfRowArgs ra{};
     ra.M = M; ra.d = d; ra.n_pos = np; ra.pos0 = pos0;
@@ -584,7 +590,7 @@ hipError_t pf_enqueue(tsd_model* m, const int32_t* d_tokens, int n_prompt, int t
     ra.wpe = m->wpe; ra.seq = m->seq; ra.B = B;
     ra.hist = talker ? nullptr : m->hist;   // the Talker's prompt frames leave their history alone, as its frames do
     ra.x = m->pf_x; ra.x_out = m->pf_x; ra.eps = c.norm_eps;
-    ra.ahi = m->pf_ahi; ra.alo = m->pf_alo; ra.lda = amax;
+    ra.ahi = m->pf_ahi; ra.alo = m->pf_alo;
     PfGemmArgs ga{};
     ga.M = M;
     ga.n_ctx = c.n_ctx; ga.n_pos = np; ga.pos0 = pos0;
@@ -592,7 +598,7 @@ hipError_t pf_enqueue(tsd_model* m, const int32_t* d_tokens, int n_prompt, int t
     PfAttnArgs aa{};
     aa.q = m->pf_q; aa.ldq = qd; aa.kv_row = ga.kv_row;
     aa.M = M; aa.H = H; aa.Hkv = Hk; aa.hd = hd; aa.n_ctx = c.n_ctx; aa.n_pos = np; aa.pos0 = pos0;
-    aa.ohi = m->pf_ahi; aa.olo = m->pf_alo; aa.ldo = amax;
+    aa.ohi = m->pf_ahi; aa.olo = m->pf_alo; aa.ldo = qd;
     // one product: the packed matrix (GPT2/LLAMA) or the tiled one (Talker)
     auto gemm = [&](PfGemmArgs g, int epi, const PackedMat* P, const TiledMat* T) {
         if (T) {
@@ -615,24 +621,24 @@ hipError_t pf_enqueue(tsd_model* m, const int32_t* d_tokens, int n_prompt, int t
         e = l == 0 ? launch_pf_embed(ra, st) : launch_pf_norm(ra, st);
         // Q/K/V: queries (after RoPE) to pf_q, keys and values into the cache
         PfGemmArgs q = ga;
-        q.ahi = m->pf_ahi; q.alo = m->pf_alo; q.lda = amax; q.bias = talker ? nullptr : w->bqkv;
+        q.ahi = m->pf_ahi; q.alo = m->pf_alo; q.bias = talker ? nullptr : w->bqkv;
         q.q = m->pf_q; q.ldq = qd; q.qrows = qd; q.krows = Hk * hd; q.hd = hd; q.rope = gpt2 ? 0 : 1;
         q.rope_tab = m->rope; q.kc = kc; q.vc = vc;
         if (e == hipSuccess) e = gemm(q, PF_QKV, talker ? nullptr : &w->qkv, talker ? &tw->qkv : nullptr);
         aa.kc = kc; aa.vc = vc;
         if (e == hipSuccess) e = launch_pf_attention(aa, st);
         PfGemmArgs o = ga;
-        o.ahi = m->pf_ahi; o.alo = m->pf_alo; o.lda = amax; o.bias = talker ? nullptr : w->bo; o.y = m->pf_x; o.ldy = d;
+        o.ahi = m->pf_ahi; o.alo = m->pf_alo; o.bias = talker ? nullptr : w->bo; o.y = m->pf_x; o.ldy = d;
         if (e == hipSuccess) e = gemm(o, PF_RESID, talker ? nullptr : &w->o, talker ? &tw->o : nullptr);
         ra.g = talker ? tw->n2g : w->n2g;
         ra.bn = talker ? nullptr : w->n2b;
         if (e == hipSuccess) e = launch_pf_norm(ra, st);
         PfGemmArgs u = ga;
-        u.ahi = m->pf_ahi; u.alo = m->pf_alo; u.lda = amax; u.bias = talker ? nullptr : w->bfc;
+        u.ahi = m->pf_ahi; u.alo = m->pf_alo; u.bias = talker ? nullptr : w->bfc;
         u.ohi = m->pf_hhi; u.olo = m->pf_hlo; u.ldo = ff;
         if (e == hipSuccess) e = gemm(u, gpt2 ? PF_GELU : PF_SWIGLU, talker ? nullptr : &w->fc, talker ? &tw->fc : nullptr);
         PfGemmArgs dn = ga;
-        dn.ahi = m->pf_hhi; dn.alo = m->pf_hlo; dn.lda = ff; dn.bias = talker ? nullptr : w->bdown; dn.y = m->pf_x; dn.ldy = d;
+        dn.ahi = m->pf_hhi; dn.alo = m->pf_hlo; dn.bias = talker ? nullptr : w->bdown; dn.y = m->pf_x; dn.ldy = d;
         if (e == hipSuccess) e = gemm(dn, PF_RESID, talker ? nullptr : &w->down, talker ? &tw->down : nullptr);
     }
     return e;
@@ -1029,7 +1035,7 @@ tsd_status tsd_time_kernel(tsd_model* m, int kind, int n_steps, float* avg_us, i
 tsd_status tsd_gemm_scratch_bytes(int M, int K, size_t* out)
 {
     if (!out || M <= 0 || K <= 0 || K % 32) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "bad shape");
-    *out = 2 * align256((size_t)M * K * 2);   // the operand rows, fp16 hi then lo
+    *out = 2 * align256((size_t)((M + 31) / 32 * 32) * K * 2);   // the operand rows (whole 32-row tiles), fp16 hi then lo
     return TSD_OK;
 }
 
@@ -1054,7 +1060,6 @@ tsd_status tsd_gemm(int wfmt, const void* d_packed, int N, int K, int M, const f
     a.M = M;
     a.ahi = hi;
     a.alo = lo;
-    a.lda = K;
     a.bias = d_bias;
     a.y = d_y;
     a.ldy = N;

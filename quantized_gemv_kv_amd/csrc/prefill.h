@@ -5,7 +5,10 @@
 // position).  With n rows every weight byte feeds n multiply-adds, so the linears are matrix
 // products on the matrix cores; the activations of all rows sit in row-major buffers:
 //   X  [rows][d]  fp32 residual stream
-//   A  [rows][K]  fp16 hi / lo operand of the next product (hi = fp16(x), lo = fp16(x - hi))
+//   A  rows x K   fp16 hi / lo operand of the next product (hi = fp16(x), lo = fp16(x - hi)), in
+//                 fragment order: per 16-row tile and 32-wide block of K, 1 KB in MFMA lane order
+//                 (element (r, k) at (((r/16 * K/32 + k/32) * 4 + (k/8) % 4) * 16 + r % 16) * 8 + k % 8),
+//                 in whole 32-row tiles
 //   Q  [rows][H hd] fp32 queries after RoPE
 // Row r is batch row b = r / n_pos, position pos0 + r % n_pos.
 #pragma once
@@ -32,13 +35,12 @@ struct PfGemmArgs {
     PackedMat W;                 // packed GEMV layout, N rows of K (W.N / W.K give the shape for either source)
     TiledMat T;                  // tiled 8-bit affine layout (launch_pf_gemm_tiled)
     int M;                       // operand rows
-    const __half* ahi;           // [M][lda] operand
+    const __half* ahi;           // operand, fragment order with W.K columns
     const __half* alo;
-    int lda;
     const float* bias;           // [N] or null
     float* y;                    // PF_STORE / PF_RESID: [M][ldy] fp32
     int ldy;
-    __half* ohi;                 // PF_GELU / PF_SWIGLU: next operand [M][ldo]
+    __half* ohi;                 // PF_GELU / PF_SWIGLU: next operand, fragment order with ldo columns
     __half* olo;
     int ldo;
     // PF_QKV
@@ -72,8 +74,7 @@ struct PfRowArgs {
     const float* g;              // gain
     const float* bn;             // LayerNorm bias (null: RMSNorm)
     float eps;
-    __half *ahi, *alo;           // operand [M][lda]
-    int lda;
+    __half *ahi, *alo;           // operand, fragment order with d columns
 };
 
 struct PfAttnArgs {
@@ -82,7 +83,7 @@ struct PfAttnArgs {
     const __half *kc, *vc;       // layer cache [B][Hkv][n_ctx][hd]
     long long kv_row;
     int M, H, Hkv, hd, n_ctx, n_pos, pos0;
-    __half *ohi, *olo;           // operand [M][ldo], head h at column h hd
+    __half *ohi, *olo;           // operand, fragment order with ldo columns (head h at column h hd)
     int ldo;
 };
 
@@ -94,7 +95,8 @@ hipError_t launch_pf_gemm_tiled(int epi, const PfGemmArgs& a, hipStream_t st);
 // X rows from the embeddings (and the history words), then the first norm into the operand
 hipError_t launch_pf_embed(const PfRowArgs& a, hipStream_t st);
 hipError_t launch_pf_norm(const PfRowArgs& a, hipStream_t st);
-// fp32 rows x [M][K] -> operand hi/lo (standalone product)
+// fp32 rows x [M][K] -> operand hi/lo in fragment order, rows up to the next multiple of 32
+// zero-filled (standalone product)
 hipError_t launch_pf_split(const float* x, int M, int K, __half* hi, __half* lo, hipStream_t st);
 hipError_t launch_pf_attention(const PfAttnArgs& a, hipStream_t st);
 

@@ -40,6 +40,15 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// The operand of a product lives in fragment order: for each 16-row tile and 32-wide block of
+// K, 1 KB in lane order (lane (j, c) holds row 16 t + c, K positions 32 blk + 8 j .. + 7), so one
+// load instruction of a wave reads 1 KB of consecutive bytes.  Element (r, k) of an operand with
+// K columns:
+__device__ __forceinline__ size_t fl_index(int r, int k, int K)
+{
+    return ((((size_t)(r >> 4) * (K >> 5) + (k >> 5)) * 4 + ((k >> 3) & 3)) * 16 + (r & 15)) * 8 + (k & 7);
+}
+
 __device__ __forceinline__ void put_hilo(__half* hi, __half* lo, size_t idx, float y)
 {
     const _Float16 h = (_Float16)y;
@@ -118,9 +127,10 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(const PfGemmArgs a)
     const TSD_GLOBAL half8* al[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-        const int r = min(m0 + 16 * s + c, M - 1);   // rows past M repeat row M-1 (never stored)
-        ah[s] = (const TSD_GLOBAL half8*)(glb(a.ahi) + (size_t)r * a.lda + 8 * j);
-        al[s] = (const TSD_GLOBAL half8*)(glb(a.alo) + (size_t)r * a.lda + 8 * j);
+        // row tile (m0 + 16 s) / 16; the operand holds whole 32-row tiles (rows past M never stored)
+        const size_t t0 = (size_t)((m0 + 16 * s) >> 4) * (K >> 5) * 64 + lane;
+        ah[s] = (const TSD_GLOBAL half8*)glb(a.ahi) + t0;
+        al[s] = (const TSD_GLOBAL half8*)glb(a.alo) + t0;
     }
     const TSD_GLOBAL uint8_t* wp[2];
     const TSD_GLOBAL _Float16* sp[2];
@@ -166,8 +176,8 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(const PfGemmArgs a)
             const int blk = g0 * GB + b;
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                xh[b][s] = ah[s][blk * 4];   // 32 halves = 4 half8 per block
-                xl[b][s] = al[s][blk * 4];
+                xh[b][s] = ah[s][(size_t)blk * 64];   // 1 KB (64 half8) per block of a row tile
+                xl[b][s] = al[s][(size_t)blk * 64];
             }
             if constexpr (F != PF_TILED8) {
 #pragma unroll
@@ -282,9 +292,9 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(const PfGemmArgs a)
                 } else if constexpr (EPI == PF_RESID) {
                     a.y[(size_t)r * a.ldy + n] += v;
                 } else if constexpr (EPI == PF_GELU) {
-                    put_hilo(a.ohi, a.olo, (size_t)r * a.ldo + n, core::gelu_tanh(v));
+                    put_hilo(a.ohi, a.olo, fl_index(r, n, a.ldo), core::gelu_tanh(v));
                 } else if constexpr (EPI == PF_SWIGLU) {
-                    if ((n & 1) == 0) put_hilo(a.ohi, a.olo, (size_t)r * a.ldo + (n >> 1), core::silu(v) * partner);
+                    if ((n & 1) == 0) put_hilo(a.ohi, a.olo, fl_index(r, n >> 1, a.ldo), core::silu(v) * partner);
                 } else {   // PF_QKV
                     const int b = r / a.n_pos, p = a.pos0 + (r - b * a.n_pos);
                     if (n < a.qrows + a.krows) {
@@ -349,7 +359,7 @@ __device__ void norm_to_operand(const PfRowArgs& a, int r, const float (&v)[PF_M
         if (k < d) {
             float y = (v[i] - mean) * rs * a.g[k];
             if (a.bn) y += a.bn[k];
-            put_hilo(a.ahi, a.alo, (size_t)r * a.lda + k, y);
+            put_hilo(a.ahi, a.alo, fl_index(r, k, d), y);
         }
     }
 }
@@ -395,10 +405,13 @@ __global__ __launch_bounds__(PF_NT) void k_pf_norm(const PfRowArgs a)
     norm_to_operand(a, r, v, red);
 }
 
-__global__ __launch_bounds__(256) void k_pf_split(const float* __restrict__ x, size_t n, __half* hi, __half* lo)
+// rows [M, Mpad) of the last tile are written as zeros
+__global__ __launch_bounds__(256) void k_pf_split(const float* __restrict__ x, int M, int Mpad, int K, __half* hi, __half* lo)
 {
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) put_hilo(hi, lo, i, x[i]);
+    if (i >= (size_t)Mpad * K) return;
+    const int r = (int)(i / K), k = (int)(i - (size_t)r * K);
+    put_hilo(hi, lo, fl_index(r, k, K), r < M ? x[i] : 0.f);
 }
 
 // ---- causal attention over the cache (matrix cores) -------------------------------------------
@@ -516,11 +529,10 @@ __global__ __launch_bounds__(64) void k_pf_fattn(const PfAttnArgs a)
     }
     if (t0 + c >= a.n_pos) return;
     const float il = 1.0f / l;
-    const size_t base = (size_t)r * a.ldo + h * HD;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) put_hilo(a.ohi, a.olo, base + (4 * j + i) * DT + dt, o[dt][i] * il);
+        for (int dt = 0; dt < DT; ++dt) put_hilo(a.ohi, a.olo, fl_index(r, h * HD + (4 * j + i) * DT + dt, a.ldo), o[dt][i] * il);
 }
 
 template <int F, int KS>
@@ -553,7 +565,7 @@ bool pf_gemm_ok(int fmt, int K)
 
 hipError_t launch_pf_gemm(int fmt, int epi, const PfGemmArgs& a, hipStream_t st)
 {
-    if (!pf_gemm_ok(fmt, a.W.K) || a.M <= 0 || a.W.N <= 0 || a.lda % 8) return hipErrorInvalidValue;
+    if (!pf_gemm_ok(fmt, a.W.K) || a.M <= 0 || a.W.N <= 0) return hipErrorInvalidValue;
     if ((epi == PF_SWIGLU || epi == PF_QKV) && a.W.N % 2) return hipErrorInvalidValue;
     const dim3 grid((a.W.N + PF_TILE - 1) / PF_TILE, (a.M + PF_TILE - 1) / PF_TILE);
     switch (fmt) {
@@ -569,7 +581,7 @@ hipError_t launch_pf_gemm(int fmt, int epi, const PfGemmArgs& a, hipStream_t st)
 
 hipError_t launch_pf_gemm_tiled(int epi, const PfGemmArgs& a, hipStream_t st)
 {
-    if (a.M <= 0 || a.W.N <= 0 || a.W.K <= 0 || a.W.K % 64 || a.lda % 8 || a.T.N != a.W.N || a.T.K != a.W.K)
+    if (a.M <= 0 || a.W.N <= 0 || a.W.K <= 0 || a.W.K % 64 || a.T.N != a.W.N || a.T.K != a.W.K)
         return hipErrorInvalidValue;
     if ((epi == PF_SWIGLU || epi == PF_QKV) && a.W.N % 2) return hipErrorInvalidValue;
     const dim3 grid((a.W.N + PF_TILE - 1) / PF_TILE, (a.M + PF_TILE - 1) / PF_TILE);
@@ -592,9 +604,10 @@ hipError_t launch_pf_norm(const PfRowArgs& a, hipStream_t st)
 
 hipError_t launch_pf_split(const float* x, int M, int K, __half* hi, __half* lo, hipStream_t st)
 {
-    const size_t n = (size_t)M * K;
-    if (!n) return hipSuccess;
-    k_pf_split<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(x, n, hi, lo);
+    if (M <= 0 || K <= 0 || K % 32) return hipErrorInvalidValue;
+    const int Mpad = (M + PF_TILE - 1) / PF_TILE * PF_TILE;
+    const size_t n = (size_t)Mpad * K;
+    k_pf_split<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(x, M, Mpad, K, hi, lo);
     return hipGetLastError();
 }
 

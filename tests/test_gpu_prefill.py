@@ -85,8 +85,9 @@ def test_gemm_rejects_bad_arguments():
     scratch = torch.zeros(binding.tsd_gemm_scratch_bytes(4, 128), dtype=torch.uint8, device="cuda")
     x = torch.zeros((4, 128), dtype=torch.float32, device="cuda")
     y = torch.zeros((4, 64), dtype=torch.float32, device="cuda")
+    # K not a block multiple / no rows / K % 64 / scratch too small (it holds one 32-row tile)
     for args in [("q4_0", packed, 64, 100, 4), ("q4_0", packed, 64, 128, 0), ("aff8", packed, 64, 96, 4),
-                 ("q4_0", packed, 64, 128, 5)]:   # K not a block multiple / no rows / K % 64 / scratch too small
+                 ("q4_0", packed, 64, 128, 33)]:
         with pytest.raises(TsdError) as e:
             binding.tsd_gemm(args[0], args[1], args[2], args[3], args[4], x, None, y, scratch)
         assert e.value.status == 1

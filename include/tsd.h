@@ -86,7 +86,8 @@ typedef enum { TSD_LAUNCH_PERSISTENT = 0, TSD_LAUNCH_PER_OPERATOR = 1 } tsd_laun
  *          then a LLAMA-shaped predictor of cp_n_layer (same widths) running n_codebooks-1
  *          sequential passes.  One step is one frame of n_codebooks codes.
  * batch: GPT2/LLAMA 1 or 2 (two rows read every weight once per step: two streams, or a
- * guided pair, see tsd_sampling.cfg; batch 2 runs PER_OPERATOR); TALKER_CP 1..16.
+ * guided pair, see tsd_sampling.cfg; batch 2 runs PERSISTENT for the GPT-2-Medium Q4_0 and
+ * Llama-520M Q8_0 shapes and the test shapes, else PER_OPERATOR); TALKER_CP 1..16.
  * norm_eps is used by every LayerNorm/RMSNorm. */
 typedef struct {
     int32_t arch, wfmt;

@@ -139,7 +139,7 @@ struct StepLayer {
     PackedMat qkv, o, fc, down;               // fc: FC (GPT-2) or interleaved gate/up (Llama)
     const float *n1g, *n1b, *n2g, *n2b;       // norm gains / LayerNorm biases (null for RMSNorm)
     const float *bqkv, *bo, *bfc, *bdown;     // linear biases (null without)
-    __half *kc, *vc;                          // this layer's cache [Hkv][n_ctx][hd]
+    __half *kc, *vc;                          // this layer's cache [B][Hkv][n_ctx][hd]
 };
 // the sampler chain's parameters (sampler.h): temperature, k largest, nucleus, min-p, repetition
 // penalty, and which of the two orders runs
@@ -164,24 +164,31 @@ struct StepArgs {
     const float *nfg, *nfb;                   // final norm
     PackedMat head;
     const float2* rope;                       // [n_ctx][hd/2] (cos, sin), Llama
-    int *pos, *tok, *hist;                    // step state (read at launch start, advanced at its end)
-    int* seq;                                 // [n_ctx] the token consumed at each position
+    int *pos, *tok, *hist;                    // step state (read at launch start, advanced at its end);
+                                              // tok [B], hist [n_ctx][B]
+    int* seq;                                 // [n_ctx][B] the token consumed at each position
     uint32_t* ctr;                            // launches completed: the epoch base
     uint32_t* abort_word;                     // sticky: a wait gave up
-    float* logits;                            // [vocab]
+    float* logits;                            // [B][vocab]
     // exchange words: QKV out, attention partials [H][max_split][hd+2], attention-block output
-    // (residual stream), MLP hidden, layer output (residual stream), per-workgroup argmax keys
+    // (residual stream), MLP hidden, layer output (residual stream), per-workgroup argmax keys;
+    // batch row b's words of each buffer start b * its row stride (xs_*) after row 0's
     uint64_t *x_qkv, *x_part, *x_attn, *x_h, *x_out, *x_best;
+    long long xs_qkv, xs_part, xs_d, xs_h, xs_best, xs_logit;   // row strides in words (xs_d: x_attn, x_out)
+    long long kv_row;                         // elements between batch rows of a layer's cache
+    int cfg;                                  // two rows guided: one draw from l0 + cfg_weight (l0 - l1)
+    float cfg_weight;
     long long spin_limit;                     // ticks of the 100 MHz clock a wait may take
     // sampler: mode 0 the greedy argmax of the head's per-workgroup keys, 1 the chain's draw on
     // workgroup 0 (the head then also publishes its logits as exchange words)
     int samp_mode;
     SampChain chain;
     unsigned long long seed;
-    uint64_t* x_logit;                        // [vocab] exchange words of the logits (draw)
+    uint64_t* x_logit;                        // [B][vocab] exchange words of the logits (draw; guided: row 0
+                                              // holds the combined logits)
 };
-// the step kernel for a shape, or null when the shape has no instantiation
-const void* step_kernel_for(int fmt, int arch_llama, int d, int h, int hk, int hd, int ff, int vocab);
+// the step kernel for a shape and batch (1 or 2), or null when the shape has no instantiation
+const void* step_kernel_for(int fmt, int arch_llama, int d, int h, int hk, int hd, int ff, int vocab, int batch);
 // d_args: the arguments in device memory (read by every phase)
 hipError_t launch_step(const void* kernel, const StepArgs* d_args, int n_wg, hipStream_t st);
 

@@ -178,9 +178,13 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     uint32_t* ctl = (uint32_t*)P.take(sizeof(uint32_t) * 64);
     StepArgs* d_sa = (StepArgs*)P.take(sizeof(StepArgs));
     const size_t n_part = (size_t)H * attn_max_split(c->n_ctx) * (hd + 2);
+    // one batch row's words of each buffer (rounded to 32 words); a buffer holds B rows
     const size_t xw[7] = {(size_t)qkv_rows, n_part, (size_t)d, (size_t)ff, (size_t)d, 2 * (size_t)MAX_STEP_WG, (size_t)vmax};
-    size_t xtot = 0;
-    for (size_t n : xw) xtot += (n + 31) & ~(size_t)31;
+    size_t xrs[7], xtot = 0;
+    for (int i = 0; i < 7; ++i) {
+        xrs[i] = (xw[i] + 31) & ~(size_t)31;
+        xtot += xrs[i] * B;
+    }
     uint64_t* xbuf = (uint64_t*)P.take(sizeof(uint64_t) * xtot);
     // prompt pass rows
     const int pf_rows = (int)std::min<long long>(PF_MAX_ROWS, ((long long)B * c->n_ctx + PF_TILE - 1) / PF_TILE * PF_TILE);
@@ -207,11 +211,13 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
         uint64_t* q = xbuf;
         for (int i = 0; i < 7; ++i) {
             xp[i] = q;
-            q += (xw[i] + 31) & ~(size_t)31;
+            q += xrs[i] * B;
         }
         StepArgs& a = m->sa;
         a.x_qkv = xp[0]; a.x_part = xp[1]; a.x_attn = xp[2]; a.x_h = xp[3]; a.x_out = xp[4]; a.x_best = xp[5];
         a.x_logit = xp[6];
+        a.xs_qkv = (long long)xrs[0]; a.xs_part = (long long)xrs[1]; a.xs_d = (long long)xrs[2]; a.xs_h = (long long)xrs[3];
+        a.xs_best = (long long)xrs[5]; a.xs_logit = (long long)xrs[6];
     }
     return align256(P.off);
 }
@@ -447,9 +453,8 @@ tsd_status setup_step(tsd_model* m)
     if (c.launch_mode == TSD_LAUNCH_PER_OPERATOR) return TSD_OK;
     if (c.launch_mode != TSD_LAUNCH_PERSISTENT) return fail(m, TSD_ERR_INVALID_ARGUMENT, "unknown launch_mode");
     if (c.arch == TSD_ARCH_TALKER_CP) return TSD_OK;   // the frame runs one launch per operator
-    if (c.batch != 1) return TSD_OK;                    // two rows run one launch per operator
     m->step_fn = step_kernel_for(c.wfmt, c.arch == TSD_ARCH_LLAMA, c.d_model, c.n_head, c.n_kv_head, c.head_dim, c.d_ff,
-                                 c.vocab);
+                                 c.vocab, c.batch);
     if (!m->step_fn) return TSD_OK;   // this shape runs one launch per operator
     int dev = 0, n_cu = 0, per_cu = 0;
     HIP_TRY(m, hipGetDevice(&dev), "device");
@@ -501,6 +506,9 @@ tsd_status setup_step(tsd_model* m)
     a.samp_mode = m->draw;
     a.chain = m->chain;
     a.seed = m->samp.seed;
+    a.kv_row = (long long)c.n_kv_head * c.n_ctx * c.head_dim;
+    a.cfg = c.batch == 2 && m->samp.cfg ? 1 : 0;
+    a.cfg_weight = m->samp.cfg_weight;
     const uint64_t nph = 5ull * c.n_layer + 1ull;
     m->max_launches = (0xFFFFFFF0ull - nph) / nph;
     return TSD_OK;

@@ -1,4 +1,4 @@
-// step.hip — the whole batch-1 decode step as one persistent launch.
+// step.hip — the whole decode step (batch 1, or a pair of rows) as one persistent launch.
 //
 // What it computes is the step of the per-operator kernels (gemv.hip, attention.hip): for each
 // layer norm -> fused QKV (+bias | +RoPE) -> K/V append -> split-KV attention -> output
@@ -51,9 +51,10 @@ enum { OUT_QKV = 0, OUT_QKV_ROPE = 1, OUT_RESID = 2, OUT_GELU = 3, OUT_SWIGLU = 
 constexpr int slices_for(int fmt_e, int K) { return K / fmt_e > 64 ? K / fmt_e / 64 : 1; }
 
 // the model shape
-template <int F_, int A_, int D_, int H_, int HK_, int HD_, int FF_, int V_>
+template <int F_, int A_, int D_, int H_, int HK_, int HD_, int FF_, int V_, int B_>
 struct Shape {
     static constexpr int F = F_, ARCH = A_, D = D_, H = H_, HK = HK_, HD = HD_, FF = FF_, V = V_;
+    static constexpr int B = B_;   // batch rows: every weight is read once for all of them
     static constexpr bool GPT2 = A_ == A_GPT2;
     static constexpr int QD = H * HD, KD = HK * HD, QKV = QD + 2 * KD;
     static constexpr int FCN = GPT2 ? FF : 2 * FF;   // FC rows (gate/up interleaved for Llama)
@@ -89,34 +90,56 @@ struct Geo {
 };
 
 struct Smem {
-    float* xl;       // [MAX_K] phase input, swizzled for the weight format
-    float* red;      // [2 * NWAVE]
-    float* ml;       // [H * SG * 2] attention (m, l) of a group of chunks
+    float* xl;       // [B][MAX_K] phase input, swizzled for the weight format
+    float* red;      // [4 * NWAVE]
+    float* ml;       // [B * H * SG * 2] attention (m, l) of a group of chunks
     int* abort;      // a wait of this workgroup timed out
 };
 
 struct Ctx {
-    int pos, tok, n_keys, S;
+    int pos, tok[2], n_keys, S;   // tok: each batch row's input token
     long long limit;
 };
 
 // ---- phase input -----------------------------------------------------------------------------
-// x[0..K) into LDS at the swizzled place of format F.  Thread t owns elements k = t + NT*j,
-// j < ceil(K / NT); every load is issued unconditionally (an element past K, when K is not a
-// multiple of NT, reads element K-1 and is discarded).
-//   IN_XCHG     exchange words src[k] (epoch ep)
-//   IN_NORM     the same, then LayerNorm (gain g, bias bt) or RMSNorm (gain g)
-//   IN_EMB_NORM the embedding row of the input token (+ the learned position row), then the norm
-//   IN_ATTN     the attention output, merged from the per-chunk partials src[(h*max_split+s)*(hd+2)]
-template <class C, int F, int K, int IN, bool LN>
-__device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const uint64_t* src, const uint32_t ep,
-                                         const float* g, const float* bt, Smem& sm)
+// x[0..K) of each batch row b < C::B into LDS (row b at xl + b * MAX_K) at the swizzled place of
+// format F.  Thread t owns elements k = t + NT*j, j < ceil(K / NT); every load is issued
+// unconditionally (an element past K, when K is not a multiple of NT, reads element K-1 and is
+// discarded), and the words of all rows are polled together (one round trip for the batch).
+//   IN_XCHG     exchange words src[b * xs + k] (epoch ep)
+//   IN_NORM     the same, then LayerNorm (gain g, bias bt) or RMSNorm (gain g) per row
+//   IN_EMB_NORM the embedding row of the row's input token (+ the learned position row), then the norm
+//   IN_ATTN     the attention output, merged from the per-chunk partials src[b * xs + (h*max_split+s)*(hd+2)]
+template <int NS>
+__device__ __forceinline__ void block_sums(float (&v)[NS], float* red)   // NS sums, one pair of barriers
 {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) v[i] = wave_sum(v[i]);
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) red[NS * (threadIdx.x >> 6) + i] = v[i];
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        float r = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWAVE; ++w) r += red[NS * w + i];
+        v[i] = r;
+    }
+    lds_barrier();
+}
+
+template <class C, int F, int K, int IN, bool LN>
+__device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const uint64_t* src, const long long xs,
+                                         const uint32_t ep, const float* g, const float* bt, Smem& sm)
+{
+    constexpr int B = C::B;
     constexpr int E = FmtT<F>::E, LPR = K / E, J = (K + NT - 1) / NT;
     constexpr bool NORM = IN == IN_NORM || IN == IN_EMB_NORM;
     const int t = threadIdx.x;
     auto elem = [&](int j) { return K % NT == 0 ? t + NT * j : min(t + NT * j, K - 1); };
-    float v[J], gg[J], bb[J];
+    float v[B][J], gg[J], bb[J];
     bool ok = true;
     if constexpr (NORM) {
 #pragma unroll
@@ -125,39 +148,48 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
             bb[j] = LN ? glb(bt)[elem(j)] : 0.f;
         }
     }
-    float x0 = 0.f;   // LayerNorm shift (see finish_x in the GEMV core)
-    if constexpr (IN == IN_EMB_NORM) {
-        const float* er = a.emb + (size_t)cx.tok * K;
-        const float* pr = a.wpe + (size_t)cx.pos * K;
+    float x0[B];   // LayerNorm shift per row (see finish_x in the GEMV core)
 #pragma unroll
-        for (int j = 0; j < J; ++j) v[j] = glb(er)[elem(j)] + (C::GPT2 ? glb(pr)[elem(j)] : 0.f);
+    for (int b = 0; b < B; ++b) x0[b] = 0.f;
+    if constexpr (IN == IN_EMB_NORM) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const float* er = a.emb + (size_t)cx.tok[b] * K;
+            const float* pr = a.wpe + (size_t)cx.pos * K;
+#pragma unroll
+            for (int j = 0; j < J; ++j) v[b][j] = glb(er)[elem(j)] + (C::GPT2 ? glb(pr)[elem(j)] : 0.f);
+        }
     } else if constexpr (IN == IN_ATTN) {
         // element k = h*HD + i; chunk s of head h published (o[0..HD), m, l) in the log2 domain
         constexpr int HD = C::HD, H = K / HD, PS = HD + 2;
-        static_assert(H * SG * 2 <= NT, "one (m, l) word per thread");
-        float Mr[J], Lr[J], Or[J];
+        static_assert(B * H * SG * 2 <= NT, "one (m, l) word per thread");
+        float Mr[B][J], Lr[B][J], Or[B][J];
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            Mr[j] = -INFINITY;
-            Lr[j] = 0.f;
-            Or[j] = 0.f;
-        }
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                Mr[b][j] = -INFINITY;
+                Lr[b][j] = 0.f;
+                Or[b][j] = 0.f;
+            }
         for (int s0 = 0; s0 < cx.S; s0 += SG) {
             const int ns = min(SG, cx.S - s0);
-            // word 0: this thread's (m or l) word of the group (table [h][u][m, l]);
-            // word 1 + j*SG + u: chunk s0+u's output for element j (chunks past the context
-            // re-read the group's last chunk and are not used)
+            // word 0: this thread's (m or l) word of the group (table [b][h][u][m, l]);
+            // word 1 + (b*J + j)*SG + u: row b's chunk s0+u output for element j (chunks past the
+            // context re-read the group's last chunk and are not used)
             const int nml = H * ns * 2;
-            const int tm = min(t, nml - 1);
-            const int mh = tm / (2 * ns), mr = tm - mh * 2 * ns;
-            const uint64_t* mp = src + ((size_t)mh * a.max_split + s0 + (mr >> 1)) * PS + HD + (mr & 1);
+            const int tm = min(t, B * nml - 1);
+            const int mb = tm / nml, tr = tm - mb * nml;
+            const int mh = tr / (2 * ns), mr = tr - mh * 2 * ns;
+            const uint64_t* mp = src + mb * xs + ((size_t)mh * a.max_split + s0 + (mr >> 1)) * PS + HD + (mr & 1);
             auto addr = [&](int q) -> const uint64_t* {
                 if (q == 0) return mp;
-                const int j = (q - 1) / SG, u = (q - 1) % SG;
+                const int bj = (q - 1) / SG, u = (q - 1) % SG;
+                const int b = bj / J, j = bj - b * J;
                 const int k = elem(j), h = k / HD, i = k - h * HD;
-                return src + ((size_t)h * a.max_split + s0 + min(u, ns - 1)) * PS + i;
+                return src + b * xs + ((size_t)h * a.max_split + s0 + min(u, ns - 1)) * PS + i;
             };
-            constexpr int NW = 1 + J * SG;
+            constexpr int NW = 1 + B * J * SG;
             auto use = [&](int q) { return q == 0 || (q - 1) % SG < ns; };
             uint64_t wv[NW];
 #pragma unroll
@@ -165,94 +197,123 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
                 if (use(q)) wv[q] = xchg::load(addr(q));
             ok &= xchg::settle_if(wv, use, addr, ep, cx.limit, a.abort_word);
             if (s0 > 0) lds_barrier();                     // the previous group's readers of ml are done
-            if (t < nml) sm.ml[t] = xchg::value(wv[0]);
+            if (t < B * nml) sm.ml[t] = xchg::value(wv[0]);
             lds_barrier();
 #pragma unroll
-            for (int j = 0; j < J; ++j) {
-                const float* mlh = sm.ml + (elem(j) / HD) * ns * 2;
-                float M = Mr[j];
+            for (int b = 0; b < B; ++b)
 #pragma unroll
-                for (int u = 0; u < SG; ++u)
-                    if (u < ns) M = fmaxf(M, mlh[2 * u]);
-                const float sc = exp2f(Mr[j] - M);          // rescale of the running sums (0 at start)
-                float L = Lr[j] * sc, O = Or[j] * sc;
+                for (int j = 0; j < J; ++j) {
+                    const float* mlh = sm.ml + b * nml + (elem(j) / HD) * ns * 2;
+                    float M = Mr[b][j];
 #pragma unroll
-                for (int u = 0; u < SG; ++u) {
-                    if (u < ns) {
-                        const float wgt = exp2f(mlh[2 * u] - M);
-                        L = fmaf(mlh[2 * u + 1], wgt, L);
-                        O = fmaf(xchg::value(wv[1 + j * SG + u]), wgt, O);
+                    for (int u = 0; u < SG; ++u)
+                        if (u < ns) M = fmaxf(M, mlh[2 * u]);
+                    const float sc = exp2f(Mr[b][j] - M);          // rescale of the running sums (0 at start)
+                    float L = Lr[b][j] * sc, O = Or[b][j] * sc;
+#pragma unroll
+                    for (int u = 0; u < SG; ++u) {
+                        if (u < ns) {
+                            const float wgt = exp2f(mlh[2 * u] - M);
+                            L = fmaf(mlh[2 * u + 1], wgt, L);
+                            O = fmaf(xchg::value(wv[1 + (b * J + j) * SG + u]), wgt, O);
+                        }
                     }
+                    Mr[b][j] = M;
+                    Lr[b][j] = L;
+                    Or[b][j] = O;
                 }
-                Mr[j] = M;
-                Lr[j] = L;
-                Or[j] = O;
-            }
         }
 #pragma unroll
-        for (int j = 0; j < J; ++j) v[j] = __fdividef(Or[j], Lr[j]);
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int j = 0; j < J; ++j) v[b][j] = __fdividef(Or[b][j], Lr[b][j]);
     } else {
-        // words 0..J-1: this thread's elements; word J: element 0 (the LayerNorm shift)
-        constexpr int NW = J + (LN ? 1 : 0);
-        auto addr = [&](int q) -> const uint64_t* { return q < J ? src + elem(q) : src; };
+        // per row: words 0..J-1 this thread's elements, word J element 0 (the LayerNorm shift)
+        constexpr int NR = J + (LN ? 1 : 0), NW = B * NR;
+        auto addr = [&](int q) -> const uint64_t* {
+            const int b = q / NR, qq = q - b * NR;
+            return src + b * xs + (qq < J ? elem(qq) : 0);
+        };
         uint64_t w[NW];
 #pragma unroll
         for (int q = 0; q < NW; ++q) w[q] = xchg::load(addr(q));
         ok = xchg::settle_n(w, NW, addr, ep, cx.limit, a.abort_word);
 #pragma unroll
-        for (int j = 0; j < J; ++j) v[j] = xchg::value(w[j]);
-        if constexpr (LN) x0 = xchg::value(w[NW - 1]);
+        for (int b = 0; b < B; ++b) {
+#pragma unroll
+            for (int j = 0; j < J; ++j) v[b][j] = xchg::value(w[b * NR + j]);
+            if constexpr (LN) x0[b] = xchg::value(w[b * NR + J]);
+        }
     }
     if (!ok) *sm.abort = 1;
 
     if constexpr (NORM) {
         constexpr float invK = 1.0f / (float)K;
-        float s1 = 0.f, q2 = 0.f;
+        constexpr int NS = (LN ? 2 : 1) * B;   // per row: (sum, sum of squares) or the sum of squares
+        float sums[NS];
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const float dx = (K % NT == 0 || t + NT * j < K) ? v[j] - x0 : 0.f;
-            s1 += dx;
-            q2 = fmaf(dx, dx, q2);
-        }
-        float mean = 0.f, var;
-        if constexpr (LN) {
-            const float2 tot = block_sum2<NT>(s1, q2, sm.red);
-            const float ms = tot.x * invK;
-            mean = x0 + ms;
-            var = fmaxf(tot.y * invK - ms * ms, 0.f);
-        } else {
-            var = block_sum<NT>(q2, sm.red) * invK;
-        }
-        const float r = 1.0f / sqrtf(var + a.eps);
+        for (int b = 0; b < B; ++b) {
+            float s1 = 0.f, q2 = 0.f;
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            float y = (v[j] - mean) * r * gg[j];
-            if constexpr (LN) y += bb[j];
-            v[j] = y;
+            for (int j = 0; j < J; ++j) {
+                const float dx = (K % NT == 0 || t + NT * j < K) ? v[b][j] - x0[b] : 0.f;
+                s1 += dx;
+                q2 = fmaf(dx, dx, q2);
+            }
+            if constexpr (LN) {
+                sums[2 * b] = s1;
+                sums[2 * b + 1] = q2;
+            } else {
+                sums[b] = q2;
+            }
+        }
+        block_sums<NS>(sums, sm.red);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            float mean = 0.f, var;
+            if constexpr (LN) {
+                const float ms = sums[2 * b] * invK;
+                mean = x0[b] + ms;
+                var = fmaxf(sums[2 * b + 1] * invK - ms * ms, 0.f);
+            } else {
+                var = sums[b] * invK;
+            }
+            const float r = 1.0f / sqrtf(var + a.eps);
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                float y = (v[b][j] - mean) * r * gg[j];
+                if constexpr (LN) y += bb[j];
+                v[b][j] = y;
+            }
         }
     } else {
         lds_barrier();   // the previous phase's readers of xl are done
     }
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const int k = t + NT * j;
-        if (K % NT == 0 || k < K) sm.xl[4 * swz<E>(k, LPR) + (k & 3)] = v[j];
-    }
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int k = t + NT * j;
+            if (K % NT == 0 || k < K) sm.xl[b * MAX_K + 4 * swz<E>(k, LPR) + (k & 3)] = v[b][j];
+        }
     lds_barrier();
 }
 
 // ---- one GEMV phase --------------------------------------------------------------------------
 struct PhaseIO {
-    const uint64_t* src;  // input words (IN_XCHG / IN_NORM / IN_ATTN)
+    const uint64_t* src;  // input words (IN_XCHG / IN_NORM / IN_ATTN); row b at src + b * src_xs
+    long long src_xs;
     uint32_t src_ep;
     const float* g;       // norm gain / bias
     const float* bt;
     const float* bias;    // linear bias or null
-    uint64_t* dst;        // output words
+    uint64_t* dst;        // output words; row b at dst + b * dst_xs
+    long long dst_xs;
     uint32_t dst_ep;
     const uint64_t* res;  // OUT_RESID: residual words, or null for the embedding row (first layer)
+    long long res_xs;
     uint32_t res_ep;
-    __half* kc;           // OUT_QKV*: this layer's cache
+    __half* kc;           // OUT_QKV*: this layer's cache (row b at kc + b * a.kv_row)
     __half* vc;
 };
 
@@ -300,7 +361,7 @@ template <class C, int K, int N, int NL, int IN, int OUT, bool LN>
 __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, const PackedMat& W, const PhaseIO& io,
                                            Smem& sm)
 {
-    constexpr int F = C::F, HD = C::HD;
+    constexpr int F = C::F, HD = C::HD, B = C::B;
     using G = Geo<F, K, N, NL>;
     constexpr int E = G::E, NP = G::NP;
     constexpr bool PAIR = OUT == OUT_QKV_ROPE || OUT == OUT_SWIGLU;
@@ -316,20 +377,32 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
     constexpr int NOUT = PAIR ? NP / 2 : NP;
     const int er = slot0 < NOUT ? slot0 : NOUT - 1;
     const bool eon = slot0 < NOUT;
+    // head: two rows guided by classifier-free guidance make one set of combined logits
+    const bool guided = B == 2 && OUT == OUT_HEAD && a.cfg;
 
-    unsigned long long best = 0ull;
+    unsigned long long best[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) best[b] = 0ull;
     bool have_x = false;
     for (int tile = blockIdx.x; tile < G::TILES; tile += gridDim.x) {
         const int row0 = (tile * NWAVE + wave) * G::RPW + sub * NP;   // first row of this lane's group
         // epilogue operands of the lane's own output row(s), issued before the weights
         const int erow = row0 + (PAIR ? 2 * er : er);
         const int erc = min(erow, N - 1);
-        float bv = 0.f, re = 0.f;
-        uint64_t rw = 0ull;
+        float bv = 0.f, re[B];
+        uint64_t rw[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            re[b] = 0.f;
+            rw[b] = 0ull;
+        }
         if constexpr (HAS_BIAS) bv = glb(io.bias)[erc];
         if constexpr (OUT == OUT_RESID) {
-            if (io.res) rw = xchg::load(io.res + erc);
-            else re = glb(a.emb)[(size_t)cx.tok * N + erc] + (C::GPT2 ? glb(a.wpe)[(size_t)cx.pos * N + erc] : 0.f);
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                if (io.res) rw[b] = xchg::load(io.res + b * io.res_xs + erc);
+                else re[b] = glb(a.emb)[(size_t)cx.tok[b] * N + erc] + (C::GPT2 ? glb(a.wpe)[(size_t)cx.pos * N + erc] : 0.f);
+            }
         }
         // every weight and raw scale of this lane (unconditional, clamped rows)
         uint4 w[NL];
@@ -349,142 +422,175 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
         __builtin_amdgcn_sched_barrier(0);
 
         if (!have_x) {
-            gather_x<C, F, K, IN, LN>(a, cx, io.src, io.src_ep, io.g, io.bt, sm);
+            gather_x<C, F, K, IN, LN>(a, cx, io.src, io.src_xs, io.src_ep, io.g, io.bt, sm);
             have_x = true;
             if (*sm.abort) return false;
         }
 
-        // this lane's x slices and their sums
-        float xs[G::SPL][E];
-        float sx[G::SPL];
-        const float4* xl4 = (const float4*)sm.xl;
+        // per row: this lane's x slices and their sums, then the dot products with the weights
+        float part[B][NP];
 #pragma unroll
-        for (int j = 0; j < G::SPL; ++j) {
-            const int slot = G::WIDE ? j * 64 + lane : slot0;
-            float s = 0.f;
+        for (int b = 0; b < B; ++b) {
+            float xs[G::SPL][E];
+            float sx[G::SPL];
+            const float4* xl4 = (const float4*)(sm.xl + b * MAX_K);
 #pragma unroll
-            for (int e4 = 0; e4 < E / 4; ++e4) {
-                const float4 v = xl4[e4 * G::LPR + slot];
-                xs[j][4 * e4 + 0] = v.x;
-                xs[j][4 * e4 + 1] = v.y;
-                xs[j][4 * e4 + 2] = v.z;
-                xs[j][4 * e4 + 3] = v.w;
-                s += (v.x + v.y) + (v.z + v.w);
+            for (int j = 0; j < G::SPL; ++j) {
+                const int slot = G::WIDE ? j * 64 + lane : slot0;
+                float s = 0.f;
+#pragma unroll
+                for (int e4 = 0; e4 < E / 4; ++e4) {
+                    const float4 v = xl4[e4 * G::LPR + slot];
+                    xs[j][4 * e4 + 0] = v.x;
+                    xs[j][4 * e4 + 1] = v.y;
+                    xs[j][4 * e4 + 2] = v.z;
+                    xs[j][4 * e4 + 3] = v.w;
+                    s += (v.x + v.y) + (v.z + v.w);
+                }
+                sx[j] = s;
             }
-            sx[j] = s;
-        }
-
-        float part[NP];
 #pragma unroll
-        for (int r = 0; r < NP; ++r) part[r] = 0.f;
+            for (int r = 0; r < NP; ++r) part[b][r] = 0.f;
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            const int j = G::WIDE ? i % G::SPL : 0;
-            const int r = G::WIDE ? i / G::SPL : i;
-            const float d = slot_dot<F>(w[i], xs[j], h_raw[i]);
-            part[r] += slot_value<F>(d, sx[j], __half2float(__ushort_as_half((unsigned short)sc_raw[i])),
-                                     __half2float(__ushort_as_half((unsigned short)sb_raw[i])));
+            for (int i = 0; i < NL; ++i) {
+                const int j = G::WIDE ? i % G::SPL : 0;
+                const int r = G::WIDE ? i / G::SPL : i;
+                const float d = slot_dot<F>(w[i], xs[j], h_raw[i]);
+                part[b][r] += slot_value<F>(d, sx[j], __half2float(__ushort_as_half((unsigned short)sc_raw[i])),
+                                            __half2float(__ushort_as_half((unsigned short)sb_raw[i])));
+            }
         }
 #pragma unroll
-        for (int r = 0; r < NP; ++r) part[r] = group_sum(part[r], G::GW);
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int r = 0; r < NP; ++r) part[b][r] = group_sum(part[b][r], G::GW);
 
         if constexpr (OUT == OUT_RESID) {
             if (io.res) {
-                uint64_t rr[1] = {rw};
-                auto addr = [&](int) { return io.res + erc; };
-                if (!xchg::settle_n(rr, 1, addr, io.res_ep, cx.limit, a.abort_word)) *sm.abort = 1;
-                re = xchg::value(rr[0]);
+                auto addr = [&](int q) { return io.res + q * io.res_xs + erc; };
+                if (!xchg::settle_n(rw, B, addr, io.res_ep, cx.limit, a.abort_word)) *sm.abort = 1;
+#pragma unroll
+                for (int b = 0; b < B; ++b) re[b] = xchg::value(rw[b]);
             }
         }
 
         if constexpr (OUT == OUT_HEAD) {
-            const float t = pick(part, er);
+            float tb[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) tb[b] = pick(part[b], er);
             if (eon && erow < N) {
-                glb(a.logits)[erow] = t;
-                if (a.samp_mode) xchg::store(a.x_logit + erow, t, io.dst_ep);
-                const unsigned long long key =
-                    ((unsigned long long)float_order_key(t) << 32) | (0xFFFFFFFFu - (uint32_t)erow);
-                best = key > best ? key : best;
+#pragma unroll
+                for (int b = 0; b < B; ++b) glb(a.logits)[(size_t)b * N + erow] = tb[b];
+                if (guided) {
+                    const float t = fmaf(a.cfg_weight, tb[0] - tb[B - 1], tb[0]);   // l0 + w (l0 - l1)
+                    if (a.samp_mode) xchg::store(a.x_logit + erow, t, io.dst_ep);
+                    const unsigned long long key =
+                        ((unsigned long long)float_order_key(t) << 32) | (0xFFFFFFFFu - (uint32_t)erow);
+                    best[0] = key > best[0] ? key : best[0];
+                } else {
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        if (a.samp_mode) xchg::store(a.x_logit + b * a.xs_logit + erow, tb[b], io.dst_ep);
+                        const unsigned long long key =
+                            ((unsigned long long)float_order_key(tb[b]) << 32) | (0xFFFFFFFFu - (uint32_t)erow);
+                        best[b] = key > best[b] ? key : best[b];
+                    }
+                }
             }
         } else if constexpr (PAIR) {
-            float pa[NP / 2], pb[NP / 2];
 #pragma unroll
-            for (int q = 0; q < NP / 2; ++q) {
-                pa[q] = part[2 * q];
-                pb[q] = part[2 * q + 1];
-            }
-            const float t0 = pick(pa, er), t1 = pick(pb, er);
-            if (eon && erow < N) {
-                if constexpr (OUT == OUT_SWIGLU) {
-                    xchg::store(io.dst + (erow >> 1), silu(t0) * t1, io.dst_ep);
-                } else {
-                    // rows (2m, 2m+1) = elements (i, i + hd/2) of a Q or K head, or (2m, 2m+1) of V
-                    constexpr int half = HD / 2;
-                    if (erow < QD + KD) {
-                        const bool isk = erow >= QD;
-                        const int m = (isk ? erow - QD : erow) >> 1;
-                        const int h = m / half, i = m - h * half;
-                        const float2 cs = ld8f(a.rope + (size_t)cx.pos * half + i);
-                        const float ra = t0 * cs.x - t1 * cs.y, rb = t0 * cs.y + t1 * cs.x;
-                        if (!isk) {
-                            xchg::store(io.dst + h * HD + i, ra, io.dst_ep);
-                            xchg::store(io.dst + h * HD + i + half, rb, io.dst_ep);
-                        } else {
-                            const __half ha = __float2half_rn(ra), hb = __float2half_rn(rb);
-                            __half* c = io.kc + ((size_t)h * a.n_ctx + cx.pos) * HD;
-                            st_half(c + i, ha);
-                            st_half(c + i + half, hb);
-                            xchg::store(io.dst + QD + h * HD + i, __half2float(ha), io.dst_ep);
-                            xchg::store(io.dst + QD + h * HD + i + half, __half2float(hb), io.dst_ep);
-                        }
+            for (int b = 0; b < B; ++b) {
+                float pa[NP / 2], pb[NP / 2];
+#pragma unroll
+                for (int q = 0; q < NP / 2; ++q) {
+                    pa[q] = part[b][2 * q];
+                    pb[q] = part[b][2 * q + 1];
+                }
+                const float t0 = pick(pa, er), t1 = pick(pb, er);
+                uint64_t* dst = io.dst + b * io.dst_xs;
+                if (eon && erow < N) {
+                    if constexpr (OUT == OUT_SWIGLU) {
+                        xchg::store(dst + (erow >> 1), silu(t0) * t1, io.dst_ep);
                     } else {
-                        const int rv = erow - QD - KD;
-                        const int h = rv / HD, i = rv - h * HD;
-                        const __half ha = __float2half_rn(t0), hb = __float2half_rn(t1);
-                        __half* c = io.vc + ((size_t)h * a.n_ctx + cx.pos) * HD;
-                        st_half(c + i, ha);
-                        st_half(c + i + 1, hb);
-                        xchg::store(io.dst + erow, __half2float(ha), io.dst_ep);
-                        xchg::store(io.dst + erow + 1, __half2float(hb), io.dst_ep);
+                        // rows (2m, 2m+1) = elements (i, i + hd/2) of a Q or K head, or (2m, 2m+1) of V
+                        constexpr int half = HD / 2;
+                        if (erow < QD + KD) {
+                            const bool isk = erow >= QD;
+                            const int m = (isk ? erow - QD : erow) >> 1;
+                            const int h = m / half, i = m - h * half;
+                            const float2 cs = ld8f(a.rope + (size_t)cx.pos * half + i);
+                            const float ra = t0 * cs.x - t1 * cs.y, rb = t0 * cs.y + t1 * cs.x;
+                            if (!isk) {
+                                xchg::store(dst + h * HD + i, ra, io.dst_ep);
+                                xchg::store(dst + h * HD + i + half, rb, io.dst_ep);
+                            } else {
+                                const __half ha = __float2half_rn(ra), hb = __float2half_rn(rb);
+                                __half* c = io.kc + b * a.kv_row + ((size_t)h * a.n_ctx + cx.pos) * HD;
+                                st_half(c + i, ha);
+                                st_half(c + i + half, hb);
+                                xchg::store(dst + QD + h * HD + i, __half2float(ha), io.dst_ep);
+                                xchg::store(dst + QD + h * HD + i + half, __half2float(hb), io.dst_ep);
+                            }
+                        } else {
+                            const int rv = erow - QD - KD;
+                            const int h = rv / HD, i = rv - h * HD;
+                            const __half ha = __float2half_rn(t0), hb = __float2half_rn(t1);
+                            __half* c = io.vc + b * a.kv_row + ((size_t)h * a.n_ctx + cx.pos) * HD;
+                            st_half(c + i, ha);
+                            st_half(c + i + 1, hb);
+                            xchg::store(dst + erow, __half2float(ha), io.dst_ep);
+                            xchg::store(dst + erow + 1, __half2float(hb), io.dst_ep);
+                        }
                     }
                 }
             }
         } else {
-            const float t = pick(part, er) + bv;
-            if (eon && erow < N) {
-                if constexpr (OUT == OUT_QKV) {
-                    if (erow < QD) {
-                        xchg::store(io.dst + erow, t, io.dst_ep);
-                    } else {
-                        const bool isk = erow < QD + KD;
-                        const int rv = isk ? erow - QD : erow - QD - KD;
-                        const int h = rv / HD, i = rv - h * HD;
-                        const __half hv = __float2half_rn(t);
-                        st_half((isk ? io.kc : io.vc) + ((size_t)h * a.n_ctx + cx.pos) * HD + i, hv);
-                        xchg::store(io.dst + erow, __half2float(hv), io.dst_ep);
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const float t = pick(part[b], er) + bv;
+                uint64_t* dst = io.dst + b * io.dst_xs;
+                if (eon && erow < N) {
+                    if constexpr (OUT == OUT_QKV) {
+                        if (erow < QD) {
+                            xchg::store(dst + erow, t, io.dst_ep);
+                        } else {
+                            const bool isk = erow < QD + KD;
+                            const int rv = isk ? erow - QD : erow - QD - KD;
+                            const int h = rv / HD, i = rv - h * HD;
+                            const __half hv = __float2half_rn(t);
+                            st_half((isk ? io.kc : io.vc) + b * a.kv_row + ((size_t)h * a.n_ctx + cx.pos) * HD + i, hv);
+                            xchg::store(dst + erow, __half2float(hv), io.dst_ep);
+                        }
+                    } else if constexpr (OUT == OUT_RESID) {
+                        xchg::store(dst + erow, t + re[b], io.dst_ep);
+                    } else if constexpr (OUT == OUT_GELU) {
+                        xchg::store(dst + erow, gelu_tanh(t), io.dst_ep);
                     }
-                } else if constexpr (OUT == OUT_RESID) {
-                    xchg::store(io.dst + erow, t + re, io.dst_ep);
-                } else if constexpr (OUT == OUT_GELU) {
-                    xchg::store(io.dst + erow, gelu_tanh(t), io.dst_ep);
                 }
             }
         }
     }
 
     if constexpr (OUT == OUT_HEAD) {
-        // this workgroup's best (ordered logit, ~index) key, published as two words
+        // this workgroup's best (ordered logit, ~index) key of each row (guided: of the combined
+        // logits, row 0 only), published as two words
         if ((int)blockIdx.x < G::TILES) {
-            __shared__ unsigned long long bkey[NWAVE];
-            best = wave_max_u64(best);
-            if (lane == 0) bkey[wave] = best;
+            __shared__ unsigned long long bkey[B][NWAVE];
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const unsigned long long m = wave_max_u64(best[b]);
+                if (lane == 0) bkey[b][wave] = m;
+            }
             lds_barrier();
             if (threadIdx.x == 0) {
-                unsigned long long m = bkey[0];
+                const int nrows = guided ? 1 : B;
+                for (int b = 0; b < nrows; ++b) {
+                    unsigned long long m = bkey[b][0];
 #pragma unroll
-                for (int i = 1; i < NWAVE; ++i) m = bkey[i] > m ? bkey[i] : m;
-                xchg::store_bits(io.dst + 2 * blockIdx.x, (uint32_t)(m >> 32), io.dst_ep);
-                xchg::store_bits(io.dst + 2 * blockIdx.x + 1, (uint32_t)m, io.dst_ep);
+                    for (int i = 1; i < NWAVE; ++i) m = bkey[b][i] > m ? bkey[b][i] : m;
+                    xchg::store_bits(io.dst + b * io.dst_xs + 2 * blockIdx.x, (uint32_t)(m >> 32), io.dst_ep);
+                    xchg::store_bits(io.dst + b * io.dst_xs + 2 * blockIdx.x + 1, (uint32_t)m, io.dst_ep);
+                }
             }
         }
     }
@@ -492,7 +598,7 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
 }
 
 // ---- attention phase -------------------------------------------------------------------------
-// Work item (head h, chunk s) = keys [256 s, 256 s + 256) of query head h; the same math as
+// Work item (row b, head h, chunk s) = keys [256 s, 256 s + 256) of query head h; the same math as
 // k_attn (attention.hip), with the query and the new position's key/value taken from the
 // exchange.  Items go to the highest-numbered workgroups, which the QKV phase leaves idle when
 // it has fewer tiles than the grid has workgroups.
@@ -504,16 +610,16 @@ __device__ __forceinline__ bool attn_phase(const StepArgs& a, const Ctx& cx, con
     constexpr int LPK = HD / 8, KPI = 64 / LPK, R = KTILE / KPI, PS = HD + 2;
     __shared__ float ow[NWAVE][HD];
     __shared__ float mw[NWAVE], lw[NWAVE];
-    const int items = H * cx.S;
+    const int items = C::B * H * cx.S;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c = lane % LPK, kq = lane / LPK;
     const int n_keys = cx.n_keys;
     const float qscale = 1.4426950408889634f / sqrtf((float)HD);
 
     for (int item = (int)gridDim.x - 1 - (int)blockIdx.x; item < items; item += gridDim.x) {
-        const int h = item % H, s = item / H, g = h / (H / HK);
+        const int h = item % H, bs = item / H, s = bs % cx.S, b = bs / cx.S, g = h / (H / HK);
         const int k0 = s * ATTN_CHUNK + wave * KTILE;
-        const size_t head_off = (size_t)g * a.n_ctx * HD;
+        const size_t head_off = (size_t)b * a.kv_row + (size_t)g * a.n_ctx * HD;
         const int klast = n_keys - 1;
         uint4 kr[R], vr[R];
 #pragma unroll
@@ -523,9 +629,10 @@ __device__ __forceinline__ bool attn_phase(const StepArgs& a, const Ctx& cx, con
             vr[r] = ld16(vcache + head_off + (size_t)key * HD + c * 8);
         }
         // words 0-7: query dims 8c..8c+7 of head h; 8-15 / 16-23: the new key / value of kv head g
-        const uint64_t* pq = a.x_qkv + h * HD + c * 8;
-        const uint64_t* pk = a.x_qkv + QD + g * HD + c * 8;
-        const uint64_t* pv = a.x_qkv + QD + KD + g * HD + c * 8;
+        const uint64_t* xq = a.x_qkv + b * a.xs_qkv;
+        const uint64_t* pq = xq + h * HD + c * 8;
+        const uint64_t* pk = xq + QD + g * HD + c * 8;
+        const uint64_t* pv = xq + QD + KD + g * HD + c * 8;
         auto addr = [&](int i) { return (i < 8 ? pq : i < 16 ? pk - 8 : pv - 16) + i; };
         uint64_t wx[24];
 #pragma unroll
@@ -610,7 +717,7 @@ __device__ __forceinline__ bool attn_phase(const StepArgs& a, const Ctx& cx, con
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, mw[w]);
-        uint64_t* part = a.x_part + ((size_t)h * a.max_split + s) * PS;
+        uint64_t* part = a.x_part + b * a.xs_part + ((size_t)h * a.max_split + s) * PS;
         if (threadIdx.x < HD) {
             float acc = 0.f;
 #pragma unroll
@@ -665,18 +772,19 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
 {
     constexpr int OUT_QKV_K = C::GPT2 ? OUT_QKV : OUT_QKV_ROPE;
     constexpr int OUT_FC_K = C::GPT2 ? OUT_GELU : OUT_SWIGLU;
+    constexpr int B = C::B;
     const ArgsPtr ap = (ArgsPtr)args;
 
-    // the phase input buffer; after the head, workgroup 0 reuses it for the chain's draw (keys,
-    // the history's bit set, the draw's scratch)
+    // the phase input buffer (one MAX_K slice per batch row); after the head, the drawing
+    // workgroup reuses it for the chain's draw (keys, the history's bit set, the draw's scratch)
     constexpr size_t KEYS_BYTES = ((size_t)samp::key_words(C::V) * 4 + 15) & ~(size_t)15;
     constexpr size_t SEEN_BYTES = ((size_t)(C::V + 31) / 32 * 4 + 15) & ~(size_t)15;
     constexpr size_t SAMP_BYTES = KEYS_BYTES + SEEN_BYTES + sizeof(samp::Scratch);
-    constexpr size_t RAW_BYTES = MAX_K * 4 > SAMP_BYTES ? MAX_K * 4 : SAMP_BYTES;
+    constexpr size_t RAW_BYTES = (size_t)B * MAX_K * 4 > SAMP_BYTES ? (size_t)B * MAX_K * 4 : SAMP_BYTES;
     static_assert(RAW_BYTES <= 56 * 1024, "LDS of one workgroup");
     __shared__ __align__(16) unsigned char raw[RAW_BYTES];
-    __shared__ float red[2 * NWAVE];
-    __shared__ float ml[C::H * SG * 2];
+    __shared__ float red[4 * NWAVE];
+    __shared__ float ml[B * C::H * SG * 2];
     __shared__ int s_abort;
     Smem sm{(float*)raw, red, ml, &s_abort};
 
@@ -689,9 +797,12 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
         // a wait of an earlier launch timed out: the exchange state is not trusted, do nothing
         if (ld_uniform((const int*)a.abort_word)) return;
         cx.pos = ld_uniform(a.pos);
-        const int tok = ld_uniform(a.tok);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const int tok = ld_uniform(a.tok + b);
+            cx.tok[b] = tok < 0 ? 0 : (tok >= C::V ? C::V - 1 : tok);
+        }
         ctr = (uint32_t)ld_uniform((const int*)a.ctr);
-        cx.tok = tok < 0 ? 0 : (tok >= C::V ? C::V - 1 : tok);
         cx.n_keys = cx.pos + 1;
         cx.S = (cx.n_keys + ATTN_CHUNK - 1) / ATTN_CHUNK;
         cx.limit = a.spin_limit;
@@ -712,11 +823,13 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
             const long long o = a.lstride * l;
             PhaseIO io{};
             io.src = a.x_out;
+            io.src_xs = a.xs_d;
             io.src_ep = e - 1u;
             io.g = shift(a.L0.n1g, o);
             io.bt = shift(a.L0.n1b, o);
             io.bias = shift(a.L0.bqkv, o);
             io.dst = a.x_qkv;
+            io.dst_xs = a.xs_qkv;
             io.dst_ep = e;
             io.kc = a.L0.kc + a.kvstride * l;
             io.vc = a.L0.vc + a.kvstride * l;
@@ -736,11 +849,14 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
             const long long o = a.lstride * l;
             PhaseIO io{};
             io.src = a.x_part;
+            io.src_xs = a.xs_part;
             io.src_ep = e + 1u;
             io.bias = shift(a.L0.bo, o);
             io.dst = a.x_attn;
+            io.dst_xs = a.xs_d;
             io.dst_ep = e + 2u;
             io.res = l == 0 ? nullptr : a.x_out;
+            io.res_xs = a.xs_d;
             io.res_ep = e - 1u;
             if (!gemv_phase<C, C::QD, C::D, C::NL_O, IN_ATTN, OUT_RESID, false>(a, cx, shift(a.L0.o, o), io, sm))
                 return give_up(a);
@@ -750,11 +866,13 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
             const long long o = a.lstride * l;
             PhaseIO io{};
             io.src = a.x_attn;
+            io.src_xs = a.xs_d;
             io.src_ep = e + 2u;
             io.g = shift(a.L0.n2g, o);
             io.bt = shift(a.L0.n2b, o);
             io.bias = shift(a.L0.bfc, o);
             io.dst = a.x_h;
+            io.dst_xs = a.xs_h;
             io.dst_ep = e + 3u;
             if (!gemv_phase<C, C::D, C::FCN, C::NL_FC, IN_NORM, OUT_FC_K, C::GPT2>(a, cx, shift(a.L0.fc, o), io, sm))
                 return give_up(a);
@@ -764,11 +882,14 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
             const long long o = a.lstride * l;
             PhaseIO io{};
             io.src = a.x_h;
+            io.src_xs = a.xs_h;
             io.src_ep = e + 3u;
             io.bias = shift(a.L0.bdown, o);
             io.dst = a.x_out;
+            io.dst_xs = a.xs_d;
             io.dst_ep = e + 4u;
             io.res = a.x_attn;
+            io.res_xs = a.xs_d;
             io.res_ep = e + 2u;
             if (!gemv_phase<C, C::FF, C::D, C::NL_F, IN_XCHG, OUT_RESID, false>(a, cx, shift(a.L0.down, o), io, sm))
                 return give_up(a);
@@ -780,78 +901,106 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
     const uint32_t eh = ep0 + 5u * (uint32_t)n_layer;
     PhaseIO io{};
     io.src = a.x_out;
+    io.src_xs = a.xs_d;
     io.src_ep = eh - 1u;
     io.g = a.nfg;
     io.bt = a.nfb;
     io.dst = a.x_best;
+    io.dst_xs = a.xs_best;
     io.dst_ep = eh;
     if (!gemv_phase<C, C::D, C::V, C::NL_HEAD, IN_NORM, OUT_HEAD, C::GPT2>(a, cx, a.head, io, sm)) return give_up(a);
 
-    if (blockIdx.x != 0) return;
-    // the token this step consumed (read before the sampler overwrites it): recorded at seq[pos]
-    // for the repetition penalty of later steps
-    const int cur = *glb(a.tok);
+    // the rows' picks: guided pairs make one pick that both rows take.  Each row records the
+    // token it consumed (read before the pick overwrites it) at seq[pos][row] for the repetition
+    // penalty of later steps, and its id at hist[pos][row]
+    const bool guided = B == 2 && a.cfg;
+    const int npick = guided ? 1 : B;
     if (a.samp_mode) {
-        // the chain's draw (workgroup 0) over every logit, from the exchange words
-        const int t = threadIdx.x;
-        uint32_t* keys = (uint32_t*)raw;
-        uint32_t* seen = (uint32_t*)(raw + KEYS_BYTES);
-        samp::Scratch& S = *(samp::Scratch*)(raw + KEYS_BYTES + SEEN_BYTES);
-        const bool pen = a.chain.penalty != 1.f;
-        if (pen) samp::build_seen<NT>(seen, C::V, a.seq, 1, cx.pos, cur);
-        const uint32_t* sp = pen ? seen : nullptr;
-        constexpr int JV = (C::V + NT - 1) / NT;
-        auto addr = [&](int q) { return a.x_logit + min(t + NT * q, C::V - 1); };
-        uint64_t w[JV];
+        // the chain's draw of pick r on workgroup r (all of them on workgroup 0 of a one-workgroup grid)
+        for (int r = blockIdx.x; r < npick; r += gridDim.x) {
+            const int t = threadIdx.x;
+            uint32_t* keys = (uint32_t*)raw;
+            uint32_t* seen = (uint32_t*)(raw + KEYS_BYTES);
+            samp::Scratch& S = *(samp::Scratch*)(raw + KEYS_BYTES + SEEN_BYTES);
+            int cur[B];
 #pragma unroll
-        for (int q = 0; q < JV; ++q) w[q] = xchg::load(addr(q));
-        if (!xchg::settle_n(w, JV, addr, eh, cx.limit, a.abort_word)) s_abort = 1;
+            for (int b = 0; b < B; ++b) cur[b] = glb(a.tok)[b];
+            const bool pen = a.chain.penalty != 1.f;
+            __syncthreads();   // the previous pick's readers of the scratch are done
+            if (pen) samp::build_seen<NT>(seen, C::V, a.seq + r, B, cx.pos, cur[r]);
+            const uint32_t* sp = pen ? seen : nullptr;
+            constexpr int JV = (C::V + NT - 1) / NT;
+            const uint64_t* xl = a.x_logit + r * a.xs_logit;
+            auto addr = [&](int q) { return xl + min(t + NT * q, C::V - 1); };
+            uint64_t w[JV];
 #pragma unroll
-        for (int q = 0; q < JV; ++q)
-            if (t + NT * q < C::V)
-                keys[samp::key_at(t + NT * q)] = samp::chain_key(xchg::value(w[q]), t + NT * q, a.chain, sp);
-        __syncthreads();
-        if (s_abort) return give_up(a);
-        const float u = samp::uniform24(a.seed, 0u, (uint32_t)cx.pos, 0u);
-        const int id = samp::chain_draw<NT>(keys, C::V, a.chain, u, S, sp);
-        if (t == 0) {
-            glb(a.seq)[cx.pos] = cur;
-            *glb(a.tok) = id;
-            glb(a.hist)[cx.pos] = id;
+            for (int q = 0; q < JV; ++q) w[q] = xchg::load(addr(q));
+            if (!xchg::settle_n(w, JV, addr, eh, cx.limit, a.abort_word)) s_abort = 1;
+#pragma unroll
+            for (int q = 0; q < JV; ++q)
+                if (t + NT * q < C::V)
+                    keys[samp::key_at(t + NT * q)] = samp::chain_key(xchg::value(w[q]), t + NT * q, a.chain, sp);
+            __syncthreads();
+            if (s_abort) return give_up(a);
+            const float u = samp::uniform24(a.seed, (uint32_t)r, (uint32_t)cx.pos, 0u);
+            const int id = samp::chain_draw<NT>(keys, C::V, a.chain, u, S, sp);
+            if (t == 0) {
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    if (!guided && b != r) continue;
+                    glb(a.seq)[(size_t)cx.pos * B + b] = cur[b];
+                    glb(a.tok)[b] = id;
+                    glb(a.hist)[(size_t)cx.pos * B + b] = id;
+                }
+            }
+        }
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
             *glb(a.pos) = cx.pos + 1;
             *glb(a.ctr) = ctr + 1u;
         }
         return;
     }
-    // greedy sampler, last stage (workgroup 0): the best of the per-workgroup keys; ties go to
-    // the lowest index because the key's low word is the inverted index
+    if (blockIdx.x != 0) return;
+    // greedy sampler, last stage (workgroup 0): the best of the per-workgroup keys of each row;
+    // ties go to the lowest index because the key's low word is the inverted index
     constexpr int HEAD_TILES = Geo<C::F, C::D, C::V, C::NL_HEAD>::TILES;
     const int nb = min((int)gridDim.x, HEAD_TILES);
-    unsigned long long bk = 0ull;
+    __shared__ unsigned long long fkey[B][NWAVE];
     bool ok = true;
-    for (int w = threadIdx.x; w < nb; w += NT) {
-        float hl[2];
-        ok &= xchg::wait_words<2>(a.x_best + 2 * w, 1, eh, hl, cx.limit, a.abort_word);
-        const unsigned long long key = ((unsigned long long)__float_as_uint(hl[0]) << 32) | __float_as_uint(hl[1]);
-        bk = key > bk ? key : bk;
+    for (int r = 0; r < npick; ++r) {
+        unsigned long long bk = 0ull;
+        for (int w = threadIdx.x; w < nb; w += NT) {
+            float hl[2];
+            ok &= xchg::wait_words<2>(a.x_best + r * a.xs_best + 2 * w, 1, eh, hl, cx.limit, a.abort_word);
+            const unsigned long long key = ((unsigned long long)__float_as_uint(hl[0]) << 32) | __float_as_uint(hl[1]);
+            bk = key > bk ? key : bk;
+        }
+        bk = wave_max_u64(bk);
+        if ((threadIdx.x & 63) == 0) fkey[r][threadIdx.x >> 6] = bk;
     }
     if (!ok) s_abort = 1;
-    bk = wave_max_u64(bk);
-    __shared__ unsigned long long fkey[NWAVE];
-    if ((threadIdx.x & 63) == 0) fkey[threadIdx.x >> 6] = bk;
     lds_barrier();
     if (threadIdx.x == 0) {
         if (s_abort) {
             xchg::raise_abort(a.abort_word);
             return;
         }
-        unsigned long long m = fkey[0];
+        int cur[B], id[B];
 #pragma unroll
-        for (int i = 1; i < NWAVE; ++i) m = fkey[i] > m ? fkey[i] : m;
-        const int id = (int)(0xFFFFFFFFu - (uint32_t)m);
-        glb(a.seq)[cx.pos] = cur;
-        *glb(a.tok) = id;
-        glb(a.hist)[cx.pos] = id;
+        for (int b = 0; b < B; ++b) cur[b] = glb(a.tok)[b];
+        for (int r = 0; r < npick; ++r) {
+            unsigned long long m = fkey[r][0];
+#pragma unroll
+            for (int i = 1; i < NWAVE; ++i) m = fkey[r][i] > m ? fkey[r][i] : m;
+            id[r] = (int)(0xFFFFFFFFu - (uint32_t)m);
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const int v = id[guided ? 0 : b];
+            glb(a.seq)[(size_t)cx.pos * B + b] = cur[b];
+            glb(a.tok)[b] = v;
+            glb(a.hist)[(size_t)cx.pos * B + b] = v;
+        }
         *glb(a.pos) = cx.pos + 1;
         *glb(a.ctr) = ctr + 1u;
     }
@@ -860,13 +1009,13 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
 // the shapes with a persistent kernel: the decoders of the pages at their real sizes, and the
 // small shapes the parity tests use; any other shape runs one launch per operator
 struct Entry {
-    int fmt, arch, d, h, hk, hd, ff, v;
+    int fmt, arch, d, h, hk, hd, ff, v, b;
     const void* fn;
 };
-template <int F, int A, int D, int H, int HK, int HD, int FF, int V>
+template <int F, int A, int D, int H, int HK, int HD, int FF, int V, int B = 1>
 Entry entry()
 {
-    return Entry{F, A, D, H, HK, HD, FF, V, (const void*)k_step<Shape<F, A, D, H, HK, HD, FF, V>>};
+    return Entry{F, A, D, H, HK, HD, FF, V, B, (const void*)k_step<Shape<F, A, D, H, HK, HD, FF, V, B>>};
 }
 
 const Entry* entries(int& n)
@@ -877,6 +1026,11 @@ const Entry* entries(int& n)
         entry<FMT_Q8_0, A_LLAMA, 1024, 16, 16, 64, 4096, 8192>(),   // Llama-shaped ~520M T3, Q8_0
         entry<FMT_Q4_0, A_LLAMA, 1024, 16, 16, 64, 4096, 8192>(),   //   and Q4_0
         entry<FMT_Q5_0, A_GPT2, 1024, 16, 16, 64, 4096, 8192>(),    // the T3 in the journal's Q5_0
+        // two rows: a guided pair (classifier-free guidance) or two streams
+        entry<FMT_Q4_0, A_GPT2, 1024, 16, 16, 64, 4096, 8192, 2>(),
+        entry<FMT_Q8_0, A_LLAMA, 1024, 16, 16, 64, 4096, 8192, 2>(),
+        entry<FMT_Q4_0, A_GPT2, 128, 2, 2, 64, 256, 160, 2>(),
+        entry<FMT_Q8_0, A_LLAMA, 128, 2, 2, 64, 256, 160, 2>(),
         // test shapes
         entry<FMT_Q4_0, A_GPT2, 128, 2, 2, 64, 256, 160>(),
         entry<FMT_Q8_0, A_GPT2, 128, 2, 2, 64, 256, 160>(),
@@ -899,14 +1053,14 @@ const Entry* entries(int& n)
 
 }  // namespace
 
-const void* step_kernel_for(int fmt, int arch_llama, int d, int h, int hk, int hd, int ff, int vocab)
+const void* step_kernel_for(int fmt, int arch_llama, int d, int h, int hk, int hd, int ff, int vocab, int batch)
 {
     int n = 0;
     const Entry* t = entries(n);
     const int arch = arch_llama ? A_LLAMA : A_GPT2;
     for (int i = 0; i < n; ++i)
         if (t[i].fmt == fmt && t[i].arch == arch && t[i].d == d && t[i].h == h && t[i].hk == hk && t[i].hd == hd &&
-            t[i].ff == ff && t[i].v == vocab)
+            t[i].ff == ff && t[i].v == vocab && t[i].b == batch)
             return t[i].fn;
     return nullptr;
 }

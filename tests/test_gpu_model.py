@@ -183,17 +183,18 @@ BATCH2 = {
 }
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("variant", list(BATCH2))
 @pytest.mark.parametrize("arch,fmt", [("gpt2", "q4_0"), ("llama", "q8_0")])
-def test_batch2_teacher_forced(arch, fmt, variant):
+def test_batch2_teacher_forced(arch, fmt, variant, mode):
     """Two rows in one step (each weight read once for both): two independent streams, or a
     classifier-free-guided pair (row 0 conditioned, row 1 not) whose one draw both rows take.
     Both rows' logits are one tensor at rel <= 2e-3; ids as in the other teacher-forced tests."""
     cfg = synth.small_config(arch, fmt, batch=2, d_ff=256, n_ctx=80, seed=99, **BATCH2[variant])
-    say(f"[model-small] batch 2 {variant} {arch} {fmt}")
+    say(f"[model-small] batch 2 {variant} {arch} {fmt} {mode}")
     w = synth.model_weights(cfg, 42, norm_std=0.5)
     om = oracle.OracleModel(cfg, w)
-    gm = gpu_model(cfg, w, "per_operator")
+    gm = gpu_model(cfg, w, mode)
     toks = synth.prompt_tokens(cfg, 6, seed=2)                  # a different prompt per row
     consumed = [[int(t) for t in toks[b, :, 0]] for b in range(2)]
     o_ids = om.prefill(toks)
@@ -221,7 +222,6 @@ def test_batch2_teacher_forced(arch, fmt, variant):
         g_ids = gm.step(dev(o_ids)).cpu().numpy()
         o_ids = om.step(o_ids)
     assert checked >= (20 if guided else 40)
-    assert not gm.uses_persistent_step()
     gm.synchronize()
     gm.close()
 

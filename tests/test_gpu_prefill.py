@@ -323,3 +323,65 @@ def test_full_size_talker_prompt_pass():
     assert r <= REL_TOL and rel_err(gl, sl) <= REL_TOL
     for b in range(cfg["batch"]):
         assert ids_agree(gi[b, 0], sl[b])
+
+
+def test_prompt_fills_the_context():
+    """A prompt of exactly n_ctx ids (the last position is n_ctx - 1); the next step reports a
+    full context and changes nothing."""
+    from quantized_gemv_kv_amd import TsdError
+    cfg = synth.small_config("llama", "q8_0", d_ff=256, n_ctx=96)
+    say("[prefill] whole context")
+    w = synth.model_weights(cfg, 8, norm_std=0.5)
+    check_prompt(cfg, w, [96], n_steps=0)
+    gm = gpu_model(cfg, w)
+    gm.prefill(dev(synth.prompt_tokens(cfg, 96, seed=30)))
+    with pytest.raises(TsdError) as e:
+        gm.step(None)
+    assert e.value.status == 4 and gm.n_past == 96
+    gm.close()
+
+
+def test_prompt_ids_outside_the_vocabulary_are_clamped():
+    """Ids below 0 or past the vocabulary enter as 0 and vocab - 1: the cache and the logits
+    are bit for bit those of the clamped prompt."""
+    cfg = synth.small_config("gpt2", "q4_0", d_ff=256, n_ctx=64)
+    w = synth.model_weights(cfg, 9, norm_std=0.5)
+    toks = synth.prompt_tokens(cfg, 40, seed=4)
+    bad = toks.copy()
+    bad[0, 3, 0], bad[0, 17, 0], bad[0, 39, 0] = -5, cfg["vocab"] + 7, 1 << 30
+    good = np.clip(bad, 0, cfg["vocab"] - 1)
+    out = []
+    for t in (bad, good):
+        gm = gpu_model(cfg, w)
+        ids = gm.prefill(dev(t)).cpu().numpy()
+        k, v = gm.get_kv()
+        out.append((ids, k.cpu().numpy().view(np.uint16), v.cpu().numpy().view(np.uint16), gm.logits().cpu().numpy()))
+        gm.close()
+    for a, b in zip(out[0], out[1]):
+        assert np.array_equal(a, b)
+
+
+def test_prompt_after_truncate():
+    """40 ids, truncated back to 25, then 30 more: the cache of the 55 positions and the logits
+    against the oracle doing the same."""
+    cfg = synth.small_config("gpt2", "q8_0", d_ff=256, n_ctx=64)
+    say("[prefill] after truncate")
+    w = synth.model_weights(cfg, 10, norm_std=0.5)
+    om = oracle.OracleModel(cfg, w)
+    gm = gpu_model(cfg, w)
+    a, b = synth.prompt_tokens(cfg, 40, seed=1), synth.prompt_tokens(cfg, 30, seed=2)
+    om.prefill(a)
+    gm.prefill(dev(a))
+    om.truncate(25)
+    gm.truncate(25)
+    om.prefill(b)
+    g_ids = gm.prefill(dev(b)).cpu().numpy()
+    gk, gv = gm.get_kv()
+    ok, ov = om.get_kv()
+    r = kv_rel(gk, gv, ok, ov, 55)
+    lo, lg = om.logits(), gm.logits().cpu().numpy()
+    say(f"  cache rel {r:.2e}, logits rel {rel_err(lg, lo):.2e}")
+    assert gm.n_past == om.n_past == 55
+    assert r <= REL_TOL and rel_err(lg, lo) <= REL_TOL
+    assert ids_agree(g_ids[0, 0], lo[0])
+    gm.close()

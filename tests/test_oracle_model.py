@@ -6,7 +6,8 @@
 * the Talker + code-predictor frame == plain Llama-shaped forwards over the sequences the
   frame loop defines (pins the embedding sum, the pass wiring, the per-frame restart);
 * greedy / top-k picks == the sampler applied to the returned logits;
-* batch rows are independent; bad inputs raise and leave the state alone.
+* batch rows are independent; bad inputs raise and leave the state alone;
+* the cache read-out returns what the cache load took, in the same layout.
 """
 import numpy as np
 import pytest
@@ -266,3 +267,23 @@ def test_step_equals_embedding_layers_norm_head(orc, arch, fmt):
         h = orc.rmsnorm(x[0], w[-2], cfg["norm_eps"])
     ref = orc.gemv(fmt, w[-1], cfg["vocab"], d, h)
     assert rel(a.logits()[0], ref) < 1e-12
+
+
+@pytest.mark.parametrize("arch", ["gpt2", "llama", "talker_cp"])
+def test_cache_read_out_round_trips(orc, arch):
+    """get_kv returns what load_kv took, in the same [layer][batch][kv_head][pos][hd] layout, bit
+    for bit; positions past n_past are refused; a step writes exactly one new position."""
+    cfg = synth.small_config(arch, "aff8" if arch == "talker_cp" else "q8_0")
+    m, _ = make(orc, cfg)
+    k, v = synth.kv_cache(cfg, 20, seed=5)
+    m.load_kv(k, v, 20)
+    k2, v2 = m.get_kv()
+    assert k2.shape == k.shape and np.array_equal(k2, k) and np.array_equal(v2, v)
+    with pytest.raises(Exception):
+        m.get_kv(21)
+    tok = synth.prompt_tokens(cfg, 1, seed=6)[:, 0, :]
+    m.step(tok)
+    k3, v3 = m.get_kv()
+    assert k3.shape[3] == 21
+    assert np.array_equal(k3[:, :, :, :20], k) and np.array_equal(v3[:, :, :, :20], v)
+    assert np.any(k3[:, :, :, 20] != 0)

@@ -108,16 +108,16 @@ __device__ __forceinline__ float4v mfma(half8 a, half8 b, float4v c)
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-template <int F, int EPI, int KS>
+template <int F, int EPI, int KS, int NU>
 __global__ __launch_bounds__(64 * KS) void k_pf_gemm(const PfGemmArgs a)
 {
     using T = PfFmt<F>;
     constexpr int GB = T::GB;
-    __shared__ float red[KS][16][64];
+    __shared__ float red[KS][8 * NU][64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int c = lane & 15, j = lane >> 4;
     const int m0 = blockIdx.y * PF_TILE;
-    const int n0 = blockIdx.x * PF_TILE;
+    const int n0 = blockIdx.x * 16 * NU;
     const int N = a.W.N, K = a.W.K, M = a.M;
     const int ngrp = K / (32 * GB);
     // wave w reduces over scale groups [g_begin, g_end): the K range is split KS ways
@@ -132,14 +132,14 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(const PfGemmArgs a)
         ah[s] = (const TSD_GLOBAL half8*)glb(a.ahi) + t0;
         al[s] = (const TSD_GLOBAL half8*)glb(a.alo) + t0;
     }
-    const TSD_GLOBAL uint8_t* wp[2];
-    const TSD_GLOBAL _Float16* sp[2];
-    const TSD_GLOBAL _Float16* bp[2];
-    const TSD_GLOBAL uint32_t* hp[2];
-    const TSD_GLOBAL u32x4* tq[2];     // PF_TILED8: lane's 16 bytes of group 0 of its 16-row tile
-    const TSD_GLOBAL uint32_t* tsb[2]; // PF_TILED8: its (scale | bias << 16) word of group 0
+    const TSD_GLOBAL uint8_t* wp[NU];
+    const TSD_GLOBAL _Float16* sp[NU];
+    const TSD_GLOBAL _Float16* bp[NU];
+    const TSD_GLOBAL uint32_t* hp[NU];
+    const TSD_GLOBAL u32x4* tq[NU];     // PF_TILED8: lane's 16 bytes of group 0 of its 16-row tile
+    const TSD_GLOBAL uint32_t* tsb[NU]; // PF_TILED8: its (scale | bias << 16) word of group 0
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NU; ++u) {
         if constexpr (F == PF_TILED8) {
             const int t = min((n0 + 16 * u) / 16, (N - 1) / 16);   // lane row c of tile t (rows past N never stored)
             tq[u] = (const TSD_GLOBAL u32x4*)glb(a.T.q) + (size_t)t * ngrp * 64 + lane;
@@ -157,20 +157,20 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(const PfGemmArgs a)
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
 
-    float4v acc[2][2];
+    float4v acc[2][NU];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) acc[s][u] = float4v{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < NU; ++u) acc[s][u] = float4v{0.f, 0.f, 0.f, 0.f};
 
     // one stage: NG scale groups (NG * GB blocks), all loads issued before the first MFMA
     auto stage = [&](int g0, auto ng_tag) {
         constexpr int NG = decltype(ng_tag)::value;
         constexpr int NB = NG * GB;
         half8 xh[NB][2], xl[NB][2];
-        u32x2 wr[NB][2];
-        uint32_t hb[NB][2];
-        float sc[NG][2], bi[NG][2];
+        u32x2 wr[NB][NU];
+        uint32_t hb[NB][NU];
+        float sc[NG][NU], bi[NG][NU];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const int blk = g0 * GB + b;
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(const PfGemmArgs a)
             }
             if constexpr (F != PF_TILED8) {
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
+                for (int u = 0; u < NU; ++u) {
                     wr[b][u] = *(const TSD_GLOBAL u32x2*)(wp[u] + (size_t)blk * T::BLOCK_BYTES);
                     hb[b][u] = F == FMT_Q5_0 ? hp[u][blk] : 0u;
                 }
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(const PfGemmArgs a)
 #pragma unroll
             for (int q = 0; q < NG; ++q)
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
+                for (int u = 0; u < NU; ++u) {
                     const u32x4 v = tq[u][(size_t)(g0 + q) * 64];
                     wr[2 * q][u] = u32x2{v.x, v.y};
                     wr[2 * q + 1][u] = u32x2{v.z, v.w};
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(const PfGemmArgs a)
 #pragma unroll
         for (int q = 0; q < NG; ++q)
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
+            for (int u = 0; u < NU; ++u) {
                 if constexpr (F == PF_TILED8) {
                     const uint32_t sb = tsb[u][(size_t)(g0 + q) * 16];
                     sc[q][u] = (float)__builtin_bit_cast(_Float16, (uint16_t)(sb & 0xFFFFu));
@@ -213,25 +213,25 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(const PfGemmArgs a)
             }
 #pragma unroll
         for (int q = 0; q < NG; ++q) {
-            float4v P[2][2], X[2];
+            float4v P[2][NU], X[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 X[s] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int u = 0; u < 2; ++u) P[s][u] = float4v{0.f, 0.f, 0.f, 0.f};
+                for (int u = 0; u < NU; ++u) P[s][u] = float4v{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
             for (int bb = 0; bb < GB; ++bb) {
                 const int b = q * GB + bb;
-                half8 wv[2];
+                half8 wv[NU];
 #pragma unroll
-                for (int u = 0; u < 2; ++u) wv[u] = T::codes(wr[b][u], j, hb[b][u]);
+                for (int u = 0; u < NU; ++u) wv[u] = T::codes(wr[b][u], j, hb[b][u]);
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     const half8 hi = xh[b][s];
                     const half8 lo = xl[b][s];
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
+                    for (int u = 0; u < NU; ++u) {
                         P[s][u] = mfma(hi, wv[u], P[s][u]);
                         P[s][u] = mfma(lo, wv[u], P[s][u]);
                     }
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(const PfGemmArgs a)
                 }
             }
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
+            for (int u = 0; u < NU; ++u) {
                 const float d = sc[q][u];
                 const float b2 = T::AFF ? fmaf(T::ZERO, d, bi[q][u]) : 0.f;   // b + zero * s
 #pragma unroll
@@ -261,17 +261,17 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(const PfGemmArgs a)
     for (; g + SG <= g_end; g += SG) stage(g, std::integral_constant<int, SG>{});
     for (; g < g_end; ++g) stage(g, std::integral_constant<int, 1>{});
 
-    // the KS partial tiles summed in wave order (deterministic); wave w < 4 then finishes the
-    // 16 x 16 sub-tile (s, u) = (w & 1, w >> 1)
+    // the KS partial tiles summed in wave order (deterministic); wave w then finishes the
+    // 16 x 16 sub-tiles st = w, w + KS, .. of the 2 x NU, (s, u) = (st & 1, st >> 1)
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < NU; ++u)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) red[w][(s * 2 + u) * 4 + i][lane] = acc[s][u][i];
+            for (int i = 0; i < 4; ++i) red[w][(u * 2 + s) * 4 + i][lane] = acc[s][u][i];
     __syncthreads();
-    if (w >= 4) return;   // whole waves; no barrier follows
-    const int s = w & 1, u = w >> 1;
+    for (int st = w; st < 2 * NU; st += KS) {   // whole waves; no barrier follows
+    const int s = st & 1, u = st >> 1;
     // epilogue: lane holds weight row n = n0 + 16u + c for activation rows m0 + 16s + 4j + i
     {
         const int n = n0 + 16 * u + c;
@@ -279,9 +279,9 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(const PfGemmArgs a)
         {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float sum = red[0][(s * 2 + u) * 4 + i][lane];
+                float sum = red[0][st * 4 + i][lane];
 #pragma unroll
-                for (int q = 1; q < KS; ++q) sum += red[q][(s * 2 + u) * 4 + i][lane];
+                for (int q = 1; q < KS; ++q) sum += red[q][st * 4 + i][lane];
                 const int r = m0 + 16 * s + 4 * j + i;
                 const float v = sum + bias;
                 float partner = 0.f;
@@ -320,6 +320,7 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(const PfGemmArgs a)
                 }
             }
         }
+    }
     }
 }
 
@@ -535,25 +536,28 @@ __global__ __launch_bounds__(64) void k_pf_fattn(const PfAttnArgs a)
         for (int dt = 0; dt < DT; ++dt) put_hilo(a.ohi, a.olo, fl_index(r, h * HD + (4 * j + i) * DT + dt, a.ldo), o[dt][i] * il);
 }
 
-template <int F, int KS>
-hipError_t gemm_epi_ks(int epi, const PfGemmArgs& a, dim3 grid, hipStream_t st)
+template <int F, int KS, int NU>
+hipError_t gemm_epi_ks(int epi, const PfGemmArgs& a, hipStream_t st)
 {
+    const dim3 grid((a.W.N + 16 * NU - 1) / (16 * NU), (a.M + PF_TILE - 1) / PF_TILE);
     switch (epi) {
-    case PF_STORE: k_pf_gemm<F, PF_STORE, KS><<<grid, 64 * KS, 0, st>>>(a); break;
-    case PF_QKV: k_pf_gemm<F, PF_QKV, KS><<<grid, 64 * KS, 0, st>>>(a); break;
-    case PF_RESID: k_pf_gemm<F, PF_RESID, KS><<<grid, 64 * KS, 0, st>>>(a); break;
-    case PF_GELU: k_pf_gemm<F, PF_GELU, KS><<<grid, 64 * KS, 0, st>>>(a); break;
-    case PF_SWIGLU: k_pf_gemm<F, PF_SWIGLU, KS><<<grid, 64 * KS, 0, st>>>(a); break;
+    case PF_STORE: k_pf_gemm<F, PF_STORE, KS, NU><<<grid, 64 * KS, 0, st>>>(a); break;
+    case PF_QKV: k_pf_gemm<F, PF_QKV, KS, NU><<<grid, 64 * KS, 0, st>>>(a); break;
+    case PF_RESID: k_pf_gemm<F, PF_RESID, KS, NU><<<grid, 64 * KS, 0, st>>>(a); break;
+    case PF_GELU: k_pf_gemm<F, PF_GELU, KS, NU><<<grid, 64 * KS, 0, st>>>(a); break;
+    case PF_SWIGLU: k_pf_gemm<F, PF_SWIGLU, KS, NU><<<grid, 64 * KS, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-// long reductions split eight ways, the rest four ways
+// long reductions split eight ways, the rest four ways; very wide products (N >= 6144) give each wave
+// 64 columns (each activation fragment then feeds four MFMA tiles), the rest 32
 template <int F>
-hipError_t gemm_epi(int epi, const PfGemmArgs& a, dim3 grid, hipStream_t st)
+hipError_t gemm_epi(int epi, const PfGemmArgs& a, hipStream_t st)
 {
-    return a.W.K >= 2048 ? gemm_epi_ks<F, 8>(epi, a, grid, st) : gemm_epi_ks<F, 4>(epi, a, grid, st);
+    if (a.W.K >= 2048) return gemm_epi_ks<F, 8, 2>(epi, a, st);
+    return a.W.N >= 6144 ? gemm_epi_ks<F, 4, 4>(epi, a, st) : gemm_epi_ks<F, 4, 2>(epi, a, st);
 }
 
 }  // namespace
@@ -567,14 +571,13 @@ hipError_t launch_pf_gemm(int fmt, int epi, const PfGemmArgs& a, hipStream_t st)
 {
     if (!pf_gemm_ok(fmt, a.W.K) || a.M <= 0 || a.W.N <= 0) return hipErrorInvalidValue;
     if ((epi == PF_SWIGLU || epi == PF_QKV) && a.W.N % 2) return hipErrorInvalidValue;
-    const dim3 grid((a.W.N + PF_TILE - 1) / PF_TILE, (a.M + PF_TILE - 1) / PF_TILE);
     switch (fmt) {
-    case FMT_Q4_0: return gemm_epi<FMT_Q4_0>(epi, a, grid, st);
-    case FMT_Q8_0: return gemm_epi<FMT_Q8_0>(epi, a, grid, st);
-    case FMT_AFF8: return gemm_epi<FMT_AFF8>(epi, a, grid, st);
-    case FMT_Q5_0: return gemm_epi<FMT_Q5_0>(epi, a, grid, st);
-    case FMT_AFF4_G64: return gemm_epi<FMT_AFF4_G64>(epi, a, grid, st);
-    case FMT_AFF4_G32: return gemm_epi<FMT_AFF4_G32>(epi, a, grid, st);
+    case FMT_Q4_0: return gemm_epi<FMT_Q4_0>(epi, a, st);
+    case FMT_Q8_0: return gemm_epi<FMT_Q8_0>(epi, a, st);
+    case FMT_AFF8: return gemm_epi<FMT_AFF8>(epi, a, st);
+    case FMT_Q5_0: return gemm_epi<FMT_Q5_0>(epi, a, st);
+    case FMT_AFF4_G64: return gemm_epi<FMT_AFF4_G64>(epi, a, st);
+    case FMT_AFF4_G32: return gemm_epi<FMT_AFF4_G32>(epi, a, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -584,8 +587,7 @@ hipError_t launch_pf_gemm_tiled(int epi, const PfGemmArgs& a, hipStream_t st)
     if (a.M <= 0 || a.W.N <= 0 || a.W.K <= 0 || a.W.K % 64 || a.T.N != a.W.N || a.T.K != a.W.K)
         return hipErrorInvalidValue;
     if ((epi == PF_SWIGLU || epi == PF_QKV) && a.W.N % 2) return hipErrorInvalidValue;
-    const dim3 grid((a.W.N + PF_TILE - 1) / PF_TILE, (a.M + PF_TILE - 1) / PF_TILE);
-    return gemm_epi<PF_TILED8>(epi, a, grid, st);
+    return gemm_epi<PF_TILED8>(epi, a, st);
 }
 
 hipError_t launch_pf_embed(const PfRowArgs& a, hipStream_t st)

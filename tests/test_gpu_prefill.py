@@ -46,8 +46,8 @@ def dev(a):
 
 FORMATS = ["q4_0", "q8_0", "aff8", "q5_0", "aff4_g64", "aff4_g32"]
 # (N, K, M): one tile; ragged rows/columns over several tiles with a partial stage of blocks;
-# tall K; a single row
-SHAPES = [(5, 64, 3), (200, 192, 37), (256, 1024, 130), (96, 4096, 65), (130, 320, 1)]
+# tall K; a single row; a very wide product (64 columns per wave) with a ragged last tile
+SHAPES = [(5, 64, 3), (200, 192, 37), (256, 1024, 130), (96, 4096, 65), (130, 320, 1), (6150, 128, 40)]
 
 
 @pytest.mark.parametrize("N,K,M", SHAPES)

@@ -256,7 +256,9 @@ __global__ __launch_bounds__(64 * KS) void k_pf_gemm(const PfGemmArgs a)
             }
         }
     };
-    constexpr int SG = 4 / GB;   // groups per stage: four blocks of 32
+    // groups per stage: four blocks of 32, or one 64-group for the group-64 formats (their
+    // registers then leave room for four waves per SIMD, which the Talker's 512-row passes use)
+    constexpr int SG = GB == 2 ? 1 : 4;
     int g = g_begin;
     for (; g + SG <= g_end; g += SG) stage(g, std::integral_constant<int, SG>{});
     for (; g < g_end; ++g) stage(g, std::integral_constant<int, 1>{});

@@ -11,7 +11,9 @@ its line also carries "gemm_rows", the batched matrix-core GEMM alone on a matri
 the Infinity Cache.
 
 The line also carries "gemv": the standalone quantized GEMV on one 524288 x 1024 Q8_0 matrix
-(~570 MB, more than the Infinity Cache holds), where a launch is amortised.
+(~570 MB, more than the Infinity Cache holds), where a launch is amortised; and "prefill": the
+prompt (the prompt pass over every prompt position but the last, then one decode step) timed
+once under HIP events after an untimed first run.
 
 One step = one replay of the captured decode graph (every layer, the head and the greedy
 sampler); by default the graph holds one persistent launch that runs the whole step.  W warm-up

@@ -272,6 +272,46 @@ def test_full_size_step_over_long_cache(name, kv_pos, mode):
     say(f"  worst rel {worst:.2e}")
 
 
+@pytest.mark.parametrize("name,kv_pos,guided", [("gpt2_medium_q4_0", 755, True), ("llama520m_q8_0", 899, True),
+                                                 ("llama520m_q8_0", 899, False)])
+def test_full_size_pair_over_long_cache(name, kv_pos, guided):
+    """The persistent pair at the real shapes (each weight read once for both rows): two
+    teacher-forced steps over a random cache of kv_pos positions per row, both rows' logits as
+    one tensor at rel <= 2e-3; a guided pair (weight 1.5) draws one id from the combined logits
+    and both rows take it, two streams pick their own argmax."""
+    cfg = dict(synth.config(name), batch=2)
+    samp = dict(mode=0, cfg=1, cfg_weight=1.5) if guided else None
+    if guided:
+        cfg.update(cfg=1, cfg_weight=1.5)
+    say(f"[model-full] {name} pair guided={guided} kv_pos={kv_pos}")
+    w = synth.model_weights(cfg, 42)
+    from quantized_gemv_kv_amd import Model
+    gm = Model(dict(cfg, launch_mode="persistent"), w, sampling=samp)
+    assert gm.uses_persistent_step()
+    om = oracle.OracleModel(cfg, w)
+    k, v = synth.kv_cache(cfg, kv_pos, seed=5)
+    om.load_kv(k, v, kv_pos)
+    gm.load_kv(dev(k), dev(v), kv_pos)
+    nxt = synth.prompt_tokens(cfg, 1, seed=6)[:, 0, :]
+    for s in range(2):
+        o_ids = om.step(nxt)
+        g_ids = gm.step(dev(nxt)).cpu().numpy()
+        lo, lg = om.logits(), gm.logits().cpu().numpy()
+        r = rel_err(lg, lo)
+        say(f"  step {s}: rel {r:.2e}")
+        assert r <= REL_TOL
+        if guided:
+            comb = lo[0] + 1.5 * (lo[0] - lo[1])
+            assert int(g_ids[0, 0]) == int(g_ids[1, 0])
+            assert ids_agree(g_ids[0, 0], comb), (g_ids, o_ids, top2_gap(comb))
+        else:
+            for b in range(2):
+                assert ids_agree(g_ids[b, 0], lo[b]), (b, g_ids, o_ids)
+        nxt = o_ids
+    gm.synchronize()
+    gm.close()
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_full_size_gpt2_q5_0_step_over_long_cache(mode):
     """The GPT-2-Medium-shaped T3 in Q5_0 (q ~ U{0..31}, d = |N| 0.02) at the decode run's last

@@ -228,7 +228,8 @@ tsd_status tsd_get_tokens(tsd_model* m, int first, int n, int32_t* d_out);
 tsd_status tsd_load_kv(tsd_model* m, const uint16_t* d_k, const uint16_t* d_v, int n_pos);
 
 /* Copy the (Talker) KV cache of positions 0..n_pos-1 (n_pos <= n_past) out to d_k/d_v, laid out
- * as tsd_load_kv takes it: [n_layer][batch][n_kv_head][n_pos][head_dim] fp16 (device). */
+ * as tsd_load_kv takes it: [n_layer][batch][n_kv_head][n_pos][head_dim] fp16 (device).
+ * n_pos = 0 copies nothing (d_k/d_v may then be null); n_pos > n_past is TSD_ERR_INVALID_ARGUMENT. */
 tsd_status tsd_get_kv(tsd_model* m, uint16_t* d_k, uint16_t* d_v, int n_pos);
 
 /* One main decoder layer on hidden states d_x [batch][d_model] at position pos: writes that

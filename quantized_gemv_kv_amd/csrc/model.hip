@@ -967,10 +967,11 @@ tsd_status tsd_load_kv(tsd_model* m, const uint16_t* d_k, const uint16_t* d_v, i
 
 tsd_status tsd_get_kv(tsd_model* m, uint16_t* d_k, uint16_t* d_v, int n_pos)
 {
-    if (!m || !d_k || !d_v) return fail(m, TSD_ERR_INVALID_ARGUMENT, "null argument");
+    if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
     const tsd_config& c = m->c;
     if (n_pos < 0 || n_pos > m->n_past) return fail(m, TSD_ERR_INVALID_ARGUMENT, "n_pos outside 0..n_past");
     if (n_pos > 0) {
+        if (!d_k || !d_v) return fail(m, TSD_ERR_INVALID_ARGUMENT, "null argument");
         const size_t w = (size_t)n_pos * c.head_dim * 2, sp = (size_t)c.n_ctx * c.head_dim * 2;
         const size_t rows = (size_t)c.n_layer * c.batch * c.n_kv_head;
         HIP_TRY(m, hipMemcpy2DAsync(d_k, w, m->kc, sp, w, rows, hipMemcpyDeviceToDevice, m->st), "get k");

@@ -376,6 +376,15 @@ def test_errors_leave_state_unchanged():
         gm.prefill(dev(synth.prompt_tokens(cfg, 7)))
     assert e.value.status == 4                     # TSD_ERR_CONTEXT_FULL
     assert gm.n_past == 10
+    with pytest.raises(TsdError) as e:
+        gm.prefill_stepwise(dev(synth.prompt_tokens(cfg, 7)))
+    assert e.value.status == 4
+    assert gm.n_past == 10
+    with pytest.raises(TsdError) as e:
+        gm.get_kv(11)                              # beyond what the cache holds
+    assert e.value.status == 1
+    k, v = gm.get_kv(0)
+    assert k.shape[3] == 0 and v.shape[3] == 0
     with pytest.raises(TsdError):
         gm.truncate(11)
     gm.truncate(3)

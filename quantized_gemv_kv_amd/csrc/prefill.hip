@@ -339,8 +339,24 @@ __device__ __forceinline__ float row_sum(float v, float* red)
     return ((red[0] + red[1]) + red[2]) + red[3];
 }
 
+// The gain and bias of the thread's elements k = t + PF_NT i, each load issued unconditionally
+// (clamped into the row) and before the row's reductions, so that they are in flight together with
+// the row itself rather than one round trip each behind the reductions.
+__device__ __forceinline__ void load_gain(const PfRowArgs& a, float (&gg)[PF_MAXV], float (&bb)[PF_MAXV])
+{
+    const int t = threadIdx.x, d = a.d;
+    const float* bsrc = a.bn ? a.bn : a.g;
+#pragma unroll
+    for (int i = 0; i < PF_MAXV; ++i) {
+        const int k = min(t + i * PF_NT, d - 1);
+        gg[i] = a.g[k];
+        bb[i] = bsrc[k];
+    }
+}
+
 // LayerNorm (bn set) or RMSNorm of the row held in v, written to the operand row r
-__device__ void norm_to_operand(const PfRowArgs& a, int r, const float (&v)[PF_MAXV], float* red)
+__device__ void norm_to_operand(const PfRowArgs& a, int r, const float (&v)[PF_MAXV], const float (&gg)[PF_MAXV],
+                                const float (&bb)[PF_MAXV], float* red)
 {
     const int t = threadIdx.x, d = a.d;
     const float invd = 1.0f / (float)d;
@@ -360,8 +376,8 @@ __device__ void norm_to_operand(const PfRowArgs& a, int r, const float (&v)[PF_M
     for (int i = 0; i < PF_MAXV; ++i) {
         const int k = t + i * PF_NT;
         if (k < d) {
-            float y = (v[i] - mean) * rs * a.g[k];
-            if (a.bn) y += a.bn[k];
+            float y = (v[i] - mean) * rs * gg[i];
+            if (a.bn) y += bb[i];
             put_hilo(a.ahi, a.alo, fl_index(r, k, d), y);
         }
     }
@@ -380,32 +396,46 @@ __global__ __launch_bounds__(PF_NT) void k_pf_embed(const PfRowArgs a)
         // the history at a prompt position holds the id that follows it (the next prompt id)
         if (a.hist && a.t0 + tt + 1 < a.n_prompt) a.hist[(size_t)p * a.B + b] = min(max(tr[a.n_tab], 0), a.tab_rows[0] - 1);
     }
+    float gg[PF_MAXV], bb[PF_MAXV];
+    load_gain(a, gg, bb);
     __syncthreads();
+    // the sum over the tables in table order, then the learned position; each table's loads are
+    // issued together (clamped into the row; elements past it are dropped below)
     float v[PF_MAXV];
+#pragma unroll
+    for (int i = 0; i < PF_MAXV; ++i) v[i] = 0.f;
+    for (int c = 0; c < a.n_tab; ++c) {
+        const float* er = a.tab[c] + (size_t)ids[c] * d;
+#pragma unroll
+        for (int i = 0; i < PF_MAXV; ++i) v[i] += er[min(t + i * PF_NT, d - 1)];
+    }
+    if (a.wpe) {
+        const float* pr = a.wpe + (size_t)p * d;
+#pragma unroll
+        for (int i = 0; i < PF_MAXV; ++i) v[i] += pr[min(t + i * PF_NT, d - 1)];
+    }
 #pragma unroll
     for (int i = 0; i < PF_MAXV; ++i) {
         const int k = t + i * PF_NT;
-        v[i] = 0.f;
-        if (k < d) {
-            for (int c = 0; c < a.n_tab; ++c) v[i] += a.tab[c][(size_t)ids[c] * d + k];
-            if (a.wpe) v[i] += a.wpe[(size_t)p * d + k];
-            a.x_out[(size_t)r * d + k] = v[i];
-        }
+        if (k < d) a.x_out[(size_t)r * d + k] = v[i];
+        else v[i] = 0.f;
     }
-    norm_to_operand(a, r, v, red);
+    norm_to_operand(a, r, v, gg, bb, red);
 }
 
 __global__ __launch_bounds__(PF_NT) void k_pf_norm(const PfRowArgs a)
 {
     __shared__ float red[4];
     const int r = blockIdx.x, t = threadIdx.x, d = a.d;
-    float v[PF_MAXV];
+    float v[PF_MAXV], gg[PF_MAXV], bb[PF_MAXV];
 #pragma unroll
     for (int i = 0; i < PF_MAXV; ++i) {
         const int k = t + i * PF_NT;
-        v[i] = k < d ? a.x[(size_t)r * d + k] : 0.f;
+        const float x = a.x[(size_t)r * d + min(k, d - 1)];
+        v[i] = k < d ? x : 0.f;
     }
-    norm_to_operand(a, r, v, red);
+    load_gain(a, gg, bb);
+    norm_to_operand(a, r, v, gg, bb, red);
 }
 
 // rows [M, Mpad) of the last tile are written as zeros

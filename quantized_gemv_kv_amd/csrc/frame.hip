@@ -361,10 +361,23 @@ constexpr int RP = MM_MAX_K / 256;   // elements per thread
 
 // id0 >= 0: the id of table 0 (ROW_EMB), else read from codes.  Rows b >= B write zeros.
 // red: 4 floats of LDS; ids: 16 ints of LDS
+// Every load is issued unconditionally (clamped into the row) ahead of its first use: the gains
+// before the row's reduction, the embedding rows four tables at a time (summed in table order), so
+// that a row costs a few memory round trips rather than one per element.
 __device__ void row_prep(const RowPrep& p, int b, int id0, float* red, int* ids)
 {
     const int t = threadIdx.x, K = p.K;
     const bool live = b < p.B;
+    auto col = [&](int i) { return min(t + 256 * i, K - 1); };
+    float gs[RP], ga[RP];   // the ROW_NORMED gain and the operand's gain
+    if (p.src == ROW_NORMED) {
+#pragma unroll
+        for (int i = 0; i < RP; ++i) gs[i] = glb(p.g_src)[col(i)];
+    }
+    if (p.g) {
+#pragma unroll
+        for (int i = 0; i < RP; ++i) ga[i] = glb(p.g)[col(i)];
+    }
     float v[RP];
 #pragma unroll
     for (int i = 0; i < RP; ++i) v[i] = 0.f;
@@ -377,22 +390,30 @@ __device__ void row_prep(const RowPrep& p, int b, int id0, float* red, int* ids)
     }
     if (live) {
         if (p.src == ROW_EMB) {
+            constexpr int TG = 4;   // tables per round
+            for (int c0 = 0; c0 < p.n_tab; c0 += TG) {
+                float e[TG][RP];
 #pragma unroll
-            for (int i = 0; i < RP; ++i) {
-                const int k = t + 256 * i;
-                if (k < K) {
-                    float s = 0.f;
-                    for (int c = 0; c < p.n_tab; ++c) s += glb(p.tab[c])[(size_t)ids[c] * K + k];
-                    v[i] = s;
+                for (int u = 0; u < TG; ++u) {
+                    const int c = min(c0 + u, p.n_tab - 1);
+                    const auto row = glb(p.tab[c]) + (size_t)ids[c] * K;
+#pragma unroll
+                    for (int i = 0; i < RP; ++i) e[u][i] = row[col(i)];
                 }
+#pragma unroll
+                for (int u = 0; u < TG; ++u)
+                    if (c0 + u < p.n_tab)
+#pragma unroll
+                        for (int i = 0; i < RP; ++i) v[i] += e[u][i];
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < RP; ++i) {
-                const int k = t + 256 * i;
-                if (k < K) v[i] = p.src == ROW_MAJOR ? glb(p.rows_src)[(size_t)b * K + k] : glb(p.rows_src)[il_x(b, k)];
-            }
+            for (int i = 0; i < RP; ++i)
+                v[i] = p.src == ROW_MAJOR ? glb(p.rows_src)[(size_t)b * K + col(i)] : glb(p.rows_src)[il_x(b, col(i))];
         }
+#pragma unroll
+        for (int i = 0; i < RP; ++i)
+            if (t + 256 * i >= K) v[i] = 0.f;
     }
     if (p.src == ROW_NORMED) {   // uniform over the workgroup
         float q2 = 0.f;
@@ -400,10 +421,7 @@ __device__ void row_prep(const RowPrep& p, int b, int id0, float* red, int* ids)
         for (int i = 0; i < RP; ++i) q2 = fmaf(v[i], v[i], q2);
         const float r = 1.0f / sqrtf(block_sum256(q2, red) / (float)K + p.eps);
 #pragma unroll
-        for (int i = 0; i < RP; ++i) {
-            const int k = t + 256 * i;
-            if (k < K) v[i] *= glb(p.g_src)[k] * r;
-        }
+        for (int i = 0; i < RP; ++i) v[i] *= gs[i] * r;
     }
     float q2 = 0.f;
 #pragma unroll
@@ -411,7 +429,7 @@ __device__ void row_prep(const RowPrep& p, int b, int id0, float* red, int* ids)
         const int k = t + 256 * i;
         if (k >= K) continue;
         if (p.x && live) glb(p.x)[il_x(b, k)] = v[i];
-        put_hilo(p.act, il_act(b, k), p.g ? v[i] * glb(p.g)[k] : v[i]);
+        put_hilo(p.act, il_act(b, k), p.g ? v[i] * ga[i] : v[i]);
         q2 = fmaf(v[i], v[i], q2);
     }
     if (p.ssq) {

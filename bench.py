@@ -339,8 +339,8 @@ def gemm_rows_headline(seed, reps=7):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode step is not sharded "
-              f"across GPUs in this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library runs the decode step "
+              f"on a single GPU and does not shard it.", file=sys.stderr)
         sys.exit(2)
     import torch
     from quantized_gemv_kv_amd import Model, roofline, synth

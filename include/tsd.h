@@ -48,7 +48,7 @@ extern "C" {
 typedef enum {
     TSD_OK = 0,
     TSD_ERR_INVALID_ARGUMENT = 1, /* null/undersized buffer, bad shape, token >= vocab */
-    TSD_ERR_UNSUPPORTED = 2,      /* a valid configuration this build has no kernel for */
+    TSD_ERR_UNSUPPORTED = 2,      /* a valid configuration the library has no kernel for */
     TSD_ERR_OUT_OF_MEMORY = 3,    /* host allocation failed */
     TSD_ERR_CONTEXT_FULL = 4,     /* n_past + n > n_ctx */
     TSD_ERR_HIP = 5,              /* a HIP runtime call failed; message has hipGetErrorString */

@@ -37,6 +37,26 @@ __device__ __forceinline__ void store_bits(uint64_t* p, uint32_t bits, uint32_t 
 __device__ __forceinline__ bool ready(uint64_t w, uint32_t epoch) { return (uint32_t)(w >> 32) == epoch; }
 __device__ __forceinline__ float value(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
+// 32-bit words, for a hand-over whose values are used once and never accumulated: the value
+// rounded to nearest even at 15 mantissa bits (relative error <= 2^-16) in the high 24 bits, and
+// in the low 8 bits a tag 1 + epoch mod 255 of its epoch, never 0, so zeroed words never match.
+// Every launch rewrites each slot, and the epochs of two successive writes of one slot never
+// differ by a multiple of 255 (a launch spans 5 L + 1 epochs, phases of one slot 5 apart), so a
+// stale word cannot carry the tag a reader waits for.  Half the bytes of the 64-bit word.
+__device__ __forceinline__ uint32_t tag8(uint32_t epoch) { return 1u + epoch % 255u; }
+__device__ __forceinline__ uint32_t load(const uint32_t* p)
+{
+    return __hip_atomic_load(glb(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store32(uint32_t* p, float v, uint32_t epoch)
+{
+    uint32_t u = __float_as_uint(v);
+    u = (u + 0x7Fu + ((u >> 8) & 1u)) & ~0xFFu;
+    __hip_atomic_store(glb(p), u | tag8(epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool ready(uint32_t w, uint32_t epoch) { return (w & 0xFFu) == tag8(epoch); }
+__device__ __forceinline__ float value(uint32_t w) { return __uint_as_float(w & ~0xFFu); }
+
 // the bounded-wait bookkeeping of one poll loop
 struct Deadline {
     long long t0;
@@ -117,8 +137,8 @@ __device__ __forceinline__ bool settle_all(uint64_t (&w)[N], Addr addr, Use use,
 // loop is uniform over the wave: while any lane still sees a stale word, every lane re-loads
 // all n (one memory round trip per round, no per-word or per-lane branch).  Returns false on
 // time-out.
-template <int N, class Addr>
-__device__ __forceinline__ bool settle_n(uint64_t (&w)[N], int n, Addr addr, uint32_t epoch, long long limit,
+template <int N, class W, class Addr>
+__device__ __forceinline__ bool settle_n(W (&w)[N], int n, Addr addr, uint32_t epoch, long long limit,
                                          const uint32_t* abort_word)
 {
     auto lane_ready = [&]() {

@@ -45,7 +45,7 @@ constexpr int KTILE = 64;    // keys per wave in the attention phase (4 waves: o
 constexpr int SG = 4;        // attention chunks merged per exchange round in the O-proj input
 
 enum { A_GPT2 = 0, A_LLAMA = 1 };
-enum { IN_XCHG = 0, IN_NORM = 1, IN_EMB_NORM = 2, IN_ATTN = 3 };
+enum { IN_XCHG = 0, IN_NORM = 1, IN_EMB_NORM = 2, IN_ATTN = 3, IN_XCHG32 = 4 };
 enum { OUT_QKV = 0, OUT_QKV_ROPE = 1, OUT_RESID = 2, OUT_GELU = 3, OUT_SWIGLU = 4, OUT_HEAD = 5 };
 
 constexpr int slices_for(int fmt_e, int K) { return K / fmt_e > 64 ? K / fmt_e / 64 : 1; }
@@ -110,6 +110,7 @@ struct Ctx {
 //   IN_NORM     the same, then LayerNorm (gain g, bias bt) or RMSNorm (gain g) per row
 //   IN_EMB_NORM the embedding row of the row's input token (+ the learned position row), then the norm
 //   IN_ATTN     the attention output, merged from the per-chunk partials src[b * xs + (h*max_split+s)*(hd+2)]
+//   IN_XCHG32   32-bit exchange words ((uint32_t*)(src + b * xs))[k] (the FC / SwiGLU output)
 template <int NS>
 __device__ __forceinline__ void block_sums(float (&v)[NS], float* red)   // NS sums, one pair of barriers
 {
@@ -227,6 +228,20 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
         for (int b = 0; b < B; ++b)
 #pragma unroll
             for (int j = 0; j < J; ++j) v[b][j] = __fdividef(Or[b][j], Lr[b][j]);
+    } else if constexpr (IN == IN_XCHG32) {
+        constexpr int NW = B * J;
+        auto addr = [&](int q) -> const uint32_t* {
+            const int b = q / J, j = q - b * J;
+            return (const uint32_t*)(src + b * xs) + elem(j);
+        };
+        uint32_t w[NW];
+#pragma unroll
+        for (int q = 0; q < NW; ++q) w[q] = xchg::load(addr(q));
+        ok = xchg::settle_n(w, NW, addr, ep, cx.limit, a.abort_word);
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int j = 0; j < J; ++j) v[b][j] = xchg::value(w[b * J + j]);
     } else {
         // per row: words 0..J-1 this thread's elements, word J element 0 (the LayerNorm shift)
         constexpr int NR = J + (LN ? 1 : 0), NW = B * NR;
@@ -510,7 +525,7 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
                 uint64_t* dst = io.dst + b * io.dst_xs;
                 if (eon && erow < N) {
                     if constexpr (OUT == OUT_SWIGLU) {
-                        xchg::store(dst + (erow >> 1), silu(t0) * t1, io.dst_ep);
+                        xchg::store32((uint32_t*)dst + (erow >> 1), silu(t0) * t1, io.dst_ep);
                     } else {
                         // rows (2m, 2m+1) = elements (i, i + hd/2) of a Q or K head, or (2m, 2m+1) of V
                         constexpr int half = HD / 2;
@@ -564,7 +579,7 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
                     } else if constexpr (OUT == OUT_RESID) {
                         xchg::store(dst + erow, t + re[b], io.dst_ep);
                     } else if constexpr (OUT == OUT_GELU) {
-                        xchg::store(dst + erow, gelu_tanh(t), io.dst_ep);
+                        xchg::store32((uint32_t*)dst + erow, gelu_tanh(t), io.dst_ep);
                     }
                 }
             }
@@ -891,7 +906,7 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
             io.res = a.x_attn;
             io.res_xs = a.xs_d;
             io.res_ep = e + 2u;
-            if (!gemv_phase<C, C::FF, C::D, C::NL_F, IN_XCHG, OUT_RESID, false>(a, cx, shift(a.L0.down, o), io, sm))
+            if (!gemv_phase<C, C::FF, C::D, C::NL_F, IN_XCHG32, OUT_RESID, false>(a, cx, shift(a.L0.down, o), io, sm))
                 return give_up(a);
         }
     }

@@ -448,7 +448,10 @@ __global__ __launch_bounds__(256) void k_pf_split(const float* __restrict__ x, i
 }
 
 // ---- causal attention over the cache (matrix cores) -------------------------------------------
-// One wave per (batch row, 16 consecutive queries, head).  Per block of 32 keys:
+constexpr int PF_ATTN_WAVES = 4;
+// One workgroup of PF_ATTN_WAVES waves per (batch row, 16 consecutive queries, head); wave w takes
+// the key blocks w, w + PF_ATTN_WAVES, .. (so the last query tiles, which see the most keys, are
+// not one long chain), and wave 0 merges the waves' running (max, sum, O^T).  Per block of 32 keys:
 //   S^T = K Q^T          A = 16 keys (lane row = key), B = Q^T (lane column = query c), K-dim =
 //                        head dims; q enters as fp16 hi/lo (scaled to the log2 domain), keys exact
 //   running max / sum    per query c over its 8 keys in the lane and the 4 lane groups
@@ -471,13 +474,13 @@ __device__ __forceinline__ float group4_sum(float v)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int HD>
-__global__ __launch_bounds__(64) void k_pf_fattn(const PfAttnArgs a)
+template <int HD, int NW>
+__global__ __launch_bounds__(64 * NW) void k_pf_fattn(const PfAttnArgs a)
 {
     constexpr int NC = HD / 32;   // K-dim chunks of S^T
     constexpr int DT = HD / 16;   // dim tiles of O^T
     typedef _Float16 halfDT __attribute__((ext_vector_type(DT)));
-    const int lane = threadIdx.x, c = lane & 15, j = lane >> 4;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 15, j = lane >> 4;
     const int ntile = (a.n_pos + 15) / 16;
     const int b = blockIdx.x / ntile, t0 = (blockIdx.x - b * ntile) * 16;
     const int h = blockIdx.y, g = h / (a.H / a.Hkv);
@@ -506,7 +509,7 @@ __global__ __launch_bounds__(64) void k_pf_fattn(const PfAttnArgs a)
     for (int dt = 0; dt < DT; ++dt) o[dt] = float4v{0.f, 0.f, 0.f, 0.f};
     float mx = -INFINITY, l = 0.f;   // query c's running max and sum (the same in its 4 lanes)
 
-    for (int k0 = 0; k0 <= plast; k0 += 32) {
+    for (int k0 = 32 * w; k0 <= plast; k0 += 32 * NW) {   // wave w: key blocks w, w + NW, ..
         // keys of this lane's operand rows / probability slots (clamped reads, masked below)
         float4v st[2];
 #pragma unroll
@@ -536,13 +539,16 @@ __global__ __launch_bounds__(64) void k_pf_fattn(const PfAttnArgs a)
             sv[e] = key <= pq ? st[e >> 2][e & 3] : -INFINITY;
             ml = fmaxf(ml, sv[e]);
         }
-        const float mn = fmaxf(mx, group4_max(ml));   // finite: key 0 is in the first block
-        const float alpha = exp2f(mx - mn);          // 0 on the first block
+        const float mn = fmaxf(mx, group4_max(ml));
+        // -inf while this wave has seen no key of query c (its blocks start past the query): a zero
+        // reference keeps every weight at 0 instead of exp2(-inf + inf)
+        const float mref = mn == -INFINITY ? 0.f : mn;
+        const float alpha = exp2f(mx - mref);        // 0 on the wave's first block
         half8 ph, pl;
         float ps = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float p = exp2f(sv[e] - mn);
+            const float p = exp2f(sv[e] - mref);
             ps += p;
             const _Float16 hi = (_Float16)p;
             ph[e] = hi;
@@ -558,6 +564,37 @@ __global__ __launch_bounds__(64) void k_pf_fattn(const PfAttnArgs a)
             o[dt] = o[dt] * alpha;
             o[dt] = mfma(va, ph, o[dt]);
             o[dt] = mfma(va, pl, o[dt]);
+        }
+    }
+    if constexpr (NW > 1) {
+        // the waves' (O^T, max, sum) merged by wave 0: every wave holds the same (query, dim) in the
+        // same lane and register, so the merge is elementwise per lane
+        __shared__ float xo[NW - 1][4 * DT + 2][64];
+        if (w > 0) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xo[w - 1][4 * dt + i][lane] = o[dt][i];
+            xo[w - 1][4 * DT][lane] = mx;
+            xo[w - 1][4 * DT + 1][lane] = l;
+        }
+        __syncthreads();
+        if (w > 0) return;
+        float M = mx;   // finite: wave 0's first block holds key 0
+#pragma unroll
+        for (int u = 0; u < NW - 1; ++u) M = fmaxf(M, xo[u][4 * DT][lane]);
+        const float s0 = exp2f(mx - M);
+        l *= s0;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] = o[dt] * s0;
+#pragma unroll
+        for (int u = 0; u < NW - 1; ++u) {
+            const float su = exp2f(xo[u][4 * DT][lane] - M);   // 0 for a wave that saw no key
+            l = fmaf(xo[u][4 * DT + 1][lane], su, l);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[dt][i] = fmaf(xo[u][4 * dt + i][lane], su, o[dt][i]);
         }
     }
     if (t0 + c >= a.n_pos) return;
@@ -650,8 +687,8 @@ hipError_t launch_pf_attention(const PfAttnArgs& a, hipStream_t st)
     if (a.M <= 0 || a.Hkv <= 0 || a.H % a.Hkv) return hipErrorInvalidValue;
     if (a.M % a.n_pos) return hipErrorInvalidValue;
     const dim3 grid((a.M / a.n_pos) * ((a.n_pos + 15) / 16), a.H);
-    if (a.hd == 64) k_pf_fattn<64><<<grid, 64, 0, st>>>(a);
-    else if (a.hd == 128) k_pf_fattn<128><<<grid, 64, 0, st>>>(a);
+    if (a.hd == 64) k_pf_fattn<64, PF_ATTN_WAVES><<<grid, 64 * PF_ATTN_WAVES, 0, st>>>(a);
+    else if (a.hd == 128) k_pf_fattn<128, PF_ATTN_WAVES><<<grid, 64 * PF_ATTN_WAVES, 0, st>>>(a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

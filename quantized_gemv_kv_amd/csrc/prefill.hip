@@ -620,13 +620,16 @@ hipError_t gemm_epi_ks(int epi, const PfGemmArgs& a, hipStream_t st)
     return hipGetLastError();
 }
 
-// long reductions split eight ways, the rest four ways; very wide products (N >= 6144) give each wave
-// 64 columns (each activation fragment then feeds four MFMA tiles), the rest 32
+// long reductions split eight ways, the rest four ways; very wide products (N >= 6144), and Q8_0
+// products from 2048 rows, give each wave 64 columns (each activation fragment then feeds four MFMA
+// tiles), the rest 32 (measured per format: the 4-bit and tiled 8-bit products lose parallelism
+// there faster than they gain operand reuse)
 template <int F>
 hipError_t gemm_epi(int epi, const PfGemmArgs& a, hipStream_t st)
 {
     if (a.W.K >= 2048) return gemm_epi_ks<F, 8, 2>(epi, a, st);
-    return a.W.N >= 6144 ? gemm_epi_ks<F, 4, 4>(epi, a, st) : gemm_epi_ks<F, 4, 2>(epi, a, st);
+    const bool wide = a.W.N >= 6144 || (F == FMT_Q8_0 && a.W.N >= 2048);
+    return wide ? gemm_epi_ks<F, 4, 4>(epi, a, st) : gemm_epi_ks<F, 4, 2>(epi, a, st);
 }
 
 }  // namespace

@@ -19,7 +19,7 @@
 namespace tsd {
 
 constexpr int PF_TILE = 32;            // rows and columns of a product tile (one workgroup)
-constexpr int PF_MAX_ROWS = 512;       // rows one pass of the prompt holds (larger prompts are chunked)
+constexpr int PF_MAX_ROWS = 4096;      // rows one pass of the prompt holds (larger prompts are chunked)
 
 enum PfEpi : int {
     PF_STORE = 0,    // y[r][n] = acc (+ bias[n])

@@ -29,8 +29,9 @@ def test_every_declared_symbol_is_exported():
 def test_workspace_sizes_and_validation():
     c3 = synth.config("gpt2_medium_q4_0")
     n = binding.tsd_workspace_bytes(c3)
-    # packed weights + fp16 cache + embedding tables fit in a few hundred MB
-    assert 300e6 < n < 340e6
+    # packed weights + fp16 cache + embedding tables + the prompt pass's row buffers (up to 4,096
+    # rows) fit in a few hundred MB
+    assert 300e6 < n < 380e6
     for bad, status in [(dict(c3, d_model=1000), 1), (dict(c3, n_head=15), 1), (dict(c3, head_dim=32, n_head=32, n_kv_head=32), 2),
                         (dict(c3, batch=3), 2), (dict(c3, wfmt="aff8", d_ff=4000), 1)]:
         with pytest.raises(binding.TsdError) as e:

@@ -12,7 +12,7 @@ likewise on its tiled weights) against the CPU oracle, through the C ABI.
   steps (rel <= 2e-3, ids as in the other model tests);
 * the causal mask ([J] §3.11): changing the ids after position i leaves every cached key and
   value at positions <= i bit for bit unchanged;
-* prompts longer than one pass (chunks of 512 rows), prompts after decoded positions, one-id
+* prompts longer than one pass (chunks of 4,096 rows), prompts after decoded positions, one-id
   prompts, two batch rows, the Talker at batch 2 and 16, and the prompt pass against the
   stepwise prefill at full size (C3, C4, C5).
 """
@@ -176,21 +176,21 @@ def test_prompt_continues_after_decoding(mode):
 
 
 def test_prompt_longer_than_one_pass():
-    """600 ids: a 512-row pass, an 87-row pass, the decode step."""
-    cfg = synth.small_config("llama", "q4_0", d_ff=256, n_ctx=640, vocab=500)
-    say("[prefill] 600 ids in two passes")
+    """4,150 ids: a 4,096-row pass, a 53-row pass, the decode step."""
+    cfg = synth.small_config("llama", "q4_0", d_ff=256, n_ctx=4160, vocab=500)
+    say("[prefill] 4150 ids in two passes")
     w = synth.model_weights(cfg, 3, norm_std=0.5)
-    check_prompt(cfg, w, [600], n_steps=2)
+    check_prompt(cfg, w, [4150], n_steps=2)
 
 
 @pytest.mark.parametrize("arch,fmt", [("gpt2", "q4_0"), ("llama", "q8_0")])
 def test_prompt_two_rows(arch, fmt):
-    """Batch 2, a different prompt per row, 300 positions each: 600 rows in passes of 256
-    positions."""
-    cfg = synth.small_config(arch, fmt, batch=2, d_ff=256, n_ctx=320, vocab=500)
+    """Batch 2, a different prompt per row, 2,100 positions each: 4,200 rows in passes of
+    2,048 positions (4,096 rows) and 51."""
+    cfg = synth.small_config(arch, fmt, batch=2, d_ff=256, n_ctx=2112, vocab=500)
     say(f"[prefill] batch 2 {arch} {fmt}")
     w = synth.model_weights(cfg, 5, norm_std=0.5)
-    check_prompt(cfg, w, [300], n_steps=2, mode="per_operator")
+    check_prompt(cfg, w, [2100], n_steps=2, mode="per_operator")
 
 
 def test_causal_mask_leaves_earlier_positions_unchanged():

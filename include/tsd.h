@@ -171,7 +171,7 @@ tsd_status tsd_model_create(const tsd_config* cfg, const tsd_tensor* weights, in
 
 /* Prefill ([J] §3.2: a prompt graph and a decode graph over one persistent KV cache; §3.11: the
  * prompt graph masks every key after its query's position).  Positions n_past .. n_past + n - 2
- * run as one causal prompt pass (matrix-core products over all their rows, chunks of up to 512
+ * run as one causal prompt pass (matrix-core products over all their rows, chunks of up to 4096
  * rows of batch x positions; for TALKER_CP the Talker only, on the sums of each frame's code
  * embeddings), the last position as one decode step (head, sampler, history; for TALKER_CP the
  * whole frame).  d_tokens is [batch][n][tokens per position] (1, or n_codebooks for TALKER_CP);

@@ -9,6 +9,12 @@
  * General conventions
  *   - Every function returns tsd_status; 0 (TSD_OK) is success.  No C++ exception crosses the
  *     ABI.  On any error the model state is unchanged and tsd_last_error() describes it.
+ *   - Token ids live in device memory, so they are checked on the device: an id outside its
+ *     vocabulary (token or code 0: [0, vocab); TALKER_CP codes 1..C-1: [0, cp_vocab)) makes that
+ *     call, and every model call after it, do nothing (no position, id, history or logit
+ *     changes), and the next tsd_synchronize returns TSD_ERR_INVALID_ARGUMENT, resets n_past to
+ *     what it was before the rejected call, and lets the model run again.  Until then tsd_n_past
+ *     counts the skipped calls as if they had run.
  *   - Pointers named d_* are device pointers (HIP global memory) owned by the caller.  The
  *     library never allocates device memory for tensors: all model state lives in the
  *     caller's workspace.  (Creating the step graph lets the HIP runtime allocate its own
@@ -179,8 +185,10 @@ tsd_status tsd_model_create(const tsd_config* cfg, const tsd_tensor* weights, in
  * position.  The token history (tsd_get_tokens) at a GPT2/LLAMA prompt position before the last
  * holds the next prompt id (TALKER_CP prompt frames leave it alone).  The cached keys and values
  * agree with tsd_prefill_stepwise's to fp32 rounding (the sums run in another order), not bit
- * for bit.  TSD_ERR_CONTEXT_FULL if n_past + n > n_ctx.  Tokens are
- * not range-checked on the device: an id outside its vocabulary is clamped into range. */
+ * for bit.  TSD_ERR_CONTEXT_FULL if n_past + n > n_ctx.  Every id of the prompt is checked on the
+ * device before the pass: one outside its vocabulary voids the call (see the conventions above;
+ * tsd_synchronize reports TSD_ERR_INVALID_ARGUMENT).  n_past advances by n only once every launch
+ * of the call has been enqueued. */
 tsd_status tsd_prefill(tsd_model* m, const int32_t* d_tokens, int n, int32_t* d_next);
 /* Prefill by the decode step at every prompt position (identical kernels, so the cache matches
  * what decoding the prompt one id at a time writes, bit for bit; TALKER_CP prompt frames run the
@@ -199,13 +207,17 @@ tsd_status tsd_step(tsd_model* m, const int32_t* d_in, int32_t* d_next);
  * Results are identical to tsd_step. */
 tsd_status tsd_step_eager(tsd_model* m, const int32_t* d_in, int32_t* d_next);
 
-/* Wait for the model's stream, then report whether any persistent step since the last
- * tsd_reset gave up on a bounded wait (TSD_ERR_TIMEOUT).  Such a step, and every step after it,
- * leaves the ids, logits and cache unspecified; nothing hangs and no memory outside the
- * workspace is touched.  Each wait in the step is limited to 20 ms. */
+/* Wait for the model's stream, then report
+ *   TSD_ERR_TIMEOUT if any persistent step since the last tsd_reset gave up on a bounded wait.
+ *     Such a step, and every step after it, leaves the ids, logits and cache unspecified;
+ *     nothing hangs and no memory outside the workspace is touched.  Each wait in the step is
+ *     limited to 20 ms.
+ *   TSD_ERR_INVALID_ARGUMENT if a call since the last tsd_synchronize passed a token id outside its
+ *     vocabulary.  That call and the model calls after it did nothing; n_past is set back to the
+ *     device's position and the rejection is cleared, so the model can be used again. */
 tsd_status tsd_synchronize(tsd_model* m);
 
-tsd_status tsd_reset(tsd_model* m);                     /* n_past = 0, history and timeout cleared */
+tsd_status tsd_reset(tsd_model* m);                     /* n_past = 0, history, timeout and rejection cleared */
 /* The launch configuration in effect: *launch_mode is PERSISTENT only when the shape has a
  * persistent kernel (else PER_OPERATOR), *n_workgroups its grid (0 for PER_OPERATOR).
  * Either pointer may be NULL. */
@@ -268,6 +280,18 @@ tsd_status tsd_sample_topk(const float* d_logits, int n, int top_k, float temper
  * tsd_sampling; TSD_ERR_UNSUPPORTED for k > 1024 or n > 12288. */
 tsd_status tsd_sample(const float* d_logits, int n, const tsd_sampling* s, const int32_t* d_hist, int n_hist,
                       int row, int pos, int pass, int32_t* d_out, void* stream);
+
+/* Debug mat-vec on the canonical blocks, no repacking ([J] appendix A3 and §3.23 for the legacy
+ * blocks, [F] §3 and §5.8 for the affine groups): d_y[b][n] = sum_k W[n][k] d_x[b][k] for b < B,
+ * with every weight decoded from d_w's bytes exactly as its format defines it and the products
+ * summed in fp32 in K order, one thread per output.  d_w is the canonical blob of an N x K matrix
+ * in format wfmt (w_bytes must equal its canonical size); d_x [B][K] and d_y [B][N] fp32
+ * row-major (device, caller-owned; d_y is overwritten).  Slow by design: a reference for checking
+ * weights or the packed kernels, never used by the step.  TSD_ERR_INVALID_ARGUMENT for null
+ * buffers, an unknown format, N, K or B not positive, K not a multiple of the format's group, or a
+ * w_bytes mismatch. */
+tsd_status tsd_debug_gemv(int wfmt, const void* d_w, size_t w_bytes, const float* d_x, float* d_y, int N, int K, int B,
+                          void* stream);
 
 /* Bytes of the kernel layout of one W[N][K] matrix (tsd_gemv_pack's output). */
 tsd_status tsd_gemv_packed_bytes(int wfmt, int N, int K, size_t* out_bytes);

@@ -27,7 +27,7 @@ EXPORTS = ["tsd_workspace_bytes", "tsd_model_create", "tsd_prefill", "tsd_step",
            "tsd_attention_scratch_bytes", "tsd_attention", "tsd_time_kernel", "tsd_synchronize",
            "tsd_model_info", "tsd_sample_topk", "tsd_sample", "tsd_gemm_rows_packed_bytes", "tsd_gemm_rows_pack",
            "tsd_gemm_rows_scratch_bytes", "tsd_gemm_rows", "tsd_prefill_stepwise", "tsd_gemm_scratch_bytes", "tsd_gemm",
-           "tsd_get_kv"]
+           "tsd_get_kv", "tsd_debug_gemv"]
 KERNEL_KINDS = {"qkv": 0, "attn": 1, "oproj": 2, "fc": 3, "down": 4, "head": 5, "step": 6}
 
 
@@ -111,6 +111,7 @@ def lib():
             "tsd_gemm_rows": [_P, _I, _I, _I, _P, _P, _I, _P, _SZ, _P],
             "tsd_gemm_scratch_bytes": [_I, _I, ctypes.POINTER(_SZ)],
             "tsd_gemm": [_I, _P, _I, _I, _I, _P, _P, _P, _P, _SZ, _P],
+            "tsd_debug_gemv": [_I, _P, _SZ, _P, _P, _I, _I, _I, _P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -171,6 +172,12 @@ def tsd_gemv_pack(fmt, w, N, K, packed, stream=None):
 
 def tsd_gemv(fmt, packed, N, K, B, x, bias, y, stream=None):
     _check(lib().tsd_gemv(FORMATS.get(fmt, fmt), _ptr(packed), N, K, B, _ptr(x), _ptr(bias), _ptr(y), _stream(stream)))
+
+
+def tsd_debug_gemv(fmt, w, x, y, N, K, B, stream=None):
+    """w: the canonical blob (device uint8); x [B][K], y [B][N] fp32 device tensors."""
+    _check(lib().tsd_debug_gemv(FORMATS.get(fmt, fmt), _ptr(w), w.numel() * w.element_size(), _ptr(x), _ptr(y), N, K, B,
+                                _stream(stream)))
 
 
 def tsd_sample_topk(logits, top_k, temperature, seed, row, pos, pss, out, stream=None):
@@ -307,7 +314,9 @@ class Model:
         self._chk(lib().tsd_truncate(self.h, n))
 
     def synchronize(self):
-        """Wait for the model's stream; TsdError(TSD_ERR_TIMEOUT) if a persistent step gave up."""
+        """Wait for the model's stream; TsdError(TSD_ERR_TIMEOUT) if a persistent step gave up,
+        TsdError(TSD_ERR_INVALID_ARGUMENT) if a call passed an id outside its vocabulary (that call
+        and the ones after it did nothing)."""
         self._chk(lib().tsd_synchronize(self.h))
 
     def logits(self):

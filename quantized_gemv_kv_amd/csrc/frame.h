@@ -85,6 +85,7 @@ struct Mm16Out {
     const float2* rope;
     const int* posp;
     int pos_value;
+    const uint32_t* err;  // STORE: when *err is set (a rejected input) nothing is written
 };
 
 // A norm's input prepared one row per workgroup: the rows (rows b < B) come from
@@ -143,12 +144,14 @@ struct PickArgs {
     // is also written to seq[*posp * B + b]
     int* seq;
     RowPrep prep;        // prep.src = -1: none
+    const uint32_t* err; // when *err is set (a rejected input) nothing is written
 };
 hipError_t launch_pick(const PickArgs& a, hipStream_t st);
 // y[i] = sum over s < S of part[s * slice + i] for i < n
 hipError_t launch_sum_slices(const float* part, int S, long long slice, float* y, long long n, hipStream_t st);
 // hist[*pos][0..n) = codes[0..n) (n may be 0), with seq: seq[*pos * B + b] = codes[b * C] for
-// b < B (the consumed code 0 of a frame no pick ran on); then *pos += 1
-hipError_t launch_frame_done(const int* codes, int n, int* hist, int* pos, int* seq, int B, int C, hipStream_t st);
+// b < B (the consumed code 0 of a frame no pick ran on); then *pos += 1.  Nothing when *err is set.
+hipError_t launch_frame_done(const int* codes, int n, int* hist, int* pos, int* seq, int B, int C, const uint32_t* err,
+                             hipStream_t st);
 
 }  // namespace tsd

@@ -232,6 +232,8 @@ __global__ __launch_bounds__(64 * NW) void k_mm16(const TiledMat W, const MmIn i
             if (sb_part + 16 * p < in.n_ssq) sp[p] = glb(in.ssq)[(size_t)(sb_part + 16 * p) * MM_ROWS + sb_row];
     // the epilogue's own inputs (wave 0 runs it)
     const int pos = EPI == MM_QKV_ROPE ? (o.posp ? ld_uniform(o.posp) : o.pos_value) : 0;
+    // a head's logits are not written after a rejected input
+    const bool skip = EPI == MM_STORE && o.err && ld_uniform((const int*)o.err);
     Pre pre[T];
     if (wave == 0)
 #pragma unroll
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(64 * NW) void k_mm16(const TiledMat W, const MmIn i
         ssp[sb_part][sb_row] = v;
     }
     __syncthreads();
-    if (wave != 0) return;
+    if (wave != 0 || skip) return;
     if (norm) {
         if (lane < 16) {
             float tsum = 0.f;
@@ -456,6 +458,7 @@ __global__ __launch_bounds__(256) void k_pick(const PickArgs a)
     __shared__ int ids[16];
     __shared__ int picked;
     const int b = blockIdx.x, t = threadIdx.x;
+    if (a.err && ld_uniform((const int*)a.err)) return;   // a rejected input: the state stays as it was
     const float* l = a.logits + (size_t)b * a.ld_l;
     const int pos = *a.posp;
     const int cur = a.seq ? a.code[(size_t)b * a.ld_code] : -1;   // read before the pick overwrites it
@@ -521,8 +524,10 @@ __global__ void k_sum_slices(const float* __restrict__ part, int S, long long sl
 }
 
 // the frame's codes appended to the history at *pos, and the position advanced
-__global__ void k_frame_done(const int* __restrict__ codes, int n, int* hist, int* pos, int* seq, int B, int C)
+__global__ void k_frame_done(const int* __restrict__ codes, int n, int* hist, int* pos, int* seq, int B, int C,
+                             const uint32_t* err)
 {
+    if (err && ld_uniform((const int*)err)) return;   // a rejected input: the state stays as it was
     const int p = *pos;
     for (int i = threadIdx.x; i < n; i += blockDim.x) hist[(size_t)p * n + i] = codes[i];
     if (seq)
@@ -631,9 +636,10 @@ hipError_t launch_sum_slices(const float* part, int S, long long slice, float* y
     return hipGetLastError();
 }
 
-hipError_t launch_frame_done(const int* codes, int n, int* hist, int* pos, int* seq, int B, int C, hipStream_t st)
+hipError_t launch_frame_done(const int* codes, int n, int* hist, int* pos, int* seq, int B, int C, const uint32_t* err,
+                             hipStream_t st)
 {
-    hipLaunchKernelGGL(k_frame_done, dim3(1), dim3(256), 0, st, codes, n, hist, pos, seq, B, C);
+    hipLaunchKernelGGL(k_frame_done, dim3(1), dim3(256), 0, st, codes, n, hist, pos, seq, B, C, err);
     return hipGetLastError();
 }
 

@@ -208,8 +208,11 @@ __global__ __launch_bounds__(WG) void k_gemv(const PackedMat W, const ProArgs pa
 #pragma unroll
     for (int r = 0; r < NP; ++r) part[r] = group_sum(part[r], SPL == 1 ? lpr : 64);
 
-    // 7. epilogue, one lane per row group
-    const bool leader = SPL == 1 ? slot0 == 0 : lane == 0;
+    // 7. epilogue, one lane per row group (the head writes no logits after a rejected input)
+    bool leader = SPL == 1 ? slot0 == 0 : lane == 0;
+    if constexpr (EPI == EPI_HEAD_ARGMAX) {
+        if (ea.err && ld_uniform((const int*)ea.err)) leader = false;
+    }
     const int pos = (EPI == EPI_QKV || EPI == EPI_QKV_ROPE) ? ld_uniform(ea.pos) : 0;
     unsigned long long best = 0ull;
     if (leader) {
@@ -367,9 +370,11 @@ int gemv_rows_per_block(int fmt, int K, int) { return rows_per_block_impl(fmt, K
 
 namespace {
 __global__ __launch_bounds__(256) void k_argmax_finalize(const unsigned long long* __restrict__ best, int n, int B, int* tok,
-                                                         int* hist, int* seq, int hist_stride, int* pos)
+                                                         int* hist, int* seq, int hist_stride, int* pos,
+                                                         const uint32_t* err)
 {
     __shared__ unsigned long long bk[NWAVE];
+    if (err && ld_uniform((const int*)err)) return;   // a rejected input: the state stays as it was
     const int p = *pos;   // every row is read before the position advances (one workgroup)
     for (int r = 0; r < B; ++r) {
         unsigned long long m = 0ull;
@@ -392,9 +397,9 @@ __global__ __launch_bounds__(256) void k_argmax_finalize(const unsigned long lon
 }  // namespace
 
 hipError_t launch_argmax_finalize(const unsigned long long* best, int n, int B, int* tok, int* hist, int* seq, int hist_stride,
-                                  int* pos, hipStream_t st)
+                                  int* pos, const uint32_t* err, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_argmax_finalize, dim3(1), dim3(WG), 0, st, best, n, B, tok, hist, seq, hist_stride, pos);
+    hipLaunchKernelGGL(k_argmax_finalize, dim3(1), dim3(WG), 0, st, best, n, B, tok, hist, seq, hist_stride, pos, err);
     return hipGetLastError();
 }
 

@@ -65,6 +65,8 @@ struct EpiArgs {
     const int* pos;      // device position (K/V slot, RoPE angle)
     // head / argmax: best key of workgroup i -> best[i]
     unsigned long long* best;
+    // head: when *err is set (a rejected input, see launch_set_input) the logits are not written
+    const uint32_t* err;
     // batch rows (blockIdx.y = row b): y moves by b * rs_y, q by b * rs_q, the caches by
     // b * rs_kv elements, best by b * (workgroups per row)
     long long rs_y, rs_q, rs_kv;
@@ -128,8 +130,9 @@ hipError_t launch_attention_merge(const AttnArgs& a, int n_keys, hipStream_t st)
 // seq: when set, seq[*pos * hist_stride] = the token consumed at this position (*tok before it is
 // overwritten by the id)
 // B rows: row b's keys at best + b * n, its id to tok[b], hist[*pos * hist_stride + b] (and seq)
+// err: when *err is set (a rejected input) nothing is written and the position stays
 hipError_t launch_argmax_finalize(const unsigned long long* best, int n, int B, int* tok, int* hist, int* seq, int hist_stride, int* pos,
-                                  hipStream_t st);
+                                  const uint32_t* err, hipStream_t st);
 
 // ---- persistent decode step (step.hip) ---------------------------------------------------------
 // One launch runs the whole batch-1 step; phases hand data over through exchange words
@@ -169,6 +172,7 @@ struct StepArgs {
     int* seq;                                 // [n_ctx][B] the token consumed at each position
     uint32_t* ctr;                            // launches completed: the epoch base
     uint32_t* abort_word;                     // sticky: a wait gave up
+    const uint32_t* bad_input;                // sticky: an input id was rejected (the launch does nothing)
     float* logits;                            // [B][vocab]
     // exchange words: QKV out, attention partials [H][max_split][hd+2], attention-block output
     // (residual stream), MLP hidden, layer output (residual stream), per-workgroup argmax keys;
@@ -221,6 +225,7 @@ struct SampleArgs {
     long long ld_logits;
     int cfg;
     float cfg_weight;
+    const uint32_t* err;   // when *err is set (a rejected input) nothing is written and the position stays
 };
 bool sample_supported(int n, int k);
 size_t sample_lds_bytes(int n);
@@ -231,6 +236,20 @@ hipError_t launch_sample(const SampleArgs& a, hipStream_t st);
 constexpr int MM_ROWS = 16;
 __host__ __device__ inline size_t il_x(int b, int k) { return ((size_t)(k >> 2) * MM_ROWS + b) * 4 + (k & 3); }
 __host__ __device__ inline size_t il_act(int b, int k) { return ((size_t)(k >> 3) * MM_ROWS + b) * 8 + (k & 7); }
+
+// ---- input ids and the rejected-input word ----------------------------------------------------
+// Ids enter the model through these kernels only.  An id is valid when 0 <= id < lim0 for column 0
+// and 0 <= id < lim1 for the other columns (the Talker's code 0 and codes 1..C-1).
+// launch_set_input: dst[r * cols + c] = src[r * src_stride + c] when every id is valid and *err is
+// clear; otherwise nothing is copied and *err is set.  launch_check_ids: *err is set when any of the
+// rows x n x cols ids at src ([rows][n][cols]) is invalid.  launch_set_pos: *pos = value unless
+// *err is set.  Every kernel that writes the model's observable state (the position, the sampled
+// ids, the history, the logits) checks *err and writes nothing when it is set, so a call given a
+// bad id leaves the state as it was; tsd_synchronize reports and clears the word.
+hipError_t launch_set_input(int* dst, const int* src, int rows, int cols, long long src_stride, int lim0, int lim1,
+                            uint32_t* err, hipStream_t st);
+hipError_t launch_check_ids(const int* src, int rows, int n, int cols, int lim0, int lim1, uint32_t* err, hipStream_t st);
+hipError_t launch_set_pos(int* pos, int value, const uint32_t* err, hipStream_t st);
 
 // ---- small state kernels ---------------------------------------------------------------------
 // dst[r * cols + c] = src[r * src_stride + c]

@@ -62,6 +62,11 @@ inline PackedMat take_mat(Planner& P, int f, int N, int K)
     return packed_view(f, p, N, K);
 }
 
+// the model's control words (64 words in the workspace): the persistent step's epoch base
+// (launches completed) and its sticky time-out word; the sticky rejected-input word that every
+// state-writing kernel checks (kernels.h launch_set_input)
+enum { CTL_EPOCH = 0, CTL_ABORT = 1, CTL_BAD_INPUT = 2, CTL_WORDS = 64 };
+
 // kernel kinds a timing probe can bracket
 enum { KIND_QKV = 0, KIND_ATTN = 1, KIND_OPROJ = 2, KIND_FC = 3, KIND_DOWN = 4, KIND_HEAD = 5, KIND_STEP = 6, TSD_KERNEL_KINDS = 7 };
 
@@ -160,6 +165,9 @@ namespace tsd {
 
 tsd_status fail(tsd_model* m, tsd_status s, const std::string& msg);
 tsd_status hip_fail(tsd_model* m, hipError_t e, const char* what);
+// the scale group of a weight format along K (64 or 32), and the bytes of a canonical N x K blob
+int group_of(int f);
+size_t canonical_matrix_bytes(int f, int N, int K);
 
 #define HIP_TRY(m, expr, what)                              \
     do {                                                    \

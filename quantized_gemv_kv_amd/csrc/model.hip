@@ -38,15 +38,7 @@ tsd_status hip_fail(tsd_model* m, hipError_t e, const char* what)
     return fail(m, TSD_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-}  // namespace tsd
-
-namespace {
-
-constexpr int MAX_STEP_WG = 1024;          // workgroups of the persistent step, at most
-constexpr long long STEP_SPIN_LIMIT = 2000000;   // 20 ms of the 100 MHz clock per wait
-
 int group_of(int f) { return f == TSD_W_AFFINE8_G64 || f == TSD_W_AFFINE4_G64 ? 64 : 32; }
-bool known_format(int f) { return f >= 0 && f < FMT_COUNT; }
 
 size_t canonical_matrix_bytes(int f, int N, int K)
 {
@@ -56,6 +48,15 @@ size_t canonical_matrix_bytes(int f, int N, int K)
     if (f == TSD_W_AFFINE4_G64 || f == TSD_W_AFFINE4_G32) return (size_t)N * K / 2 + (size_t)N * (K / group_of(f)) * 4;
     return (size_t)N * K + (size_t)N * (K / 64) * 4;
 }
+
+}  // namespace tsd
+
+namespace {
+
+constexpr int MAX_STEP_WG = 1024;          // workgroups of the persistent step, at most
+constexpr long long STEP_SPIN_LIMIT = 2000000;   // 20 ms of the 100 MHz clock per wait
+
+bool known_format(int f) { return f >= 0 && f < FMT_COUNT; }
 
 tsd_status validate(const tsd_config* c, std::string& msg)
 {
@@ -362,6 +363,7 @@ hipError_t enqueue_step(tsd_model* m, hipStream_t st, Probe* pr = nullptr)
     eh.y = m->logits;
     eh.ldy = c.vocab;
     eh.best = m->best;
+    eh.err = m->ctl + CTL_BAD_INPUT;
     eh.rs_y = c.vocab;
     Bracket br(pr, KIND_HEAD, st);
     hipError_t e = launch_gemv(c.wfmt, c.arch == TSD_ARCH_GPT2 ? PRO_LN : PRO_RMS, EPI_HEAD_ARGMAX, m->head, ph, eh, st,
@@ -386,11 +388,13 @@ hipError_t enqueue_step(tsd_model* m, hipStream_t st, Probe* pr = nullptr)
         s.n_seq = -1;
         s.cur = m->tok;
         s.seq_out = m->seq;
+        s.err = m->ctl + CTL_BAD_INPUT;
         return launch_sample(s, st);
     }
     const int nblk = (c.vocab + gemv_rows_per_block(c.wfmt, c.d_model, EPI_HEAD_ARGMAX) - 1) /
                      gemv_rows_per_block(c.wfmt, c.d_model, EPI_HEAD_ARGMAX);
-    return launch_argmax_finalize(m->best, nblk, c.batch, m->tok, m->hist, m->seq, c.batch * m->tpp, m->pos, st);
+    return launch_argmax_finalize(m->best, nblk, c.batch, m->tok, m->hist, m->seq, c.batch * m->tpp, m->pos,
+                                  m->ctl + CTL_BAD_INPUT, st);
 }
 
 tsd_status pack_weights(tsd_model* m, const tsd_tensor* w)
@@ -441,7 +445,7 @@ tsd_status pack_weights(tsd_model* m, const tsd_tensor* w)
 hipError_t reset_exchange(tsd_model* m)
 {
     hipError_t e = launch_fill_u64((unsigned long long*)m->xbuf, 0ull, (int)m->xbuf_words, m->st);
-    if (e == hipSuccess) e = launch_fill_u32(m->ctl, 0u, 64, m->st);
+    if (e == hipSuccess) e = launch_fill_u32(m->ctl + CTL_EPOCH, 0u, 2, m->st);   // epoch base and time-out word
     m->launches = 0;
     return e;
 }
@@ -500,7 +504,8 @@ tsd_status setup_step(tsd_model* m)
     a.max_split = attn_max_split(c.n_ctx);
     a.eps = c.norm_eps;
     a.emb = m->emb[0]; a.wpe = m->wpe; a.nfg = m->nfg; a.nfb = m->nfb; a.head = m->head; a.rope = m->rope;
-    a.pos = m->pos; a.tok = m->tok; a.hist = m->hist; a.seq = m->seq; a.ctr = m->ctl; a.abort_word = m->ctl + 1;
+    a.pos = m->pos; a.tok = m->tok; a.hist = m->hist; a.seq = m->seq; a.ctr = m->ctl + CTL_EPOCH; a.abort_word = m->ctl + CTL_ABORT;
+    a.bad_input = m->ctl + CTL_BAD_INPUT;
     a.logits = m->logits;
     a.spin_limit = STEP_SPIN_LIMIT;
     a.samp_mode = m->draw;
@@ -554,6 +559,7 @@ tsd_status init_state(tsd_model* m)
         HIP_TRY(m, hipMemcpyAsync(m->d_sa, &m->sa, sizeof(StepArgs), hipMemcpyHostToDevice, st), "step arguments");
         HIP_TRY(m, hipStreamSynchronize(st), "step arguments");
     }
+    HIP_TRY(m, launch_fill_u32(m->ctl, 0u, CTL_WORDS, st), "control words");
     HIP_TRY(m, reset_exchange(m), "exchange init");
     HIP_TRY(m, hipStreamSynchronize(st), "create sync");
     return TSD_OK;
@@ -575,18 +581,17 @@ void count_launches(tsd_model* m)
 
 // ---- the prompt pass -------------------------------------------------------------------------
 // Prompt positions t0 .. t0 + np - 1 of every batch row (ids d_tokens[b][n_prompt][tokens per
-// position]) at cache positions m->n_past .. m->n_past + np - 1: the embedding rows (the sum of
+// position]) at cache positions pos0 .. pos0 + np - 1: the embedding rows (the sum of
 // the frame's code embeddings for the Talker), then per layer norm, QKV product (queries, RoPE,
 // K/V into the cache), causal attention, output projection into the residual stream, norm,
 // FC / gate-up product and down projection.  No head: the last prompt position goes through the
 // decode step (the whole frame for TALKER_CP).
-hipError_t pf_enqueue(tsd_model* m, const int32_t* d_tokens, int n_prompt, int t0, int np, hipStream_t st)
+hipError_t pf_enqueue(tsd_model* m, const int32_t* d_tokens, int n_prompt, int t0, int np, int pos0, hipStream_t st)
 {
     const tsd_config& c = m->c;
     const int d = c.d_model, H = c.n_head, Hk = c.n_kv_head, hd = c.head_dim, ff = c.d_ff, B = c.batch, f = c.wfmt;
     const bool gpt2 = c.arch == TSD_ARCH_GPT2, talker = c.arch == TSD_ARCH_TALKER_CP;
     const int M = B * np, qd = H * hd;
-    const int pos0 = m->n_past;
     PfRowArgs ra{};
     ra.M = M; ra.d = d; ra.n_pos = np; ra.pos0 = pos0;
     ra.tok = d_tokens; ra.tok_stride = n_prompt; ra.t0 = t0; ra.n_prompt = n_prompt;
@@ -813,12 +818,23 @@ tsd_status tsd_model_destroy(tsd_model* m)
 
 const char* tsd_last_error(const tsd_model* m) { return m ? m->err.c_str() : g_err.c_str(); }
 
+namespace {
+// the ids of one position (rows of tok_per_pos ids, src_stride apart) into the step's input slots,
+// checked on the device: a rejected set leaves the slots alone and raises the bad-input word
+hipError_t set_input(tsd_model* m, const int32_t* src, long long src_stride)
+{
+    const bool talker = m->c.arch == TSD_ARCH_TALKER_CP;
+    return launch_set_input(m->tok, src, m->c.batch, m->tpp, src_stride, m->c.vocab, talker ? m->c.cp_vocab : m->c.vocab,
+                            m->ctl + CTL_BAD_INPUT, m->st);
+}
+}  // namespace
+
 tsd_status tsd_step(tsd_model* m, const int32_t* d_in, int32_t* d_next)
 {
     if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
     if (m->n_past >= m->c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "context full");
     const int nt = m->c.batch * m->tpp;
-    if (d_in) HIP_TRY(m, launch_copy_i32(m->tok, d_in, nt, m->st), "set input");
+    if (d_in) HIP_TRY(m, set_input(m, d_in, m->tpp), "set input");
     HIP_TRY(m, before_launch(m), "exchange restart");
     HIP_TRY(m, hipGraphLaunch(m->exec, m->st), "graph launch");
     if (d_next) HIP_TRY(m, launch_copy_i32(d_next, m->tok, nt, m->st), "copy ids");
@@ -831,7 +847,7 @@ tsd_status tsd_step_eager(tsd_model* m, const int32_t* d_in, int32_t* d_next)
     if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
     if (m->n_past >= m->c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "context full");
     const int nt = m->c.batch * m->tpp;
-    if (d_in) HIP_TRY(m, launch_copy_i32(m->tok, d_in, nt, m->st), "set input");
+    if (d_in) HIP_TRY(m, set_input(m, d_in, m->tpp), "set input");
     HIP_TRY(m, before_launch(m), "exchange restart");
     HIP_TRY(m, enqueue_step(m, m->st), "eager step");
     if (d_next) HIP_TRY(m, launch_copy_i32(d_next, m->tok, nt, m->st), "copy ids");
@@ -845,20 +861,34 @@ tsd_status tsd_prefill(tsd_model* m, const int32_t* d_tokens, int n, int32_t* d_
     if (!d_tokens || n <= 0) return fail(m, TSD_ERR_INVALID_ARGUMENT, "empty prompt");
     if (m->n_past + n > m->c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "prompt does not fit the context");
     const int nt = m->c.batch * m->tpp;
-    // every position but the last through the prompt pass, in chunks of pf_rows rows
+    const bool talker = m->c.arch == TSD_ARCH_TALKER_CP;
+    // every id of the prompt is checked first; a bad one makes every launch below leave the state
+    // alone (the prompt pass only writes cache rows and records at positions from n_past on,
+    // which no step reads before they are written again)
+    HIP_TRY(m, launch_check_ids(d_tokens, m->c.batch, n, m->tpp, m->c.vocab, talker ? m->c.cp_vocab : m->c.vocab,
+                                m->ctl + CTL_BAD_INPUT, m->st),
+            "check ids");
+    const int n_past0 = m->n_past;
+    // every position but the last through the prompt pass, in chunks of pf_rows rows; the model's
+    // position count changes only once everything is enqueued
     const int chunk = m->pf_rows / m->c.batch;
+    int p = n_past0;
     for (int t0 = 0; t0 < n - 1; t0 += chunk) {
         const int np = std::min(chunk, n - 1 - t0);
-        HIP_TRY(m, pf_enqueue(m, d_tokens, n, t0, np, m->st), "prompt pass");
-        m->n_past += np;
+        HIP_TRY(m, pf_enqueue(m, d_tokens, n, t0, np, p, m->st), "prompt pass");
+        p += np;
     }
-    if (n > 1) HIP_TRY(m, launch_fill_i32(m->pos, m->n_past, 1, m->st), "set position");
+    hipError_t e = hipSuccess;
+    if (n > 1) e = launch_set_pos(m->pos, p, m->ctl + CTL_BAD_INPUT, m->st);
     // the last position: one decode step (head, sampler, history; the whole frame for TALKER_CP)
-    HIP_TRY(m, launch_gather_i32(m->tok, d_tokens + (size_t)(n - 1) * m->tpp, m->c.batch, m->tpp, (long long)n * m->tpp, m->st),
-            "set input");
-    HIP_TRY(m, before_launch(m), "exchange restart");
-    HIP_TRY(m, hipGraphLaunch(m->exec, m->st), "graph launch");
-    m->n_past += 1;
+    if (e == hipSuccess) e = set_input(m, d_tokens + (size_t)(n - 1) * m->tpp, (long long)n * m->tpp);
+    if (e == hipSuccess) e = before_launch(m);
+    if (e == hipSuccess) e = hipGraphLaunch(m->exec, m->st);
+    if (e != hipSuccess) {
+        if (n > 1) (void)launch_fill_i32(m->pos, n_past0, 1, m->st);   // the position as it was
+        return hip_fail(m, e, "prefill");
+    }
+    m->n_past = p + 1;
     if (d_next) HIP_TRY(m, launch_copy_i32(d_next, m->tok, nt, m->st), "copy ids");
     return TSD_OK;
 }
@@ -869,10 +899,13 @@ tsd_status tsd_prefill_stepwise(tsd_model* m, const int32_t* d_tokens, int n, in
     if (!d_tokens || n <= 0) return fail(m, TSD_ERR_INVALID_ARGUMENT, "empty prompt");
     if (m->n_past + n > m->c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "prompt does not fit the context");
     const int nt = m->c.batch * m->tpp;
+    const bool talker = m->c.arch == TSD_ARCH_TALKER_CP;
+    HIP_TRY(m, launch_check_ids(d_tokens, m->c.batch, n, m->tpp, m->c.vocab, talker ? m->c.cp_vocab : m->c.vocab,
+                                m->ctl + CTL_BAD_INPUT, m->st),
+            "check ids");
     for (int t = 0; t < n; ++t) {
         // tokens are [batch][n][tokens per position]: position t of every row
-        HIP_TRY(m, launch_gather_i32(m->tok, d_tokens + (size_t)t * m->tpp, m->c.batch, m->tpp, (long long)n * m->tpp, m->st),
-                "set input");
+        HIP_TRY(m, set_input(m, d_tokens + (size_t)t * m->tpp, (long long)n * m->tpp), "set input");
         HIP_TRY(m, before_launch(m), "exchange restart");
         // TALKER_CP prompt frames before the last need neither head nor predictor
         hipGraphExec_t x = (m->exec_talker && t + 1 < n) ? m->exec_talker : m->exec;
@@ -887,11 +920,21 @@ tsd_status tsd_synchronize(tsd_model* m)
 {
     if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
     HIP_TRY(m, hipStreamSynchronize(m->st), "stream sync");
-    if (m->step_fn) {
-        uint32_t ab = 0;
-        HIP_TRY(m, hipMemcpy(&ab, m->ctl + 1, sizeof(ab), hipMemcpyDeviceToHost), "read abort word");
-        if (ab) return fail(m, TSD_ERR_TIMEOUT, "a wait inside the persistent step timed out; the steps since are void "
-                                                "(tsd_reset clears the state)");
+    uint32_t ctl[CTL_BAD_INPUT + 1] = {};
+    HIP_TRY(m, hipMemcpy(ctl, m->ctl, sizeof(ctl), hipMemcpyDeviceToHost), "read control words");
+    if (m->step_fn && ctl[CTL_ABORT])
+        return fail(m, TSD_ERR_TIMEOUT, "a wait inside the persistent step timed out; the steps since are void "
+                                        "(tsd_reset clears the state)");
+    if (ctl[CTL_BAD_INPUT]) {
+        // the calls since the rejected input did nothing: the position count is the device's
+        int pos = 0;
+        HIP_TRY(m, hipMemcpy(&pos, m->pos, sizeof(pos), hipMemcpyDeviceToHost), "read position");
+        m->n_past = pos;
+        HIP_TRY(m, launch_fill_u32(m->ctl + CTL_BAD_INPUT, 0u, 1, m->st), "clear bad-input word");
+        HIP_TRY(m, hipStreamSynchronize(m->st), "stream sync");
+        return fail(m, TSD_ERR_INVALID_ARGUMENT, "a token id outside its vocabulary was passed in; that call and "
+                                                 "every model call after it until now did nothing (the model state "
+                                                 "is as it was before that call)");
     }
     return TSD_OK;
 }
@@ -910,6 +953,7 @@ tsd_status tsd_reset(tsd_model* m)
     HIP_TRY(m, launch_fill_i32(m->pos, 0, 1, m->st), "reset");
     HIP_TRY(m, launch_fill_i32(m->hist, 0, m->c.n_ctx * m->c.batch * m->tpp, m->st), "reset");
     HIP_TRY(m, launch_fill_i32(m->seq, -1, m->c.n_ctx * m->c.batch, m->st), "reset");
+    HIP_TRY(m, launch_fill_u32(m->ctl + CTL_BAD_INPUT, 0u, 1, m->st), "reset");
     if (m->step_fn) HIP_TRY(m, reset_exchange(m), "reset");
     m->n_past = 0;
     return TSD_OK;

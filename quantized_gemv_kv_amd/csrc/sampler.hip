@@ -19,6 +19,7 @@ __global__ __launch_bounds__(NT) void k_sample(const SampleArgs a)
     const int n = a.n;
     uint32_t* keys = lds;
     uint32_t* seen = lds + samp::key_words(n);
+    if (a.err && ld_uniform((const int*)a.err)) return;   // a rejected input: the state stays as it was
     const int pos = a.posp ? *a.posp : a.pos_value;   // read once: the position advances at the end
     const int rows = a.rows > 0 ? a.rows : 1;
     const bool pen = a.ch.penalty != 1.f;

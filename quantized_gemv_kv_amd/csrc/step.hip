@@ -809,11 +809,13 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
     int n_layer;
     {
         const StepArgs& a = opaque(ap);
-        // a wait of an earlier launch timed out: the exchange state is not trusted, do nothing
-        if (ld_uniform((const int*)a.abort_word)) return;
+        // a wait of an earlier launch timed out (the exchange state is not trusted), or an input id
+        // was rejected (the state must stay as it was): do nothing
+        if (ld_uniform((const int*)a.abort_word) | ld_uniform((const int*)a.bad_input)) return;
         cx.pos = ld_uniform(a.pos);
 #pragma unroll
         for (int b = 0; b < B; ++b) {
+            // ids enter through the checked input copy; the clamp only keeps every gather in bounds
             const int tok = ld_uniform(a.tok + b);
             cx.tok[b] = tok < 0 ? 0 : (tok >= C::V ? C::V - 1 : tok);
         }

@@ -144,6 +144,7 @@ hipError_t head16(tsd_model* m, hipStream_t st, Probe* pr, const TiledMat& W, in
     oh.y = m->logits + (size_t)j * m->vmax;
     oh.ldy = c.n_codebooks * m->vmax;
     oh.rows = c.batch;
+    oh.err = m->ctl + CTL_BAD_INPUT;
     Bracket br(pr, KIND_HEAD, st);
     return launch_mm16(MM_STORE, W, ih, 1, oh, st);
 }
@@ -167,6 +168,7 @@ hipError_t pick16(tsd_model* m, hipStream_t st, int j, int vocab, const RowPrep*
     a.ld_code = c.n_codebooks;
     a.prep.src = -1;
     if (prep) a.prep = *prep;
+    a.err = m->ctl + CTL_BAD_INPUT;
     return launch_pick(a, st);
 }
 
@@ -396,7 +398,7 @@ hipError_t talker_enqueue(tsd_model* m, hipStream_t st, bool with_cp, Probe* pr)
         n_ssq = tiles_d;
     }
     if (!with_cp)   // advance the position and record the consumed code 0 only
-        return launch_frame_done(m->tok, 0, m->hist, m->pos, m->seq, c.batch, c.n_codebooks, st);
+        return launch_frame_done(m->tok, 0, m->hist, m->pos, m->seq, c.batch, c.n_codebooks, m->ctl + CTL_BAD_INPUT, st);
     // code 0; the Talker's final-normed hidden state is the predictor's position 0
     TRY(head16(m, st, pr, m->t_head, 0));
     RowPrep h{};
@@ -428,7 +430,7 @@ hipError_t talker_enqueue(tsd_model* m, hipStream_t st, bool with_cp, Probe* pr)
         const RowPrep p = cp_input_emb(m, cpos, nullptr);
         TRY(pick16(m, st, cpos, c.cp_vocab, cpos + 1 < C ? &p : nullptr));
     }
-    return launch_frame_done(m->tok, B * C, m->hist, m->pos, nullptr, B, C, st);
+    return launch_frame_done(m->tok, B * C, m->hist, m->pos, nullptr, B, C, m->ctl + CTL_BAD_INPUT, st);
 }
 
 hipError_t talker_layer(tsd_model* m, int l, hipStream_t st, const float* d_x, const int* pos)

@@ -71,3 +71,18 @@ def test_talker_workspace_and_validation():
             binding.tsd_workspace_bytes(bad)
         assert e.value.status == status, bad
     assert binding.tsd_gemm_rows_scratch_bytes(1024, 3072, 4) >= 4 * 16 * 1024 * 4      # the split-K slices
+
+
+def test_debug_gemv_host_validation():
+    """tsd_debug_gemv rejects bad arguments on the host, before anything reaches the device."""
+    lib = binding.lib()
+    one = ctypes.c_void_p(1)
+    cases = [(0, None, 18, one, one, 1, 32, 1),       # null weights
+             (9, one, 18, one, one, 1, 32, 1),        # unknown format
+             (0, one, 18, one, one, 1, 48, 1),        # K not a multiple of 32
+             (2, one, 96 + 4, one, one, 1, 96, 1),    # affine-8: K not a multiple of 64
+             (0, one, 17, one, one, 1, 32, 1),        # not the canonical size of 1 x 32 Q4_0
+             (1, one, 34, one, one, 1, 32, 0)]        # no batch rows
+    for fmt, w, nb, x, y, N, K, B in cases:
+        rc = lib.tsd_debug_gemv(fmt, w, nb, x, y, N, K, B, None)
+        assert rc == 1, (fmt, nb, N, K, B)

@@ -10,8 +10,9 @@ compared head, taken together as the frame's output tensor: rel <= 2e-3.
 The small models use norm gains ~N(0, 0.1): with gains ~N(0, 0.5) these random networks amplify
 the fp16 rounding of cached keys and values (a value computed 1e-7 apart on two sides rounds to
 neighbouring fp16 numbers now and then) into logit differences of a few 1e-3 late in the
-predictor's chain, as much between two GPU runs whose embeddings differ by 2e-7 as between the
-GPU and the oracle."""
+predictor's chain.  The oracle shows it against itself: one ulp on every code embedding moves
+its frame logits by more than 2e-3 at gains ~N(0, 0.5) and by less than 5e-4 at ~N(0, 0.1)
+(test_oracle_model.py::test_small_talker_conditioning_under_one_ulp)."""
 import sys
 
 import numpy as np
@@ -301,6 +302,55 @@ def test_talker_errors():
     gm.close()
     with pytest.raises(TsdError):
         gpu_model(cfg, w[:-1])
+
+
+@pytest.mark.parametrize("slot,bad_id", [(0, -1), (0, "vocab"), (1, "cp_vocab"), (3, 1 << 30)])
+def test_talker_codes_outside_the_vocabulary_are_rejected(slot, bad_id):
+    """A frame (or a prompt) given a code outside its vocabulary (code 0: [0, vocab), codes
+    1..C-1: [0, cp_vocab)) does nothing, nor do the calls after it until tsd_synchronize reports
+    TSD_ERR_INVALID_ARGUMENT; the codes, history, logits and Talker cache of the earlier positions
+    are unchanged bit for bit, and the model then goes on as one that never saw the bad code."""
+    from quantized_gemv_kv_amd import TsdError
+    cfg = small_talker(batch=2, n_ctx=16)
+    say(f"[frame] bad code in slot {slot}: {bad_id}")
+    bad_id = cfg[bad_id] if isinstance(bad_id, str) else bad_id
+    w = synth.model_weights(cfg, 3, norm_std=0.1)
+    prompt = synth.prompt_tokens(cfg, 5, seed=2)
+    nxt = synth.prompt_tokens(cfg, 1, seed=3)[:, 0, :]
+
+    def state(m):
+        k, v = m.get_kv(m.n_past)
+        return (m.n_past, m.logits().cpu().numpy(), m.tokens(0, m.n_past).cpu().numpy(),
+                k.cpu().numpy().view(np.uint16), v.cpu().numpy().view(np.uint16))
+
+    ref = gpu_model(cfg, w)
+    ref.prefill(dev(prompt))
+    ref.step(dev(nxt))
+    want = state(ref)
+    ref.close()
+    gm = gpu_model(cfg, w)
+    gm.prefill(dev(prompt))
+    before = state(gm)
+    bad = nxt.copy()
+    bad[1, slot] = bad_id
+    gm.step(dev(bad))
+    gm.step(None)
+    badp = synth.prompt_tokens(cfg, 3, seed=4)
+    badp[0, 1, slot] = bad_id
+    gm.prefill(dev(badp))
+    with pytest.raises(TsdError) as e:
+        gm.synchronize()
+    assert e.value.status == 1
+    after = state(gm)
+    assert after[0] == before[0] == 5
+    for x, y in zip(before[1:], after[1:]):
+        assert np.array_equal(x, y)
+    gm.step(dev(nxt))
+    got = state(gm)
+    assert got[0] == want[0]
+    for x, y in zip(want[1:], got[1:]):
+        assert np.array_equal(x, y)
+    gm.close()
 
 
 def test_full_size_frames_sampled_rows():

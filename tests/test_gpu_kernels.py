@@ -82,6 +82,36 @@ def test_gemv_matches_oracle(fmt, N, K, B):
     assert np.all(np.abs(got - ref) <= 4 * K * 2.0 ** -24 * mag + 1e-30)
 
 
+DEBUG_GEMV_CASES = [(f, N, K, B) for f in ("q4_0", "q8_0", "aff8", "q5_0", "aff4_g64", "aff4_g32")
+                    for (N, K, B) in ((37, 128, 3), (300, 1024, 1), (64, 192 if f in ("aff8", "aff4_g64") else 96, 2))]
+
+
+@pytest.mark.parametrize("fmt,N,K,B", DEBUG_GEMV_CASES)
+def test_debug_gemv_on_canonical_blocks(fmt, N, K, B):
+    """tsd_debug_gemv decodes the canonical blob itself (no repacking): against the oracle's fp64
+    mat-vec, within the fp32 bound of a K-long sequential sum, and equal to the packed kernel's
+    result to the same bound."""
+    torch = _t()
+    from quantized_gemv_kv_amd import binding as tb
+    say(f"[debug-gemv] fmt={fmt} N={N} K={K} B={B}")
+    rng = synth.rng_for(17, N, K, B)
+    blob = synth.matrix(fmt, rng, N, K)
+    x = synth.normal_f32(rng, (B, K))
+    ref = oracle.gemv_f32(fmt, blob, N, K, x, None)
+    y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+    tb.tsd_debug_gemv(fmt, dev(blob), dev(x), y, N, K, B)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    W = oracle.dequant(fmt, blob, N, K)
+    mag = np.abs(x.astype(np.float64)) @ np.abs(W).T
+    assert np.all(np.abs(got - ref) <= 2 * K * 2.0 ** -24 * mag + 1e-30)
+    assert rel_err(got, ref) <= 1e-5
+    with pytest.raises(tb.TsdError) as e:
+        tb.tsd_debug_gemv(fmt, dev(blob[:-1]), dev(x), y, N, K, B)       # not the canonical size
+    assert e.value.status == 1
+
+
 def test_tall_gemv_sampled_rows():
     """The tall Q8_0 GEMV the benchmark times (524288 x 1024, ~570 MB), in the same launch
     configuration; 96 sampled rows checked against the oracle row by row."""

@@ -404,6 +404,61 @@ def test_errors_leave_state_unchanged():
     assert e.value.status == 2
 
 
+@pytest.mark.parametrize("arch,fmt,batch,mode", [
+    ("gpt2", "q4_0", 1, "persistent"), ("gpt2", "q4_0", 1, "per_operator"), ("llama", "q8_0", 2, "persistent"),
+    ("llama", "q8_0", 1, "per_operator"),
+])
+def test_step_ids_outside_the_vocabulary_are_rejected(arch, fmt, batch, mode):
+    """A step given an id outside [0, vocab) does nothing, and neither does any call after it until
+    tsd_synchronize, which reports TSD_ERR_INVALID_ARGUMENT and sets n_past back: the ids, history,
+    logits and cache of the earlier positions are unchanged bit for bit, and the model then goes on
+    exactly as one that never saw the bad id."""
+    from quantized_gemv_kv_amd import TsdError
+    torch = torch_mod()
+    cfg = synth.small_config(arch, fmt, d_ff=256, n_ctx=64, batch=batch)
+    say(f"[step] bad ids, {arch} {fmt} batch {batch} {mode}")
+    w = synth.model_weights(cfg, 5, norm_std=0.5)
+    prompt = dev(synth.prompt_tokens(cfg, 9, seed=2))
+    good = torch.tensor([[3]] * batch, dtype=torch.int32, device="cuda")
+
+    def state(m):
+        k, v = m.get_kv(m.n_past)
+        return (m.n_past, m.logits().cpu().numpy(), m.tokens(0, m.n_past).cpu().numpy(),
+                k.cpu().numpy().view(np.uint16), v.cpu().numpy().view(np.uint16))
+
+    ref = gpu_model(cfg, w, mode)
+    ref.prefill(prompt)
+    ref.step(good)
+    ref.step(None)
+    want = state(ref)
+    ref.close()
+    for bad_id in (-1, cfg["vocab"], 1 << 30):
+        gm = gpu_model(cfg, w, mode)
+        gm.prefill(prompt)
+        before = state(gm)
+        bad = good.clone()
+        bad[batch - 1, 0] = bad_id
+        gm.step(bad)
+        gm.step(None)
+        gm.step(good)
+        assert gm.n_past == 12                     # counted until the device says otherwise
+        with pytest.raises(TsdError) as e:
+            gm.synchronize()
+        assert e.value.status == 1
+        after = state(gm)
+        assert after[0] == before[0] == 9
+        for x, y in zip(before[1:], after[1:]):
+            assert np.array_equal(x, y)
+        gm.synchronize()                           # reported once
+        gm.step(good)
+        gm.step(None)
+        got = state(gm)
+        assert got[0] == want[0]
+        for x, y in zip(want[1:], got[1:]):
+            assert np.array_equal(x, y)
+        gm.close()
+
+
 def test_step_timing_kinds_follow_launch_mode():
     from quantized_gemv_kv_amd import TsdError
     cfg = synth.small_config("gpt2", "q4_0", d_ff=256, n_ctx=64)

@@ -58,6 +58,36 @@ def test_philox_matches_numpy(orc, ctr, key):
     assert np.array_equal(got, ref)
 
 
+def _numpy_counter_before(ctr):
+    """The counter numpy's Philox must hold so that its next block is generated at `ctr` (it adds
+    one, with carry, before each block of 4 words)."""
+    c = list(ctr)
+    for i in range(4):
+        if c[i] > 0:
+            c[i] -= 1
+            return c
+        c[i] = 2 ** 64 - 1
+    return c
+
+
+@pytest.mark.parametrize("seed,row,pos,pss", [
+    (42, 0, 256, 0), (42, 1, 256, 0), (42, 0, 257, 0), (42, 15, 3, 7), (7, 3, 15, 1),
+    (0, 1, 0, 0), (2 ** 63 + 5, 2, 900, 14), (123456789, 9, 1, 2),
+])
+def test_uniform24_is_the_top_24_bits_of_word_0(orc, seed, row, pos, pss):
+    # the sampler's uniform: counter (position, row, pass, 0), key (seed, 0), top 24 bits of the
+    # first output word of Philox4x64-10, recomputed with numpy's independent implementation
+    bg = np.random.Philox(counter=np.array(_numpy_counter_before((pos, row, pss, 0)), np.uint64),
+                          key=np.array((seed, 0), np.uint64))
+    w0 = int(bg.random_raw(4)[0])
+    assert orc.uniform24(seed, row, pos, pss) == (w0 >> 40) / 2.0 ** 24
+    # the counter words are not interchangeable: a swapped (row, position) draws another value
+    if row != pos:
+        bg = np.random.Philox(counter=np.array(_numpy_counter_before((row, pos, pss, 0)), np.uint64),
+                              key=np.array((seed, 0), np.uint64))
+        assert orc.uniform24(seed, row, pos, pss) != (int(bg.random_raw(4)[0]) >> 40) / 2.0 ** 24
+
+
 def test_uniform24_range_and_granularity(orc):
     us = np.array([orc.uniform24(42, r, p, s) for r in range(4) for p in range(64) for s in range(4)])
     assert us.min() >= 0.0 and us.max() < 1.0

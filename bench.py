@@ -36,14 +36,22 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# workload name -> (prompt positions, default steps, description, dtype)
+# workload name -> (prompt positions, default steps, description, dtype).  The dtype strings
+# name every rounding the path makes beyond the weights' own format: the FC / SwiGLU output
+# reaches the down projection rounded to a 15-bit mantissa in the persistent step's hand-over.
 WORKLOADS = {
     "gpt2_medium_q4_0": (256, 500, "GPT-2-Medium-shaped 24-layer speech-token decoder, Q4_0, 256-token prefill then {K} "
-                                   "{S} decode steps, batch 1", "q4_0 weights, fp32 accumulate, fp16 kv"),
+                                   "{S} decode steps, batch 1",
+                         "q4_0 weights, fp32 accumulate, fp16 kv; the FC output enters the down projection rounded "
+                         "to a 15-bit mantissa"),
     "gpt2_medium_q5_0": (256, 500, "GPT-2-Medium-shaped 24-layer speech-token decoder, Q5_0, 256-token prefill then {K} "
-                                   "{S} decode steps, batch 1", "q5_0 weights, fp32 accumulate, fp16 kv"),
+                                   "{S} decode steps, batch 1",
+                         "q5_0 weights, fp32 accumulate, fp16 kv; the FC output enters the down projection rounded "
+                         "to a 15-bit mantissa"),
     "llama520m_q8_0": (300, 600, "Llama-shaped ~520M 30-layer speech-token decoder, Q8_0, 300-token prefill then {K} "
-                                 "{S} decode steps, batch 1", "q8_0 weights, fp32 accumulate, fp16 kv"),
+                                 "{S} decode steps, batch 1",
+                       "q8_0 weights, fp32 accumulate, fp16 kv; the SwiGLU output enters the down projection rounded "
+                       "to a 15-bit mantissa"),
     "talker_cp_aff8": (170, 200, "Talker (28 layers, d 1024, 16 q / 8 kv heads of 128, SwiGLU 3072) + code predictor "
                                  "(5 layers, 15 sequential passes, vocab 2048), 8-bit affine group-64 weights, "
                                  "170 prompt frames then {K} {S} frames of 16 codes, batch 16",
@@ -88,7 +96,9 @@ def parse():
                     help="greedy, or a sampler-chain preset (t3: the T3 port's defaults; qwen: the Qwen3-TTS settings)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-gemv", action="store_true", help="skip the standalone tall-GEMV measurement")
+    ap.add_argument("--no-gemv", action="store_true", help="skip the standalone GEMV measurements")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="skip the Llama-520M (c4) and Talker + code predictor (c5) objects of the default line")
     ap.add_argument("--gemv-format", default="q8_0", choices=["q8_0", "q4_0", "q5_0", "aff8", "aff4_g64", "aff4_g32"],
                     help="weight format of the standalone tall GEMV (q8_0: the lone-GEMV workload's)")
     ap.add_argument("--eager", action="store_true",
@@ -119,18 +129,21 @@ def step_sources_hash():
         text = fh.read()
     h.update(text[text.index(a):text.index(b)].encode())
     return h.hexdigest()[:16]
-COUNTERS = os.path.join(ROOT, "profiles", "step_gpt2_medium_q4_0_counters.json")
-
-
-def counted_traffic(kernel, workload="gpt2_medium_q4_0"):
+def counted_traffic(kernel, workload, bytes_per_launch):
     """HBM-side bytes per launch of the step kernel from the committed FETCH_SIZE / WRITE_SIZE
-    summary (scaled by the copy calibration), or None when that summary was taken on other
-    kernel sources than the ones built now."""
-    if kernel != "step" or workload != "gpt2_medium_q4_0" or not os.path.exists(COUNTERS):
-        return None
-    with open(COUNTERS) as fh:
+    summary of this workload (scaled by the copy calibration), carried over to this run's window
+    of positions by the ratio counted / algorithmic bytes the summary measured; (None, reason)
+    when there is no summary or it was taken on other kernel sources than the ones built now."""
+    path = os.path.join(ROOT, "profiles", f"step_{workload}_counters.json")
+    if kernel != "step" or not os.path.exists(path):
+        return None, "no counter summary for this kernel and workload"
+    with open(path) as fh:
         d = json.load(fh)
-    return d["traffic_bytes_per_launch"] if d.get("sources_sha256_16") == step_sources_hash() else None
+    if d.get("sources_sha256_16") != step_sources_hash() or "algorithmic_bytes_per_launch" not in d:
+        return None, "the step kernel changed since its counters were taken"
+    ratio = d["traffic_bytes_per_launch"] / d["algorithmic_bytes_per_launch"]
+    return ratio * bytes_per_launch, (f"FETCH_SIZE + WRITE_SIZE (copy-calibrated) over {d['window']} read {ratio:.3f} x "
+                                      f"that window's algorithmic bytes; that ratio times this run's bytes_per_launch")
 
 
 class DeviceState:
@@ -236,10 +249,110 @@ def gemv_headline(seed, reps=7, fmt="q8_0"):
             "frac": gbs / roofline.HBM_PEAK_GBS, "timing": f"median over {reps} bursts of {burst} back-to-back launches, after 0.25 s of warm-up launches"}
 
 
+C1_N, C1_K, C1_CHAIN = 1024, 1024, 512
+
+
+def gemv_c1(seed, reps=200):
+    """The lone GEMV workload (one 1024 x 1024 Q8_0 matrix, x ~ N(0,1), batch 1): 1.12 MB, which
+    HBM streams in 0.14 us, so a single launch measures the launch, not the memory ("Every Frame Is
+    a Memory Read", §4: a fixed cost per kernel, and matvec efficiency growing with size).  Two
+    readings: the median duration of `reps` single launches, each bracketed by HIP events and
+    synchronised (minus the median of as many empty brackets); and the slope, a graph of 512
+    launches on 512 distinct matrices (574 MB, more than the Infinity Cache) replayed after a
+    warm-up, time per launch."""
+    import torch
+    from quantized_gemv_kv_amd import binding, roofline, synth
+    N, K = C1_N, C1_K
+    rng = synth.rng_for(seed, 4)
+    x = torch.from_numpy(synth.normal_f32(rng, (1, K))).cuda()
+    y = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    pb = binding.tsd_gemv_packed_bytes("q8_0", N, K)
+    row_b = K // 32 * 34
+    packed = torch.empty((C1_CHAIN, pb), dtype=torch.uint8, device="cuda")
+    canon = torch.empty(C1_CHAIN * N * row_b, dtype=torch.uint8, device="cuda")
+    for r0, blob in synth.q8_0_row_chunks(C1_CHAIN * N, K, seed):
+        canon[r0 * row_b: r0 * row_b + blob.size].copy_(torch.from_numpy(blob))
+    for i in range(C1_CHAIN):
+        binding.tsd_gemv_pack("q8_0", canon[i * N * row_b:(i + 1) * N * row_b], N, K, packed[i])
+    del canon
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+
+    def bracket(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3
+
+    warm(lambda: binding.tsd_gemv("q8_0", packed[0], N, K, 1, x, None, y))
+    empty = float(np.median([bracket(lambda: None) for _ in range(reps)]))
+    single = float(np.median([bracket(lambda: binding.tsd_gemv("q8_0", packed[0], N, K, 1, x, None, y))
+                              for _ in range(reps)])) - empty
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cs):
+        for i in range(C1_CHAIN):
+            binding.tsd_gemv("q8_0", packed[i], N, K, 1, x, None, y, stream=cs)
+    warm(g.replay)
+    per = float(np.median([bracket(g.replay) for _ in range(7)])) / C1_CHAIN
+    nbytes = roofline.gemv_bytes("q8_0", N, K)
+    del packed, g
+    return {"shape": f"Q8_0 {N}x{K}, batch 1", "bytes_per_gemv": nbytes,
+            "single_launch_us": single, "single_launch_gbs": nbytes / (single * 1e-6) / 1e9,
+            "chain_us_per_gemv": per, "chain_gbs": nbytes / (per * 1e-6) / 1e9,
+            "chain_frac": nbytes / (per * 1e-6) / 1e9 / roofline.HBM_PEAK_GBS,
+            "timing": f"single: median of {reps} synchronised launches under HIP events, minus the median empty "
+                      f"bracket ({empty:.1f} us); chain: one graph of {C1_CHAIN} launches on {C1_CHAIN} distinct "
+                      f"matrices, median of 7 replays after 0.25 s of warm-up replays, per launch"}
+
+
+def host_cpu():
+    """(CPU model name, logical CPUs of the host, CPUs this process may run on)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count(), len(os.sched_getaffinity(0))
+
+
+class pinned_thread:
+    """Pins the calling thread (Linux: pid 0 is the calling thread) to one CPU it may run on,
+    restoring its affinity afterwards; the oracle runs on this thread through ctypes."""
+
+    def __enter__(self):
+        self.saved = os.sched_getaffinity(0)
+        self.cpu = max(self.saved)
+        os.sched_setaffinity(0, {self.cpu})
+        return self
+
+    def __exit__(self, *exc):
+        os.sched_setaffinity(0, self.saved)
+
+
+def describe_host(pin):
+    model, n, _ = host_cpu()
+    return {"cpu_model": model, "nproc": n, "cpus_allowed": len(pin.saved), "pinned_to_cpu": pin.cpu, "threads": 1}
+
+
 def cpu_baseline(cfg, weights, seconds, seed):
-    """The CPU oracle as it stands (single-threaded C, fp64), timed on this host: decode steps
-    from position 256 over a random 256-position fp16 cache, until the time budget is spent."""
+    """The CPU oracle as it stands (single-threaded C, fp64), timed on this host with its thread
+    pinned to one CPU: decode steps from position 256 over a random 256-position fp16 cache, until
+    the time budget is spent."""
     import oracle
+    with pinned_thread() as pin:
+        r = _cpu_baseline(oracle, cfg, weights, seconds, seed)
+        r["host"] = describe_host(pin)
+    return r
+
+
+def _cpu_baseline(oracle, cfg, weights, seconds, seed):
     om = oracle.OracleModel(cfg, weights)
     from quantized_gemv_kv_amd import synth
     k, v = synth.kv_cache(cfg, PROMPT, seed=seed)
@@ -261,8 +374,16 @@ def cpu_baseline(cfg, weights, seconds, seed):
 
 def cpu_baseline_frames(cfg, weights, seconds, seed):
     """The CPU oracle on one batch row of the frame loop (rows are independent, so a 16-row frame
-    costs 16 row-frames): frames at positions 170.. over a random 170-position Talker cache."""
+    costs 16 row-frames): frames at positions 170.. over a random 170-position Talker cache, the
+    thread pinned to one CPU."""
     import oracle
+    with pinned_thread() as pin:
+        r = _cpu_baseline_frames(oracle, cfg, weights, seconds, seed)
+        r["host"] = describe_host(pin)
+    return r
+
+
+def _cpu_baseline_frames(oracle, cfg, weights, seconds, seed):
     from quantized_gemv_kv_amd import synth
     c1 = dict(cfg, batch=1)
     om = oracle.OracleModel(c1, weights)
@@ -336,49 +457,32 @@ def gemm_rows_headline(seed, reps=7):
             "timing": f"median over {reps} bursts of {burst} back-to-back calls (operand split + GEMM), after 0.25 s of warm-up calls"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library runs the decode step "
-              f"on a single GPU and does not shard it.", file=sys.stderr)
-        sys.exit(2)
+def measure(workload, K, W, seed, launch_mode="persistent", samp=None, cfg_weight=None, eager=False, time_kinds=True):
+    """One workload: the model at its real shape on seeded synthetic weights, its prompt (once
+    untimed, then from a reset model under HIP events), W warm-up steps, the context truncated back
+    to the prompt, then K timed steps (graph replays) bracketed by stream synchronisation and HIP
+    events on the model's stream.  With time_kinds, every kernel kind is then timed inside real
+    steps and the dominant one re-timed over the same K positions."""
     import torch
     from quantized_gemv_kv_amd import Model, roofline, synth
-
-    global WORKLOAD, PROMPT
-    WORKLOAD = args.workload
-    PROMPT, default_steps, desc, dtype = WORKLOADS[WORKLOAD]
-    if args.steps is None:
-        args.steps = default_steps
-    cfg = dict(synth.config(WORKLOAD), launch_mode=args.launch_mode)
+    prompt_n, _, desc, dtype = WORKLOADS[workload]
+    cfg = dict(synth.config(workload), launch_mode=launch_mode)
     frames = cfg["arch"] == "talker_cp"
-    if args.cfg is not None:
-        if frames:
-            print("--cfg applies to the GPT2/LLAMA workloads", file=sys.stderr)
-            sys.exit(2)
+    if cfg_weight is not None:
         cfg["batch"] = 2
-    K, W = args.steps, args.warmup
-    if PROMPT + max(K, W) > cfg["n_ctx"]:
-        print(f"steps/warmup exceed the {cfg['n_ctx']}-position context", file=sys.stderr)
-        sys.exit(2)
-    weights = synth.model_weights(cfg, args.seed)
+    if prompt_n + max(K, W) > cfg["n_ctx"]:
+        raise SystemExit(f"steps/warmup exceed the {cfg['n_ctx']}-position context")
+    weights = synth.model_weights(cfg, seed)
     stream = torch.cuda.Stream()
-    samp = SAMPLERS[args.sampler]
-    if samp is not None:
-        samp = dict(samp, seed=args.seed)
-    if args.cfg is not None:
-        samp = dict(samp or {"mode": 0, "seed": args.seed}, cfg=1, cfg_weight=args.cfg)
     model = Model(cfg, weights, stream=stream, sampling=samp)
-    prompt = torch.from_numpy(synth.prompt_tokens(cfg, PROMPT, seed=args.seed)).to("cuda")
-    dev_state = DeviceState()
-    step = model.step_eager if args.eager else model.step
+    prompt = torch.from_numpy(synth.prompt_tokens(cfg, prompt_n, seed=seed)).to("cuda")
+    step = model.step_eager if eager else model.step
+    prefill_ms = None
     with torch.cuda.stream(stream):
-        if args.eager:
-            k, v = synth.kv_cache(cfg, PROMPT, seed=args.seed)
-            model.load_kv(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), PROMPT)
+        if eager:
+            k, v = synth.kv_cache(cfg, prompt_n, seed=seed)
+            model.load_kv(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), prompt_n)
         else:
-            # the prompt, once untimed (first launches of its kernels), then again from a reset
-            # model under events
             model.prefill(prompt)
             stream.synchronize()
             model.reset()
@@ -391,7 +495,7 @@ def main():
         for _ in range(W):
             step(None, out=False)
         stream.synchronize()
-        model.truncate(PROMPT)
+        model.truncate(prompt_n)
         stream.synchronize()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -403,35 +507,95 @@ def main():
         stream.synchronize()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        wall = t1 - t0
     ms = e0.elapsed_time(e1)
-    ids = model.tokens(PROMPT, K).cpu().numpy()
+    model.synchronize()
+    ids = model.tokens(prompt_n, K).cpu().numpy()
     if frames:
         assert ids[..., 1:].max() < cfg["cp_vocab"], "sampled codes out of range"
     ids = ids.reshape(-1)
     assert ids.min() >= 0 and ids.max() < cfg["vocab"], "sampled ids out of range"
-
-    # dominant kernel: every kind timed inside real steps (event records around each launch on
-    # the model's stream), then the largest one re-timed over the timed region's positions.
-    # With the persistent step there is one kind: the step kernel itself.
     mode, n_wg = model.info()
-    kind_list = ("step",) if mode == "persistent" else ("qkv", "attn", "oproj", "fc", "down", "head")
-    kinds = {}
-    with torch.cuda.stream(stream):
-        for kind in kind_list:
-            model.truncate(PROMPT)
-            kinds[kind] = model.time_kernel(kind, min(K, 100))
-        dom = max(kinds, key=lambda k: kinds[k][0] * kinds[k][1])
-        model.truncate(PROMPT)
-        dom_us, dom_n = model.time_kernel(dom, K)
-    model.synchronize()
-    dom_bytes = (roofline.mean_step_bytes(cfg, PROMPT, K) if dom == "step"
-                 else roofline.mean_kernel_bytes(cfg, dom, PROMPT, K))
-    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    out = {"cfg": cfg, "weights": weights, "desc": desc, "prompt": prompt_n, "ms": ms, "wall_s": t1 - t0, "t0": t0, "t1": t1,
+           "mode": mode, "n_wg": n_wg, "prefill_ms": prefill_ms,
+           "dtype": dtype if mode == "persistent" or frames else dtype.split(";")[0]}
+    step_bytes = roofline.mean_step_bytes(cfg, prompt_n, K)
+    out["step_bytes"] = step_bytes
+    if time_kinds:
+        kind_list = ("step",) if mode == "persistent" else ("qkv", "attn", "oproj", "fc", "down", "head")
+        kinds = {}
+        with torch.cuda.stream(stream):
+            for kind in kind_list:
+                model.truncate(prompt_n)
+                kinds[kind] = model.time_kernel(kind, min(K, 100))
+            dom = max(kinds, key=lambda k: kinds[k][0] * kinds[k][1])
+            model.truncate(prompt_n)
+            dom_us, dom_n = model.time_kernel(dom, K)
+        model.synchronize()
+        dom_bytes = step_bytes if dom == "step" else roofline.mean_kernel_bytes(cfg, dom, prompt_n, K)
+        out.update(kinds=kinds, dom=dom, dom_us=dom_us, dom_n=dom_n, dom_bytes=dom_bytes)
+    model.close()
+    return out
 
-    step_bytes = roofline.mean_step_bytes(cfg, PROMPT, K)
+
+def summary_of(m, K):
+    """The compact object the default line carries for a second workload."""
+    from quantized_gemv_kv_amd import roofline
+    ms_step = m["ms"] / K
+    gbs = m["step_bytes"] / (ms_step * 1e-3) / 1e9
+    frames = m["cfg"]["arch"] == "talker_cp"
+    r = {"workload": m["desc"].format(K=K, S="greedy"), "steps": K, "ms_per_step": ms_step,
+         "value": K / (m["ms"] * 1e-3), "unit": "frames/s" if frames else "tokens/s",
+         "step_bytes": m["step_bytes"], "step_gbs": gbs, "step_frac_of_hbm_peak": gbs / roofline.HBM_PEAK_GBS,
+         "launch_mode": m["mode"], "dtype": m["dtype"], "prefill_ms": m["prefill_ms"]}
+    if "dom" in m:
+        r["kernel"] = m["dom"]
+        r["kernel_us"] = m["dom_us"]
+        r["kernel_frac_of_hbm_peak"] = m["dom_bytes"] / (m["dom_us"] * 1e-6) / 1e9 / roofline.HBM_PEAK_GBS
+    if frames:
+        r["codes_per_s"] = r["value"] * m["cfg"]["batch"] * m["cfg"]["n_codebooks"]
+    return r
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library runs the decode step "
+              f"on a single GPU and does not shard it.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from quantized_gemv_kv_amd import roofline
+
+    global WORKLOAD, PROMPT
+    WORKLOAD = args.workload
+    PROMPT, default_steps, _, _ = WORKLOADS[WORKLOAD]
+    if args.steps is None:
+        args.steps = default_steps
+    K, W = args.steps, args.warmup
+    frames = WORKLOAD == "talker_cp_aff8"
+    if args.cfg is not None and frames:
+        print("--cfg applies to the GPT2/LLAMA workloads", file=sys.stderr)
+        sys.exit(2)
+    samp = SAMPLERS[args.sampler]
+    if samp is not None:
+        samp = dict(samp, seed=args.seed)
+    if args.cfg is not None:
+        samp = dict(samp or {"mode": 0, "seed": args.seed}, cfg=1, cfg_weight=args.cfg)
+    dev_state = DeviceState()
+    m = measure(WORKLOAD, K, W, args.seed, args.launch_mode, samp, args.cfg, args.eager)
+    cfg, weights = m["cfg"], m.pop("weights")
+    ms = m["ms"]
+    dom, dom_us, dom_n, dom_bytes = m["dom"], m["dom_us"], m["dom_n"], m["dom_bytes"]
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    traffic, traffic_note = counted_traffic(dom, WORKLOAD, dom_bytes)
+    step_bytes = m["step_bytes"]
     ms_step = ms / K
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": achieved, "peak": roofline.HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / roofline.HBM_PEAK_GBS, "traffic": traffic, "traffic_note": traffic_note,
+            "kernel": dom, "launch_us": dom_us, "launches_per_step": dom_n, "bytes_per_launch": dom_bytes}
+    if WORKLOAD.startswith("gpt2_medium"):
+        roof["cache_note"] = ("the 176 MB of fixed weights fit MI355X's 256 MB Infinity Cache, so part of this 'HBM' "
+                              "stream may be served from that memory-side cache")
     result = {
         "metric": ("Talker + code-predictor frames/sec at batch 16 + achieved HBM GB/s (% of peak) per frame" if frames
                    else "decode tokens/sec at batch 1 + achieved HBM GB/s (% of peak) per step"),
@@ -444,24 +608,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": m["dtype"],
         "data": "synthetic (seeded random weights, prompt ids and values; no checkpoint)",
-        "config": {"workload": desc.format(K=K, S="greedy" if samp is None or samp.get("mode", 0) == 0 else "sampled")
+        "config": {"workload": m["desc"].format(K=K, S="greedy" if samp is None or samp.get("mode", 0) == 0 else "sampled")
                    + ("" if args.cfg is None else f"; classifier-free guidance: a conditioned and an unconditioned row "
                                                   f"per step (batch 2), one token from cond + {args.cfg} (cond - uncond)"), "d_model": cfg["d_model"], "n_layer": cfg["n_layer"],
                    "n_head": cfg["n_head"], "d_ff": cfg["d_ff"], "vocab": cfg["vocab"],
-                   "prompt": PROMPT, "global_batch": cfg["batch"], "launch_mode": mode, "workgroups": n_wg,
+                   "prompt": PROMPT, "global_batch": cfg["batch"], "launch_mode": m["mode"], "workgroups": m["n_wg"],
                    "sampler": args.sampler if samp is None else dict(samp, preset=args.sampler),
                    "cfg": args.cfg},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": roofline.HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / roofline.HBM_PEAK_GBS, "traffic": counted_traffic(dom, WORKLOAD),
-                     "kernel": dom, "launch_us": dom_us, "launches_per_step": dom_n,
-                     "bytes_per_launch": dom_bytes},
-        "kernel_us": {k: round(v[0], 3) for k, v in kinds.items()},
+        "roofline": roof,
+        "kernel_us": {k: round(v[0], 3) for k, v in m["kinds"].items()},
         "step_gbs": gbs,
         "step_frac_of_hbm_peak": gbs / roofline.HBM_PEAK_GBS,
         "step_bytes": step_bytes,
-        "wall_tokens_per_s": K / wall,
+        "wall_tokens_per_s": K / m["wall_s"],
     }
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib * (1 << 20) // 4
@@ -478,17 +639,26 @@ def main():
             result["gemm_rows"] = gemm_rows_headline(args.seed)
         else:
             result["gemv"] = gemv_headline(args.seed, fmt=args.gemv_format)
+            result["gemv_1024"] = gemv_c1(args.seed)
     if not args.eager:
-        result["prefill"] = {"positions": PROMPT, "rows": PROMPT * cfg["batch"], "ms": prefill_ms,
-                             "positions_per_s": PROMPT / (prefill_ms * 1e-3),
+        result["prefill"] = {"positions": PROMPT, "rows": PROMPT * cfg["batch"], "ms": m["prefill_ms"],
+                             "positions_per_s": PROMPT / (m["prefill_ms"] * 1e-3),
                              "path": "prompt pass (matrix-core products over all prompt rows, causal flash "
                                      "attention), the last position through the decode step"
                                      + (" (the whole frame)" if frames else "")}
-    result["device_state"] = dev_state.summary(t0, t1)
+    # the other two decoders the pages time, at their real shapes, in the same run (greedy)
+    if WORKLOAD == "gpt2_medium_q4_0" and not args.no_extra_configs and not args.eager and args.cfg is None \
+            and samp is None:
+        c4 = measure("llama520m_q8_0", min(K, 100), min(W, 20), args.seed)
+        c4.pop("weights")
+        result["c4"] = summary_of(c4, min(K, 100))
+        c5 = measure("talker_cp_aff8", min(K, 50), min(W, 5), args.seed, time_kinds=False)
+        c5.pop("weights")
+        result["c5"] = summary_of(c5, min(K, 50))
+    result["device_state"] = dev_state.summary(m["t0"], m["t1"])
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = (cpu_baseline_frames if frames else cpu_baseline)(with_sampler(cfg, samp), weights,
                                                                                     args.cpu_seconds, args.seed)
-    model.close()
     print(json.dumps(result), flush=True)
 
 

@@ -348,6 +348,19 @@ tsd_status tsd_attention(const float* d_q, const uint16_t* d_k, const uint16_t* 
                          int Hkv, int hd, int n_keys, int n_ctx, float* d_out, void* d_scratch,
                          size_t scratch_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, serving loops or
+ * harnesses that forbid hipMalloc): tsd_attention with the split partials in a fixed array inside
+ * the library (TSD_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends) instead of
+ * d_scratch.  Arguments, layouts and results are those of tsd_attention (the same kernels).  It
+ * allocates nothing.  TSD_ERR_INVALID_ARGUMENT when the shape's partials
+ * (tsd_attention_scratch_bytes) exceed TSD_NOALLOC_SCRATCH_BYTES, and for what tsd_attention
+ * rejects.  Every call on one GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams or threads) race and must be serialised by the caller.  The stream must belong to the
+ * current device. */
+#define TSD_NOALLOC_SCRATCH_BYTES (4u << 20)
+tsd_status tsd_attention_noalloc(const float* d_q, const uint16_t* d_k, const uint16_t* d_v, int B, int H, int Hkv,
+                                 int hd, int n_keys, int n_ctx, float* d_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

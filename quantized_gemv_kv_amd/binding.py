@@ -27,7 +27,7 @@ EXPORTS = ["tsd_workspace_bytes", "tsd_model_create", "tsd_prefill", "tsd_step",
            "tsd_attention_scratch_bytes", "tsd_attention", "tsd_time_kernel", "tsd_synchronize",
            "tsd_model_info", "tsd_sample_topk", "tsd_sample", "tsd_gemm_rows_packed_bytes", "tsd_gemm_rows_pack",
            "tsd_gemm_rows_scratch_bytes", "tsd_gemm_rows", "tsd_prefill_stepwise", "tsd_gemm_scratch_bytes", "tsd_gemm",
-           "tsd_get_kv", "tsd_debug_gemv"]
+           "tsd_get_kv", "tsd_debug_gemv", "tsd_attention_noalloc"]
 KERNEL_KINDS = {"qkv": 0, "attn": 1, "oproj": 2, "fc": 3, "down": 4, "head": 5, "step": 6}
 
 
@@ -112,6 +112,7 @@ def lib():
             "tsd_gemm_scratch_bytes": [_I, _I, ctypes.POINTER(_SZ)],
             "tsd_gemm": [_I, _P, _I, _I, _I, _P, _P, _P, _P, _SZ, _P],
             "tsd_debug_gemv": [_I, _P, _SZ, _P, _P, _I, _I, _I, _P],
+            "tsd_attention_noalloc": [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -234,6 +235,15 @@ def tsd_attention_scratch_bytes(B, H, n_ctx, hd) -> int:
 def tsd_attention(q, k, v, B, H, Hkv, hd, n_keys, n_ctx, out, scratch, stream=None):
     _check(lib().tsd_attention(_ptr(q), _ptr(k), _ptr(v), B, H, Hkv, hd, n_keys, n_ctx, _ptr(out), _ptr(scratch),
                                scratch.numel(), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 4 << 20   # TSD_NOALLOC_SCRATCH_BYTES
+
+
+def tsd_attention_noalloc(q, k, v, B, H, Hkv, hd, n_keys, n_ctx, out, stream=None):
+    """tsd_attention with the library's own per-GPU partials array (no scratch argument)."""
+    _check(lib().tsd_attention_noalloc(_ptr(q), _ptr(k), _ptr(v), B, H, Hkv, hd, n_keys, n_ctx, _ptr(out),
+                                       _stream(stream)))
 
 
 # ---- convenience: a model whose memory torch owns --------------------------------------------

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libtsd.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["gemv.hip", "attention.hip", "misc.hip", "sampler.hip", "step.hip", "frame.hip", "talker.hip", "prefill.hip", "model.hip", "debug.hip"]
+SOURCES = ["gemv.hip", "attention.hip", "misc.hip", "sampler.hip", "step.hip", "frame.hip", "talker.hip", "prefill.hip", "model.hip", "debug.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

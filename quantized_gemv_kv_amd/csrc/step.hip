@@ -42,7 +42,7 @@ using namespace core;
 constexpr int NT = 256;
 constexpr int NWAVE = NT / 64;
 constexpr int KTILE = 64;    // keys per wave in the attention phase (4 waves: one 256-key chunk)
-constexpr int SG = 4;        // attention chunks merged per exchange round in the O-proj input
+constexpr int SG = 4;        // attention chunks merged per exchange round in the O-proj input (at most)
 
 enum { A_GPT2 = 0, A_LLAMA = 1 };
 enum { IN_XCHG = 0, IN_NORM = 1, IN_EMB_NORM = 2, IN_ATTN = 3, IN_XCHG32 = 4 };
@@ -92,7 +92,6 @@ struct Geo {
 struct Smem {
     float* xl;       // [B][MAX_K] phase input, swizzled for the weight format
     float* red;      // [4 * NWAVE]
-    float* ml;       // [B * H * SG * 2] attention (m, l) of a group of chunks
     int* abort;      // a wait of this workgroup timed out
 };
 
@@ -161,9 +160,23 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
             for (int j = 0; j < J; ++j) v[b][j] = glb(er)[elem(j)] + (C::GPT2 ? glb(pr)[elem(j)] : 0.f);
         }
     } else if constexpr (IN == IN_ATTN) {
-        // element k = h*HD + i; chunk s of head h published (o[0..HD), m, l) in the log2 domain
-        constexpr int HD = C::HD, H = K / HD, PS = HD + 2;
-        static_assert(B * H * SG * 2 <= NT, "one (m, l) word per thread");
+        // element k = t + NT*j of row b is dim k % HD of head k / HD; chunk s of head h published
+        // (o[0..HD), m, l) in the log2 domain.  A wave covers 64 consecutive elements and HD is a
+        // multiple of 64, so each (b, j) is one head on every lane of a wave: the wave merges its
+        // own heads (the (m, l) words spread over its lanes, then read back as uniform values),
+        // with no barrier and no index arithmetic that depends on the context length.
+        constexpr int HD = C::HD, PS = HD + 2;
+        static_assert(HD % 64 == 0 && K % 64 == 0, "a wave's 64 elements lie in one head");
+        constexpr int SGA = 2 * B * J * SG <= 64 ? SG : (32 / (B * J) > 0 ? 32 / (B * J) : 1);
+        static_assert(2 * B * J * SGA <= 64, "one (m or l) word per lane");
+        const int lane = t & 63;
+        int hj[J], ij[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int base = min((t & ~63) + NT * j, K - 64);   // the wave's first element (clamped into K)
+            hj[j] = base / HD;
+            ij[j] = base % HD + lane;
+        }
         float Mr[B][J], Lr[B][J], Or[B][J];
 #pragma unroll
         for (int b = 0; b < B; ++b)
@@ -173,50 +186,56 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
                 Lr[b][j] = 0.f;
                 Or[b][j] = 0.f;
             }
-        for (int s0 = 0; s0 < cx.S; s0 += SG) {
-            const int ns = min(SG, cx.S - s0);
-            // word 0: this thread's (m or l) word of the group (table [b][h][u][m, l]);
-            // word 1 + (b*J + j)*SG + u: row b's chunk s0+u output for element j (chunks past the
-            // context re-read the group's last chunk and are not used)
-            const int nml = H * ns * 2;
-            const int tm = min(t, B * nml - 1);
-            const int mb = tm / nml, tr = tm - mb * nml;
-            const int mh = tr / (2 * ns), mr = tr - mh * 2 * ns;
-            const uint64_t* mp = src + mb * xs + ((size_t)mh * a.max_split + s0 + (mr >> 1)) * PS + HD + (mr & 1);
+        // lane 2 * ((b * J + j) * SGA + u) + c holds word c (m, l) of chunk s0 + u of (b, j)
+        const int ml_q = min(lane >> 1, B * J * SGA - 1), ml_u = ml_q % SGA, ml_bj = ml_q / SGA;
+        const int ml_b = ml_bj / J, ml_j = ml_bj - ml_b * J;
+        for (int s0 = 0; s0 < cx.S; s0 += SGA) {
+            const int ns = min(SGA, cx.S - s0);
+            // word 0: this lane's (m or l) word; 1 + (b*J + j)*SGA + u: the chunk-(s0+u) output of
+            // (b, j) at this lane's dim (chunks past the context re-read the last one, unused)
             auto addr = [&](int q) -> const uint64_t* {
-                if (q == 0) return mp;
-                const int bj = (q - 1) / SG, u = (q - 1) % SG;
+                if (q == 0) {
+                    int hh = 0;
+#pragma unroll
+                    for (int j = 0; j < J; ++j)
+                        if (j == ml_j) hh = hj[j];
+                    return src + ml_b * xs + ((size_t)hh * a.max_split + s0 + min(ml_u, ns - 1)) * PS + HD + (lane & 1);
+                }
+                const int bj = (q - 1) / SGA, u = (q - 1) % SGA;
                 const int b = bj / J, j = bj - b * J;
-                const int k = elem(j), h = k / HD, i = k - h * HD;
-                return src + b * xs + ((size_t)h * a.max_split + s0 + min(u, ns - 1)) * PS + i;
+                return src + b * xs + ((size_t)hj[j] * a.max_split + s0 + min(u, ns - 1)) * PS + ij[j];
             };
-            constexpr int NW = 1 + B * J * SG;
-            auto use = [&](int q) { return q == 0 || (q - 1) % SG < ns; };
+            constexpr int NW = 1 + B * J * SGA;
+            auto use = [&](int q) { return q == 0 || (q - 1) % SGA < ns; };
             uint64_t wv[NW];
 #pragma unroll
             for (int q = 0; q < NW; ++q)
                 if (use(q)) wv[q] = xchg::load(addr(q));
             ok &= xchg::settle_if(wv, use, addr, ep, cx.limit, a.abort_word);
-            if (s0 > 0) lds_barrier();                     // the previous group's readers of ml are done
-            if (t < B * nml) sm.ml[t] = xchg::value(wv[0]);
-            lds_barrier();
+            const float mlv = xchg::value(wv[0]);
 #pragma unroll
             for (int b = 0; b < B; ++b)
 #pragma unroll
                 for (int j = 0; j < J; ++j) {
-                    const float* mlh = sm.ml + b * nml + (elem(j) / HD) * ns * 2;
+                    float mu[SGA], lu[SGA];
+#pragma unroll
+                    for (int u = 0; u < SGA; ++u) {
+                        const int ln = 2 * ((b * J + j) * SGA + u);
+                        mu[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv), ln));
+                        lu[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv), ln + 1));
+                    }
                     float M = Mr[b][j];
 #pragma unroll
-                    for (int u = 0; u < SG; ++u)
-                        if (u < ns) M = fmaxf(M, mlh[2 * u]);
+                    for (int u = 0; u < SGA; ++u)
+                        if (u < ns) M = fmaxf(M, mu[u]);
                     const float sc = exp2f(Mr[b][j] - M);          // rescale of the running sums (0 at start)
                     float L = Lr[b][j] * sc, O = Or[b][j] * sc;
 #pragma unroll
-                    for (int u = 0; u < SG; ++u) {
+                    for (int u = 0; u < SGA; ++u) {
                         if (u < ns) {
-                            const float wgt = exp2f(mlh[2 * u] - M);
-                            L = fmaf(mlh[2 * u + 1], wgt, L);
-                            O = fmaf(xchg::value(wv[1 + (b * J + j) * SG + u]), wgt, O);
+                            const float wgt = exp2f(mu[u] - M);
+                            L = fmaf(lu[u], wgt, L);
+                            O = fmaf(xchg::value(wv[1 + (b * J + j) * SGA + u]), wgt, O);
                         }
                     }
                     Mr[b][j] = M;
@@ -625,6 +644,7 @@ __device__ __forceinline__ bool attn_phase(const StepArgs& a, const Ctx& cx, con
     constexpr int LPK = HD / 8, KPI = 64 / LPK, R = KTILE / KPI, PS = HD + 2;
     __shared__ float ow[NWAVE][HD];
     __shared__ float mw[NWAVE], lw[NWAVE];
+    __shared__ float qkv_l[3 * HD];   // the query, new key and new value of the item
     const int items = C::B * H * cx.S;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c = lane % LPK, kq = lane / LPK;
@@ -643,26 +663,36 @@ __device__ __forceinline__ bool attn_phase(const StepArgs& a, const Ctx& cx, con
             kr[r] = ld16(kcache + head_off + (size_t)key * HD + c * 8);
             vr[r] = ld16(vcache + head_off + (size_t)key * HD + c * 8);
         }
-        // words 0-7: query dims 8c..8c+7 of head h; 8-15 / 16-23: the new key / value of kv head g
-        const uint64_t* xq = a.x_qkv + b * a.xs_qkv;
-        const uint64_t* pq = xq + h * HD + c * 8;
-        const uint64_t* pk = xq + QD + g * HD + c * 8;
-        const uint64_t* pv = xq + QD + KD + g * HD + c * 8;
-        auto addr = [&](int i) { return (i < 8 ? pq : i < 16 ? pk - 8 : pv - 16) + i; };
-        uint64_t wx[24];
+        // The query of head h and the new key / value of kv head g (3 HD words) are polled by wave 0
+        // alone, each lane its own words, and handed to the other waves through LDS: when every
+        // wave polled the same words, the waves of one workgroup saw them up to a microsecond
+        // apart (polls of one line from one compute unit merge, and a merged poll can return the
+        // stale word).
+        constexpr int NQ = 3 * HD / 64;   // words per lane of wave 0
+        if (wave == 0) {
+            const uint64_t* xq = a.x_qkv + b * a.xs_qkv;
+            auto addr = [&](int i) {
+                const int w = lane + 64 * i;
+                return w < HD ? xq + h * HD + w : w < 2 * HD ? xq + QD + g * HD + (w - HD) : xq + QD + KD + g * HD + (w - 2 * HD);
+            };
+            uint64_t wx[NQ];
 #pragma unroll
-        for (int i = 0; i < 24; ++i) wx[i] = xchg::load(addr(i));
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        if (!xchg::settle_n(wx, 24, addr, ep_qkv, cx.limit, a.abort_word)) *sm.abort = 1;
+            for (int i = 0; i < NQ; ++i) wx[i] = xchg::load(addr(i));
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            if (!xchg::settle_n(wx, NQ, addr, ep_qkv, cx.limit, a.abort_word)) *sm.abort = 1;
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) qkv_l[lane + 64 * i] = xchg::value(wx[i]);
+        }
+        lds_barrier();
         // the new position's row (exact fp16 values) replaces whatever the cache held there
         uint4 nk, nv;
         {
             __half2 hk[4], hv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                hk[e] = __floats2half2_rn(xchg::value(wx[8 + 2 * e]), xchg::value(wx[8 + 2 * e + 1]));
-                hv[e] = __floats2half2_rn(xchg::value(wx[16 + 2 * e]), xchg::value(wx[16 + 2 * e + 1]));
+                hk[e] = __floats2half2_rn(qkv_l[HD + c * 8 + 2 * e], qkv_l[HD + c * 8 + 2 * e + 1]);
+                hv[e] = __floats2half2_rn(qkv_l[2 * HD + c * 8 + 2 * e], qkv_l[2 * HD + c * 8 + 2 * e + 1]);
             }
             nk = *(const uint4*)hk;
             nv = *(const uint4*)hv;
@@ -675,7 +705,7 @@ __device__ __forceinline__ bool attn_phase(const StepArgs& a, const Ctx& cx, con
             }
         float q[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) q[e] = xchg::value(wx[e]) * qscale;
+        for (int e = 0; e < 8; ++e) q[e] = qkv_l[c * 8 + e] * qscale;
 
         float sc[R];
         float mloc = -INFINITY;
@@ -799,9 +829,8 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
     static_assert(RAW_BYTES <= 56 * 1024, "LDS of one workgroup");
     __shared__ __align__(16) unsigned char raw[RAW_BYTES];
     __shared__ float red[4 * NWAVE];
-    __shared__ float ml[B * C::H * SG * 2];
     __shared__ int s_abort;
-    Smem sm{(float*)raw, red, ml, &s_abort};
+    Smem sm{(float*)raw, red, &s_abort};
 
     if (threadIdx.x == 0) s_abort = 0;
     Ctx cx;

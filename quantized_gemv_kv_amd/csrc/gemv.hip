@@ -485,15 +485,18 @@ hipError_t launch_gemv_stream(int fmt, const PackedMat& W, const ProArgs& pa, co
 {
     if (W.K > MAX_K || !gemv_shape_ok(fmt, W.K) || W.N <= 0) return hipErrorInvalidValue;
     const int lpr = W.K / fmt_elems_per_slot(fmt);
-    if (lpr <= 64 && lpr >= 4) {   // rows fit one wave and a row group holds at least NL lanes
-        constexpr int NL = 4;
-        const int rpb = NWAVE * (64 / lpr) * NL;
+    // rows fit one wave and a row group holds at least NL lanes; the 4-bit formats take eight rows
+    // per lane (their per-lane overhead, spread over twice the codes)
+    const int nl = fmt_nibbles(fmt) && lpr >= 8 ? 8 : 4;
+    if (lpr <= 64 && lpr >= 4) {
+        const int rpb = NWAVE * (64 / lpr) * nl;
         const dim3 grid((W.N + rpb - 1) / rpb);
         const size_t lds = (size_t)W.K * sizeof(float);
-#define TSD_STREAM(F_) \
-    if (fmt == F_) hipLaunchKernelGGL((k_gemv_stream<F_, NL>), grid, dim3(WG), lds, st, W, pa.src, ea.bias, ea.y);
-        TSD_STREAM(FMT_Q4_0) TSD_STREAM(FMT_Q8_0) TSD_STREAM(FMT_AFF8) TSD_STREAM(FMT_Q5_0) TSD_STREAM(FMT_AFF4_G64)
-        TSD_STREAM(FMT_AFF4_G32)
+#define TSD_STREAM(F_, NL_) \
+    if (fmt == F_ && nl == NL_) hipLaunchKernelGGL((k_gemv_stream<F_, NL_>), grid, dim3(WG), lds, st, W, pa.src, ea.bias, ea.y);
+        TSD_STREAM(FMT_Q4_0, 4) TSD_STREAM(FMT_Q8_0, 4) TSD_STREAM(FMT_AFF8, 4) TSD_STREAM(FMT_Q5_0, 4)
+        TSD_STREAM(FMT_AFF4_G64, 4) TSD_STREAM(FMT_AFF4_G32, 4)
+        TSD_STREAM(FMT_Q4_0, 8) TSD_STREAM(FMT_Q5_0, 8) TSD_STREAM(FMT_AFF4_G64, 8) TSD_STREAM(FMT_AFF4_G32, 8)
 #undef TSD_STREAM
         return hipGetLastError();
     }

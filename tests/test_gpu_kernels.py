@@ -55,6 +55,10 @@ GEMV_CASES = [
     ("aff4_g32", 4096, 1024, 1), # and of 32
     ("aff4_g32", 1024, 2048, 4),
     ("aff4_g32", 5, 32, 1),
+    ("q4_0", 1000, 1024, 2),     # eight rows per lane (rows of 32 lanes), a ragged last tile
+    ("aff4_g64", 1000, 1024, 1),
+    ("aff4_g32", 70, 1024, 1),
+    ("q5_0", 65, 1024, 1),
 ]
 
 

@@ -196,7 +196,9 @@ tsd_status tsd_prefill(tsd_model* m, const int32_t* d_tokens, int n, int32_t* d_
  * the id the step sampled there. */
 tsd_status tsd_prefill_stepwise(tsd_model* m, const int32_t* d_tokens, int n, int32_t* d_next);
 
-/* One decode step (one frame for TALKER_CP) at position n_past: replays the captured graph.
+/* One decode step (one frame for TALKER_CP) at position n_past: launches the persistent step
+ * kernel (PERSISTENT: one launch, which a caller may capture into its own graph), or replays the
+ * captured step graph (PER_OPERATOR, TALKER_CP).
  * d_in is [batch][tokens per position] or NULL for "the ids sampled by the previous step";
  * d_next may be NULL.  The sampled ids are also appended to the device token history
  * (tsd_get_tokens).  n_past increases by one. */

@@ -819,6 +819,15 @@ tsd_status tsd_model_destroy(tsd_model* m)
 const char* tsd_last_error(const tsd_model* m) { return m ? m->err.c_str() : g_err.c_str(); }
 
 namespace {
+// One step on the model's stream.  A persistent step is a single kernel: it is launched directly,
+// which leaves ~2 us between back-to-back steps where replaying it as a one-node graph left ~7 us
+// (it can still be captured into a caller's graph); the other modes replay their step graph.
+hipError_t launch_one_step(tsd_model* m, hipGraphExec_t x)
+{
+    if (m->step_fn && x == m->exec) return launch_step(m->step_fn, m->d_sa, m->n_wg, m->st);
+    return hipGraphLaunch(x, m->st);
+}
+
 // the ids of one position (rows of tok_per_pos ids, src_stride apart) into the step's input slots,
 // checked on the device: a rejected set leaves the slots alone and raises the bad-input word
 hipError_t set_input(tsd_model* m, const int32_t* src, long long src_stride)
@@ -836,7 +845,7 @@ tsd_status tsd_step(tsd_model* m, const int32_t* d_in, int32_t* d_next)
     const int nt = m->c.batch * m->tpp;
     if (d_in) HIP_TRY(m, set_input(m, d_in, m->tpp), "set input");
     HIP_TRY(m, before_launch(m), "exchange restart");
-    HIP_TRY(m, hipGraphLaunch(m->exec, m->st), "graph launch");
+    HIP_TRY(m, launch_one_step(m, m->exec), "step launch");
     if (d_next) HIP_TRY(m, launch_copy_i32(d_next, m->tok, nt, m->st), "copy ids");
     m->n_past += 1;
     return TSD_OK;
@@ -883,7 +892,7 @@ tsd_status tsd_prefill(tsd_model* m, const int32_t* d_tokens, int n, int32_t* d_
     // the last position: one decode step (head, sampler, history; the whole frame for TALKER_CP)
     if (e == hipSuccess) e = set_input(m, d_tokens + (size_t)(n - 1) * m->tpp, (long long)n * m->tpp);
     if (e == hipSuccess) e = before_launch(m);
-    if (e == hipSuccess) e = hipGraphLaunch(m->exec, m->st);
+    if (e == hipSuccess) e = launch_one_step(m, m->exec);
     if (e != hipSuccess) {
         if (n > 1) (void)launch_fill_i32(m->pos, n_past0, 1, m->st);   // the position as it was
         return hip_fail(m, e, "prefill");
@@ -909,7 +918,7 @@ tsd_status tsd_prefill_stepwise(tsd_model* m, const int32_t* d_tokens, int n, in
         HIP_TRY(m, before_launch(m), "exchange restart");
         // TALKER_CP prompt frames before the last need neither head nor predictor
         hipGraphExec_t x = (m->exec_talker && t + 1 < n) ? m->exec_talker : m->exec;
-        HIP_TRY(m, hipGraphLaunch(x, m->st), "graph launch");
+        HIP_TRY(m, launch_one_step(m, x), "step launch");
         m->n_past += 1;
     }
     if (d_next) HIP_TRY(m, launch_copy_i32(d_next, m->tok, nt, m->st), "copy ids");

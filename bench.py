@@ -146,6 +146,11 @@ def counted_traffic(kernel, workload, bytes_per_launch):
                                       f"that window's algorithmic bytes; that ratio times this run's bytes_per_launch")
 
 
+def under_profiler():
+    """True when a rocprofv3 tool library is loaded into this process."""
+    return "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ)
+
+
 class DeviceState:
     """amd-smi samples (socket power, graphics and memory clocks, temperatures) taken by a
     background thread while the benchmark runs; summary() reports those that fall inside the
@@ -154,8 +159,12 @@ class DeviceState:
     def __init__(self):
         import threading
         self.samples, self.stop = [], threading.Event()
-        self.thread = threading.Thread(target=self._run, daemon=True)
-        self.thread.start()
+        # under a profiler every child process gets its tool library, which initialises the GPU,
+        # and amd-smi's launcher would then replace such a process: no sampling there
+        self.skipped = under_profiler()
+        if not self.skipped:
+            self.thread = threading.Thread(target=self._run, daemon=True)
+            self.thread.start()
 
     @staticmethod
     def _one():
@@ -184,6 +193,8 @@ class DeviceState:
 
     def summary(self, t_begin, t_end):
         self.stop.set()
+        if self.skipped:
+            return {"skipped": "running under a profiler"}
         inside = [v for a, b, v in self.samples if t_begin + self.LAG <= b <= t_end + self.LAG + 0.1]
         powers = [v["power_w"] for _, _, v in self.samples if v["power_w"] is not None]
         return {"samples_in_timed_region": inside, "samples_total": len(self.samples),

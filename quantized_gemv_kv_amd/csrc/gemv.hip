@@ -420,43 +420,86 @@ hipError_t launch_gemv(int fmt, int pro, int epi, const PackedMat& W, const ProA
 }
 
 namespace {
+// sum over a slot of 32 four-bit codes in Q4_0's nibble order times x, where the x of the high
+// nibbles (elements 16..31) has already been divided by 16: a high code is then used in place,
+// as the byte value 16 q (one mask per word instead of a shift and a mask), and each product
+// (16 q) (x / 16) is exactly q x
+__device__ __forceinline__ float slot_dot_hi16(const uint4 w, const float* __restrict__ x)
+{
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = ws[j] & 0x0F0F0F0Fu, hi = ws[j] & 0xF0F0F0F0u;
+        a0 = fmaf(ubyte<0>(lo), x[4 * j + 0], a0);
+        a1 = fmaf(ubyte<0>(hi), x[16 + 4 * j + 0], a1);
+        a0 = fmaf(ubyte<1>(lo), x[4 * j + 1], a0);
+        a1 = fmaf(ubyte<1>(hi), x[16 + 4 * j + 1], a1);
+        a0 = fmaf(ubyte<2>(lo), x[4 * j + 2], a0);
+        a1 = fmaf(ubyte<2>(hi), x[16 + 4 * j + 2], a1);
+        a0 = fmaf(ubyte<3>(lo), x[4 * j + 3], a0);
+        a1 = fmaf(ubyte<3>(hi), x[16 + 4 * j + 3], a1);
+    }
+    return a0 + a1;
+}
+
 // y = W x (+bias) for a matrix streamed once, rows of at most one wave (slots per row a power of
 // two <= 64): every lane issues its NL weight loads (non-temporal) and scale loads first, then x
-// is staged in LDS, then the lane dots its slot with each of its rows; lane r of a row group
-// writes the group's row r.
+// is staged in LDS, then the lane dots its slot with each of its rows.  With eight rows per lane
+// the partial sums are reduced across the row group by a butterfly that halves them at each of
+// its first three stages (each lane keeps one half and sends the other to its partner: seven
+// lane moves and adds instead of eight full reductions), after which lane s holds the total of
+// row s % 8; with four, each row is reduced on its own.  Lane s < NL stores row s.
 template <int F, int NL>
 __global__ __launch_bounds__(WG) void k_gemv_stream(const PackedMat W, const float* __restrict__ x,
                                                     const float* __restrict__ bias, float* __restrict__ y)
 {
     constexpr int E = FmtT<F>::E, SPS = FmtT<F>::SLOTS_PER_SCALE, G = FmtT<F>::SCALE_GROUP;
+    constexpr bool HI16 = fmt_nibbles(F) && F != FMT_Q5_0;   // Q5_0's fifth bit does not fit 16 q
+    static_assert(NL == 4 || NL == 8, "four or eight rows per lane");
     extern __shared__ float4 xl4[];
     const int K = W.K, N = W.N, lpr = K / E, spr = K / G;
     const size_t rb = fmt_row_bytes(F, K);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int slot = lane & (lpr - 1), sub = lane / lpr;
-    const int row0 = ((blockIdx.x * NWAVE + wave) * (64 / lpr) + sub) * NL;
+    const int lsh = __ffs(lpr) - 1;   // lpr is a power of two
+    const int slot = lane & (lpr - 1), sub = lane >> lsh;
+    const int row0 = ((blockIdx.x * NWAVE + wave) * (64 >> lsh) + sub) * NL;
     typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    // 32-bit byte offsets from the arrays' bases (the launcher keeps this kernel to matrices of
+    // less than 4 GB) and 24-bit multiplies: no 64-bit or quarter-rate arithmetic per row; rows
+    // past the matrix (j > lim) reload its last row, whose result no lane stores
+    const int lim = N - 1 - row0;
+    const uint32_t q0 = (uint32_t)row0 * (uint32_t)rb + (uint32_t)slot * 16u;
+    const uint32_t s0 = (uint32_t)row0 * (uint32_t)spr + (uint32_t)(slot / SPS);
+    const uint32_t h0 = (uint32_t)row0 * (uint32_t)(K / 32) + (uint32_t)slot;
     uint4 w[NL];
     uint32_t sc[NL], sb[NL], hb[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-        const int row = min(row0 + i, N - 1);
-        const v4u v = __builtin_nontemporal_load((const v4u*)(W.q + (size_t)row * rb + (size_t)slot * 16));
+        const int j = min(i, lim);
+        const uint32_t so = 2u * (s0 + (uint32_t)__mul24(j, spr));
+        const v4u v = __builtin_nontemporal_load((const v4u*)(W.q + (q0 + (uint32_t)__mul24(j, (int)rb))));
         w[i] = make_uint4(v.x, v.y, v.z, v.w);
-        sc[i] = __half_as_ushort(W.s[(size_t)row * spr + slot / SPS]);
+        sc[i] = *(const unsigned short*)((const uint8_t*)W.s + so);
         sb[i] = 0u;
         hb[i] = 0u;
-        if constexpr (fmt_affine(F)) sb[i] = __half_as_ushort(W.b[(size_t)row * spr + slot / SPS]);
-        if constexpr (F == FMT_Q5_0) hb[i] = W.h[(size_t)row * (K / 32) + slot];
+        if constexpr (fmt_affine(F)) sb[i] = *(const unsigned short*)((const uint8_t*)W.b + so);
+        if constexpr (F == FMT_Q5_0) hb[i] = *(const uint32_t*)((const uint8_t*)W.h + 4u * (h0 + (uint32_t)__mul24(j, K / 32)));
     }
     const int er = min(row0 + (slot < NL ? slot : NL - 1), N - 1);
     const float bv = bias ? bias[er] : 0.f;
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    for (int c = threadIdx.x; c < K / 4; c += WG) xl4[swz<E>(4 * c, lpr)] = ((const float4*)x)[c];
+    // x staged in LDS; for the nibble formats the high half of every 32-element block (elements
+    // 16..31, the high nibbles) is stored divided by 16 (see slot_dot_hi16)
+    for (int c = threadIdx.x; c < K / 4; c += WG) {
+        float4 v = ((const float4*)x)[c];
+        if (HI16 && (c & 7) >= 4) v = make_float4(v.x * 0.0625f, v.y * 0.0625f, v.z * 0.0625f, v.w * 0.0625f);
+        xl4[swz<E>(4 * c, lpr)] = v;
+    }
     __syncthreads();
     float xs[E];
-    float sx = 0.f;
+    float sl = 0.f, sh = 0.f;   // the slot's sums of x over its low and high halves (high: / 16)
 #pragma unroll
     for (int e4 = 0; e4 < E / 4; ++e4) {
         const float4 v = xl4[e4 * lpr + slot];
@@ -464,19 +507,42 @@ __global__ __launch_bounds__(WG) void k_gemv_stream(const PackedMat W, const flo
         xs[4 * e4 + 1] = v.y;
         xs[4 * e4 + 2] = v.z;
         xs[4 * e4 + 3] = v.w;
-        sx += (v.x + v.y) + (v.z + v.w);
+        if (HI16 && e4 >= 4) sh += (v.x + v.y) + (v.z + v.w);
+        else sl += (v.x + v.y) + (v.z + v.w);
     }
-    float part[NL];
+    const float sx = HI16 ? fmaf(16.f, sh, sl) : sl;
+    float p[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-        const float d = slot_dot<F>(w[i], xs, hb[i]);
-        const float v = slot_value<F>(d, sx, __half2float(__ushort_as_half((unsigned short)sc[i])),
-                                      __half2float(__ushort_as_half((unsigned short)sb[i])));
-        part[i] = group_sum(v, lpr);
+        float d;
+        if constexpr (HI16) d = slot_dot_hi16(w[i], xs);
+        else d = slot_dot<F>(w[i], xs, hb[i]);
+        p[i] = slot_value<F>(d, sx, __half2float(__ushort_as_half((unsigned short)sc[i])),
+                             __half2float(__ushort_as_half((unsigned short)sb[i])));
     }
-    float t = part[0];
+    float t;
+    if constexpr (NL == 8) {
+        // stage 1: partner slot ^ 7 (half-row mirror), the half kept chosen by slot bit 2; then
+        // partner slot ^ 2 by bit 1, and slot ^ 1 by bit 0: lane s keeps row s % 8
+        const bool k2 = slot & 4, k1 = slot & 2, k0 = slot & 1;
+        float q[4], r[2];
 #pragma unroll
-    for (int i = 1; i < NL; ++i) t = slot == i ? part[i] : t;
+        for (int i = 0; i < 4; ++i) q[i] = (k2 ? p[i + 4] : p[i]) + dpp_mov<0x141>(k2 ? p[i] : p[i + 4]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) r[i] = (k1 ? q[i + 2] : q[i]) + dpp_mov<0x4E>(k1 ? q[i] : q[i + 2]);
+        t = (k0 ? r[1] : r[0]) + dpp_mov<0xB1>(k0 ? r[0] : r[1]);
+        // the lanes 8, 16 and 32 apart hold the same row
+        if (lpr >= 16) t += dpp_mov<0x128>(t);   // row_ror:8
+        if (lpr >= 32) t = swap16_sum(t);
+        if (lpr >= 64) t = swap32_sum(t);
+    } else {
+        float part[NL];
+#pragma unroll
+        for (int i = 0; i < NL; ++i) part[i] = group_sum(p[i], lpr);
+        t = part[0];
+#pragma unroll
+        for (int i = 1; i < NL; ++i) t = slot == i ? part[i] : t;
+    }
     if (slot < NL && row0 + slot < N) y[row0 + slot] = t + bv;
 }
 }  // namespace
@@ -485,10 +551,11 @@ hipError_t launch_gemv_stream(int fmt, const PackedMat& W, const ProArgs& pa, co
 {
     if (W.K > MAX_K || !gemv_shape_ok(fmt, W.K) || W.N <= 0) return hipErrorInvalidValue;
     const int lpr = W.K / fmt_elems_per_slot(fmt);
-    // rows fit one wave and a row group holds at least NL lanes; the 4-bit formats take eight rows
-    // per lane (their per-lane overhead, spread over twice the codes)
+    // rows fit one wave, a row group holds at least NL lanes and the payload is under 4 GB (the
+    // kernel's 32-bit offsets); the 4-bit formats take eight rows per lane (their per-lane
+    // overhead, spread over twice the codes)
     const int nl = fmt_nibbles(fmt) && lpr >= 8 ? 8 : 4;
-    if (lpr <= 64 && lpr >= 4) {
+    if (lpr <= 64 && lpr >= 4 && (size_t)W.N * fmt_row_bytes(fmt, W.K) < ((size_t)1 << 32)) {
         const int rpb = NWAVE * (64 / lpr) * nl;
         const dim3 grid((W.N + rpb - 1) / rpb);
         const size_t lds = (size_t)W.K * sizeof(float);

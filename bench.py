@@ -548,7 +548,7 @@ def measure(workload, K, W, seed, launch_mode="persistent", samp=None, cfg_weigh
     return out
 
 
-def summary_of(m, K):
+def summary_of(m, K, workload):
     """The compact object the default line carries for a second workload."""
     from quantized_gemv_kv_amd import roofline
     ms_step = m["ms"] / K
@@ -562,6 +562,7 @@ def summary_of(m, K):
         r["kernel"] = m["dom"]
         r["kernel_us"] = m["dom_us"]
         r["kernel_frac_of_hbm_peak"] = m["dom_bytes"] / (m["dom_us"] * 1e-6) / 1e9 / roofline.HBM_PEAK_GBS
+        r["kernel_traffic"], r["kernel_traffic_note"] = counted_traffic(m["dom"], workload, m["dom_bytes"])
     if frames:
         r["codes_per_s"] = r["value"] * m["cfg"]["batch"] * m["cfg"]["n_codebooks"]
     return r
@@ -662,10 +663,10 @@ def main():
             and samp is None:
         c4 = measure("llama520m_q8_0", min(K, 100), min(W, 20), args.seed)
         c4.pop("weights")
-        result["c4"] = summary_of(c4, min(K, 100))
+        result["c4"] = summary_of(c4, min(K, 100), "llama520m_q8_0")
         c5 = measure("talker_cp_aff8", min(K, 50), min(W, 5), args.seed, time_kinds=False)
         c5.pop("weights")
-        result["c5"] = summary_of(c5, min(K, 50))
+        result["c5"] = summary_of(c5, min(K, 50), "talker_cp_aff8")
     result["device_state"] = dev_state.summary(m["t0"], m["t1"])
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = (cpu_baseline_frames if frames else cpu_baseline)(with_sampler(cfg, samp), weights,

@@ -129,6 +129,15 @@ __device__ __forceinline__ float group_sum(float v, int g)
     return v;
 }
 __device__ __forceinline__ float wave_sum(float v) { return group_sum(v, 64); }
+// maximum over aligned groups of g lanes (g a power of two <= 16); every lane gets its group's
+__device__ __forceinline__ float group_max(float v, int g)
+{
+    if (g >= 2) v = fmaxf(v, dpp_mov<0xB1>(v));
+    if (g >= 4) v = fmaxf(v, dpp_mov<0x4E>(v));
+    if (g >= 8) v = fmaxf(v, dpp_mov<0x141>(v));
+    if (g >= 16) v = fmaxf(v, dpp_mov<0x140>(v));
+    return v;
+}
 __device__ __forceinline__ float wave_max(float v)
 {
     v = fmaxf(v, dpp_mov<0xB1>(v));

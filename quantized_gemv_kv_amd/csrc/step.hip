@@ -189,21 +189,21 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
         // lane 2 * ((b * J + j) * SGA + u) + c holds word c (m, l) of chunk s0 + u of (b, j)
         const int ml_q = min(lane >> 1, B * J * SGA - 1), ml_u = ml_q % SGA, ml_bj = ml_q / SGA;
         const int ml_b = ml_bj / J, ml_j = ml_bj - ml_b * J;
-        for (int s0 = 0; s0 < cx.S; s0 += SGA) {
-            const int ns = min(SGA, cx.S - s0);
-            // word 0: this lane's (m or l) word; 1 + (b*J + j)*SGA + u: the chunk-(s0+u) output of
-            // (b, j) at this lane's dim (chunks past the context re-read the last one, unused)
+        if (cx.S <= SGA) {
+            // every chunk in one round (up to SGA chunks of context): the merge weights are
+            // computed across the lanes that hold the (m, l) words, then read back per (b, j)
+            const int ns = cx.S;
             auto addr = [&](int q) -> const uint64_t* {
                 if (q == 0) {
                     int hh = 0;
 #pragma unroll
                     for (int j = 0; j < J; ++j)
                         if (j == ml_j) hh = hj[j];
-                    return src + ml_b * xs + ((size_t)hh * a.max_split + s0 + min(ml_u, ns - 1)) * PS + HD + (lane & 1);
+                    return src + ml_b * xs + ((size_t)hh * a.max_split + min(ml_u, ns - 1)) * PS + HD + (lane & 1);
                 }
                 const int bj = (q - 1) / SGA, u = (q - 1) % SGA;
                 const int b = bj / J, j = bj - b * J;
-                return src + b * xs + ((size_t)hj[j] * a.max_split + s0 + min(u, ns - 1)) * PS + ij[j];
+                return src + b * xs + ((size_t)hj[j] * a.max_split + min(u, ns - 1)) * PS + ij[j];
             };
             constexpr int NW = 1 + B * J * SGA;
             auto use = [&](int q) { return q == 0 || (q - 1) % SGA < ns; };
@@ -212,41 +212,88 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
             for (int q = 0; q < NW; ++q)
                 if (use(q)) wv[q] = xchg::load(addr(q));
             ok &= xchg::settle_if(wv, use, addr, ep, cx.limit, a.abort_word);
+            // lane 2 q + c, q = (b J + j) SGA + u: m (c = 0) or l (c = 1) of chunk u of (b, j); the
+            // 2 SGA lanes of a (b, j) form one aligned group
             const float mlv = xchg::value(wv[0]);
+            const bool live = ml_u < ns && lane < 2 * B * J * SGA;
+            const float mm = (lane & 1) == 0 && live ? mlv : -INFINITY;
+            const float M = group_max(mm, 2 * SGA);
+            const float w = exp2f(mm - M);                       // the chunk's weight on its m lane, else 0
+            const float wl = dpp_mov<0xB1>(w);                   // on an l lane: its chunk's weight
+            const float L = group_sum((lane & 1) && live ? mlv * wl : 0.f, 2 * SGA);
+            const float f = w / L;                               // final weight of the chunk (m lanes)
 #pragma unroll
             for (int b = 0; b < B; ++b)
 #pragma unroll
                 for (int j = 0; j < J; ++j) {
-                    float mu[SGA], lu[SGA];
-#pragma unroll
-                    for (int u = 0; u < SGA; ++u) {
-                        const int ln = 2 * ((b * J + j) * SGA + u);
-                        mu[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv), ln));
-                        lu[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv), ln + 1));
-                    }
-                    float M = Mr[b][j];
+                    float O = 0.f;
 #pragma unroll
                     for (int u = 0; u < SGA; ++u)
-                        if (u < ns) M = fmaxf(M, mu[u]);
-                    const float sc = exp2f(Mr[b][j] - M);          // rescale of the running sums (0 at start)
-                    float L = Lr[b][j] * sc, O = Or[b][j] * sc;
-#pragma unroll
-                    for (int u = 0; u < SGA; ++u) {
-                        if (u < ns) {
-                            const float wgt = exp2f(mu[u] - M);
-                            L = fmaf(lu[u], wgt, L);
-                            O = fmaf(xchg::value(wv[1 + (b * J + j) * SGA + u]), wgt, O);
-                        }
-                    }
-                    Mr[b][j] = M;
-                    Lr[b][j] = L;
-                    Or[b][j] = O;
+                        if (u < ns)
+                            O = fmaf(xchg::value(wv[1 + (b * J + j) * SGA + u]),
+                                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), 2 * ((b * J + j) * SGA + u))), O);
+                    v[b][j] = O;
                 }
+        } else {
+            for (int s0 = 0; s0 < cx.S; s0 += SGA) {
+                const int ns = min(SGA, cx.S - s0);
+                // word 0: this lane's (m or l) word; 1 + (b*J + j)*SGA + u: the chunk-(s0+u) output of
+                // (b, j) at this lane's dim (chunks past the context re-read the last one, unused)
+                auto addr = [&](int q) -> const uint64_t* {
+                    if (q == 0) {
+                        int hh = 0;
+    #pragma unroll
+                        for (int j = 0; j < J; ++j)
+                            if (j == ml_j) hh = hj[j];
+                        return src + ml_b * xs + ((size_t)hh * a.max_split + s0 + min(ml_u, ns - 1)) * PS + HD + (lane & 1);
+                    }
+                    const int bj = (q - 1) / SGA, u = (q - 1) % SGA;
+                    const int b = bj / J, j = bj - b * J;
+                    return src + b * xs + ((size_t)hj[j] * a.max_split + s0 + min(u, ns - 1)) * PS + ij[j];
+                };
+                constexpr int NW = 1 + B * J * SGA;
+                auto use = [&](int q) { return q == 0 || (q - 1) % SGA < ns; };
+                uint64_t wv[NW];
+    #pragma unroll
+                for (int q = 0; q < NW; ++q)
+                    if (use(q)) wv[q] = xchg::load(addr(q));
+                ok &= xchg::settle_if(wv, use, addr, ep, cx.limit, a.abort_word);
+                const float mlv = xchg::value(wv[0]);
+    #pragma unroll
+                for (int b = 0; b < B; ++b)
+    #pragma unroll
+                    for (int j = 0; j < J; ++j) {
+                        float mu[SGA], lu[SGA];
+    #pragma unroll
+                        for (int u = 0; u < SGA; ++u) {
+                            const int ln = 2 * ((b * J + j) * SGA + u);
+                            mu[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv), ln));
+                            lu[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv), ln + 1));
+                        }
+                        float M = Mr[b][j];
+    #pragma unroll
+                        for (int u = 0; u < SGA; ++u)
+                            if (u < ns) M = fmaxf(M, mu[u]);
+                        const float sc = exp2f(Mr[b][j] - M);          // rescale of the running sums (0 at start)
+                        float L = Lr[b][j] * sc, O = Or[b][j] * sc;
+    #pragma unroll
+                        for (int u = 0; u < SGA; ++u) {
+                            if (u < ns) {
+                                const float wgt = exp2f(mu[u] - M);
+                                L = fmaf(lu[u], wgt, L);
+                                O = fmaf(xchg::value(wv[1 + (b * J + j) * SGA + u]), wgt, O);
+                            }
+                        }
+                        Mr[b][j] = M;
+                        Lr[b][j] = L;
+                        Or[b][j] = O;
+                    }
+            }
+    #pragma unroll
+            for (int b = 0; b < B; ++b)
+    #pragma unroll
+                for (int j = 0; j < J; ++j) v[b][j] = __fdividef(Or[b][j], Lr[b][j]);
         }
-#pragma unroll
-        for (int b = 0; b < B; ++b)
-#pragma unroll
-            for (int j = 0; j < J; ++j) v[b][j] = __fdividef(Or[b][j], Lr[b][j]);
     } else if constexpr (IN == IN_XCHG32) {
         constexpr int NW = B * J;
         auto addr = [&](int q) -> const uint32_t* {

@@ -86,7 +86,15 @@ struct Mm16Out {
     const int* posp;
     int pos_value;
     const uint32_t* err;  // STORE: when *err is set (a rejected input) nothing is written
+    // QKV_ROPE, fused with the attention (launch_qkv_attention): every value also goes out as an
+    // exchange word xq[b * ldx + col] (q, then the fp16-rounded k, then v, columns as the rows of
+    // W) tagged with epoch (*xctr) * FUSE_EPOCHS + xidx + 1; null xq: not published
+    uint64_t* xq;
+    int ldx;
+    const uint32_t* xctr;
+    int xidx;
 };
+constexpr int FUSE_EPOCHS = 128;   // fused launches per frame, at most (epochs FUSE_EPOCHS apart per frame)
 
 // A norm's input prepared one row per workgroup: the rows (rows b < B) come from
 //   ROW_EMB:  sum over c < n_tab of tab[c][codes[b * ld_codes + c]] (ids clamped into rows[c]),
@@ -147,11 +155,22 @@ struct PickArgs {
     const uint32_t* err; // when *err is set (a rejected input) nothing is written
 };
 hipError_t launch_pick(const PickArgs& a, hipStream_t st);
+// The QKV product of a layer (QKV_ROPE epilogue, publishing its values as exchange words, o.xq
+// set) and the attention of that layer in one launch: after the product's workgroups, one
+// workgroup per (head, row) preloads the cache rows of the positions before the new one, polls
+// its query and the new key and value from the exchange (bounded by limit ticks of the 100 MHz
+// clock; on time-out it raises *abort_word and leaves its output unwritten) and writes the
+// output projection's operand as attention with act_hi set does (a.n_ctx <= 512).
+hipError_t launch_qkv_attention(const TiledMat& W, const MmIn& in, const Mm16Out& o, const AttnArgs& a, long long limit,
+                                uint32_t* abort_word, hipStream_t st);
+bool qkv_attention_fits(const TiledMat& W, const AttnArgs& a);
 // y[i] = sum over s < S of part[s * slice + i] for i < n
 hipError_t launch_sum_slices(const float* part, int S, long long slice, float* y, long long n, hipStream_t st);
 // hist[*pos][0..n) = codes[0..n) (n may be 0), with seq: seq[*pos * B + b] = codes[b * C] for
 // b < B (the consumed code 0 of a frame no pick ran on); then *pos += 1.  Nothing when *err is set.
+// *fctr (the fused launches' epoch counter, unless null) += 1 in every case.
 hipError_t launch_frame_done(const int* codes, int n, int* hist, int* pos, int* seq, int B, int C, const uint32_t* err,
-                             hipStream_t st);
+                             uint32_t* fctr, hipStream_t st);
+hipError_t launch_bump_u32(uint32_t* p, hipStream_t st);   // *p += 1 (one thread)
 
 }  // namespace tsd

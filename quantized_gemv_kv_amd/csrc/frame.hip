@@ -28,6 +28,7 @@
 // between layers and the residual stream is never re-read to build an operand.
 #include <math.h>
 
+#include "exchange.h"
 #include "gemv_core.h"
 #include "frame.h"
 #include "sampler.h"
@@ -133,7 +134,7 @@ __device__ __forceinline__ void prefetch(const Mm16Out& o, int tile, int N, int 
 // lane (j, c16) holds Y[4 j + i][n] for i < 4; tile = the 16-row tile of W
 template <int EPI>
 __device__ __forceinline__ void epilogue(const Mm16Out& o, int tile, int N, int j, int c16, int sl, int pos,
-                                         const Pre& pre, const float4v& acc)
+                                         const Pre& pre, const float4v& acc, uint32_t xep)
 {
     const int n = tile * 16 + c16;
     if constexpr (EPI == MM_STORE) {
@@ -166,11 +167,13 @@ __device__ __forceinline__ void epilogue(const Mm16Out& o, int tile, int N, int 
         }
     } else {
         const int half = o.hd >> 1;
+        // the exchange copy for a fused attention (the words of row b at xq + b * ldx, epoch xep)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float partner = __shfl_xor(acc[i], 1, 64);
             const int b = 4 * j + i;
             if (b >= o.rows || n >= N) continue;
+            uint64_t* xr = o.xq ? o.xq + (size_t)b * o.ldx : nullptr;
             if (n < o.qrows + o.krows) {
                 if (c16 & 1) continue;
                 const bool isk = n >= o.qrows;
@@ -182,15 +185,26 @@ __device__ __forceinline__ void epilogue(const Mm16Out& o, int tile, int N, int 
                     TSD_GLOBAL float* qr = glb(o.q) + (size_t)b * o.qrows + h * o.hd;
                     qr[e] = ra;
                     qr[e + half] = rb;
+                    if (xr) {
+                        xchg::store(xr + h * o.hd + e, ra, xep);
+                        xchg::store(xr + h * o.hd + e + half, rb, xep);
+                    }
                 } else {
                     TSD_GLOBAL _Float16* kr =
                         (TSD_GLOBAL _Float16*)glb(o.kc) + (((size_t)b * o.Hkv + h) * o.n_ctx + pos) * o.hd;
-                    kr[e] = (_Float16)ra;
-                    kr[e + half] = (_Float16)rb;
+                    const _Float16 ka = (_Float16)ra, kb = (_Float16)rb;
+                    kr[e] = ka;
+                    kr[e + half] = kb;
+                    if (xr) {
+                        xchg::store(xr + o.qrows + h * o.hd + e, (float)ka, xep);
+                        xchg::store(xr + o.qrows + h * o.hd + e + half, (float)kb, xep);
+                    }
                 }
             } else {
                 const int rr = n - o.qrows - o.krows, h = rr / o.hd, e = rr - h * o.hd;
-                ((TSD_GLOBAL _Float16*)glb(o.vc))[(((size_t)b * o.Hkv + h) * o.n_ctx + pos) * o.hd + e] = (_Float16)acc[i];
+                const _Float16 v = (_Float16)acc[i];
+                ((TSD_GLOBAL _Float16*)glb(o.vc))[(((size_t)b * o.Hkv + h) * o.n_ctx + pos) * o.hd + e] = v;
+                if (xr) xchg::store(xr + n, (float)v, xep);
             }
         }
     }
@@ -202,11 +216,11 @@ __device__ __forceinline__ void epilogue(const Mm16Out& o, int tile, int N, int 
 // tiles, then its operand fragment, which serves all T tiles), then converts and runs the MFMAs;
 // the waves add their results in LDS and wave 0 runs the epilogue.
 template <int EPI, int T, int NW, int U>
-__global__ __launch_bounds__(64 * NW) void k_mm16(const TiledMat W, const MmIn in, const Mm16Out o)
+__device__ __forceinline__ void mm16_block(const TiledMat& W, const MmIn& in, const Mm16Out& o, const int bx, const int S,
+                                           const int sl)
 {
     const int K = W.K, G = K >> 6, N = W.N, tiles = (N + 15) >> 4;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane >> 4, c16 = lane & 15;
-    const int S = gridDim.y, sl = blockIdx.y;
     const int g_lo = (int)((long long)G * sl / S), g_hi = (int)((long long)G * (sl + 1) / S);
     const int cnt = g_hi - g_lo, q = cnt / NW, r = cnt - q * NW;
     const int w_lo = g_lo + wave * q + (wave < r ? wave : r), w_n = q + (wave < r ? 1 : 0);
@@ -215,7 +229,7 @@ __global__ __launch_bounds__(64 * NW) void k_mm16(const TiledMat W, const MmIn i
     const TSD_GLOBAL uint32_t* sbr[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-        int tile = blockIdx.x * T + t;
+        int tile = bx * T + t;
         tile = tile < tiles ? tile : tiles - 1;   // tiles past the matrix reload the last one and store nothing
         wr[t] = (const TSD_GLOBAL u32x4*)glb(W.q) + (size_t)tile * G * 64 + lane;
         sbr[t] = glb(W.sb) + (size_t)tile * G * 16 + c16;
@@ -232,12 +246,14 @@ __global__ __launch_bounds__(64 * NW) void k_mm16(const TiledMat W, const MmIn i
             if (sb_part + 16 * p < in.n_ssq) sp[p] = glb(in.ssq)[(size_t)(sb_part + 16 * p) * MM_ROWS + sb_row];
     // the epilogue's own inputs (wave 0 runs it)
     const int pos = EPI == MM_QKV_ROPE ? (o.posp ? ld_uniform(o.posp) : o.pos_value) : 0;
+    // a fused attention's epoch, read with the position (long before the epilogue needs it)
+    const uint32_t xep = EPI == MM_QKV_ROPE && o.xq ? (uint32_t)ld_uniform((const int*)o.xctr) * (uint32_t)FUSE_EPOCHS + (uint32_t)o.xidx + 1u : 0u;
     // a head's logits are not written after a rejected input
     const bool skip = EPI == MM_STORE && o.err && ld_uniform((const int*)o.err);
     Pre pre[T];
     if (wave == 0)
 #pragma unroll
-        for (int t = 0; t < T; ++t) prefetch<EPI>(o, blockIdx.x * T + t, N, j, c16, pos, pre[t]);
+        for (int t = 0; t < T; ++t) prefetch<EPI>(o, bx * T + t, N, j, c16, pos, pre[t]);
     half8 ones;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
@@ -333,8 +349,195 @@ __global__ __launch_bounds__(64 * NW) void k_mm16(const TiledMat W, const MmIn i
         if (norm)
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[t][i] *= rrow[4 * j + i];
-        epilogue<EPI>(o, blockIdx.x * T + t, N, j, c16, sl, pos, pre[t], acc[t]);
+        epilogue<EPI>(o, bx * T + t, N, j, c16, sl, pos, pre[t], acc[t], xep);
     }
+}
+
+template <int EPI, int T, int NW, int U>
+__global__ __launch_bounds__(64 * NW) void k_mm16(const TiledMat W, const MmIn in, const Mm16Out o)
+{
+    mm16_block<EPI, T, NW, U>(W, in, o, blockIdx.x, gridDim.y, blockIdx.y);
+}
+
+// ---- the QKV product fused with the attention --------------------------------------------------
+// One workgroup (four waves) per (head h, row b): the split-KV attention of attention.hip with the
+// whole cache in one item (n_ctx <= 512), each wave taking key tiles wave, wave + 4, ...  The rows
+// of the positions before the new one were written by earlier launches; the new position's key
+// and value, and the query, come from the exchange words the product's workgroups publish in the
+// same launch.  The first tile of each wave is loaded before the wait, so it streams in while the
+// product finishes elsewhere.
+template <int HD, int TILE>
+__device__ __forceinline__ void attn16_item(const AttnArgs& a, const int h, const int b, const uint64_t* xq, const int ldx,
+                                            const uint32_t ep, const long long limit, uint32_t* abort_word)
+{
+    constexpr int NWV = 4;
+    constexpr int LPK = HD / 8;           // lanes per key, 8 dims (16 bytes) each
+    constexpr int KPI = 64 / LPK;         // keys per load instruction
+    constexpr int R = TILE / KPI;         // load rounds per tile
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int pos = a.pos ? ld_uniform(a.pos) : a.n_keys - 1;   // the new position
+    const int n_keys = pos + 1;
+    const int g = h / (a.H / a.Hkv);
+    const int c = lane % LPK, kq = lane / LPK;
+    const size_t head_off = ((size_t)b * a.Hkv + g) * a.n_ctx * HD;
+    __shared__ float ow[NWV][HD];
+    __shared__ float mw[NWV], lw[NWV];
+    __shared__ float qs[HD];
+    __shared__ __align__(16) _Float16 kn[HD], vn[HD];
+    __shared__ int bail;
+
+    auto load_tile = [&](int tile, uint4 (&kr)[R], uint4 (&vr)[R]) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int key = min(tile * TILE + r * KPI + kq, pos);   // the slot of pos itself is replaced below
+            kr[r] = *(const uint4*)(a.k + head_off + (size_t)key * HD + c * 8);
+            vr[r] = *(const uint4*)(a.v + head_off + (size_t)key * HD + c * 8);
+        }
+    };
+    uint4 kr[R], vr[R];
+    int tile = wave;
+    load_tile(tile, kr, vr);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    // wave 0 polls the query of head h and the new key and value of kv head g (row b)
+    if (wave == 0) {
+        constexpr int NQ = 3 * HD / 64;
+        const int qd = a.H * HD, kd = a.Hkv * HD;
+        auto addr = [&](int i) -> const uint64_t* {
+            const int e = lane + 64 * i, part = e / HD, d = e - part * HD;
+            const int col = part == 0 ? h * HD + d : (part == 1 ? qd : qd + kd) + g * HD + d;
+            return xq + (size_t)b * ldx + col;
+        };
+        uint64_t w[NQ];
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) w[i] = xchg::load(addr(i));
+        const bool ok = xchg::settle_n(w, NQ, addr, ep, limit, abort_word);
+        const float qscale = 1.4426950408889634f / sqrtf((float)HD);   // log2(e) / sqrt(hd): exp2 softmax
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int e = lane + 64 * i, part = e / HD, d = e - part * HD;
+            const float v = xchg::value(w[i]);
+            if (part == 0) qs[d] = v * qscale;
+            else if (part == 1) kn[d] = (_Float16)v;
+            else vn[d] = (_Float16)v;
+        }
+        if (lane == 0) bail = ok ? 0 : 1;
+        if (!ok && lane == 0) xchg::raise_abort(abort_word);
+    }
+    __syncthreads();
+    if (bail) return;
+    float q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = qs[c * 8 + e];
+    const uint4 knew = *(const uint4*)&kn[c * 8], vnew = *(const uint4*)&vn[c * 8];
+
+    // online softmax over this wave's tiles (log2 domain)
+    float m = -INFINITY, l = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (; tile * TILE < n_keys; tile += NWV) {
+        if (tile != wave) load_tile(tile, kr, vr);
+        float sc[R];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int key = tile * TILE + r * KPI + kq;
+            if (key == pos) {
+                kr[r] = knew;
+                vr[r] = vnew;
+            }
+            const __half2* kh = (const __half2*)&kr[r];
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float2 f = __half22float2(kh[e]);
+                acc = fmaf(f.x, q[2 * e], acc);
+                acc = fmaf(f.y, q[2 * e + 1], acc);
+            }
+            acc = group_sum(acc, LPK);
+            sc[r] = key < n_keys ? acc : -INFINITY;
+            mt = fmaxf(mt, sc[r]);
+        }
+        mt = wave_max(mt);
+        const float mn = fmaxf(m, mt);
+        const float rs = exp2f(m - mn);   // 0 for the first tile (m = -inf)
+        l *= rs;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= rs;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const bool valid = tile * TILE + r * KPI + kq < n_keys;
+            const float p = valid ? exp2f(sc[r] - mn) : 0.f;
+            l += p;
+            const uint4 vv = valid ? vr[r] : make_uint4(0u, 0u, 0u, 0u);
+            const __half2* vh = (const __half2*)&vv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float2 f = __half22float2(vh[e]);
+                o[2 * e] = fmaf(p, f.x, o[2 * e]);
+                o[2 * e + 1] = fmaf(p, f.y, o[2 * e + 1]);
+            }
+        }
+        m = mn;
+    }
+    // every key's p is held by its LPK lanes: the wave sum counts it LPK times (exact scaling)
+    l = wave_sum(l) * (1.0f / LPK);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        if constexpr (LPK == 8) o[e] += dpp_mov<0x128>(o[e]);   // lanes i and i ^ 8 share dims
+        o[e] = swap32_sum(swap16_sum(o[e]));
+    }
+    if (kq == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ow[wave][c * 8 + e] = o[e];
+    }
+    if (lane == 0) {
+        mw[wave] = m;
+        lw[wave] = l;
+    }
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) M = fmaxf(M, mw[w]);
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) L = fmaf(lw[w], exp2f(mw[w] - M), L);   // a wave without keys adds 0
+    const float inv = 1.0f / L;
+    for (int i = threadIdx.x; i < HD; i += 64 * NWV) {
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) acc = fmaf(ow[w][i], exp2f(mw[w] - M), acc);
+        const float y = acc * inv;
+        const _Float16 hi = (_Float16)y;
+        const size_t idx = il_act(b, h * HD + i);
+        ((TSD_GLOBAL _Float16*)a.act_hi)[idx] = hi;
+        ((TSD_GLOBAL _Float16*)a.act_lo)[idx] = (_Float16)(y - (float)hi);
+    }
+}
+
+// workgroups [0, n_gemm): the QKV product (one 16-row tile each); then one per (head, row)
+template <int U, int HD, int TILE>
+__global__ __launch_bounds__(256) void k_qkv_attn(const TiledMat W, const MmIn in, const Mm16Out o, const AttnArgs a,
+                                                  const int n_gemm, const long long limit, uint32_t* abort_word)
+{
+    if ((int)blockIdx.x < n_gemm) {
+        mm16_block<MM_QKV_ROPE, 1, 4, U>(W, in, o, blockIdx.x, 1, 0);
+        return;
+    }
+    // the R = H / Hkv query heads of one (row, kv head) read the same cache rows: their items
+    // are 8 workgroups apart, which puts them on one XCD and lets its L2 serve the second read
+    // (when the (row, kv head) pairs come in multiples of 8; else items in (row, head) order)
+    const int item = blockIdx.x - n_gemm, R = a.H / a.Hkv;
+    int h, b;
+    if ((a.B * a.Hkv) % 8 == 0) {
+        const int pair = item / (8 * R) * 8 + item % 8, r = item / 8 % R;
+        b = pair / a.Hkv;
+        h = (pair - b * a.Hkv) * R + r;
+    } else {
+        h = item % a.H;
+        b = item / a.H;
+    }
+    const uint32_t ep = (uint32_t)ld_uniform((const int*)o.xctr) * (uint32_t)FUSE_EPOCHS + (uint32_t)o.xidx + 1u;
+    attn16_item<HD, TILE>(a, h, b, o.xq, o.ldx, ep, limit, abort_word);
 }
 
 // ---- repack a canonical 8-bit affine matrix into the tiled layout --------------------------
@@ -525,8 +728,11 @@ __global__ void k_sum_slices(const float* __restrict__ part, int S, long long sl
 
 // the frame's codes appended to the history at *pos, and the position advanced
 __global__ void k_frame_done(const int* __restrict__ codes, int n, int* hist, int* pos, int* seq, int B, int C,
-                             const uint32_t* err)
+                             const uint32_t* err, uint32_t* fctr)
 {
+    // the epoch counter of the fused launches advances every frame, a rejected one included, so
+    // that no later launch can take a stale exchange word for its own
+    if (fctr && threadIdx.x == 0) *fctr += 1u;
     if (err && ld_uniform((const int*)err)) return;   // a rejected input: the state stays as it was
     const int p = *pos;
     for (int i = threadIdx.x; i < n; i += blockDim.x) hist[(size_t)p * n + i] = codes[i];
@@ -534,6 +740,11 @@ __global__ void k_frame_done(const int* __restrict__ codes, int n, int* hist, in
         for (int b = threadIdx.x; b < B; b += blockDim.x) seq[(size_t)p * B + b] = codes[(size_t)b * C];
     __syncthreads();
     if (threadIdx.x == 0) *pos = p + 1;
+}
+
+__global__ void k_bump_u32(uint32_t* p)
+{
+    if (threadIdx.x == 0) *p += 1u;
 }
 
 template <int EPI, int T, int NW, int U>
@@ -577,6 +788,33 @@ hipError_t launch_mm16(int epi, const TiledMat& W, const MmIn& in, int splits, c
     if (epi == MM_SWIGLU) return launch_e<MM_SWIGLU>(W, in, splits, o, st);
     if (epi == MM_QKV_ROPE) return launch_e<MM_QKV_ROPE>(W, in, splits, o, st);
     return hipErrorInvalidValue;
+}
+
+bool qkv_attention_fits(const TiledMat& W, const AttnArgs& a)
+{
+    const int qd = a.H * a.hd, kd = a.Hkv * a.hd;
+    return (a.hd == 64 || a.hd == 128) && attn_direct_fits(a.n_ctx) && a.Hkv > 0 && a.H % a.Hkv == 0 &&
+           W.N == qd + 2 * kd && W.K / 64 <= 16 && mm16_supported(W.N, W.K) && a.B >= 1 && a.B <= MM_ROWS;
+}
+
+hipError_t launch_qkv_attention(const TiledMat& W, const MmIn& in, const Mm16Out& o, const AttnArgs& a, long long limit,
+                                uint32_t* abort_word, hipStream_t st)
+{
+    // the product's shape as launch_mm16 runs it for K <= 1024 (one tile, four waves, four groups per round)
+    if (!qkv_attention_fits(W, a) || !o.xq || !o.xctr || o.xidx < 0 || o.xidx >= FUSE_EPOCHS - 1 || o.ldx != W.N ||
+        !a.act_hi || !a.act_lo || !abort_word || o.rows < 1 || o.rows > MM_ROWS || in.rows < 1 || in.rows > MM_ROWS ||
+        !in.a.hi || !in.a.lo || (in.ssq && (in.n_ssq < 1 || in.n_ssq > MM_MAX_SSQ)))
+        return hipErrorInvalidValue;
+    const int n_gemm = (W.N + 15) / 16;
+    const dim3 grid(n_gemm + a.H * a.B);
+    if (a.hd == 64) {
+        if (a.n_ctx <= 64) hipLaunchKernelGGL((k_qkv_attn<4, 64, 16>), grid, dim3(256), 0, st, W, in, o, a, n_gemm, limit, abort_word);
+        else hipLaunchKernelGGL((k_qkv_attn<4, 64, 64>), grid, dim3(256), 0, st, W, in, o, a, n_gemm, limit, abort_word);
+    } else {
+        if (a.n_ctx <= 64) hipLaunchKernelGGL((k_qkv_attn<4, 128, 16>), grid, dim3(256), 0, st, W, in, o, a, n_gemm, limit, abort_word);
+        else hipLaunchKernelGGL((k_qkv_attn<4, 128, 32>), grid, dim3(256), 0, st, W, in, o, a, n_gemm, limit, abort_word);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_pack_tiled(const void* src, int N, int K, void* dst_base, int dst_N, int dst_row0, int mode, int hd,
@@ -637,9 +875,15 @@ hipError_t launch_sum_slices(const float* part, int S, long long slice, float* y
 }
 
 hipError_t launch_frame_done(const int* codes, int n, int* hist, int* pos, int* seq, int B, int C, const uint32_t* err,
-                             hipStream_t st)
+                             uint32_t* fctr, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_frame_done, dim3(1), dim3(256), 0, st, codes, n, hist, pos, seq, B, C, err);
+    hipLaunchKernelGGL(k_frame_done, dim3(1), dim3(256), 0, st, codes, n, hist, pos, seq, B, C, err, fctr);
+    return hipGetLastError();
+}
+
+hipError_t launch_bump_u32(uint32_t* p, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_bump_u32, dim3(1), dim3(64), 0, st, p);
     return hipGetLastError();
 }
 

@@ -62,10 +62,12 @@ inline PackedMat take_mat(Planner& P, int f, int N, int K)
     return packed_view(f, p, N, K);
 }
 
-// the model's control words (64 words in the workspace): the persistent step's epoch base
-// (launches completed) and its sticky time-out word; the sticky rejected-input word that every
+// the model's control words (64 words in the workspace): the epoch base (the persistent step:
+// launches completed; TALKER_CP: frames completed, which tags the fused QKV + attention launches)
+// and the sticky time-out word of the bounded waits; the sticky rejected-input word that every
 // state-writing kernel checks (kernels.h launch_set_input)
 enum { CTL_EPOCH = 0, CTL_ABORT = 1, CTL_BAD_INPUT = 2, CTL_WORDS = 64 };
+constexpr long long STEP_SPIN_LIMIT = 2000000;   // 20 ms of the 100 MHz clock per wait
 
 // kernel kinds a timing probe can bracket
 enum { KIND_QKV = 0, KIND_ATTN = 1, KIND_OPROJ = 2, KIND_FC = 3, KIND_DOWN = 4, KIND_HEAD = 5, KIND_STEP = 6, TSD_KERNEL_KINDS = 7 };
@@ -127,6 +129,7 @@ struct tsd_model {
     size_t xbuf_words = 0;
     uint32_t* ctl = nullptr;          // [0] epoch base (launches), [1] abort word
     uint64_t launches = 0, max_launches = 0;
+    bool frame_fused = false;         // TALKER_CP: the QKV product and attention share a launch
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
     // TALKER_CP: batch rows through the matrix-core GEMM; the code predictor's own layers,

@@ -54,7 +54,6 @@ size_t canonical_matrix_bytes(int f, int N, int K)
 namespace {
 
 constexpr int MAX_STEP_WG = 1024;          // workgroups of the persistent step, at most
-constexpr long long STEP_SPIN_LIMIT = 2000000;   // 20 ms of the 100 MHz clock per wait
 
 bool known_format(int f) { return f >= 0 && f < FMT_COUNT; }
 
@@ -522,7 +521,7 @@ tsd_status setup_step(tsd_model* m)
 // before each persistent launch: restart the epochs before they would wrap
 hipError_t before_launch(tsd_model* m)
 {
-    if (!m->step_fn) return hipSuccess;
+    if (!m->step_fn && !m->frame_fused) return hipSuccess;
     if (m->launches >= m->max_launches) {
         hipError_t e = reset_exchange(m);
         if (e != hipSuccess) return e;
@@ -931,8 +930,8 @@ tsd_status tsd_synchronize(tsd_model* m)
     HIP_TRY(m, hipStreamSynchronize(m->st), "stream sync");
     uint32_t ctl[CTL_BAD_INPUT + 1] = {};
     HIP_TRY(m, hipMemcpy(ctl, m->ctl, sizeof(ctl), hipMemcpyDeviceToHost), "read control words");
-    if (m->step_fn && ctl[CTL_ABORT])
-        return fail(m, TSD_ERR_TIMEOUT, "a wait inside the persistent step timed out; the steps since are void "
+    if ((m->step_fn || m->frame_fused) && ctl[CTL_ABORT])
+        return fail(m, TSD_ERR_TIMEOUT, "a wait inside a step launch timed out; the steps since are void "
                                         "(tsd_reset clears the state)");
     if (ctl[CTL_BAD_INPUT]) {
         // the calls since the rejected input did nothing: the position count is the device's
@@ -963,7 +962,7 @@ tsd_status tsd_reset(tsd_model* m)
     HIP_TRY(m, launch_fill_i32(m->hist, 0, m->c.n_ctx * m->c.batch * m->tpp, m->st), "reset");
     HIP_TRY(m, launch_fill_i32(m->seq, -1, m->c.n_ctx * m->c.batch, m->st), "reset");
     HIP_TRY(m, launch_fill_u32(m->ctl + CTL_BAD_INPUT, 0u, 1, m->st), "reset");
-    if (m->step_fn) HIP_TRY(m, reset_exchange(m), "reset");
+    if (m->step_fn || m->frame_fused) HIP_TRY(m, reset_exchange(m), "reset");
     m->n_past = 0;
     return TSD_OK;
 }
@@ -1041,6 +1040,7 @@ tsd_status tsd_layer_forward(tsd_model* m, int layer, const float* d_x, int pos,
     if (pos < 0 || pos >= c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "position outside the context");
     HIP_TRY(m, launch_fill_i32(m->dbg_pos, pos, 1, m->st), "set position");
     if (c.arch == TSD_ARCH_TALKER_CP) {   // the batched frame keeps its rows interleaved
+        HIP_TRY(m, before_launch(m), "exchange restart");
         HIP_TRY(m, talker_layer(m, layer, m->st, d_x, m->dbg_pos), "layer");
         HIP_TRY(m, launch_il_to_rows(m->x, c.batch, c.d_model, d_out, m->st), "copy out");
         return TSD_OK;

@@ -41,7 +41,7 @@ namespace {
 // hi/lo of x * n1g with n_ssq partial row sums of x^2 in ssq; on exit the same for the next norm,
 // whose gain is g_after.
 hipError_t layer16(tsd_model* m, const TLayerW& w, float* x, int n_ssq, const float* g_after, __half* kc, __half* vc,
-                   int n_ctx, const int* posp, int pos_value, hipStream_t st, Probe* pr)
+                   int n_ctx, const int* posp, int pos_value, hipStream_t st, Probe* pr, int fuse_idx)
 {
     const tsd_config& c = m->c;
     const int d = c.d_model, H = c.n_head, Hk = c.n_kv_head, hd = c.head_dim, B = c.batch;
@@ -66,10 +66,6 @@ hipError_t layer16(tsd_model* m, const TLayerW& w, float* x, int n_ssq, const fl
     oq.rope = m->rope;
     oq.posp = posp;
     oq.pos_value = pos_value;
-    {
-        Bracket br(pr, KIND_QKV, st);
-        TRY(launch_mm16(MM_QKV_ROPE, w.qkv, iq, 1, oq, st));
-    }
     // attention; a cache of one chunk writes the output projection's operand directly
     const bool direct = attn_direct_fits(n_ctx);
     AttnArgs aa{};
@@ -88,11 +84,26 @@ hipError_t layer16(tsd_model* m, const TLayerW& w, float* x, int n_ssq, const fl
     aa.n_keys = pos_value + 1;
     aa.act_hi = direct ? m->act.hi : nullptr;
     aa.act_lo = direct ? m->act.lo : nullptr;
-    {
-        Bracket br(pr, KIND_ATTN, st);
-        TRY(launch_attention(aa, st));
+    if (fuse_idx >= 0 && m->frame_fused && qkv_attention_fits(w.qkv, aa)) {
+        // the product and the attention in one launch (the query and the new key and value cross
+        // through exchange words tagged for this launch)
+        oq.xq = m->xbuf;
+        oq.ldx = w.qkv.N;
+        oq.xctr = m->ctl + CTL_EPOCH;
+        oq.xidx = fuse_idx;
+        Bracket br(pr, KIND_QKV, st);
+        TRY(launch_qkv_attention(w.qkv, iq, oq, aa, STEP_SPIN_LIMIT, m->ctl + CTL_ABORT, st));
+    } else {
+        {
+            Bracket br(pr, KIND_QKV, st);
+            TRY(launch_mm16(MM_QKV_ROPE, w.qkv, iq, 1, oq, st));
+        }
+        {
+            Bracket br(pr, KIND_ATTN, st);
+            TRY(launch_attention(aa, st));
+        }
+        if (!direct) TRY(launch_merge16(m->part, B, H, hd, attn_max_split(n_ctx), posp, pos_value + 1, m->act, st));
     }
-    if (!direct) TRY(launch_merge16(m->part, B, H, hd, attn_max_split(n_ctx), posp, pos_value + 1, m->act, st));
     // output projection into the residual, which also prepares the second norm's input
     MmIn ia{};
     ia.a = m->act;
@@ -266,6 +277,9 @@ size_t talker_plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     float* logits = (float*)P.take(sizeof(float) * (size_t)B * C * vmax);
     float* part = (float*)P.take(attn_part_bytes(B, H, c->n_ctx, hd));
     float2* rope = (float2*)P.take(sizeof(float2) * (size_t)rope_rows * (hd / 2));
+    // exchange words of the fused QKV + attention launches (one row of q, k, v per batch row)
+    const size_t xwords = (size_t)MM_ROWS * (qd + 2 * kd);
+    uint64_t* xq = (uint64_t*)P.take(sizeof(uint64_t) * xwords);
     float* emb[16] = {};
     emb[0] = (float*)P.take(sizeof(float) * (size_t)V * d);
     for (int k = 1; k < C; ++k) emb[k] = (float*)P.take(sizeof(float) * (size_t)Vc * d);
@@ -308,6 +322,10 @@ size_t talker_plan(tsd_model* m, const tsd_config* c, uint8_t* base)
         m->x = x; m->xc = xc; m->qkv = q; m->h = h; m->logits = logits; m->part = part;
         m->act.hi = hi; m->act.lo = lo; m->act2.hi = hi2; m->act2.lo = lo2; m->ssq = ssq;
         m->rope = rope; m->rope_rows = rope_rows;
+        m->xbuf = xq; m->xbuf_words = xwords;
+        // every fused launch of a frame needs its own epoch
+        m->frame_fused = c->n_layer + c->n_codebooks * c->cp_n_layer <= FUSE_EPOCHS - 1;
+        m->max_launches = 0xFFFFFFFFull / FUSE_EPOCHS - 2;
         for (int k = 0; k < C; ++k) {
             m->emb[k] = emb[k];
             m->emb_rows[k] = k == 0 ? V : Vc;
@@ -394,11 +412,12 @@ hipError_t talker_enqueue(tsd_model* m, hipStream_t st, bool with_cp, Probe* pr)
     int n_ssq = 1;
     for (int l = 0; l < L; ++l) {
         TRY(layer16(m, m->Lt[l], m->x, n_ssq, l + 1 < L ? m->Lt[l + 1].n1g : m->nfg, m->kc + m->kv_layer_elems * l,
-                    m->vc + m->kv_layer_elems * l, c.n_ctx, m->pos, 0, st, pr));
+                    m->vc + m->kv_layer_elems * l, c.n_ctx, m->pos, 0, st, pr, l));
         n_ssq = tiles_d;
     }
     if (!with_cp)   // advance the position and record the consumed code 0 only
-        return launch_frame_done(m->tok, 0, m->hist, m->pos, m->seq, c.batch, c.n_codebooks, m->ctl + CTL_BAD_INPUT, st);
+        return launch_frame_done(m->tok, 0, m->hist, m->pos, m->seq, c.batch, c.n_codebooks, m->ctl + CTL_BAD_INPUT,
+                                 m->ctl + CTL_EPOCH, st);
     // code 0; the Talker's final-normed hidden state is the predictor's position 0
     TRY(head16(m, st, pr, m->t_head, 0));
     RowPrep h{};
@@ -421,7 +440,8 @@ hipError_t talker_enqueue(tsd_model* m, hipStream_t st, bool with_cp, Probe* pr)
         n_ssq = 1;
         for (int l = 0; l < Lc; ++l) {
             TRY(layer16(m, m->Lc[l], m->xc, n_ssq, l + 1 < Lc ? m->Lc[l + 1].n1g : m->cp_nfg,
-                        m->ckc + m->ckv_layer_elems * l, m->cvc + m->ckv_layer_elems * l, C, nullptr, cpos, st, pr));
+                        m->ckc + m->ckv_layer_elems * l, m->cvc + m->ckv_layer_elems * l, C, nullptr, cpos, st, pr,
+                        L + cpos * Lc + l));
             n_ssq = tiles_d;
         }
         if (cpos == 0) continue;
@@ -430,7 +450,7 @@ hipError_t talker_enqueue(tsd_model* m, hipStream_t st, bool with_cp, Probe* pr)
         const RowPrep p = cp_input_emb(m, cpos, nullptr);
         TRY(pick16(m, st, cpos, c.cp_vocab, cpos + 1 < C ? &p : nullptr));
     }
-    return launch_frame_done(m->tok, B * C, m->hist, m->pos, nullptr, B, C, m->ctl + CTL_BAD_INPUT, st);
+    return launch_frame_done(m->tok, B * C, m->hist, m->pos, nullptr, B, C, m->ctl + CTL_BAD_INPUT, m->ctl + CTL_EPOCH, st);
 }
 
 hipError_t talker_layer(tsd_model* m, int l, hipStream_t st, const float* d_x, const int* pos)
@@ -446,8 +466,9 @@ hipError_t talker_layer(tsd_model* m, int l, hipStream_t st, const float* d_x, c
     p.g = m->Lt[l].n1g;
     p.ssq = m->ssq;
     TRY(launch_row_prep(p, st));
-    return layer16(m, m->Lt[l], m->x, 1, m->Lt[l].n1g, m->kc + m->kv_layer_elems * l, m->vc + m->kv_layer_elems * l,
-                   c.n_ctx, pos, 0, st, nullptr);
+    TRY(layer16(m, m->Lt[l], m->x, 1, m->Lt[l].n1g, m->kc + m->kv_layer_elems * l, m->vc + m->kv_layer_elems * l,
+                c.n_ctx, pos, 0, st, nullptr, 0));
+    return launch_bump_u32(m->ctl + CTL_EPOCH, st);   // the next launch tags its words anew
 }
 
 void talker_kind_launches(const tsd_model* m, int* out)
@@ -455,6 +476,7 @@ void talker_kind_launches(const tsd_model* m, int* out)
     const tsd_config& c = m->c;
     const int per_layer = c.n_layer + c.n_codebooks * c.cp_n_layer;
     for (int k : {KIND_QKV, KIND_ATTN, KIND_OPROJ, KIND_FC, KIND_DOWN}) out[k] = per_layer;
+    if (m->frame_fused) out[KIND_ATTN] = 0;   // the attention runs inside the QKV launches
     out[KIND_HEAD] = c.n_codebooks;
     out[KIND_STEP] = 0;
 }

@@ -158,6 +158,8 @@ def frame_kernel_bytes(c, kind: str, pos: int) -> float:
     if kind == "head":
         mats = matrix_bytes(f, c["vocab"], d) + (C - 1) * matrix_bytes(f, c["cp_vocab"], d)
         return mats / C + operand(d) + B * 4 * (c["vocab"] + (C - 1) * c["cp_vocab"]) / C
+    if kind == "qkv_attn":   # the QKV product and the attention in one launch
+        return frame_kernel_bytes(c, "qkv", pos) + frame_kernel_bytes(c, "attn", pos)
     if kind == "attn":
         keys = L * (pos + 1) + Lc * sum(j + 1 for j in range(C))
         n_launch = L + Lc * C

@@ -389,3 +389,34 @@ def test_full_size_frames_sampled_rows():
             codes[b] = want[b][0]
     om.close()
     gm.close()
+
+
+def test_frames_repeat_after_truncate_and_reset():
+    """The QKV product and the attention share a launch and hand the query and the new key and
+    value over through exchange words tagged per frame: frames run again at the same positions
+    (after truncate, and after reset) must not pick up the words of the earlier run, and so give
+    the same logits bit for bit."""
+    cfg = small_talker(batch=2, n_ctx=32)
+    w = synth.model_weights(cfg, 7, norm_std=0.1)
+    gm = gpu_model(cfg, w)
+    toks = synth.prompt_tokens(cfg, 4, seed=2)
+    codes = [synth.prompt_tokens(cfg, 1, seed=10 + f)[:, 0, :] for f in range(3)]
+
+    def run():
+        out = []
+        for c in codes:
+            gm.step(dev(c))
+            out.append(gm.logits().cpu().numpy().copy())
+        return out
+
+    gm.prefill(dev(toks))
+    first = run()
+    gm.truncate(4)
+    again = run()
+    gm.reset()
+    gm.prefill(dev(toks))
+    after_reset = run()
+    gm.synchronize()
+    for a, b, c in zip(first, again, after_reset):
+        assert np.array_equal(a, b) and np.array_equal(a, c)
+    gm.close()

@@ -209,15 +209,28 @@ tsd_status tsd_step(tsd_model* m, const int32_t* d_in, int32_t* d_next);
  * Results are identical to tsd_step. */
 tsd_status tsd_step_eager(tsd_model* m, const int32_t* d_in, int32_t* d_next);
 
-/* Wait for the model's stream, then report
- *   TSD_ERR_TIMEOUT if any persistent step since the last tsd_reset gave up on a bounded wait.
- *     Such a step, and every step after it, leaves the ids, logits and cache unspecified;
- *     nothing hangs and no memory outside the workspace is touched.  Each wait in the step is
- *     limited to 20 ms.
+/* Wait for the model's stream, then report what went wrong since the last call:
+ *   a persistent step gave up on a bounded wait (each wait between its workgroups is limited to
+ *     20 ms; it can only run out when other work holds compute units the grid needs, or on a
+ *     fault).  That launch and every persistent launch after it returned without moving the
+ *     position; nothing hangs and no memory outside the workspace is touched.  The model then
+ *     switches to one launch per operator for good (tsd_model_info reports it) and restarts its
+ *     exchange.  If every step since the last tsd_synchronize was a plain tsd_step(m, NULL, NULL)
+ *     (ids from the device, none copied out), those steps run again at once and TSD_OK is returned
+ *     (tsd_last_error says what happened); otherwise n_past is set back to the first lost
+ *     position and TSD_ERR_TIMEOUT is returned, and the caller submits the positions from there
+ *     again.  A TALKER_CP frame whose fused attention gave up on its wait reports TSD_ERR_TIMEOUT
+ *     with the frames since unspecified until tsd_reset.
  *   TSD_ERR_INVALID_ARGUMENT if a call since the last tsd_synchronize passed a token id outside its
  *     vocabulary.  That call and the model calls after it did nothing; n_past is set back to the
  *     device's position and the rejection is cleared, so the model can be used again. */
 tsd_status tsd_synchronize(tsd_model* m);
+
+/* For tests of the time-out path only: the limit of every bounded wait of the persistent step,
+ * in ticks of the 100 MHz constant clock (ticks <= 0: the normal 20 ms).  With a tiny limit the
+ * first wait of the next step gives up at once and every workgroup leaves the kernel normally.
+ * TSD_ERR_UNSUPPORTED when the model does not run the persistent step. */
+tsd_status tsd_debug_set_wait_limit(tsd_model* m, int64_t ticks);
 
 tsd_status tsd_reset(tsd_model* m);                     /* n_past = 0, history, timeout and rejection cleared */
 /* The launch configuration in effect: *launch_mode is PERSISTENT only when the shape has a

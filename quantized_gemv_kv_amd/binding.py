@@ -27,7 +27,7 @@ EXPORTS = ["tsd_workspace_bytes", "tsd_model_create", "tsd_prefill", "tsd_step",
            "tsd_attention_scratch_bytes", "tsd_attention", "tsd_time_kernel", "tsd_synchronize",
            "tsd_model_info", "tsd_sample_topk", "tsd_sample", "tsd_gemm_rows_packed_bytes", "tsd_gemm_rows_pack",
            "tsd_gemm_rows_scratch_bytes", "tsd_gemm_rows", "tsd_prefill_stepwise", "tsd_gemm_scratch_bytes", "tsd_gemm",
-           "tsd_get_kv", "tsd_debug_gemv", "tsd_attention_noalloc"]
+           "tsd_get_kv", "tsd_debug_gemv", "tsd_attention_noalloc", "tsd_debug_set_wait_limit"]
 KERNEL_KINDS = {"qkv": 0, "attn": 1, "oproj": 2, "fc": 3, "down": 4, "head": 5, "step": 6}
 
 
@@ -102,6 +102,7 @@ def lib():
             "tsd_attention": [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P],
             "tsd_time_kernel": [_P, _I, _I, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_I)],
             "tsd_synchronize": [_P],
+            "tsd_debug_set_wait_limit": [_P, ctypes.c_int64],
             "tsd_model_info": [_P, _P, _P],
             "tsd_sample_topk": [_P, _I, _I, ctypes.c_float, ctypes.c_uint64, _I, _I, _I, _P, _P],
             "tsd_sample": [_P, _I, ctypes.POINTER(tsd_sampling), _P, _I, _I, _I, _I, _P, _P],
@@ -322,6 +323,11 @@ class Model:
 
     def truncate(self, n):
         self._chk(lib().tsd_truncate(self.h, n))
+
+    def debug_set_wait_limit(self, ticks):
+        """Tests of the time-out path: every bounded wait of the persistent step gives up after
+        `ticks` of the 100 MHz clock (<= 0: the normal limit)."""
+        self._chk(lib().tsd_debug_set_wait_limit(self.h, int(ticks)))
 
     def synchronize(self):
         """Wait for the model's stream; TsdError(TSD_ERR_TIMEOUT) if a persistent step gave up,

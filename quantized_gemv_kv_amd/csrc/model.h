@@ -130,6 +130,7 @@ struct tsd_model {
     uint32_t* ctl = nullptr;          // [0] epoch base (launches), [1] abort word
     uint64_t launches = 0, max_launches = 0;
     bool frame_fused = false;         // TALKER_CP: the QKV product and attention share a launch
+    bool io_since_sync = false;       // a step or prompt since the last tsd_synchronize took or gave ids through caller buffers
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
     // TALKER_CP: batch rows through the matrix-core GEMM; the code predictor's own layers,

@@ -842,6 +842,7 @@ tsd_status tsd_step(tsd_model* m, const int32_t* d_in, int32_t* d_next)
     if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
     if (m->n_past >= m->c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "context full");
     const int nt = m->c.batch * m->tpp;
+    if (d_in || d_next) m->io_since_sync = true;
     if (d_in) HIP_TRY(m, set_input(m, d_in, m->tpp), "set input");
     HIP_TRY(m, before_launch(m), "exchange restart");
     HIP_TRY(m, launch_one_step(m, m->exec), "step launch");
@@ -855,6 +856,7 @@ tsd_status tsd_step_eager(tsd_model* m, const int32_t* d_in, int32_t* d_next)
     if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
     if (m->n_past >= m->c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "context full");
     const int nt = m->c.batch * m->tpp;
+    if (d_in || d_next) m->io_since_sync = true;
     if (d_in) HIP_TRY(m, set_input(m, d_in, m->tpp), "set input");
     HIP_TRY(m, before_launch(m), "exchange restart");
     HIP_TRY(m, enqueue_step(m, m->st), "eager step");
@@ -868,6 +870,7 @@ tsd_status tsd_prefill(tsd_model* m, const int32_t* d_tokens, int n, int32_t* d_
     if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
     if (!d_tokens || n <= 0) return fail(m, TSD_ERR_INVALID_ARGUMENT, "empty prompt");
     if (m->n_past + n > m->c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "prompt does not fit the context");
+    m->io_since_sync = true;
     const int nt = m->c.batch * m->tpp;
     const bool talker = m->c.arch == TSD_ARCH_TALKER_CP;
     // every id of the prompt is checked first; a bad one makes every launch below leave the state
@@ -906,6 +909,7 @@ tsd_status tsd_prefill_stepwise(tsd_model* m, const int32_t* d_tokens, int n, in
     if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
     if (!d_tokens || n <= 0) return fail(m, TSD_ERR_INVALID_ARGUMENT, "empty prompt");
     if (m->n_past + n > m->c.n_ctx) return fail(m, TSD_ERR_CONTEXT_FULL, "prompt does not fit the context");
+    m->io_since_sync = true;
     const int nt = m->c.batch * m->tpp;
     const bool talker = m->c.arch == TSD_ARCH_TALKER_CP;
     HIP_TRY(m, launch_check_ids(d_tokens, m->c.batch, n, m->tpp, m->c.vocab, talker ? m->c.cp_vocab : m->c.vocab,
@@ -924,14 +928,60 @@ tsd_status tsd_prefill_stepwise(tsd_model* m, const int32_t* d_tokens, int n, in
     return TSD_OK;
 }
 
+namespace {
+// A wait inside a persistent step timed out (another kernel held compute units the grid needed,
+// or a fault in the exchange): that launch and every persistent launch after it returned without
+// moving the position.  The model falls back to one launch per operator for good (no waits
+// between workgroups), the exchange restarts, and the lost positions, which read their input from
+// the device, run again; those whose ids came from or went to caller buffers are left for the
+// caller to submit again (TSD_ERR_TIMEOUT, with n_past at the first lost position).
+tsd_status recover_persistent(tsd_model* m)
+{
+    int pos = 0;
+    HIP_TRY(m, hipMemcpy(&pos, m->pos, sizeof(pos), hipMemcpyDeviceToHost), "read position");
+    const int lost = m->n_past - pos;
+    const void* fn = m->step_fn;
+    m->step_fn = nullptr;
+    hipGraph_t g = nullptr;
+    hipGraphExec_t x = nullptr;
+    tsd_status s = capture(m, false, &g, &x);
+    if (s != TSD_OK) {
+        m->step_fn = fn;
+        return s;
+    }
+    if (m->exec) (void)hipGraphExecDestroy(m->exec);
+    if (m->graph) (void)hipGraphDestroy(m->graph);
+    m->graph = g;
+    m->exec = x;
+    count_launches(m);
+    HIP_TRY(m, reset_exchange(m), "exchange restart");
+    m->n_past = pos;
+    if (m->io_since_sync) {
+        m->io_since_sync = false;
+        HIP_TRY(m, hipStreamSynchronize(m->st), "stream sync");
+        return fail(m, TSD_ERR_TIMEOUT, "a wait inside the persistent step timed out; the model now runs one launch "
+                                        "per operator, and the positions from n_past on must be submitted again");
+    }
+    for (int i = 0; i < lost; ++i) {
+        HIP_TRY(m, launch_one_step(m, m->exec), "step launch");
+        m->n_past += 1;
+    }
+    HIP_TRY(m, hipStreamSynchronize(m->st), "stream sync");
+    m->err = "a wait inside the persistent step timed out; the " + std::to_string(lost) +
+             " steps since ran again with one launch per operator, which the model keeps using";
+    return TSD_OK;
+}
+}  // namespace
+
 tsd_status tsd_synchronize(tsd_model* m)
 {
     if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
     HIP_TRY(m, hipStreamSynchronize(m->st), "stream sync");
     uint32_t ctl[CTL_BAD_INPUT + 1] = {};
     HIP_TRY(m, hipMemcpy(ctl, m->ctl, sizeof(ctl), hipMemcpyDeviceToHost), "read control words");
-    if ((m->step_fn || m->frame_fused) && ctl[CTL_ABORT])
-        return fail(m, TSD_ERR_TIMEOUT, "a wait inside a step launch timed out; the steps since are void "
+    if (m->step_fn && ctl[CTL_ABORT]) return recover_persistent(m);
+    if (m->frame_fused && ctl[CTL_ABORT])
+        return fail(m, TSD_ERR_TIMEOUT, "a wait inside a frame launch timed out; the frames since are void "
                                         "(tsd_reset clears the state)");
     if (ctl[CTL_BAD_INPUT]) {
         // the calls since the rejected input did nothing: the position count is the device's
@@ -940,10 +990,12 @@ tsd_status tsd_synchronize(tsd_model* m)
         m->n_past = pos;
         HIP_TRY(m, launch_fill_u32(m->ctl + CTL_BAD_INPUT, 0u, 1, m->st), "clear bad-input word");
         HIP_TRY(m, hipStreamSynchronize(m->st), "stream sync");
+        m->io_since_sync = false;
         return fail(m, TSD_ERR_INVALID_ARGUMENT, "a token id outside its vocabulary was passed in; that call and "
                                                  "every model call after it until now did nothing (the model state "
                                                  "is as it was before that call)");
     }
+    m->io_since_sync = false;
     return TSD_OK;
 }
 
@@ -952,6 +1004,16 @@ tsd_status tsd_model_info(const tsd_model* m, int32_t* launch_mode, int32_t* n_w
     if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
     if (launch_mode) *launch_mode = m->step_fn ? TSD_LAUNCH_PERSISTENT : TSD_LAUNCH_PER_OPERATOR;
     if (n_workgroups) *n_workgroups = m->step_fn ? m->n_wg : 0;
+    return TSD_OK;
+}
+
+tsd_status tsd_debug_set_wait_limit(tsd_model* m, int64_t ticks)
+{
+    if (!m) return fail(nullptr, TSD_ERR_INVALID_ARGUMENT, "null model");
+    if (!m->step_fn) return fail(m, TSD_ERR_UNSUPPORTED, "the model does not run the persistent step");
+    m->sa.spin_limit = ticks > 0 ? (long long)ticks : STEP_SPIN_LIMIT;
+    HIP_TRY(m, hipMemcpyAsync(m->d_sa, &m->sa, sizeof(StepArgs), hipMemcpyHostToDevice, m->st), "step arguments");
+    HIP_TRY(m, hipStreamSynchronize(m->st), "step arguments");
     return TSD_OK;
 }
 

@@ -474,3 +474,71 @@ def test_step_timing_kinds_follow_launch_mode():
         assert e.value.status == 2 and gm.n_past == before
         gm.synchronize()
         gm.close()
+
+
+def test_persistent_time_out_reruns_lost_steps_per_operator():
+    """A persistent step that gives up on a bounded wait (forced from the host: a wait limit of one
+    tick, so every workgroup leaves the kernel normally) voids itself and the persistent launches
+    after it.  tsd_synchronize then switches the model to one launch per operator and runs the
+    lost steps again, since they took their ids from the device: the ids follow the oracle's
+    free-running greedy decode as if nothing had happened."""
+    cfg = synth.small_config("gpt2", "q4_0", d_ff=256, n_ctx=64)
+    w = synth.model_weights(cfg, 42, norm_std=0.5)
+    gm = gpu_model(cfg, w, "persistent")
+    om = oracle.OracleModel(cfg, w)
+    toks = synth.prompt_tokens(cfg, 5, seed=1)
+    gm.prefill(dev(toks))
+    o = om.prefill(toks)
+    for _ in range(3):
+        gm.step(None, out=False)
+    gm.synchronize()
+    gm.debug_set_wait_limit(1)
+    for _ in range(4):
+        gm.step(None, out=False)
+    gm.synchronize()   # the four lost steps run again, one launch per operator
+    assert gm.info()[0] == "per_operator"
+    for _ in range(3):
+        gm.step(None, out=False)
+    gm.synchronize()
+    assert gm.n_past == 15
+    ids = [int(v) for v in gm.tokens(4, 11).cpu().numpy()[:, 0, 0]]
+    o_ids = [int(o[0, 0])]
+    for _ in range(10):
+        if top2_gap(om.logits()[0]) < TIE_GAP:
+            break
+        o_ids.append(int(om.step()[0, 0]))
+    assert ids[:len(o_ids)] == o_ids
+    gm.close()
+    om.close()
+
+
+def test_persistent_time_out_with_caller_ids_rolls_back():
+    """When the lost steps took ids from a caller buffer, tsd_synchronize reports TSD_ERR_TIMEOUT and
+    sets n_past back to the first lost position; the caller submits those positions again, now with
+    one launch per operator, and they match the oracle."""
+    from quantized_gemv_kv_amd import TsdError
+    cfg = synth.small_config("gpt2", "q4_0", d_ff=256, n_ctx=64)
+    w = synth.model_weights(cfg, 42, norm_std=0.5)
+    gm = gpu_model(cfg, w, "persistent")
+    om = oracle.OracleModel(cfg, w)
+    toks = synth.prompt_tokens(cfg, 5, seed=2)
+    gm.prefill(dev(toks))
+    nxt = om.prefill(toks)
+    gm.synchronize()
+    gm.debug_set_wait_limit(1)
+    gm.step(dev(nxt))
+    gm.step(dev(nxt))
+    with pytest.raises(TsdError) as e:
+        gm.synchronize()
+    assert e.value.status == 7 and gm.n_past == 5
+    assert gm.info()[0] == "per_operator"
+    for s in range(3):
+        o_ids = om.step(nxt)
+        gm.step(dev(nxt))
+        lo, lg = om.logits()[0], gm.logits().cpu().numpy()[0]
+        assert rel_err(lg, lo) <= REL_TOL, (s, rel_err(lg, lo))
+        nxt = o_ids
+    assert gm.n_past == om.n_past
+    gm.synchronize()
+    gm.close()
+    om.close()

@@ -30,6 +30,7 @@
 // at batch 1) small.
 // Epochs: launch n uses n * P + 1 .. n * P + P for its P = 5 * n_layer + 1 phases.
 #include <math.h>
+#include <type_traits>
 
 #include "exchange.h"
 #include "gemv_core.h"
@@ -419,6 +420,42 @@ __device__ __forceinline__ float2 ld8f(const float2* p)
 // fp16 store through the global address space
 __device__ __forceinline__ void st_half(__half* p, __half v) { *glb((unsigned short*)p) = __half_as_ushort(v); }
 
+// The partial sums of NU units of NV rows each (unit u = rows u NV .. u NV + NV - 1) reduced over
+// aligned groups of GW lanes: lane s of a group ends with the NV totals of unit s % NU.  Each
+// selecting stage halves the units a lane carries: the lane keeps the half that one bit of its
+// slot names and adds that half as a partner lane (the bit flipped, the bits of earlier stages
+// kept) held it, having sent the other half.  The stages after them add lanes that carry the same
+// unit (rotations by 4 and 8 within a row of 16, then the 16- and 32-lane swaps).
+template <int NU, int NV, int GW>
+__device__ __forceinline__ void fold_units(const float (&p)[NU * NV], float (&t)[NV], int slot)
+{
+    static_assert(NU == 2 || NU == 4 || NU == 8, "two to eight units");
+    static_assert(GW == 16 || GW == 32 || GW == 64, "groups of 16 to 64 lanes");
+    float c[NU * NV];
+#pragma unroll
+    for (int i = 0; i < NU * NV; ++i) c[i] = p[i];
+    auto stage = [&](auto ctrl, int half, bool k) {
+#pragma unroll
+        for (int i = 0; i < half * NV; ++i) {
+            const float keep = k ? c[i + half * NV] : c[i], send = k ? c[i] : c[i + half * NV];
+            c[i] = keep + dpp_mov<decltype(ctrl)::value>(send);
+        }
+    };
+    if constexpr (NU >= 8) stage(std::integral_constant<int, 0x141>{}, 4, slot & 4);   // partner s ^ 7
+    if constexpr (NU >= 4) stage(std::integral_constant<int, 0x4E>{}, 2, slot & 2);    // partner s ^ 2
+    stage(std::integral_constant<int, 0xB1>{}, 1, slot & 1);                            // partner s ^ 1
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        float x = c[v];
+        if constexpr (NU <= 2) x += dpp_mov<0x4E>(x);
+        if constexpr (NU <= 4) x += dpp_mov<0x124>(x);   // row_ror:4
+        x += dpp_mov<0x128>(x);                          // row_ror:8
+        if constexpr (GW >= 32) x = swap16_sum(x);
+        if constexpr (GW >= 64) x = swap32_sum(x);
+        t[v] = x;
+    }
+}
+
 // v[i] for a runtime i < N: a tree of selects on the bits of i (the opaque intermediates keep
 // the compiler from rebuilding it as an indexed load through scratch memory)
 template <int N>
@@ -543,10 +580,23 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
                                             __half2float(__ushort_as_half((unsigned short)sb_raw[i])));
             }
         }
+        // the lane's output row(s): fin[b][v] = row er * NV + v of the group
+        constexpr int NV = PAIR ? 2 : 1;
+        float fin[B][NV];
 #pragma unroll
-        for (int b = 0; b < B; ++b)
+        for (int b = 0; b < B; ++b) {
+            if constexpr (G::GW >= 16 && NOUT >= 2 && NOUT <= 8) {
+                fold_units<NOUT, NV, G::GW>(part[b], fin[b], slot0);
+            } else {
+                float pv[NV][NOUT];
 #pragma unroll
-            for (int r = 0; r < NP; ++r) part[b][r] = group_sum(part[b][r], G::GW);
+                for (int u = 0; u < NOUT; ++u)
+#pragma unroll
+                    for (int v = 0; v < NV; ++v) pv[v][u] = group_sum(part[b][u * NV + v], G::GW);
+#pragma unroll
+                for (int v = 0; v < NV; ++v) fin[b][v] = pick(pv[v], er);
+            }
+        }
 
         if constexpr (OUT == OUT_RESID) {
             if (io.res) {
@@ -560,7 +610,7 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
         if constexpr (OUT == OUT_HEAD) {
             float tb[B];
 #pragma unroll
-            for (int b = 0; b < B; ++b) tb[b] = pick(part[b], er);
+            for (int b = 0; b < B; ++b) tb[b] = fin[b][0];
             if (eon && erow < N) {
 #pragma unroll
                 for (int b = 0; b < B; ++b) glb(a.logits)[(size_t)b * N + erow] = tb[b];
@@ -583,13 +633,7 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
         } else if constexpr (PAIR) {
 #pragma unroll
             for (int b = 0; b < B; ++b) {
-                float pa[NP / 2], pb[NP / 2];
-#pragma unroll
-                for (int q = 0; q < NP / 2; ++q) {
-                    pa[q] = part[b][2 * q];
-                    pb[q] = part[b][2 * q + 1];
-                }
-                const float t0 = pick(pa, er), t1 = pick(pb, er);
+                const float t0 = fin[b][0], t1 = fin[b][NV - 1];
                 uint64_t* dst = io.dst + b * io.dst_xs;
                 if (eon && erow < N) {
                     if constexpr (OUT == OUT_SWIGLU) {
@@ -630,7 +674,7 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
         } else {
 #pragma unroll
             for (int b = 0; b < B; ++b) {
-                const float t = pick(part[b], er) + bv;
+                const float t = fin[b][0] + bv;
                 uint64_t* dst = io.dst + b * io.dst_xs;
                 if (eon && erow < N) {
                     if constexpr (OUT == OUT_QKV) {

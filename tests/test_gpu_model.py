@@ -273,7 +273,7 @@ def test_full_size_step_over_long_cache(name, kv_pos, mode):
 
 
 @pytest.mark.parametrize("name,kv_pos,guided", [("gpt2_medium_q4_0", 755, True), ("llama520m_q8_0", 899, True),
-                                                 ("llama520m_q8_0", 899, False)])
+                                                 ("llama520m_q8_0", 899, False), ("llama520m_q8_0", 300, False)])
 def test_full_size_pair_over_long_cache(name, kv_pos, guided):
     """The persistent pair at the real shapes (each weight read once for both rows): two
     teacher-forced steps over a random cache of kv_pos positions per row, both rows' logits as
@@ -310,6 +310,18 @@ def test_full_size_pair_over_long_cache(name, kv_pos, guided):
         nxt = o_ids
     gm.synchronize()
     gm.close()
+
+
+@pytest.mark.parametrize("n_wg,kv_pos", [(208, 100), (208, 300)])
+def test_full_size_step_on_a_smaller_grid(n_wg, kv_pos):
+    """The GPT-2-Medium-shaped T3 on 208 workgroups: 192 QKV tiles leave 16 workgroups for the
+    attention items, one chunk per head (101 keys) or two (301 keys), so the items of a head
+    share workgroups with the product's tiles at the longer context."""
+    cfg = synth.config("gpt2_medium_q4_0")
+    say(f"[model-full] gpt2_medium n_wg={n_wg} kv_pos={kv_pos}")
+    w = synth.model_weights(cfg, 42)
+    worst = teacher_forced(cfg, w, n_prompt=0, n_steps=2, kv_pos=kv_pos, mode="persistent", n_wg=n_wg)
+    say(f"  worst rel {worst:.2e}")
 
 
 @pytest.mark.parametrize("mode", MODES)

@@ -113,8 +113,10 @@ struct Ctx {
 //   IN_EMB_NORM the embedding row of the row's input token (+ the learned position row), then the norm
 //   IN_ATTN     the attention output, merged from the per-chunk partials src[b * xs + (h*max_split+s)*(hd+2)]
 //   IN_XCHG32   32-bit exchange words ((uint32_t*)(src + b * xs))[k] (the FC / SwiGLU output)
+// NS sums over the workgroup with one barrier: every wave must have passed a barrier since the
+// last readers of red (the gather's early barrier) before the first writer here
 template <int NS>
-__device__ __forceinline__ void block_sums(float (&v)[NS], float* red)   // NS sums, one pair of barriers
+__device__ __forceinline__ void block_sums(float (&v)[NS], float* red)
 {
 #pragma unroll
     for (int i = 0; i < NS; ++i) v[i] = wave_sum(v[i]);
@@ -130,12 +132,12 @@ __device__ __forceinline__ void block_sums(float (&v)[NS], float* red)   // NS s
         for (int w = 0; w < NWAVE; ++w) r += red[NS * w + i];
         v[i] = r;
     }
-    lds_barrier();
 }
 
 template <class C, int F, int K, int IN, bool LN>
 __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const uint64_t* src, const long long xs,
-                                         const uint32_t ep, const float* g, const float* bt, Smem& sm)
+                                         const uint32_t ep, const float* g, const float* bt, Smem& sm,
+                                         float (&rs)[C::B])
 {
     constexpr int B = C::B;
     constexpr int E = FmtT<F>::E, LPR = K / E, J = (K + NT - 1) / NT;
@@ -144,6 +146,13 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
     auto elem = [&](int j) { return K % NT == 0 ? t + NT * j : min(t + NT * j, K - 1); };
     float v[B][J], gg[J], bb[J];
     bool ok = true;
+    // The early barrier: every wave passes one barrier after issuing its first round of polls and
+    // before waiting on them, so that the previous phase's readers of xl and red are done before
+    // anything here writes them, while the polls' round trip hides the barrier (the context-long
+    // merge, which polls in several rounds, passes it after its last round instead).
+    bool early = false;
+#pragma unroll
+    for (int b = 0; b < B; ++b) rs[b] = 1.f;
     if constexpr (NORM) {
 #pragma unroll
         for (int j = 0; j < J; ++j) {
@@ -162,6 +171,8 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
 #pragma unroll
             for (int j = 0; j < J; ++j) v[b][j] = glb(er)[elem(j)] + (C::GPT2 ? glb(pr)[elem(j)] : 0.f);
         }
+        lds_barrier();   // early barrier (below)
+        early = true;
     } else if constexpr (IN == IN_ATTN) {
         // element k = t + NT*j of row b is dim k % HD of head k / HD; chunk s of head h published
         // (o[0..HD), m, l) in the log2 domain.  A wave covers 64 consecutive elements and HD is a
@@ -214,6 +225,8 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
 #pragma unroll
             for (int q = 0; q < NW; ++q)
                 if (use(q)) wv[q] = xchg::load(addr(q));
+            lds_barrier();   // early barrier (below)
+            early = true;
             ok &= xchg::settle_if(wv, use, addr, ep, cx.limit, a.abort_word);
             // lane 2 q + c, q = (b J + j) SGA + u: m (c = 0) or l (c = 1) of chunk u of (b, j); the
             // 2 SGA lanes of a (b, j) form one aligned group
@@ -306,6 +319,8 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
         uint32_t w[NW];
 #pragma unroll
         for (int q = 0; q < NW; ++q) w[q] = xchg::load(addr(q));
+        lds_barrier();   // early barrier (below)
+        early = true;
         ok = xchg::settle_n(w, NW, addr, ep, cx.limit, a.abort_word);
 #pragma unroll
         for (int b = 0; b < B; ++b)
@@ -321,6 +336,8 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
         uint64_t w[NW];
 #pragma unroll
         for (int q = 0; q < NW; ++q) w[q] = xchg::load(addr(q));
+        lds_barrier();   // early barrier (below)
+        early = true;
         ok = xchg::settle_n(w, NW, addr, ep, cx.limit, a.abort_word);
 #pragma unroll
         for (int b = 0; b < B; ++b) {
@@ -330,6 +347,11 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
         }
     }
     if (!ok) *sm.abort = 1;
+    if (!early) lds_barrier();   // the previous phase's readers of xl and red are done
+    auto put = [&](int b, int j, float y) {
+        const int k = t + NT * j;
+        if (K % NT == 0 || k < K) sm.xl[b * MAX_K + 4 * swz<E>(k, LPR) + (k & 3)] = y;
+    };
 
     if constexpr (NORM) {
         constexpr float invK = 1.0f / (float)K;
@@ -351,35 +373,34 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
                 sums[b] = q2;
             }
         }
+        if constexpr (!LN) {
+            // RMSNorm: x * g goes to LDS at once and 1 / rms (rs) scales the finished dot
+            // products, so the sums' barrier also publishes xl
+#pragma unroll
+            for (int b = 0; b < B; ++b)
+#pragma unroll
+                for (int j = 0; j < J; ++j) put(b, j, v[b][j] * gg[j]);
+            block_sums<NS>(sums, sm.red);
+#pragma unroll
+            for (int b = 0; b < B; ++b) rs[b] = 1.0f / sqrtf(sums[b] * invK + a.eps);
+            return;
+        }
         block_sums<NS>(sums, sm.red);
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-            float mean = 0.f, var;
-            if constexpr (LN) {
-                const float ms = sums[2 * b] * invK;
-                mean = x0[b] + ms;
-                var = fmaxf(sums[2 * b + 1] * invK - ms * ms, 0.f);
-            } else {
-                var = sums[b] * invK;
-            }
+            const float ms = sums[2 * b] * invK;
+            const float mean = x0[b] + ms;
+            const float var = fmaxf(sums[2 * b + 1] * invK - ms * ms, 0.f);
             const float r = 1.0f / sqrtf(var + a.eps);
 #pragma unroll
-            for (int j = 0; j < J; ++j) {
-                float y = (v[b][j] - mean) * r * gg[j];
-                if constexpr (LN) y += bb[j];
-                v[b][j] = y;
-            }
+            for (int j = 0; j < J; ++j) put(b, j, fmaf((v[b][j] - mean) * r, gg[j], bb[j]));
         }
     } else {
-        lds_barrier();   // the previous phase's readers of xl are done
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int j = 0; j < J; ++j) put(b, j, v[b][j]);
     }
-#pragma unroll
-    for (int b = 0; b < B; ++b)
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int k = t + NT * j;
-            if (K % NT == 0 || k < K) sm.xl[b * MAX_K + 4 * swz<E>(k, LPR) + (k & 3)] = v[b][j];
-        }
     lds_barrier();
 }
 
@@ -504,6 +525,7 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
 #pragma unroll
     for (int b = 0; b < B; ++b) best[b] = 0ull;
     bool have_x = false;
+    float rs[B];   // per row: the deferred RMSNorm scale of the dot products (1 otherwise)
     for (int tile = blockIdx.x; tile < G::TILES; tile += gridDim.x) {
         const int row0 = (tile * NWAVE + wave) * G::RPW + sub * NP;   // first row of this lane's group
         // epilogue operands of the lane's own output row(s), issued before the weights
@@ -542,7 +564,7 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
         __builtin_amdgcn_sched_barrier(0);
 
         if (!have_x) {
-            gather_x<C, F, K, IN, LN>(a, cx, io.src, io.src_xs, io.src_ep, io.g, io.bt, sm);
+            gather_x<C, F, K, IN, LN>(a, cx, io.src, io.src_xs, io.src_ep, io.g, io.bt, sm, rs);
             have_x = true;
             if (*sm.abort) return false;
         }
@@ -595,6 +617,10 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
                     for (int v = 0; v < NV; ++v) pv[v][u] = group_sum(part[b][u * NV + v], G::GW);
 #pragma unroll
                 for (int v = 0; v < NV; ++v) fin[b][v] = pick(pv[v], er);
+            }
+            if constexpr ((IN == IN_NORM || IN == IN_EMB_NORM) && !LN) {
+#pragma unroll
+                for (int v = 0; v < NV; ++v) fin[b][v] *= rs[b];
             }
         }
 

@@ -142,6 +142,8 @@ struct StepLayer {
     PackedMat qkv, o, fc, down;               // fc: FC (GPT-2) or interleaved gate/up (Llama)
     const float *n1g, *n1b, *n2g, *n2b;       // norm gains / LayerNorm biases (null for RMSNorm)
     const float *bqkv, *bo, *bfc, *bdown;     // linear biases (null without)
+    // LayerNorm-fed products (GPT-2): c = W g and d = W beta + bias per output row (null for RMSNorm)
+    const float *cqkv, *dqkv, *cfc, *dfc;
     __half *kc, *vc;                          // this layer's cache [B][Hkv][n_ctx][hd]
 };
 // the sampler chain's parameters (sampler.h): temperature, k largest, nucleus, min-p, repetition
@@ -165,6 +167,7 @@ struct StepArgs {
     const float* emb;                         // [vocab][d]
     const float* wpe;                         // [n_ctx][d] learned positions, or null
     const float *nfg, *nfb;                   // final norm
+    const float *hc, *hdv;                    // the head's W nfg and W nfb (LayerNorm), else null
     PackedMat head;
     const float2* rope;                       // [n_ctx][hd/2] (cos, sin), Llama
     int *pos, *tok, *hist;                    // step state (read at launch start, advanced at its end);

@@ -14,6 +14,9 @@ struct LayerW {
     PackedMat qkv, o, fc, down;            // fc = fc (GPT-2) or interleaved gate/up (Llama, Talker)
     float *n1g = nullptr, *n1b = nullptr, *n2g = nullptr, *n2b = nullptr;
     float *bqkv = nullptr, *bo = nullptr, *bfc = nullptr, *bdown = nullptr;
+    // GPT-2, for the persistent step: c = W g and d = W beta + bias of the two LayerNorm-fed
+    // products (QKV with n1, FC with n2), so that the step can normalise after the dot product
+    float *cqkv = nullptr, *dqkv = nullptr, *cfc = nullptr, *dfc = nullptr;
 };
 
 // bump planner over the workspace: the same walk sizes it and lays it out
@@ -112,6 +115,7 @@ struct tsd_model {
     int emb_rows[16] = {};
     const float* wpe = nullptr;
     float *nfg = nullptr, *nfb = nullptr;
+    float *hc = nullptr, *hdv = nullptr;   // GPT-2: head W nfg and W nfb (as cqkv / dqkv)
     tsd::PackedMat head{};
     __half *kc = nullptr, *vc = nullptr;
     size_t kv_layer_elems = 0;

@@ -159,6 +159,8 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
             w.n2g = (float*)P.take(4 * d); w.n2b = (float*)P.take(4 * d);
             w.bqkv = (float*)P.take(4 * 3 * d); w.bo = (float*)P.take(4 * d);
             w.bfc = (float*)P.take(4 * (size_t)ff); w.bdown = (float*)P.take(4 * d);
+            w.cqkv = (float*)P.take(4 * 3 * d); w.dqkv = (float*)P.take(4 * 3 * d);
+            w.cfc = (float*)P.take(4 * (size_t)ff); w.dfc = (float*)P.take(4 * (size_t)ff);
         } else {
             w.qkv = take_mat(P, f, qkv_rows, d);
             w.o = take_mat(P, f, d, H * hd);
@@ -171,6 +173,8 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     float* nfg = (float*)P.take(4 * d);
     float* nfb = c->arch == TSD_ARCH_GPT2 ? (float*)P.take(4 * d) : nullptr;
     PackedMat head = take_mat(P, f, c->vocab, d);
+    float* hc = c->arch == TSD_ARCH_GPT2 ? (float*)P.take(4 * (size_t)c->vocab) : nullptr;
+    float* hdv = c->arch == TSD_ARCH_GPT2 ? (float*)P.take(4 * (size_t)c->vocab) : nullptr;
     const size_t kv_layer = (size_t)B * Hk * c->n_ctx * hd;
     __half* kc = (__half*)P.take(2 * kv_layer * c->n_layer);
     __half* vc = (__half*)P.take(2 * kv_layer * c->n_layer);
@@ -201,6 +205,7 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
         m->pos = pos; m->dbg_pos = pos + 1; m->tok = tok; m->best = best;
         m->hist = hist; m->seq = seq; m->x = x; m->qkv = qkv; m->attn = attn; m->h = h; m->logits = logits; m->part = part;
         m->rope = rope; m->rope_rows = c->n_ctx; m->emb[0] = emb0; m->emb_rows[0] = c->vocab; m->wpe = wpe; m->L = Ls; m->nfg = nfg; m->nfb = nfb;
+        m->hc = hc; m->hdv = hdv;
         m->head = head; m->kc = kc; m->vc = vc; m->kv_layer_elems = kv_layer; m->tpp = tpp; m->vmax = vmax;
         m->qkv_rows = qkv_rows;
         m->ctl = ctl;
@@ -437,6 +442,27 @@ tsd_status pack_weights(tsd_model* m, const tsd_tensor* w)
     HIP_TRY(m, cp(m->nfg, i++), "copy");
     if (c.arch == TSD_ARCH_GPT2) HIP_TRY(m, cp(m->nfb, i++), "copy");
     HIP_TRY(m, pk(m->head, i++, c.vocab, d, 0, PACK_IDENTITY), "pack head");
+    if (c.arch == TSD_ARCH_GPT2) {
+        // c = W g, d = W beta + bias for every LayerNorm-fed product (the persistent step's
+        // deferred normalisation: LN(x) . W = r (W g (x - x0) - (mean - x0) c) + d)
+        auto mv = [&](const PackedMat& W, const float* x, const float* bias, float* y) {
+            ProArgs pa{};
+            pa.src = x;
+            EpiArgs ea{};
+            ea.y = y;
+            ea.bias = bias;
+            return launch_gemv(f, PRO_LOAD, EPI_STORE, W, pa, ea, st);
+        };
+        for (int l = 0; l < c.n_layer; ++l) {
+            const LayerW& L = m->L[l];
+            HIP_TRY(m, mv(L.qkv, L.n1g, nullptr, L.cqkv), "layer-norm constants");
+            HIP_TRY(m, mv(L.qkv, L.n1b, L.bqkv, L.dqkv), "layer-norm constants");
+            HIP_TRY(m, mv(L.fc, L.n2g, nullptr, L.cfc), "layer-norm constants");
+            HIP_TRY(m, mv(L.fc, L.n2b, L.bfc, L.dfc), "layer-norm constants");
+        }
+        HIP_TRY(m, mv(m->head, m->nfg, nullptr, m->hc), "layer-norm constants");
+        HIP_TRY(m, mv(m->head, m->nfb, nullptr, m->hdv), "layer-norm constants");
+    }
     return TSD_OK;
 }
 
@@ -476,6 +502,7 @@ tsd_status setup_step(tsd_model* m)
         t.qkv = w.qkv; t.o = w.o; t.fc = w.fc; t.down = w.down;
         t.n1g = w.n1g; t.n1b = w.n1b; t.n2g = w.n2g; t.n2b = w.n2b;
         t.bqkv = w.bqkv; t.bo = w.bo; t.bfc = w.bfc; t.bdown = w.bdown;
+        t.cqkv = w.cqkv; t.dqkv = w.dqkv; t.cfc = w.cfc; t.dfc = w.dfc;
         t.kc = m->kc + m->kv_layer_elems * l;
         t.vc = m->vc + m->kv_layer_elems * l;
         return t;
@@ -488,9 +515,11 @@ tsd_status setup_step(tsd_model* m)
     for (int l = 1; l < c.n_layer; ++l) {
         const StepLayer t = lay(l);
         const void* a0[] = {L0.qkv.q, L0.qkv.s, L0.qkv.b, L0.o.q, L0.o.s, L0.o.b, L0.fc.q, L0.fc.s, L0.fc.b, L0.down.q,
-                            L0.down.s, L0.down.b, L0.n1g, L0.n1b, L0.n2g, L0.n2b, L0.bqkv, L0.bo, L0.bfc, L0.bdown};
+                            L0.down.s, L0.down.b, L0.n1g, L0.n1b, L0.n2g, L0.n2b, L0.bqkv, L0.bo, L0.bfc, L0.bdown,
+                            L0.cqkv, L0.dqkv, L0.cfc, L0.dfc};
         const void* al[] = {t.qkv.q, t.qkv.s, t.qkv.b, t.o.q, t.o.s, t.o.b, t.fc.q, t.fc.s, t.fc.b, t.down.q,
-                            t.down.s, t.down.b, t.n1g, t.n1b, t.n2g, t.n2b, t.bqkv, t.bo, t.bfc, t.bdown};
+                            t.down.s, t.down.b, t.n1g, t.n1b, t.n2g, t.n2b, t.bqkv, t.bo, t.bfc, t.bdown,
+                            t.cqkv, t.dqkv, t.cfc, t.dfc};
         for (size_t i = 0; i < sizeof(a0) / sizeof(a0[0]); ++i)
             if (!same(a0[i], al[i], l)) return fail(m, TSD_ERR_STATE, "layer tensors are not at a uniform stride");
     }
@@ -502,7 +531,7 @@ tsd_status setup_step(tsd_model* m)
     a.n_layer = c.n_layer; a.H = c.n_head; a.Hk = c.n_kv_head; a.n_ctx = c.n_ctx; a.vocab = c.vocab;
     a.max_split = attn_max_split(c.n_ctx);
     a.eps = c.norm_eps;
-    a.emb = m->emb[0]; a.wpe = m->wpe; a.nfg = m->nfg; a.nfb = m->nfb; a.head = m->head; a.rope = m->rope;
+    a.emb = m->emb[0]; a.wpe = m->wpe; a.nfg = m->nfg; a.nfb = m->nfb; a.hc = m->hc; a.hdv = m->hdv; a.head = m->head; a.rope = m->rope;
     a.pos = m->pos; a.tok = m->tok; a.hist = m->hist; a.seq = m->seq; a.ctr = m->ctl + CTL_EPOCH; a.abort_word = m->ctl + CTL_ABORT;
     a.bad_input = m->ctl + CTL_BAD_INPUT;
     a.logits = m->logits;

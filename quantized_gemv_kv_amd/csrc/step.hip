@@ -109,7 +109,8 @@ struct Ctx {
 // unconditionally (an element past K, when K is not a multiple of NT, reads element K-1 and is
 // discarded), and the words of all rows are polled together (one round trip for the batch).
 //   IN_XCHG     exchange words src[b * xs + k] (epoch ep)
-//   IN_NORM     the same, then LayerNorm (gain g, bias bt) or RMSNorm (gain g) per row
+//   IN_NORM     the same, for a LayerNorm or RMSNorm with gain g: LDS gets g * (x - x0) and the
+//               norm's scale and shift per row come back in rs / ms (applied after the dot products)
 //   IN_EMB_NORM the embedding row of the row's input token (+ the learned position row), then the norm
 //   IN_ATTN     the attention output, merged from the per-chunk partials src[b * xs + (h*max_split+s)*(hd+2)]
 //   IN_XCHG32   32-bit exchange words ((uint32_t*)(src + b * xs))[k] (the FC / SwiGLU output)
@@ -136,15 +137,15 @@ __device__ __forceinline__ void block_sums(float (&v)[NS], float* red)
 
 template <class C, int F, int K, int IN, bool LN>
 __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const uint64_t* src, const long long xs,
-                                         const uint32_t ep, const float* g, const float* bt, Smem& sm,
-                                         float (&rs)[C::B])
+                                         const uint32_t ep, const float* g, Smem& sm, float (&rs)[C::B],
+                                         float (&ms)[C::B])
 {
     constexpr int B = C::B;
     constexpr int E = FmtT<F>::E, LPR = K / E, J = (K + NT - 1) / NT;
     constexpr bool NORM = IN == IN_NORM || IN == IN_EMB_NORM;
     const int t = threadIdx.x;
     auto elem = [&](int j) { return K % NT == 0 ? t + NT * j : min(t + NT * j, K - 1); };
-    float v[B][J], gg[J], bb[J];
+    float v[B][J], gg[J];
     bool ok = true;
     // The early barrier: every wave passes one barrier after issuing its first round of polls and
     // before waiting on them, so that the previous phase's readers of xl and red are done before
@@ -152,12 +153,14 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
     // merge, which polls in several rounds, passes it after its last round instead).
     bool early = false;
 #pragma unroll
-    for (int b = 0; b < B; ++b) rs[b] = 1.f;
+    for (int b = 0; b < B; ++b) {
+        rs[b] = 1.f;
+        ms[b] = 0.f;
+    }
     if constexpr (NORM) {
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             gg[j] = glb(g)[elem(j)];
-            bb[j] = LN ? glb(bt)[elem(j)] : 0.f;
         }
     }
     float x0[B];   // LayerNorm shift per row (see finish_x in the GEMV core)
@@ -373,28 +376,26 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
                 sums[b] = q2;
             }
         }
-        if constexpr (!LN) {
-            // RMSNorm: x * g goes to LDS at once and 1 / rms (rs) scales the finished dot
-            // products, so the sums' barrier also publishes xl
+        // The norm is applied after the dot products: g * (x - x0) goes to LDS at once (x0 the
+        // LayerNorm shift, 0 for RMSNorm), and with the row's sums known the caller turns each
+        // dot product p into rs (p - ms c) + d (LayerNorm: rs = 1 / sigma, ms = mean - x0, c = W g,
+        // d = W beta + bias) or rs p (RMSNorm), so the sums' one barrier also publishes xl.
 #pragma unroll
-            for (int b = 0; b < B; ++b)
+        for (int b = 0; b < B; ++b)
 #pragma unroll
-                for (int j = 0; j < J; ++j) put(b, j, v[b][j] * gg[j]);
-            block_sums<NS>(sums, sm.red);
-#pragma unroll
-            for (int b = 0; b < B; ++b) rs[b] = 1.0f / sqrtf(sums[b] * invK + a.eps);
-            return;
-        }
+            for (int j = 0; j < J; ++j) put(b, j, (v[b][j] - x0[b]) * gg[j]);
         block_sums<NS>(sums, sm.red);
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-            const float ms = sums[2 * b] * invK;
-            const float mean = x0[b] + ms;
-            const float var = fmaxf(sums[2 * b + 1] * invK - ms * ms, 0.f);
-            const float r = 1.0f / sqrtf(var + a.eps);
-#pragma unroll
-            for (int j = 0; j < J; ++j) put(b, j, fmaf((v[b][j] - mean) * r, gg[j], bb[j]));
+            if constexpr (LN) {
+                const float m1 = sums[2 * b] * invK;
+                rs[b] = 1.0f / sqrtf(fmaxf(sums[2 * b + 1] * invK - m1 * m1, 0.f) + a.eps);
+                ms[b] = m1;
+            } else {
+                rs[b] = 1.0f / sqrtf(sums[b] * invK + a.eps);
+            }
         }
+        return;
     } else {
 #pragma unroll
         for (int b = 0; b < B; ++b)
@@ -409,8 +410,9 @@ struct PhaseIO {
     const uint64_t* src;  // input words (IN_XCHG / IN_NORM / IN_ATTN); row b at src + b * src_xs
     long long src_xs;
     uint32_t src_ep;
-    const float* g;       // norm gain / bias
-    const float* bt;
+    const float* g;       // norm gain
+    const float* lc;      // LayerNorm-fed: W g and W beta + bias per output row (normalised after
+    const float* ld;      // the dot products, see gather_x)
     const float* bias;    // linear bias or null
     uint64_t* dst;        // output words; row b at dst + b * dst_xs
     long long dst_xs;
@@ -506,7 +508,9 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
     using G = Geo<F, K, N, NL>;
     constexpr int E = G::E, NP = G::NP;
     constexpr bool PAIR = OUT == OUT_QKV_ROPE || OUT == OUT_SWIGLU;
-    constexpr bool HAS_BIAS = C::GPT2 && !PAIR && OUT != OUT_HEAD;
+    constexpr bool NORM = IN == IN_NORM || IN == IN_EMB_NORM;
+    constexpr bool LNP = NORM && LN;   // LayerNorm applied after the dot products (the bias is in io.ld)
+    constexpr bool HAS_BIAS = C::GPT2 && !PAIR && OUT != OUT_HEAD && !LNP;
     constexpr int QD = C::QD, KD = C::KD;
     static_assert(!PAIR || NP % 2 == 0, "pair epilogues need an even number of rows per lane");
 
@@ -525,7 +529,7 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
 #pragma unroll
     for (int b = 0; b < B; ++b) best[b] = 0ull;
     bool have_x = false;
-    float rs[B];   // per row: the deferred RMSNorm scale of the dot products (1 otherwise)
+    float rs[B], ms[B];   // per row: the norm applied after the dot products (see gather_x)
     for (int tile = blockIdx.x; tile < G::TILES; tile += gridDim.x) {
         const int row0 = (tile * NWAVE + wave) * G::RPW + sub * NP;   // first row of this lane's group
         // epilogue operands of the lane's own output row(s), issued before the weights
@@ -539,6 +543,11 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
             rw[b] = 0ull;
         }
         if constexpr (HAS_BIAS) bv = glb(io.bias)[erc];
+        float lcv = 0.f, ldv = 0.f;
+        if constexpr (LNP) {
+            lcv = glb(io.lc)[erc];
+            ldv = glb(io.ld)[erc];
+        }
         if constexpr (OUT == OUT_RESID) {
 #pragma unroll
             for (int b = 0; b < B; ++b) {
@@ -564,7 +573,7 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
         __builtin_amdgcn_sched_barrier(0);
 
         if (!have_x) {
-            gather_x<C, F, K, IN, LN>(a, cx, io.src, io.src_xs, io.src_ep, io.g, io.bt, sm, rs);
+            gather_x<C, F, K, IN, LN>(a, cx, io.src, io.src_xs, io.src_ep, io.g, sm, rs, ms);
             have_x = true;
             if (*sm.abort) return false;
         }
@@ -618,7 +627,10 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
 #pragma unroll
                 for (int v = 0; v < NV; ++v) fin[b][v] = pick(pv[v], er);
             }
-            if constexpr ((IN == IN_NORM || IN == IN_EMB_NORM) && !LN) {
+            if constexpr (LNP) {
+#pragma unroll
+                for (int v = 0; v < NV; ++v) fin[b][v] = fmaf(rs[b], fmaf(-ms[b], lcv, fin[b][v]), ldv);
+            } else if constexpr (NORM) {
 #pragma unroll
                 for (int v = 0; v < NV; ++v) fin[b][v] *= rs[b];
             }
@@ -991,7 +1003,8 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
             io.src_xs = a.xs_d;
             io.src_ep = e - 1u;
             io.g = shift(a.L0.n1g, o);
-            io.bt = shift(a.L0.n1b, o);
+            io.lc = shift(a.L0.cqkv, o);
+            io.ld = shift(a.L0.dqkv, o);
             io.bias = shift(a.L0.bqkv, o);
             io.dst = a.x_qkv;
             io.dst_xs = a.xs_qkv;
@@ -1034,7 +1047,8 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
             io.src_xs = a.xs_d;
             io.src_ep = e + 2u;
             io.g = shift(a.L0.n2g, o);
-            io.bt = shift(a.L0.n2b, o);
+            io.lc = shift(a.L0.cfc, o);
+            io.ld = shift(a.L0.dfc, o);
             io.bias = shift(a.L0.bfc, o);
             io.dst = a.x_h;
             io.dst_xs = a.xs_h;
@@ -1069,7 +1083,8 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
     io.src_xs = a.xs_d;
     io.src_ep = eh - 1u;
     io.g = a.nfg;
-    io.bt = a.nfb;
+    io.lc = a.hc;
+    io.ld = a.hdv;
     io.dst = a.x_best;
     io.dst_xs = a.xs_best;
     io.dst_ep = eh;

@@ -158,6 +158,12 @@ struct SampChain {
     int order;           // SAMP_ORDER_T3: temperature, top-k, top-p, penalty; SAMP_ORDER_MTL: penalty,
                          // temperature, min-p, top-p, top-k
 };
+// The residual-stream words (x_attn, x_out) of a batch row hold d words, then room for
+// STEP_SHIFT_COPIES copies of word 0, STEP_SHIFT_STRIDE words apart (written by the batch-1
+// GPT-2 step): the LayerNorm shift every thread of a consumer needs.  Each wave polls its own copy, on its own cache line, so that the waves of a
+// compute unit never poll one line together (such polls merge, and a merged poll can return the
+// word as it was when the first of them left).
+constexpr int STEP_SHIFT_COPIES = 4, STEP_SHIFT_STRIDE = 16;
 struct StepArgs {
     StepLayer L0;                             // layer 0; layer l is layer 0 moved by l strides
     long long lstride;                        // bytes between consecutive layers' weights and vectors

@@ -183,7 +183,8 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     StepArgs* d_sa = (StepArgs*)P.take(sizeof(StepArgs));
     const size_t n_part = (size_t)H * attn_max_split(c->n_ctx) * (hd + 2);
     // one batch row's words of each buffer (rounded to 32 words); a buffer holds B rows
-    const size_t xw[7] = {(size_t)qkv_rows, n_part, (size_t)d, (size_t)ff, (size_t)d, 2 * (size_t)MAX_STEP_WG, (size_t)vmax};
+    const size_t dsh = (size_t)d + STEP_SHIFT_COPIES * STEP_SHIFT_STRIDE;   // residual words + the shift's copies
+    const size_t xw[7] = {(size_t)qkv_rows, n_part, dsh, (size_t)ff, dsh, 2 * (size_t)MAX_STEP_WG, (size_t)vmax};
     size_t xrs[7], xtot = 0;
     for (int i = 0; i < 7; ++i) {
         xrs[i] = (xw[i] + 31) & ~(size_t)31;

@@ -42,6 +42,7 @@ namespace {
 using namespace core;
 constexpr int NT = 256;
 constexpr int NWAVE = NT / 64;
+static_assert(NWAVE <= STEP_SHIFT_COPIES, "a copy of the LayerNorm shift per wave");
 constexpr int KTILE = 64;    // keys per wave in the attention phase (4 waves: one 256-key chunk)
 constexpr int SG = 4;        // attention chunks merged per exchange round in the O-proj input (at most)
 
@@ -334,7 +335,9 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
         constexpr int NR = J + (LN ? 1 : 0), NW = B * NR;
         auto addr = [&](int q) -> const uint64_t* {
             const int b = q / NR, qq = q - b * NR;
-            return src + b * xs + (qq < J ? elem(qq) : 0);
+            // word 0 from this wave's copy at batch 1 (the pair, short of registers, was slower
+            // with the copies than polling word 0 itself)
+            return src + b * xs + (qq < J ? elem(qq) : B == 1 ? K + STEP_SHIFT_STRIDE * (t >> 6) : 0);
         };
         uint64_t w[NW];
 #pragma unroll
@@ -728,6 +731,13 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
                         }
                     } else if constexpr (OUT == OUT_RESID) {
                         xchg::store(dst + erow, t + re[b], io.dst_ep);
+                        if constexpr (C::GPT2 && B == 1) {
+                            if (erow == 0) {   // the LayerNorm shift's copies (one per consuming wave)
+#pragma unroll
+                                for (int w = 0; w < STEP_SHIFT_COPIES; ++w)
+                                    xchg::store(dst + N + STEP_SHIFT_STRIDE * w, t + re[b], io.dst_ep);
+                            }
+                        }
                     } else if constexpr (OUT == OUT_GELU) {
                         xchg::store32((uint32_t*)dst + erow, gelu_tanh(t), io.dst_ep);
                     }

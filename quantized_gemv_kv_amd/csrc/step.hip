@@ -113,7 +113,7 @@ struct Ctx {
 //   IN_NORM     the same, for a LayerNorm or RMSNorm with gain g: LDS gets g * (x - x0) and the
 //               norm's scale and shift per row come back in rs / ms (applied after the dot products)
 //   IN_EMB_NORM the embedding row of the row's input token (+ the learned position row), then the norm
-//   IN_ATTN     the attention output, merged from the per-chunk partials src[b * xs + (h*max_split+s)*(hd+2)]
+//   IN_ATTN     the attention output, merged from the per-chunk partials src[b * xs + (h*max_split+s)*(hd+STEP_PART_PAD)]
 //   IN_XCHG32   32-bit exchange words ((uint32_t*)(src + b * xs))[k] (the FC / SwiGLU output)
 // NS sums over the workgroup with one barrier: every wave must have passed a barrier since the
 // last readers of red (the gather's early barrier) before the first writer here
@@ -183,7 +183,7 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
         // multiple of 64, so each (b, j) is one head on every lane of a wave: the wave merges its
         // own heads (the (m, l) words spread over its lanes, then read back as uniform values),
         // with no barrier and no index arithmetic that depends on the context length.
-        constexpr int HD = C::HD, PS = HD + 2;
+        constexpr int HD = C::HD, PS = HD + STEP_PART_PAD;
         static_assert(HD % 64 == 0 && K % 64 == 0, "a wave's 64 elements lie in one head");
         constexpr int SGA = 2 * B * J * SG <= 64 ? SG : (32 / (B * J) > 0 ? 32 / (B * J) : 1);
         static_assert(2 * B * J * SGA <= 64, "one (m or l) word per lane");
@@ -782,7 +782,7 @@ __device__ __forceinline__ bool attn_phase(const StepArgs& a, const Ctx& cx, con
                                            const uint32_t ep_qkv, const uint32_t ep_part, Smem& sm)
 {
     constexpr int HD = C::HD, H = C::H, HK = C::HK, QD = C::QD, KD = C::KD;
-    constexpr int LPK = HD / 8, KPI = 64 / LPK, R = KTILE / KPI, PS = HD + 2;
+    constexpr int LPK = HD / 8, KPI = 64 / LPK, R = KTILE / KPI, PS = HD + STEP_PART_PAD;
     __shared__ float ow[NWAVE][HD];
     __shared__ float mw[NWAVE], lw[NWAVE];
     __shared__ float qkv_l[3 * HD];   // the query, new key and new value of the item

@@ -19,6 +19,10 @@
 //     barrier, only data dependencies, each resolved by one round trip to the memory-side cache;
 //   * each tile issues its weight, scale, bias and residual loads before it polls its input, so
 //     they are in flight while the previous phase finishes elsewhere;
+//   * a norm's scale (and a LayerNorm's mean) is applied to the finished dot products, so a
+//     phase's input goes to LDS as soon as its words arrive, behind one barrier;
+//   * no cache line is polled by two waves of one workgroup: polls of one line from one compute
+//     unit merge, and a merged poll can return the words as they were when the first one left;
 //   * the new token's key and value travel through the exchange (the attention of the same
 //     launch reads them from there); the cache rows are written with plain stores and are read
 //     by later launches, after the kernel boundary has made them visible on every XCD;

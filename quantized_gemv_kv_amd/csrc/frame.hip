@@ -514,19 +514,24 @@ __device__ __forceinline__ void attn16_item(const AttnArgs& a, const int h, cons
     }
 }
 
-// workgroups [0, n_gemm): the QKV product (one 16-row tile each); then one per (head, row)
-template <int U, int HD, int TILE>
+// STACKED = false: workgroups [0, n_gemm) take the QKV product (one 16-row tile each), the ones
+// after them one attention item per (head, row).  STACKED = true (short caches, whose items have
+// little to preload): workgroup w takes product tile w, then item w, on a grid of
+// max(n_gemm, items); the products never wait, so every item's words arrive once the grid's
+// workgroups are resident together (one per compute unit here).
+template <int U, int HD, int TILE, bool STACKED>
 __global__ __launch_bounds__(256) void k_qkv_attn(const TiledMat W, const MmIn in, const Mm16Out o, const AttnArgs a,
                                                   const int n_gemm, const long long limit, uint32_t* abort_word)
 {
     if ((int)blockIdx.x < n_gemm) {
         mm16_block<MM_QKV_ROPE, 1, 4, U>(W, in, o, blockIdx.x, 1, 0);
-        return;
+        if (!STACKED) return;
     }
     // the R = H / Hkv query heads of one (row, kv head) read the same cache rows: their items
     // are 8 workgroups apart, which puts them on one XCD and lets its L2 serve the second read
     // (when the (row, kv head) pairs come in multiples of 8; else items in (row, head) order)
-    const int item = blockIdx.x - n_gemm, R = a.H / a.Hkv;
+    const int item = STACKED ? (int)blockIdx.x : (int)blockIdx.x - n_gemm, R = a.H / a.Hkv;
+    if (STACKED && item >= a.H * a.B) return;
     int h, b;
     if ((a.B * a.Hkv) % 8 == 0) {
         const int pair = item / (8 * R) * 8 + item % 8, r = item / 8 % R;
@@ -805,14 +810,15 @@ hipError_t launch_qkv_attention(const TiledMat& W, const MmIn& in, const Mm16Out
         !a.act_hi || !a.act_lo || !abort_word || o.rows < 1 || o.rows > MM_ROWS || in.rows < 1 || in.rows > MM_ROWS ||
         !in.a.hi || !in.a.lo || (in.ssq && (in.n_ssq < 1 || in.n_ssq > MM_MAX_SSQ)))
         return hipErrorInvalidValue;
-    const int n_gemm = (W.N + 15) / 16;
-    const dim3 grid(n_gemm + a.H * a.B);
+    const int n_gemm = (W.N + 15) / 16, items = a.H * a.B;
+    // short caches (the code predictor's): product and item stacked on one workgroup
+    const dim3 grid(n_gemm + items), stacked(n_gemm > items ? n_gemm : items);
     if (a.hd == 64) {
-        if (a.n_ctx <= 64) hipLaunchKernelGGL((k_qkv_attn<4, 64, 16>), grid, dim3(256), 0, st, W, in, o, a, n_gemm, limit, abort_word);
-        else hipLaunchKernelGGL((k_qkv_attn<4, 64, 64>), grid, dim3(256), 0, st, W, in, o, a, n_gemm, limit, abort_word);
+        if (a.n_ctx <= 64) hipLaunchKernelGGL((k_qkv_attn<4, 64, 16, true>), stacked, dim3(256), 0, st, W, in, o, a, n_gemm, limit, abort_word);
+        else hipLaunchKernelGGL((k_qkv_attn<4, 64, 64, false>), grid, dim3(256), 0, st, W, in, o, a, n_gemm, limit, abort_word);
     } else {
-        if (a.n_ctx <= 64) hipLaunchKernelGGL((k_qkv_attn<4, 128, 16>), grid, dim3(256), 0, st, W, in, o, a, n_gemm, limit, abort_word);
-        else hipLaunchKernelGGL((k_qkv_attn<4, 128, 32>), grid, dim3(256), 0, st, W, in, o, a, n_gemm, limit, abort_word);
+        if (a.n_ctx <= 64) hipLaunchKernelGGL((k_qkv_attn<4, 128, 16, true>), stacked, dim3(256), 0, st, W, in, o, a, n_gemm, limit, abort_word);
+        else hipLaunchKernelGGL((k_qkv_attn<4, 128, 32, false>), grid, dim3(256), 0, st, W, in, o, a, n_gemm, limit, abort_word);
     }
     return hipGetLastError();
 }

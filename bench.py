@@ -118,16 +118,29 @@ STEP_SOURCES = ["quantized_gemv_kv_amd/csrc/" + f for f in ("step.hip", "exchang
 STEP_DECLS = ("quantized_gemv_kv_amd/csrc/kernels.h", "// ---- persistent decode step", "// ---- sampler chain")
 
 
-def step_sources_hash():
+def _code_only(text):
+    """C++ source without its comments and with whitespace collapsed: an edit of comments or
+    layout leaves the kernel, and so this text, unchanged."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def step_sources_hash(read=None):
+    """Hash of the code the step kernel is compiled from (comments and layout ignored); read(path)
+    returns a file's text (default: the working tree)."""
     import hashlib
+    if read is None:
+        def read(path):
+            with open(os.path.join(ROOT, path)) as fh:
+                return fh.read()
     h = hashlib.sha256()
     for f in STEP_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        h.update(_code_only(read(f)).encode())
     path, a, b = STEP_DECLS
-    with open(os.path.join(ROOT, path)) as fh:
-        text = fh.read()
-    h.update(text[text.index(a):text.index(b)].encode())
+    text = read(path)
+    h.update(_code_only(text[text.index(a):text.index(b)]).encode())
     return h.hexdigest()[:16]
 def counted_traffic(kernel, workload, bytes_per_launch):
     """HBM-side bytes per launch of the step kernel from the committed FETCH_SIZE / WRITE_SIZE

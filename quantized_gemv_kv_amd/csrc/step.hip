@@ -179,7 +179,7 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
 #pragma unroll
             for (int j = 0; j < J; ++j) v[b][j] = glb(er)[elem(j)] + (C::GPT2 ? glb(pr)[elem(j)] : 0.f);
         }
-        lds_barrier();   // early barrier (below)
+        lds_barrier();   // the early barrier (see early above)
         early = true;
     } else if constexpr (IN == IN_ATTN) {
         // element k = t + NT*j of row b is dim k % HD of head k / HD; chunk s of head h published
@@ -233,7 +233,7 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
 #pragma unroll
             for (int q = 0; q < NW; ++q)
                 if (use(q)) wv[q] = xchg::load(addr(q));
-            lds_barrier();   // early barrier (below)
+            lds_barrier();   // the early barrier (see early above)
             early = true;
             ok &= xchg::settle_if(wv, use, addr, ep, cx.limit, a.abort_word);
             // lane 2 q + c, q = (b J + j) SGA + u: m (c = 0) or l (c = 1) of chunk u of (b, j); the
@@ -327,7 +327,7 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
         uint32_t w[NW];
 #pragma unroll
         for (int q = 0; q < NW; ++q) w[q] = xchg::load(addr(q));
-        lds_barrier();   // early barrier (below)
+        lds_barrier();   // the early barrier (see early above)
         early = true;
         ok = xchg::settle_n(w, NW, addr, ep, cx.limit, a.abort_word);
 #pragma unroll
@@ -346,7 +346,7 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
         uint64_t w[NW];
 #pragma unroll
         for (int q = 0; q < NW; ++q) w[q] = xchg::load(addr(q));
-        lds_barrier();   // early barrier (below)
+        lds_barrier();   // the early barrier (see early above)
         early = true;
         ok = xchg::settle_n(w, NW, addr, ep, cx.limit, a.abort_word);
 #pragma unroll

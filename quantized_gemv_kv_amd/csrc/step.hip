@@ -140,7 +140,9 @@ __device__ __forceinline__ void block_sums(float (&v)[NS], float* red)
     }
 }
 
-template <class C, int F, int K, int IN, bool LN>
+// X16: elements 16..31 of every 32 go to LDS divided by 16 (the high nibbles' weights are then
+// taken as 16 q)
+template <class C, int F, int K, int IN, bool LN, bool X16 = false>
 __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const uint64_t* src, const long long xs,
                                          const uint32_t ep, const float* g, Smem& sm, float (&rs)[C::B],
                                          float (&ms)[C::B])
@@ -360,6 +362,7 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
     if (!early) lds_barrier();   // the previous phase's readers of xl and red are done
     auto put = [&](int b, int j, float y) {
         const int k = t + NT * j;
+        if (X16 && (k & 31) >= 16) y *= 0.0625f;   // exact
         if (K % NT == 0 || k < K) sm.xl[b * MAX_K + 4 * swz<E>(k, LPR) + (k & 3)] = y;
     };
 
@@ -486,6 +489,8 @@ __device__ __forceinline__ void fold_units(const float (&p)[NU * NV], float (&t)
     }
 }
 
+typedef _Float16 h2t __attribute__((ext_vector_type(2)));
+
 // v[i] for a runtime i < N: a tree of selects on the bits of i (the opaque intermediates keep
 // the compiler from rebuilding it as an indexed load through scratch memory)
 template <int N>
@@ -517,6 +522,7 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
     constexpr bool PAIR = OUT == OUT_QKV_ROPE || OUT == OUT_SWIGLU;
     constexpr bool NORM = IN == IN_NORM || IN == IN_EMB_NORM;
     constexpr bool LNP = NORM && LN;   // LayerNorm applied after the dot products (the bias is in io.ld)
+    constexpr bool PREH = F == FMT_Q4_0 && NL <= 2 && B == 2;   // weights as fp16 pairs (below)
     constexpr bool HAS_BIAS = C::GPT2 && !PAIR && OUT != OUT_HEAD && !LNP;
     constexpr int QD = C::QD, KD = C::KD;
     static_assert(!PAIR || NP % 2 == 0, "pair epilogues need an even number of rows per lane");
@@ -579,11 +585,33 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
 
+        // the pair in Q4_0 with at most two slots a lane: the weights as fp16 pairs, q - 8 for the
+        // low nibbles and 16 (q - 8) for the high ones (against x / 16), each pair two elements two
+        // apart, multiplied with one mixed fp16 x fp32 FMA per weight, the -8 offset needing no sum
+        // of x (fewer live registers than the per-row decode; at batch 1 it measured slower)
+        h2t wh[PREH ? NL : 1][16];
+        auto pre = [&]() {
+            if constexpr (PREH) {
+#pragma unroll
+                for (int i = 0; i < NL; ++i) {
+                    const uint32_t ws[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t w8 = ws[q] >> 8;
+                        wh[i][4 * q + 0] = __builtin_bit_cast(h2t, (ws[q] & 0x000F000Fu) | 0x64006400u) - h2t{1032.f, 1032.f};
+                        wh[i][4 * q + 1] = __builtin_bit_cast(h2t, (ws[q] & 0x00F000F0u) | 0x64006400u) - h2t{1152.f, 1152.f};
+                        wh[i][4 * q + 2] = __builtin_bit_cast(h2t, (w8 & 0x000F000Fu) | 0x64006400u) - h2t{1032.f, 1032.f};
+                        wh[i][4 * q + 3] = __builtin_bit_cast(h2t, (w8 & 0x00F000F0u) | 0x64006400u) - h2t{1152.f, 1152.f};
+                    }
+                }
+            }
+        };
         if (!have_x) {
-            gather_x<C, F, K, IN, LN>(a, cx, io.src, io.src_xs, io.src_ep, io.g, sm, rs, ms);
+            gather_x<C, F, K, IN, LN, PREH>(a, cx, io.src, io.src_xs, io.src_ep, io.g, sm, rs, ms);
             have_x = true;
             if (*sm.abort) return false;
         }
+        pre();
 
         // per row: this lane's x slices and their sums, then the dot products with the weights
         float part[B][NP];
@@ -613,9 +641,26 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
             for (int i = 0; i < NL; ++i) {
                 const int j = G::WIDE ? i % G::SPL : 0;
                 const int r = G::WIDE ? i / G::SPL : i;
-                const float d = slot_dot<F>(w[i], xs[j], h_raw[i]);
-                part[b][r] += slot_value<F>(d, sx[j], __half2float(__ushort_as_half((unsigned short)sc_raw[i])),
-                                            __half2float(__ushort_as_half((unsigned short)sb_raw[i])));
+                const float sc = __half2float(__ushort_as_half((unsigned short)sc_raw[i]));
+                if constexpr (PREH) {
+                    // word q: pairs (4q, 4q+2), (16+4q, 16+4q+2), (4q+1, 4q+3), (16+4q+1, 16+4q+3)
+                    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        a0 = fmaf((float)wh[i][4 * q + 0].x, xs[j][4 * q], a0);
+                        a1 = fmaf((float)wh[i][4 * q + 1].x, xs[j][16 + 4 * q], a1);
+                        a0 = fmaf((float)wh[i][4 * q + 0].y, xs[j][4 * q + 2], a0);
+                        a1 = fmaf((float)wh[i][4 * q + 1].y, xs[j][16 + 4 * q + 2], a1);
+                        a0 = fmaf((float)wh[i][4 * q + 2].x, xs[j][4 * q + 1], a0);
+                        a1 = fmaf((float)wh[i][4 * q + 3].x, xs[j][16 + 4 * q + 1], a1);
+                        a0 = fmaf((float)wh[i][4 * q + 2].y, xs[j][4 * q + 3], a0);
+                        a1 = fmaf((float)wh[i][4 * q + 3].y, xs[j][16 + 4 * q + 3], a1);
+                    }
+                    part[b][r] = fmaf(sc, a0 + a1, part[b][r]);
+                } else {
+                    const float d = slot_dot<F>(w[i], xs[j], h_raw[i]);
+                    part[b][r] += slot_value<F>(d, sx[j], sc, __half2float(__ushort_as_half((unsigned short)sb_raw[i])));
+                }
             }
         }
         // the lane's output row(s): fin[b][v] = row er * NV + v of the group

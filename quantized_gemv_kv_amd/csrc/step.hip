@@ -523,6 +523,7 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
     constexpr bool NORM = IN == IN_NORM || IN == IN_EMB_NORM;
     constexpr bool LNP = NORM && LN;   // LayerNorm applied after the dot products (the bias is in io.ld)
     constexpr bool PREH = F == FMT_Q4_0 && NL <= 2 && B == 2;   // weights as fp16 pairs (below)
+    constexpr bool PRE8 = F == FMT_Q8_0 && B == 2;               // the same for Q8_0
     constexpr bool HAS_BIAS = C::GPT2 && !PAIR && OUT != OUT_HEAD && !LNP;
     constexpr int QD = C::QD, KD = C::KD;
     static_assert(!PAIR || NP % 2 == 0, "pair epilogues need an even number of rows per lane");
@@ -589,8 +590,21 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
         // low nibbles and 16 (q - 8) for the high ones (against x / 16), each pair two elements two
         // apart, multiplied with one mixed fp16 x fp32 FMA per weight, the -8 offset needing no sum
         // of x (fewer live registers than the per-row decode; at batch 1 it measured slower)
-        h2t wh[PREH ? NL : 1][16];
+        h2t wh[PREH || PRE8 ? NL : 1][PRE8 ? 8 : 16];
         auto pre = [&]() {
+            if constexpr (PRE8) {
+                // bytes q -> fp16 q - 128 in pairs (byte permutes build 1024 + q, a packed
+                // subtract of 1152 centres them exactly)
+#pragma unroll
+                for (int i = 0; i < NL; ++i) {
+                    const uint32_t ws[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        wh[i][2 * q + 0] = __builtin_bit_cast(h2t, __builtin_amdgcn_perm(0x64646464u, ws[q], 0x04010400u)) - h2t{1152.f, 1152.f};
+                        wh[i][2 * q + 1] = __builtin_bit_cast(h2t, __builtin_amdgcn_perm(0x64646464u, ws[q], 0x04030402u)) - h2t{1152.f, 1152.f};
+                    }
+                }
+            }
             if constexpr (PREH) {
 #pragma unroll
                 for (int i = 0; i < NL; ++i) {
@@ -642,7 +656,18 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
                 const int j = G::WIDE ? i % G::SPL : 0;
                 const int r = G::WIDE ? i / G::SPL : i;
                 const float sc = __half2float(__ushort_as_half((unsigned short)sc_raw[i]));
-                if constexpr (PREH) {
+                if constexpr (PRE8) {
+                    // word q: pairs (4q, 4q+1), (4q+2, 4q+3)
+                    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        a0 = fmaf((float)wh[i][2 * q].x, xs[j][4 * q], a0);
+                        a1 = fmaf((float)wh[i][2 * q + 1].x, xs[j][4 * q + 2], a1);
+                        a0 = fmaf((float)wh[i][2 * q].y, xs[j][4 * q + 1], a0);
+                        a1 = fmaf((float)wh[i][2 * q + 1].y, xs[j][4 * q + 3], a1);
+                    }
+                    part[b][r] = fmaf(sc, a0 + a1, part[b][r]);
+                } else if constexpr (PREH) {
                     // word q: pairs (4q, 4q+2), (16+4q, 16+4q+2), (4q+1, 4q+3), (16+4q+1, 16+4q+3)
                     float a0 = 0.f, a1 = 0.f;
 #pragma unroll

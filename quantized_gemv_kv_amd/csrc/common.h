@@ -109,6 +109,14 @@ __device__ __forceinline__ float swap32_sum(float v)
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// the value of lane l ^ 32 (the swap returns this lane's value and the other's, in an order that
+// depends on the lane half; their xor with this lane's value leaves the other's whatever the order)
+__device__ __forceinline__ float swap32_other(float v)
+{
+    const uint32_t u = __float_as_uint(v);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0] ^ r[1] ^ u);
+}
 #ifndef TSD_PERMLANE_SWAP
 #define TSD_PERMLANE_SWAP 1
 #endif

@@ -159,6 +159,7 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
     // anything here writes them, while the polls' round trip hides the barrier (the context-long
     // merge, which polls in several rounds, passes it after its last round instead).
     bool early = false;
+    bool paired = false;   // IN_ATTN: lane l holds dim 2 (l % 32) + l / 32 of its wave's 64 elements
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         rs[b] = 1.f;
@@ -215,51 +216,87 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
         const int ml_b = ml_bj / J, ml_j = ml_bj - ml_b * J;
         if (cx.S <= SGA) {
             // every chunk in one round (up to SGA chunks of context): the merge weights are
-            // computed across the lanes that hold the (m, l) words, then read back per (b, j)
-            const int ns = cx.S;
-            auto addr = [&](int q) -> const uint64_t* {
-                if (q == 0) {
-                    int hh = 0;
+            // computed across the lanes that hold the (m, l) words, then read back per (b, j).
+            // With PAIRS the outputs are read two chunks per 16-byte load: lanes 0..31 read dims
+            // 2i, 2i + 1 of chunk 2p, lanes 32..63 the same dims of chunk 2p + 1 (half the load
+            // instructions of one word per lane and chunk); a swap between the lane halves then
+            // sums the chunks, and lane l ends with dim 2 (l % 32) + l / 32 of the wave's 64.
+            // Without PAIRS (the Q4_0 pair: short of registers) lane l reads dim l of each chunk.
+            constexpr bool PAIRS = !(B == 2 && F == FMT_Q4_0);
+            constexpr int NPR = (SGA + 1) / 2, NQ = PAIRS ? B * J * NPR : B * J * SGA;
+            const int ns = cx.S, npr = (ns + 1) / 2;
+            const int hi = lane >> 5, dl = 2 * (lane & 31);
+            const __amdgpu_buffer_rsrc_t rs_p = xchg::words_rsrc(src, (size_t)B * xs);
+            int hh = 0;
 #pragma unroll
-                    for (int j = 0; j < J; ++j)
-                        if (j == ml_j) hh = hj[j];
-                    return src + ml_b * xs + ((size_t)hh * a.max_split + min(ml_u, ns - 1)) * PS + HD + (lane & 1);
-                }
-                const int bj = (q - 1) / SGA, u = (q - 1) % SGA;
+            for (int j = 0; j < J; ++j)
+                if (j == ml_j) hh = hj[j];
+            const uint64_t* mlp = src + ml_b * xs + ((size_t)hh * a.max_split + min(ml_u, ns - 1)) * PS + HD + (lane & 1);
+            // PAIRS: pair q = (b J + j) NPR + p, the second chunk of a last, odd pair re-reading
+            // chunk ns - 1 (its weight is 0); else word q = (b J + j) SGA + u, chunk u
+            auto use = [&](int q) { return PAIRS ? q % NPR < npr : q % SGA < ns; };
+            auto off = [&](int q) -> uint32_t {
+                const int bj = q / NPR, pp = q % NPR;
+                const int b = bj / J, j = bj - b * J;
+                const int sc = min(2 * pp + hi, ns - 1);
+                return (uint32_t)(8 * (b * xs + ((size_t)hj[j] * a.max_split + sc) * PS + (ij[j] - lane) + dl));
+            };
+            auto addr = [&](int q) -> const uint64_t* {
+                const int bj = q / SGA, u = q % SGA;
                 const int b = bj / J, j = bj - b * J;
                 return src + b * xs + ((size_t)hj[j] * a.max_split + min(u, ns - 1)) * PS + ij[j];
             };
-            constexpr int NW = 1 + B * J * SGA;
-            auto use = [&](int q) { return q == 0 || (q - 1) % SGA < ns; };
-            uint64_t wv[NW];
+            using WT = std::conditional_t<PAIRS, xchg::u64x2, uint64_t>;
+            auto ld = [&](int q) -> WT {
+                if constexpr (PAIRS) return xchg::load2(rs_p, off(q));
+                else return xchg::load(addr(q));
+            };
+            uint64_t wml = xchg::load(mlp);
+            WT wo[NQ];
 #pragma unroll
-            for (int q = 0; q < NW; ++q)
-                if (use(q)) wv[q] = xchg::load(addr(q));
+            for (int q = 0; q < NQ; ++q)
+                if (use(q)) wo[q] = ld(q);
             lds_barrier();   // the early barrier (see early above)
             early = true;
-            ok &= xchg::settle_if(wv, use, addr, ep, cx.limit, a.abort_word);
+            ok &= xchg::settle_with(wml, mlp, wo, use, ld, ep, cx.limit, a.abort_word);
             // lane 2 q + c, q = (b J + j) SGA + u: m (c = 0) or l (c = 1) of chunk u of (b, j); the
             // 2 SGA lanes of a (b, j) form one aligned group
-            const float mlv = xchg::value(wv[0]);
+            const float mlv = xchg::value(wml);
             const bool live = ml_u < ns && lane < 2 * B * J * SGA;
             const float mm = (lane & 1) == 0 && live ? mlv : -INFINITY;
             const float M = group_max(mm, 2 * SGA);
             const float w = exp2f(mm - M);                       // the chunk's weight on its m lane, else 0
             const float wl = dpp_mov<0xB1>(w);                   // on an l lane: its chunk's weight
             const float L = group_sum((lane & 1) && live ? mlv * wl : 0.f, 2 * SGA);
-            const float f = w / L;                               // final weight of the chunk (m lanes)
+            const float f = w / L;                               // final weight of the chunk (m lanes), 0 past ns
+            auto fw = [&](int c) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), 2 * c)); };
 #pragma unroll
             for (int b = 0; b < B; ++b)
 #pragma unroll
                 for (int j = 0; j < J; ++j) {
-                    float O = 0.f;
+                    const int c0 = (b * J + j) * SGA;   // chunk 0 of (b, j) among the (m, l) lanes
+                    if constexpr (PAIRS) {
+                        float O0 = 0.f, O1 = 0.f;   // dims dl and dl + 1 from this lane's chunks
 #pragma unroll
-                    for (int u = 0; u < SGA; ++u)
-                        if (u < ns)
-                            O = fmaf(xchg::value(wv[1 + (b * J + j) * SGA + u]),
-                                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), 2 * ((b * J + j) * SGA + u))), O);
-                    v[b][j] = O;
+                        for (int pp = 0; pp < NPR; ++pp)
+                            if (pp < npr) {
+                                const float f0 = fw(c0 + 2 * pp), f1 = 2 * pp + 1 < SGA ? fw(c0 + 2 * pp + 1) : 0.f;
+                                const float fs = hi ? f1 : f0;
+                                const xchg::u64x2 wq = wo[(b * J + j) * NPR + pp];
+                                O0 = fmaf(xchg::value(wq.x), fs, O0);
+                                O1 = fmaf(xchg::value(wq.y), fs, O1);
+                            }
+                        // lanes 0..31 keep dim dl and take the other half's share of it; lanes 32..63 dim dl + 1
+                        v[b][j] = (hi ? O1 : O0) + swap32_other(hi ? O0 : O1);
+                    } else {
+                        float O = 0.f;
+#pragma unroll
+                        for (int u = 0; u < SGA; ++u)
+                            if (u < ns) O = fmaf(xchg::value(wo[c0 + u]), fw(c0 + u), O);
+                        v[b][j] = O;
+                    }
                 }
+            paired = PAIRS;
         } else {
             for (int s0 = 0; s0 < cx.S; s0 += SGA) {
                 const int ns = min(SGA, cx.S - s0);
@@ -361,7 +398,7 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
     if (!ok) *sm.abort = 1;
     if (!early) lds_barrier();   // the previous phase's readers of xl and red are done
     auto put = [&](int b, int j, float y) {
-        const int k = t + NT * j;
+        const int k = (paired ? (t & ~63) + 2 * (t & 31) + ((t >> 5) & 1) : t) + NT * j;
         if (X16 && (k & 31) >= 16) y *= 0.0625f;   // exact
         if (K % NT == 0 || k < K) sm.xl[b * MAX_K + 4 * swz<E>(k, LPR) + (k & 3)] = y;
     };

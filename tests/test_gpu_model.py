@@ -312,6 +312,36 @@ def test_full_size_pair_over_long_cache(name, kv_pos, guided):
     gm.close()
 
 
+@pytest.mark.parametrize("name,batch,kv_pos", [("gpt2_medium_q4_0", 1, 1300), ("llama520m_q8_0", 2, 1100)])
+def test_full_size_step_past_four_chunks(name, batch, kv_pos):
+    """A context of more than four 256-key chunks (1,536 positions): the output projection's input
+    merges the chunks' partials in rounds of four, which no shorter context reaches; two
+    teacher-forced steps over a random cache, every row's logits at rel <= 2e-3."""
+    cfg = dict(synth.config(name), n_ctx=1536, batch=batch)
+    say(f"[model-full] {name} n_ctx=1536 batch={batch} kv_pos={kv_pos}")
+    w = synth.model_weights(cfg, 42)
+    from quantized_gemv_kv_amd import Model
+    gm = Model(dict(cfg, launch_mode="persistent"), w)
+    assert gm.uses_persistent_step()
+    om = oracle.OracleModel(cfg, w)
+    k, v = synth.kv_cache(cfg, kv_pos, seed=5)
+    om.load_kv(k, v, kv_pos)
+    gm.load_kv(dev(k), dev(v), kv_pos)
+    nxt = synth.prompt_tokens(cfg, 1, seed=6)[:, 0, :]
+    for s in range(2):
+        o_ids = om.step(nxt)
+        g_ids = gm.step(dev(nxt)).cpu().numpy()
+        lo, lg = om.logits(), gm.logits().cpu().numpy()
+        r = rel_err(lg, lo)
+        say(f"  step {s}: rel {r:.2e}")
+        assert r <= REL_TOL
+        for b in range(batch):
+            assert ids_agree(g_ids[b, 0], lo[b]), (b, g_ids, o_ids)
+        nxt = o_ids
+    gm.synchronize()
+    gm.close()
+
+
 @pytest.mark.parametrize("n_wg,kv_pos", [(208, 100), (208, 300)])
 def test_full_size_step_on_a_smaller_grid(n_wg, kv_pos):
     """The GPT-2-Medium-shaped T3 on 208 workgroups: 192 QKV tiles leave 16 workgroups for the

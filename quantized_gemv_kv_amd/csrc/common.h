@@ -109,14 +109,6 @@ __device__ __forceinline__ float swap32_sum(float v)
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-// the value of lane l ^ 32 (the swap returns this lane's value and the other's, in an order that
-// depends on the lane half; their xor with this lane's value leaves the other's whatever the order)
-__device__ __forceinline__ float swap32_other(float v)
-{
-    const uint32_t u = __float_as_uint(v);
-    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return __uint_as_float(r[0] ^ r[1] ^ u);
-}
 #ifndef TSD_PERMLANE_SWAP
 #define TSD_PERMLANE_SWAP 1
 #endif
@@ -137,15 +129,6 @@ __device__ __forceinline__ float group_sum(float v, int g)
     return v;
 }
 __device__ __forceinline__ float wave_sum(float v) { return group_sum(v, 64); }
-// maximum over aligned groups of g lanes (g a power of two <= 16); every lane gets its group's
-__device__ __forceinline__ float group_max(float v, int g)
-{
-    if (g >= 2) v = fmaxf(v, dpp_mov<0xB1>(v));
-    if (g >= 4) v = fmaxf(v, dpp_mov<0x4E>(v));
-    if (g >= 8) v = fmaxf(v, dpp_mov<0x141>(v));
-    if (g >= 16) v = fmaxf(v, dpp_mov<0x140>(v));
-    return v;
-}
 __device__ __forceinline__ float wave_max(float v)
 {
     v = fmaxf(v, dpp_mov<0xB1>(v));

@@ -166,7 +166,7 @@ struct SampChain {
 constexpr int STEP_SHIFT_COPIES = 4, STEP_SHIFT_STRIDE = 16;
 // An attention partial of the persistent step (o[0..hd), m, l) takes hd + STEP_PART_PAD words, a
 // whole number of 128-byte lines, so that no line holds words of two partials (which the waves of
-// one consumer poll separately).
+// the merging item poll separately).
 constexpr int STEP_PART_PAD = 16;
 struct StepArgs {
     StepLayer L0;                             // layer 0; layer l is layer 0 moved by l strides
@@ -187,7 +187,8 @@ struct StepArgs {
     uint32_t* abort_word;                     // sticky: a wait gave up
     const uint32_t* bad_input;                // sticky: an input id was rejected (the launch does nothing)
     float* logits;                            // [B][vocab]
-    // exchange words: QKV out, attention partials [H][max_split][hd+STEP_PART_PAD], attention-block output
+    // exchange words: QKV out, attention partials [H][max_split][hd+STEP_PART_PAD] then the heads'
+    // outputs [H * hd], attention-block output
     // (residual stream), MLP hidden, layer output (residual stream), per-workgroup argmax keys;
     // batch row b's words of each buffer start b * its row stride (xs_*) after row 0's
     uint64_t *x_qkv, *x_part, *x_attn, *x_h, *x_out, *x_best;

@@ -181,7 +181,7 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     // persistent step: layer table, control words, exchange words
     uint32_t* ctl = (uint32_t*)P.take(sizeof(uint32_t) * 64);
     StepArgs* d_sa = (StepArgs*)P.take(sizeof(StepArgs));
-    const size_t n_part = (size_t)H * attn_max_split(c->n_ctx) * (hd + STEP_PART_PAD);
+    const size_t n_part = (size_t)H * attn_max_split(c->n_ctx) * (hd + STEP_PART_PAD) + (size_t)H * hd;   // + one writer's outputs
     // one batch row's words of each buffer (rounded to 32 words); a buffer holds B rows
     const size_t dsh = (size_t)d + STEP_SHIFT_COPIES * STEP_SHIFT_STRIDE;   // residual words + the shift's copies
     const size_t xw[7] = {(size_t)qkv_rows, n_part, dsh, (size_t)ff, dsh, 2 * (size_t)MAX_STEP_WG, (size_t)vmax};

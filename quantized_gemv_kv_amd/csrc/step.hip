@@ -48,10 +48,9 @@ constexpr int NT = 256;
 constexpr int NWAVE = NT / 64;
 static_assert(NWAVE <= STEP_SHIFT_COPIES, "a copy of the LayerNorm shift per wave");
 constexpr int KTILE = 64;    // keys per wave in the attention phase (4 waves: one 256-key chunk)
-constexpr int SG = 4;        // attention chunks merged per exchange round in the O-proj input (at most)
 
 enum { A_GPT2 = 0, A_LLAMA = 1 };
-enum { IN_XCHG = 0, IN_NORM = 1, IN_EMB_NORM = 2, IN_ATTN = 3, IN_XCHG32 = 4 };
+enum { IN_XCHG = 0, IN_NORM = 1, IN_EMB_NORM = 2, IN_XCHG32 = 3 };
 enum { OUT_QKV = 0, OUT_QKV_ROPE = 1, OUT_RESID = 2, OUT_GELU = 3, OUT_SWIGLU = 4, OUT_HEAD = 5 };
 
 constexpr int slices_for(int fmt_e, int K) { return K / fmt_e > 64 ? K / fmt_e / 64 : 1; }
@@ -117,7 +116,6 @@ struct Ctx {
 //   IN_NORM     the same, for a LayerNorm or RMSNorm with gain g: LDS gets g * (x - x0) and the
 //               norm's scale and shift per row come back in rs / ms (applied after the dot products)
 //   IN_EMB_NORM the embedding row of the row's input token (+ the learned position row), then the norm
-//   IN_ATTN     the attention output, merged from the per-chunk partials src[b * xs + (h*max_split+s)*(hd+STEP_PART_PAD)]
 //   IN_XCHG32   32-bit exchange words ((uint32_t*)(src + b * xs))[k] (the FC / SwiGLU output)
 // NS sums over the workgroup with one barrier: every wave must have passed a barrier since the
 // last readers of red (the gather's early barrier) before the first writer here
@@ -156,10 +154,8 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
     bool ok = true;
     // The early barrier: every wave passes one barrier after issuing its first round of polls and
     // before waiting on them, so that the previous phase's readers of xl and red are done before
-    // anything here writes them, while the polls' round trip hides the barrier (the context-long
-    // merge, which polls in several rounds, passes it after its last round instead).
+    // anything here writes them, while the polls' round trip hides the barrier.
     bool early = false;
-    bool paired = false;   // IN_ATTN: lane l holds dim 2 (l % 32) + l / 32 of its wave's 64 elements
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         rs[b] = 1.f;
@@ -184,179 +180,6 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
         }
         lds_barrier();   // the early barrier (see early above)
         early = true;
-    } else if constexpr (IN == IN_ATTN) {
-        // element k = t + NT*j of row b is dim k % HD of head k / HD; chunk s of head h published
-        // (o[0..HD), m, l) in the log2 domain.  A wave covers 64 consecutive elements and HD is a
-        // multiple of 64, so each (b, j) is one head on every lane of a wave: the wave merges its
-        // own heads (the (m, l) words spread over its lanes, then read back as uniform values),
-        // with no barrier and no index arithmetic that depends on the context length.
-        constexpr int HD = C::HD, PS = HD + STEP_PART_PAD;
-        static_assert(HD % 64 == 0 && K % 64 == 0, "a wave's 64 elements lie in one head");
-        constexpr int SGA = 2 * B * J * SG <= 64 ? SG : (32 / (B * J) > 0 ? 32 / (B * J) : 1);
-        static_assert(2 * B * J * SGA <= 64, "one (m or l) word per lane");
-        const int lane = t & 63;
-        int hj[J], ij[J];
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int base = min((t & ~63) + NT * j, K - 64);   // the wave's first element (clamped into K)
-            hj[j] = base / HD;
-            ij[j] = base % HD + lane;
-        }
-        float Mr[B][J], Lr[B][J], Or[B][J];
-#pragma unroll
-        for (int b = 0; b < B; ++b)
-#pragma unroll
-            for (int j = 0; j < J; ++j) {
-                Mr[b][j] = -INFINITY;
-                Lr[b][j] = 0.f;
-                Or[b][j] = 0.f;
-            }
-        // lane 2 * ((b * J + j) * SGA + u) + c holds word c (m, l) of chunk s0 + u of (b, j)
-        const int ml_q = min(lane >> 1, B * J * SGA - 1), ml_u = ml_q % SGA, ml_bj = ml_q / SGA;
-        const int ml_b = ml_bj / J, ml_j = ml_bj - ml_b * J;
-        if (cx.S <= SGA) {
-            // every chunk in one round (up to SGA chunks of context): the merge weights are
-            // computed across the lanes that hold the (m, l) words, then read back per (b, j).
-            // With PAIRS the outputs are read two chunks per 16-byte load: lanes 0..31 read dims
-            // 2i, 2i + 1 of chunk 2p, lanes 32..63 the same dims of chunk 2p + 1 (half the load
-            // instructions of one word per lane and chunk); a swap between the lane halves then
-            // sums the chunks, and lane l ends with dim 2 (l % 32) + l / 32 of the wave's 64.
-            // Without PAIRS (the Q4_0 pair: short of registers) lane l reads dim l of each chunk.
-            constexpr bool PAIRS = !(B == 2 && F == FMT_Q4_0);
-            constexpr int NPR = (SGA + 1) / 2, NQ = PAIRS ? B * J * NPR : B * J * SGA;
-            const int ns = cx.S, npr = (ns + 1) / 2;
-            const int hi = lane >> 5, dl = 2 * (lane & 31);
-            const __amdgpu_buffer_rsrc_t rs_p = xchg::words_rsrc(src, (size_t)B * xs);
-            int hh = 0;
-#pragma unroll
-            for (int j = 0; j < J; ++j)
-                if (j == ml_j) hh = hj[j];
-            const uint64_t* mlp = src + ml_b * xs + ((size_t)hh * a.max_split + min(ml_u, ns - 1)) * PS + HD + (lane & 1);
-            // PAIRS: pair q = (b J + j) NPR + p, the second chunk of a last, odd pair re-reading
-            // chunk ns - 1 (its weight is 0); else word q = (b J + j) SGA + u, chunk u
-            auto use = [&](int q) { return PAIRS ? q % NPR < npr : q % SGA < ns; };
-            auto off = [&](int q) -> uint32_t {
-                const int bj = q / NPR, pp = q % NPR;
-                const int b = bj / J, j = bj - b * J;
-                const int sc = min(2 * pp + hi, ns - 1);
-                return (uint32_t)(8 * (b * xs + ((size_t)hj[j] * a.max_split + sc) * PS + (ij[j] - lane) + dl));
-            };
-            auto addr = [&](int q) -> const uint64_t* {
-                const int bj = q / SGA, u = q % SGA;
-                const int b = bj / J, j = bj - b * J;
-                return src + b * xs + ((size_t)hj[j] * a.max_split + min(u, ns - 1)) * PS + ij[j];
-            };
-            using WT = std::conditional_t<PAIRS, xchg::u64x2, uint64_t>;
-            auto ld = [&](int q) -> WT {
-                if constexpr (PAIRS) return xchg::load2(rs_p, off(q));
-                else return xchg::load(addr(q));
-            };
-            uint64_t wml = xchg::load(mlp);
-            WT wo[NQ];
-#pragma unroll
-            for (int q = 0; q < NQ; ++q)
-                if (use(q)) wo[q] = ld(q);
-            lds_barrier();   // the early barrier (see early above)
-            early = true;
-            ok &= xchg::settle_with(wml, mlp, wo, use, ld, ep, cx.limit, a.abort_word);
-            // lane 2 q + c, q = (b J + j) SGA + u: m (c = 0) or l (c = 1) of chunk u of (b, j); the
-            // 2 SGA lanes of a (b, j) form one aligned group
-            const float mlv = xchg::value(wml);
-            const bool live = ml_u < ns && lane < 2 * B * J * SGA;
-            const float mm = (lane & 1) == 0 && live ? mlv : -INFINITY;
-            const float M = group_max(mm, 2 * SGA);
-            const float w = exp2f(mm - M);                       // the chunk's weight on its m lane, else 0
-            const float wl = dpp_mov<0xB1>(w);                   // on an l lane: its chunk's weight
-            const float L = group_sum((lane & 1) && live ? mlv * wl : 0.f, 2 * SGA);
-            const float f = w / L;                               // final weight of the chunk (m lanes), 0 past ns
-            auto fw = [&](int c) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), 2 * c)); };
-#pragma unroll
-            for (int b = 0; b < B; ++b)
-#pragma unroll
-                for (int j = 0; j < J; ++j) {
-                    const int c0 = (b * J + j) * SGA;   // chunk 0 of (b, j) among the (m, l) lanes
-                    if constexpr (PAIRS) {
-                        float O0 = 0.f, O1 = 0.f;   // dims dl and dl + 1 from this lane's chunks
-#pragma unroll
-                        for (int pp = 0; pp < NPR; ++pp)
-                            if (pp < npr) {
-                                const float f0 = fw(c0 + 2 * pp), f1 = 2 * pp + 1 < SGA ? fw(c0 + 2 * pp + 1) : 0.f;
-                                const float fs = hi ? f1 : f0;
-                                const xchg::u64x2 wq = wo[(b * J + j) * NPR + pp];
-                                O0 = fmaf(xchg::value(wq.x), fs, O0);
-                                O1 = fmaf(xchg::value(wq.y), fs, O1);
-                            }
-                        // lanes 0..31 keep dim dl and take the other half's share of it; lanes 32..63 dim dl + 1
-                        v[b][j] = (hi ? O1 : O0) + swap32_other(hi ? O0 : O1);
-                    } else {
-                        float O = 0.f;
-#pragma unroll
-                        for (int u = 0; u < SGA; ++u)
-                            if (u < ns) O = fmaf(xchg::value(wo[c0 + u]), fw(c0 + u), O);
-                        v[b][j] = O;
-                    }
-                }
-            paired = PAIRS;
-        } else {
-            for (int s0 = 0; s0 < cx.S; s0 += SGA) {
-                const int ns = min(SGA, cx.S - s0);
-                // word 0: this lane's (m or l) word; 1 + (b*J + j)*SGA + u: the chunk-(s0+u) output of
-                // (b, j) at this lane's dim (chunks past the context re-read the last one, unused)
-                auto addr = [&](int q) -> const uint64_t* {
-                    if (q == 0) {
-                        int hh = 0;
-    #pragma unroll
-                        for (int j = 0; j < J; ++j)
-                            if (j == ml_j) hh = hj[j];
-                        return src + ml_b * xs + ((size_t)hh * a.max_split + s0 + min(ml_u, ns - 1)) * PS + HD + (lane & 1);
-                    }
-                    const int bj = (q - 1) / SGA, u = (q - 1) % SGA;
-                    const int b = bj / J, j = bj - b * J;
-                    return src + b * xs + ((size_t)hj[j] * a.max_split + s0 + min(u, ns - 1)) * PS + ij[j];
-                };
-                constexpr int NW = 1 + B * J * SGA;
-                auto use = [&](int q) { return q == 0 || (q - 1) % SGA < ns; };
-                uint64_t wv[NW];
-    #pragma unroll
-                for (int q = 0; q < NW; ++q)
-                    if (use(q)) wv[q] = xchg::load(addr(q));
-                ok &= xchg::settle_if(wv, use, addr, ep, cx.limit, a.abort_word);
-                const float mlv = xchg::value(wv[0]);
-    #pragma unroll
-                for (int b = 0; b < B; ++b)
-    #pragma unroll
-                    for (int j = 0; j < J; ++j) {
-                        float mu[SGA], lu[SGA];
-    #pragma unroll
-                        for (int u = 0; u < SGA; ++u) {
-                            const int ln = 2 * ((b * J + j) * SGA + u);
-                            mu[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv), ln));
-                            lu[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv), ln + 1));
-                        }
-                        float M = Mr[b][j];
-    #pragma unroll
-                        for (int u = 0; u < SGA; ++u)
-                            if (u < ns) M = fmaxf(M, mu[u]);
-                        const float sc = exp2f(Mr[b][j] - M);          // rescale of the running sums (0 at start)
-                        float L = Lr[b][j] * sc, O = Or[b][j] * sc;
-    #pragma unroll
-                        for (int u = 0; u < SGA; ++u) {
-                            if (u < ns) {
-                                const float wgt = exp2f(mu[u] - M);
-                                L = fmaf(lu[u], wgt, L);
-                                O = fmaf(xchg::value(wv[1 + (b * J + j) * SGA + u]), wgt, O);
-                            }
-                        }
-                        Mr[b][j] = M;
-                        Lr[b][j] = L;
-                        Or[b][j] = O;
-                    }
-            }
-    #pragma unroll
-            for (int b = 0; b < B; ++b)
-    #pragma unroll
-                for (int j = 0; j < J; ++j) v[b][j] = __fdividef(Or[b][j], Lr[b][j]);
-        }
     } else if constexpr (IN == IN_XCHG32) {
         constexpr int NW = B * J;
         auto addr = [&](int q) -> const uint32_t* {
@@ -398,7 +221,7 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
     if (!ok) *sm.abort = 1;
     if (!early) lds_barrier();   // the previous phase's readers of xl and red are done
     auto put = [&](int b, int j, float y) {
-        const int k = (paired ? (t & ~63) + 2 * (t & 31) + ((t >> 5) & 1) : t) + NT * j;
+        const int k = t + NT * j;
         if (X16 && (k & 31) >= 16) y *= 0.0625f;   // exact
         if (K % NT == 0 || k < K) sm.xl[b * MAX_K + 4 * swz<E>(k, LPR) + (k & 3)] = y;
     };
@@ -454,7 +277,7 @@ __device__ __forceinline__ void gather_x(const StepArgs& a, const Ctx& cx, const
 
 // ---- one GEMV phase --------------------------------------------------------------------------
 struct PhaseIO {
-    const uint64_t* src;  // input words (IN_XCHG / IN_NORM / IN_ATTN); row b at src + b * src_xs
+    const uint64_t* src;  // input words (IN_XCHG / IN_NORM); row b at src + b * src_xs
     long long src_xs;
     uint32_t src_ep;
     const float* g;       // norm gain
@@ -887,7 +710,11 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
 // Work item (row b, head h, chunk s) = keys [256 s, 256 s + 256) of query head h; the same math as
 // k_attn (attention.hip), with the query and the new position's key/value taken from the
 // exchange.  Items go to the highest-numbered workgroups, which the QKV phase leaves idle when
-// it has fewer tiles than the grid has workgroups.
+// it has fewer tiles than the grid has workgroups.  One writer per head: the item of the head's
+// last chunk merges the other chunks' (o, m, l) partials into its own and publishes the head's
+// output o / l as plain exchange words (after the partials, at word H * max_split * (hd +
+// STEP_PART_PAD) of a row), so the output projection polls hd words per head like any other
+// input instead of every chunk's partial.
 template <class C>
 __device__ __forceinline__ bool attn_phase(const StepArgs& a, const Ctx& cx, const __half* kcache, const __half* vcache,
                                            const uint32_t ep_qkv, const uint32_t ep_part, Smem& sm)
@@ -898,13 +725,29 @@ __device__ __forceinline__ bool attn_phase(const StepArgs& a, const Ctx& cx, con
     __shared__ float mw[NWAVE], lw[NWAVE];
     __shared__ float qkv_l[3 * HD];   // the query, new key and new value of the item
     const int items = C::B * H * cx.S;
+    const int last = cx.S - 1;                 // a head's last chunk
+    const int n_first = C::B * H * last;       // the other chunks' items come first
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c = lane % LPK, kq = lane / LPK;
     const int n_keys = cx.n_keys;
     const float qscale = 1.4426950408889634f / sqrtf((float)HD);
 
     for (int item = (int)gridDim.x - 1 - (int)blockIdx.x; item < items; item += gridDim.x) {
-        const int h = item % H, bs = item / H, s = bs % cx.S, b = bs / cx.S, g = h / (H / HK);
+        // Items 0 .. n_first - 1 are the chunks before the last, then one item per (row, head) for
+        // its last chunk, which waits for the others' partials.  A workgroup takes its items in
+        // increasing order, so every item queued ahead of an awaited one never waits itself: the
+        // waits always end.
+        int h, s, b;
+        if (item < n_first) {
+            h = item % H;
+            s = (item / H) % last;
+            b = item / H / last;
+        } else {
+            h = (item - n_first) % H;
+            b = (item - n_first) / H;
+            s = last;
+        }
+        const int g = h / (H / HK);
         const int k0 = s * ATTN_CHUNK + wave * KTILE;
         const size_t head_off = (size_t)b * a.kv_row + (size_t)g * a.n_ctx * HD;
         const int klast = n_keys - 1;
@@ -1015,17 +858,61 @@ __device__ __forceinline__ bool attn_phase(const StepArgs& a, const Ctx& cx, con
 #pragma unroll
         for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, mw[w]);
         uint64_t* part = a.x_part + b * a.xs_part + ((size_t)h * a.max_split + s) * PS;
-        if (threadIdx.x < HD) {
-            float acc = 0.f;
+        const int tc = min((int)threadIdx.x, HD - 1);
+        float acc = 0.f, L = 0.f;
 #pragma unroll
-            for (int w = 0; w < NWAVE; ++w) acc = fmaf(ow[w][threadIdx.x], exp2f(mw[w] - M), acc);
-            xchg::store(part + threadIdx.x, acc, ep_part);
-        } else if (threadIdx.x == HD) {
-            float L = 0.f;
+        for (int w = 0; w < NWAVE; ++w) {
+            const float f = exp2f(mw[w] - M);
+            acc = fmaf(ow[w][tc], f, acc);
+            L = fmaf(lw[w], f, L);
+        }
+        if (s != last) {   // a partial for the head's last chunk to merge
+            if (threadIdx.x < HD) {
+                xchg::store(part + threadIdx.x, acc, ep_part);
+            } else if (threadIdx.x == HD) {
+                xchg::store(part + HD, M, ep_part);
+                xchg::store(part + HD + 1, L, ep_part);
+            }
+        } else {
+            // the other chunks' partials, one per wave and round, through LDS
+            for (int s0 = 0; s0 < last; s0 += NWAVE) {
+                lds_barrier();   // every reader of ow, mw and lw is done
+                const int sib = s0 + wave;
+                if (sib < last) {
+                    const uint64_t* ps = a.x_part + b * a.xs_part + ((size_t)h * a.max_split + sib) * PS;
+                    constexpr int NO = HD / 64;   // output words per lane, then this lane's (m or l) word
+                    auto addr = [&](int i) { return i < NO ? ps + lane + 64 * i : ps + HD + min(lane, 1); };
+                    uint64_t wv[NO + 1];
 #pragma unroll
-            for (int w = 0; w < NWAVE; ++w) L = fmaf(lw[w], exp2f(mw[w] - M), L);
-            xchg::store(part + HD, M, ep_part);
-            xchg::store(part + HD + 1, L, ep_part);
+                    for (int i = 0; i <= NO; ++i) wv[i] = xchg::load(addr(i));
+                    if (!xchg::settle_n(wv, NO + 1, addr, ep_part, cx.limit, a.abort_word)) *sm.abort = 1;
+#pragma unroll
+                    for (int i = 0; i < NO; ++i) ow[wave][lane + 64 * i] = xchg::value(wv[i]);
+                    if (lane == 0) mw[wave] = xchg::value(wv[NO]);
+                    if (lane == 1) lw[wave] = xchg::value(wv[NO]);
+                }
+                lds_barrier();
+                if (*sm.abort) return false;
+                const int nw = min(NWAVE, last - s0);
+                float Mn = M;
+#pragma unroll
+                for (int w = 0; w < NWAVE; ++w)
+                    if (w < nw) Mn = fmaxf(Mn, mw[w]);
+                const float sc = exp2f(M - Mn);
+                acc *= sc;
+                L *= sc;
+#pragma unroll
+                for (int w = 0; w < NWAVE; ++w)
+                    if (w < nw) {
+                        const float f = exp2f(mw[w] - Mn);
+                        acc = fmaf(ow[w][tc], f, acc);
+                        L = fmaf(lw[w], f, L);
+                    }
+                M = Mn;
+            }
+            if (threadIdx.x < HD)
+                xchg::store(a.x_part + b * a.xs_part + (size_t)H * a.max_split * PS + h * HD + threadIdx.x,
+                            acc / L, ep_part);
         }
     }
     return true;
@@ -1147,7 +1034,7 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
             const StepArgs& a = opaque(ap);
             const long long o = a.lstride * l;
             PhaseIO io{};
-            io.src = a.x_part;
+            io.src = a.x_part + (size_t)C::H * a.max_split * (C::HD + STEP_PART_PAD);   // the heads' outputs
             io.src_xs = a.xs_part;
             io.src_ep = e + 1u;
             io.bias = shift(a.L0.bo, o);
@@ -1157,7 +1044,7 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
             io.res = l == 0 ? nullptr : a.x_out;
             io.res_xs = a.xs_d;
             io.res_ep = e - 1u;
-            if (!gemv_phase<C, C::QD, C::D, C::NL_O, IN_ATTN, OUT_RESID, false>(a, cx, shift(a.L0.o, o), io, sm))
+            if (!gemv_phase<C, C::QD, C::D, C::NL_O, IN_XCHG, OUT_RESID, false>(a, cx, shift(a.L0.o, o), io, sm))
                 return give_up(a);
         }
         {   // 4. norm + FC (+bias, GELU) | gate/up (SwiGLU)

@@ -168,6 +168,8 @@ constexpr int STEP_SHIFT_COPIES = 4, STEP_SHIFT_STRIDE = 16;
 // whole number of 128-byte lines, so that no line holds words of two partials (which the waves of
 // the merging item poll separately).
 constexpr int STEP_PART_PAD = 16;
+// chunks per head the persistent step may split a context of n_ctx keys into (128 keys or more each)
+__host__ __device__ inline int step_max_split(int n_ctx) { return (n_ctx + 127) / 128; }
 struct StepArgs {
     StepLayer L0;                             // layer 0; layer l is layer 0 moved by l strides
     long long lstride;                        // bytes between consecutive layers' weights and vectors
@@ -187,12 +189,13 @@ struct StepArgs {
     uint32_t* abort_word;                     // sticky: a wait gave up
     const uint32_t* bad_input;                // sticky: an input id was rejected (the launch does nothing)
     float* logits;                            // [B][vocab]
-    // exchange words: QKV out, attention partials [H][max_split][hd+STEP_PART_PAD] then the heads'
-    // outputs [H * hd], attention-block output
+    // exchange words: QKV out, attention partials [H][max_split][hd+STEP_PART_PAD], attention-block output
     // (residual stream), MLP hidden, layer output (residual stream), per-workgroup argmax keys;
     // batch row b's words of each buffer start b * its row stride (xs_*) after row 0's
     uint64_t *x_qkv, *x_part, *x_attn, *x_h, *x_out, *x_best;
     long long xs_qkv, xs_part, xs_d, xs_h, xs_best, xs_logit;   // row strides in words (xs_d: x_attn, x_out)
+    uint64_t* x_ao;                           // [B][H * hd] the heads' attention outputs (one writer per head)
+    long long xs_ao;
     long long kv_row;                         // elements between batch rows of a layer's cache
     int cfg;                                  // two rows guided: one draw from l0 + cfg_weight (l0 - l1)
     float cfg_weight;

@@ -31,6 +31,12 @@ struct Planner {
         off += bytes;
         return p;
     }
+    // move to the next device address that is a multiple of a (a power of two); when only sizing
+    // (no base), reserve the most that can take
+    void align_abs(size_t a)
+    {
+        off += base ? (a - ((size_t)(uintptr_t)base + off) % a) % a : a - 1;
+    }
 };
 
 // a LLAMA-shaped layer of the batched frame: tiled matrices (qkv rows in RoPE pairs, gate/up

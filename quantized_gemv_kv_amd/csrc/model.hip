@@ -181,15 +181,28 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
     // persistent step: layer table, control words, exchange words
     uint32_t* ctl = (uint32_t*)P.take(sizeof(uint32_t) * 64);
     StepArgs* d_sa = (StepArgs*)P.take(sizeof(StepArgs));
-    const size_t n_part = (size_t)H * attn_max_split(c->n_ctx) * (hd + STEP_PART_PAD) + (size_t)H * hd;   // + one writer's outputs
-    // one batch row's words of each buffer (rounded to 32 words); a buffer holds B rows
+    const size_t n_part = (size_t)H * step_max_split(c->n_ctx) * (hd + STEP_PART_PAD);
+    // one batch row's words of each buffer (rounded up as below); a buffer holds B rows
     const size_t dsh = (size_t)d + STEP_SHIFT_COPIES * STEP_SHIFT_STRIDE;   // residual words + the shift's copies
-    const size_t xw[7] = {(size_t)qkv_rows, n_part, dsh, (size_t)ff, dsh, 2 * (size_t)MAX_STEP_WG, (size_t)vmax};
-    size_t xrs[7], xtot = 0;
-    for (int i = 0; i < 7; ++i) {
-        xrs[i] = (xw[i] + 31) & ~(size_t)31;
-        xtot += xrs[i] * B;
+    const size_t xw[8] = {(size_t)qkv_rows, n_part, dsh, (size_t)ff, dsh, 2 * (size_t)MAX_STEP_WG, (size_t)vmax, (size_t)H * hd};
+    size_t xrs[8], xtot = 0;
+    // Placement (measured, same-box A/B): every buffer in a region of its own that starts at a
+    // 64 KB boundary of the device address space, 4 KB times its index further on, with each
+    // batch row of a buffer at a 4 KB boundary plus 256 bytes.  Against rows packed at 256-byte
+    // steps from wherever the weights end, the 64 KB start and the 4 KB rows took C3 293.8 ->
+    // 289.6 us per step and C4 420.1 -> 415.7 us; the regions keep a buffer's place independent
+    // of the other buffers' sizes.
+    // The polls of a phase go to the memory-side cache, whose slice follows the address, so
+    // where the polled lines sit decides how they queue.
+    constexpr size_t XREG = 8192;   // 64 KB in words
+    static const size_t XSKEW[8] = {0, 512, 1024, 1536, 2048, 2560, 3072, 3584};
+    size_t xoff[8];
+    for (int i = 0; i < 8; ++i) {
+        xrs[i] = ((xw[i] + 511) & ~(size_t)511) + 32;
+        xoff[i] = xtot + XSKEW[i];
+        xtot = (xoff[i] + xrs[i] * B + XREG - 1) / XREG * XREG;
     }
+    P.align_abs(65536);
     uint64_t* xbuf = (uint64_t*)P.take(sizeof(uint64_t) * xtot);
     // prompt pass rows
     const int pf_rows = (int)std::min<long long>(PF_MAX_ROWS, ((long long)B * c->n_ctx + PF_TILE - 1) / PF_TILE * PF_TILE);
@@ -213,17 +226,14 @@ size_t plan(tsd_model* m, const tsd_config* c, uint8_t* base)
         m->d_sa = d_sa;
         m->xbuf = xbuf;
         m->xbuf_words = xtot;
-        uint64_t* xp[7];
-        uint64_t* q = xbuf;
-        for (int i = 0; i < 7; ++i) {
-            xp[i] = q;
-            q += xrs[i] * B;
-        }
+        uint64_t* xp[8];
+        for (int i = 0; i < 8; ++i) xp[i] = xbuf + xoff[i];
         StepArgs& a = m->sa;
         a.x_qkv = xp[0]; a.x_part = xp[1]; a.x_attn = xp[2]; a.x_h = xp[3]; a.x_out = xp[4]; a.x_best = xp[5];
         a.x_logit = xp[6];
         a.xs_qkv = (long long)xrs[0]; a.xs_part = (long long)xrs[1]; a.xs_d = (long long)xrs[2]; a.xs_h = (long long)xrs[3];
         a.xs_best = (long long)xrs[5]; a.xs_logit = (long long)xrs[6];
+        a.x_ao = xp[7]; a.xs_ao = (long long)xrs[7];
     }
     return align256(P.off);
 }
@@ -530,7 +540,7 @@ tsd_status setup_step(tsd_model* m)
     a.lstride = stride;
     a.kvstride = (long long)m->kv_layer_elems;
     a.n_layer = c.n_layer; a.H = c.n_head; a.Hk = c.n_kv_head; a.n_ctx = c.n_ctx; a.vocab = c.vocab;
-    a.max_split = attn_max_split(c.n_ctx);
+    a.max_split = step_max_split(c.n_ctx);
     a.eps = c.norm_eps;
     a.emb = m->emb[0]; a.wpe = m->wpe; a.nfg = m->nfg; a.nfb = m->nfb; a.hc = m->hc; a.hdv = m->hdv; a.head = m->head; a.rope = m->rope;
     a.pos = m->pos; a.tok = m->tok; a.hist = m->hist; a.seq = m->seq; a.ctr = m->ctl + CTL_EPOCH; a.abort_word = m->ctl + CTL_ABORT;

@@ -47,7 +47,7 @@ using namespace core;
 constexpr int NT = 256;
 constexpr int NWAVE = NT / 64;
 static_assert(NWAVE <= STEP_SHIFT_COPIES, "a copy of the LayerNorm shift per wave");
-constexpr int KTILE = 64;    // keys per wave in the attention phase (4 waves: one 256-key chunk)
+constexpr int KTILE = 64;    // keys per wave in the attention phase (4 waves: one 256-key chunk), or half
 
 enum { A_GPT2 = 0, A_LLAMA = 1 };
 enum { IN_XCHG = 0, IN_NORM = 1, IN_EMB_NORM = 2, IN_XCHG32 = 3 };
@@ -103,7 +103,8 @@ struct Smem {
 };
 
 struct Ctx {
-    int pos, tok[2], n_keys, S;   // tok: each batch row's input token
+    int pos, tok[2], n_keys, S;   // tok: each batch row's input token; S attention chunks per head
+    bool half_chunks;             // chunks of 128 keys (else 256)
     long long limit;
 };
 
@@ -707,20 +708,20 @@ __device__ __forceinline__ bool gemv_phase(const StepArgs& a, const Ctx& cx, con
 }
 
 // ---- attention phase -------------------------------------------------------------------------
-// Work item (row b, head h, chunk s) = keys [256 s, 256 s + 256) of query head h; the same math as
+// Work item (row b, head h, chunk s) = keys [C s, C s + C) of query head h, C = NWAVE * KT (256
+// or 128 keys: KT per wave); the same math as
 // k_attn (attention.hip), with the query and the new position's key/value taken from the
 // exchange.  Items go to the highest-numbered workgroups, which the QKV phase leaves idle when
 // it has fewer tiles than the grid has workgroups.  One writer per head: the item of the head's
 // last chunk merges the other chunks' (o, m, l) partials into its own and publishes the head's
-// output o / l as plain exchange words (after the partials, at word H * max_split * (hd +
-// STEP_PART_PAD) of a row), so the output projection polls hd words per head like any other
-// input instead of every chunk's partial.
-template <class C>
+// output o / l as plain exchange words (x_ao), so the output projection polls hd words per head
+// like any other input instead of every chunk's partial.
+template <class C, int KT>
 __device__ __forceinline__ bool attn_phase(const StepArgs& a, const Ctx& cx, const __half* kcache, const __half* vcache,
                                            const uint32_t ep_qkv, const uint32_t ep_part, Smem& sm)
 {
     constexpr int HD = C::HD, H = C::H, HK = C::HK, QD = C::QD, KD = C::KD;
-    constexpr int LPK = HD / 8, KPI = 64 / LPK, R = KTILE / KPI, PS = HD + STEP_PART_PAD;
+    constexpr int LPK = HD / 8, KPI = 64 / LPK, R = KT / KPI, PS = HD + STEP_PART_PAD;
     __shared__ float ow[NWAVE][HD];
     __shared__ float mw[NWAVE], lw[NWAVE];
     __shared__ float qkv_l[3 * HD];   // the query, new key and new value of the item
@@ -748,7 +749,7 @@ __device__ __forceinline__ bool attn_phase(const StepArgs& a, const Ctx& cx, con
             s = last;
         }
         const int g = h / (H / HK);
-        const int k0 = s * ATTN_CHUNK + wave * KTILE;
+        const int k0 = (s * NWAVE + wave) * KT;
         const size_t head_off = (size_t)b * a.kv_row + (size_t)g * a.n_ctx * HD;
         const int klast = n_keys - 1;
         uint4 kr[R], vr[R];
@@ -911,8 +912,7 @@ __device__ __forceinline__ bool attn_phase(const StepArgs& a, const Ctx& cx, con
                 M = Mn;
             }
             if (threadIdx.x < HD)
-                xchg::store(a.x_part + b * a.xs_part + (size_t)H * a.max_split * PS + h * HD + threadIdx.x,
-                            acc / L, ep_part);
+                xchg::store(a.x_ao + b * a.xs_ao + h * HD + threadIdx.x, acc / L, ep_part);
         }
     }
     return true;
@@ -989,7 +989,16 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
         }
         ctr = (uint32_t)ld_uniform((const int*)a.ctr);
         cx.n_keys = cx.pos + 1;
-        cx.S = (cx.n_keys + ATTN_CHUNK - 1) / ATTN_CHUNK;
+        // 128-key chunks halve each item's chain of dependent arithmetic, where that needs no
+        // more merging (a context of at most 128 keys, or one already split) than one round
+        // of the merging item, and the items still fit the workgroups the QKV phase leaves free
+        {
+            constexpr int CH = NWAVE * KTILE, QKV_TILES = Geo<C::F, C::D, C::QKV, C::NL_D>::TILES;
+            const int s_full = (cx.n_keys + CH - 1) / CH, s_half = (cx.n_keys + CH / 2 - 1) / (CH / 2);
+            cx.half_chunks = (s_full >= 2 || s_half == 1) && s_half - 1 <= NWAVE &&
+                             B * C::H * s_half <= (int)gridDim.x - QKV_TILES;
+            cx.S = cx.half_chunks ? s_half : s_full;
+        }
         cx.limit = a.spin_limit;
         n_layer = a.n_layer;
         lds_barrier();
@@ -1027,15 +1036,18 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs* __restrict__ args)
         }
         {   // 2. attention partials
             const StepArgs& a = opaque(ap);
-            if (!attn_phase<C>(a, cx, a.L0.kc + a.kvstride * l, a.L0.vc + a.kvstride * l, e, e + 1u, sm))
+            const __half* kc = a.L0.kc + a.kvstride * l;
+            const __half* vc = a.L0.vc + a.kvstride * l;
+            if (!(cx.half_chunks ? attn_phase<C, KTILE / 2>(a, cx, kc, vc, e, e + 1u, sm)
+                                 : attn_phase<C, KTILE>(a, cx, kc, vc, e, e + 1u, sm)))
                 return give_up(a);
         }
         {   // 3. merge + output projection + bias + residual
             const StepArgs& a = opaque(ap);
             const long long o = a.lstride * l;
             PhaseIO io{};
-            io.src = a.x_part + (size_t)C::H * a.max_split * (C::HD + STEP_PART_PAD);   // the heads' outputs
-            io.src_xs = a.xs_part;
+            io.src = a.x_ao;
+            io.src_xs = a.xs_ao;
             io.src_ep = e + 1u;
             io.bias = shift(a.L0.bo, o);
             io.dst = a.x_attn;

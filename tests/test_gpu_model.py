@@ -261,10 +261,13 @@ def test_gpt2_medium_one_layer_after_512_positions():
 
 
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("name,kv_pos", [("gpt2_medium_q4_0", 755), ("llama520m_q8_0", 899)])
+@pytest.mark.parametrize("name,kv_pos", [("gpt2_medium_q4_0", 755), ("llama520m_q8_0", 899), ("gpt2_medium_q4_0", 300),
+                                         ("llama520m_q8_0", 511)])
 def test_full_size_step_over_long_cache(name, kv_pos, mode):
-    """All layers at their real shapes, one teacher-forced step at the last position of the
-    decode run (756 / 900 keys), and one more at the next position."""
+    """All layers at their real shapes, one teacher-forced step at kv_pos and one more at the next
+    position: the last positions of the decode runs (756 / 900 keys, 256-key attention chunks),
+    301 keys (three 128-key chunks), and 512 then 513 keys (the persistent step switching from
+    four 128-key chunks to three 256-key chunks between the two steps)."""
     cfg = synth.config(name)
     say(f"[model-full] {name} kv_pos={kv_pos} {mode}")
     w = synth.model_weights(cfg, 42)

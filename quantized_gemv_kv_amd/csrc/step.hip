@@ -12,8 +12,10 @@
 // ramp of each new grid adds more; the journal measures the same effect as a step that is
 // "dispatch-bound" (§3.14) and the frame post as a fixed cost per kernel (§4).  Here the grid
 // is launched once, one workgroup per compute unit, and walks the step's phases in order:
-//   * a phase's work is cut into tiles (rows of a matrix, or one head x 256-key chunk of the
-//     cache); workgroup w takes tile w (and w + G, ... when there are more tiles);
+//   * a phase's work is cut into tiles (rows of a matrix, or one head x 256- or 128-key chunk
+//     of the cache); workgroup w takes tile w (and w + G, ... when there are more tiles);
+//   * the attention output reaches the output projection through one writer per head, the item
+//     of the head's last chunk, which merges the other chunks' partials;
 //   * a phase's output is published as exchange words (exchange.h) carrying the phase's epoch,
 //     and the next phase's workgroups poll exactly the words they need — there is no grid-wide
 //     barrier, only data dependencies, each resolved by one round trip to the memory-side cache;
